@@ -1,0 +1,243 @@
+"""MI355X-native fused scaled-dot-product attention (Python binding).
+
+Thin ctypes layer over the C ABI in include/sdpa.h (libsdpa.so, built
+in-tree for gfx950 by attention_flash_sdpa_amd/build.py).  This module only
+marshals arguments: torch provides device memory and the current stream;
+every step of the attention runs in the library's HIP kernels.  There is no
+CPU fallback -- if the library or a GPU is missing, the calls raise.
+
+    O = softmax(Q . K^T * scale + B) . V
+
+[Axon PR 650] "Axon.Layers.scaled_dot_product_attention/4", description:
+bshd (default) / bhsd layouts, scale defaulting to 1/sqrt(head_dim), causal /
+sliding-window / tensor masks, grouped-query attention.
+[mlx-examples issue 1451] "segment_anything: fuse attention with
+mx.fast.scaled_dot_product_attention", body: SAM's decomposed rel-pos bias.
+[Candle PR 3280] "feat(metal): SDPA with Relative Positional Embeddings &
+LayerNorm Stability", Key Changes: term_h / term_w injected into the scores.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import threading
+
+import torch
+
+__all__ = ["load", "lib_path", "sdpa", "sdpa_relpos", "relpos_terms", "workspace_size",
+           "set_tuning", "SdpaError", "F32", "BF16", "BSHD", "BHSD"]
+
+F32, BF16 = 0, 1
+BSHD, BHSD = 0, 1
+_MASK_KIND = {"none": 0, "causal": 1, "sliding": 2, "additive": 3, "bool": 4}
+_LAYOUT = {"bshd": BSHD, "bhsd": BHSD}
+_DTYPE = {torch.float32: F32, torch.bfloat16: BF16}
+
+
+class SdpaError(RuntimeError):
+    def __init__(self, status, where, detail):
+        super().__init__(f"{where}: status {status} ({detail})")
+        self.status = status
+
+
+class _Mask(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("data_dtype", ctypes.c_int32),
+                ("offset", ctypes.c_int64), ("window", ctypes.c_int64),
+                ("data", ctypes.c_void_p), ("stride", ctypes.c_int64 * 4)]
+
+
+_LIB = None
+_LOCK = threading.Lock()
+_P, _I64, _I32, _F = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float
+
+
+def lib_path():
+    return os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsdpa.so")
+
+
+def load():
+    """Load libsdpa.so (raises if it has not been built)."""
+    global _LIB
+    with _LOCK:
+        if _LIB is not None:
+            return _LIB
+        path = lib_path()
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing: build it with attention_flash_sdpa_amd/build.py")
+        lib = ctypes.CDLL(path)
+        lib.sdpa_workspace_size.restype = ctypes.c_size_t
+        lib.sdpa_workspace_size.argtypes = [_I64] * 6 + [_I32, _I64, _I64]
+        lib.sdpa_fwd.restype = _I32
+        lib.sdpa_fwd.argtypes = [_P, _P, _P, _P, _I32, _I32, _I32] + [_I64] * 6 + \
+            [_F, ctypes.POINTER(_Mask), _P, _P, ctypes.c_size_t, _P]
+        lib.relpos_terms.restype = _I32
+        lib.relpos_terms.argtypes = [_P, _I32, _I32] + [_I64] * 5 + [_P, _P, _P, _P, _P]
+        lib.sdpa_relpos_fwd.restype = _I32
+        lib.sdpa_relpos_fwd.argtypes = [_P, _P, _P, _P, _I32, _I32, _I32] + [_I64] * 5 + \
+            [_P, _P, _F, _P, _P, ctypes.c_size_t, _P]
+        lib.sdpa_status_string.restype = ctypes.c_char_p
+        lib.sdpa_status_string.argtypes = [_I32]
+        lib.sdpa_last_error.restype = ctypes.c_char_p
+        lib.sdpa_last_error.argtypes = []
+        lib.sdpa_set_tuning.restype = _I32
+        lib.sdpa_set_tuning.argtypes = [ctypes.c_char_p, _I64]
+        _LIB = lib
+        return lib
+
+
+def _check(status, where):
+    if status != 0:
+        lib = load()
+        detail = lib.sdpa_last_error().decode() or lib.sdpa_status_string(status).decode()
+        raise SdpaError(status, where, detail)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _need_gpu(*ts):
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError("tensors must live on the GPU (no CPU path exists)")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous in the stated layout")
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def set_tuning(key, value):
+    """Process-wide knob: "num_splits" (0 = auto) or "relpos_fused" (0/1)."""
+    _check(load().sdpa_set_tuning(key.encode(), int(value)), "sdpa_set_tuning")
+
+
+def workspace_size(B, Hq, Hkv, Tq, Tkv, D, relpos=False, grid=(0, 0)):
+    n = load().sdpa_workspace_size(B, Hq, Hkv, Tq, Tkv, D, int(bool(relpos)), grid[0], grid[1])
+    if n == ctypes.c_size_t(-1).value:
+        raise ValueError("invalid sizes for sdpa_workspace_size")
+    return n
+
+
+def _dims(q, k, layout):
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q, k, v must be rank-4")
+    if layout == "bhsd":
+        B, Hq, Tq, D = q.shape
+        _, Hkv, Tkv, _ = k.shape
+    else:
+        B, Tq, Hq, D = q.shape
+        _, Tkv, Hkv, _ = k.shape
+    return B, Hq, Hkv, Tq, Tkv, D
+
+
+def _mask_struct(mask, B, Hq, Tq, Tkv, keep):
+    m = _Mask()
+    m.kind = 0
+    if mask is None:
+        return m
+    kind = mask["kind"]
+    m.kind = _MASK_KIND[kind]
+    m.offset = int(mask.get("offset", 0))
+    m.window = int(mask.get("window", 0))
+    if kind in ("additive", "bool"):
+        data = mask["data"]
+        _need_gpu(data)
+        if data.dim() != 4:
+            raise ValueError("tensor masks are rank-4, broadcastable to [B, Hq, Tq, Tkv]")
+        if kind == "bool":
+            if data.dtype != torch.bool:
+                raise ValueError("bool masks must be torch.bool")
+            data = data.view(torch.uint8)
+        else:
+            if data.dtype not in _DTYPE:
+                raise ValueError("additive masks must be float32 or bfloat16")
+            m.data_dtype = _DTYPE[data.dtype]
+        ex = data.expand(B, Hq, Tq, Tkv)
+        for a in range(4):
+            m.stride[a] = ex.stride(a)
+        m.data = data.data_ptr()
+        keep.append(data)
+    return m
+
+
+def sdpa(q, k, v, *, layout="bhsd", scale=None, mask=None, out_dtype=None, return_lse=False,
+         stream=None, out=None):
+    """Fused attention on the GPU.
+
+    q: [B, Hq, Tq, D] (bhsd) or [B, Tq, Hq, D] (bshd); k, v with Hkv heads.
+    mask: None | {"kind": "causal", "offset": d} | {"kind": "sliding", "window": w, "offset": d}
+          | {"kind": "additive", "data": tensor} | {"kind": "bool", "data": bool tensor}
+    out_dtype: None (= q.dtype) or torch.float32.
+    """
+    lib = load()
+    _need_gpu(q, k, v)
+    if q.dtype not in _DTYPE or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share dtype float32 or bfloat16")
+    B, Hq, Hkv, Tq, Tkv, D = _dims(q, k, layout)
+    odt = q.dtype if out_dtype is None else out_dtype
+    o = out if out is not None else torch.empty(q.shape, dtype=odt, device=q.device)
+    lse = torch.empty((B, Hq, Tq), dtype=torch.float32, device=q.device) if return_lse else None
+    keep = []
+    ms = _mask_struct(mask, B, Hq, Tq, Tkv, keep)
+    ws_n = lib.sdpa_workspace_size(B, Hq, Hkv, Tq, Tkv, D, 0, 0, 0)
+    ws = torch.empty(ws_n, dtype=torch.uint8, device=q.device) if ws_n else None
+    sc = float("nan") if scale is None else float(scale)
+    st = lib.sdpa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _DTYPE[q.dtype], _DTYPE[odt], _LAYOUT[layout],
+                      B, Hq, Hkv, Tq, Tkv, D, sc, ctypes.byref(ms), _ptr(lse), _ptr(ws), ws_n, _stream(stream))
+    _check(st, "sdpa_fwd")
+    return (o, lse) if return_lse else o
+
+
+def relpos_terms(q, rel_pos_h, rel_pos_w, grid, *, layout="bhsd", stream=None):
+    """term_h [B, H, T, grid_h], term_w [B, H, T, grid_w] (fp32) on the GPU."""
+    lib = load()
+    _need_gpu(q, rel_pos_h, rel_pos_w)
+    gh, gw = grid
+    if layout == "bhsd":
+        B, H, T, D = q.shape
+    else:
+        B, T, H, D = q.shape
+    th = torch.empty((B, H, T, gh), dtype=torch.float32, device=q.device)
+    tw = torch.empty((B, H, T, gw), dtype=torch.float32, device=q.device)
+    st = lib.relpos_terms(_ptr(q), _DTYPE[q.dtype], _LAYOUT[layout], B, H, gh, gw, D,
+                          _ptr(rel_pos_h), _ptr(rel_pos_w), _ptr(th), _ptr(tw), _stream(stream))
+    _check(st, "relpos_terms")
+    return th, tw
+
+
+def sdpa_relpos(q, k, v, rel_pos_h, rel_pos_w, grid, *, layout="bhsd", scale=None, out_dtype=None,
+                return_lse=False, stream=None, out=None, workspace=None):
+    """Fused attention with the decomposed rel-pos bias (self-attention on a grid)."""
+    lib = load()
+    _need_gpu(q, k, v, rel_pos_h, rel_pos_w)
+    if q.dtype not in _DTYPE or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share dtype float32 or bfloat16")
+    gh, gw = grid
+    if layout == "bhsd":
+        B, H, T, D = q.shape
+    else:
+        B, T, H, D = q.shape
+    odt = q.dtype if out_dtype is None else out_dtype
+    o = out if out is not None else torch.empty(q.shape, dtype=odt, device=q.device)
+    lse = torch.empty((B, H, T), dtype=torch.float32, device=q.device) if return_lse else None
+    ws_n = lib.sdpa_workspace_size(B, H, H, T, T, D, 1, gh, gw)
+    if ws_n == ctypes.c_size_t(-1).value:
+        raise ValueError("grid does not match the sequence length")
+    ws = workspace
+    if ws is None or ws.numel() < ws_n:
+        ws = torch.empty(ws_n, dtype=torch.uint8, device=q.device)
+    sc = float("nan") if scale is None else float(scale)
+    st = lib.sdpa_relpos_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _DTYPE[q.dtype], _DTYPE[odt],
+                             _LAYOUT[layout], B, H, gh, gw, D, _ptr(rel_pos_h), _ptr(rel_pos_w), sc,
+                             _ptr(lse), _ptr(ws), ws.numel(), _stream(stream))
+    _check(st, "sdpa_relpos_fwd")
+    return (o, lse) if return_lse else o
+
+
+def default_scale(D):
+    """[Axon PR 650], description: the scale defaults to 1/sqrt(head_dim)."""
+    return 1.0 / math.sqrt(D)

@@ -1,0 +1,264 @@
+// Host side of the C ABI declared in include/sdpa.h: argument validation,
+// workspace planning and kernel selection.  Validation happens before any
+// HIP call, so argument errors need no GPU and leave outputs untouched.
+#include "sdpa.h"
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+std::atomic<int64_t> g_num_splits{0};
+std::atomic<int64_t> g_relpos_fused{1};
+
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+bool dtype_ok(int d) { return d == SDPA_F32 || d == SDPA_BF16; }
+
+void set_strides(int layout, int64_t H, int64_t T, int64_t D, int64_t* sb, int64_t* sh, int64_t* st) {
+  if (layout == SDPA_BHSD) { *sb = H * T * D; *sh = T * D; *st = D; }
+  else { *sb = T * H * D; *sh = D; *st = H * D; }
+}
+
+// Split-KV chunk count: few query rows against a long key range leave most of
+// the GPU idle, so the key range is cut into chunks that run in parallel and
+// are merged by their log-sum-exp afterwards.
+int plan_splits(int64_t B, int64_t Hq, int64_t Tq, int64_t Tkv, int64_t D, int dtype) {
+  if (!sdpa::kSplitKvBuilt || dtype != SDPA_BF16 || D != 16) return 1;  // split-KV exists for the head_dim-16 kernel
+  const int64_t forced = g_num_splits.load();
+  if (forced >= 1) return (int)std::min<int64_t>(forced, std::max<int64_t>(1, (Tkv + 63) / 64));
+  const int64_t row_blocks = B * Hq * ((Tq + 31) / 32);
+  if (row_blocks >= 256 || Tkv < 512) return 1;
+  int64_t s = 512 / row_blocks;                          // aim at ~2 workgroups per CU
+  s = std::min<int64_t>(s, (Tkv + 127) / 128);           // keep >= 128 keys per chunk
+  return (int)std::max<int64_t>(1, std::min<int64_t>(s, 64));
+}
+
+size_t split_bytes(int splits, int64_t B, int64_t Hq, int64_t Tq, int64_t D) {
+  if (splits <= 1) return 0;
+  return align256((size_t)splits * B * Hq * Tq * D * 4) + align256((size_t)splits * B * Hq * Tq * 2 * 4);
+}
+
+size_t terms_bytes(int64_t B, int64_t H, int64_t T, int64_t gh, int64_t gw) {
+  return align256((size_t)B * H * T * gh * 4) + align256((size_t)B * H * T * gw * 4);
+}
+
+int check_sizes(int64_t B, int64_t Hq, int64_t Hkv, int64_t Tq, int64_t Tkv, int64_t D) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Tq <= 0 || Tkv <= 0 || D <= 0)
+    return fail(SDPA_ERR_INVALID, "all sizes must be positive (B=%lld Hq=%lld Hkv=%lld Tq=%lld Tkv=%lld D=%lld)",
+                (long long)B, (long long)Hq, (long long)Hkv, (long long)Tq, (long long)Tkv, (long long)D);
+  if (Hq % Hkv) return fail(SDPA_ERR_INVALID, "Hq (%lld) must be a multiple of Hkv (%lld)", (long long)Hq, (long long)Hkv);
+  if (Tq > INT32_MAX || Tkv > INT32_MAX || B > 65535 || Hq > 65535)
+    return fail(SDPA_ERR_UNSUPPORTED, "sizes beyond the launch grid limits");
+  return SDPA_OK;
+}
+
+int check_dtypes(int dtype, int out_dtype, int layout, int64_t D) {
+  if (!dtype_ok(dtype)) return fail(SDPA_ERR_INVALID, "unknown dtype %d", dtype);
+  if (!dtype_ok(out_dtype) || (out_dtype != dtype && out_dtype != SDPA_F32))
+    return fail(SDPA_ERR_INVALID, "out_dtype must equal dtype or be SDPA_F32");
+  if (layout != SDPA_BSHD && layout != SDPA_BHSD) return fail(SDPA_ERR_INVALID, "unknown layout %d", layout);
+  if (D > 128) return fail(SDPA_ERR_UNSUPPORTED, "head_dim %lld > 128 is not built", (long long)D);
+  if (dtype == SDPA_BF16 && D != 16 && D != 32 && D != 64 && D != 128)
+    return fail(SDPA_ERR_UNSUPPORTED, "bf16 head_dim must be 16, 32, 64 or 128 (got %lld)", (long long)D);
+  return SDPA_OK;
+}
+
+sdpa::FwdParams base_params(const void* q, const void* k, const void* v, void* o, int dtype, int out_dtype,
+                            int layout, int64_t B, int64_t Hq, int64_t Hkv, int64_t Tq, int64_t Tkv, int64_t D,
+                            float scale, float* lse) {
+  sdpa::FwdParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.q = q; p.k = k; p.v = v; p.o = o; p.lse = lse;
+  p.dtype = dtype; p.out_dtype = out_dtype;
+  p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.Tq = Tq; p.Tkv = Tkv; p.D = D;
+  set_strides(layout, Hq, Tq, D, &p.q_sb, &p.q_sh, &p.q_st);
+  set_strides(layout, Hkv, Tkv, D, &p.k_sb, &p.k_sh, &p.k_st);
+  p.scale = std::isnan(scale) ? (float)(1.0 / std::sqrt((double)D)) : scale;
+  p.bias = sdpa::BIAS_NONE;
+  p.num_splits = 1;
+  return p;
+}
+
+int launch(const sdpa::FwdParams& p, hipStream_t s) {
+  hipError_t e = sdpa::flash_mfma_supports(p) ? sdpa::launch_flash_mfma(p, s) : sdpa::launch_generic_fwd(p, s);
+  if (e != hipSuccess) return fail(SDPA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return SDPA_OK;
+}
+
+bool relpos_fused_ok(const sdpa::FwdParams& p) {
+  (void)p;
+  return false;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t sdpa_workspace_size(int64_t B, int64_t Hq, int64_t Hkv, int64_t Tq, int64_t Tkv, int64_t D, int relpos,
+                           int64_t grid_h, int64_t grid_w) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Tq <= 0 || Tkv <= 0 || D <= 0) return (size_t)-1;
+  if (relpos) {
+    if (grid_h <= 0 || grid_w <= 0 || grid_h * grid_w != Tq || Tq != Tkv) return (size_t)-1;
+    return terms_bytes(B, Hq, Tq, grid_h, grid_w);
+  }
+  return split_bytes(plan_splits(B, Hq, Tq, Tkv, D, SDPA_BF16), B, Hq, Tq, D);
+}
+
+int sdpa_fwd(const void* q, const void* k, const void* v, void* o, int dtype, int out_dtype, int layout,
+             int64_t B, int64_t Hq, int64_t Hkv, int64_t Tq, int64_t Tkv, int64_t D, float scale,
+             const sdpa_mask* mask, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  if (!q || !k || !v || !o) return fail(SDPA_ERR_INVALID, "q, k, v and o must be non-null");
+  int st = check_sizes(B, Hq, Hkv, Tq, Tkv, D);
+  if (st) return st;
+  st = check_dtypes(dtype, out_dtype, layout, D);
+  if (st) return st;
+  sdpa::FwdParams p = base_params(q, k, v, o, dtype, out_dtype, layout, B, Hq, Hkv, Tq, Tkv, D, scale, lse);
+  if (mask && mask->kind != SDPA_MASK_NONE) {
+    switch (mask->kind) {
+      case SDPA_MASK_CAUSAL:
+        p.bias = sdpa::BIAS_CAUSAL;
+        p.offset = mask->offset;
+        break;
+      case SDPA_MASK_SLIDING:
+        if (mask->window < 1) return fail(SDPA_ERR_INVALID, "sliding window must be >= 1 (got %lld)", (long long)mask->window);
+        p.bias = sdpa::BIAS_SLIDING;
+        p.offset = mask->offset;
+        p.window = mask->window;
+        break;
+      case SDPA_MASK_ADDITIVE:
+      case SDPA_MASK_BOOL:
+        if (!mask->data) return fail(SDPA_ERR_INVALID, "tensor mask needs a data pointer");
+        if (mask->kind == SDPA_MASK_ADDITIVE && !dtype_ok(mask->data_dtype))
+          return fail(SDPA_ERR_INVALID, "additive mask dtype must be SDPA_F32 or SDPA_BF16");
+        for (int a = 0; a < 4; ++a)
+          if (mask->stride[a] < 0) return fail(SDPA_ERR_INVALID, "mask strides must be >= 0");
+        p.bias = mask->kind == SDPA_MASK_ADDITIVE ? sdpa::BIAS_ADDITIVE : sdpa::BIAS_BOOL;
+        p.mdata = mask->data;
+        p.mdtype = mask->data_dtype;
+        for (int a = 0; a < 4; ++a) p.ms[a] = mask->stride[a];
+        break;
+      default:
+        return fail(SDPA_ERR_INVALID, "unknown mask kind %d", mask->kind);
+    }
+  }
+  p.num_splits = plan_splits(B, Hq, Tq, Tkv, D, dtype);
+  const size_t need = split_bytes(p.num_splits, B, Hq, Tq, D);
+  if (need) {
+    if (!workspace || workspace_bytes < need)
+      return fail(SDPA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : (size_t)0);
+    p.part_o = (float*)workspace;
+    p.part_ml = (float*)((char*)workspace + align256((size_t)p.num_splits * B * Hq * Tq * D * 4));
+  }
+  return launch(p, (hipStream_t)stream);
+}
+
+int relpos_terms(const void* q, int dtype, int layout, int64_t B, int64_t H, int64_t grid_h, int64_t grid_w,
+                 int64_t D, const void* rel_pos_h, const void* rel_pos_w, float* term_h, float* term_w,
+                 void* stream) {
+  g_last_error.clear();
+  if (!q || !rel_pos_h || !rel_pos_w || !term_h || !term_w)
+    return fail(SDPA_ERR_INVALID, "q, tables and term outputs must be non-null");
+  if (B <= 0 || H <= 0 || grid_h <= 0 || grid_w <= 0 || D <= 0) return fail(SDPA_ERR_INVALID, "all sizes must be positive");
+  if (!dtype_ok(dtype)) return fail(SDPA_ERR_INVALID, "unknown dtype %d", dtype);
+  if (layout != SDPA_BSHD && layout != SDPA_BHSD) return fail(SDPA_ERR_INVALID, "unknown layout %d", layout);
+  if (D > 128 || grid_h > 1024 || grid_w > 1024 || (D + 1) * grid_w * 4 > 65536)
+    return fail(SDPA_ERR_UNSUPPORTED, "grid %lldx%lld with head_dim %lld is not built", (long long)grid_h,
+                (long long)grid_w, (long long)D);
+  if (B > 65535 || H > 65535) return fail(SDPA_ERR_UNSUPPORTED, "sizes beyond the launch grid limits");
+  sdpa::TermsParams t;
+  t.q = q; t.dtype = dtype; t.B = B; t.H = H; t.T = grid_h * grid_w; t.D = D;
+  set_strides(layout, H, t.T, D, &t.q_sb, &t.q_sh, &t.q_st);
+  t.rel_h = rel_pos_h; t.rel_w = rel_pos_w;
+  t.grid_h = (int)grid_h; t.grid_w = (int)grid_w;
+  t.term_h = term_h; t.term_w = term_w;
+  hipError_t e = sdpa::launch_relpos_terms(t, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(SDPA_ERR_HIP, "relpos_terms launch failed: %s", hipGetErrorString(e));
+  return SDPA_OK;
+}
+
+int sdpa_relpos_fwd(const void* q, const void* k, const void* v, void* o, int dtype, int out_dtype, int layout,
+                    int64_t B, int64_t H, int64_t grid_h, int64_t grid_w, int64_t D, const void* rel_pos_h,
+                    const void* rel_pos_w, float scale, float* lse, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+  g_last_error.clear();
+  if (!q || !k || !v || !o || !rel_pos_h || !rel_pos_w)
+    return fail(SDPA_ERR_INVALID, "q, k, v, o and both tables must be non-null");
+  if (grid_h <= 0 || grid_w <= 0) return fail(SDPA_ERR_INVALID, "grid sizes must be positive");
+  const int64_t T = grid_h * grid_w;
+  int st = check_sizes(B, H, H, T, T, D);
+  if (st) return st;
+  st = check_dtypes(dtype, out_dtype, layout, D);
+  if (st) return st;
+  if (grid_h > 1024 || grid_w > 1024 || (D + 1) * grid_w * 4 > 65536)
+    return fail(SDPA_ERR_UNSUPPORTED, "grid %lldx%lld with head_dim %lld is not built", (long long)grid_h,
+                (long long)grid_w, (long long)D);
+  sdpa::FwdParams p = base_params(q, k, v, o, dtype, out_dtype, layout, B, H, H, T, T, D, scale, lse);
+  p.bias = sdpa::BIAS_RELPOS;
+  p.grid_h = (int)grid_h;
+  p.grid_w = (int)grid_w;
+  p.rel_h = rel_pos_h;
+  p.rel_w = rel_pos_w;
+  const size_t need = terms_bytes(B, H, T, grid_h, grid_w);
+  if (!workspace || workspace_bytes < need)
+    return fail(SDPA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : (size_t)0);
+  if (g_relpos_fused.load() && relpos_fused_ok(p)) return launch(p, (hipStream_t)stream);
+  float* th = (float*)workspace;
+  float* tw = (float*)((char*)workspace + align256((size_t)B * H * T * grid_h * 4));
+  st = relpos_terms(q, dtype, layout, B, H, grid_h, grid_w, D, rel_pos_h, rel_pos_w, th, tw, stream);
+  if (st) return st;
+  p.term_h = th;
+  p.term_w = tw;
+  return launch(p, (hipStream_t)stream);
+}
+
+const char* sdpa_status_string(int status) {
+  switch (status) {
+    case SDPA_OK: return "ok";
+    case SDPA_ERR_INVALID: return "invalid argument";
+    case SDPA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case SDPA_ERR_WORKSPACE: return "workspace too small";
+    case SDPA_ERR_HIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+const char* sdpa_last_error(void) { return g_last_error.c_str(); }
+
+int sdpa_set_tuning(const char* key, int64_t value) {
+  g_last_error.clear();
+  if (!key) return fail(SDPA_ERR_INVALID, "null key");
+  if (!std::strcmp(key, "num_splits")) {
+    if (value < 0 || value > 1024) return fail(SDPA_ERR_INVALID, "num_splits must be in [0, 1024]");
+    g_num_splits.store(value);
+    return SDPA_OK;
+  }
+  if (!std::strcmp(key, "relpos_fused")) {
+    if (value != 0 && value != 1) return fail(SDPA_ERR_INVALID, "relpos_fused must be 0 or 1");
+    g_relpos_fused.store(value);
+    return SDPA_OK;
+  }
+  return fail(SDPA_ERR_INVALID, "unknown tuning key '%s'", key);
+}
+
+}  // extern "C"

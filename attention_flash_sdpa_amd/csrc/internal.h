@@ -1,0 +1,67 @@
+// Internal interface between the host dispatcher (abi.cpp) and the HIP kernels.
+// Not part of the public ABI.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sdpa {
+
+enum BiasKind : int {
+  BIAS_NONE = 0,
+  BIAS_CAUSAL = 1,     // j <= i + offset
+  BIAS_SLIDING = 2,    // i + offset - window < j <= i + offset
+  BIAS_ADDITIVE = 3,   // + data[b,h,i,j] through strides
+  BIAS_BOOL = 4,       // data[b,h,i,j] != 0 attends
+  BIAS_RELPOS = 5      // + term_h[b,h,i,row(j)] + term_w[b,h,i,col(j)]
+};
+
+// Everything a forward kernel needs.  Strides are in elements.
+struct FwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;                 // [B, Hq, Tq] or nullptr
+  int dtype;                  // SDPA_F32 / SDPA_BF16
+  int out_dtype;
+  int64_t B, Hq, Hkv, Tq, Tkv, D;
+  int64_t q_sb, q_sh, q_st;   // q and o
+  int64_t k_sb, k_sh, k_st;   // k and v
+  float scale;
+  int bias;                   // BiasKind
+  int64_t offset, window;     // causal / sliding
+  const void* mdata;          // additive / bool data
+  int mdtype;                 // additive element type
+  int64_t ms[4];              // mask strides over [B, Hq, Tq, Tkv]
+  const float* term_h;        // rel-pos terms [B, Hq, Tq, grid_h] fp32
+  const float* term_w;        // [B, Hq, Tq, grid_w] fp32
+  const void* rel_h;          // rel-pos tables for kernels that form the terms themselves
+  const void* rel_w;
+  int grid_h, grid_w;
+  int num_splits;             // split-KV chunks (1 = no split)
+  float* part_o;              // split-KV partial outputs [splits, B, Hq, Tq, D] fp32
+  float* part_ml;             // split-KV partial (max, sum) [splits, B, Hq, Tq, 2] fp32
+};
+
+struct TermsParams {
+  const void* q;
+  int dtype;
+  int64_t B, H, T, D;
+  int64_t q_sb, q_sh, q_st;
+  const void* rel_h;
+  const void* rel_w;
+  int grid_h, grid_w;
+  float* term_h;
+  float* term_w;
+};
+
+// Split-KV (chunked key range + log-sum-exp merge) is available.
+constexpr bool kSplitKvBuilt = false;
+
+// Launchers: return hipSuccess or the launch error.  Each only enqueues work.
+hipError_t launch_generic_fwd(const FwdParams& p, hipStream_t s);
+hipError_t launch_relpos_terms(const TermsParams& p, hipStream_t s);
+hipError_t launch_flash_mfma(const FwdParams& p, hipStream_t s);   // bf16, D in {64, 128}
+bool flash_mfma_supports(const FwdParams& p);
+
+}  // namespace sdpa

@@ -1,0 +1,176 @@
+/*
+ * sdpa.h -- C ABI of the MI355X (gfx950) fused scaled-dot-product-attention library.
+ *
+ *   O = softmax(Q . K^T * scale + B) . V
+ *
+ * computed without ever writing the T_q x T_kv score matrix, where the
+ * additive bias B is one of
+ *   - none;
+ *   - a causal or sliding-window mask (optionally offset);
+ *   - a caller-supplied additive (float) or boolean tensor, broadcast over
+ *     [B, Hq, T_q, T_kv] through strides;
+ *   - SAM-style decomposed relative position:
+ *       B[i, j] = term_h[i, row(j)] + term_w[i, col(j)].
+ *
+ * Sources (the pages that define the operation):
+ *   [Axon PR 650] elixir-nx/axon "Axon.Layers.scaled_dot_product_attention/4",
+ *       description: softmax(Q . K^T * scale + mask) . V over rank-4 inputs;
+ *       bshd (default) or bhsd axes; scale defaults to 1/sqrt(head_dim);
+ *       masks causal, {causal, offset}, {sliding_window, w[, offset]} or a
+ *       runtime boolean/float tensor; grouped/multi-query attention by
+ *       repeating KV heads.  Review comment on the diff: the output comes
+ *       back in the caller's layout, and the contraction should use the
+ *       right axes instead of transposing the inputs.
+ *   [mlx-examples issue 1451] "segment_anything: fuse attention with
+ *       mx.fast.scaled_dot_product_attention", body: SAM's attention blocks,
+ *       the add_decomposed_rel_pos bias, and the additive mask broadcast to
+ *       [B, N, T_q, T_kv].
+ *   [Candle PR 3280] "feat(metal): SDPA with Relative Positional Embeddings
+ *       & LayerNorm Stability", Key Changes: a rel-pos attention kernel that
+ *       injects per-query term_h / term_w biases into the scores; SDPA for
+ *       head_dim 16.
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers owned by the caller.  The
+ *     library never allocates or frees device memory; scratch space comes in
+ *     through `workspace`.
+ *   - Dense tensors only.  Layout SDPA_BHSD stores [B, H, T, D] row-major;
+ *     SDPA_BSHD stores [B, T, H, D] row-major.  Q and O use Hq heads, K and V
+ *     use Hkv heads.  No input is transposed or copied.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Every call only
+ *     enqueues kernels on that stream and returns; it never synchronises.
+ *   - Status codes: SDPA_OK (0) or a negative sdpa_status.  Argument errors
+ *     are detected before any HIP call is made, so they leave every output
+ *     untouched and need no GPU.  sdpa_last_error() gives a thread-local
+ *     message for the most recent failing call on the calling thread.
+ *   - Calls are thread-safe and deterministic (no atomics in reductions; the
+ *     same inputs give bitwise-identical outputs on the same device).
+ */
+#ifndef SDPA_MI355X_H
+#define SDPA_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum sdpa_status {
+  SDPA_OK = 0,
+  SDPA_ERR_INVALID = -1,      /* null pointer, non-positive size, inconsistent shapes   */
+  SDPA_ERR_UNSUPPORTED = -2,  /* valid request this build does not implement             */
+  SDPA_ERR_WORKSPACE = -3,    /* workspace missing or smaller than sdpa_workspace_size() */
+  SDPA_ERR_HIP = -4           /* a kernel launch failed; see sdpa_last_error()           */
+} sdpa_status;
+
+typedef enum sdpa_dtype { SDPA_F32 = 0, SDPA_BF16 = 1 } sdpa_dtype;
+
+/* [Axon PR 650], description: `:axes` is :bshd (default) or :bhsd. */
+typedef enum sdpa_layout { SDPA_BSHD = 0, SDPA_BHSD = 1 } sdpa_layout;
+
+/* [Axon PR 650], description: the `:mask` option family;
+ * [mlx-examples issue 1451], body: an additive array broadcast to [B, N, T_q, T_kv]. */
+typedef enum sdpa_mask_kind {
+  SDPA_MASK_NONE = 0,
+  SDPA_MASK_CAUSAL = 1,    /* key j allowed for query i iff j <= i + offset                 */
+  SDPA_MASK_SLIDING = 2,   /* allowed iff i + offset - window < j <= i + offset (w keys)     */
+  SDPA_MASK_ADDITIVE = 3,  /* B[b,h,i,j] = data[...] (F32 or BF16), added to the scores      */
+  SDPA_MASK_BOOL = 4       /* uint8: nonzero = attend, zero = masked (-inf)                   */
+} sdpa_mask_kind;
+
+typedef struct sdpa_mask {
+  int32_t kind;            /* sdpa_mask_kind                                                  */
+  int32_t data_dtype;      /* ADDITIVE: SDPA_F32 or SDPA_BF16; ignored otherwise              */
+  int64_t offset;          /* CAUSAL / SLIDING diagonal offset (0 = top-left aligned)         */
+  int64_t window;          /* SLIDING: number of keys, >= 1                                   */
+  const void* data;        /* ADDITIVE / BOOL: device pointer; NULL otherwise                 */
+  int64_t stride[4];       /* ADDITIVE / BOOL: element strides over [B, Hq, T_q, T_kv];
+                              0 broadcasts that axis                                          */
+} sdpa_mask;
+
+/*
+ * Bytes of device workspace that sdpa_fwd (relpos = 0) or sdpa_relpos_fwd
+ * (relpos = 1; then Tq = Tkv = grid_h * grid_w and Hkv = Hq) needs for these
+ * sizes.  Pure host arithmetic: no HIP call.  Returns 0 when no workspace is
+ * needed and (size_t)-1 for invalid sizes.
+ */
+size_t sdpa_workspace_size(int64_t B, int64_t Hq, int64_t Hkv, int64_t Tq, int64_t Tkv,
+                           int64_t D, int relpos, int64_t grid_h, int64_t grid_w);
+
+/*
+ * Fused attention with an optional mask.  [Axon PR 650], description.
+ *   q [B, Hq, Tq, D] / [B, Tq, Hq, D], k and v [.., Hkv, Tkv, ..], o like q.
+ *   dtype      element type of q, k, v (SDPA_F32 or SDPA_BF16).
+ *   out_dtype  element type of o: dtype, or SDPA_F32 for unrounded output.
+ *   Hq % Hkv == 0; query head h reads KV head h / (Hq / Hkv).
+ *   D          head_dim: 16, 32, 64 or 128 (SDPA_BF16); 1..128 (SDPA_F32).
+ *   scale      multiplies Q.K^T; NaN selects 1/sqrt(D).
+ *   mask       NULL or &sdpa_mask{kind = NONE} for no mask.
+ *   lse        optional [B, Hq, Tq] fp32 log-sum-exp of each score row
+ *              (natural log; -inf for a row with no allowed key); NULL skips it.
+ *   Rows with no allowed key produce O = 0.
+ *   workspace  device scratch of at least sdpa_workspace_size(..., 0, 0, 0)
+ *              bytes (may be NULL when that size is 0).
+ */
+int sdpa_fwd(const void* q, const void* k, const void* v, void* o,
+             int dtype, int out_dtype, int layout,
+             int64_t B, int64_t Hq, int64_t Hkv, int64_t Tq, int64_t Tkv, int64_t D,
+             float scale, const sdpa_mask* mask, float* lse,
+             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Decomposed rel-pos terms of SAM's attention ([mlx-examples issue 1451],
+ * body: add_decomposed_rel_pos; [Candle PR 3280], Key Changes: term_h/term_w):
+ *   term_h[b,h,i,y] = sum_c q[b,h,i,c] * rel_pos_h[row(i) - y + grid_h - 1, c]
+ *   term_w[b,h,i,x] = sum_c q[b,h,i,c] * rel_pos_w[col(i) - x + grid_w - 1, c]
+ * with row(i) = i / grid_w, col(i) = i % grid_w and the UNSCALED query.
+ *   q          [B, H, T, D] or [B, T, H, D] with T = grid_h * grid_w, in dtype.
+ *   rel_pos_h  [2*grid_h - 1, D] in dtype; rel_pos_w [2*grid_w - 1, D].
+ *   term_h     [B, H, T, grid_h] fp32 output; term_w [B, H, T, grid_w] fp32.
+ *   Products accumulate in fp32.
+ */
+int relpos_terms(const void* q, int dtype, int layout,
+                 int64_t B, int64_t H, int64_t grid_h, int64_t grid_w, int64_t D,
+                 const void* rel_pos_h, const void* rel_pos_w,
+                 float* term_h, float* term_w, void* stream);
+
+/*
+ * Fused attention with the decomposed rel-pos bias, never materialising a
+ * T x T array ([Candle PR 3280], Key Changes: the bias is injected from the
+ * term rows; [mlx-examples issue 1451], body: SAM's image-encoder block).
+ *   Self-attention on a grid_h x grid_w token grid: Tq = Tkv = grid_h*grid_w,
+ *   Hq = Hkv = H.  Scores are scale * q.k + term_h[i,row(j)] + term_w[i,col(j)]
+ *   (the bias is not scaled).  Other arguments as in sdpa_fwd.
+ *   workspace  at least sdpa_workspace_size(B, H, H, T, T, D, 1, grid_h, grid_w).
+ */
+int sdpa_relpos_fwd(const void* q, const void* k, const void* v, void* o,
+                    int dtype, int out_dtype, int layout,
+                    int64_t B, int64_t H, int64_t grid_h, int64_t grid_w, int64_t D,
+                    const void* rel_pos_h, const void* rel_pos_w,
+                    float scale, float* lse,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static description of a status code. */
+const char* sdpa_status_string(int status);
+
+/* Thread-local detail of the last failing call on this thread ("" if none). */
+const char* sdpa_last_error(void);
+
+/*
+ * Process-wide tuning knobs (tests and benchmarks), each an int64:
+ *   "num_splits"   split-KV chunk count for sdpa_fwd; 0 = automatic (default),
+ *                  1 = never split, n > 1 = n chunks when the kernel supports it.
+ *   "relpos_fused" 1 (default) = sdpa_relpos_fwd forms the rel-pos terms
+ *                  inside the attention kernel where the grid allows it;
+ *                  0 = always run relpos_terms into the workspace first.
+ * Returns SDPA_OK, or SDPA_ERR_INVALID for an unknown key or bad value.
+ * The workspace size accounts for every setting.
+ */
+int sdpa_set_tuning(const char* key, int64_t value);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SDPA_MI355X_H */

@@ -1,0 +1,137 @@
+"""CPU-side checks of the C ABI: the library loads, exports every function
+include/sdpa.h declares, and rejects bad arguments before touching HIP."""
+import ctypes
+import math
+import os
+import re
+import subprocess
+
+import pytest
+
+import attention_flash_sdpa_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sdpa.h")
+FAKE = ctypes.c_void_p(0x1000)     # never dereferenced: every call below fails validation first
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^[A-Za-z_][\w \*]*?\b(\w+)\s*\(", src, flags=re.M)) - {"defined"})
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("sdpa_fwd", "sdpa_relpos_fwd", "relpos_terms", "sdpa_workspace_size",
+              "sdpa_status_string", "sdpa_last_error", "sdpa_set_tuning"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = fa.load()
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", fa.lib_path()], capture_output=True, text=True).stdout
+    exported = set(re.findall(r" T (\w+)$", out, flags=re.M))
+    assert set(declared_functions()) <= exported
+
+
+def test_header_compiles_as_plain_c(tmp_path):
+    src = tmp_path / "t.c"
+    src.write_text('#include "sdpa.h"\nint main(void){ sdpa_mask m; (void)m; return (int)sizeof(sdpa_mask) - 64; }\n')
+    r = subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"),
+                        str(src), "-o", str(tmp_path / "t")], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    assert subprocess.run([str(tmp_path / "t")]).returncode == 0      # struct is 64 bytes, as ctypes assumes
+    assert ctypes.sizeof(fa._Mask) == 64
+
+
+def call_fwd(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, dtype=1, out_dtype=1, layout=1, B=1, Hq=2, Hkv=2, Tq=8, Tkv=8,
+             D=64, scale=float("nan"), mask=None, lse=None, ws=None, wsn=0, stream=None)
+    a.update(kw)
+    lib = fa.load()
+    m = a["mask"]
+    return lib.sdpa_fwd(a["q"], a["k"], a["v"], a["o"], a["dtype"], a["out_dtype"], a["layout"], a["B"], a["Hq"],
+                        a["Hkv"], a["Tq"], a["Tkv"], a["D"], a["scale"], ctypes.byref(m) if m else None,
+                        a["lse"], a["ws"], a["wsn"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), -1), (dict(o=None), -1), (dict(B=0), -1), (dict(Tq=-3), -1), (dict(D=0), -1),
+    (dict(Hq=3, Hkv=2), -1), (dict(dtype=7), -1), (dict(out_dtype=7), -1), (dict(dtype=0, out_dtype=1), -1),
+    (dict(layout=5), -1), (dict(D=48), -2), (dict(D=256), -2), (dict(dtype=0, out_dtype=0, D=200), -2),
+])
+def test_fwd_rejects(kw, status):
+    assert call_fwd(**kw) == status
+    assert fa.load().sdpa_last_error().decode() != ""
+
+
+def test_fwd_rejects_bad_masks():
+    m = fa._Mask()
+    m.kind = 2
+    m.window = 0
+    assert call_fwd(mask=m) == -1 and b"window" in fa.load().sdpa_last_error()
+    m = fa._Mask()
+    m.kind = 3
+    assert call_fwd(mask=m) == -1                 # additive without data
+    m.data = 0x2000
+    m.data_dtype = 9
+    assert call_fwd(mask=m) == -1                 # bad additive dtype
+    m = fa._Mask()
+    m.kind = 4
+    m.data = 0x2000
+    m.stride[2] = -1
+    assert call_fwd(mask=m) == -1
+    m = fa._Mask()
+    m.kind = 42
+    assert call_fwd(mask=m) == -1
+
+
+def test_relpos_rejects():
+    lib = fa.load()
+    args = [FAKE, FAKE, FAKE, FAKE, 1, 1, 1, 1, 2, 8, 8, 64, FAKE, FAKE, float("nan"), None, None, 0, None]
+    assert lib.sdpa_relpos_fwd(*args) == -3          # no workspace
+    bad = list(args)
+    bad[12] = None
+    assert lib.sdpa_relpos_fwd(*bad) == -1           # missing table
+    bad = list(args)
+    bad[9] = 0
+    assert lib.sdpa_relpos_fwd(*bad) == -1           # empty grid
+    bad = list(args)
+    bad[11] = 48
+    assert lib.sdpa_relpos_fwd(*bad) == -2           # unsupported bf16 head_dim
+    assert lib.relpos_terms(None, 1, 1, 1, 2, 8, 8, 64, FAKE, FAKE, FAKE, FAKE, None) == -1
+    assert lib.relpos_terms(FAKE, 1, 1, 1, 2, 0, 8, 64, FAKE, FAKE, FAKE, FAKE, None) == -1
+    assert lib.relpos_terms(FAKE, 3, 1, 1, 2, 8, 8, 64, FAKE, FAKE, FAKE, FAKE, None) == -1
+
+
+def test_workspace_sizes():
+    lib = fa.load()
+    assert lib.sdpa_workspace_size(1, 12, 12, 4096, 4096, 64, 1, 64, 64) >= 1 * 12 * 4096 * 128 * 4
+    assert lib.sdpa_workspace_size(1, 12, 12, 4096, 4096, 64, 1, 63, 64) == ctypes.c_size_t(-1).value
+    assert lib.sdpa_workspace_size(0, 12, 12, 4096, 4096, 64, 0, 0, 0) == ctypes.c_size_t(-1).value
+    assert lib.sdpa_workspace_size(4, 32, 8, 4096, 4096, 128, 0, 0, 0) == 0
+
+
+def test_status_strings_and_tuning():
+    lib = fa.load()
+    assert lib.sdpa_status_string(0) == b"ok"
+    assert lib.sdpa_status_string(-3) == b"workspace too small"
+    assert lib.sdpa_set_tuning(b"nope", 1) == -1
+    assert lib.sdpa_set_tuning(b"num_splits", -1) == -1
+    assert lib.sdpa_set_tuning(b"num_splits", 0) == 0
+    assert lib.sdpa_set_tuning(b"relpos_fused", 2) == -1
+    assert lib.sdpa_set_tuning(b"relpos_fused", 1) == 0
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros(1, 1, 4, 16)
+    with pytest.raises(ValueError):
+        fa.sdpa(x, x, x)
+
+
+def test_default_scale():
+    assert fa.default_scale(64) == 0.125 and math.isclose(fa.default_scale(128), 128 ** -0.5)
