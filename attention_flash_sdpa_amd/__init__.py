@@ -25,7 +25,7 @@ import threading
 
 import torch
 
-__all__ = ["load", "lib_path", "sdpa", "sdpa_relpos", "relpos_terms", "workspace_size",
+__all__ = ["load", "lib_path", "sdpa", "sdpa_relpos", "relpos_terms", "workspace_size", "relpos_fused",
            "set_tuning", "SdpaError", "F32", "BF16", "BSHD", "BHSD"]
 
 F32, BF16 = 0, 1
@@ -82,6 +82,8 @@ def load():
         lib.sdpa_last_error.argtypes = []
         lib.sdpa_set_tuning.restype = _I32
         lib.sdpa_set_tuning.argtypes = [ctypes.c_char_p, _I64]
+        lib.sdpa_relpos_fused.restype = _I32
+        lib.sdpa_relpos_fused.argtypes = [_I32, _I64, _I64, _I64]
         _LIB = lib
         return lib
 
@@ -113,6 +115,11 @@ def _stream(stream):
 def set_tuning(key, value):
     """Process-wide knob: "num_splits" (0 = auto) or "relpos_fused" (0/1)."""
     _check(load().sdpa_set_tuning(key.encode(), int(value)), "sdpa_set_tuning")
+
+
+def relpos_fused(dtype, D, grid):
+    """True if sdpa_relpos runs as a single kernel that forms the terms itself."""
+    return bool(load().sdpa_relpos_fused(_DTYPE[dtype], D, grid[0], grid[1]))
 
 
 def workspace_size(B, Hq, Hkv, Tq, Tkv, D, relpos=False, grid=(0, 0)):

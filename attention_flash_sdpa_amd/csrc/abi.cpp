@@ -105,10 +105,7 @@ int launch(const sdpa::FwdParams& p, hipStream_t s) {
   return SDPA_OK;
 }
 
-bool relpos_fused_ok(const sdpa::FwdParams& p) {
-  (void)p;
-  return false;
-}
+bool relpos_fused_ok(const sdpa::FwdParams& p) { return sdpa::relpos_fused_supported(p); }
 
 }  // namespace
 
@@ -230,6 +227,16 @@ int sdpa_relpos_fwd(const void* q, const void* k, const void* v, void* o, int dt
   p.term_h = th;
   p.term_w = tw;
   return launch(p, (hipStream_t)stream);
+}
+
+int sdpa_relpos_fused(int dtype, int64_t D, int64_t grid_h, int64_t grid_w) {
+  sdpa::FwdParams p;
+  std::memset(&p, 0, sizeof(p));
+  static const char dummy = 0;
+  p.dtype = dtype; p.D = D; p.grid_h = (int)grid_h; p.grid_w = (int)grid_w;
+  p.Tq = p.Tkv = grid_h * grid_w;
+  p.rel_h = p.rel_w = &dummy;
+  return (g_relpos_fused.load() && grid_h > 0 && grid_w > 0 && relpos_fused_ok(p)) ? 1 : 0;
 }
 
 const char* sdpa_status_string(int status) {

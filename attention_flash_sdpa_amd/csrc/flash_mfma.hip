@@ -1,7 +1,471 @@
-// bf16 MFMA flash-attention kernels for gfx950 (placeholder until built).
+// Flash attention forward on gfx950 bf16 matrix cores (MFMA 32x32x16).
+//
+//   O = softmax(Q . K^T * scale + B) . V      ([Axon PR 650]
+//   "Axon.Layers.scaled_dot_product_attention/4", description)
+//
+// computed tile by tile with an online softmax, so no T_q x T_kv array is
+// written.  Bias kinds: none, causal / sliding-window (index masks, with
+// tile skipping), additive / boolean tensors (through broadcast strides), and
+// SAM's decomposed rel-pos bias rebuilt in registers from the per-query
+// term rows ([Candle PR 3280] "feat(metal): SDPA with Relative Positional
+// Embeddings & LayerNorm Stability", Key Changes; [mlx-examples issue 1451]
+// "segment_anything: fuse attention with mx.fast.scaled_dot_product_attention",
+// body).
+//
+// Work split.  A workgroup is 4 waves; each wave owns 32 query rows of one
+// head.  With grouped-query attention the waves of a workgroup are the query
+// heads that share one KV head (same 32 positions), so one K/V tile in LDS
+// feeds all of them and their mask patterns coincide.  Without sharing the
+// waves take 4 consecutive 32-row blocks of one head.
+//
+// Per 64-key tile and wave:
+//   S^T[key, q] = K . Q^T        2 key blocks x D/16 MFMAs; K from LDS
+//                                (ds_read_b128), Q^T held in registers.
+//                                The transposed orientation puts one query
+//                                per lane, so the row max and sum of the
+//                                softmax are in-lane plus one lane swap.
+//   x = S^T * scale * log2(e) + bias * log2(e)   (log2 domain, exp2 below)
+//   online softmax: the running max is only moved when a tile's max exceeds
+//                   it by more than 8 (log2 units); otherwise probabilities up
+//                   to 2^8 are accumulated against the old max, which is
+//                   exact after the final division and skips most rescales.
+//   O^T[d, q] += V^T . P^T       D/32 row blocks x 4 MFMAs; P^T comes straight
+//                                from the S^T registers (bf16), V^T from LDS
+//                                through the gfx950 transposing LDS read
+//                                (ds_read_b64_tr_b16) on the row-major V tile.
+//
+// Rel-pos with a 64-wide grid row (the key tile = one grid row): the
+// term_w[q, col] / scale values for the 64 key columns are the same for every
+// tile, so they initialise the S^T accumulators of the first MFMA of each key
+// block (zero VALU cost), and term_h[q, row] is one scalar per query per tile
+// folded into the exponent's offset.
+//
+// Fused rel-pos (64-wide grid rows, head_dim 64): the workgroup forms the
+// terms itself from its Q tile and the tables, so no term array exists:
+//   term_h for the wave's 32 queries (one grid row r) is one small GEMM
+//     TH^T[y, q] = sum_c rel_pos_h[r + grid_h - 1 - y, c] * Q[q, c]
+//   on the matrix cores, kept in LDS as [y][q] and read once per tile;
+//   term_w[q, x] = q . rel_pos_w[col(q) - x + 63] is the skewed diagonal of
+//     AW^T[m, q] = sum_c rel_pos_w[m, c] * Q[q, c]  (m = col - x + 63),
+//   formed by MFMA over the 96 table rows the wave can touch, then gathered
+//   along the skew through LDS into the accumulator-initialisation registers.
 #include "common.h"
 
 namespace sdpa {
-bool flash_mfma_supports(const FwdParams&) { return false; }
-hipError_t launch_flash_mfma(const FwdParams&, hipStream_t) { return hipErrorInvalidDeviceFunction; }
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) char lds_char;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kTau = 8.0f;      // lazy-rescale threshold (log2 units)
+
+enum Mode { M_NONE = 0, M_INDEX = 1, M_TENSOR = 2, M_RELPOS_ROW = 3, M_RELPOS_FUSED = 4 };
+
+template <int D>
+struct Cfg {
+  static constexpr int BN = 64;                   // keys per tile
+  static constexpr int PITCH = D * 2 + 16;        // LDS row pitch in bytes (16 B pad: conflict-free b128 reads)
+  static constexpr int TILE = BN * PITCH;         // bytes of one K or V tile
+  static constexpr int CH = D / 8;                // 16-byte chunks per row
+  static constexpr int LOADS = BN * CH / 256;     // 16-byte global loads per thread per tile (K or V)
+  static constexpr int QC = D / 16;               // MFMA k-chunks of Q.K^T
+  static constexpr int DB = D / 32;               // 32-row blocks of O^T
+};
+
+__device__ __forceinline__ bf16x8 lds_read_b128(const lds_char* p) {
+  return *(const __attribute__((address_space(3))) bf16x8*)p;
+}
+__device__ __forceinline__ s16x4 lds_read_tr(const lds_char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p);
+}
+__device__ __forceinline__ void lds_write_b128(lds_char* p, bf16x8 v) {
+  *(__attribute__((address_space(3))) bf16x8*)p = v;
+}
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Fused rel-pos prologue (head_dim 64, grid_w 64).  Forms term_w / scale for
+// the wave's 32 queries in the accumulator layout (cinit) and writes term_h^T
+// [y][q] into the wave's LDS slot after the K/V buffers.  Uses the K/V buffer
+// space as scratch, so it runs before the first tile is staged.
+template <int D>
+__device__ __forceinline__ void relpos_prologue(const FwdParams& p, lds_char* smem, const bf16x8* qf, int wave,
+                                                int lane, int64_t qw0, f32x16* cinit) {
+  using C = Cfg<D>;
+  const int g = lane >> 5, ql = lane & 31;
+  const int gh = p.grid_h;
+  const int64_t r = qw0 / 64;            // grid row of all 32 queries of this wave
+  const int c0 = (int)(qw0 % 64);        // column of the wave's first query (0 or 32)
+  const __bf16* rh = (const __bf16*)p.rel_h;
+  const __bf16* rw = (const __bf16*)p.rel_w;
+  // TH^T[y, q] for y = yb*32 + row: A rows are rel_pos_h[r + gh - 1 - y].
+  f32x16 th[2];
+#pragma unroll
+  for (int yb = 0; yb < 2; ++yb) {
+    th[yb] = (f32x16){};
+    const int y = yb * 32 + ql;
+    const int64_t tr = r + gh - 1 - y;
+#pragma unroll
+    for (int c = 0; c < C::QC; ++c) {
+      bf16x8 a = (bf16x8){};
+      if (y < gh) a = *(const bf16x8*)(rh + tr * D + c * 16 + 8 * g);
+      th[yb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[c], th[yb], 0, 0, 0);
+    }
+  }
+  // AW^T[m', q] = rel_pos_w[c0 + m'] . q for m' in [0, 96).
+  f32x16 aw[3];
+#pragma unroll
+  for (int mb = 0; mb < 3; ++mb) {
+    aw[mb] = (f32x16){};
+    const int m = c0 + mb * 32 + ql;
+#pragma unroll
+    for (int c = 0; c < C::QC; ++c) {
+      bf16x8 a = (bf16x8){};
+      if (m < 127) a = *(const bf16x8*)(rw + (int64_t)m * D + c * 16 + 8 * g);
+      aw[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[c], aw[mb], 0, 0, 0);
+    }
+  }
+  // Skewed gather through LDS: slot per wave [32 q][97] fp32 (odd pitch: conflict-free).
+  typedef __attribute__((address_space(3))) float lds_float;
+  lds_float* slot = (lds_float*)(smem + wave * (32 * 97 * 4));
+#pragma unroll
+  for (int mb = 0; mb < 3; ++mb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) slot[ql * 97 + mb * 32 + 8 * (i / 4) + 4 * g + (i % 4)] = aw[mb][i];
+  __syncthreads();
+  const float inv_scale = 1.0f / p.scale;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int x = kb * 32 + 8 * (i / 4) + 4 * g + (i % 4);
+      cinit[kb][i] = slot[ql * 97 + ql + 63 - x] * inv_scale;     // m' = col - x + 63 - c0 = ql + 63 - x
+    }
+  __syncthreads();
+  lds_float* ths = (lds_float*)(smem + 4 * C::TILE + wave * (64 * 32 * 4));
+#pragma unroll
+  for (int yb = 0; yb < 2; ++yb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) ths[(yb * 32 + 8 * (i / 4) + 4 * g + (i % 4)) * 32 + ql] = th[yb][i];
+}
+
+template <int D, int MODE, bool OUT_BF16>
+__global__ __launch_bounds__(256, 2) void flash_mfma_kernel(FwdParams p, int hpw) {
+  using C = Cfg<D>;
+  // K/V double buffer, then (fused rel-pos) per-wave term_h^T [64 y][32 q] fp32.
+  constexpr int TH_BYTES = (MODE == M_RELPOS_FUSED) ? 4 * 64 * 32 * 4 : 0;
+  __shared__ __attribute__((aligned(16))) char smem_raw[4 * C::TILE + TH_BYTES];
+  lds_char* smem = (lds_char*)smem_raw;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 5;            // lane half: selects rows of the MFMA layouts
+  const int ql = lane & 31;           // query column of this lane
+  const int nqb = 4 / hpw;            // 32-row query blocks per workgroup
+  const int64_t b = blockIdx.z;
+  const int64_t qtile = (MODE == M_INDEX) ? (int64_t)(gridDim.x - 1 - blockIdx.x) : (int64_t)blockIdx.x;
+  const int64_t h = (int64_t)blockIdx.y * hpw + (wave % hpw);
+  const int64_t hk = h / (p.Hq / p.Hkv);
+  const int64_t wg_q0 = qtile * 32 * nqb;
+  const int64_t wg_q1 = min(wg_q0 + 32 * nqb, p.Tq) - 1;
+  const int64_t wq0 = wg_q0 + 32 * (wave / hpw);
+  const int64_t wq1 = min(wq0 + 31, p.Tq - 1);
+  const int64_t qrow = wq0 + ql;
+  const bool qvalid = qrow < p.Tq;
+  const int64_t qsafe = qvalid ? qrow : 0;
+
+  const __bf16* qp = (const __bf16*)p.q + b * p.q_sb + h * p.q_sh;
+  const __bf16* kp = (const __bf16*)p.k + b * p.k_sb + hk * p.k_sh;
+  const __bf16* vp = (const __bf16*)p.v + b * p.k_sb + hk * p.k_sh;
+
+  // Q^T as the B operand: lane holds query ql, head dims c*16 + 8*g .. +7.
+  bf16x8 qf[C::QC];
+#pragma unroll
+  for (int c = 0; c < C::QC; ++c) {
+    if (qvalid) qf[c] = *(const bf16x8*)(qp + qrow * p.q_st + c * 16 + 8 * g);
+    else qf[c] = (bf16x8){};
+  }
+
+  // Key range of the workgroup.
+  int64_t lo = 0, hi = p.Tkv;
+  if (MODE == M_INDEX) {
+    hi = min(hi, wg_q1 + p.offset + 1);
+    if (p.bias == BIAS_SLIDING) lo = max((int64_t)0, wg_q0 + p.offset - p.window + 1);
+  }
+  const int64_t t0 = lo / C::BN;
+  const int ntiles = hi > lo ? (int)((hi - t0 * C::BN + C::BN - 1) / C::BN) : 0;
+
+  const float c2 = p.scale * kLog2e;
+
+  // Rel-pos (64-wide grid rows): term_w / scale initialises the score accumulators.
+  f32x16 cinit[2];
+  const float* thp = nullptr;
+  if (MODE == M_RELPOS_ROW) {
+    const float inv_scale = 1.0f / p.scale;
+    const float* twp = p.term_w + ((b * p.Hq + h) * p.Tq + qsafe) * 64;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const f32x4 t = *(const f32x4*)(twp + kb * 32 + 8 * i4 + 4 * g);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) cinit[kb][4 * i4 + e] = t[e] * inv_scale;
+      }
+    thp = p.term_h + ((b * p.Hq + h) * p.Tq + qsafe) * p.grid_h;
+  } else if (MODE == M_RELPOS_FUSED) {
+    relpos_prologue<D>(p, smem, qf, wave, lane, wq0, cinit);
+  } else {
+    cinit[0] = (f32x16){};
+    cinit[1] = (f32x16){};
+  }
+  const lds_char* th_lds = smem + 4 * C::TILE + wave * (64 * 32 * 4) + ql * 4;
+
+  f32x16 o[C::DB];
+#pragma unroll
+  for (int d = 0; d < C::DB; ++d) o[d] = (f32x16){};
+  float m = -INFINITY, l = 0.0f;
+
+  // Global -> register staging of one K/V tile, then register -> LDS.
+  bf16x8 kst[C::LOADS], vst[C::LOADS];
+  auto gload = [&](int64_t k0) {
+#pragma unroll
+    for (int r = 0; r < C::LOADS; ++r) {
+      const int cidx = tid + 256 * r;
+      const int row = cidx / C::CH, col = cidx % C::CH;
+      const int64_t key = k0 + row;
+      if (key < p.Tkv) {
+        kst[r] = *(const bf16x8*)(kp + key * p.k_st + col * 8);
+        vst[r] = *(const bf16x8*)(vp + key * p.k_st + col * 8);
+      } else {
+        kst[r] = (bf16x8){};
+        vst[r] = (bf16x8){};
+      }
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int r = 0; r < C::LOADS; ++r) {
+      const int cidx = tid + 256 * r;
+      const int row = cidx / C::CH, col = cidx % C::CH;
+      lds_write_b128(smem + (2 * buf) * C::TILE + row * C::PITCH + col * 16, kst[r]);
+      lds_write_b128(smem + (2 * buf + 1) * C::TILE + row * C::PITCH + col * 16, vst[r]);
+    }
+  };
+
+  if (ntiles > 0) {
+    gload(t0 * C::BN);
+    lstore(0);
+  }
+  __syncthreads();
+
+  float th_next = 0.0f;
+  if (MODE == M_RELPOS_ROW && ntiles > 0) th_next = thp[t0];
+  if (MODE == M_RELPOS_FUSED && ntiles > 0) th_next = *(const __attribute__((address_space(3))) float*)(th_lds + t0 * 128);
+
+  for (int it = 0; it < ntiles; ++it) {
+    const int64_t k0 = (t0 + it) * C::BN;
+    const int buf = it & 1;
+    if (it + 1 < ntiles) gload(k0 + C::BN);
+    float th_cur = th_next;
+    if (MODE == M_RELPOS_ROW && it + 1 < ntiles) th_next = thp[t0 + it + 1];
+    if (MODE == M_RELPOS_FUSED && it + 1 < ntiles)
+      th_next = *(const __attribute__((address_space(3))) float*)(th_lds + (t0 + it + 1) * 128);
+
+    // Tile class for this wave: skip (no allowed key), partial (per-element test) or full.
+    bool skip = false;
+    bool partial = (k0 + C::BN > p.Tkv);
+    if (MODE == M_INDEX) {
+      const int64_t klast = k0 + C::BN - 1;
+      if (k0 > wq1 + p.offset) skip = true;
+      if (klast > wq0 + p.offset) partial = true;
+      if (p.bias == BIAS_SLIDING) {
+        if (klast <= wq0 + p.offset - p.window) skip = true;
+        if (k0 <= wq1 + p.offset - p.window) partial = true;
+      }
+    }
+    if (MODE == M_TENSOR) partial = true;
+
+    if (!skip) {
+      const lds_char* ks = smem + (2 * buf) * C::TILE;
+      const lds_char* vs = ks + C::TILE;
+      f32x16 s[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        s[kb] = cinit[kb];
+#pragma unroll
+        for (int c = 0; c < C::QC; ++c) {
+          const bf16x8 a = lds_read_b128(ks + (kb * 32 + ql) * C::PITCH + (c * 16 + 8 * g) * 2);
+          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[c], s[kb], 0, 0, 0);
+        }
+      }
+      // Scores in log2 units, with bias and masks.
+      const float rowb = (MODE == M_RELPOS_ROW || MODE == M_RELPOS_FUSED) ? th_cur * kLog2e : 0.0f;
+      // Tensor masks: per-lane row base (64-bit) plus small 32-bit key deltas.
+      const char* mrow = nullptr;
+      int msz = 0;
+      if (MODE == M_TENSOR) {
+        msz = (p.bias == BIAS_BOOL) ? 1 : (p.mdtype == 0 ? 4 : 2);
+        mrow = (const char*)p.mdata + (b * p.ms[0] + h * p.ms[1] + qsafe * p.ms[2] + (k0 + 4 * g) * p.ms[3]) * msz;
+      }
+      const int mstep = (int)p.ms[3] * msz;
+      float x[2][16];
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float v = fmaf(s[kb][i], c2, rowb);
+          if (partial) {
+            const int64_t key = k0 + kb * 32 + 8 * (i / 4) + 4 * g + (i % 4);
+            bool ok = key < p.Tkv;
+            if (MODE == M_INDEX) ok = ok && index_allowed(p.bias, qrow, key, p.offset, p.window);
+            if (MODE == M_TENSOR) {
+              if (ok && qvalid) {
+                const char* mp = mrow + (kb * 32 + 8 * (i / 4) + (i % 4)) * mstep;
+                float mv;
+                if (msz == 1) mv = *(const uint8_t*)mp ? 0.0f : -INFINITY;
+                else if (msz == 4) mv = *(const float*)mp;
+                else mv = (float)*(const __bf16*)mp;
+                v += mv * kLog2e;
+              }
+            }
+            v = ok ? v : -INFINITY;
+          }
+          x[kb][i] = v;
+          tmax = fmaxf(tmax, v);
+        }
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+      const bool need = tmax > m + kTau;
+      if (__any(need)) {
+        const float mn = need ? tmax : m;
+        const float alpha = need ? ((m == -INFINITY) ? 0.0f : fast_exp2(m - mn)) : 1.0f;
+        m = mn;
+        l *= alpha;
+#pragma unroll
+        for (int d = 0; d < C::DB; ++d)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) o[d][i] *= alpha;
+      }
+      const float mref = (m == -INFINITY) ? 0.0f : m;
+      // P^T operands for the 4 PV MFMAs (16 keys each).
+      bf16x8 pb[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float pv = fast_exp2(x[t / 2][8 * (t % 2) + e] - mref);
+          l += pv;
+          pb[t][e] = (__bf16)pv;
+        }
+      // O^T += V^T . P^T with transposed LDS reads of the row-major V tile.
+      const int j = lane & 15;
+      const int dh = (lane >> 4) & 1;
+#pragma unroll
+      for (int d = 0; d < C::DB; ++d)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int col = d * 32 + 16 * dh + 4 * (j & 3);
+          const int row0 = 16 * t + 4 * g + (j >> 2);
+          const s16x4 lo4 = lds_read_tr(vs + row0 * C::PITCH + col * 2);
+          const s16x4 hi4 = lds_read_tr(vs + (row0 + 8) * C::PITCH + col * 2);
+          const s16x8 a8 = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+          o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a8), pb[t], o[d], 0, 0, 0);
+        }
+    }
+    if (it + 1 < ntiles) lstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  // Epilogue: the two lane halves hold disjoint keys of the same query.
+  const float lt = l + __shfl_xor(l, 32);
+  const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+  if (qvalid) {
+    const int64_t ob = b * p.q_sb + h * p.q_sh + qrow * p.q_st;
+#pragma unroll
+    for (int d = 0; d < C::DB; ++d)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int dd = d * 32 + 8 * i4 + 4 * g;
+        if (OUT_BF16) {
+          __bf16* op = (__bf16*)p.o + ob + dd;
+          typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+          bf16x4 v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = (__bf16)(o[d][4 * i4 + e] * inv);
+          *(bf16x4*)op = v;
+        } else {
+          float* op = (float*)p.o + ob + dd;
+          f32x4 v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = o[d][4 * i4 + e] * inv;
+          *(f32x4*)op = v;
+        }
+      }
+    if (p.lse && g == 0) p.lse[(b * p.Hq + h) * p.Tq + qrow] = lt > 0.0f ? (m + __log2f(lt)) * kLn2 : -INFINITY;
+  }
+}
+
+int mode_of(const FwdParams& p) {
+  switch (p.bias) {
+    case BIAS_NONE: return M_NONE;
+    case BIAS_CAUSAL:
+    case BIAS_SLIDING: return M_INDEX;
+    case BIAS_ADDITIVE:
+    case BIAS_BOOL: return M_TENSOR;
+    case BIAS_RELPOS: return p.term_h ? M_RELPOS_ROW : M_RELPOS_FUSED;
+    default: return -1;
+  }
+}
+
+template <int D, int MODE>
+hipError_t launch_mode(const FwdParams& p, hipStream_t s) {
+  const int64_t grp = p.Hq / p.Hkv;
+  const int hpw = (grp % 4 == 0) ? 4 : (grp % 2 == 0) ? 2 : 1;
+  const int64_t rows = 32 * (4 / hpw);
+  dim3 grid((unsigned)((p.Tq + rows - 1) / rows), (unsigned)(p.Hq / hpw), (unsigned)p.B);
+  if (p.out_dtype == 1) hipLaunchKernelGGL((flash_mfma_kernel<D, MODE, true>), grid, dim3(256), 0, s, p, hpw);
+  else hipLaunchKernelGGL((flash_mfma_kernel<D, MODE, false>), grid, dim3(256), 0, s, p, hpw);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_d(const FwdParams& p, hipStream_t s) {
+  switch (mode_of(p)) {
+    case M_NONE: return launch_mode<D, M_NONE>(p, s);
+    case M_INDEX: return launch_mode<D, M_INDEX>(p, s);
+    case M_TENSOR: return launch_mode<D, M_TENSOR>(p, s);
+    case M_RELPOS_ROW: return launch_mode<D, M_RELPOS_ROW>(p, s);
+    case M_RELPOS_FUSED: return D == 64 ? launch_mode<64, M_RELPOS_FUSED>(p, s) : hipErrorInvalidValue;
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+bool relpos_fused_supported(const FwdParams& p) {
+  return p.dtype == 1 && p.D == 64 && p.grid_w == 64 && p.grid_h >= 1 && p.grid_h <= 64 && p.rel_h && p.rel_w &&
+         p.Tq == (int64_t)p.grid_h * 64 && p.Tkv == p.Tq;
+}
+
+bool flash_mfma_supports(const FwdParams& p) {
+  if (p.dtype != 1 || (p.D != 64 && p.D != 128) || p.num_splits != 1) return false;
+  if (mode_of(p) < 0) return false;
+  if (p.bias == BIAS_RELPOS) {
+    if (p.D != 64 || p.grid_w != 64) return false;
+    if (!p.term_h && !relpos_fused_supported(p)) return false;
+  }
+  // Tensor masks index keys with 32-bit deltas inside a tile.
+  if ((p.bias == BIAS_ADDITIVE || p.bias == BIAS_BOOL) && p.ms[3] * 4 * 64 > INT32_MAX) return false;
+  return true;
+}
+
+hipError_t launch_flash_mfma(const FwdParams& p, hipStream_t s) {
+  return p.D == 64 ? launch_d<64>(p, s) : launch_d<128>(p, s);
+}
+
 }  // namespace sdpa

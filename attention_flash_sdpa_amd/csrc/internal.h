@@ -63,5 +63,7 @@ hipError_t launch_generic_fwd(const FwdParams& p, hipStream_t s);
 hipError_t launch_relpos_terms(const TermsParams& p, hipStream_t s);
 hipError_t launch_flash_mfma(const FwdParams& p, hipStream_t s);   // bf16, D in {64, 128}
 bool flash_mfma_supports(const FwdParams& p);
+// Rel-pos terms can be formed inside the MFMA kernel (no term arrays needed).
+bool relpos_fused_supported(const FwdParams& p);
 
 }  // namespace sdpa

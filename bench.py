@@ -1,0 +1,208 @@
+"""Benchmark: attention TFLOP/s (and % of MI355X dense bf16 MFMA peak) of the
+fused rel-pos SDPA on SAM ViT-B's 64x64 global attention (B1, 12 heads,
+T 4096, head_dim 64, bf16), one sdpa_relpos_fwd call per step.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
+
+Prints ONE JSON line.  A step is one full pass of the fused path (rel-pos
+terms + flash attention, all on the GPU) over the seeded synthetic inputs,
+which are resident in HBM before timing starts.  `roofline` describes the
+dominant kernel (the flash attention kernel); `cpu_baseline` times the fp64
+CPU oracle on a bounded sample of the same workload on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+HBM_PEAK_GBS = 8000.0               # MI355X HBM3E, published
+
+
+def allowed_pairs(wl):
+    """Number of (query, key) pairs the mask allows, per (batch, head)."""
+    Tq, Tkv = wl.Tq, wl.Tkv
+    if wl.mask is None:
+        return Tq * Tkv
+    d = wl.mask.get("offset", 0)
+    tot = 0
+    for i in range(Tq):
+        hi = min(Tkv - 1, i + d)
+        lo = 0 if wl.mask["kind"] == "causal" else max(0, i + d - wl.mask["window"] + 1)
+        tot += max(0, hi - lo + 1)
+    return tot
+
+
+def flop_model(wl):
+    """Algorithmic FLOPs: 4*D per allowed pair (Q.K^T and P.V), plus for rel-pos
+    2*D per term entry (B*H*T*(grid_h+grid_w) dot products) and 2 adds per score."""
+    pairs = allowed_pairs(wl) * wl.B * wl.Hq
+    attn = 4 * wl.D * pairs
+    bias = 0
+    if wl.relpos:
+        gh, gw = wl.grid
+        bias = 2 * wl.B * wl.Hq * wl.Tq * (gh + gw) * wl.D + 2 * pairs
+    return attn, bias
+
+
+def byte_model(wl):
+    """Algorithmic HBM bytes of one call: read Q, K, V once, write O once."""
+    es = 4 if wl.dtype == "fp32" else 2
+    return es * wl.D * (2 * wl.B * wl.Hq * wl.Tq + 2 * wl.B * wl.Hkv * wl.Tkv)
+
+
+def run_call(fa, wl, g, out):
+    if wl.relpos:
+        return fa.sdpa_relpos(g["q"], g["k"], g["v"], g["rel_pos_h"], g["rel_pos_w"], wl.grid, layout=wl.layout,
+                              scale=wl.scale, out=out, workspace=g.get("ws"))
+    return fa.sdpa(g["q"], g["k"], g["v"], layout=wl.layout, scale=wl.scale, mask=wl.mask, out=out)
+
+
+def time_gpu(fa, wl, g, steps, warmup):
+    import torch
+    out = torch.empty_like(g["q"])
+    for _ in range(warmup):
+        run_call(fa, wl, g, out)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        run_call(fa, wl, g, out)
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps
+
+
+def kernel_events(fa, wl, g, steps):
+    """Average duration of the whole call and of the separate rel-pos terms
+    launch, from HIP events recorded on the stream the kernels run on."""
+    import torch
+    out = torch.empty_like(g["q"])
+    s = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record(s)
+    for _ in range(steps):
+        run_call(fa, wl, g, out)
+    ev[1].record(s)
+    ev[1].synchronize()
+    call_ms = ev[0].elapsed_time(ev[1]) / steps
+    terms_ms = 0.0
+    if wl.relpos and not fa.relpos_fused(g["q"].dtype, wl.D, wl.grid):
+        ev[0].record(s)
+        for _ in range(steps):
+            fa.relpos_terms(g["q"], g["rel_pos_h"], g["rel_pos_w"], wl.grid, layout=wl.layout)
+        ev[1].record(s)
+        ev[1].synchronize()
+        terms_ms = ev[0].elapsed_time(ev[1]) / steps
+    return call_ms, terms_ms
+
+
+def cpu_baseline(wl, x, budget_s=20.0):
+    """Time the fp64 oracle on whole (batch, head) slices of the same inputs until
+    about `budget_s` seconds of CPU work are done; report it at the metric's unit."""
+    import numpy as np
+    import oracle
+    from threadpoolctl import threadpool_info
+    f64 = lambda t: t.to("cpu").double().numpy()
+    q, k, v = f64(x["q"]), f64(x["k"]), f64(x["v"])
+    kw = {"layout": wl.layout, "scale": wl.scale, "mask": wl.mask}
+    if wl.relpos:
+        kw["rel_pos"] = {"rel_pos_h": f64(x["rel_pos_h"]), "rel_pos_w": f64(x["rel_pos_w"]), "grid": wl.grid}
+    hsel = lambda a, h, grp=1: (a[:, h // grp:h // grp + 1] if wl.layout == "bhsd" else a[:, :, h // grp:h // grp + 1])
+    grp = wl.Hq // wl.Hkv
+    done, t_total = 0, 0.0
+    for h in range(wl.B * 0 + wl.Hq):
+        t0 = time.perf_counter()
+        oracle.sdpa(hsel(q, h), hsel(k, h, grp), hsel(v, h, grp), **kw)
+        t_total += time.perf_counter() - t0
+        done += 1
+        if t_total >= budget_s:
+            break
+    sub = wl.with_(Hq=done, Hkv=max(1, done // grp))
+    attn, bias = flop_model(sub)
+    frac = done / wl.Hq
+    info = threadpool_info()
+    threads = max([i.get("num_threads", 1) for i in info] or [1])
+    return {"value": round((attn + bias) * (wl.B if False else 1) / t_total / 1e12, 6), "unit": "TFLOP/s",
+            "cores": threads, "kind": "oracle",
+            "sample": f"{done} of {wl.Hq} heads (batch 0; {frac:.3f} of the workload), fp64 numpy, "
+                      f"{t_total:.1f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="sam_global_relpos")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the path would shard by (batch, head) with no exchange, but no multi-GPU run exists.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import attention_flash_sdpa_amd as fa
+    import workloads
+
+    fa.load()
+    if os.environ.get("SDPA_BENCH_UNFUSED", "0") == "1":
+        fa.set_tuning("relpos_fused", 0)
+    wl = workloads.WORKLOADS[args.workload]
+    x = workloads.generate(wl, seed=0)
+    g = {k: t.cuda() for k, t in x.items()}
+    if wl.relpos:
+        n = fa.workspace_size(wl.B, wl.Hq, wl.Hkv, wl.Tq, wl.Tkv, wl.D, True, wl.grid)
+        g["ws"] = torch.empty(n, dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+
+    sec = time_gpu(fa, wl, g, args.steps, args.warmup)
+    attn, bias = flop_model(wl)
+    total = attn + bias
+    tflops = total / sec / 1e12
+    call_ms, terms_ms = kernel_events(fa, wl, g, args.steps)
+    flash_ms = call_ms - terms_ms
+    flash_flops = attn + (2 * allowed_pairs(wl) * wl.B * wl.Hq if wl.relpos else 0)
+    if wl.relpos and terms_ms == 0.0:
+        flash_flops = total             # terms formed inside the flash kernel: one launch per call
+    achieved = flash_flops / (flash_ms * 1e-3) / 1e12
+    line = {
+        "metric": "attention TFLOP/s + % bf16 MFMA peak, SAM ViT-B 64x64 global rel-pos SDPA",
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "pct_of_bf16_peak": round(100.0 * tflops / MFMA_BF16_PEAK_TFLOPS, 2),
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(sec * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "description": wl.description, "layout": wl.layout, "B": wl.B,
+                   "Hq": wl.Hq, "Hkv": wl.Hkv, "Tq": wl.Tq, "Tkv": wl.Tkv, "head_dim": wl.D,
+                   "grid": list(wl.grid) if wl.grid else None, "mask": wl.mask, "scale": wl.scale,
+                   "flop_per_step": total, "attn_flop": attn, "bias_flop": bias},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel": "flash_mfma_kernel", "kernel_ms": round(flash_ms, 5),
+                     "terms_kernel_ms": round(terms_ms, 5), "flop_per_launch": flash_flops,
+                     "algorithmic_bytes_per_launch": byte_model(wl)},
+    }
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(wl, x, args.cpu_budget)
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

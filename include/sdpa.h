@@ -151,6 +151,13 @@ int sdpa_relpos_fwd(const void* q, const void* k, const void* v, void* o,
                     float scale, float* lse,
                     void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * 1 if sdpa_relpos_fwd with these parameters forms the rel-pos terms inside
+ * the attention kernel (a single kernel launch, no term arrays), 0 if it
+ * first runs relpos_terms into the workspace.  Pure host logic, no HIP call.
+ */
+int sdpa_relpos_fused(int dtype, int64_t D, int64_t grid_h, int64_t grid_w);
+
 /* Static description of a status code. */
 const char* sdpa_status_string(int status);
 

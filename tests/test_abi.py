@@ -124,6 +124,12 @@ def test_status_strings_and_tuning():
     assert lib.sdpa_set_tuning(b"num_splits", 0) == 0
     assert lib.sdpa_set_tuning(b"relpos_fused", 2) == -1
     assert lib.sdpa_set_tuning(b"relpos_fused", 1) == 0
+    assert lib.sdpa_relpos_fused(1, 64, 64, 64) == 1      # SAM ViT-B global grid: one kernel
+    assert lib.sdpa_relpos_fused(1, 64, 14, 14) == 0      # windowed grid: terms kernel first
+    assert lib.sdpa_relpos_fused(0, 64, 64, 64) == 0
+    assert lib.sdpa_set_tuning(b"relpos_fused", 0) == 0
+    assert lib.sdpa_relpos_fused(1, 64, 64, 64) == 0
+    assert lib.sdpa_set_tuning(b"relpos_fused", 1) == 0
 
 
 def test_binding_refuses_cpu_tensors():

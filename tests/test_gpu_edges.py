@@ -1,0 +1,180 @@
+"""GPU edge cases and invariants: ragged sizes, every mask kind with
+broadcast strides and offsets, fully masked rows, GQA ratios, non-default
+scale, head_dims, both output dtypes, determinism, and the equivalences the
+pages state (rel-pos bias == the same bias passed as an additive mask)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from parity_util import TOL, max_err, np64
+
+pytestmark = pytest.mark.gpu
+
+
+def rnd(shape, dtype, seed):
+    g = torch.Generator().manual_seed(seed)
+    return torch.randn(shape, generator=g, dtype=torch.float32).to(dtype)
+
+
+def layout_shape(B, H, T, D, layout):
+    return (B, H, T, D) if layout == "bhsd" else (B, T, H, D)
+
+
+def check(fa, B, Hq, Hkv, Tq, Tkv, D, *, dtype=torch.bfloat16, layout="bhsd", mask=None, scale=None, seed=0,
+          omask=None):
+    q = rnd(layout_shape(B, Hq, Tq, D, layout), dtype, seed)
+    k = rnd(layout_shape(B, Hkv, Tkv, D, layout), dtype, seed + 1)
+    v = rnd(layout_shape(B, Hkv, Tkv, D, layout), dtype, seed + 2)
+    gm = None
+    if mask is not None and "data" in mask:
+        gm = dict(mask, data=mask["data"].cuda())
+    elif mask is not None:
+        gm = mask
+    o, lse = fa.sdpa(q.cuda(), k.cuda(), v.cuda(), layout=layout, scale=scale, mask=gm, out_dtype=torch.float32,
+                     return_lse=True)
+    torch.cuda.synchronize()
+    om = omask if omask is not None else mask
+    if om is not None and "data" in om:
+        om = dict(om, data=np64(om["data"]) if om["data"].dtype != torch.bool else om["data"].numpy())
+    ref = oracle.sdpa(np64(q), np64(k), np64(v), layout=layout, scale=scale, mask=om)
+    tol = TOL["fp32" if dtype == torch.float32 else "bf16"]
+    err = max_err(np64(o), ref["o"])
+    assert err <= tol, f"max-abs {err:.3e}"
+    rl, gl = ref["lse"], np64(lse)
+    assert np.array_equal(np.isneginf(rl), np.isneginf(gl))
+    fin = np.isfinite(rl)
+    assert max_err(gl[fin], rl[fin]) <= tol
+    return o
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("Tq,Tkv", [(1, 1), (1, 200), (77, 1), (33, 65), (130, 257), (256, 64)])
+def test_ragged_sizes(gpu, D, Tq, Tkv):
+    check(gpu, 2, 2, 2, Tq, Tkv, D, seed=Tq * 7 + Tkv)
+
+
+@pytest.mark.parametrize("ratio", [1, 2, 4, 8])
+@pytest.mark.parametrize("layout", ["bhsd", "bshd"])
+def test_gqa_ratios(gpu, ratio, layout):
+    check(gpu, 2, 8, 8 // ratio, 97, 150, 64, layout=layout, seed=ratio)
+
+
+@pytest.mark.parametrize("offset", [0, 5, -7, -200])
+@pytest.mark.parametrize("D", [64, 128])
+def test_causal_offsets(gpu, offset, D):
+    check(gpu, 1, 4, 1, 150, 190, D, mask={"kind": "causal", "offset": offset}, seed=3)
+
+
+@pytest.mark.parametrize("w,offset", [(1, 0), (7, 0), (64, 3), (100, -5), (1000, 0)])
+def test_sliding(gpu, w, offset):
+    check(gpu, 1, 4, 2, 260, 260, 128, layout="bshd", mask={"kind": "sliding", "window": w, "offset": offset}, seed=4)
+
+
+@pytest.mark.parametrize("mshape", [(2, 4, 70, 130), (1, 1, 70, 130), (2, 1, 1, 130), (1, 4, 70, 1)])
+@pytest.mark.parametrize("mdt", [torch.float32, torch.bfloat16])
+def test_additive_mask_broadcast(gpu, mshape, mdt):
+    m = rnd(mshape, mdt, 9)
+    check(gpu, 2, 4, 2, 70, 130, 64, mask={"kind": "additive", "data": m}, seed=5)
+
+
+def test_bool_mask_with_dead_rows(gpu):
+    g = torch.Generator().manual_seed(11)
+    m = torch.rand((2, 4, 70, 130), generator=g) < 0.3
+    m[0, 1, 5] = False          # a fully masked row: output 0, lse -inf
+    check(gpu, 2, 4, 4, 70, 130, 128, mask={"kind": "bool", "data": m}, seed=6)
+
+
+def test_non_default_scale_and_fp32(gpu):
+    check(gpu, 1, 2, 2, 100, 90, 64, scale=0.37, seed=7)
+    check(gpu, 1, 2, 1, 100, 90, 40, dtype=torch.float32, scale=0.2, seed=8)
+    check(gpu, 1, 2, 2, 50, 90, 16, scale=0.9, seed=9)
+    check(gpu, 1, 2, 2, 50, 90, 32, seed=10, mask={"kind": "causal", "offset": 40})
+
+
+def test_bf16_output_rounding(gpu):
+    q, k, v = (rnd((1, 2, 96, 64), torch.bfloat16, s).cuda() for s in (1, 2, 3))
+    o32 = gpu.sdpa(q, k, v, out_dtype=torch.float32)
+    o16 = gpu.sdpa(q, k, v)
+    assert o16.dtype == torch.bfloat16
+    assert torch.equal(o16, o32.to(torch.bfloat16))
+
+
+def test_deterministic(gpu):
+    wl = workloads.replica("gqa_causal")
+    x = {k_: t.cuda() for k_, t in workloads.generate(wl, seed=1).items()}
+    a = gpu.sdpa(x["q"], x["k"], x["v"], layout=wl.layout, mask=wl.mask)
+    b = gpu.sdpa(x["q"], x["k"], x["v"], layout=wl.layout, mask=wl.mask)
+    assert torch.equal(a, b)
+
+
+def test_gqa_equals_repeated_kv(gpu):
+    q, k, v = (rnd(s, torch.bfloat16, i).cuda() for i, s in enumerate([(1, 8, 70, 64), (1, 2, 90, 64), (1, 2, 90, 64)]))
+    a = gpu.sdpa(q, k, v, out_dtype=torch.float32)
+    b = gpu.sdpa(q, k.repeat_interleave(4, dim=1).contiguous(), v.repeat_interleave(4, dim=1).contiguous(),
+                 out_dtype=torch.float32)
+    assert max_err(np64(a), np64(b)) <= 1e-6
+
+
+def test_relpos_equals_additive_route(gpu):
+    """The rel-pos bias injected from term rows matches the same bias passed as
+    an additive [B, H, T, T] mask (mlx-examples issue 1451, body)."""
+    wl = workloads.replica("sam_global_relpos")
+    x = {k_: t.cuda() for k_, t in workloads.generate(wl, seed=2).items()}
+    o1 = gpu.sdpa_relpos(x["q"], x["k"], x["v"], x["rel_pos_h"], x["rel_pos_w"], wl.grid, scale=wl.scale,
+                         out_dtype=torch.float32)
+    th, tw = gpu.relpos_terms(x["q"], x["rel_pos_h"], x["rel_pos_w"], wl.grid)
+    gh, gw = wl.grid
+    j = torch.arange(gh * gw, device="cuda")
+    bias = (th[..., j // gw] + tw[..., j % gw]).contiguous()
+    o2 = gpu.sdpa(x["q"], x["k"], x["v"], scale=wl.scale, mask={"kind": "additive", "data": bias},
+                  out_dtype=torch.float32)
+    # Both routes round P to bf16; the bias enters the fp32 scores at different
+    # points (accumulator initialisation vs an added mask), which can flip the
+    # rounding of single P entries (2^-9 relative), so agreement is ~1e-4.
+    assert max_err(np64(o1), np64(o2)) <= 1e-3
+
+
+def test_windowed_equals_independent_windows(gpu):
+    wl = workloads.WORKLOADS["sam_window_relpos"]
+    x = {k_: t.cuda() for k_, t in workloads.generate(wl, seed=0).items()}
+    o = gpu.sdpa_relpos(x["q"], x["k"], x["v"], x["rel_pos_h"], x["rel_pos_w"], wl.grid, scale=wl.scale,
+                        out_dtype=torch.float32)
+    for wdx in (0, 7, 24):
+        s = slice(wdx, wdx + 1)
+        o1 = gpu.sdpa_relpos(x["q"][s].contiguous(), x["k"][s].contiguous(), x["v"][s].contiguous(),
+                             x["rel_pos_h"], x["rel_pos_w"], wl.grid, scale=wl.scale, out_dtype=torch.float32)
+        assert torch.equal(o1, o[s])
+    # the last window is mostly zero padding: a padded query (q = 0) has zero
+    # scores and zero rel-pos terms, so its output is the mean of the window's V
+    last = x["v"][24].float().mean(dim=1)      # [H, D]
+    assert max_err(np64(o[24, :, 195]), np64(last)) <= 1e-3
+
+
+def test_first_causal_row_is_v0(gpu):
+    wl = workloads.WORKLOADS["gqa_causal"]
+    x = {k_: t.cuda() for k_, t in workloads.generate(wl.with_(B=1), seed=0).items()}
+    o = gpu.sdpa(x["q"], x["k"], x["v"], layout="bshd", mask=wl.mask, out_dtype=torch.float32)
+    v0 = x["v"][:, 0].float().repeat_interleave(4, dim=1)   # [B, Hq, D]
+    assert max_err(np64(o[:, 0]), np64(v0)) <= 1e-6
+
+
+@pytest.mark.parametrize("name", ["sam_global_relpos", "sam_window_relpos"])
+def test_relpos_fused_equals_unfused(gpu, name):
+    """The single-kernel rel-pos path (terms formed in the attention kernel) and
+    the two-kernel path (relpos_terms into the workspace) agree."""
+    wl = workloads.replica(name)
+    x = {k_: t.cuda() for k_, t in workloads.generate(wl, seed=4).items()}
+    args = (x["q"], x["k"], x["v"], x["rel_pos_h"], x["rel_pos_w"], wl.grid)
+    a = gpu.sdpa_relpos(*args, scale=wl.scale, out_dtype=torch.float32)
+    gpu.set_tuning("relpos_fused", 0)
+    try:
+        b = gpu.sdpa_relpos(*args, scale=wl.scale, out_dtype=torch.float32)
+    finally:
+        gpu.set_tuning("relpos_fused", 1)
+    assert max_err(np64(a), np64(b)) <= 1e-3
+    ref = oracle.sdpa(np64(x["q"].cpu()), np64(x["k"].cpu()), np64(x["v"].cpu()), scale=wl.scale,
+                      rel_pos={"rel_pos_h": np64(x["rel_pos_h"].cpu()), "rel_pos_w": np64(x["rel_pos_w"].cpu()),
+                               "grid": wl.grid})
+    assert max_err(np64(b), ref["o"]) <= TOL["bf16"]
