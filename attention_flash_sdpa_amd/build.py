@@ -31,10 +31,16 @@ def hipcc():
     return exe
 
 
+# Per-file extra flags.  The MFMA attention kernels take row maxima of scores
+# produced by the matrix cores; without NaN honouring the maxima need no
+# quieting moves (NaN scores still reach the output through exp and P.V).
+EXTRA = {"flash_mfma.hip": ["-fno-honor-nans"]}
+
+
 def _compile(src):
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
     lang = ["-x", "hip", f"--offload-arch={ARCH}"] if src.endswith(".hip") else []
-    cmd = [hipcc()] + COMMON + lang + ["-c", src, "-o", obj]
+    cmd = [hipcc()] + COMMON + EXTRA.get(os.path.basename(src), []) + lang + ["-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     out = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if "packed-fp32-ops" not in l)
     if r.returncode != 0:

@@ -43,7 +43,8 @@ void set_strides(int layout, int64_t H, int64_t T, int64_t D, int64_t* sb, int64
 // the GPU idle, so the key range is cut into chunks that run in parallel and
 // are merged by their log-sum-exp afterwards.
 int plan_splits(int64_t B, int64_t Hq, int64_t Tq, int64_t Tkv, int64_t D, int dtype) {
-  if (!sdpa::kSplitKvBuilt || dtype != SDPA_BF16 || D != 16) return 1;  // split-KV exists for the head_dim-16 kernel
+  // split-KV exists for the head_dim-16 query-packed kernel (few queries)
+  if (!sdpa::kSplitKvBuilt || dtype != SDPA_BF16 || D != 16 || Tq > 8) return 1;
   const int64_t forced = g_num_splits.load();
   if (forced >= 1) return (int)std::min<int64_t>(forced, std::max<int64_t>(1, (Tkv + 63) / 64));
   const int64_t row_blocks = B * Hq * ((Tq + 31) / 32);
@@ -100,7 +101,10 @@ sdpa::FwdParams base_params(const void* q, const void* k, const void* v, void* o
 }
 
 int launch(const sdpa::FwdParams& p, hipStream_t s) {
-  hipError_t e = sdpa::flash_mfma_supports(p) ? sdpa::launch_flash_mfma(p, s) : sdpa::launch_generic_fwd(p, s);
+  hipError_t e;
+  if (sdpa::d16_supports(p)) e = sdpa::launch_d16(p, s);
+  else if (sdpa::flash_mfma_supports(p)) e = sdpa::launch_flash_mfma(p, s);
+  else e = sdpa::launch_generic_fwd(p, s);
   if (e != hipSuccess) return fail(SDPA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return SDPA_OK;
 }

@@ -70,12 +70,19 @@ enum Mode { M_NONE = 0, M_INDEX = 1, M_TENSOR = 2, M_RELPOS_ROW = 3, M_RELPOS_FU
 template <int D>
 struct Cfg {
   static constexpr int BN = 64;                   // keys per tile
-  static constexpr int PITCH = D * 2 + 16;        // LDS row pitch in bytes (16 B pad: conflict-free b128 reads)
+  static constexpr int PITCH = D * 2;             // LDS row pitch in bytes (rows unpadded; chunks XOR-swizzled)
   static constexpr int TILE = BN * PITCH;         // bytes of one K or V tile
   static constexpr int CH = D / 8;                // 16-byte chunks per row
   static constexpr int LOADS = BN * CH / 256;     // 16-byte global loads per thread per tile (K or V)
   static constexpr int QC = D / 16;               // MFMA k-chunks of Q.K^T
   static constexpr int DB = D / 32;               // 32-row blocks of O^T
+  static constexpr int RPB = 256 / (2 * D);       // rows per 256-byte bank sweep (64 banks x 4 B)
+  // 16-byte chunk c of K row r lives at chunk position c ^ kswz(r): the 16 rows
+  // read by 16 lanes at one chunk index land in 16 distinct bank groups.
+  static __device__ __forceinline__ int kswz(int r) { return (r / RPB) & (CH - 1); }
+  // V rows are read 4 at a time, 64 contiguous bytes each (transposing reads):
+  // flipping whole 64-byte groups per row keeps the 4 rows in distinct banks.
+  static __device__ __forceinline__ int vswz(int r) { return ((r / RPB) % (4 / RPB)) << 2; }
 };
 
 __device__ __forceinline__ bf16x8 lds_read_b128(const lds_char* p) {
@@ -88,6 +95,20 @@ __device__ __forceinline__ void lds_write_b128(lds_char* p, bf16x8 v) {
   *(__attribute__((address_space(3))) bf16x8*)p = v;
 }
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float max3f(float a, float b, float c) { return fmaxf(a, fmaxf(b, c)); }
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+__device__ constexpr bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
+// Max / sum of the value held by lane l and lane l ^ 32 (v_permlane32_swap).
+__device__ __forceinline__ float halves_max(float v) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  const float a = __uint_as_float(r[0]), b = __uint_as_float(r[1]);
+  return a > b ? a : b;
+}
+__device__ __forceinline__ float halves_sum(float v) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 // Fused rel-pos prologue (head_dim 64, grid_w 64).  Forms term_w / scale for
 // the wave's 32 queries in the accumulator layout (cinit) and writes term_h^T
@@ -157,6 +178,9 @@ __device__ __forceinline__ void relpos_prologue(const FwdParams& p, lds_char* sm
 template <int D, int MODE, bool OUT_BF16>
 __global__ __launch_bounds__(256, 2) void flash_mfma_kernel(FwdParams p, int hpw) {
   using C = Cfg<D>;
+  // Software pipelining (next tile's scores in flight during this tile's
+  // softmax) needs a second score tile in registers: affordable at head_dim 64.
+  constexpr bool PIPE = false;
   // K/V double buffer, then (fused rel-pos) per-wave term_h^T [64 y][32 q] fp32.
   constexpr int TH_BYTES = (MODE == M_RELPOS_FUSED) ? 4 * 64 * 32 * 4 : 0;
   __shared__ __attribute__((aligned(16))) char smem_raw[4 * C::TILE + TH_BYTES];
@@ -167,9 +191,17 @@ __global__ __launch_bounds__(256, 2) void flash_mfma_kernel(FwdParams p, int hpw
   const int g = lane >> 5;            // lane half: selects rows of the MFMA layouts
   const int ql = lane & 31;           // query column of this lane
   const int nqb = 4 / hpw;            // 32-row query blocks per workgroup
-  const int64_t b = blockIdx.z;
-  const int64_t qtile = (MODE == M_INDEX) ? (int64_t)(gridDim.x - 1 - blockIdx.x) : (int64_t)blockIdx.x;
-  const int64_t h = (int64_t)blockIdx.y * hpw + (wave % hpw);
+  // Workgroups are dealt to the 8 XCDs round-robin by linear id; renumber them
+  // so that each XCD gets a contiguous range of (batch, head, query tile) and
+  // keeps its heads' K/V resident in its own L2.
+  const int64_t nblk = (int64_t)gridDim.x * gridDim.y * gridDim.z;
+  const int64_t lin = blockIdx.x + (int64_t)gridDim.x * (blockIdx.y + (int64_t)gridDim.y * blockIdx.z);
+  const int64_t per = nblk / 8, rem = nblk % 8, xcd = lin % 8;
+  const int64_t lid = xcd * per + min(xcd, rem) + lin / 8;
+  const int64_t bx = lid % gridDim.x, by = (lid / gridDim.x) % gridDim.y, bz = lid / ((int64_t)gridDim.x * gridDim.y);
+  const int64_t b = bz;
+  const int64_t qtile = (MODE == M_INDEX) ? (int64_t)(gridDim.x - 1 - bx) : bx;
+  const int64_t h = by * hpw + (wave % hpw);
   const int64_t hk = h / (p.Hq / p.Hkv);
   const int64_t wg_q0 = qtile * 32 * nqb;
   const int64_t wg_q1 = min(wg_q0 + 32 * nqb, p.Tq) - 1;
@@ -230,118 +262,166 @@ __global__ __launch_bounds__(256, 2) void flash_mfma_kernel(FwdParams p, int hpw
   for (int d = 0; d < C::DB; ++d) o[d] = (f32x16){};
   float m = -INFINITY, l = 0.0f;
 
-  // Global -> register staging of one K/V tile, then register -> LDS.
+  // LDS rings: K tiles run one tile ahead of V tiles.  Iteration `it` reads
+  // K_{it+1} (scores of the next tile, issued to the matrix cores before the
+  // softmax of this tile so the two overlap) and V_it (P.V of this tile); it
+  // stages K_{it+2} and V_{it+1} from HBM into the buffers freed by the
+  // previous iteration.
+  auto kbuf = [&](int i) -> lds_char* { return smem + (i & 1) * C::TILE; };
+  auto vbuf = [&](int i) -> lds_char* { return smem + (2 + (i & 1)) * C::TILE; };
   bf16x8 kst[C::LOADS], vst[C::LOADS];
-  auto gload = [&](int64_t k0) {
+  auto gload = [&](const __bf16* src, int64_t k0, bf16x8* dst) {
+    if (k0 + C::BN <= p.Tkv) {          // whole tile in range: no per-load predicate
 #pragma unroll
-    for (int r = 0; r < C::LOADS; ++r) {
-      const int cidx = tid + 256 * r;
-      const int row = cidx / C::CH, col = cidx % C::CH;
-      const int64_t key = k0 + row;
-      if (key < p.Tkv) {
-        kst[r] = *(const bf16x8*)(kp + key * p.k_st + col * 8);
-        vst[r] = *(const bf16x8*)(vp + key * p.k_st + col * 8);
-      } else {
-        kst[r] = (bf16x8){};
-        vst[r] = (bf16x8){};
+      for (int r = 0; r < C::LOADS; ++r) {
+        const int cidx = tid + 256 * r;
+        const int row = cidx / C::CH, col = cidx % C::CH;
+        dst[r] = *(const bf16x8*)(src + (k0 + row) * p.k_st + col * 8);
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < C::LOADS; ++r) {
+        const int cidx = tid + 256 * r;
+        const int row = cidx / C::CH, col = cidx % C::CH;
+        const int64_t key = k0 + row;
+        dst[r] = (key < p.Tkv) ? *(const bf16x8*)(src + key * p.k_st + col * 8) : (bf16x8){};
       }
     }
   };
-  auto lstore = [&](int buf) {
+  auto lstore = [&](lds_char* dstbuf, const bf16x8* src, bool is_v) {
 #pragma unroll
     for (int r = 0; r < C::LOADS; ++r) {
       const int cidx = tid + 256 * r;
       const int row = cidx / C::CH, col = cidx % C::CH;
-      lds_write_b128(smem + (2 * buf) * C::TILE + row * C::PITCH + col * 16, kst[r]);
-      lds_write_b128(smem + (2 * buf + 1) * C::TILE + row * C::PITCH + col * 16, vst[r]);
+      const int pos = col ^ (is_v ? C::vswz(row) : C::kswz(row));
+      lds_write_b128(dstbuf + row * C::PITCH + pos * 16, src[r]);
     }
+  };
+  // Tile classes for this wave: skip (no allowed key) / partial (per-element test) / full.
+  auto tile_skip = [&](int64_t k0) -> bool {
+    if (MODE != M_INDEX) return false;
+    const int64_t klast = k0 + C::BN - 1;
+    if (k0 > wq1 + p.offset) return true;
+    if (p.bias == BIAS_SLIDING && klast <= wq0 + p.offset - p.window) return true;
+    return false;
+  };
+  auto tile_partial = [&](int64_t k0) -> bool {
+    bool part = (k0 + C::BN > p.Tkv) || (MODE == M_TENSOR);
+    if (MODE == M_INDEX) {
+      if (k0 + C::BN - 1 > wq0 + p.offset) part = true;
+      if (p.bias == BIAS_SLIDING && k0 <= wq1 + p.offset - p.window) part = true;
+    }
+    return part;
+  };
+  // S^T = K . Q^T (+ rel-pos accumulator initialisation) for the tile in `ks`.
+  auto qk = [&](const lds_char* ks, f32x16* sc) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) sc[kb] = cinit[kb];
+#pragma unroll
+    for (int c = 0; c < C::QC; ++c)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const int row = kb * 32 + ql;
+        const bf16x8 a = lds_read_b128(ks + row * C::PITCH + ((2 * c + g) ^ C::kswz(row)) * 16);
+        sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[c], sc[kb], 0, 0, 0);
+      }
   };
 
   if (ntiles > 0) {
-    gload(t0 * C::BN);
-    lstore(0);
+    gload(kp, t0 * C::BN, kst);
+    gload(vp, t0 * C::BN, vst);
+    lstore(kbuf(0), kst, false);
+    lstore(vbuf(0), vst, true);
+    if (PIPE && ntiles > 1) {
+      gload(kp, (t0 + 1) * C::BN, kst);
+      lstore(kbuf(1), kst, false);
+    }
   }
   __syncthreads();
 
-  float th_next = 0.0f;
-  if (MODE == M_RELPOS_ROW && ntiles > 0) th_next = thp[t0];
-  if (MODE == M_RELPOS_FUSED && ntiles > 0) th_next = *(const __attribute__((address_space(3))) float*)(th_lds + t0 * 128);
+  // Allowed key interval of this lane's query: lim_lo < key <= lim_hi (int32).
+  int lim_hi = (int)(p.Tkv - 1), lim_lo = -1;
+  if (MODE == M_INDEX) {
+    const int64_t hi64 = min(qrow + p.offset, p.Tkv - 1);
+    lim_hi = (int)max(hi64, (int64_t)-2);
+    if (p.bias == BIAS_SLIDING) lim_lo = (int)min(max(qrow + p.offset - p.window, (int64_t)-1), p.Tkv);
+  }
+  auto th_of = [&](int64_t tile) -> float {
+    if (MODE == M_RELPOS_ROW) return thp[tile];
+    if (MODE == M_RELPOS_FUSED) return *(const __attribute__((address_space(3))) float*)(th_lds + tile * 128);
+    return 0.0f;
+  };
+
+  f32x16 s[2];
+  s[0] = (f32x16){};
+  s[1] = (f32x16){};
+  if (PIPE && ntiles > 0 && !tile_skip(t0 * C::BN)) qk(kbuf(0), s);
 
   for (int it = 0; it < ntiles; ++it) {
     const int64_t k0 = (t0 + it) * C::BN;
-    const int buf = it & 1;
-    if (it + 1 < ntiles) gload(k0 + C::BN);
-    float th_cur = th_next;
-    if (MODE == M_RELPOS_ROW && it + 1 < ntiles) th_next = thp[t0 + it + 1];
-    if (MODE == M_RELPOS_FUSED && it + 1 < ntiles)
-      th_next = *(const __attribute__((address_space(3))) float*)(th_lds + (t0 + it + 1) * 128);
-
-    // Tile class for this wave: skip (no allowed key), partial (per-element test) or full.
-    bool skip = false;
-    bool partial = (k0 + C::BN > p.Tkv);
-    if (MODE == M_INDEX) {
-      const int64_t klast = k0 + C::BN - 1;
-      if (k0 > wq1 + p.offset) skip = true;
-      if (klast > wq0 + p.offset) partial = true;
-      if (p.bias == BIAS_SLIDING) {
-        if (klast <= wq0 + p.offset - p.window) skip = true;
-        if (k0 <= wq1 + p.offset - p.window) partial = true;
-      }
+    const bool stage_k = it + (PIPE ? 2 : 1) < ntiles, stage_v = it + 1 < ntiles;
+    if (stage_k) gload(kp, k0 + (PIPE ? 2 : 1) * C::BN, kst);
+    if (stage_v) gload(vp, k0 + C::BN, vst);
+    const float th_cur = th_of(t0 + it);
+    const bool skip = tile_skip(k0);
+    const bool partial = tile_partial(k0);
+    // Scores of the next tile go to the matrix cores first.
+    f32x16 sn[2];
+    sn[0] = (f32x16){};
+    sn[1] = (f32x16){};
+    if (PIPE) {
+      if (it + 1 < ntiles && !tile_skip(k0 + C::BN)) qk(kbuf(it + 1), sn);
+    } else if (!skip) {
+      qk(kbuf(it), s);
     }
-    if (MODE == M_TENSOR) partial = true;
 
     if (!skip) {
-      const lds_char* ks = smem + (2 * buf) * C::TILE;
-      const lds_char* vs = ks + C::TILE;
-      f32x16 s[2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        s[kb] = cinit[kb];
-#pragma unroll
-        for (int c = 0; c < C::QC; ++c) {
-          const bf16x8 a = lds_read_b128(ks + (kb * 32 + ql) * C::PITCH + (c * 16 + 8 * g) * 2);
-          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[c], s[kb], 0, 0, 0);
-        }
-      }
-      // Scores in log2 units, with bias and masks.
-      const float rowb = (MODE == M_RELPOS_ROW || MODE == M_RELPOS_FUSED) ? th_cur * kLog2e : 0.0f;
-      // Tensor masks: per-lane row base (64-bit) plus small 32-bit key deltas.
-      const char* mrow = nullptr;
-      int msz = 0;
+      const lds_char* vs = vbuf(it);
+      // Masks and tensor biases act on the raw scores (bias / scale), so every
+      // mode shares one exponent: p = exp2(s * scale * log2e + (rowb - m)).
       if (MODE == M_TENSOR) {
-        msz = (p.bias == BIAS_BOOL) ? 1 : (p.mdtype == 0 ? 4 : 2);
-        mrow = (const char*)p.mdata + (b * p.ms[0] + h * p.ms[1] + qsafe * p.ms[2] + (k0 + 4 * g) * p.ms[3]) * msz;
+        const float inv_scale = 1.0f / p.scale;
+        const int msz = (p.bias == BIAS_BOOL) ? 1 : (p.mdtype == 0 ? 4 : 2);
+        const int mstep = (int)p.ms[3] * msz;
+        const char* mrow = (const char*)p.mdata +
+                           (b * p.ms[0] + h * p.ms[1] + qsafe * p.ms[2] + (k0 + 4 * g) * p.ms[3]) * msz;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int kofs = kb * 32 + 8 * (i / 4) + (i % 4);
+            if (qvalid && k0 + 4 * g + kofs < p.Tkv) {
+              const char* mp = mrow + kofs * mstep;
+              float mv;
+              if (msz == 1) mv = *(const uint8_t*)mp ? 0.0f : -INFINITY;
+              else if (msz == 4) mv = *(const float*)mp;
+              else mv = (float)*(const __bf16*)mp;
+              s[kb][i] = fmaf(mv, inv_scale, s[kb][i]);
+            }
+          }
       }
-      const int mstep = (int)p.ms[3] * msz;
-      float x[2][16];
-      float tmax = -INFINITY;
+      if (partial) {
+        asm volatile("" ::: "memory");   // keep this a real branch: full tiles skip the mask work
+        const int kl0 = (int)(k0 + 4 * g);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int key = kl0 + kb * 32 + 8 * (i / 4) + (i % 4);
+            const bool ok = (key <= lim_hi) & (key > lim_lo);
+            s[kb][i] = ok ? s[kb][i] : -INFINITY;
+          }
+      }
+      const float rowb = (MODE == M_RELPOS_ROW || MODE == M_RELPOS_FUSED) ? th_cur * kLog2e : 0.0f;
+      float smax = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float v = fmaf(s[kb][i], c2, rowb);
-          if (partial) {
-            const int64_t key = k0 + kb * 32 + 8 * (i / 4) + 4 * g + (i % 4);
-            bool ok = key < p.Tkv;
-            if (MODE == M_INDEX) ok = ok && index_allowed(p.bias, qrow, key, p.offset, p.window);
-            if (MODE == M_TENSOR) {
-              if (ok && qvalid) {
-                const char* mp = mrow + (kb * 32 + 8 * (i / 4) + (i % 4)) * mstep;
-                float mv;
-                if (msz == 1) mv = *(const uint8_t*)mp ? 0.0f : -INFINITY;
-                else if (msz == 4) mv = *(const float*)mp;
-                else mv = (float)*(const __bf16*)mp;
-                v += mv * kLog2e;
-              }
-            }
-            v = ok ? v : -INFINITY;
-          }
-          x[kb][i] = v;
-          tmax = fmaxf(tmax, v);
-        }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+        for (int i = 0; i < 16; i += 2) smax = max3f(smax, s[kb][i], s[kb][i + 1]);
+      smax = halves_max(smax);
+      const float tmax = fmaf(smax, c2, rowb);        // -inf stays -inf (c2 > 0)
       const bool need = tmax > m + kTau;
-      if (__any(need)) {
+      if (__builtin_expect(__any(need), 0)) {
         const float mn = need ? tmax : m;
         const float alpha = need ? ((m == -INFINITY) ? 0.0f : fast_exp2(m - mn)) : 1.0f;
         m = mn;
@@ -351,17 +431,23 @@ __global__ __launch_bounds__(256, 2) void flash_mfma_kernel(FwdParams p, int hpw
 #pragma unroll
           for (int i = 0; i < 16; ++i) o[d][i] *= alpha;
       }
-      const float mref = (m == -INFINITY) ? 0.0f : m;
-      // P^T operands for the 4 PV MFMAs (16 keys each).
+      const float off = rowb - ((m == -INFINITY) ? 0.0f : m);
+      // P^T operands for the 4 PV MFMAs (16 keys each); the row sum adds the
+      // bf16-rounded probabilities that the MFMA consumes (dot2 with ones).
       bf16x8 pb[4];
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
+      for (int t = 0; t < 4; ++t) {
+        bf16x2 pk[4];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float pv = fast_exp2(x[t / 2][8 * (t % 2) + e] - mref);
-          l += pv;
-          pb[t][e] = (__bf16)pv;
+        for (int e = 0; e < 8; e += 2) {
+          const f32x2 pp = {fast_exp2(fmaf(s[t / 2][8 * (t % 2) + e], c2, off)),
+                            fast_exp2(fmaf(s[t / 2][8 * (t % 2) + e + 1], c2, off))};
+          pk[e / 2] = __builtin_convertvector(pp, bf16x2);
+          l = __builtin_amdgcn_fdot2_f32_bf16(pk[e / 2], kOnes2, l, false);
         }
+        pb[t] = __builtin_shufflevector(__builtin_shufflevector(pk[0], pk[1], 0, 1, 2, 3),
+                                        __builtin_shufflevector(pk[2], pk[3], 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
+      }
       // O^T += V^T . P^T with transposed LDS reads of the row-major V tile.
       const int j = lane & 15;
       const int dh = (lane >> 4) & 1;
@@ -371,18 +457,27 @@ __global__ __launch_bounds__(256, 2) void flash_mfma_kernel(FwdParams p, int hpw
         for (int t = 0; t < 4; ++t) {
           const int col = d * 32 + 16 * dh + 4 * (j & 3);
           const int row0 = 16 * t + 4 * g + (j >> 2);
-          const s16x4 lo4 = lds_read_tr(vs + row0 * C::PITCH + col * 2);
-          const s16x4 hi4 = lds_read_tr(vs + (row0 + 8) * C::PITCH + col * 2);
+          // byte offset col*2 = 16 * chunk + 8 * ((j & 3) & 1); rows row0 and row0 + 8
+          // have the same swizzle (the swizzle depends on row / RPB modulo 4 / RPB).
+          const int chunk = (col * 2) >> 4, within = (col * 2) & 15;
+          const int off = ((chunk ^ C::vswz(row0)) << 4) + within;
+          const s16x4 lo4 = lds_read_tr(vs + row0 * C::PITCH + off);
+          const s16x4 hi4 = lds_read_tr(vs + (row0 + 8) * C::PITCH + off);
           const s16x8 a8 = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
           o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a8), pb[t], o[d], 0, 0, 0);
         }
     }
-    if (it + 1 < ntiles) lstore(buf ^ 1);
+    if (stage_k) lstore(kbuf(PIPE ? it : it + 1), kst, false);
+    if (stage_v) lstore(vbuf(it + 1), vst, true);
     __syncthreads();
+    if (PIPE) {
+      s[0] = sn[0];
+      s[1] = sn[1];
+    }
   }
 
   // Epilogue: the two lane halves hold disjoint keys of the same query.
-  const float lt = l + __shfl_xor(l, 32);
+  const float lt = halves_sum(l);
   const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
   if (qvalid) {
     const int64_t ob = b * p.q_sb + h * p.q_sh + qrow * p.q_st;

@@ -56,13 +56,15 @@ struct TermsParams {
 };
 
 // Split-KV (chunked key range + log-sum-exp merge) is available.
-constexpr bool kSplitKvBuilt = false;
+constexpr bool kSplitKvBuilt = true;
 
 // Launchers: return hipSuccess or the launch error.  Each only enqueues work.
 hipError_t launch_generic_fwd(const FwdParams& p, hipStream_t s);
 hipError_t launch_relpos_terms(const TermsParams& p, hipStream_t s);
 hipError_t launch_flash_mfma(const FwdParams& p, hipStream_t s);   // bf16, D in {64, 128}
 bool flash_mfma_supports(const FwdParams& p);
+hipError_t launch_d16(const FwdParams& p, hipStream_t s);            // bf16, D = 16, head-packed (+ split-KV)
+bool d16_supports(const FwdParams& p);
 // Rel-pos terms can be formed inside the MFMA kernel (no term arrays needed).
 bool relpos_fused_supported(const FwdParams& p);
 
