@@ -19,6 +19,7 @@ namespace {
 thread_local std::string g_last_error;
 std::atomic<int64_t> g_num_splits{0};
 std::atomic<int64_t> g_relpos_fused{1};
+std::atomic<int64_t> g_split64{1};
 
 int fail(int status, const char* fmt, ...) {
   char buf[512];
@@ -103,6 +104,7 @@ sdpa::FwdParams base_params(const void* q, const void* k, const void* v, void* o
 int launch(const sdpa::FwdParams& p, hipStream_t s) {
   hipError_t e;
   if (sdpa::d16_supports(p)) e = sdpa::launch_d16(p, s);
+  else if (g_split64.load() && sdpa::split64_supports(p)) e = sdpa::launch_split64(p, s);
   else if (sdpa::flash_mfma_supports(p)) e = sdpa::launch_flash_mfma(p, s);
   else e = sdpa::launch_generic_fwd(p, s);
   if (e != hipSuccess) return fail(SDPA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
@@ -262,6 +264,11 @@ int sdpa_set_tuning(const char* key, int64_t value) {
   if (!std::strcmp(key, "num_splits")) {
     if (value < 0 || value > 1024) return fail(SDPA_ERR_INVALID, "num_splits must be in [0, 1024]");
     g_num_splits.store(value);
+    return SDPA_OK;
+  }
+  if (!std::strcmp(key, "split_halves")) {
+    if (value != 0 && value != 1) return fail(SDPA_ERR_INVALID, "split_halves must be 0 or 1");
+    g_split64.store(value);
     return SDPA_OK;
   }
   if (!std::strcmp(key, "relpos_fused")) {

@@ -187,7 +187,8 @@ __global__ __launch_bounds__(256, 2) void flash_mfma_kernel(FwdParams p, int hpw
   lds_char* smem = (lds_char*)smem_raw;
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);     // wave-uniform (scalar) index
   const int g = lane >> 5;            // lane half: selects rows of the MFMA layouts
   const int ql = lane & 31;           // query column of this lane
   const int nqb = 4 / hpw;            // 32-row query blocks per workgroup

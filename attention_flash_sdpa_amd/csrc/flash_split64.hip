@@ -1,0 +1,378 @@
+// head_dim-64 flash attention for shapes with few query rows per GPU, such as
+// SAM ViT-B's 64x64 global attention (12 heads x 4096 queries = 1536 blocks of
+// 32 rows for 1024 SIMDs), with no mask or the decomposed rel-pos bias.
+//
+//   O = softmax(Q . K^T * scale + B) . V   ([Axon PR 650]
+//   "Axon.Layers.scaled_dot_product_attention/4", description;
+//   B = term_h[q, row(k)] + term_w[q, col(k)]: [Candle PR 3280] "feat(metal):
+//   SDPA with Relative Positional Embeddings & LayerNorm Stability", Key
+//   Changes; [mlx-examples issue 1451] "segment_anything: fuse attention with
+//   mx.fast.scaled_dot_product_attention", body).
+//
+// Work split.  A workgroup of 4 waves covers 64 query rows of one head: two
+// 32-row query blocks times two halves of the key range.  Each wave runs the
+// online softmax over its half; at the end the two halves of a query block
+// are merged through LDS by their running max and sum.  The GPU then holds
+// 3 workgroups per CU (12 waves, 3 per SIMD) and a 12 x 4096 problem deals
+// out evenly: 768 workgroups for 256 CUs.
+//
+// Per 32-key tile and wave: S^T = K . Q^T (4 MFMA 32x32x16, K from LDS, Q^T in
+// registers), softmax in log2 units (one query per lane), O^T += V^T . P^T
+// (4 MFMAs, V^T through the transposing LDS read).  Tiles are copied from HBM
+// into LDS by buffer loads that write LDS directly (no staging registers;
+// rows beyond the key range read as zero), double-buffered per half.
+//
+// Rel-pos (64-wide grid rows): term_w / scale for the 64 columns of a grid row
+// initialises the score accumulators (two 32-key tiles per grid row, one half
+// of the columns each), term_h of the row is one scalar per query.  The terms
+// are either formed here from Q and the tables (MFMA, as in the general
+// kernel) or read from precomputed term arrays.
+#include "common.h"
+
+#include <type_traits>
+
+namespace sdpa {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) char lds_char;
+typedef __attribute__((address_space(3))) float lds_float;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kTau = 8.0f;          // lazy-rescale threshold (log2 units)
+constexpr int BN = 32;                // keys per tile
+constexpr int ROWB = 128;             // bytes per K / V row (64 bf16)
+constexpr int TILEB = BN * ROWB;      // 4 KB
+constexpr int HALFB = 4 * TILEB;      // per half: 2 buffers x (K + V)
+constexpr int KV_BYTES = 2 * HALFB;   // 32 KB
+constexpr int TH_BYTES = 2 * 64 * 32 * 4;   // term_h^T per query block [y][q]
+
+enum Mode { S_NONE = 0, S_RELPOS_FUSED = 1, S_RELPOS_TERMS = 2 };
+
+// 16 lanes read rows r..r+15 at one 16-byte chunk index: distinct bank groups.
+__device__ __forceinline__ int kswz(int r) { return (r >> 1) & 7; }
+// Transposing reads take 4 rows x 64 contiguous bytes: flip 64-byte halves.
+__device__ __forceinline__ int vswz(int r) { return ((r >> 1) & 1) << 2; }
+
+__device__ __forceinline__ bf16x8 lds_b128(const lds_char* p) { return *(const __attribute__((address_space(3))) bf16x8*)p; }
+__device__ __forceinline__ s16x4 lds_tr(const lds_char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p);
+}
+__device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float pair_max(float v) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  const float a = __uint_as_float(r[0]), b = __uint_as_float(r[1]);
+  return a > b ? a : b;
+}
+__device__ __forceinline__ float pair_sum(float v) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+template <int MODE, bool OUT_BF16>
+__global__ __launch_bounds__(256, 3) void flash_split64_kernel(FwdParams p) {
+  __shared__ __attribute__((aligned(16))) char smem_raw[KV_BYTES + (MODE == S_RELPOS_FUSED ? TH_BYTES : 0)];
+  lds_char* smem = (lds_char*)smem_raw;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);     // wave-uniform (scalar) index
+  const int g = lane >> 5, ql = lane & 31;
+  const int qb = wave & 1, hf = wave >> 1;
+
+  // XCD-aware renumbering: each of the 8 XCDs gets a contiguous range of
+  // (batch, head, query tile), so its heads' K/V stay in its own L2.
+  const int64_t nblk = (int64_t)gridDim.x * gridDim.y * gridDim.z;
+  const int64_t lin = blockIdx.x + (int64_t)gridDim.x * (blockIdx.y + (int64_t)gridDim.y * blockIdx.z);
+  const int64_t per = nblk / 8, rem = nblk % 8, xcd = lin % 8;
+  const int64_t lid = xcd * per + min(xcd, rem) + lin / 8;
+  const int64_t tile = lid % gridDim.x, h = (lid / gridDim.x) % gridDim.y, b = lid / ((int64_t)gridDim.x * gridDim.y);
+  const int64_t hk = h / (p.Hq / p.Hkv);
+  const int64_t wq0 = tile * 64 + 32 * qb;
+  const int64_t qrow = wq0 + ql;
+  const bool qvalid = qrow < p.Tq;
+  const int64_t qsafe = qvalid ? qrow : 0;
+
+  const __bf16* qp = (const __bf16*)p.q + b * p.q_sb + h * p.q_sh;
+  bf16x8 qf[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) qf[c] = qvalid ? *(const bf16x8*)(qp + qrow * p.q_st + c * 16 + 8 * g) : (bf16x8){};
+
+  const float c2 = p.scale * kLog2e;
+  // ---- rel-pos: accumulator initialisation (term_w / scale) and term_h access
+  f32x16 cinit[2];
+  cinit[0] = (f32x16){};
+  cinit[1] = (f32x16){};
+  const float* thp = nullptr;
+  const lds_float* th_lds = (const lds_float*)(smem + KV_BYTES) + qb * (64 * 32) + ql;
+  if (MODE == S_RELPOS_TERMS) {
+    const float inv_scale = 1.0f / p.scale;
+    const float* twp = p.term_w + ((b * p.Hq + h) * p.Tq + qsafe) * 64;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const f32x4 t = *(const f32x4*)(twp + kb * 32 + 8 * i4 + 4 * g);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) cinit[kb][4 * i4 + e] = t[e] * inv_scale;
+      }
+    thp = p.term_h + ((b * p.Hq + h) * p.Tq + qsafe) * p.grid_h;
+  }
+  if (MODE == S_RELPOS_FUSED) {
+    // TH^T[y, q] = rel_pos_h[r + gh - 1 - y] . q and AW^T[m', q] = rel_pos_w[c0 + m'] . q
+    // on the matrix cores; term_w[q, x] is the skewed diagonal m' = col(q) - c0 + 63 - x.
+    const int gh = p.grid_h;
+    const int64_t r = wq0 / 64;
+    const int c0 = (int)(wq0 % 64);
+    const __bf16* rh = (const __bf16*)p.rel_h;
+    const __bf16* rw = (const __bf16*)p.rel_w;
+    f32x16 th[2], aw[3];
+#pragma unroll
+    for (int yb = 0; yb < 2; ++yb) {
+      th[yb] = (f32x16){};
+      const int y = yb * 32 + ql;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const bf16x8 a = (y < gh) ? *(const bf16x8*)(rh + (r + gh - 1 - y) * 64 + c * 16 + 8 * g) : (bf16x8){};
+        th[yb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[c], th[yb], 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int mb = 0; mb < 3; ++mb) {
+      aw[mb] = (f32x16){};
+      const int m = c0 + mb * 32 + ql;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const bf16x8 a = (m < 127) ? *(const bf16x8*)(rw + (int64_t)m * 64 + c * 16 + 8 * g) : (bf16x8){};
+        aw[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[c], aw[mb], 0, 0, 0);
+      }
+    }
+    lds_float* slot = (lds_float*)smem + qb * (32 * 97);        // [32 q][97] per query block
+    if (hf == 0) {
+#pragma unroll
+      for (int mb = 0; mb < 3; ++mb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) slot[ql * 97 + mb * 32 + 8 * (i / 4) + 4 * g + (i % 4)] = aw[mb][i];
+    }
+    __syncthreads();
+    const float inv_scale = 1.0f / p.scale;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int x = kb * 32 + 8 * (i / 4) + 4 * g + (i % 4);
+        cinit[kb][i] = slot[ql * 97 + ql + 63 - x] * inv_scale;
+      }
+    if (hf == 0) {
+      lds_float* ths = (lds_float*)(smem + KV_BYTES) + qb * (64 * 32);
+#pragma unroll
+      for (int yb = 0; yb < 2; ++yb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) ths[(yb * 32 + 8 * (i / 4) + 4 * g + (i % 4)) * 32 + ql] = th[yb][i];
+    }
+    __syncthreads();
+  }
+
+  // ---- key halves and LDS-direct tile copies
+  // Half 0 takes an even number of tiles so both halves start on an even tile:
+  // tile parity (which half of a 64-wide grid row) is then the unrolled step.
+  const int nt = (int)((p.Tkv + BN - 1) / BN);
+  const int nt0 = min(nt, (((nt + 1) / 2) + 1) & ~1);
+  const int tbeg = hf ? nt0 : 0;
+  const int tend = hf ? nt : nt0;
+  const int niter = nt0;                        // half 0 has at least as many tiles
+  const char* kvbase = (const char*)((const __bf16*)(qb ? p.v : p.k) + b * p.k_sb + hk * p.k_sh);
+  const int rstride = (int)(p.k_st * 2);
+  const int64_t span = ((p.Tkv - 1) * p.k_st + 64) * 2;     // bytes from the row base to the end of the last key row
+  // Wave qb of half hf copies the K (qb = 0) or V (qb = 1) tile of its half:
+  // 4 instructions of 64 lanes x 16 bytes; lane data lands at LDS offset 16 * lane.
+  // Per-lane byte offsets inside a tile are fixed; a per-tile descriptor moves
+  // the base and shrinks the record count, so rows past the key range read 0.
+  int voff[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int L = 64 * j + lane, row = L >> 3, pos = L & 7;
+    voff[j] = row * rstride + ((pos ^ (qb ? vswz(row) : kswz(row))) << 4);
+  }
+  auto stage = [&](int t, int buf) {
+    const int64_t tb = (int64_t)t * BN * rstride;
+    const int nrec = (int)max((int64_t)0, min(span - tb, (int64_t)0x7fffffff));
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)(kvbase + tb), 0, nrec, 0x00020000);
+    lds_char* dst = smem + hf * HALFB + buf * (2 * TILEB) + qb * TILEB;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(dst + j * 1024), 16,
+                                               voff[j], 0, 0, 0);
+  };
+
+  f32x16 o[2] = {(f32x16){}, (f32x16){}};
+  float m = -INFINITY, l = 0.0f;
+  const int j16 = lane & 15, dh = (lane >> 4) & 1;
+  // Transposing-read offsets of the V tile (tile-invariant).
+  int vro[2][2];
+#pragma unroll
+  for (int tc = 0; tc < 2; ++tc)
+#pragma unroll
+    for (int d = 0; d < 2; ++d) {
+      const int row0 = 16 * tc + 4 * g + (j16 >> 2);
+      vro[tc][d] = row0 * ROWB + ((((4 * d + 2 * dh + ((j16 & 3) >> 1)) ^ vswz(row0)) << 4) + ((j16 & 1) << 3));
+    }
+  int kro[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) kro[c] = ql * ROWB + (((2 * c + g) ^ kswz(ql)) << 4);
+
+  auto step = [&](int t, auto par) {
+    constexpr int PAR = decltype(par)::value;     // tile parity: buffer and grid-row half
+    const lds_char* ks = smem + hf * HALFB + PAR * (2 * TILEB);
+    const lds_char* vs = ks + TILEB;
+    f32x16 s = (MODE == S_NONE) ? (f32x16){} : cinit[PAR];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(ks + kro[c]), qf[c], s, 0, 0, 0);
+    if ((t + 1) * BN > p.Tkv) {
+      asm volatile("" ::: "memory");     // ragged last tile: a real branch, full tiles skip it
+      const int kl0 = t * BN + 4 * g;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[i] = (kl0 + 8 * (i / 4) + (i % 4) < (int)p.Tkv) ? s[i] : -INFINITY;
+    }
+    float rowb = 0.0f;
+    if (MODE == S_RELPOS_FUSED) rowb = th_lds[(t >> 1) * 32] * kLog2e;
+    if (MODE == S_RELPOS_TERMS) rowb = thp[t >> 1] * kLog2e;
+    float smax = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+#pragma unroll
+    for (int i = 4; i < 16; i += 2) smax = fmaxf(smax, fmaxf(s[i], s[i + 1]));
+    smax = pair_max(smax);
+    const float tmax = fmaf(smax, c2, rowb);
+    const bool need = tmax > m + kTau;
+    if (__builtin_expect(__any(need), 0)) {
+      const float mn = need ? tmax : m;
+      const float alpha = need ? ((m == -INFINITY) ? 0.0f : fexp2(m - mn)) : 1.0f;
+      m = mn;
+      l *= alpha;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        o[0][i] *= alpha;
+        o[1][i] *= alpha;
+      }
+    }
+    const float off = rowb - ((m == -INFINITY) ? 0.0f : m);
+    bf16x8 pb[2];
+#pragma unroll
+    for (int tc = 0; tc < 2; ++tc) {
+      bf16x2 pk[4];
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const f32x2 pp = {fexp2(fmaf(s[8 * tc + e], c2, off)), fexp2(fmaf(s[8 * tc + e + 1], c2, off))};
+        pk[e / 2] = __builtin_convertvector(pp, bf16x2);
+        l = __builtin_amdgcn_fdot2_f32_bf16(pk[e / 2], (bf16x2){(__bf16)1.0f, (__bf16)1.0f}, l, false);
+      }
+      pb[tc] = __builtin_shufflevector(__builtin_shufflevector(pk[0], pk[1], 0, 1, 2, 3),
+                                       __builtin_shufflevector(pk[2], pk[3], 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+#pragma unroll
+    for (int tc = 0; tc < 2; ++tc)
+#pragma unroll
+      for (int d = 0; d < 2; ++d) {
+        const s16x4 lo4 = lds_tr(vs + vro[tc][d]);
+        const s16x4 hi4 = lds_tr(vs + vro[tc][d] + 8 * ROWB);
+        const s16x8 a8 = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+        o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a8), pb[tc], o[d], 0, 0, 0);
+      }
+  };
+
+  if (tbeg < tend) stage(tbeg, 0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int it = 0; it < niter; it += 2) {
+    const int t = tbeg + it;
+    if (t + 1 < tend) stage(t + 1, 1);
+    if (t < tend) step(t, std::integral_constant<int, 0>{});
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (it + 1 < niter) {
+      if (t + 2 < tend) stage(t + 2, 0);
+      if (t + 1 < tend) step(t + 1, std::integral_constant<int, 1>{});
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    }
+  }
+
+  // ---- merge the two key halves of each query block through LDS
+  lds_float* xch = (lds_float*)smem + qb * (64 * 34);
+  if (hf == 1) {
+    xch[lane] = m;
+    xch[64 + lane] = l;
+#pragma unroll
+    for (int d = 0; d < 2; ++d)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) xch[128 + (d * 16 + i) * 64 + lane] = o[d][i];
+  }
+  __syncthreads();
+  if (hf == 1) return;
+  const float m1 = xch[lane], l1 = xch[64 + lane];
+  const float mm = fmaxf(m, m1);
+  const float w0 = (m == -INFINITY) ? 0.0f : fexp2(m - mm);
+  const float w1 = (m1 == -INFINITY) ? 0.0f : fexp2(m1 - mm);
+  const float lt = pair_sum(fmaf(l, w0, l1 * w1));
+  const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+  if (!qvalid) return;
+  const int64_t ob = b * p.q_sb + h * p.q_sh + qrow * p.q_st;
+#pragma unroll
+  for (int d = 0; d < 2; ++d)
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      const int dd = d * 32 + 8 * i4 + 4 * g;
+      float v[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = 4 * i4 + e;
+        v[e] = fmaf(o[d][i], w0, xch[128 + (d * 16 + i) * 64 + lane] * w1) * inv;
+      }
+      if (OUT_BF16) {
+        bf16x4 vb;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) vb[e] = (__bf16)v[e];
+        *(bf16x4*)((__bf16*)p.o + ob + dd) = vb;
+      } else {
+        *(f32x4*)((float*)p.o + ob + dd) = (f32x4){v[0], v[1], v[2], v[3]};
+      }
+    }
+  if (p.lse && g == 0) p.lse[(b * p.Hq + h) * p.Tq + qrow] = lt > 0.0f ? (mm + __log2f(lt)) * kLn2 : -INFINITY;
+}
+
+template <int MODE>
+hipError_t launch_mode(const FwdParams& p, hipStream_t s) {
+  dim3 grid((unsigned)((p.Tq + 63) / 64), (unsigned)p.Hq, (unsigned)p.B);
+  if (p.out_dtype == 1) hipLaunchKernelGGL((flash_split64_kernel<MODE, true>), grid, dim3(256), 0, s, p);
+  else hipLaunchKernelGGL((flash_split64_kernel<MODE, false>), grid, dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool split64_supports(const FwdParams& p) {
+  if (p.dtype != 1 || p.D != 64 || p.num_splits != 1) return false;
+  // key rows addressed with 32-bit byte offsets
+  if ((p.Tkv + BN) * p.k_st * 2 > 0x7fffffffLL) return false;
+  // worth it when the query blocks leave SIMDs idle: fewer than ~4 blocks of 32 rows per SIMD
+  if (p.B * p.Hq * ((p.Tq + 31) / 32) > 4096) return false;
+  if (p.bias == BIAS_NONE) return true;
+  if (p.bias == BIAS_RELPOS) {
+    if (p.grid_w != 64 || p.Tkv != p.Tq) return false;
+    if (p.term_h && p.term_w) return true;
+    return p.grid_h >= 1 && p.grid_h <= 64 && p.rel_h && p.rel_w;
+  }
+  return false;
+}
+
+hipError_t launch_split64(const FwdParams& p, hipStream_t s) {
+  if (p.bias == BIAS_RELPOS) return p.term_h ? launch_mode<S_RELPOS_TERMS>(p, s) : launch_mode<S_RELPOS_FUSED>(p, s);
+  return launch_mode<S_NONE>(p, s);
+}
+
+}  // namespace sdpa

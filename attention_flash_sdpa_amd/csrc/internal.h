@@ -65,6 +65,8 @@ hipError_t launch_flash_mfma(const FwdParams& p, hipStream_t s);   // bf16, D in
 bool flash_mfma_supports(const FwdParams& p);
 hipError_t launch_d16(const FwdParams& p, hipStream_t s);            // bf16, D = 16, head-packed (+ split-KV)
 bool d16_supports(const FwdParams& p);
+hipError_t launch_split64(const FwdParams& p, hipStream_t s);        // bf16, D = 64, key range split in-workgroup
+bool split64_supports(const FwdParams& p);
 // Rel-pos terms can be formed inside the MFMA kernel (no term arrays needed).
 bool relpos_fused_supported(const FwdParams& p);
 

@@ -168,6 +168,9 @@ const char* sdpa_last_error(void);
  * Process-wide tuning knobs (tests and benchmarks), each an int64:
  *   "num_splits"   split-KV chunk count for sdpa_fwd; 0 = automatic (default),
  *                  1 = never split, n > 1 = n chunks when the kernel supports it.
+ *   "split_halves" 1 (default) = for head_dim 64 with few query rows, each
+ *                  workgroup splits the key range between its waves and merges
+ *                  the halves; 0 = always one key range per wave.
  *   "relpos_fused" 1 (default) = sdpa_relpos_fwd forms the rel-pos terms
  *                  inside the attention kernel where the grid allows it;
  *                  0 = always run relpos_terms into the workspace first.

@@ -178,3 +178,64 @@ def test_relpos_fused_equals_unfused(gpu, name):
                       rel_pos={"rel_pos_h": np64(x["rel_pos_h"].cpu()), "rel_pos_w": np64(x["rel_pos_w"].cpu()),
                                "grid": wl.grid})
     assert max_err(np64(b), ref["o"]) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("splits", [1, 2, 5, 32, 0])
+def test_d16_split_kv_invariance(gpu, splits):
+    """Few queries against a long key range: any split-KV chunk count merges
+    (by log-sum-exp) to the same attention."""
+    gpu.set_tuning("num_splits", splits)
+    try:
+        check(gpu, 1, 8, 8, 7, 4096, 16, scale=0.25, seed=12)
+        check(gpu, 2, 6, 3, 5, 1000, 16, layout="bshd", seed=13, mask={"kind": "causal", "offset": 600})
+    finally:
+        gpu.set_tuning("num_splits", 0)
+
+
+@pytest.mark.parametrize("Tkv", [1, 7, 8, 9, 33, 64])
+def test_d16_key_packing(gpu, Tkv):
+    check(gpu, 1, 8, 8, 300, Tkv, 16, scale=0.25, seed=14)
+    check(gpu, 2, 6, 2, 70, Tkv, 16, layout="bshd", seed=15)
+
+
+def test_d16_masks(gpu):
+    g = torch.Generator().manual_seed(16)
+    m = torch.rand((1, 8, 7, 500), generator=g) < 0.5
+    check(gpu, 1, 8, 8, 7, 500, 16, mask={"kind": "bool", "data": m}, seed=17)
+    a = rnd((1, 1, 100, 9), torch.float32, 18)
+    check(gpu, 1, 8, 4, 100, 9, 16, mask={"kind": "additive", "data": a}, seed=19)
+    check(gpu, 1, 4, 4, 100, 50, 16, mask={"kind": "sliding", "window": 5, "offset": -40}, seed=20)
+
+
+@pytest.mark.parametrize("name", ["sam_global_relpos"])
+@pytest.mark.parametrize("halves", [0, 1])
+@pytest.mark.parametrize("fused", [0, 1])
+def test_relpos_kernel_variants(gpu, name, halves, fused):
+    """Every kernel route for the SAM global rel-pos shape agrees with the oracle:
+    key range split in-workgroup or not, terms formed in-kernel or precomputed."""
+    wl = workloads.replica(name, grid=(5, 64), Tq=5 * 64, Tkv=5 * 64)
+    x = {k_: t.cuda() for k_, t in workloads.generate(wl, seed=5).items()}
+    gpu.set_tuning("split_halves", halves)
+    gpu.set_tuning("relpos_fused", fused)
+    try:
+        o, lse = gpu.sdpa_relpos(x["q"], x["k"], x["v"], x["rel_pos_h"], x["rel_pos_w"], wl.grid, scale=wl.scale,
+                                 out_dtype=torch.float32, return_lse=True)
+    finally:
+        gpu.set_tuning("split_halves", 1)
+        gpu.set_tuning("relpos_fused", 1)
+    ref = oracle.sdpa(np64(x["q"].cpu()), np64(x["k"].cpu()), np64(x["v"].cpu()), scale=wl.scale,
+                      rel_pos={"rel_pos_h": np64(x["rel_pos_h"].cpu()), "rel_pos_w": np64(x["rel_pos_w"].cpu()),
+                               "grid": wl.grid})
+    assert max_err(np64(o), ref["o"]) <= TOL["bf16"]
+    assert max_err(np64(lse), ref["lse"]) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("halves", [0, 1])
+@pytest.mark.parametrize("Tkv", [32, 33, 95, 200, 4096])
+def test_d64_no_mask_key_splits(gpu, halves, Tkv):
+    gpu.set_tuning("split_halves", halves)
+    try:
+        check(gpu, 1, 3, 3, 130, Tkv, 64, seed=21)
+        check(gpu, 1, 4, 2, 64, Tkv, 64, layout="bshd", seed=22)
+    finally:
+        gpu.set_tuning("split_halves", 1)
