@@ -48,6 +48,7 @@ typedef __attribute__((address_space(3))) float lds_float;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kTau = 8.0f;          // lazy-rescale threshold (log2 units)
+constexpr float kTauSum = 256.0f;     // a tile row sum above 2^tau flags a probability that may exceed 2^tau
 constexpr int BN = 32;                // keys per tile
 constexpr int ROWB = 128;             // bytes per K / V row (64 bf16)
 constexpr int TILEB = BN * ROWB;      // 4 KB
@@ -127,38 +128,68 @@ __global__ __launch_bounds__(256, 3) void flash_split64_kernel(FwdParams p) {
   if (MODE == S_RELPOS_FUSED) {
     // TH^T[y, q] = rel_pos_h[r + gh - 1 - y] . q and AW^T[m', q] = rel_pos_w[c0 + m'] . q
     // on the matrix cores; term_w[q, x] is the skewed diagonal m' = col(q) - c0 + 63 - x.
+    // Both query blocks of the workgroup lie in grid row r, so the workgroup
+    // first copies the rel_pos_h rows r .. r + 63 and all of rel_pos_w into LDS
+    // (once per workgroup instead of once per wave), and only the waves of key
+    // half 0 form the products (those of half 1 read the results).
     const int gh = p.grid_h;
     const int64_t r = wq0 / 64;
     const int c0 = (int)(wq0 % 64);
-    const __bf16* rh = (const __bf16*)p.rel_h;
-    const __bf16* rw = (const __bf16*)p.rel_w;
+    {
+      // 64 + 128 rows x 128 B = 24 KB into the K/V area, K-tile swizzle;
+      // rows past each table read as zero (record count = table size).
+      const __amdgpu_buffer_rsrc_t rhs = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)((const __bf16*)p.rel_h + r * 64), 0, (int)max((int64_t)0, (2 * gh - 1 - r) * 128), 0x00020000);
+      const __amdgpu_buffer_rsrc_t rws = __builtin_amdgcn_make_buffer_rsrc((void*)p.rel_w, 0, 127 * 128, 0x00020000);
+#pragma unroll
+      for (int j = 0; j < 6; ++j) {                 // 6 x 256 lanes x 16 B = 24 KB
+        const int L = 256 * j + tid;               // linear 16-byte chunk: rows 0..63 Rh, 64..191 Rw
+        const int row = L >> 3, pos = L & 7;
+        const int trow = j < 2 ? row : row - 64;    // rows 0..63 <=> j < 2 (uniform per instruction)
+        const int voff = trow * 128 + ((pos ^ kswz(row)) << 4);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(j < 2 ? rhs : rws,
+                                                 (__attribute__((address_space(3))) void*)(smem + 4096 * j + 1024 * wave), 16,
+                                                 voff, 0, 0, 0);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
     f32x16 th[2], aw[3];
+    if (hf == 0) {
+      // LDS row of rel_pos_h[r + gh - 1 - y] is gh - 1 - y (zero for y >= gh)
 #pragma unroll
-    for (int yb = 0; yb < 2; ++yb) {
-      th[yb] = (f32x16){};
-      const int y = yb * 32 + ql;
+      for (int yb = 0; yb < 2; ++yb) {
+        th[yb] = (f32x16){};
+        const int y = yb * 32 + ql;
+        const int lr = max(gh - 1 - y, 0);
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const bf16x8 a = (y < gh) ? *(const bf16x8*)(rh + (r + gh - 1 - y) * 64 + c * 16 + 8 * g) : (bf16x8){};
-        th[yb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[c], th[yb], 0, 0, 0);
+        for (int c = 0; c < 4; ++c) {
+          const bf16x8 a = lds_b128(smem + lr * ROWB + (((2 * c + g) ^ kswz(lr)) << 4));
+          th[yb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(y < gh ? a : (bf16x8){}, qf[c], th[yb], 0, 0, 0);
+        }
+      }
+#pragma unroll
+      for (int mb = 0; mb < 3; ++mb) {
+        aw[mb] = (f32x16){};
+        const int lr = 64 + c0 + mb * 32 + ql;       // row 127 of the table area is zero
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          aw[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(smem + lr * ROWB + (((2 * c + g) ^ kswz(lr)) << 4)),
+                                                           qf[c], aw[mb], 0, 0, 0);
       }
     }
-#pragma unroll
-    for (int mb = 0; mb < 3; ++mb) {
-      aw[mb] = (f32x16){};
-      const int m = c0 + mb * 32 + ql;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const bf16x8 a = (m < 127) ? *(const bf16x8*)(rw + (int64_t)m * 64 + c * 16 + 8 * g) : (bf16x8){};
-        aw[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[c], aw[mb], 0, 0, 0);
-      }
-    }
+    __syncthreads();                                 // table rows no longer needed
     lds_float* slot = (lds_float*)smem + qb * (32 * 97);        // [32 q][97] per query block
     if (hf == 0) {
 #pragma unroll
       for (int mb = 0; mb < 3; ++mb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) slot[ql * 97 + mb * 32 + 8 * (i / 4) + 4 * g + (i % 4)] = aw[mb][i];
+      lds_float* ths = (lds_float*)(smem + KV_BYTES) + qb * (64 * 32);
+#pragma unroll
+      for (int yb = 0; yb < 2; ++yb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) ths[(yb * 32 + 8 * (i / 4) + 4 * g + (i % 4)) * 32 + ql] = th[yb][i];
     }
     __syncthreads();
     const float inv_scale = 1.0f / p.scale;
@@ -169,13 +200,6 @@ __global__ __launch_bounds__(256, 3) void flash_split64_kernel(FwdParams p) {
         const int x = kb * 32 + 8 * (i / 4) + 4 * g + (i % 4);
         cinit[kb][i] = slot[ql * 97 + ql + 63 - x] * inv_scale;
       }
-    if (hf == 0) {
-      lds_float* ths = (lds_float*)(smem + KV_BYTES) + qb * (64 * 32);
-#pragma unroll
-      for (int yb = 0; yb < 2; ++yb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) ths[(yb * 32 + 8 * (i / 4) + 4 * g + (i % 4)) * 32 + ql] = th[yb][i];
-    }
     __syncthreads();
   }
 
@@ -243,13 +267,38 @@ __global__ __launch_bounds__(256, 3) void flash_split64_kernel(FwdParams p) {
     float rowb = 0.0f;
     if (MODE == S_RELPOS_FUSED) rowb = th_lds[(t >> 1) * 32] * kLog2e;
     if (MODE == S_RELPOS_TERMS) rowb = thp[t >> 1] * kLog2e;
-    float smax = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+    // Probabilities against the running reference m (log2 units).  The tile
+    // max is not computed up front: a probability above 2^tau -- detected from
+    // the tile's row sum, which also catches overflow and the first tile
+    // (m = -inf) -- sends the wave through the exact path, which moves m to
+    // the tile max, rescales O and l, and recomputes the probabilities.
+    bf16x8 pb[2];
+    auto probs = [&](float off) -> float {
+      float acc0 = 0.0f, acc1 = 0.0f;
 #pragma unroll
-    for (int i = 4; i < 16; i += 2) smax = fmaxf(smax, fmaxf(s[i], s[i + 1]));
-    smax = pair_max(smax);
-    const float tmax = fmaf(smax, c2, rowb);
-    const bool need = tmax > m + kTau;
-    if (__builtin_expect(__any(need), 0)) {
+      for (int tc = 0; tc < 2; ++tc) {
+        bf16x2 pk[4];
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const f32x2 pp = {fexp2(fmaf(s[8 * tc + e], c2, off)), fexp2(fmaf(s[8 * tc + e + 1], c2, off))};
+          pk[e / 2] = __builtin_convertvector(pp, bf16x2);
+          if (e & 2) acc1 = __builtin_amdgcn_fdot2_f32_bf16(pk[e / 2], (bf16x2){(__bf16)1.0f, (__bf16)1.0f}, acc1, false);
+          else acc0 = __builtin_amdgcn_fdot2_f32_bf16(pk[e / 2], (bf16x2){(__bf16)1.0f, (__bf16)1.0f}, acc0, false);
+        }
+        pb[tc] = __builtin_shufflevector(__builtin_shufflevector(pk[0], pk[1], 0, 1, 2, 3),
+                                         __builtin_shufflevector(pk[2], pk[3], 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
+      }
+      return acc0 + acc1;
+    };
+    float lt = probs(rowb - ((m == -INFINITY) ? 0.0f : m));
+    // (m = -inf: no key seen yet; the reference must come from an actual max)
+    if (__builtin_expect(__any(!(lt <= kTauSum) || m == -INFINITY), 0)) {
+      float smax = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+#pragma unroll
+      for (int i = 4; i < 16; i += 2) smax = fmaxf(smax, fmaxf(s[i], s[i + 1]));
+      smax = pair_max(smax);
+      const float tmax = fmaf(smax, c2, rowb);
+      const bool need = tmax > m + kTau;
       const float mn = need ? tmax : m;
       const float alpha = need ? ((m == -INFINITY) ? 0.0f : fexp2(m - mn)) : 1.0f;
       m = mn;
@@ -259,21 +308,9 @@ __global__ __launch_bounds__(256, 3) void flash_split64_kernel(FwdParams p) {
         o[0][i] *= alpha;
         o[1][i] *= alpha;
       }
+      lt = probs(rowb - ((m == -INFINITY) ? 0.0f : m));
     }
-    const float off = rowb - ((m == -INFINITY) ? 0.0f : m);
-    bf16x8 pb[2];
-#pragma unroll
-    for (int tc = 0; tc < 2; ++tc) {
-      bf16x2 pk[4];
-#pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        const f32x2 pp = {fexp2(fmaf(s[8 * tc + e], c2, off)), fexp2(fmaf(s[8 * tc + e + 1], c2, off))};
-        pk[e / 2] = __builtin_convertvector(pp, bf16x2);
-        l = __builtin_amdgcn_fdot2_f32_bf16(pk[e / 2], (bf16x2){(__bf16)1.0f, (__bf16)1.0f}, l, false);
-      }
-      pb[tc] = __builtin_shufflevector(__builtin_shufflevector(pk[0], pk[1], 0, 1, 2, 3),
-                                       __builtin_shufflevector(pk[2], pk[3], 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
-    }
+    l += lt;
 #pragma unroll
     for (int tc = 0; tc < 2; ++tc)
 #pragma unroll

@@ -239,3 +239,35 @@ def test_d64_no_mask_key_splits(gpu, halves, Tkv):
         check(gpu, 1, 4, 2, 64, Tkv, 64, layout="bshd", seed=22)
     finally:
         gpu.set_tuning("split_halves", 1)
+
+
+@pytest.mark.parametrize("pattern", ["rising", "falling", "spike", "huge"])
+@pytest.mark.parametrize("D", [64, 128])
+def test_running_max_paths(gpu, pattern, D):
+    """Score patterns that move the running max: scores rising across key tiles
+    (rescale on almost every tile), falling (probabilities far below the
+    reference), one dominant late key, and logits of +-200 that would overflow
+    exp2 against a stale reference."""
+    T = 700
+    g = torch.Generator().manual_seed(31)
+    q = torch.randn((1, 2, 65, D), generator=g)
+    k = torch.randn((1, 2, T, D), generator=g) * 0.1
+    v = torch.randn((1, 2, T, D), generator=g)
+    ramp = torch.linspace(0, 1, T).view(1, 1, T, 1)
+    if pattern == "rising":
+        k = k + ramp * q.mean(dim=2, keepdim=True) * 3
+    elif pattern == "falling":
+        k = k + (1 - ramp) * q.mean(dim=2, keepdim=True) * 3
+    elif pattern == "spike":
+        k[:, :, 650] = q.mean(dim=2) * 2
+    else:
+        k = k * 40.0
+    q, k, v = (x.to(torch.bfloat16) for x in (q, k, v))
+    for halves in (0, 1):
+        gpu.set_tuning("split_halves", halves)
+        try:
+            o = gpu.sdpa(q.cuda(), k.cuda(), v.cuda(), scale=1.0 / D ** 0.5, out_dtype=torch.float32)
+        finally:
+            gpu.set_tuning("split_halves", 1)
+        ref = oracle.sdpa(np64(q), np64(k), np64(v), scale=1.0 / D ** 0.5)
+        assert max_err(np64(o), ref["o"]) <= TOL["bf16"], (pattern, halves)
