@@ -52,9 +52,18 @@ constexpr float kTauSum = 256.0f;     // a tile row sum above 2^tau flags a prob
 constexpr int BN = 32;                // keys per tile
 constexpr int ROWB = 128;             // bytes per K / V row (64 bf16)
 constexpr int TILEB = BN * ROWB;      // 4 KB
-constexpr int HALFB = 4 * TILEB;      // per half: 2 buffers x (K + V)
-constexpr int KV_BYTES = 2 * HALFB;   // 32 KB
-constexpr int TH_BYTES = 2 * 64 * 32 * 4;   // term_h^T per query block [y][q]
+constexpr int TH_FLOATS = 2 * 64 * 34;   // term_h^T [2 query blocks][64 y][32 q]; the half exchange uses [2][34][64]
+
+// LDS: four distinct objects for the K / V tiles of buffer parity 0 / 1 (one
+// tile per key half each) and one for term_h^T.  A step copies into the
+// parity-(t+1) objects while it reads the parity-t ones; because they are
+// distinct objects the compiler knows the in-flight LDS-direct copies cannot
+// alias the reads, and does not stall the reads on the copies.
+__shared__ __attribute__((aligned(16))) char s64_ka[2 * TILEB];
+__shared__ __attribute__((aligned(16))) char s64_kb[2 * TILEB];
+__shared__ __attribute__((aligned(16))) char s64_va[2 * TILEB];
+__shared__ __attribute__((aligned(16))) char s64_vb[2 * TILEB];
+__shared__ __attribute__((aligned(16))) float s64_th[TH_FLOATS];
 
 enum Mode { S_NONE = 0, S_RELPOS_FUSED = 1, S_RELPOS_TERMS = 2 };
 
@@ -80,8 +89,11 @@ __device__ __forceinline__ float pair_sum(float v) {
 
 template <int MODE, bool OUT_BF16>
 __global__ __launch_bounds__(256, 3) void flash_split64_kernel(FwdParams p) {
-  __shared__ __attribute__((aligned(16))) char smem_raw[KV_BYTES + (MODE == S_RELPOS_FUSED ? TH_BYTES : 0)];
-  lds_char* smem = (lds_char*)smem_raw;
+  lds_char* const ka = (lds_char*)s64_ka;
+  lds_char* const kb = (lds_char*)s64_kb;
+  lds_char* const va = (lds_char*)s64_va;
+  lds_char* const vb = (lds_char*)s64_vb;
+  lds_float* const ths = (lds_float*)s64_th;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);     // wave-uniform (scalar) index
   const int g = lane >> 5, ql = lane & 31;
@@ -111,7 +123,7 @@ __global__ __launch_bounds__(256, 3) void flash_split64_kernel(FwdParams p) {
   cinit[0] = (f32x16){};
   cinit[1] = (f32x16){};
   const float* thp = nullptr;
-  const lds_float* th_lds = (const lds_float*)(smem + KV_BYTES) + qb * (64 * 32) + ql;
+  const lds_float* th_lds = ths + qb * (64 * 32) + ql;
   if (MODE == S_RELPOS_TERMS) {
     const float inv_scale = 1.0f / p.scale;
     const float* twp = p.term_w + ((b * p.Hq + h) * p.Tq + qsafe) * 64;
@@ -136,20 +148,22 @@ __global__ __launch_bounds__(256, 3) void flash_split64_kernel(FwdParams p) {
     const int64_t r = wq0 / 64;
     const int c0 = (int)(wq0 % 64);
     {
-      // 64 + 128 rows x 128 B = 24 KB into the K/V area, K-tile swizzle;
+      // 64 + 128 rows x 128 B = 24 KB into the tile objects (rel_pos_h rows in
+      // ka, rel_pos_w rows 0..63 in kb and 64..127 in va), K-tile swizzle;
       // rows past each table read as zero (record count = table size).
       const __amdgpu_buffer_rsrc_t rhs = __builtin_amdgcn_make_buffer_rsrc(
           (void*)((const __bf16*)p.rel_h + r * 64), 0, (int)max((int64_t)0, (2 * gh - 1 - r) * 128), 0x00020000);
       const __amdgpu_buffer_rsrc_t rws = __builtin_amdgcn_make_buffer_rsrc((void*)p.rel_w, 0, 127 * 128, 0x00020000);
 #pragma unroll
       for (int j = 0; j < 6; ++j) {                 // 6 x 256 lanes x 16 B = 24 KB
-        const int L = 256 * j + tid;               // linear 16-byte chunk: rows 0..63 Rh, 64..191 Rw
+        const int L = 256 * (j & 1) + tid;         // 16-byte chunk within the object (rows 0..63)
         const int row = L >> 3, pos = L & 7;
-        const int trow = j < 2 ? row : row - 64;    // rows 0..63 <=> j < 2 (uniform per instruction)
+        const int trow = (j < 2 ? 0 : (j < 4 ? 0 : 64)) + row;
         const int voff = trow * 128 + ((pos ^ kswz(row)) << 4);
+        lds_char* obj = j < 2 ? ka : (j < 4 ? kb : va);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(j < 2 ? rhs : rws,
-                                                 (__attribute__((address_space(3))) void*)(smem + 4096 * j + 1024 * wave), 16,
-                                                 voff, 0, 0, 0);
+                                                 (__attribute__((address_space(3))) void*)(obj + 4096 * (j & 1) + 1024 * wave),
+                                                 16, voff, 0, 0, 0);
       }
     }
     __builtin_amdgcn_s_waitcnt(0);
@@ -164,42 +178,52 @@ __global__ __launch_bounds__(256, 3) void flash_split64_kernel(FwdParams p) {
         const int lr = max(gh - 1 - y, 0);
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          const bf16x8 a = lds_b128(smem + lr * ROWB + (((2 * c + g) ^ kswz(lr)) << 4));
+          const bf16x8 a = lds_b128(ka + lr * ROWB + (((2 * c + g) ^ kswz(lr)) << 4));
           th[yb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(y < gh ? a : (bf16x8){}, qf[c], th[yb], 0, 0, 0);
         }
       }
 #pragma unroll
       for (int mb = 0; mb < 3; ++mb) {
         aw[mb] = (f32x16){};
-        const int lr = 64 + c0 + mb * 32 + ql;       // row 127 of the table area is zero
+        const int m = c0 + mb * 32 + ql;            // table row; row 127 reads as zero
+        const lds_char* rowp = (m < 64 ? kb + m * ROWB : va + (m - 64) * ROWB);
 #pragma unroll
         for (int c = 0; c < 4; ++c)
-          aw[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(smem + lr * ROWB + (((2 * c + g) ^ kswz(lr)) << 4)),
+          aw[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(rowp + (((2 * c + g) ^ kswz(m & 63)) << 4)),
                                                            qf[c], aw[mb], 0, 0, 0);
       }
     }
     __syncthreads();                                 // table rows no longer needed
-    lds_float* slot = (lds_float*)smem + qb * (32 * 97);        // [32 q][97] per query block
+    // Skewed gather through the term_h object, one query block at a time
+    // ([32 q][97] fp32 slot), then term_h^T itself.
+    const float inv_scale = 1.0f / p.scale;
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+      if (qb == pass && hf == 0) {
+#pragma unroll
+        for (int mb = 0; mb < 3; ++mb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) ths[ql * 97 + mb * 32 + 8 * (i / 4) + 4 * g + (i % 4)] = aw[mb][i];
+      }
+      __syncthreads();
+      if (qb == pass) {
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int x = kk * 32 + 8 * (i / 4) + 4 * g + (i % 4);
+            cinit[kk][i] = ths[ql * 97 + ql + 63 - x] * inv_scale;
+          }
+      }
+      __syncthreads();
+    }
     if (hf == 0) {
-#pragma unroll
-      for (int mb = 0; mb < 3; ++mb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) slot[ql * 97 + mb * 32 + 8 * (i / 4) + 4 * g + (i % 4)] = aw[mb][i];
-      lds_float* ths = (lds_float*)(smem + KV_BYTES) + qb * (64 * 32);
+      lds_float* thw = ths + qb * (64 * 32);
 #pragma unroll
       for (int yb = 0; yb < 2; ++yb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) ths[(yb * 32 + 8 * (i / 4) + 4 * g + (i % 4)) * 32 + ql] = th[yb][i];
+        for (int i = 0; i < 16; ++i) thw[(yb * 32 + 8 * (i / 4) + 4 * g + (i % 4)) * 32 + ql] = th[yb][i];
     }
-    __syncthreads();
-    const float inv_scale = 1.0f / p.scale;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int x = kb * 32 + 8 * (i / 4) + 4 * g + (i % 4);
-        cinit[kb][i] = slot[ql * 97 + ql + 63 - x] * inv_scale;
-      }
     __syncthreads();
   }
 
@@ -212,6 +236,7 @@ __global__ __launch_bounds__(256, 3) void flash_split64_kernel(FwdParams p) {
   const int tend = hf ? nt : nt0;
   const int niter = nt0;                        // half 0 has at least as many tiles
   const char* kvbase = (const char*)((const __bf16*)(qb ? p.v : p.k) + b * p.k_sb + hk * p.k_sh);
+  // Wave qb of half hf copies the K (qb = 0) or V (qb = 1) tile of its half.
   const int rstride = (int)(p.k_st * 2);
   const int64_t span = ((p.Tkv - 1) * p.k_st + 64) * 2;     // bytes from the row base to the end of the last key row
   // Wave qb of half hf copies the K (qb = 0) or V (qb = 1) tile of its half:
@@ -224,15 +249,20 @@ __global__ __launch_bounds__(256, 3) void flash_split64_kernel(FwdParams p) {
     const int L = 64 * j + lane, row = L >> 3, pos = L & 7;
     voff[j] = row * rstride + ((pos ^ (qb ? vswz(row) : kswz(row))) << 4);
   }
-  auto stage = [&](int t, int buf) {
+  auto stage = [&](int t, auto par) {          // tile t into the parity-PAR objects
+    constexpr int PAR = decltype(par)::value;
     const int64_t tb = (int64_t)t * BN * rstride;
     const int nrec = (int)max((int64_t)0, min(span - tb, (int64_t)0x7fffffff));
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)(kvbase + tb), 0, nrec, 0x00020000);
-    lds_char* dst = smem + hf * HALFB + buf * (2 * TILEB) + qb * TILEB;
+    auto issue = [&](lds_char* obj) {
+      lds_char* dst = obj + hf * TILEB;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(dst + j * 1024), 16,
-                                               voff[j], 0, 0, 0);
+      for (int j = 0; j < 4; ++j)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(dst + j * 1024), 16,
+                                                 voff[j], 0, 0, 0);
+    };
+    if (qb == 0) issue(PAR ? kb : ka);          // one static destination object per call site
+    else issue(PAR ? vb : va);
   };
 
   f32x16 o[2] = {(f32x16){}, (f32x16){}};
@@ -251,10 +281,10 @@ __global__ __launch_bounds__(256, 3) void flash_split64_kernel(FwdParams p) {
 #pragma unroll
   for (int c = 0; c < 4; ++c) kro[c] = ql * ROWB + (((2 * c + g) ^ kswz(ql)) << 4);
 
-  auto step = [&](int t, auto par) {
+  auto step = [&](int t, auto par, float th_pair) {
     constexpr int PAR = decltype(par)::value;     // tile parity: buffer and grid-row half
-    const lds_char* ks = smem + hf * HALFB + PAR * (2 * TILEB);
-    const lds_char* vs = ks + TILEB;
+    const lds_char* ks = (PAR ? kb : ka) + hf * TILEB;
+    const lds_char* vs = (PAR ? vb : va) + hf * TILEB;
     f32x16 s = (MODE == S_NONE) ? (f32x16){} : cinit[PAR];
 #pragma unroll
     for (int c = 0; c < 4; ++c) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(ks + kro[c]), qf[c], s, 0, 0, 0);
@@ -264,9 +294,7 @@ __global__ __launch_bounds__(256, 3) void flash_split64_kernel(FwdParams p) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) s[i] = (kl0 + 8 * (i / 4) + (i % 4) < (int)p.Tkv) ? s[i] : -INFINITY;
     }
-    float rowb = 0.0f;
-    if (MODE == S_RELPOS_FUSED) rowb = th_lds[(t >> 1) * 32] * kLog2e;
-    if (MODE == S_RELPOS_TERMS) rowb = thp[t >> 1] * kLog2e;
+    const float rowb = th_pair * kLog2e;
     // Probabilities against the running reference m (log2 units).  The tile
     // max is not computed up front: a probability above 2^tau -- detected from
     // the tile's row sum, which also catches overflow and the first tile
@@ -322,25 +350,36 @@ __global__ __launch_bounds__(256, 3) void flash_split64_kernel(FwdParams p) {
       }
   };
 
-  if (tbeg < tend) stage(tbeg, 0);
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
+  // term_h of a grid row (two tiles), read one iteration ahead
+  auto th_of = [&](int t) -> float {
+    if (MODE == S_RELPOS_FUSED) return th_lds[(t >> 1) * 32];
+    if (MODE == S_RELPOS_TERMS) return thp[t >> 1];
+    return 0.0f;
+  };
+  if (tbeg < tend) stage(tbeg, P0{});
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  float th_next = (tbeg < tend) ? th_of(tbeg) : 0.0f;
   for (int it = 0; it < niter; it += 2) {
     const int t = tbeg + it;
-    if (t + 1 < tend) stage(t + 1, 1);
-    if (t < tend) step(t, std::integral_constant<int, 0>{});
+    const float th_cur = th_next;
+    if (t + 2 < tend) th_next = th_of(t + 2);
+    if (t + 1 < tend) stage(t + 1, P1{});
+    if (t < tend) step(t, P0{}, th_cur);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (it + 1 < niter) {
-      if (t + 2 < tend) stage(t + 2, 0);
-      if (t + 1 < tend) step(t + 1, std::integral_constant<int, 1>{});
+      if (t + 2 < tend) stage(t + 2, P0{});
+      if (t + 1 < tend) step(t + 1, P1{}, th_cur);
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
     }
   }
 
   // ---- merge the two key halves of each query block through LDS
-  lds_float* xch = (lds_float*)smem + qb * (64 * 34);
+  lds_float* xch = ths + qb * (64 * 34);
   if (hf == 1) {
     xch[lane] = m;
     xch[64 + lane] = l;
