@@ -34,7 +34,7 @@ def hipcc():
 # Per-file extra flags.  The MFMA attention kernels take row maxima of scores
 # produced by the matrix cores; without NaN honouring the maxima need no
 # quieting moves (NaN scores still reach the output through exp and P.V).
-EXTRA = {"flash_mfma.hip": ["-fno-honor-nans"], "flash_split64.hip": ["-fno-honor-nans"]}
+EXTRA = {f: ["-fno-honor-nans"] for f in ("flash_mfma.hip", "flash_split64.hip", "flash_tiled.hip")}
 
 
 def _compile(src):

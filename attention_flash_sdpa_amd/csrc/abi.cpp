@@ -20,6 +20,7 @@ thread_local std::string g_last_error;
 std::atomic<int64_t> g_num_splits{0};
 std::atomic<int64_t> g_relpos_fused{1};
 std::atomic<int64_t> g_split64{1};
+std::atomic<int64_t> g_tiled{1};
 
 int fail(int status, const char* fmt, ...) {
   char buf[512];
@@ -103,15 +104,22 @@ sdpa::FwdParams base_params(const void* q, const void* k, const void* v, void* o
 
 int launch(const sdpa::FwdParams& p, hipStream_t s) {
   hipError_t e;
-  if (sdpa::d16_supports(p)) e = sdpa::launch_d16(p, s);
+  // The MFMA kernels take each row's running max on scores already multiplied
+  // by scale, which needs scale > 0; other scales run on the generic kernel.
+  const bool fast = p.scale > 0.0f && std::isfinite(p.scale);
+  if (!fast) e = sdpa::launch_generic_fwd(p, s);
+  else if (sdpa::d16_supports(p)) e = sdpa::launch_d16(p, s);
   else if (g_split64.load() && sdpa::split64_supports(p)) e = sdpa::launch_split64(p, s);
+  else if (g_tiled.load() && sdpa::tiled_supports(p)) e = sdpa::launch_tiled(p, s);
   else if (sdpa::flash_mfma_supports(p)) e = sdpa::launch_flash_mfma(p, s);
   else e = sdpa::launch_generic_fwd(p, s);
   if (e != hipSuccess) return fail(SDPA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return SDPA_OK;
 }
 
-bool relpos_fused_ok(const sdpa::FwdParams& p) { return sdpa::relpos_fused_supported(p); }
+bool relpos_fused_ok(const sdpa::FwdParams& p) {
+  return p.scale > 0.0f && std::isfinite(p.scale) && sdpa::relpos_fused_supported(p);
+}
 
 }  // namespace
 
@@ -242,6 +250,7 @@ int sdpa_relpos_fused(int dtype, int64_t D, int64_t grid_h, int64_t grid_w) {
   p.dtype = dtype; p.D = D; p.grid_h = (int)grid_h; p.grid_w = (int)grid_w;
   p.Tq = p.Tkv = grid_h * grid_w;
   p.rel_h = p.rel_w = &dummy;
+  p.scale = 1.0f;
   return (g_relpos_fused.load() && grid_h > 0 && grid_w > 0 && relpos_fused_ok(p)) ? 1 : 0;
 }
 
@@ -269,6 +278,11 @@ int sdpa_set_tuning(const char* key, int64_t value) {
   if (!std::strcmp(key, "split_halves")) {
     if (value != 0 && value != 1) return fail(SDPA_ERR_INVALID, "split_halves must be 0 or 1");
     g_split64.store(value);
+    return SDPA_OK;
+  }
+  if (!std::strcmp(key, "tiled")) {
+    if (value != 0 && value != 1) return fail(SDPA_ERR_INVALID, "tiled must be 0 or 1");
+    g_tiled.store(value);
     return SDPA_OK;
   }
   if (!std::strcmp(key, "relpos_fused")) {

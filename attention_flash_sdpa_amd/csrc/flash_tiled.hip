@@ -1,0 +1,331 @@
+// Flash attention forward for head_dim 64 / 128 with no mask or a causal /
+// sliding-window mask, grouped-query K/V sharing, bshd or bhsd layouts: the
+// decoder-style path (many query rows, long key ranges).
+//
+//   O = softmax(Q . K^T * scale + M) . V     ([Axon PR 650]
+//   "Axon.Layers.scaled_dot_product_attention/4", description: masks
+//   {causal, offset} and {sliding_window, w, offset}; grouped-query attention
+//   by repeating key/value heads).
+//
+// Work split.  A workgroup is 4 waves of 32 query rows.  With grouped-query
+// attention the 4 waves are query heads that share one KV head at the same 32
+// positions: each K/V tile in LDS feeds all of them and their mask patterns
+// coincide.  Workgroups are ordered so each XCD works through a contiguous
+// range of (batch, KV head) groups, heaviest (latest) query blocks first.
+//
+// Per 32-key tile and wave: S^T = K . Q^T (D/16 MFMA 32x32x16; K from LDS,
+// Q^T in registers), online softmax in log2 units with one query per lane,
+// O^T += V^T . P^T (D/32 x 2 MFMAs; V^T through the transposing LDS read).
+// Tiles are copied from HBM by buffer loads that write LDS directly (rows
+// past the key range read as zero), double-buffered in distinct LDS objects
+// so in-flight copies never stall the reads of the current tile.  Tiles
+// wholly outside a wave's causal / sliding band are skipped; only tiles the
+// band boundary crosses pay for per-element masking.
+//
+// The running max is optimistic: probabilities are formed against the current
+// reference and only a tile whose row sum exceeds 2^8 (a probability above
+// 2^8, an overflow, or no reference yet) takes the exact path that moves the
+// reference to the tile max and rescales O and the row sum.
+#include "common.h"
+
+#include <type_traits>
+
+namespace sdpa {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) char lds_char;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kTau = 8.0f;
+constexpr float kTauSum = 256.0f;
+constexpr int BN = 32;
+constexpr int MAXTILE = BN * 128 * 2;     // 8 KB: one K or V tile at head_dim 128
+
+__shared__ __attribute__((aligned(16))) char ft_ka[MAXTILE];
+__shared__ __attribute__((aligned(16))) char ft_kb[MAXTILE];
+__shared__ __attribute__((aligned(16))) char ft_va[MAXTILE];
+__shared__ __attribute__((aligned(16))) char ft_vb[MAXTILE];
+
+enum Mode { T_NONE = 0, T_INDEX = 1 };
+
+template <int D>
+struct TCfg {
+  static constexpr int ROWB = 2 * D;               // bytes per K / V row
+  static constexpr int TILEB = BN * ROWB;          // bytes per tile
+  static constexpr int CH = D / 8;                 // 16-byte chunks per row
+  static constexpr int RPB = 256 / ROWB;           // rows per 256-byte bank sweep
+  static constexpr int QC = D / 16;                // Q.K^T MFMA chunks
+  static constexpr int DB = D / 32;                // O^T row blocks
+  static constexpr int NI = TILEB / 4096;          // copy instructions per wave per tile (4 waves x 1 KB each)
+  static_assert(NI <= 2, "per-lane copy offsets hold two tiles pieces");
+  // 16 lanes read 16 rows at one chunk index: distinct bank groups
+  static __device__ __forceinline__ int kswz(int r) { return (r / RPB) & (CH - 1); }
+  // transposing reads take 4 rows x 64 bytes: distinct 64-byte groups
+  static __device__ __forceinline__ int vswz(int r) { return ((r / RPB) % (4 / RPB)) << 2; }
+};
+
+__device__ __forceinline__ bf16x8 lds_b128(const lds_char* p) { return *(const __attribute__((address_space(3))) bf16x8*)p; }
+__device__ __forceinline__ s16x4 lds_tr(const lds_char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p);
+}
+__device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float pair_max(float v) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  const float a = __uint_as_float(r[0]), b = __uint_as_float(r[1]);
+  return a > b ? a : b;
+}
+__device__ __forceinline__ float pair_sum(float v) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+template <int D, int MODE, bool OUT_BF16>
+__global__ __launch_bounds__(256, 3) void flash_tiled_kernel(FwdParams p, int hpw) {
+  using C = TCfg<D>;
+  lds_char* const ka = (lds_char*)ft_ka;
+  lds_char* const kb = (lds_char*)ft_kb;
+  lds_char* const va = (lds_char*)ft_va;
+  lds_char* const vb = (lds_char*)ft_vb;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 5, ql = lane & 31;
+  const int nqb = 4 / hpw;
+
+  // (batch, head group, query tile): XCD-contiguous ranges; within a range the
+  // query tiles of a head group run from the last (heaviest for causal) down.
+  const int64_t nblk = (int64_t)gridDim.x * gridDim.y * gridDim.z;
+  const int64_t lin = blockIdx.x + (int64_t)gridDim.x * (blockIdx.y + (int64_t)gridDim.y * blockIdx.z);
+  const int64_t per = nblk / 8, rem = nblk % 8, xcd = lin % 8;
+  const int64_t lid = xcd * per + min(xcd, rem) + lin / 8;
+  const int64_t bx = lid % gridDim.x, hgrp = (lid / gridDim.x) % gridDim.y, b = lid / ((int64_t)gridDim.x * gridDim.y);
+  const int64_t qtile = (MODE == T_INDEX) ? (int64_t)gridDim.x - 1 - bx : bx;
+  const int64_t h = hgrp * hpw + (wave % hpw);
+  const int64_t hk = h / (p.Hq / p.Hkv);
+  const int64_t wg_q0 = qtile * 32 * nqb;
+  const int64_t wg_q1 = min(wg_q0 + 32 * nqb, p.Tq) - 1;
+  const int64_t wq0 = wg_q0 + 32 * (wave / hpw);
+  const int64_t wq1 = min(wq0 + 31, p.Tq - 1);
+  const int64_t qrow = wq0 + ql;
+  const bool qvalid = qrow < p.Tq;
+
+  const __bf16* qp = (const __bf16*)p.q + b * p.q_sb + h * p.q_sh;
+  bf16x8 qf[C::QC];
+#pragma unroll
+  for (int c = 0; c < C::QC; ++c) qf[c] = qvalid ? *(const bf16x8*)(qp + qrow * p.q_st + c * 16 + 8 * g) : (bf16x8){};
+  const float c2 = p.scale * kLog2e;
+
+  // Key tiles of the workgroup.
+  int64_t lo = 0, hi = p.Tkv;
+  if (MODE == T_INDEX) {
+    hi = min(hi, wg_q1 + p.offset + 1);
+    if (p.bias == BIAS_SLIDING) lo = max((int64_t)0, wg_q0 + p.offset - p.window + 1);
+  }
+  const int tlo = (int)(lo / BN);
+  const int thi = hi > lo ? (int)((hi + BN - 1) / BN) : tlo;
+  // Allowed key interval of this lane's query: lim_lo < key <= lim_hi.
+  int lim_hi = (int)(p.Tkv - 1), lim_lo = -1;
+  if (MODE == T_INDEX) {
+    lim_hi = (int)max(min(qrow + p.offset, p.Tkv - 1), (int64_t)-2);
+    if (p.bias == BIAS_SLIDING) lim_lo = (int)min(max(qrow + p.offset - p.window, (int64_t)-1), p.Tkv);
+  }
+
+  // LDS-direct copies: every wave issues C::NI of the 1 KB pieces of each tile.
+  const char* kbase = (const char*)((const __bf16*)p.k + b * p.k_sb + hk * p.k_sh);
+  const char* vbase = (const char*)((const __bf16*)p.v + b * p.k_sb + hk * p.k_sh);
+  const int rstride = (int)(p.k_st * 2);
+  const int64_t span = ((p.Tkv - 1) * p.k_st + D) * 2;
+  int kvo[2], vvo[2];                   // C::NI <= 2 (a dependent bound here breaks the host-side lambda capture)
+#pragma unroll
+  for (int j = 0; j < C::NI; ++j) {
+    const int L = 64 * (wave + 4 * j) + lane, row = L / C::CH, pos = L % C::CH;
+    kvo[j] = row * rstride + ((pos ^ C::kswz(row)) << 4);
+    vvo[j] = row * rstride + ((pos ^ C::vswz(row)) << 4);
+  }
+  auto stage = [&](int t, auto par) {
+    constexpr int PAR = decltype(par)::value;
+    const int64_t tb = (int64_t)t * BN * rstride;
+    const int nrec = (int)max((int64_t)0, min(span - tb, (int64_t)0x7fffffff));
+    const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)(kbase + tb), 0, nrec, 0x00020000);
+    const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)(vbase + tb), 0, nrec, 0x00020000);
+#pragma unroll
+    for (int j = 0; j < C::NI; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (__attribute__((address_space(3))) void*)((PAR ? kb : ka) + 1024 * (wave + 4 * j)),
+                                               16, kvo[j], 0, 0, 0);
+#pragma unroll
+    for (int j = 0; j < C::NI; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (__attribute__((address_space(3))) void*)((PAR ? vb : va) + 1024 * (wave + 4 * j)),
+                                               16, vvo[j], 0, 0, 0);
+  };
+
+  const int j16 = lane & 15, dh = (lane >> 4) & 1;
+  int vro[2][C::DB];
+#pragma unroll
+  for (int tc = 0; tc < 2; ++tc)
+#pragma unroll
+    for (int d = 0; d < C::DB; ++d) {
+      const int row0 = 16 * tc + 4 * g + (j16 >> 2);
+      vro[tc][d] = row0 * C::ROWB + ((((4 * d + 2 * dh + ((j16 & 3) >> 1)) ^ C::vswz(row0)) << 4) + ((j16 & 1) << 3));
+    }
+  int kro[C::QC];
+#pragma unroll
+  for (int c = 0; c < C::QC; ++c) kro[c] = ql * C::ROWB + (((2 * c + g) ^ C::kswz(ql)) << 4);
+
+  f32x16 o[C::DB];
+#pragma unroll
+  for (int d = 0; d < C::DB; ++d) o[d] = (f32x16){};
+  float m = -INFINITY, l = 0.0f;
+
+  auto step = [&](int t, auto par) {
+    constexpr int PAR = decltype(par)::value;
+    const int64_t k0 = (int64_t)t * BN;
+    if (MODE == T_INDEX) {       // nothing allowed for this wave's rows: skip
+      if (k0 > wq1 + p.offset) return;
+      if (p.bias == BIAS_SLIDING && k0 + BN - 1 <= wq0 + p.offset - p.window) return;
+    }
+    const lds_char* ks = PAR ? kb : ka;
+    const lds_char* vs = PAR ? vb : va;
+    f32x16 s = (f32x16){};
+#pragma unroll
+    for (int c = 0; c < C::QC; ++c) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(ks + kro[c]), qf[c], s, 0, 0, 0);
+    bool partial = k0 + BN > p.Tkv;
+    if (MODE == T_INDEX) {
+      if (k0 + BN - 1 > wq0 + p.offset) partial = true;
+      if (p.bias == BIAS_SLIDING && k0 <= wq1 + p.offset - p.window) partial = true;
+    }
+    if (partial) {
+      asm volatile("" ::: "memory");     // keep a real branch: full tiles skip the mask
+      const int kl0 = (int)k0 + 4 * g;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = kl0 + 8 * (i / 4) + (i % 4);
+        s[i] = (key <= lim_hi && key > lim_lo) ? s[i] : -INFINITY;
+      }
+    }
+    bf16x8 pb[2];
+    auto probs = [&](float off) -> float {
+      float acc0 = 0.0f, acc1 = 0.0f;
+#pragma unroll
+      for (int tc = 0; tc < 2; ++tc) {
+        bf16x2 pk[4];
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const f32x2 pp = {fexp2(fmaf(s[8 * tc + e], c2, off)), fexp2(fmaf(s[8 * tc + e + 1], c2, off))};
+          pk[e / 2] = __builtin_convertvector(pp, bf16x2);
+          if (e & 2) acc1 = __builtin_amdgcn_fdot2_f32_bf16(pk[e / 2], (bf16x2){(__bf16)1.0f, (__bf16)1.0f}, acc1, false);
+          else acc0 = __builtin_amdgcn_fdot2_f32_bf16(pk[e / 2], (bf16x2){(__bf16)1.0f, (__bf16)1.0f}, acc0, false);
+        }
+        pb[tc] = __builtin_shufflevector(__builtin_shufflevector(pk[0], pk[1], 0, 1, 2, 3),
+                                         __builtin_shufflevector(pk[2], pk[3], 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
+      }
+      return acc0 + acc1;
+    };
+    float lt = probs((m == -INFINITY) ? 0.0f : -m);
+    if (__builtin_expect(__any(!(lt <= kTauSum) || m == -INFINITY), 0)) {
+      float smax = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+#pragma unroll
+      for (int i = 4; i < 16; i += 2) smax = fmaxf(smax, fmaxf(s[i], s[i + 1]));
+      smax = pair_max(smax);
+      const float tmax = smax * c2;
+      const bool need = tmax > m + kTau;
+      const float mn = need ? tmax : m;
+      const float alpha = need ? ((m == -INFINITY) ? 0.0f : fexp2(m - mn)) : 1.0f;
+      m = mn;
+      l *= alpha;
+#pragma unroll
+      for (int d = 0; d < C::DB; ++d)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[d][i] *= alpha;
+      lt = probs((m == -INFINITY) ? 0.0f : -m);
+    }
+    l += lt;
+#pragma unroll
+    for (int tc = 0; tc < 2; ++tc)
+#pragma unroll
+      for (int d = 0; d < C::DB; ++d) {
+        const s16x4 lo4 = lds_tr(vs + vro[tc][d]);
+        const s16x4 hi4 = lds_tr(vs + vro[tc][d] + 8 * C::ROWB);
+        const s16x8 a8 = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+        o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a8), pb[tc], o[d], 0, 0, 0);
+      }
+  };
+
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
+  if (tlo < thi) stage(tlo, P0{});
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int t = tlo; t < thi; t += 2) {
+    if (t + 1 < thi) stage(t + 1, P1{});
+    step(t, P0{});
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (t + 1 < thi) {
+      if (t + 2 < thi) stage(t + 2, P0{});
+      step(t + 1, P1{});
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    }
+  }
+
+  const float lt = pair_sum(l);
+  const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+  if (!qvalid) return;
+  const int64_t ob = b * p.q_sb + h * p.q_sh + qrow * p.q_st;
+#pragma unroll
+  for (int d = 0; d < C::DB; ++d)
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      const int dd = d * 32 + 8 * i4 + 4 * g;
+      if (OUT_BF16) {
+        bf16x4 vb4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) vb4[e] = (__bf16)(o[d][4 * i4 + e] * inv);
+        *(bf16x4*)((__bf16*)p.o + ob + dd) = vb4;
+      } else {
+        f32x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = o[d][4 * i4 + e] * inv;
+        *(f32x4*)((float*)p.o + ob + dd) = v;
+      }
+    }
+  if (p.lse && g == 0) p.lse[(b * p.Hq + h) * p.Tq + qrow] = lt > 0.0f ? (m + __log2f(lt)) * kLn2 : -INFINITY;
+}
+
+template <int D, int MODE>
+hipError_t launch_t(const FwdParams& p, hipStream_t s) {
+  const int64_t grp = p.Hq / p.Hkv;
+  const int hpw = (grp % 4 == 0) ? 4 : (grp % 2 == 0) ? 2 : 1;
+  const int64_t rows = 32 * (4 / hpw);
+  dim3 grid((unsigned)((p.Tq + rows - 1) / rows), (unsigned)(p.Hq / hpw), (unsigned)p.B);
+  if (p.out_dtype == 1) hipLaunchKernelGGL((flash_tiled_kernel<D, MODE, true>), grid, dim3(256), 0, s, p, hpw);
+  else hipLaunchKernelGGL((flash_tiled_kernel<D, MODE, false>), grid, dim3(256), 0, s, p, hpw);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool tiled_supports(const FwdParams& p) {
+  if (p.dtype != 1 || (p.D != 64 && p.D != 128) || p.num_splits != 1) return false;
+  if (p.bias != BIAS_NONE && p.bias != BIAS_CAUSAL && p.bias != BIAS_SLIDING) return false;
+  if ((int64_t)BN * p.k_st * 2 > 0x7fffffffLL) return false;     // 32-bit byte offsets within a tile
+  if (p.B > 65535 || p.Hq > 65535 || (p.Tq + 31) / 32 > 0x7fffffffLL) return false;   // grid limits
+  if (p.Tkv > 0x3fffffffLL) return false;                         // key indices in 32-bit lanes
+  return true;
+}
+
+hipError_t launch_tiled(const FwdParams& p, hipStream_t s) {
+  const bool idx = p.bias == BIAS_CAUSAL || p.bias == BIAS_SLIDING;
+  if (p.D == 64) return idx ? launch_t<64, T_INDEX>(p, s) : launch_t<64, T_NONE>(p, s);
+  return idx ? launch_t<128, T_INDEX>(p, s) : launch_t<128, T_NONE>(p, s);
+}
+
+}  // namespace sdpa

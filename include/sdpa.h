@@ -154,7 +154,9 @@ int sdpa_relpos_fwd(const void* q, const void* k, const void* v, void* o,
 /*
  * 1 if sdpa_relpos_fwd with these parameters forms the rel-pos terms inside
  * the attention kernel (a single kernel launch, no term arrays), 0 if it
- * first runs relpos_terms into the workspace.  Pure host logic, no HIP call.
+ * first runs relpos_terms into the workspace.  Holds for a positive finite
+ * scale; any other scale always takes the two-launch route.  Pure host logic,
+ * no HIP call.
  */
 int sdpa_relpos_fused(int dtype, int64_t D, int64_t grid_h, int64_t grid_w);
 
@@ -171,6 +173,9 @@ const char* sdpa_last_error(void);
  *   "split_halves" 1 (default) = for head_dim 64 with few query rows, each
  *                  workgroup splits the key range between its waves and merges
  *                  the halves; 0 = always one key range per wave.
+ *   "tiled"        1 (default) = bf16 head_dim 64 / 128 attention with no mask
+ *                  or a causal / sliding mask runs on the double-buffered
+ *                  kernel; 0 = on the general MFMA kernel.
  *   "relpos_fused" 1 (default) = sdpa_relpos_fwd forms the rel-pos terms
  *                  inside the attention kernel where the grid allows it;
  *                  0 = always run relpos_terms into the workspace first.

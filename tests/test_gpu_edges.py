@@ -263,11 +263,55 @@ def test_running_max_paths(gpu, pattern, D):
     else:
         k = k * 40.0
     q, k, v = (x.to(torch.bfloat16) for x in (q, k, v))
-    for halves in (0, 1):
+    ref = oracle.sdpa(np64(q), np64(k), np64(v), scale=1.0 / D ** 0.5)
+    for halves, tiled in ((0, 0), (0, 1), (1, 1)):
         gpu.set_tuning("split_halves", halves)
+        gpu.set_tuning("tiled", tiled)
         try:
             o = gpu.sdpa(q.cuda(), k.cuda(), v.cuda(), scale=1.0 / D ** 0.5, out_dtype=torch.float32)
         finally:
             gpu.set_tuning("split_halves", 1)
-        ref = oracle.sdpa(np64(q), np64(k), np64(v), scale=1.0 / D ** 0.5)
-        assert max_err(np64(o), ref["o"]) <= TOL["bf16"], (pattern, halves)
+            gpu.set_tuning("tiled", 1)
+        assert max_err(np64(o), ref["o"]) <= TOL["bf16"], (pattern, halves, tiled)
+
+
+@pytest.mark.parametrize("tiled", [0, 1])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("mask", [None, {"kind": "causal", "offset": 0}, {"kind": "causal", "offset": 37},
+                                  {"kind": "sliding", "window": 45, "offset": -3}])
+@pytest.mark.parametrize("Hq,Hkv", [(8, 2), (6, 3), (3, 3)])
+def test_long_range_kernels(gpu, tiled, D, mask, Hq, Hkv):
+    """The double-buffered kernel (4, 2 or 1 query heads per workgroup sharing
+    a KV head) and the general MFMA kernel on the same masked, ragged inputs:
+    several query blocks, key tiles skipped outside the band, partial tiles on
+    both band edges and at the end of the key range."""
+    gpu.set_tuning("split_halves", 0)
+    gpu.set_tuning("tiled", tiled)
+    try:
+        for layout in ("bhsd", "bshd"):
+            check(gpu, 2, Hq, Hkv, 261, 299, D, layout=layout, mask=mask, seed=D + Hq)
+    finally:
+        gpu.set_tuning("split_halves", 1)
+        gpu.set_tuning("tiled", 1)
+
+
+@pytest.mark.parametrize("scale", [-0.125, 0.0])
+@pytest.mark.parametrize("mask", [None, {"kind": "causal", "offset": 0}])
+def test_non_positive_scale(gpu, scale, mask):
+    """A negative scale flips which key scores highest; a zero scale averages
+    the allowed values.  Both follow the plain definition."""
+    check(gpu, 1, 4, 2, 70, 90, 64, mask=mask, scale=scale, seed=11)
+    check(gpu, 1, 4, 2, 70, 90, 128, mask=mask, scale=scale, seed=12)
+
+
+def test_relpos_non_positive_scale(gpu):
+    """Rel-pos attention with a negative scale runs the two-launch route and
+    still matches the definition (the bias itself is never scaled)."""
+    wl = workloads.replica("sam_global_relpos", B=1, Hq=2, Hkv=2, Tq=192, Tkv=192, grid=(3, 64), scale=-0.2)
+    x = workloads.generate(wl, seed=5, layout="bhsd")
+    g = {k: v.cuda() for k, v in x.items()}
+    o = gpu.sdpa_relpos(g["q"], g["k"], g["v"], g["rel_pos_h"], g["rel_pos_w"], wl.grid, scale=wl.scale,
+                        out_dtype=torch.float32)
+    ref = oracle.sdpa(np64(x["q"]), np64(x["k"]), np64(x["v"]), scale=wl.scale,
+                      rel_pos={"rel_pos_h": np64(x["rel_pos_h"]), "rel_pos_w": np64(x["rel_pos_w"]), "grid": wl.grid})
+    assert max_err(np64(o), ref["o"]) <= TOL["bf16"]
