@@ -80,6 +80,8 @@ def load():
         lib.sdpa_status_string.argtypes = [_I32]
         lib.sdpa_last_error.restype = ctypes.c_char_p
         lib.sdpa_last_error.argtypes = []
+        lib.sdpa_last_kernel.restype = ctypes.c_char_p
+        lib.sdpa_last_kernel.argtypes = []
         lib.sdpa_set_tuning.restype = _I32
         lib.sdpa_set_tuning.argtypes = [ctypes.c_char_p, _I64]
         lib.sdpa_relpos_fused.restype = _I32
@@ -112,8 +114,13 @@ def _stream(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def last_kernel():
+    """Name of the attention kernel the last successful call on this thread launched."""
+    return load().sdpa_last_kernel().decode()
+
+
 def set_tuning(key, value):
-    """Process-wide knob: "num_splits" (0 = auto) or "relpos_fused" (0/1)."""
+    """Process-wide knob: "num_splits" (0 = auto), "split_halves", "tiled" or "relpos_fused" (0/1)."""
     _check(load().sdpa_set_tuning(key.encode(), int(value)), "sdpa_set_tuning")
 
 

@@ -34,7 +34,7 @@ def hipcc():
 # Per-file extra flags.  The MFMA attention kernels take row maxima of scores
 # produced by the matrix cores; without NaN honouring the maxima need no
 # quieting moves (NaN scores still reach the output through exp and P.V).
-EXTRA = {f: ["-fno-honor-nans"] for f in ("flash_mfma.hip", "flash_split64.hip", "flash_tiled.hip")}
+EXTRA = {f: ["-fno-honor-nans"] for f in ("flash_mfma.hip", "flash_split64.hip", "flash_tiled.hip", "flash_window.hip")}
 
 
 def _compile(src):

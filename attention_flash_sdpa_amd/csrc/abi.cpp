@@ -17,6 +17,7 @@
 namespace {
 
 thread_local std::string g_last_error;
+thread_local const char* g_last_kernel = "";
 std::atomic<int64_t> g_num_splits{0};
 std::atomic<int64_t> g_relpos_fused{1};
 std::atomic<int64_t> g_split64{1};
@@ -49,11 +50,13 @@ int plan_splits(int64_t B, int64_t Hq, int64_t Tq, int64_t Tkv, int64_t D, int d
   if (!sdpa::kSplitKvBuilt || dtype != SDPA_BF16 || D != 16 || Tq > 8) return 1;
   const int64_t forced = g_num_splits.load();
   if (forced >= 1) return (int)std::min<int64_t>(forced, std::max<int64_t>(1, (Tkv + 63) / 64));
-  const int64_t row_blocks = B * Hq * ((Tq + 31) / 32);
-  if (row_blocks >= 256 || Tkv < 512) return 1;
-  int64_t s = 512 / row_blocks;                          // aim at ~2 workgroups per CU
-  s = std::min<int64_t>(s, (Tkv + 127) / 128);           // keep >= 128 keys per chunk
-  return (int)std::max<int64_t>(1, std::min<int64_t>(s, 64));
+  // one wave per (4 heads, 8 queries, key chunk): aim at ~512 waves with
+  // chunks of >= 64 keys (two tiles: the loads of the second overlap the first)
+  const int64_t waves = B * ((Hq + 3) / 4) * ((Tq + 7) / 8);
+  if (waves >= 512 || Tkv <= 64) return 1;
+  int64_t s = (512 + waves - 1) / waves;
+  s = std::min<int64_t>(s, (Tkv + 63) / 64);
+  return (int)std::max<int64_t>(1, std::min<int64_t>(s, 1024));
 }
 
 size_t split_bytes(int splits, int64_t B, int64_t Hq, int64_t Tq, int64_t D) {
@@ -107,18 +110,23 @@ int launch(const sdpa::FwdParams& p, hipStream_t s) {
   // The MFMA kernels take each row's running max on scores already multiplied
   // by scale, which needs scale > 0; other scales run on the generic kernel.
   const bool fast = p.scale > 0.0f && std::isfinite(p.scale);
-  if (!fast) e = sdpa::launch_generic_fwd(p, s);
-  else if (sdpa::d16_supports(p)) e = sdpa::launch_d16(p, s);
-  else if (g_split64.load() && sdpa::split64_supports(p)) e = sdpa::launch_split64(p, s);
-  else if (g_tiled.load() && sdpa::tiled_supports(p)) e = sdpa::launch_tiled(p, s);
-  else if (sdpa::flash_mfma_supports(p)) e = sdpa::launch_flash_mfma(p, s);
-  else e = sdpa::launch_generic_fwd(p, s);
+  const char* name;
+  if (!fast) { name = "generic_fwd_kernel"; e = sdpa::launch_generic_fwd(p, s); }
+  else if (sdpa::d16_supports(p)) {
+    name = p.Tq <= 8 ? "d16_qpack_kernel" : "d16_kpack_kernel";
+    e = sdpa::launch_d16(p, s);
+  } else if (sdpa::window_supports(p)) { name = "flash_window_kernel"; e = sdpa::launch_window(p, s); }
+  else if (g_split64.load() && sdpa::split64_supports(p)) { name = "flash_split64_kernel"; e = sdpa::launch_split64(p, s); }
+  else if (g_tiled.load() && sdpa::tiled_supports(p)) { name = "flash_tiled_kernel"; e = sdpa::launch_tiled(p, s); }
+  else if (sdpa::flash_mfma_supports(p)) { name = "flash_mfma_kernel"; e = sdpa::launch_flash_mfma(p, s); }
+  else { name = "generic_fwd_kernel"; e = sdpa::launch_generic_fwd(p, s); }
+  g_last_kernel = name;
   if (e != hipSuccess) return fail(SDPA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return SDPA_OK;
 }
 
 bool relpos_fused_ok(const sdpa::FwdParams& p) {
-  return p.scale > 0.0f && std::isfinite(p.scale) && sdpa::relpos_fused_supported(p);
+  return p.scale > 0.0f && std::isfinite(p.scale) && (sdpa::relpos_fused_supported(p) || sdpa::window_supports(p));
 }
 
 }  // namespace
@@ -251,6 +259,10 @@ int sdpa_relpos_fused(int dtype, int64_t D, int64_t grid_h, int64_t grid_w) {
   p.Tq = p.Tkv = grid_h * grid_w;
   p.rel_h = p.rel_w = &dummy;
   p.scale = 1.0f;
+  p.B = p.Hq = p.Hkv = 1;
+  p.k_st = p.q_st = D;
+  p.num_splits = 1;
+  p.bias = sdpa::BIAS_RELPOS;
   return (g_relpos_fused.load() && grid_h > 0 && grid_w > 0 && relpos_fused_ok(p)) ? 1 : 0;
 }
 
@@ -266,6 +278,8 @@ const char* sdpa_status_string(int status) {
 }
 
 const char* sdpa_last_error(void) { return g_last_error.c_str(); }
+
+const char* sdpa_last_kernel(void) { return g_last_kernel; }
 
 int sdpa_set_tuning(const char* key, int64_t value) {
   g_last_error.clear();

@@ -39,17 +39,24 @@ __device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(
 __device__ __forceinline__ float xor32_max(float v) { return fmaxf(v, __shfl_xor(v, 32)); }
 __device__ __forceinline__ float xor32_sum(float v) { return v + __shfl_xor(v, 32); }
 
-// Allowed test for the index masks and the key range, plus tensor-mask bias.
-__device__ __forceinline__ float bias_of(const FwdParams& p, int64_t b, int64_t h, int64_t i, int64_t j, bool qok) {
-  if (!qok || j >= p.Tkv || j < 0) return -INFINITY;
-  if (!index_allowed(p.bias, i, j, p.offset, p.window)) return -INFINITY;
-  if (p.bias == BIAS_ADDITIVE || p.bias == BIAS_BOOL) return tensor_mask_bias(p, b, h, i, j);
-  return 0.0f;
+// Mask families, one kernel instance each: no mask (only the key range),
+// index masks (causal / sliding), tensor masks (additive / bool).  Keeping
+// them apart keeps each instance's code small; these kernels run few waves
+// per CU, so a large kernel waits on instruction fetch more than on anything.
+enum MaskFamily { MF_NONE = 0, MF_INDEX = 1, MF_TENSOR = 2 };
+
+template <int MF>
+__device__ __forceinline__ float bias_of(const FwdParams& p, int64_t b, int64_t h, int64_t i, int64_t j, bool ok) {
+  if (!ok) return -INFINITY;
+  if (MF == MF_NONE) return 0.0f;
+  if (MF == MF_INDEX) return index_allowed(p.bias, i, j, p.offset, p.window) ? 0.0f : -INFINITY;
+  return tensor_mask_bias(p, b, h, i, j);
 }
 
 // ------------------------------------------------------------ query packing
 // grid: (splits, ceil(Tq / 8), B * ceil(Hq / 4)); one wave per block.
 // Lane column n = lane % 32 holds head hh = n / 8 of the group and query t = n % 8.
+template <int MF>
 __global__ __launch_bounds__(64) void d16_qpack_kernel(FwdParams p, int keys_per_split) {
   __shared__ __attribute__((aligned(16))) __bf16 vl[4][32][16];     // V tile: [head][key][d]
   const int lane = threadIdx.x, g = lane >> 5, n = lane & 31;
@@ -66,48 +73,62 @@ __global__ __launch_bounds__(64) void d16_qpack_kernel(FwdParams p, int keys_per
 
   // Q'^T operands: chunk c carries head h0 + c, nonzero only in that head's columns.
   bf16x8 qb[4];
+  {
+    bf16x8 qv = (bf16x8){};
+    if (colok) qv = *(const bf16x8*)((const __bf16*)p.q + b * p.q_sb + hcol * p.q_sh + qcol * p.q_st + 8 * g);
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    qb[c] = (bf16x8){};
-    if (c == hh && colok) qb[c] = *(const bf16x8*)((const __bf16*)p.q + b * p.q_sb + hcol * p.q_sh + qcol * p.q_st + 8 * g);
+    for (int c = 0; c < 4; ++c) qb[c] = (c == hh) ? qv : (bf16x8){};
   }
   const float c2 = p.scale * kLog2e;
   f32x16 o[2] = {(f32x16){}, (f32x16){}};
   float m = -INFINITY, l = 0.0f;
 
-  for (int64_t k0 = kbeg; k0 < kend; k0 += 32) {
-    // K' operands: row = key k0 + (lane % 32), chunk c = head h0 + c, dims 8g..8g+7.
-    const int64_t key = k0 + n;
-    bf16x8 ka[4];
+  // Tile loads go out one tile ahead: K' operands straight to registers, V as
+  // 16-byte pieces that pass through LDS for the transposed operand.
+  //   K' row = key k0 + (lane % 32), chunk c = head h0 + c, dims 8g..8g+7.
+  //   V piece e = lane + 64r: [head r][key (lane/2)%32][half lane%2].
+  // Head bases are loop invariant; heads past Hq read nothing.
+  const __bf16* kh[4];
+  const __bf16* vh[4];
+  bool hok[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    hok[c] = h0 + c < p.Hq;
+    const int64_t hk = (hok[c] ? h0 + c : h0) / grp;
+    kh[c] = (const __bf16*)p.k + b * p.k_sb + hk * p.k_sh + 8 * g;
+    vh[c] = (const __bf16*)p.v + b * p.k_sb + hk * p.k_sh + 8 * (lane & 1);
+  }
+  const int vkk = (lane >> 1) & 31;
+  auto load_tile = [&](int64_t k0, bf16x8 (&ka)[4], bf16x8 (&vv)[4]) {
+    const int64_t key = k0 + n, kj = k0 + vkk;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       ka[c] = (bf16x8){};
-      const int64_t hc = h0 + c;
-      if (hc < p.Hq && key < kend)
-        ka[c] = *(const bf16x8*)((const __bf16*)p.k + b * p.k_sb + (hc / grp) * p.k_sh + key * p.k_st + 8 * g);
+      if (hok[c] && key < kend) ka[c] = *(const bf16x8*)(kh[c] + key * p.k_st);
+      vv[c] = (bf16x8){};
+      if (hok[c] && kj < kend) vv[c] = *(const bf16x8*)(vh[c] + kj * p.k_st);
     }
-    // Stage V for the 4 heads: 4 x 32 keys x 16 dims; lane -> (head, key pair).
-    __syncthreads();
+  };
+  bf16x8 ka[4], vv[4];
+  if (kbeg < kend) load_tile(kbeg, ka, vv);
+  for (int64_t k0 = kbeg; k0 < kend; k0 += 32) {
+    __syncthreads();                 // previous tile's V reads are done
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int e = lane + 64 * r;            // 256 16-byte pieces: [head 4][key 32][half 2]
-      const int hv = e >> 6, kk = (e >> 1) & 31, half = e & 1;
-      const int64_t hc = h0 + hv, kj = k0 + kk;
-      bf16x8 v = (bf16x8){};
-      if (hc < p.Hq && kj < kend)
-        v = *(const bf16x8*)((const __bf16*)p.v + b * p.k_sb + (hc / grp) * p.k_sh + kj * p.k_st + 8 * half);
-      *(bf16x8*)&vl[hv][kk][8 * half] = v;
+      const int e = lane + 64 * r;
+      *(bf16x8*)&vl[e >> 6][(e >> 1) & 31][8 * (e & 1)] = vv[r];
     }
     f32x16 s = (f32x16){};
 #pragma unroll
     for (int c = 0; c < 4; ++c) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[c], qb[c], s, 0, 0, 0);
+    if (k0 + 32 < kend) load_tile(k0 + 32, ka, vv);
     // Scores -> log2 units with masks.
     float x[16];
     float tmax = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int64_t kj = k0 + 8 * (i / 4) + 4 * g + (i % 4);
-      const float bb = (kj < kend) ? bias_of(p, b, hcol, qcol, kj, colok) : -INFINITY;
+      const float bb = bias_of<MF>(p, b, hcol, qcol, kj, colok && kj < kend);
       x[i] = (bb == -INFINITY) ? -INFINITY : fmaf(s[i], c2, bb * kLog2e);
       tmax = fmaxf(tmax, x[i]);
     }
@@ -131,7 +152,7 @@ __global__ __launch_bounds__(64) void d16_qpack_kernel(FwdParams p, int keys_per
         l += pv;
         pb[kc][e] = (__bf16)pv;
       }
-    __syncthreads();
+    __syncthreads();                 // V tile visible to every lane
     // V'^T operands: rows (head 2*rb + (n/16), d = n % 16); element e <-> key
     // 16*kc + 8*(e/4) + 4*g + e%4 (the order the score registers hold keys in).
 #pragma unroll
@@ -145,93 +166,106 @@ __global__ __launch_bounds__(64) void d16_qpack_kernel(FwdParams p, int keys_per
         o[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[kc], o[rb], 0, 0, 0);
       }
   }
-  // Lane (hh, t) keeps the O^T rows of its own head: block rb = hh / 2, rows
-  // 16 * (hh % 2) + d.  Registers i with 8*(i/4) + 4g + i%4 in that range.
+  // Lane (hh, t) keeps the O^T rows of its own head: block hh / 2, rows
+  // 16 * (hh % 2) + d, i.e. registers 8 * (hh % 2) + 4j + e, d = 8j + 4g + e.
   const float lt = xor32_sum(l);
-  const int rb = hh >> 1, base = 16 * (hh & 1);
   if (!colok) return;
+  float ov[8];
+  {
+    const f32x16 blk = (hh >> 1) ? o[1] : o[0];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ov[i] = (hh & 1) ? blk[8 + i] : blk[i];
+  }
   if (p.num_splits > 1) {
     // partial: unnormalised O and (m, l) of this key chunk
     const int64_t row = ((int64_t)split * p.B + b) * p.Hq * p.Tq + hcol * p.Tq + qcol;
     float* po = p.part_o + row * 16;
 #pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4) {
-      const int r0 = 8 * i4 + 4 * g;
-      if (r0 >= base && r0 < base + 16) {
-        f32x4 v;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = o[rb][4 * i4 + e];
-        *(f32x4*)(po + r0 - base) = v;
-      }
-    }
-    if (g == 0) {
-      p.part_ml[row * 2 + 0] = m;
-      p.part_ml[row * 2 + 1] = lt;
-    }
+    for (int j = 0; j < 2; ++j) *(f32x4*)(po + 8 * j + 4 * g) = (f32x4){ov[4 * j], ov[4 * j + 1], ov[4 * j + 2], ov[4 * j + 3]};
+    if (g == 0) *(float2*)(p.part_ml + row * 2) = make_float2(m, lt);
     return;
   }
   const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
   const int64_t ob = b * p.q_sb + hcol * p.q_sh + qcol * p.q_st;
 #pragma unroll
-  for (int i4 = 0; i4 < 4; ++i4) {
-    const int r0 = 8 * i4 + 4 * g;
-    if (r0 >= base && r0 < base + 16) {
-      if (p.out_dtype == 1) {
-        bf16x4 v;
+  for (int j = 0; j < 2; ++j) {
+    if (p.out_dtype == 1) {
+      bf16x4 v;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = (__bf16)(o[rb][4 * i4 + e] * inv);
-        *(bf16x4*)((__bf16*)p.o + ob + r0 - base) = v;
-      } else {
-        f32x4 v;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = o[rb][4 * i4 + e] * inv;
-        *(f32x4*)((float*)p.o + ob + r0 - base) = v;
-      }
+      for (int e = 0; e < 4; ++e) v[e] = (__bf16)(ov[4 * j + e] * inv);
+      *(bf16x4*)((__bf16*)p.o + ob + 8 * j + 4 * g) = v;
+    } else {
+      *(f32x4*)((float*)p.o + ob + 8 * j + 4 * g) =
+          (f32x4){ov[4 * j] * inv, ov[4 * j + 1] * inv, ov[4 * j + 2] * inv, ov[4 * j + 3] * inv};
     }
   }
   if (p.lse && g == 0) p.lse[(b * p.Hq + hcol) * p.Tq + qcol] = lt > 0.0f ? (m + __log2f(lt)) * kLn2 : -INFINITY;
 }
 
-// Merge split-KV partials in a fixed order: O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s.
-// One thread per (b, h, query) row.
+// Merge split-KV partials: O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s.
+// One wave per (b, h, query) row, lanes over chunks: each lane folds the
+// chunks s = lane, lane + 64, ... in order, then the lanes meet in a fixed
+// butterfly, so the result does not depend on timing.  Every load of a row
+// is issued at once (one memory round trip for up to 64 chunks).
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int k = 32; k >= 1; k >>= 1) v = fmaxf(v, __shfl_xor(v, k));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int k = 32; k >= 1; k >>= 1) v += __shfl_xor(v, k);
+  return v;
+}
+
 __global__ __launch_bounds__(256) void d16_combine_kernel(FwdParams p) {
   const int64_t rows = p.B * p.Hq * p.Tq;
-  const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (r >= rows) return;
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (r >= rows) return;                       // whole waves leave together
   const int S = p.num_splits;
-  float M = -INFINITY;
-  for (int s = 0; s < S; ++s) M = fmaxf(M, p.part_ml[((int64_t)s * rows + r) * 2]);
-  float acc[16];
+  float ml = -INFINITY, ll = 0.0f, acc[16];
 #pragma unroll
   for (int d = 0; d < 16; ++d) acc[d] = 0.0f;
-  float L = 0.0f;
-  if (M != -INFINITY) {
-    for (int s = 0; s < S; ++s) {
-      const int64_t sr = (int64_t)s * rows + r;
-      const float ms = p.part_ml[sr * 2];
-      if (ms == -INFINITY) continue;
-      const float w = fexp2(ms - M);
-      L = fmaf(w, p.part_ml[sr * 2 + 1], L);
-      const f32x4* po = (const f32x4*)(p.part_o + sr * 16);
+  for (int sp = lane; sp < S; sp += 64) {
+    const int64_t sr = (int64_t)sp * rows + r;
+    const float2 mls = *(const float2*)(p.part_ml + sr * 2);
+    const f32x4* po = (const f32x4*)(p.part_o + sr * 16);
+    f32x4 v[4];
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const f32x4 v = po[q4];
+    for (int q4 = 0; q4 < 4; ++q4) v[q4] = po[q4];
+    if (mls.x == -INFINITY) continue;
+    const float mn = fmaxf(ml, mls.x);
+    const float a = (ml == -INFINITY) ? 0.0f : fexp2(ml - mn), w = fexp2(mls.x - mn);
+    ml = mn;
+    ll = fmaf(w, mls.y, ll * a);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc[4 * q4 + e] = fmaf(w, v[e], acc[4 * q4 + e]);
-      }
-    }
+    for (int q4 = 0; q4 < 4; ++q4)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[4 * q4 + e] = fmaf(w, v[q4][e], acc[4 * q4 + e] * a);
   }
+  const float M = wave_max(ml);
+  const float w = (ml == -INFINITY) ? 0.0f : fexp2(ml - M);
+  const float L = wave_sum(w * ll);
+#pragma unroll
+  for (int d = 0; d < 16; ++d) acc[d] = wave_sum(w * acc[d]);
+  if (lane != 0) return;
   const float inv = L > 0.0f ? 1.0f / L : 0.0f;
   const int64_t b = r / (p.Hq * p.Tq), h = (r / p.Tq) % p.Hq, i = r % p.Tq;
   const int64_t ob = b * p.q_sb + h * p.q_sh + i * p.q_st;
   if (p.out_dtype == 1) {
-    __bf16* op = (__bf16*)p.o + ob;
+    bf16x8 v0, v1;
 #pragma unroll
-    for (int d = 0; d < 16; ++d) op[d] = (__bf16)(acc[d] * inv);
+    for (int d = 0; d < 8; ++d) {
+      v0[d] = (__bf16)(acc[d] * inv);
+      v1[d] = (__bf16)(acc[d + 8] * inv);
+    }
+    *(bf16x8*)((__bf16*)p.o + ob) = v0;
+    *(bf16x8*)((__bf16*)p.o + ob + 8) = v1;
   } else {
-    float* op = (float*)p.o + ob;
+    f32x4* op = (f32x4*)((float*)p.o + ob);
 #pragma unroll
-    for (int d = 0; d < 16; ++d) op[d] = acc[d] * inv;
+    for (int q4 = 0; q4 < 4; ++q4) op[q4] = (f32x4){acc[4 * q4] * inv, acc[4 * q4 + 1] * inv, acc[4 * q4 + 2] * inv, acc[4 * q4 + 3] * inv};
   }
   if (p.lse) p.lse[r] = L > 0.0f ? (M + __log2f(L)) * kLn2 : -INFINITY;
 }
@@ -239,6 +273,7 @@ __global__ __launch_bounds__(256) void d16_combine_kernel(FwdParams p) {
 // -------------------------------------------------------------- key packing
 // grid: (ceil(Tq / 32), B * ceil(Hq / 4)); one wave per block.  Lane column
 // n = lane % 32 is query q0 + n for all 4 heads; score rows are (head, key slot).
+template <int MF>
 __global__ __launch_bounds__(64) void d16_kpack_kernel(FwdParams p) {
   const int lane = threadIdx.x, g = lane >> 5, n = lane & 31;
   const int64_t ngrp = (p.Hq + 3) / 4;
@@ -262,20 +297,49 @@ __global__ __launch_bounds__(64) void d16_kpack_kernel(FwdParams p) {
     m[hh] = -INFINITY;
     l[hh] = 0.0f;
   }
-  for (int64_t k0 = 0; k0 < p.Tkv; k0 += 8) {
-    // K' rows (head r/8, key slot r%8): block diagonal over the 4 head chunks.
-    const int hr = n >> 3, jr = n & 7;
-    const int64_t kr = k0 + jr;
-    bf16x8 ka[4];
+  // Tile loads (K' rows and the V'^T diagonal blocks) go out one tile ahead.
+  //   K' rows (head r/8, key slot r%8): block diagonal over the 4 head chunks;
+  //   this lane loads only chunk hr = n / 8.
+  //   V'^T block rb: rows (head 2rb + n/16, d = n%16); element e <-> (head
+  //   2rb + e/4, key slot 4g + e%4); zero off the head's own slots, so this
+  //   lane loads elements 4 * (n/16) + 0..3.
+  const int hr = n >> 3, jr = n & 7, vhalf = n >> 4;
+  const bool kok = h0 + hr < p.Hq;
+  const __bf16* kbase = (const __bf16*)p.k + b * p.k_sb + ((kok ? h0 + hr : h0) / grp) * p.k_sh + 8 * g;
+  const __bf16* vbase[2];
+  bool vok[2];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      ka[c] = (bf16x8){};
-      if (c == hr && h0 + c < p.Hq && kr < p.Tkv)
-        ka[c] = *(const bf16x8*)((const __bf16*)p.k + b * p.k_sb + ((h0 + c) / grp) * p.k_sh + kr * p.k_st + 8 * g);
+  for (int rb = 0; rb < 2; ++rb) {
+    const int64_t hc = h0 + 2 * rb + vhalf;
+    vok[rb] = hc < p.Hq;
+    vbase[rb] = (const __bf16*)p.v + b * p.k_sb + ((vok[rb] ? hc : h0) / grp) * p.k_sh + (n & 15);
+  }
+  auto load_tile = [&](int64_t k0, bf16x8 (&ka)[4], bf16x8 (&va)[2]) {
+    const int64_t kr = k0 + jr;
+    bf16x8 kv = (bf16x8){};
+    if (kok && kr < p.Tkv) kv = *(const bf16x8*)(kbase + kr * p.k_st);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) ka[c] = (c == hr) ? kv : (bf16x8){};
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      __bf16 t[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int64_t kj = k0 + 4 * g + e;
+        t[e] = (vok[rb] && kj < p.Tkv) ? vbase[rb][kj * p.k_st] : (__bf16)0.0f;
+      }
+      const __bf16 z = (__bf16)0.0f;
+      va[rb] = vhalf ? (bf16x8){z, z, z, z, t[0], t[1], t[2], t[3]} : (bf16x8){t[0], t[1], t[2], t[3], z, z, z, z};
     }
+  };
+  bf16x8 ka[4], va[2];
+  load_tile(0, ka, va);
+  for (int64_t k0 = 0; k0 < p.Tkv; k0 += 8) {
     f32x16 s = (f32x16){};
 #pragma unroll
     for (int c = 0; c < 4; ++c) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[c], qb[c], s, 0, 0, 0);
+    const bf16x8 vc0 = va[0], vc1 = va[1];
+    if (k0 + 8 < p.Tkv) load_tile(k0 + 8, ka, va);
     // Registers 4hh..4hh+3 hold head hh, key slots 4g + 0..3.
     bf16x8 pb[2];
 #pragma unroll
@@ -286,7 +350,7 @@ __global__ __launch_bounds__(64) void d16_kpack_kernel(FwdParams p) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int64_t kj = k0 + 4 * g + e;
-        const float bb = (hc < p.Hq) ? bias_of(p, b, hc, q, kj, qok) : -INFINITY;
+        const float bb = bias_of<MF>(p, b, hc, q, kj, qok && hc < p.Hq && kj < p.Tkv);
         x[e] = (bb == -INFINITY) ? -INFINITY : fmaf(s[4 * hh + e], c2, bb * kLog2e);
         tmax = fmaxf(tmax, x[e]);
       }
@@ -306,21 +370,8 @@ __global__ __launch_bounds__(64) void d16_kpack_kernel(FwdParams p) {
         pb[hh >> 1][4 * (hh & 1) + e] = (__bf16)pv;
       }
     }
-    // V'^T, diagonal block rb: rows (head 2rb + n/16, d = n%16); element e <->
-    // (head 2rb + e/4, key slot 4g + e%4); zero off the head's own slots.
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-      const int hv = 2 * rb + (n >> 4), d = n & 15;
-      const int64_t hc = h0 + hv;
-      bf16x8 va = (bf16x8){};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int64_t kj = k0 + 4 * g + (e % 4);
-        if ((e >> 2) == (n >> 4) && hc < p.Hq && kj < p.Tkv)
-          va[e] = ((const __bf16*)p.v)[b * p.k_sb + (hc / grp) * p.k_sh + kj * p.k_st + d];
-      }
-      o[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[rb], o[rb], 0, 0, 0);
-    }
+    o[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vc0, pb[0], o[0], 0, 0, 0);
+    o[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vc1, pb[1], o[1], 0, 0, 0);
   }
   if (!qok) return;
   // Block rb, register i: head 2rb + i/8, d = 8*((i%8)/4) + 4g + i%4.
@@ -359,19 +410,24 @@ bool d16_supports(const FwdParams& p) {
 
 hipError_t launch_d16(const FwdParams& p, hipStream_t s) {
   const int64_t ngrp = (p.Hq + 3) / 4;
+  const int mf = p.bias == BIAS_NONE ? MF_NONE : (p.bias == BIAS_CAUSAL || p.bias == BIAS_SLIDING) ? MF_INDEX : MF_TENSOR;
   if (p.Tq <= 8) {
     const int splits = p.num_splits > 1 ? p.num_splits : 1;
     const int64_t kps = ((p.Tkv + splits - 1) / splits + 31) / 32 * 32;
     dim3 grid((unsigned)splits, (unsigned)((p.Tq + 7) / 8), (unsigned)(p.B * ngrp));
-    hipLaunchKernelGGL(d16_qpack_kernel, grid, dim3(64), 0, s, p, (int)kps);
+    if (mf == MF_NONE) hipLaunchKernelGGL(d16_qpack_kernel<MF_NONE>, grid, dim3(64), 0, s, p, (int)kps);
+    else if (mf == MF_INDEX) hipLaunchKernelGGL(d16_qpack_kernel<MF_INDEX>, grid, dim3(64), 0, s, p, (int)kps);
+    else hipLaunchKernelGGL(d16_qpack_kernel<MF_TENSOR>, grid, dim3(64), 0, s, p, (int)kps);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || splits == 1) return e;
     const int64_t rows = p.B * p.Hq * p.Tq;
-    hipLaunchKernelGGL(d16_combine_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, s, p);
+    hipLaunchKernelGGL(d16_combine_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, p);
     return hipGetLastError();
   }
   dim3 grid((unsigned)((p.Tq + 31) / 32), (unsigned)(p.B * ngrp));
-  hipLaunchKernelGGL(d16_kpack_kernel, grid, dim3(64), 0, s, p);
+  if (mf == MF_NONE) hipLaunchKernelGGL(d16_kpack_kernel<MF_NONE>, grid, dim3(64), 0, s, p);
+  else if (mf == MF_INDEX) hipLaunchKernelGGL(d16_kpack_kernel<MF_INDEX>, grid, dim3(64), 0, s, p);
+  else hipLaunchKernelGGL(d16_kpack_kernel<MF_TENSOR>, grid, dim3(64), 0, s, p);
   return hipGetLastError();
 }
 

@@ -1,0 +1,272 @@
+// Windowed attention with the decomposed rel-pos bias, for SAM's 14 x 14
+// windows (196 tokens, head_dim 64, bf16): one workgroup per (window, head),
+// the bias terms formed inside the kernel.
+//
+//   z_ij = scale * q_i . k_j + term_h[i, row(j)] + term_w[i, col(j)]
+//   term_h[i, y] = q_i . Rh[row(i) - y + 13],  term_w[i, x] = q_i . Rw[col(i) - x + 13]
+//
+// ([mlx-examples issue 1451] "segment_anything: fuse attention with
+// mx.fast.scaled_dot_product_attention", body: SAM's windowed blocks add
+// add_decomposed_rel_pos's bias to the scores of each window; [Candle PR 3280]
+// "feat(metal): SDPA with Relative Positional Embeddings & LayerNorm
+// Stability", Key Changes: the rel-pos bias enters the fused SDPA kernel.)
+//
+// Layout of the work.  Seven waves of 32 query rows cover the window's 196
+// rows; K and V of the whole window (25 KB each) are copied to LDS once by
+// buffer loads that write LDS directly.  A key tile is two grid rows (28
+// keys, padded to the 32 of the matrix op), so within a tile the key slot s
+// fixes the grid column s % 14 and the row offset s / 14:
+//   * term_w / scale depends only on (query, slot): it initialises the score
+//     accumulators, identical for every tile (slots 28..31 start at -inf);
+//   * term_h / scale depends on (query, tile, s / 14): it enters the matrix op
+//     as one extra 16-deep chunk, K' rows one-hot in s / 14 against the query's
+//     two term_h values of the tile, each split into a bf16 high and low part
+//     (so the bias keeps ~16 bits, not bf16's 8).
+// The terms come from two 32 x 32 x 64 products per wave, Q . Rh^T and
+// Q . Rw^T over all 27 table rows, followed by a skewed gather through LDS.
+#include "common.h"
+
+namespace sdpa {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) char lds_char;
+typedef __attribute__((address_space(3))) float lds_float;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kTau = 8.0f;
+
+constexpr int G = 14;                 // grid side of a window
+constexpr int T = G * G;              // tokens per window
+constexpr int NTAB = 2 * G - 1;       // rel-pos table rows
+constexpr int RPT = 32 / G;           // grid rows per key tile
+constexpr int TK = RPT * G;           // keys per tile
+constexpr int NT = G / RPT;           // key tiles
+constexpr int NW = (T + 31) / 32;     // waves (32 query rows each)
+constexpr int ROWB = 128;             // bytes per K / V row (64 bf16)
+constexpr int ROWS = (NT - 1) * TK + 32;   // LDS rows: the last tile reads 32 rows
+constexpr int PIECES = ROWS * ROWB / 1024; // 1 KB copy pieces per tensor
+static_assert(G % RPT == 0 && RPT <= 4, "tile = whole grid rows, at most 4");
+static_assert(ROWS * ROWB % 1024 == 0, "copy pieces of 64 lanes x 16 B");
+
+__shared__ __attribute__((aligned(16))) char fw_k[ROWS * ROWB];
+__shared__ __attribute__((aligned(16))) char fw_v[ROWS * ROWB];
+__shared__ __attribute__((aligned(16))) float fw_sc[NW * 32 * 32];    // per-wave [table row][query]
+
+__device__ __forceinline__ int kswz(int r) { return (r >> 1) & 7; }
+__device__ __forceinline__ int vswz(int r) { return ((r >> 1) & 1) << 2; }
+__device__ __forceinline__ bf16x8 lds_b128(const lds_char* p) { return *(const __attribute__((address_space(3))) bf16x8*)p; }
+__device__ __forceinline__ s16x4 lds_tr(const lds_char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p);
+}
+__device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float pair_max(float v) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  const float a = __uint_as_float(r[0]), b = __uint_as_float(r[1]);
+  return a > b ? a : b;
+}
+__device__ __forceinline__ float pair_sum(float v) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+template <bool OUT_BF16>
+__global__ __launch_bounds__(NW * 64, 4) void flash_window_kernel(FwdParams p) {
+  lds_char* const ks = (lds_char*)fw_k;
+  lds_char* const vs = (lds_char*)fw_v;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 5, ql = lane & 31;
+  const int64_t b = blockIdx.x / p.Hq, h = blockIdx.x % p.Hq;
+
+  // ---- K and V of the window into LDS (rows past the window read as zero)
+  {
+    const int rstride = (int)(p.k_st * 2);
+    const int nrec = (int)(((int64_t)(T - 1) * p.k_st + 64) * 2);
+    const char* kb = (const char*)((const __bf16*)p.k + b * p.k_sb + h * p.k_sh);
+    const char* vb = (const char*)((const __bf16*)p.v + b * p.k_sb + h * p.k_sh);
+    const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)kb, 0, nrec, 0x00020000);
+    const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)vb, 0, nrec, 0x00020000);
+    for (int pc = wave; pc < PIECES; pc += NW) {
+      const int L = 64 * pc + lane, row = L >> 3, pos = L & 7;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (__attribute__((address_space(3))) void*)(ks + 1024 * pc), 16,
+                                               row * rstride + ((pos ^ kswz(row)) << 4), 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (__attribute__((address_space(3))) void*)(vs + 1024 * pc), 16,
+                                               row * rstride + ((pos ^ vswz(row)) << 4), 0, 0, 0);
+    }
+  }
+
+  // ---- queries of this wave
+  const int qrow = 32 * wave + ql;
+  const bool qvalid = qrow < T;
+  const int qs = qvalid ? qrow : T - 1;
+  const int ih = qs / G, iw = qs % G;
+  const __bf16* qp = (const __bf16*)p.q + b * p.q_sb + h * p.q_sh;
+  bf16x8 qf[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) qf[c] = *(const bf16x8*)(qp + (int64_t)qs * p.q_st + c * 16 + 8 * g);
+  const float c2 = p.scale * kLog2e;
+  const float inv_scale = 1.0f / p.scale;
+
+  // ---- rel-pos terms: A^T[r, q] = table[r] . q on the matrix cores, then the
+  // skewed gathers term[q, y] = A[q, coord(q) - y + G - 1] through LDS.
+  lds_float* const sc = (lds_float*)fw_sc + wave * 1024;
+  auto table_product = [&](const void* tab) {
+    const __bf16* tp = (const __bf16*)tab + ql * 64 + 8 * g;
+    f32x16 a = (f32x16){};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const bf16x8 r = ql < NTAB ? *(const bf16x8*)(tp + 16 * c) : (bf16x8){};
+      a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(r, qf[c], a, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sc[(8 * (i / 4) + 4 * g + (i % 4)) * 32 + ql] = a[i];
+  };
+  // term_h / scale per grid row of the keys, as bf16 high + low parts
+  bf16x2 thhl[G];
+  table_product(p.rel_h);
+  __syncthreads();
+#pragma unroll
+  for (int y = 0; y < G; ++y) {
+    const float t = sc[(ih - y + G - 1) * 32 + ql] * inv_scale;
+    const __bf16 hi = (__bf16)t;
+    thhl[y] = (bf16x2){hi, (__bf16)(t - (float)hi)};
+  }
+  __syncthreads();
+  // term_w / scale per key slot of a tile: the score accumulators' start
+  f32x16 cinit;
+  table_product(p.rel_w);
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int s = 8 * (i / 4) + 4 * g + (i % 4);
+    const int x = s % G;
+    const float t = sc[(iw - x + G - 1) * 32 + ql] * inv_scale;
+    cinit[i] = s < TK ? t : -INFINITY;
+  }
+  // K' chunk: key slot ql (lanes g = 0) is one-hot at s / 14 and 4 + s / 14.
+  bf16x8 kaug = (bf16x8){};
+  if (g == 0 && ql < TK) {
+    const int ro = ql / G;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      kaug[e] = (__bf16)(e == ro ? 1.0f : 0.0f);
+      kaug[4 + e] = (__bf16)(e == ro ? 1.0f : 0.0f);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);        // this wave's copies have landed
+  __syncthreads();                      // ... and every other wave's
+
+  const int j16 = lane & 15, dh = (lane >> 4) & 1;
+  f32x16 o[2] = {(f32x16){}, (f32x16){}};
+  float m = -INFINITY, l = 0.0f;
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    // Q' chunk of this tile: high parts of term_h rows RPT*t + e at e, low parts at 4 + e.
+    bf16x8 qaug = (bf16x8){};
+    if (g == 0) {
+#pragma unroll
+      for (int e = 0; e < RPT; ++e) {
+        qaug[e] = thhl[RPT * t + e][0];
+        qaug[4 + e] = thhl[RPT * t + e][1];
+      }
+    }
+    f32x16 s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kaug, qaug, cinit, 0, 0, 0);
+    const int kr = TK * t + ql;
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(ks + kr * ROWB + (((2 * c + g) ^ kswz(kr)) << 4)), qf[c], s, 0,
+                                                  0, 0);
+    float smax = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+#pragma unroll
+    for (int i = 4; i < 16; i += 2) smax = fmaxf(smax, fmaxf(s[i], s[i + 1]));
+    const float tmax = pair_max(smax) * c2;
+    const bool need = tmax > m + kTau;
+    const float mn = need ? tmax : m;
+    const float alpha = (need && m != -INFINITY) ? fexp2(m - mn) : (need ? 0.0f : 1.0f);
+    if (__any(need)) {
+      l *= alpha;
+#pragma unroll
+      for (int d = 0; d < 2; ++d)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[d][i] *= alpha;
+    }
+    m = mn;
+    const float off = -m;
+    bf16x8 pb[2];
+    float acc0 = 0.0f, acc1 = 0.0f;
+#pragma unroll
+    for (int tc = 0; tc < 2; ++tc) {
+      bf16x2 pk[4];
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const f32x2 pp = {fexp2(fmaf(s[8 * tc + e], c2, off)), fexp2(fmaf(s[8 * tc + e + 1], c2, off))};
+        pk[e / 2] = __builtin_convertvector(pp, bf16x2);
+        if (e & 2) acc1 = __builtin_amdgcn_fdot2_f32_bf16(pk[e / 2], (bf16x2){(__bf16)1.0f, (__bf16)1.0f}, acc1, false);
+        else acc0 = __builtin_amdgcn_fdot2_f32_bf16(pk[e / 2], (bf16x2){(__bf16)1.0f, (__bf16)1.0f}, acc0, false);
+      }
+      pb[tc] = __builtin_shufflevector(__builtin_shufflevector(pk[0], pk[1], 0, 1, 2, 3),
+                                       __builtin_shufflevector(pk[2], pk[3], 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+    l += acc0 + acc1;
+#pragma unroll
+    for (int tc = 0; tc < 2; ++tc)
+#pragma unroll
+      for (int d = 0; d < 2; ++d) {
+        const int row0 = TK * t + 16 * tc + 4 * g + (j16 >> 2);
+        const int vo = row0 * ROWB + ((((4 * d + 2 * dh + ((j16 & 3) >> 1)) ^ vswz(row0)) << 4) + ((j16 & 1) << 3));
+        const s16x4 lo4 = lds_tr(vs + vo);
+        const s16x4 hi4 = lds_tr(vs + vo + 8 * ROWB);
+        const s16x8 a8 = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+        o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a8), pb[tc], o[d], 0, 0, 0);
+      }
+  }
+
+  const float lt = pair_sum(l);
+  const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+  if (!qvalid) return;
+  const int64_t ob = b * p.q_sb + h * p.q_sh + (int64_t)qrow * p.q_st;
+#pragma unroll
+  for (int d = 0; d < 2; ++d)
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      const int dd = d * 32 + 8 * i4 + 4 * g;
+      if (OUT_BF16) {
+        bf16x4 v4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v4[e] = (__bf16)(o[d][4 * i4 + e] * inv);
+        *(bf16x4*)((__bf16*)p.o + ob + dd) = v4;
+      } else {
+        f32x4 v4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v4[e] = o[d][4 * i4 + e] * inv;
+        *(f32x4*)((float*)p.o + ob + dd) = v4;
+      }
+    }
+  if (p.lse && g == 0) p.lse[(b * p.Hq + h) * p.Tq + qrow] = lt > 0.0f ? (m + __log2f(lt)) * kLn2 : -INFINITY;
+}
+
+}  // namespace
+
+bool window_supports(const FwdParams& p) {
+  return p.dtype == 1 && p.D == 64 && p.bias == BIAS_RELPOS && !p.term_h && p.rel_h && p.rel_w &&
+         p.grid_h == G && p.grid_w == G && p.Tq == T && p.Tkv == T && p.Hq == p.Hkv && p.num_splits == 1 &&
+         p.B * p.Hq <= 0x7fffffffLL && (int64_t)T * p.k_st * 2 <= 0x7fffffffLL;
+}
+
+hipError_t launch_window(const FwdParams& p, hipStream_t s) {
+  const dim3 grid((unsigned)(p.B * p.Hq));
+  if (p.out_dtype == 1) hipLaunchKernelGGL(flash_window_kernel<true>, grid, dim3(NW * 64), 0, s, p);
+  else hipLaunchKernelGGL(flash_window_kernel<false>, grid, dim3(NW * 64), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace sdpa

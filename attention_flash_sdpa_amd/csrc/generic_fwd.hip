@@ -16,16 +16,22 @@
 
 namespace sdpa {
 
-template <typename TIN, int DMAX>
+// Mask families, one kernel instance each (small code per instance: with few
+// waves per CU, instruction fetch dominates large kernels).
+enum GenericFamily { GF_NONE = 0, GF_INDEX = 1, GF_TENSOR = 2, GF_RELPOS = 3 };
+
+template <typename TIN, int DMAX, int GF>
 __global__ __launch_bounds__(64) void generic_fwd_kernel(FwdParams p) {
   constexpr int BK = 32;
   __shared__ float ks[BK][DMAX];
   __shared__ float vs[BK][DMAX];
+  __shared__ float zs[BK][64];        // this tile's scores, one column per lane
+  const int lane = threadIdx.x;
   const int64_t b = blockIdx.z, h = blockIdx.y;
   const int64_t i0 = (int64_t)blockIdx.x * 64;
-  const int64_t i = i0 + threadIdx.x;
+  const int64_t i = i0 + lane;
   const bool live = i < p.Tq;
-  const int64_t D = p.D;
+  const int D = (int)p.D;
   const int64_t hk = h / (p.Hq / p.Hkv);
   const TIN* qp = (const TIN*)p.q + b * p.q_sb + h * p.q_sh + (live ? i : 0) * p.q_st;
   const TIN* kp = (const TIN*)p.k + b * p.k_sb + hk * p.k_sh;
@@ -42,7 +48,7 @@ __global__ __launch_bounds__(64) void generic_fwd_kernel(FwdParams p) {
   // Key range any row of this block can see.
   int64_t lo = 0, hi = p.Tkv;
   const int64_t ilast = (i0 + 63 < p.Tq - 1) ? i0 + 63 : p.Tq - 1;
-  if (p.bias == BIAS_CAUSAL || p.bias == BIAS_SLIDING) {
+  if (GF == GF_INDEX) {
     hi = ilast + p.offset + 1;
     if (hi > p.Tkv) hi = p.Tkv;
     if (p.bias == BIAS_SLIDING) {
@@ -52,14 +58,14 @@ __global__ __launch_bounds__(64) void generic_fwd_kernel(FwdParams p) {
   }
   const float* th = nullptr;
   const float* tw = nullptr;
-  if (p.bias == BIAS_RELPOS && live) {
-    th = p.term_h + ((b * p.Hq + h) * p.Tq + i) * p.grid_h;
-    tw = p.term_w + ((b * p.Hq + h) * p.Tq + i) * p.grid_w;
+  if (GF == GF_RELPOS) {
+    th = p.term_h + ((b * p.Hq + h) * p.Tq + (live ? i : 0)) * p.grid_h;
+    tw = p.term_w + ((b * p.Hq + h) * p.Tq + (live ? i : 0)) * p.grid_w;
   }
 
   for (int64_t j0 = lo; j0 < hi; j0 += BK) {
     __syncthreads();
-    for (int e = threadIdx.x; e < BK * DMAX; e += 64) {
+    for (int e = lane; e < BK * DMAX; e += 64) {
       const int jj = e / DMAX, c = e % DMAX;
       const int64_t j = j0 + jj;
       const bool ok = j < hi && c < D;
@@ -67,22 +73,22 @@ __global__ __launch_bounds__(64) void generic_fwd_kernel(FwdParams p) {
       vs[jj][c] = ok ? to_f32(vp[j * p.k_st + c]) : 0.0f;
     }
     __syncthreads();
-    float z[BK];
+    const int nk = (int)((hi - j0 < BK) ? hi - j0 : BK);
     float tmax = -INFINITY;
-#pragma unroll
-    for (int jj = 0; jj < BK; ++jj) {
+#pragma unroll 2
+    for (int jj = 0; jj < nk; ++jj) {
       const int64_t j = j0 + jj;
-      float s = -INFINITY;
-      if (live && j < hi && index_allowed(p.bias, i, j, p.offset, p.window)) {
-        float d = 0.0f;
+      float d = 0.0f;
 #pragma unroll
-        for (int c = 0; c < DMAX; ++c) d = fmaf(qr[c], ks[jj][c], d);
-        s = d * p.scale;
-        if (p.bias == BIAS_RELPOS) s += th[j / p.grid_w] + tw[j % p.grid_w];
-        else if (p.bias == BIAS_ADDITIVE || p.bias == BIAS_BOOL) s += tensor_mask_bias(p, b, h, i, j);
-      }
-      z[jj] = s;
-      tmax = fmaxf(tmax, s);
+      for (int c = 0; c < DMAX; ++c) d = fmaf(qr[c], ks[jj][c], d);
+      float z = d * p.scale;
+      bool ok = live;
+      if (GF == GF_INDEX) ok = ok && index_allowed(p.bias, i, j, p.offset, p.window);
+      if (GF == GF_RELPOS && ok) z += th[j / p.grid_w] + tw[j % p.grid_w];
+      if (GF == GF_TENSOR && ok) z += tensor_mask_bias(p, b, h, i, j);
+      z = ok ? z : -INFINITY;
+      zs[jj][lane] = z;
+      tmax = fmaxf(tmax, z);
     }
     if (tmax > m) {             // the running max grows: rescale what has been summed
       const float corr = (m == -INFINITY) ? 0.0f : expf(m - tmax);
@@ -92,9 +98,10 @@ __global__ __launch_bounds__(64) void generic_fwd_kernel(FwdParams p) {
       m = tmax;
     }
     if (m != -INFINITY) {
-#pragma unroll
-      for (int jj = 0; jj < BK; ++jj) {
-        const float pj = (z[jj] == -INFINITY) ? 0.0f : expf(z[jj] - m);
+#pragma unroll 2
+      for (int jj = 0; jj < nk; ++jj) {
+        const float z = zs[jj][lane];
+        const float pj = (z == -INFINITY) ? 0.0f : expf(z - m);
         l += pj;
 #pragma unroll
         for (int c = 0; c < DMAX; ++c) acc[c] = fmaf(pj, vs[jj][c], acc[c]);
@@ -106,21 +113,34 @@ __global__ __launch_bounds__(64) void generic_fwd_kernel(FwdParams p) {
   const int64_t ob = b * p.q_sb + h * p.q_sh + i * p.q_st;
   if (p.out_dtype == 0) {
     float* op = (float*)p.o + ob;
+#pragma unroll
     for (int c = 0; c < DMAX; ++c) if (c < D) op[c] = acc[c] * inv;
   } else {
     __bf16* op = (__bf16*)p.o + ob;
+#pragma unroll
     for (int c = 0; c < DMAX; ++c) if (c < D) op[c] = (__bf16)(acc[c] * inv);
   }
   if (p.lse) p.lse[(b * p.Hq + h) * p.Tq + i] = (l > 0.0f) ? m + logf(l) : -INFINITY;
 }
 
+template <typename TIN, int DMAX>
+static void launch_dim(const FwdParams& p, dim3 grid, hipStream_t s) {
+  switch (p.bias) {
+    case BIAS_NONE: hipLaunchKernelGGL((generic_fwd_kernel<TIN, DMAX, GF_NONE>), grid, dim3(64), 0, s, p); break;
+    case BIAS_CAUSAL:
+    case BIAS_SLIDING: hipLaunchKernelGGL((generic_fwd_kernel<TIN, DMAX, GF_INDEX>), grid, dim3(64), 0, s, p); break;
+    case BIAS_RELPOS: hipLaunchKernelGGL((generic_fwd_kernel<TIN, DMAX, GF_RELPOS>), grid, dim3(64), 0, s, p); break;
+    default: hipLaunchKernelGGL((generic_fwd_kernel<TIN, DMAX, GF_TENSOR>), grid, dim3(64), 0, s, p); break;
+  }
+}
+
 template <typename TIN>
 static hipError_t launch_typed(const FwdParams& p, hipStream_t s) {
   dim3 grid((unsigned)((p.Tq + 63) / 64), (unsigned)p.Hq, (unsigned)p.B);
-  if (p.D <= 16) hipLaunchKernelGGL((generic_fwd_kernel<TIN, 16>), grid, dim3(64), 0, s, p);
-  else if (p.D <= 32) hipLaunchKernelGGL((generic_fwd_kernel<TIN, 32>), grid, dim3(64), 0, s, p);
-  else if (p.D <= 64) hipLaunchKernelGGL((generic_fwd_kernel<TIN, 64>), grid, dim3(64), 0, s, p);
-  else hipLaunchKernelGGL((generic_fwd_kernel<TIN, 128>), grid, dim3(64), 0, s, p);
+  if (p.D <= 16) launch_dim<TIN, 16>(p, grid, s);
+  else if (p.D <= 32) launch_dim<TIN, 32>(p, grid, s);
+  else if (p.D <= 64) launch_dim<TIN, 64>(p, grid, s);
+  else launch_dim<TIN, 128>(p, grid, s);
   return hipGetLastError();
 }
 

@@ -67,6 +67,8 @@ hipError_t launch_d16(const FwdParams& p, hipStream_t s);            // bf16, D 
 bool d16_supports(const FwdParams& p);
 hipError_t launch_split64(const FwdParams& p, hipStream_t s);        // bf16, D = 64, key range split in-workgroup
 bool split64_supports(const FwdParams& p);
+hipError_t launch_window(const FwdParams& p, hipStream_t s);         // bf16, D = 64, 14 x 14 rel-pos windows, terms in-kernel
+bool window_supports(const FwdParams& p);
 hipError_t launch_tiled(const FwdParams& p, hipStream_t s);          // bf16, D in {64, 128}, none / causal / sliding
 bool tiled_supports(const FwdParams& p);
 // Rel-pos terms can be formed inside the MFMA kernel (no term arrays needed).

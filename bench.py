@@ -3,6 +3,8 @@ fused rel-pos SDPA on SAM ViT-B's 64x64 global attention (B1, 12 heads,
 T 4096, head_dim 64, bf16), one sdpa_relpos_fwd call per step.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
+    python bench.py --copy-calibration MIB [--steps K]
+
 
 Prints ONE JSON line.  A step is one full pass of the fused path (rel-pos
 terms + flash attention, all on the GPU) over the seeded synthetic inputs,
@@ -25,6 +27,17 @@ if ROOT not in sys.path:
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 HBM_PEAK_GBS = 8000.0               # MI355X HBM3E, published
+
+# Source file of each attention kernel, for matching recorded counter data.
+KERNEL_SOURCE = {
+    "flash_split64_kernel": "flash_split64.hip",
+    "flash_tiled_kernel": "flash_tiled.hip",
+    "flash_window_kernel": "flash_window.hip",
+    "flash_mfma_kernel": "flash_mfma.hip",
+    "d16_qpack_kernel": "flash_d16.hip",
+    "d16_kpack_kernel": "flash_d16.hip",
+    "generic_fwd_kernel": "generic_fwd.hip",
+}
 
 
 def allowed_pairs(wl):
@@ -103,6 +116,49 @@ def kernel_events(fa, wl, g, steps):
     return call_ms, terms_ms
 
 
+def source_sha256(kernel):
+    import hashlib
+    path = os.path.join(ROOT, "attention_flash_sdpa_amd", "csrc", KERNEL_SOURCE.get(kernel, ""))
+    if not os.path.isfile(path):
+        return None
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def recorded_traffic(kernel, workload):
+    """HBM bytes per launch from the recorded FETCH_SIZE / WRITE_SIZE counter
+    runs (scaled by the plain-copy calibration), if a record exists for this
+    kernel and workload AND was taken on the kernel source as it is now."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.md")
+    if not os.path.isfile(path):
+        return None, "no counter record"
+    rec = None
+    with open(path) as f:
+        for line in f:
+            if line.startswith("traffic: "):
+                rec = json.loads(line[len("traffic: "):])
+                break
+    if rec is None:
+        return None, "counter record has no traffic line"
+    if rec.get("source_sha256") != source_sha256(kernel):
+        return None, "counters predate the current kernel source"
+    return rec["bytes_per_launch"], f"{os.path.relpath(path, ROOT)}"
+
+
+def copy_calibration(mib, steps):
+    """A plain device-to-device copy of known size: its FETCH_SIZE / WRITE_SIZE
+    per dispatch calibrate the counters against true bytes."""
+    import torch
+    n = mib * 1024 * 1024
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_per_dispatch": n, "read_bytes": n, "write_bytes": n, "steps": steps}))
+
+
 def cpu_baseline(wl, x, budget_s=20.0):
     """Time the fp64 oracle on whole (batch, head) slices of the same inputs until
     about `budget_s` seconds of CPU work are done; report it at the metric's unit."""
@@ -143,9 +199,11 @@ def main():
     ap.add_argument("--workload", default="sam_global_relpos")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB per step (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+        print(f"bench.py: the library runs on one GPU per process (asked for --gpus {args.gpus}); "
               "the path would shard by (batch, head) with no exchange, but no multi-GPU run exists.",
               file=sys.stderr)
         sys.exit(2)
@@ -154,6 +212,9 @@ def main():
     import attention_flash_sdpa_amd as fa
     import workloads
 
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration, args.steps)
+        return
     fa.load()
     if os.environ.get("SDPA_BENCH_UNFUSED", "0") == "1":
         fa.set_tuning("relpos_fused", 0)
@@ -170,6 +231,9 @@ def main():
     total = attn + bias
     tflops = total / sec / 1e12
     call_ms, terms_ms = kernel_events(fa, wl, g, args.steps)
+    run_call(fa, wl, g, torch.empty_like(g["q"]))
+    kernel = fa.last_kernel()
+    traffic, traffic_src = recorded_traffic(kernel, wl.name)
     flash_ms = call_ms - terms_ms
     flash_flops = attn + (2 * allowed_pairs(wl) * wl.B * wl.Hq if wl.relpos else 0)
     if wl.relpos and terms_ms == 0.0:
@@ -194,8 +258,9 @@ def main():
                    "grid": list(wl.grid) if wl.grid else None, "mask": wl.mask, "scale": wl.scale,
                    "flop_per_step": total, "attn_flop": attn, "bias_flop": bias},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": MFMA_BF16_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
-                     "kernel": "flash_mfma_kernel", "kernel_ms": round(flash_ms, 5),
+                     "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": traffic,
+                     "traffic_source": traffic_src,
+                     "kernel": kernel, "kernel_ms": round(flash_ms, 5),
                      "terms_kernel_ms": round(terms_ms, 5), "flop_per_launch": flash_flops,
                      "algorithmic_bytes_per_launch": byte_model(wl)},
     }

@@ -59,7 +59,7 @@ extern "C" {
 typedef enum sdpa_status {
   SDPA_OK = 0,
   SDPA_ERR_INVALID = -1,      /* null pointer, non-positive size, inconsistent shapes   */
-  SDPA_ERR_UNSUPPORTED = -2,  /* valid request this build does not implement             */
+  SDPA_ERR_UNSUPPORTED = -2,  /* valid request that the library does not implement         */
   SDPA_ERR_WORKSPACE = -3,    /* workspace missing or smaller than sdpa_workspace_size() */
   SDPA_ERR_HIP = -4           /* a kernel launch failed; see sdpa_last_error()           */
 } sdpa_status;
@@ -165,6 +165,14 @@ const char* sdpa_status_string(int status);
 
 /* Thread-local detail of the last failing call on this thread ("" if none). */
 const char* sdpa_last_error(void);
+
+/*
+ * Name of the attention kernel that the last successful sdpa_fwd /
+ * sdpa_relpos_fwd call on this thread launched (its dominant kernel; a
+ * split-KV combine or a separate relpos_terms launch is not named), or "" if
+ * none yet.  Static string, never freed.  For profiling and benchmarks.
+ */
+const char* sdpa_last_kernel(void);
 
 /*
  * Process-wide tuning knobs (tests and benchmarks), each an int64:

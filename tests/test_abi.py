@@ -24,7 +24,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("sdpa_fwd", "sdpa_relpos_fwd", "relpos_terms", "sdpa_workspace_size",
-              "sdpa_status_string", "sdpa_last_error", "sdpa_set_tuning"):
+              "sdpa_status_string", "sdpa_last_error", "sdpa_last_kernel", "sdpa_set_tuning"):
         assert n in names
 
 
@@ -125,10 +125,12 @@ def test_status_strings_and_tuning():
     assert lib.sdpa_set_tuning(b"relpos_fused", 2) == -1
     assert lib.sdpa_set_tuning(b"relpos_fused", 1) == 0
     assert lib.sdpa_relpos_fused(1, 64, 64, 64) == 1      # SAM ViT-B global grid: one kernel
-    assert lib.sdpa_relpos_fused(1, 64, 14, 14) == 0      # windowed grid: terms kernel first
+    assert lib.sdpa_relpos_fused(1, 64, 14, 14) == 1      # SAM 14x14 window: one kernel
+    assert lib.sdpa_relpos_fused(1, 64, 13, 14) == 0      # other windowed grids: terms kernel first
     assert lib.sdpa_relpos_fused(0, 64, 64, 64) == 0
     assert lib.sdpa_set_tuning(b"relpos_fused", 0) == 0
     assert lib.sdpa_relpos_fused(1, 64, 64, 64) == 0
+    assert lib.sdpa_relpos_fused(1, 64, 14, 14) == 0
     assert lib.sdpa_set_tuning(b"relpos_fused", 1) == 0
 
 
@@ -141,3 +143,13 @@ def test_binding_refuses_cpu_tensors():
 
 def test_default_scale():
     assert fa.default_scale(64) == 0.125 and math.isclose(fa.default_scale(128), 128 ** -0.5)
+
+
+def test_last_kernel_starts_empty_per_thread():
+    import threading
+    lib = fa.load()
+    got = []
+    th = threading.Thread(target=lambda: got.append(lib.sdpa_last_kernel()))
+    th.start()
+    th.join()
+    assert got == [b""]

@@ -163,7 +163,11 @@ def test_first_causal_row_is_v0(gpu):
 @pytest.mark.parametrize("name", ["sam_global_relpos", "sam_window_relpos"])
 def test_relpos_fused_equals_unfused(gpu, name):
     """The single-kernel rel-pos path (terms formed in the attention kernel) and
-    the two-kernel path (relpos_terms into the workspace) agree."""
+    the two-kernel path (relpos_terms into the workspace) agree.  For the global
+    grid both routes run the same matrix-core kernel (bf16 probabilities), so
+    only the order of term arithmetic differs (1e-3).  For windows the unfused
+    route runs the fp32 vector kernel: the fused kernel's bf16 rounding of each
+    probability (relative 2^-9) moves an output by at most 2^-9 * max|v|."""
     wl = workloads.replica(name)
     x = {k_: t.cuda() for k_, t in workloads.generate(wl, seed=4).items()}
     args = (x["q"], x["k"], x["v"], x["rel_pos_h"], x["rel_pos_w"], wl.grid)
@@ -173,10 +177,12 @@ def test_relpos_fused_equals_unfused(gpu, name):
         b = gpu.sdpa_relpos(*args, scale=wl.scale, out_dtype=torch.float32)
     finally:
         gpu.set_tuning("relpos_fused", 1)
-    assert max_err(np64(a), np64(b)) <= 1e-3
+    tol = 1e-3 if name == "sam_global_relpos" else 2.0 ** -9 * float(x["v"].float().abs().max()) + 1e-4
+    assert max_err(np64(a), np64(b)) <= tol
     ref = oracle.sdpa(np64(x["q"].cpu()), np64(x["k"].cpu()), np64(x["v"].cpu()), scale=wl.scale,
                       rel_pos={"rel_pos_h": np64(x["rel_pos_h"].cpu()), "rel_pos_w": np64(x["rel_pos_w"].cpu()),
                                "grid": wl.grid})
+    assert max_err(np64(a), ref["o"]) <= TOL["bf16"]
     assert max_err(np64(b), ref["o"]) <= TOL["bf16"]
 
 
@@ -315,3 +321,34 @@ def test_relpos_non_positive_scale(gpu):
     ref = oracle.sdpa(np64(x["q"]), np64(x["k"]), np64(x["v"]), scale=wl.scale,
                       rel_pos={"rel_pos_h": np64(x["rel_pos_h"]), "rel_pos_w": np64(x["rel_pos_w"]), "grid": wl.grid})
     assert max_err(np64(o), ref["o"]) <= TOL["bf16"]
+
+
+def test_dispatch_names_the_kernel(gpu):
+    """Which kernel each workload family reaches (the benchmark and profiles
+    name the dominant kernel from this)."""
+    def run(Hq, Hkv, Tq, Tkv, D, dtype=torch.bfloat16, mask=None, scale=None):
+        q = rnd((1, Hq, Tq, D), dtype, 1).cuda()
+        k = rnd((1, Hkv, Tkv, D), dtype, 2).cuda()
+        v = rnd((1, Hkv, Tkv, D), dtype, 3).cuda()
+        gm = dict(mask, data=mask["data"].cuda()) if mask and "data" in mask else mask
+        gpu.sdpa(q, k, v, mask=gm, scale=scale)
+        torch.cuda.synchronize()
+        return gpu.last_kernel()
+    assert run(4, 1, 300, 300, 128, mask={"kind": "causal", "offset": 0}) == "flash_tiled_kernel"
+    assert run(2, 2, 300, 300, 64) == "flash_split64_kernel"
+    add = {"kind": "additive", "data": rnd((1, 1, 300, 300), torch.float32, 4)}
+    assert run(2, 2, 300, 300, 64, mask=add) == "flash_mfma_kernel"
+    assert run(2, 2, 100, 100, 64, dtype=torch.float32) == "generic_fwd_kernel"
+    assert run(8, 8, 7, 500, 16) == "d16_qpack_kernel"
+    assert run(8, 8, 500, 7, 16) == "d16_kpack_kernel"
+    assert run(2, 2, 100, 100, 64, scale=-1.0) == "generic_fwd_kernel"
+    wl = workloads.replica("sam_global_relpos")
+    x = {k_: t.cuda() for k_, t in workloads.generate(wl, seed=0, layout="bhsd").items()}
+    gpu.sdpa_relpos(x["q"], x["k"], x["v"], x["rel_pos_h"], x["rel_pos_w"], wl.grid)
+    torch.cuda.synchronize()
+    assert gpu.last_kernel() == "flash_split64_kernel"
+    wl = workloads.replica("sam_window_relpos")
+    x = {k_: t.cuda() for k_, t in workloads.generate(wl, seed=0, layout="bhsd").items()}
+    gpu.sdpa_relpos(x["q"], x["k"], x["v"], x["rel_pos_h"], x["rel_pos_w"], wl.grid)
+    torch.cuda.synchronize()
+    assert gpu.last_kernel() == "flash_window_kernel"
