@@ -21,7 +21,8 @@
 //   * term_h / scale depends on (query, tile, s / 14): it enters the matrix op
 //     as one extra 16-deep chunk, K' rows one-hot in s / 14 against the query's
 //     two term_h values of the tile, each split into a bf16 high and low part
-//     (so the bias keeps ~16 bits, not bf16's 8).
+//     (so the bias keeps ~16 bits, not bf16's 8); the products Q . Rh^T stay
+//     in LDS and each tile reads its two values.
 // The terms come from two 32 x 32 x 64 products per wave, Q . Rh^T and
 // Q . Rw^T over all 27 table rows, followed by a skewed gather through LDS.
 #include "common.h"
@@ -104,46 +105,43 @@ __global__ __launch_bounds__(NW * 64, 4) void flash_window_kernel(FwdParams p) {
     }
   }
 
-  // ---- queries of this wave
+  // ---- queries of this wave, and the rel-pos table rows as matrix operands
+  // (all issued together: one memory round trip; table rows past 2G-1 are zeroed)
   const int qrow = 32 * wave + ql;
   const bool qvalid = qrow < T;
   const int qs = qvalid ? qrow : T - 1;
   const int ih = qs / G, iw = qs % G;
-  const __bf16* qp = (const __bf16*)p.q + b * p.q_sb + h * p.q_sh;
-  bf16x8 qf[4];
+  const __bf16* qp = (const __bf16*)p.q + b * p.q_sb + h * p.q_sh + (int64_t)qs * p.q_st + 8 * g;
+  const int trow = ql < NTAB ? ql : NTAB - 1;
+  const __bf16* rhp = (const __bf16*)p.rel_h + trow * 64 + 8 * g;
+  const __bf16* rwp = (const __bf16*)p.rel_w + trow * 64 + 8 * g;
+  bf16x8 qf[4], rh[4], rw[4];
 #pragma unroll
-  for (int c = 0; c < 4; ++c) qf[c] = *(const bf16x8*)(qp + (int64_t)qs * p.q_st + c * 16 + 8 * g);
+  for (int c = 0; c < 4; ++c) {
+    qf[c] = *(const bf16x8*)(qp + c * 16);
+    rh[c] = *(const bf16x8*)(rhp + c * 16);
+    rw[c] = *(const bf16x8*)(rwp + c * 16);
+  }
+  if (ql >= NTAB) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) rh[c] = rw[c] = (bf16x8){};
+  }
   const float c2 = p.scale * kLog2e;
   const float inv_scale = 1.0f / p.scale;
 
   // ---- rel-pos terms: A^T[r, q] = table[r] . q on the matrix cores, then the
   // skewed gathers term[q, y] = A[q, coord(q) - y + G - 1] through LDS.
   lds_float* const sc = (lds_float*)fw_sc + wave * 1024;
-  auto table_product = [&](const void* tab) {
-    const __bf16* tp = (const __bf16*)tab + ql * 64 + 8 * g;
+  auto table_product = [&](const bf16x8 (&tab)[4]) {
     f32x16 a = (f32x16){};
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const bf16x8 r = ql < NTAB ? *(const bf16x8*)(tp + 16 * c) : (bf16x8){};
-      a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(r, qf[c], a, 0, 0, 0);
-    }
+    for (int c = 0; c < 4; ++c) a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tab[c], qf[c], a, 0, 0, 0);
 #pragma unroll
     for (int i = 0; i < 16; ++i) sc[(8 * (i / 4) + 4 * g + (i % 4)) * 32 + ql] = a[i];
   };
-  // term_h / scale per grid row of the keys, as bf16 high + low parts
-  bf16x2 thhl[G];
-  table_product(p.rel_h);
-  __syncthreads();
-#pragma unroll
-  for (int y = 0; y < G; ++y) {
-    const float t = sc[(ih - y + G - 1) * 32 + ql] * inv_scale;
-    const __bf16 hi = (__bf16)t;
-    thhl[y] = (bf16x2){hi, (__bf16)(t - (float)hi)};
-  }
-  __syncthreads();
   // term_w / scale per key slot of a tile: the score accumulators' start
   f32x16 cinit;
-  table_product(p.rel_w);
+  table_product(rw);
   __syncthreads();
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
@@ -152,6 +150,9 @@ __global__ __launch_bounds__(NW * 64, 4) void flash_window_kernel(FwdParams p) {
     const float t = sc[(iw - x + G - 1) * 32 + ql] * inv_scale;
     cinit[i] = s < TK ? t : -INFINITY;
   }
+  __syncthreads();
+  // A_h stays in LDS; each tile reads its two term_h values from it.
+  table_product(rh);
   // K' chunk: key slot ql (lanes g = 0) is one-hot at s / 14 and 4 + s / 14.
   bf16x8 kaug = (bf16x8){};
   if (g == 0 && ql < TK) {
@@ -175,16 +176,19 @@ __global__ __launch_bounds__(NW * 64, 4) void flash_window_kernel(FwdParams p) {
     if (g == 0) {
 #pragma unroll
       for (int e = 0; e < RPT; ++e) {
-        qaug[e] = thhl[RPT * t + e][0];
-        qaug[4 + e] = thhl[RPT * t + e][1];
+        const float th = sc[(ih - RPT * t - e + G - 1) * 32 + ql] * inv_scale;
+        const __bf16 hi = (__bf16)th;
+        qaug[e] = hi;
+        qaug[4 + e] = (__bf16)(th - (float)hi);
       }
     }
     f32x16 s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kaug, qaug, cinit, 0, 0, 0);
     const int kr = TK * t + ql;
+    bf16x8 kf[4];
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(ks + kr * ROWB + (((2 * c + g) ^ kswz(kr)) << 4)), qf[c], s, 0,
-                                                  0, 0);
+    for (int c = 0; c < 4; ++c) kf[c] = lds_b128(ks + kr * ROWB + (((2 * c + g) ^ kswz(kr)) << 4));
+#pragma unroll
+    for (int c = 0; c < 4; ++c) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[c], qf[c], s, 0, 0, 0);
     float smax = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
 #pragma unroll
     for (int i = 4; i < 16; i += 2) smax = fmaxf(smax, fmaxf(s[i], s[i + 1]));
