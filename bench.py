@@ -92,27 +92,55 @@ def time_gpu(fa, wl, g, steps, warmup):
     return (time.perf_counter() - t0) / steps
 
 
-def kernel_events(fa, wl, g, steps):
-    """Average duration of the whole call and of the separate rel-pos terms
-    launch, from HIP events recorded on the stream the kernels run on."""
+def _hold_stream(ms):
+    """Keep the current stream busy for about `ms` milliseconds (a bounded
+    spin kernel), so that the launches queued behind it run back to back and
+    HIP events between them time the GPU work, not the host's launch rate."""
+    import torch
+    global _SPIN_PER_MS
+    if _SPIN_PER_MS is None:
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        torch.cuda.synchronize()
+        ev[0].record()
+        torch.cuda._sleep(1_000_000)
+        ev[1].record()
+        ev[1].synchronize()
+        _SPIN_PER_MS = 1_000_000 / max(ev[0].elapsed_time(ev[1]), 1e-3)
+    torch.cuda._sleep(int(min(ms, 200.0) * _SPIN_PER_MS))
+
+
+_SPIN_PER_MS = None
+
+
+def kernel_events(fa, wl, g, steps, reps=5):
+    """Average GPU duration of the whole call and of the separate rel-pos terms
+    launch, from HIP events recorded on the stream the kernels run on (torch's
+    current stream, which the binding passes to the library).  The launches of
+    each repetition queue up behind a spin kernel, so they run back to back;
+    the median over `reps` repetitions is returned."""
+    import statistics
     import torch
     out = torch.empty_like(g["q"])
     s = torch.cuda.current_stream()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    ev[0].record(s)
-    for _ in range(steps):
-        run_call(fa, wl, g, out)
-    ev[1].record(s)
-    ev[1].synchronize()
-    call_ms = ev[0].elapsed_time(ev[1]) / steps
+
+    def timed(fn):
+        ts = []
+        for _ in range(reps):
+            torch.cuda.synchronize()
+            _hold_stream(2.0 + 0.2 * steps)
+            ev[0].record(s)
+            for _ in range(steps):
+                fn()
+            ev[1].record(s)
+            ev[1].synchronize()
+            ts.append(ev[0].elapsed_time(ev[1]) / steps)
+        return statistics.median(ts)
+
+    call_ms = timed(lambda: run_call(fa, wl, g, out))
     terms_ms = 0.0
     if wl.relpos and not fa.relpos_fused(g["q"].dtype, wl.D, wl.grid):
-        ev[0].record(s)
-        for _ in range(steps):
-            fa.relpos_terms(g["q"], g["rel_pos_h"], g["rel_pos_w"], wl.grid, layout=wl.layout)
-        ev[1].record(s)
-        ev[1].synchronize()
-        terms_ms = ev[0].elapsed_time(ev[1]) / steps
+        terms_ms = timed(lambda: fa.relpos_terms(g["q"], g["rel_pos_h"], g["rel_pos_w"], wl.grid, layout=wl.layout))
     return call_ms, terms_ms
 
 
