@@ -159,7 +159,8 @@ def _mask_struct(mask, B, Hq, Tq, Tkv, keep):
     m.window = int(mask.get("window", 0))
     if kind in ("additive", "bool"):
         data = mask["data"]
-        _need_gpu(data)
+        if not data.is_cuda:
+            raise ValueError("mask tensors must live on the GPU (no CPU path exists)")
         if data.dim() != 4:
             raise ValueError("tensor masks are rank-4, broadcastable to [B, Hq, Tq, Tkv]")
         if kind == "bool":

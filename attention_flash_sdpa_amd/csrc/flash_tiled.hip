@@ -22,6 +22,11 @@
 // wholly outside a wave's causal / sliding band are skipped; only tiles the
 // band boundary crosses pay for per-element masking.
 //
+// Tensor masks (additive fp32 / bf16, boolean bytes, contiguous along keys,
+// any broadcast strides over batch, head and query) travel the same way: each
+// wave copies its 32 x 32 block of the mask next to the K/V tile, XOR-swizzled
+// by 16-byte chunks, and reads its 16 values per tile with 4 vector LDS reads.
+//
 // The running max is optimistic: probabilities are formed against the current
 // reference and only a tile whose row sum exceeds 2^8 (a probability above
 // 2^8, an overflow, or no reference yet) takes the exact path that moves the
@@ -48,14 +53,21 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kTau = 8.0f;
 constexpr float kTauSum = 256.0f;
 constexpr int BN = 32;
-constexpr int MAXTILE = BN * 128 * 2;     // 8 KB: one K or V tile at head_dim 128
 
-__shared__ __attribute__((aligned(16))) char ft_ka[MAXTILE];
-__shared__ __attribute__((aligned(16))) char ft_kb[MAXTILE];
-__shared__ __attribute__((aligned(16))) char ft_va[MAXTILE];
-__shared__ __attribute__((aligned(16))) char ft_vb[MAXTILE];
 
-enum Mode { T_NONE = 0, T_INDEX = 1 };
+enum Mode { T_NONE = 0, T_INDEX = 1, T_ADD_F32 = 2, T_ADD_BF16 = 3, T_BOOL = 4 };
+
+// Mask block geometry per mode: element size, bytes per 32-key row, 16-byte
+// chunks per row, copy instructions per wave, rows per 256-byte bank sweep.
+template <int MODE>
+struct MCfg {
+  static constexpr int ES = MODE == T_ADD_F32 ? 4 : (MODE == T_ADD_BF16 ? 2 : 1);
+  static constexpr int ROWB = 32 * ES;
+  static constexpr int CPR = ROWB / 16;
+  static constexpr int NI = 32 * CPR / 64;
+  static constexpr int WB = 32 * ROWB;                 // bytes per wave block
+  static __device__ __forceinline__ int swz(int r) { return (r / (256 / ROWB)) & (CPR - 1); }
+};
 
 template <int D>
 struct TCfg {
@@ -89,8 +101,18 @@ __device__ __forceinline__ float pair_sum(float v) {
 }
 
 template <int D, int MODE, bool OUT_BF16>
-__global__ __launch_bounds__(256, 3) void flash_tiled_kernel(FwdParams p, int hpw) {
+__global__ __launch_bounds__(256, 3) void flash_tiled_kernel(FwdParams p, int hpw, int64_t mask_bytes) {
+  constexpr bool TENSOR = MODE >= T_ADD_F32;
+  using M = MCfg<MODE>;
   using C = TCfg<D>;
+  // Double-buffered tiles, each buffer a distinct LDS object (no false
+  // dependence between copies in flight and reads of the current tile).
+  __shared__ __attribute__((aligned(16))) char ft_ka[C::TILEB];
+  __shared__ __attribute__((aligned(16))) char ft_kb[C::TILEB];
+  __shared__ __attribute__((aligned(16))) char ft_va[C::TILEB];
+  __shared__ __attribute__((aligned(16))) char ft_vb[C::TILEB];
+  __shared__ __attribute__((aligned(16))) char ft_ma[TENSOR ? 4 * M::WB : 16];   // mask blocks of the 4 waves
+  __shared__ __attribute__((aligned(16))) char ft_mb[TENSOR ? 4 * M::WB : 16];
   lds_char* const ka = (lds_char*)ft_ka;
   lds_char* const kb = (lds_char*)ft_kb;
   lds_char* const va = (lds_char*)ft_va;
@@ -150,8 +172,31 @@ __global__ __launch_bounds__(256, 3) void flash_tiled_kernel(FwdParams p, int hp
     kvo[j] = row * rstride + ((pos ^ C::kswz(row)) << 4);
     vvo[j] = row * rstride + ((pos ^ C::vswz(row)) << 4);
   }
+  // Mask block of this wave: rows wq0 .. wq0 + 31, keys of the tile; the
+  // descriptor's record count ends at the mask's last element (reads past it are 0).
+  const char* mbase = nullptr;
+  int mvo[4] = {0, 0, 0, 0};
+  if (TENSOR) {
+    mbase = (const char*)p.mdata + (b * p.ms[0] + h * p.ms[1] + wq0 * p.ms[2]) * M::ES;
+#pragma unroll
+    for (int j = 0; j < M::NI; ++j) {
+      const int L = 64 * j + lane, row = L / M::CPR, pos = L % M::CPR;
+      mvo[j] = row * (int)(p.ms[2] * M::ES) + ((pos ^ M::swz(row)) << 4);
+    }
+  }
   auto stage = [&](int t, auto par) {
     constexpr int PAR = decltype(par)::value;
+    if (TENSOR) {
+      const int64_t moff = (mbase - (const char*)p.mdata) + (int64_t)t * BN * M::ES;
+      const int mrec = (int)max((int64_t)0, min(mask_bytes - moff, (int64_t)0x7fffffff));
+      const __amdgpu_buffer_rsrc_t mrs =
+          __builtin_amdgcn_make_buffer_rsrc((void*)(mbase + (int64_t)t * BN * M::ES), 0, mrec, 0x00020000);
+#pragma unroll
+      for (int j = 0; j < M::NI; ++j)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            mrs, (__attribute__((address_space(3))) void*)((lds_char*)(PAR ? ft_mb : ft_ma) + M::WB * wave + 1024 * j), 16,
+            mvo[j], 0, 0, 0);
+    }
     const int64_t tb = (int64_t)t * BN * rstride;
     const int nrec = (int)max((int64_t)0, min(span - tb, (int64_t)0x7fffffff));
     const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)(kbase + tb), 0, nrec, 0x00020000);
@@ -196,6 +241,29 @@ __global__ __launch_bounds__(256, 3) void flash_tiled_kernel(FwdParams p, int hp
     f32x16 s = (f32x16){};
 #pragma unroll
     for (int c = 0; c < C::QC; ++c) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(ks + kro[c]), qf[c], s, 0, 0, 0);
+    if (TENSOR) {
+      // this lane's 16 mask values: keys 8 * i4 + 4g + e of the tile, row ql
+      const lds_char* mrow = (const lds_char*)(PAR ? ft_mb : ft_ma) + M::WB * wave + ql * M::ROWB;
+      const float inv_scale = 1.0f / p.scale;
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int byte = (8 * i4 + 4 * g) * M::ES;
+        const lds_char* a = mrow + (((byte >> 4) ^ M::swz(ql)) << 4) + (byte & 15);
+        if (MODE == T_ADD_F32) {
+          const f32x4 v = *(const __attribute__((address_space(3))) f32x4*)a;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) s[4 * i4 + e] = fmaf(v[e], inv_scale, s[4 * i4 + e]);
+        } else if (MODE == T_ADD_BF16) {
+          const bf16x4 v = *(const __attribute__((address_space(3))) bf16x4*)a;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) s[4 * i4 + e] = fmaf((float)v[e], inv_scale, s[4 * i4 + e]);
+        } else {
+          const unsigned v = *(const __attribute__((address_space(3))) unsigned*)a;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) s[4 * i4 + e] = ((v >> (8 * e)) & 0xffu) ? s[4 * i4 + e] : -INFINITY;
+        }
+      }
+    }
     bool partial = k0 + BN > p.Tkv;
     if (MODE == T_INDEX) {
       if (k0 + BN - 1 > wq0 + p.offset) partial = true;
@@ -300,22 +368,58 @@ __global__ __launch_bounds__(256, 3) void flash_tiled_kernel(FwdParams p, int hp
   if (p.lse && g == 0) p.lse[(b * p.Hq + h) * p.Tq + qrow] = lt > 0.0f ? (m + __log2f(lt)) * kLn2 : -INFINITY;
 }
 
+int mask_es(const FwdParams& p) { return p.bias == BIAS_BOOL ? 1 : (p.mdtype == 0 ? 4 : 2); }
+
 template <int D, int MODE>
 hipError_t launch_t(const FwdParams& p, hipStream_t s) {
   const int64_t grp = p.Hq / p.Hkv;
   const int hpw = (grp % 4 == 0) ? 4 : (grp % 2 == 0) ? 2 : 1;
   const int64_t rows = 32 * (4 / hpw);
   dim3 grid((unsigned)((p.Tq + rows - 1) / rows), (unsigned)(p.Hq / hpw), (unsigned)p.B);
-  if (p.out_dtype == 1) hipLaunchKernelGGL((flash_tiled_kernel<D, MODE, true>), grid, dim3(256), 0, s, p, hpw);
-  else hipLaunchKernelGGL((flash_tiled_kernel<D, MODE, false>), grid, dim3(256), 0, s, p, hpw);
+  // Record count of the mask descriptors: through the end of the 16-byte chunk
+  // that holds the last element.  The copies move whole chunks and the
+  // descriptor zeroes every dword past the record count, so a count that
+  // stopped inside the last chunk would zero the last valid elements; the
+  // chunk itself (16-byte aligned, like the base) lies within the allocation's
+  // last page.  Bytes past the last element land on keys >= Tkv, masked anyway.
+  int64_t mask_bytes = 0;
+  if (MODE >= T_ADD_F32)
+    mask_bytes = ((p.B - 1) * p.ms[0] + (p.Hq - 1) * p.ms[1] + (p.Tq - 1) * p.ms[2] + (p.Tkv - 1) * p.ms[3] + 1) *
+                 mask_es(p);
+  mask_bytes = (mask_bytes + 15) & ~(int64_t)15;
+  if (p.out_dtype == 1) hipLaunchKernelGGL((flash_tiled_kernel<D, MODE, true>), grid, dim3(256), 0, s, p, hpw, mask_bytes);
+  else hipLaunchKernelGGL((flash_tiled_kernel<D, MODE, false>), grid, dim3(256), 0, s, p, hpw, mask_bytes);
   return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_d(const FwdParams& p, hipStream_t s) {
+  switch (p.bias) {
+    case BIAS_CAUSAL:
+    case BIAS_SLIDING: return launch_t<D, T_INDEX>(p, s);
+    case BIAS_ADDITIVE: return p.mdtype == 0 ? launch_t<D, T_ADD_F32>(p, s) : launch_t<D, T_ADD_BF16>(p, s);
+    case BIAS_BOOL: return launch_t<D, T_BOOL>(p, s);
+    default: return launch_t<D, T_NONE>(p, s);
+  }
 }
 
 }  // namespace
 
 bool tiled_supports(const FwdParams& p) {
   if (p.dtype != 1 || (p.D != 64 && p.D != 128) || p.num_splits != 1) return false;
-  if (p.bias != BIAS_NONE && p.bias != BIAS_CAUSAL && p.bias != BIAS_SLIDING) return false;
+  if (p.bias == BIAS_ADDITIVE || p.bias == BIAS_BOOL) {
+    // mask blocks are copied by 16-byte chunks along contiguous keys; row
+    // offsets of one block and every element offset stay within 32 / 64 bits
+    if (p.ms[3] != 1 || !p.mdata) return false;
+    if (p.bias == BIAS_ADDITIVE && p.mdtype != 0 && p.mdtype != 1) return false;
+    const int64_t es = mask_es(p);
+    if (p.ms[0] < 0 || p.ms[1] < 0 || p.ms[2] < 0 || 32 * p.ms[2] * es > 0x7fffffffLL) return false;
+    if (((uintptr_t)p.mdata & 15) != 0 || (p.ms[2] * es) % 16 != 0 || (p.ms[1] * es) % 16 != 0 ||
+        (p.ms[0] * es) % 16 != 0)
+      return false;
+  } else if (p.bias != BIAS_NONE && p.bias != BIAS_CAUSAL && p.bias != BIAS_SLIDING) {
+    return false;
+  }
   if ((int64_t)BN * p.k_st * 2 > 0x7fffffffLL) return false;     // 32-bit byte offsets within a tile
   if (p.B > 65535 || p.Hq > 65535 || (p.Tq + 31) / 32 > 0x7fffffffLL) return false;   // grid limits
   if (p.Tkv > 0x3fffffffLL) return false;                         // key indices in 32-bit lanes
@@ -323,9 +427,7 @@ bool tiled_supports(const FwdParams& p) {
 }
 
 hipError_t launch_tiled(const FwdParams& p, hipStream_t s) {
-  const bool idx = p.bias == BIAS_CAUSAL || p.bias == BIAS_SLIDING;
-  if (p.D == 64) return idx ? launch_t<64, T_INDEX>(p, s) : launch_t<64, T_NONE>(p, s);
-  return idx ? launch_t<128, T_INDEX>(p, s) : launch_t<128, T_NONE>(p, s);
+  return p.D == 64 ? launch_d<64>(p, s) : launch_d<128>(p, s);
 }
 
 }  // namespace sdpa

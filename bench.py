@@ -73,6 +73,9 @@ def byte_model(wl):
 
 
 def run_call(fa, wl, g, out):
+    if "bias" in g:                 # the materialised-bias route: rel-pos bias as an additive mask
+        return fa.sdpa(g["q"], g["k"], g["v"], layout=wl.layout, scale=wl.scale,
+                       mask={"kind": "additive", "data": g["bias"]}, out=out)
     if wl.relpos:
         return fa.sdpa_relpos(g["q"], g["k"], g["v"], g["rel_pos_h"], g["rel_pos_w"], wl.grid, layout=wl.layout,
                               scale=wl.scale, out=out, workspace=g.get("ws"))
@@ -139,7 +142,7 @@ def kernel_events(fa, wl, g, steps, reps=5):
 
     call_ms = timed(lambda: run_call(fa, wl, g, out))
     terms_ms = 0.0
-    if wl.relpos and not fa.relpos_fused(g["q"].dtype, wl.D, wl.grid):
+    if wl.relpos and "bias" not in g and not fa.relpos_fused(g["q"].dtype, wl.D, wl.grid):
         terms_ms = timed(lambda: fa.relpos_terms(g["q"], g["rel_pos_h"], g["rel_pos_w"], wl.grid, layout=wl.layout))
     return call_ms, terms_ms
 
@@ -227,6 +230,9 @@ def main():
     ap.add_argument("--workload", default="sam_global_relpos")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--route", choices=["relpos", "additive"], default="relpos",
+                    help="rel-pos workloads: 'additive' times the bias materialised as a [B, H, T, T] "
+                         "additive mask in the input dtype (formed before timing) instead of the fused terms")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB per step (counter calibration)")
     args = ap.parse_args()
@@ -252,21 +258,32 @@ def main():
     if wl.relpos:
         n = fa.workspace_size(wl.B, wl.Hq, wl.Hkv, wl.Tq, wl.Tkv, wl.D, True, wl.grid)
         g["ws"] = torch.empty(n, dtype=torch.uint8, device="cuda")
+    if args.route == "additive":
+        if not wl.relpos:
+            print("bench.py: --route additive needs a rel-pos workload", file=sys.stderr)
+            sys.exit(2)
+        th, tw = fa.relpos_terms(g["q"], g["rel_pos_h"], g["rel_pos_w"], wl.grid, layout=wl.layout)
+        j = torch.arange(wl.grid[0] * wl.grid[1], device="cuda")
+        g["bias"] = (th[..., j // wl.grid[1]] + tw[..., j % wl.grid[1]]).to(g["q"].dtype).contiguous()
+        del th, tw, j
     torch.cuda.synchronize()
 
     sec = time_gpu(fa, wl, g, args.steps, args.warmup)
     attn, bias = flop_model(wl)
+    if args.route == "additive":
+        bias = 2 * allowed_pairs(wl) * wl.B * wl.Hq      # the terms were formed before timing
     total = attn + bias
     tflops = total / sec / 1e12
     call_ms, terms_ms = kernel_events(fa, wl, g, args.steps)
     run_call(fa, wl, g, torch.empty_like(g["q"]))
     kernel = fa.last_kernel()
-    traffic, traffic_src = recorded_traffic(kernel, wl.name)
+    traffic, traffic_src = recorded_traffic(kernel, wl.name if args.route == "relpos" else wl.name + "_additive")
     flash_ms = call_ms - terms_ms
     flash_flops = attn + (2 * allowed_pairs(wl) * wl.B * wl.Hq if wl.relpos else 0)
     if wl.relpos and terms_ms == 0.0:
         flash_flops = total             # terms formed inside the flash kernel: one launch per call
     achieved = flash_flops / (flash_ms * 1e-3) / 1e12
+    nbytes = byte_model(wl) + (g["bias"].numel() * g["bias"].element_size() if "bias" in g else 0)
     line = {
         "metric": "attention TFLOP/s + % bf16 MFMA peak, SAM ViT-B 64x64 global rel-pos SDPA",
         "value": round(tflops, 3),
@@ -290,8 +307,14 @@ def main():
                      "traffic_source": traffic_src,
                      "kernel": kernel, "kernel_ms": round(flash_ms, 5),
                      "terms_kernel_ms": round(terms_ms, 5), "flop_per_launch": flash_flops,
-                     "algorithmic_bytes_per_launch": byte_model(wl)},
+                     "algorithmic_bytes_per_launch": nbytes},
     }
+    if args.route == "additive":
+        # Reading the materialised bias bounds this route: report it against HBM.
+        gbs = nbytes / (flash_ms * 1e-3) / 1e9
+        line["config"]["route"] = "additive mask (bias materialised before timing)"
+        line["roofline"].update({"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                 "frac": round(gbs / HBM_PEAK_GBS, 4), "attention_tflops": round(achieved, 3)})
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(wl, x, args.cpu_budget)
     print(json.dumps(line))

@@ -337,7 +337,9 @@ def test_dispatch_names_the_kernel(gpu):
     assert run(4, 1, 300, 300, 128, mask={"kind": "causal", "offset": 0}) == "flash_tiled_kernel"
     assert run(2, 2, 300, 300, 64) == "flash_split64_kernel"
     add = {"kind": "additive", "data": rnd((1, 1, 300, 300), torch.float32, 4)}
-    assert run(2, 2, 300, 300, 64, mask=add) == "flash_mfma_kernel"
+    assert run(2, 2, 300, 300, 64, mask=add) == "flash_tiled_kernel"
+    keyb = {"kind": "additive", "data": rnd((1, 1, 300, 1), torch.float32, 4)}     # broadcast along keys
+    assert run(2, 2, 300, 300, 64, mask=keyb) == "flash_mfma_kernel"
     assert run(2, 2, 100, 100, 64, dtype=torch.float32) == "generic_fwd_kernel"
     assert run(8, 8, 7, 500, 16) == "d16_qpack_kernel"
     assert run(8, 8, 500, 7, 16) == "d16_kpack_kernel"
@@ -352,3 +354,34 @@ def test_dispatch_names_the_kernel(gpu):
     gpu.sdpa_relpos(x["q"], x["k"], x["v"], x["rel_pos_h"], x["rel_pos_w"], wl.grid)
     torch.cuda.synchronize()
     assert gpu.last_kernel() == "flash_window_kernel"
+
+
+def _mask_store(shape, Tkv_store, kind, mdt, seed):
+    """Storage for a mask of `shape` (last axis Tkv) with rows Tkv_store wide."""
+    full = rnd(shape[:-1] + (Tkv_store,), torch.float32, seed)
+    if kind == "bool":
+        full = full > -0.5
+        full[..., :3] = True
+        return full
+    return full.to(mdt)
+
+
+@pytest.mark.parametrize("tiled", [0, 1])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("kind,mdt", [("additive", torch.float32), ("additive", torch.bfloat16), ("bool", torch.bool)])
+@pytest.mark.parametrize("mshape,Tkv_store", [((2, 4, 100, 224), 224), ((1, 1, 100, 201), 208), ((2, 1, 1, 201), 208),
+                                              ((1, 4, 100, 201), 208)])
+def test_tensor_mask_kernels(gpu, tiled, D, kind, mdt, mshape, Tkv_store):
+    """Additive (fp32, bf16) and boolean masks with broadcast strides and rows
+    wider than the key range, through the double-buffered kernel (mask blocks
+    copied to LDS) and through the general MFMA kernel: both against the oracle."""
+    full = _mask_store(mshape, Tkv_store, kind, mdt, seed=D + len(kind))
+    Tkv = mshape[-1]
+    m, mg = full[..., :Tkv], full.cuda()[..., :Tkv]       # the same strided view on both sides
+    assert mg.stride() == m.stride()
+    gpu.set_tuning("tiled", tiled)
+    try:
+        check(gpu, 2, 4, 2, 100, Tkv, D, mask={"kind": kind, "data": mg}, seed=D,
+              omask={"kind": kind, "data": m.contiguous()})
+    finally:
+        gpu.set_tuning("tiled", 1)
