@@ -125,8 +125,15 @@ int launch(const sdpa::FwdParams& p, hipStream_t s) {
   return SDPA_OK;
 }
 
+// True if the attention kernel the call reaches forms the rel-pos terms itself
+// (no relpos_terms launch, no term arrays): the MFMA kernels for 64-wide grids
+// and 14 x 14 windows, or the generic kernel where tables and term rows fit its LDS.
 bool relpos_fused_ok(const sdpa::FwdParams& p) {
-  return p.scale > 0.0f && std::isfinite(p.scale) && (sdpa::relpos_fused_supported(p) || sdpa::window_supports(p));
+  // Without term arrays a rel-pos call reaches an MFMA kernel only through
+  // these two tests; every other one runs on the generic kernel.
+  const bool fast = p.scale > 0.0f && std::isfinite(p.scale);
+  if (fast && (sdpa::relpos_fused_supported(p) || sdpa::window_supports(p))) return true;
+  return sdpa::generic_relpos_supported(p, true);
 }
 
 }  // namespace

@@ -3,7 +3,8 @@
 // MFMA kernels do not cover.
 //
 // One wave per block, one query row per lane.  K/V tiles of 32 keys are staged
-// through LDS as fp32; each lane keeps its query row and output accumulator in
+// through LDS as fp32 (rel-pos: each lane's term rows too, formed here from
+// the tables when the grid is small); each lane keeps its query row and output accumulator in
 // registers and runs the online softmax (running max m, running sum l; the
 // accumulator is rescaled by exp(m_old - m_new) when the max grows), so no
 // score row is ever stored.
@@ -26,6 +27,10 @@ __global__ __launch_bounds__(64) void generic_fwd_kernel(FwdParams p) {
   __shared__ float ks[BK][DMAX];
   __shared__ float vs[BK][DMAX];
   __shared__ float zs[BK][64];        // this tile's scores, one column per lane
+  // Rel-pos: each lane's term_h row (grid_h values) and term_w row (grid_w
+  // values) in LDS, [grid_h + grid_w][64 lanes]; with the fused terms the two
+  // tables follow ([2 grid_h - 1 + 2 grid_w - 1][D]).
+  extern __shared__ float dyn[];
   const int lane = threadIdx.x;
   const int64_t b = blockIdx.z, h = blockIdx.y;
   const int64_t i0 = (int64_t)blockIdx.x * 64;
@@ -56,25 +61,96 @@ __global__ __launch_bounds__(64) void generic_fwd_kernel(FwdParams p) {
       if (lo < 0) lo = 0;
     }
   }
-  const float* th = nullptr;
-  const float* tw = nullptr;
-  if (GF == GF_RELPOS) {
-    th = p.term_h + ((b * p.Hq + h) * p.Tq + (live ? i : 0)) * p.grid_h;
-    tw = p.term_w + ((b * p.Hq + h) * p.Tq + (live ? i : 0)) * p.grid_w;
+  const int gh = p.grid_h, gw = p.grid_w;
+  // Grids too large for LDS rows read the workspace terms from memory.
+  const bool rows_in_lds = (GF == GF_RELPOS) && (p.relpos_rows_lds != 0);
+  const float* thg = nullptr;
+  const float* twg = nullptr;
+  if (GF == GF_RELPOS && !rows_in_lds) {
+    const int64_t is = live ? i : 0;
+    thg = p.term_h + ((b * p.Hq + h) * p.Tq + is) * gh;
+    twg = p.term_w + ((b * p.Hq + h) * p.Tq + is) * gw;
+  }
+  if (rows_in_lds) {
+    const int64_t is = live ? i : 0;
+    if (p.term_h) {                   // terms from the workspace
+      const float* th = p.term_h + ((b * p.Hq + h) * p.Tq + is) * gh;
+      const float* tw = p.term_w + ((b * p.Hq + h) * p.Tq + is) * gw;
+#pragma unroll 4
+      for (int y = 0; y < gh; ++y) dyn[y * 64 + lane] = th[y];
+#pragma unroll 4
+      for (int x = 0; x < gw; ++x) dyn[(gh + x) * 64 + lane] = tw[x];
+    } else {                          // terms formed here: term[i, y] = q_i . table[coord(i) - y + G - 1]
+      float* tab = dyn + (gh + gw) * 64;
+      const int nh = 2 * gh - 1, nw = 2 * gw - 1;
+#pragma unroll 8
+      for (int e = lane; e < (nh + nw) * D; e += 64) {
+        const int r = e / D, c = e % D;
+        tab[e] = r < nh ? to_f32(((const TIN*)p.rel_h)[r * D + c]) : to_f32(((const TIN*)p.rel_w)[(r - nh) * D + c]);
+      }
+      __syncthreads();
+      const int ih = (int)(is / gw), iw = (int)(is % gw);
+      for (int y = 0; y < gh; ++y) {
+        const float* row = tab + (ih - y + gh - 1) * D;
+        float d = 0.0f;
+#pragma unroll
+        for (int c = 0; c < DMAX; ++c) d = (c < D) ? fmaf(qr[c], row[c], d) : d;
+        dyn[y * 64 + lane] = d;
+      }
+      for (int x = 0; x < gw; ++x) {
+        const float* row = tab + (nh + iw - x + gw - 1) * D;
+        float d = 0.0f;
+#pragma unroll
+        for (int c = 0; c < DMAX; ++c) d = (c < D) ? fmaf(qr[c], row[c], d) : d;
+        dyn[(gh + x) * 64 + lane] = d;
+      }
+    }
   }
 
+  // Tile copies.  With D == DMAX and 16-byte aligned rows every lane moves
+  // whole 16-byte pieces, all loads of a tile issued before any LDS store (one
+  // memory round trip per tile); other shapes copy element by element.
+  constexpr int EPP = 16 / sizeof(TIN);               // elements per 16-byte piece
+  constexpr int PPL = BK * DMAX / EPP / 64;           // pieces per lane per tensor
+  const bool vec = D == DMAX && (p.k_st % EPP) == 0 && (((uintptr_t)kp | (uintptr_t)vp) & 15) == 0;
   for (int64_t j0 = lo; j0 < hi; j0 += BK) {
     __syncthreads();
-    for (int e = lane; e < BK * DMAX; e += 64) {
-      const int jj = e / DMAX, c = e % DMAX;
-      const int64_t j = j0 + jj;
-      const bool ok = j < hi && c < D;
-      ks[jj][c] = ok ? to_f32(kp[j * p.k_st + c]) : 0.0f;
-      vs[jj][c] = ok ? to_f32(vp[j * p.k_st + c]) : 0.0f;
+    if (vec) {
+      typedef TIN tin16 __attribute__((ext_vector_type(EPP)));
+      tin16 kr[PPL], vr[PPL];
+#pragma unroll
+      for (int u = 0; u < PPL; ++u) {
+        const int e = lane + 64 * u, jj = e / (DMAX / EPP), c = (e % (DMAX / EPP)) * EPP;
+        const int64_t j = j0 + jj;
+        kr[u] = j < hi ? *(const tin16*)(kp + j * p.k_st + c) : (tin16){};
+        vr[u] = j < hi ? *(const tin16*)(vp + j * p.k_st + c) : (tin16){};
+      }
+#pragma unroll
+      for (int u = 0; u < PPL; ++u) {
+        const int e = lane + 64 * u, jj = e / (DMAX / EPP), c = (e % (DMAX / EPP)) * EPP;
+#pragma unroll
+        for (int x = 0; x < EPP; ++x) {
+          ks[jj][c + x] = to_f32(kr[u][x]);
+          vs[jj][c + x] = to_f32(vr[u][x]);
+        }
+      }
+    } else {
+      for (int e = lane; e < BK * DMAX; e += 64) {
+        const int jj = e / DMAX, c = e % DMAX;
+        const int64_t j = j0 + jj;
+        const bool ok = j < hi && c < D;
+        ks[jj][c] = ok ? to_f32(kp[j * p.k_st + c]) : 0.0f;
+        vs[jj][c] = ok ? to_f32(vp[j * p.k_st + c]) : 0.0f;
+      }
     }
     __syncthreads();
     const int nk = (int)((hi - j0 < BK) ? hi - j0 : BK);
     float tmax = -INFINITY;
+    int jh = 0, jw = 0;                 // grid row and column of key j0 + jj
+    if (GF == GF_RELPOS) {
+      jh = (int)(j0 / gw);
+      jw = (int)(j0 % gw);
+    }
 #pragma unroll 2
     for (int jj = 0; jj < nk; ++jj) {
       const int64_t j = j0 + jj;
@@ -84,7 +160,13 @@ __global__ __launch_bounds__(64) void generic_fwd_kernel(FwdParams p) {
       float z = d * p.scale;
       bool ok = live;
       if (GF == GF_INDEX) ok = ok && index_allowed(p.bias, i, j, p.offset, p.window);
-      if (GF == GF_RELPOS && ok) z += th[j / p.grid_w] + tw[j % p.grid_w];
+      if (GF == GF_RELPOS) {
+        z += rows_in_lds ? dyn[jh * 64 + lane] + dyn[(gh + jw) * 64 + lane] : thg[jh] + twg[jw];
+        if (++jw == gw) {
+          jw = 0;
+          ++jh;
+        }
+      }
       if (GF == GF_TENSOR && ok) z += tensor_mask_bias(p, b, h, i, j);
       z = ok ? z : -INFINITY;
       zs[jj][lane] = z;
@@ -123,13 +205,32 @@ __global__ __launch_bounds__(64) void generic_fwd_kernel(FwdParams p) {
   if (p.lse) p.lse[(b * p.Hq + h) * p.Tq + i] = (l > 0.0f) ? m + logf(l) : -INFINITY;
 }
 
+// Bytes of dynamic LDS for rel-pos: per-lane term rows, plus the tables when
+// the terms are formed in the kernel.
+size_t relpos_lds(const FwdParams& p, bool fused) {
+  size_t n = (size_t)(p.grid_h + p.grid_w) * 64;
+  if (fused) n += (size_t)(2 * p.grid_h - 1 + 2 * p.grid_w - 1) * p.D;
+  return n * sizeof(float);
+}
+
+int dmax_of(int64_t D) { return D <= 16 ? 16 : D <= 32 ? 32 : D <= 64 ? 64 : 128; }
+
+// Static LDS of one instance: K and V tiles plus the score column block.
+size_t static_lds(int64_t D) { return (size_t)2 * 32 * dmax_of(D) * 4 + 32 * 64 * 4; }
+
 template <typename TIN, int DMAX>
 static void launch_dim(const FwdParams& p, dim3 grid, hipStream_t s) {
   switch (p.bias) {
     case BIAS_NONE: hipLaunchKernelGGL((generic_fwd_kernel<TIN, DMAX, GF_NONE>), grid, dim3(64), 0, s, p); break;
     case BIAS_CAUSAL:
     case BIAS_SLIDING: hipLaunchKernelGGL((generic_fwd_kernel<TIN, DMAX, GF_INDEX>), grid, dim3(64), 0, s, p); break;
-    case BIAS_RELPOS: hipLaunchKernelGGL((generic_fwd_kernel<TIN, DMAX, GF_RELPOS>), grid, dim3(64), 0, s, p); break;
+    case BIAS_RELPOS: {
+      FwdParams q = p;
+      q.relpos_rows_lds = generic_relpos_supported(p, !p.term_h) ? 1 : 0;
+      hipLaunchKernelGGL((generic_fwd_kernel<TIN, DMAX, GF_RELPOS>), grid, dim3(64),
+                         q.relpos_rows_lds ? relpos_lds(p, !p.term_h) : 0, s, q);
+      break;
+    }
     default: hipLaunchKernelGGL((generic_fwd_kernel<TIN, DMAX, GF_TENSOR>), grid, dim3(64), 0, s, p); break;
   }
 }
@@ -142,6 +243,10 @@ static hipError_t launch_typed(const FwdParams& p, hipStream_t s) {
   else if (p.D <= 64) launch_dim<TIN, 64>(p, grid, s);
   else launch_dim<TIN, 128>(p, grid, s);
   return hipGetLastError();
+}
+
+bool generic_relpos_supported(const FwdParams& p, bool fused) {
+  return p.grid_h >= 1 && p.grid_w >= 1 && static_lds(p.D) + relpos_lds(p, fused) <= 64 * 1024;
 }
 
 hipError_t launch_generic_fwd(const FwdParams& p, hipStream_t s) {

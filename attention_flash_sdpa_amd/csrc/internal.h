@@ -38,6 +38,7 @@ struct FwdParams {
   const void* rel_h;          // rel-pos tables for kernels that form the terms themselves
   const void* rel_w;
   int grid_h, grid_w;
+  int relpos_rows_lds;        // generic kernel: term rows staged in LDS (set by its launcher)
   int num_splits;             // split-KV chunks (1 = no split)
   float* part_o;              // split-KV partial outputs [splits, B, Hq, Tq, D] fp32
   float* part_ml;             // split-KV partial (max, sum) [splits, B, Hq, Tq, 2] fp32
@@ -60,6 +61,8 @@ constexpr bool kSplitKvBuilt = true;
 
 // Launchers: return hipSuccess or the launch error.  Each only enqueues work.
 hipError_t launch_generic_fwd(const FwdParams& p, hipStream_t s);
+// Rel-pos on the generic kernel: the per-lane term rows (and, fused, the tables) fit its LDS.
+bool generic_relpos_supported(const FwdParams& p, bool fused);
 hipError_t launch_relpos_terms(const TermsParams& p, hipStream_t s);
 hipError_t launch_flash_mfma(const FwdParams& p, hipStream_t s);   // bf16, D in {64, 128}
 bool flash_mfma_supports(const FwdParams& p);

@@ -126,7 +126,9 @@ def test_status_strings_and_tuning():
     assert lib.sdpa_set_tuning(b"relpos_fused", 1) == 0
     assert lib.sdpa_relpos_fused(1, 64, 64, 64) == 1      # SAM ViT-B global grid: one kernel
     assert lib.sdpa_relpos_fused(1, 64, 14, 14) == 1      # SAM 14x14 window: one kernel
-    assert lib.sdpa_relpos_fused(1, 64, 13, 14) == 0      # other windowed grids: terms kernel first
+    assert lib.sdpa_relpos_fused(1, 64, 13, 14) == 1      # other small grids: generic kernel forms the terms
+    assert lib.sdpa_relpos_fused(0, 16, 8, 8) == 1        # tiny fp32 grid: generic kernel forms the terms
+    assert lib.sdpa_relpos_fused(1, 128, 64, 64) == 0     # tables too large to stage: terms kernel first
     assert lib.sdpa_relpos_fused(0, 64, 64, 64) == 0
     assert lib.sdpa_set_tuning(b"relpos_fused", 0) == 0
     assert lib.sdpa_relpos_fused(1, 64, 64, 64) == 0
