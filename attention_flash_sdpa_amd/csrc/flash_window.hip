@@ -44,6 +44,7 @@ typedef __attribute__((address_space(3))) float lds_float;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kTau = 8.0f;
+constexpr float kTauSum = 256.0f;
 
 constexpr int G = 14;                 // grid side of a window
 constexpr int T = G * G;              // tokens per window
@@ -189,38 +190,45 @@ __global__ __launch_bounds__(NW * 64, 4) void flash_window_kernel(FwdParams p) {
     for (int c = 0; c < 4; ++c) kf[c] = lds_b128(ks + kr * ROWB + (((2 * c + g) ^ kswz(kr)) << 4));
 #pragma unroll
     for (int c = 0; c < 4; ++c) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[c], qf[c], s, 0, 0, 0);
-    float smax = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+    // Probabilities against the running reference m; only a tile whose row
+    // sum passes 2^8 (or the first tile) takes the exact path that moves m
+    // to the tile max and rescales O and l.
+    bf16x8 pb[2];
+    auto probs = [&](float off) -> float {
+      float acc0 = 0.0f, acc1 = 0.0f;
 #pragma unroll
-    for (int i = 4; i < 16; i += 2) smax = fmaxf(smax, fmaxf(s[i], s[i + 1]));
-    const float tmax = pair_max(smax) * c2;
-    const bool need = tmax > m + kTau;
-    const float mn = need ? tmax : m;
-    const float alpha = (need && m != -INFINITY) ? fexp2(m - mn) : (need ? 0.0f : 1.0f);
-    if (__any(need)) {
+      for (int tc = 0; tc < 2; ++tc) {
+        bf16x2 pk[4];
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const f32x2 pp = {fexp2(fmaf(s[8 * tc + e], c2, off)), fexp2(fmaf(s[8 * tc + e + 1], c2, off))};
+          pk[e / 2] = __builtin_convertvector(pp, bf16x2);
+          if (e & 2) acc1 = __builtin_amdgcn_fdot2_f32_bf16(pk[e / 2], (bf16x2){(__bf16)1.0f, (__bf16)1.0f}, acc1, false);
+          else acc0 = __builtin_amdgcn_fdot2_f32_bf16(pk[e / 2], (bf16x2){(__bf16)1.0f, (__bf16)1.0f}, acc0, false);
+        }
+        pb[tc] = __builtin_shufflevector(__builtin_shufflevector(pk[0], pk[1], 0, 1, 2, 3),
+                                         __builtin_shufflevector(pk[2], pk[3], 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
+      }
+      return acc0 + acc1;
+    };
+    float lt = probs((m == -INFINITY) ? 0.0f : -m);
+    if (__builtin_expect(__any(!(lt <= kTauSum) || m == -INFINITY), 0)) {
+      float smax = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+#pragma unroll
+      for (int i = 4; i < 16; i += 2) smax = fmaxf(smax, fmaxf(s[i], s[i + 1]));
+      const float tmax = pair_max(smax) * c2;
+      const bool need = tmax > m + kTau;
+      const float mn = need ? tmax : m;
+      const float alpha = need ? ((m == -INFINITY) ? 0.0f : fexp2(m - mn)) : 1.0f;
+      m = mn;
       l *= alpha;
 #pragma unroll
       for (int d = 0; d < 2; ++d)
 #pragma unroll
         for (int i = 0; i < 16; ++i) o[d][i] *= alpha;
+      lt = probs((m == -INFINITY) ? 0.0f : -m);
     }
-    m = mn;
-    const float off = -m;
-    bf16x8 pb[2];
-    float acc0 = 0.0f, acc1 = 0.0f;
-#pragma unroll
-    for (int tc = 0; tc < 2; ++tc) {
-      bf16x2 pk[4];
-#pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        const f32x2 pp = {fexp2(fmaf(s[8 * tc + e], c2, off)), fexp2(fmaf(s[8 * tc + e + 1], c2, off))};
-        pk[e / 2] = __builtin_convertvector(pp, bf16x2);
-        if (e & 2) acc1 = __builtin_amdgcn_fdot2_f32_bf16(pk[e / 2], (bf16x2){(__bf16)1.0f, (__bf16)1.0f}, acc1, false);
-        else acc0 = __builtin_amdgcn_fdot2_f32_bf16(pk[e / 2], (bf16x2){(__bf16)1.0f, (__bf16)1.0f}, acc0, false);
-      }
-      pb[tc] = __builtin_shufflevector(__builtin_shufflevector(pk[0], pk[1], 0, 1, 2, 3),
-                                       __builtin_shufflevector(pk[2], pk[3], 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
-    }
-    l += acc0 + acc1;
+    l += lt;
 #pragma unroll
     for (int tc = 0; tc < 2; ++tc)
 #pragma unroll

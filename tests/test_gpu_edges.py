@@ -385,3 +385,21 @@ def test_tensor_mask_kernels(gpu, tiled, D, kind, mdt, mshape, Tkv_store):
               omask={"kind": kind, "data": m.contiguous()})
     finally:
         gpu.set_tuning("tiled", 1)
+
+
+@pytest.mark.parametrize("qmul", [1.0, 12.0, 60.0])
+def test_window_running_max(gpu, qmul):
+    """The 14x14 window kernel's optimistic running max: scaled-up queries give
+    logits of tens to hundreds, so tiles past the first must move the reference
+    (exact path) or overflow; every case matches the definition."""
+    wl = workloads.replica("sam_window_relpos", B=1, Hq=2, Hkv=2)
+    x = workloads.generate(wl, seed=9, layout="bhsd")
+    x["q"] = (x["q"].float() * qmul).to(torch.bfloat16)
+    g = {k_: t.cuda() for k_, t in x.items()}
+    o = gpu.sdpa_relpos(g["q"], g["k"], g["v"], g["rel_pos_h"], g["rel_pos_w"], wl.grid, scale=wl.scale,
+                        out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert gpu.last_kernel() == "flash_window_kernel"
+    ref = oracle.sdpa(np64(x["q"]), np64(x["k"]), np64(x["v"]), scale=wl.scale,
+                      rel_pos={"rel_pos_h": np64(x["rel_pos_h"]), "rel_pos_w": np64(x["rel_pos_w"]), "grid": wl.grid})
+    assert max_err(np64(o), ref["o"]) <= TOL["bf16"]
