@@ -26,13 +26,14 @@ import threading
 import torch
 
 __all__ = ["load", "lib_path", "sdpa", "sdpa_relpos", "relpos_terms", "workspace_size", "relpos_fused",
-           "set_tuning", "SdpaError", "F32", "BF16", "BSHD", "BHSD"]
+           "set_tuning", "SdpaError", "F32", "BF16", "F16", "BSHD", "BHSD"]
 
-F32, BF16 = 0, 1
+F32, BF16, F16 = 0, 1, 2
 BSHD, BHSD = 0, 1
 _MASK_KIND = {"none": 0, "causal": 1, "sliding": 2, "additive": 3, "bool": 4}
 _LAYOUT = {"bshd": BSHD, "bhsd": BHSD}
-_DTYPE = {torch.float32: F32, torch.bfloat16: BF16}
+_DTYPE = {torch.float32: F32, torch.bfloat16: BF16, torch.float16: F16}
+_MASK_DTYPE = {torch.float32: F32, torch.bfloat16: BF16}
 
 
 class SdpaError(RuntimeError):
@@ -168,9 +169,9 @@ def _mask_struct(mask, B, Hq, Tq, Tkv, keep):
                 raise ValueError("bool masks must be torch.bool")
             data = data.view(torch.uint8)
         else:
-            if data.dtype not in _DTYPE:
+            if data.dtype not in _MASK_DTYPE:
                 raise ValueError("additive masks must be float32 or bfloat16")
-            m.data_dtype = _DTYPE[data.dtype]
+            m.data_dtype = _MASK_DTYPE[data.dtype]
         ex = data.expand(B, Hq, Tq, Tkv)
         for a in range(4):
             m.stride[a] = ex.stride(a)
@@ -191,7 +192,7 @@ def sdpa(q, k, v, *, layout="bhsd", scale=None, mask=None, out_dtype=None, retur
     lib = load()
     _need_gpu(q, k, v)
     if q.dtype not in _DTYPE or k.dtype != q.dtype or v.dtype != q.dtype:
-        raise ValueError("q, k, v must share dtype float32 or bfloat16")
+        raise ValueError("q, k, v must share dtype float32, bfloat16 or float16")
     B, Hq, Hkv, Tq, Tkv, D = _dims(q, k, layout)
     odt = q.dtype if out_dtype is None else out_dtype
     o = out if out is not None else torch.empty(q.shape, dtype=odt, device=q.device)
@@ -230,7 +231,7 @@ def sdpa_relpos(q, k, v, rel_pos_h, rel_pos_w, grid, *, layout="bhsd", scale=Non
     lib = load()
     _need_gpu(q, k, v, rel_pos_h, rel_pos_w)
     if q.dtype not in _DTYPE or k.dtype != q.dtype or v.dtype != q.dtype:
-        raise ValueError("q, k, v must share dtype float32 or bfloat16")
+        raise ValueError("q, k, v must share dtype float32, bfloat16 or float16")
     gh, gw = grid
     if layout == "bhsd":
         B, H, T, D = q.shape

@@ -35,7 +35,8 @@ int fail(int status, const char* fmt, ...) {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-bool dtype_ok(int d) { return d == SDPA_F32 || d == SDPA_BF16; }
+bool dtype_ok(int d) { return d == SDPA_F32 || d == SDPA_BF16 || d == SDPA_F16; }
+bool is16(int d) { return d == SDPA_BF16 || d == SDPA_F16; }
 
 void set_strides(int layout, int64_t H, int64_t T, int64_t D, int64_t* sb, int64_t* sh, int64_t* st) {
   if (layout == SDPA_BHSD) { *sb = H * T * D; *sh = T * D; *st = D; }
@@ -47,7 +48,7 @@ void set_strides(int layout, int64_t H, int64_t T, int64_t D, int64_t* sb, int64
 // are merged by their log-sum-exp afterwards.
 int plan_splits(int64_t B, int64_t Hq, int64_t Tq, int64_t Tkv, int64_t D, int dtype) {
   // split-KV exists for the head_dim-16 query-packed kernel (few queries)
-  if (!sdpa::kSplitKvBuilt || dtype != SDPA_BF16 || D != 16 || Tq > 8) return 1;
+  if (!sdpa::kSplitKvBuilt || !is16(dtype) || D != 16 || Tq > 8) return 1;
   const int64_t forced = g_num_splits.load();
   if (forced >= 1) return (int)std::min<int64_t>(forced, std::max<int64_t>(1, (Tkv + 63) / 64));
   // one wave per (4 heads, 8 queries, key chunk): aim at ~512 waves with
@@ -84,8 +85,8 @@ int check_dtypes(int dtype, int out_dtype, int layout, int64_t D) {
     return fail(SDPA_ERR_INVALID, "out_dtype must equal dtype or be SDPA_F32");
   if (layout != SDPA_BSHD && layout != SDPA_BHSD) return fail(SDPA_ERR_INVALID, "unknown layout %d", layout);
   if (D > 128) return fail(SDPA_ERR_UNSUPPORTED, "head_dim %lld > 128 is not built", (long long)D);
-  if (dtype == SDPA_BF16 && D != 16 && D != 32 && D != 64 && D != 128)
-    return fail(SDPA_ERR_UNSUPPORTED, "bf16 head_dim must be 16, 32, 64 or 128 (got %lld)", (long long)D);
+  if (is16(dtype) && D != 16 && D != 32 && D != 64 && D != 128)
+    return fail(SDPA_ERR_UNSUPPORTED, "16-bit head_dim must be 16, 32, 64 or 128 (got %lld)", (long long)D);
   return SDPA_OK;
 }
 
@@ -105,35 +106,49 @@ sdpa::FwdParams base_params(const void* q, const void* k, const void* v, void* o
   return p;
 }
 
-int launch(const sdpa::FwdParams& p, hipStream_t s) {
-  hipError_t e;
+enum Route { R_GENERIC, R_D16, R_WINDOW, R_SPLIT64, R_TILED, R_MFMA };
+
+// The kernel a call runs on: the first route whose conditions hold.
+Route route_of(const sdpa::FwdParams& p) {
   // The MFMA kernels take each row's running max on scores already multiplied
   // by scale, which needs scale > 0; other scales run on the generic kernel.
-  const bool fast = p.scale > 0.0f && std::isfinite(p.scale);
+  if (!(p.scale > 0.0f && std::isfinite(p.scale))) return R_GENERIC;
+  if (sdpa::d16_supports(p)) return R_D16;
+  if (sdpa::window_supports(p)) return R_WINDOW;
+  if (g_split64.load() && sdpa::split64_supports(p)) return R_SPLIT64;
+  if (g_tiled.load() && sdpa::tiled_supports(p)) return R_TILED;
+  if (sdpa::flash_mfma_supports(p)) return R_MFMA;
+  return R_GENERIC;
+}
+
+int launch(const sdpa::FwdParams& p, hipStream_t s) {
+  hipError_t e;
   const char* name;
-  if (!fast) { name = "generic_fwd_kernel"; e = sdpa::launch_generic_fwd(p, s); }
-  else if (sdpa::d16_supports(p)) {
-    name = p.Tq <= 8 ? "d16_qpack_kernel" : "d16_kpack_kernel";
-    e = sdpa::launch_d16(p, s);
-  } else if (sdpa::window_supports(p)) { name = "flash_window_kernel"; e = sdpa::launch_window(p, s); }
-  else if (g_split64.load() && sdpa::split64_supports(p)) { name = "flash_split64_kernel"; e = sdpa::launch_split64(p, s); }
-  else if (g_tiled.load() && sdpa::tiled_supports(p)) { name = "flash_tiled_kernel"; e = sdpa::launch_tiled(p, s); }
-  else if (sdpa::flash_mfma_supports(p)) { name = "flash_mfma_kernel"; e = sdpa::launch_flash_mfma(p, s); }
-  else { name = "generic_fwd_kernel"; e = sdpa::launch_generic_fwd(p, s); }
+  switch (route_of(p)) {
+    case R_D16:
+      name = p.Tq <= 8 ? "d16_qpack_kernel" : "d16_kpack_kernel";
+      e = sdpa::launch_d16(p, s);
+      break;
+    case R_WINDOW: name = "flash_window_kernel"; e = sdpa::launch_window(p, s); break;
+    case R_SPLIT64: name = "flash_split64_kernel"; e = sdpa::launch_split64(p, s); break;
+    case R_TILED: name = "flash_tiled_kernel"; e = sdpa::launch_tiled(p, s); break;
+    case R_MFMA: name = "flash_mfma_kernel"; e = sdpa::launch_flash_mfma(p, s); break;
+    default: name = "generic_fwd_kernel"; e = sdpa::launch_generic_fwd(p, s); break;
+  }
   g_last_kernel = name;
   if (e != hipSuccess) return fail(SDPA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return SDPA_OK;
 }
 
-// True if the attention kernel the call reaches forms the rel-pos terms itself
-// (no relpos_terms launch, no term arrays): the MFMA kernels for 64-wide grids
-// and 14 x 14 windows, or the generic kernel where tables and term rows fit its LDS.
+// True if the attention kernel a rel-pos call reaches without term arrays
+// forms the terms itself (no relpos_terms launch): every MFMA route that
+// accepts such a call does; the generic kernel does where the tables and the
+// per-lane term rows fit its LDS.
 bool relpos_fused_ok(const sdpa::FwdParams& p) {
-  // Without term arrays a rel-pos call reaches an MFMA kernel only through
-  // these two tests; every other one runs on the generic kernel.
-  const bool fast = p.scale > 0.0f && std::isfinite(p.scale);
-  if (fast && (sdpa::relpos_fused_supported(p) || sdpa::window_supports(p))) return true;
-  return sdpa::generic_relpos_supported(p, true);
+  sdpa::FwdParams q = p;
+  q.term_h = nullptr;
+  q.term_w = nullptr;
+  return route_of(q) != R_GENERIC || sdpa::generic_relpos_supported(q, true);
 }
 
 }  // namespace
@@ -175,7 +190,7 @@ int sdpa_fwd(const void* q, const void* k, const void* v, void* o, int dtype, in
       case SDPA_MASK_ADDITIVE:
       case SDPA_MASK_BOOL:
         if (!mask->data) return fail(SDPA_ERR_INVALID, "tensor mask needs a data pointer");
-        if (mask->kind == SDPA_MASK_ADDITIVE && !dtype_ok(mask->data_dtype))
+        if (mask->kind == SDPA_MASK_ADDITIVE && mask->data_dtype != SDPA_F32 && mask->data_dtype != SDPA_BF16)
           return fail(SDPA_ERR_INVALID, "additive mask dtype must be SDPA_F32 or SDPA_BF16");
         for (int a = 0; a < 4; ++a)
           if (mask->stride[a] < 0) return fail(SDPA_ERR_INVALID, "mask strides must be >= 0");

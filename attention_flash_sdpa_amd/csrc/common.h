@@ -8,6 +8,7 @@ namespace sdpa {
 
 __device__ __forceinline__ float to_f32(float x) { return x; }
 __device__ __forceinline__ float to_f32(__bf16 x) { return (float)x; }
+__device__ __forceinline__ float to_f32(_Float16 x) { return (float)x; }
 
 // Load one element of an additive (F32/BF16) or boolean (uint8) mask and turn it
 // into an additive bias: ADDITIVE adds the value, BOOL adds 0 (attend) or -inf.

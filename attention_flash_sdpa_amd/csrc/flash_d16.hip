@@ -4,7 +4,7 @@
 // [Candle PR 3280] "feat(metal): SDPA with Relative Positional Embeddings &
 // LayerNorm Stability", Key Changes: SDPA for head_dim 16 with a packed
 // vector kernel that processes two heads per SIMD group.  On gfx950 a wave
-// is 64 lanes and the bf16 matrix op is 32x32x16, whose 16-deep contraction
+// is 64 lanes and the 16-bit matrix op is 32x32x16, whose 16-deep contraction
 // is exactly one head of 16 dims; this file packs FOUR heads per wave:
 //
 //  * Query packing (few queries, long key range -- e.g. SAM's mask decoder,
@@ -23,12 +23,11 @@
 // Definition followed: [Axon PR 650] "Axon.Layers.scaled_dot_product_attention/4",
 // description (softmax(Q . K^T * scale + mask) . V; masks; grouped-query heads).
 #include "common.h"
+#include "elem16.h"
 
 namespace sdpa {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -56,9 +55,11 @@ __device__ __forceinline__ float bias_of(const FwdParams& p, int64_t b, int64_t 
 // ------------------------------------------------------------ query packing
 // grid: (splits, ceil(Tq / 8), B * ceil(Hq / 4)); one wave per block.
 // Lane column n = lane % 32 holds head hh = n / 8 of the group and query t = n % 8.
-template <int MF>
+template <typename E, int MF>
 __global__ __launch_bounds__(64) void d16_qpack_kernel(FwdParams p, int keys_per_split) {
-  __shared__ __attribute__((aligned(16))) __bf16 vl[4][32][16];     // V tile: [head][key][d]
+  typedef typename Vec16<E>::x8 e8;
+  typedef typename Vec16<E>::x4 e4;
+  __shared__ __attribute__((aligned(16))) E vl[4][32][16];     // V tile: [head][key][d]
   const int lane = threadIdx.x, g = lane >> 5, n = lane & 31;
   const int hh = n >> 3, t = n & 7;
   const int64_t ngrp = (p.Hq + 3) / 4;
@@ -72,12 +73,12 @@ __global__ __launch_bounds__(64) void d16_qpack_kernel(FwdParams p, int keys_per
   const bool colok = hcol < p.Hq && qcol < p.Tq;
 
   // Q'^T operands: chunk c carries head h0 + c, nonzero only in that head's columns.
-  bf16x8 qb[4];
+  e8 qb[4];
   {
-    bf16x8 qv = (bf16x8){};
-    if (colok) qv = *(const bf16x8*)((const __bf16*)p.q + b * p.q_sb + hcol * p.q_sh + qcol * p.q_st + 8 * g);
+    e8 qv = (e8){};
+    if (colok) qv = *(const e8*)((const E*)p.q + b * p.q_sb + hcol * p.q_sh + qcol * p.q_st + 8 * g);
 #pragma unroll
-    for (int c = 0; c < 4; ++c) qb[c] = (c == hh) ? qv : (bf16x8){};
+    for (int c = 0; c < 4; ++c) qb[c] = (c == hh) ? qv : (e8){};
   }
   const float c2 = p.scale * kLog2e;
   f32x16 o[2] = {(f32x16){}, (f32x16){}};
@@ -88,39 +89,39 @@ __global__ __launch_bounds__(64) void d16_qpack_kernel(FwdParams p, int keys_per
   //   K' row = key k0 + (lane % 32), chunk c = head h0 + c, dims 8g..8g+7.
   //   V piece e = lane + 64r: [head r][key (lane/2)%32][half lane%2].
   // Head bases are loop invariant; heads past Hq read nothing.
-  const __bf16* kh[4];
-  const __bf16* vh[4];
+  const E* kh[4];
+  const E* vh[4];
   bool hok[4];
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     hok[c] = h0 + c < p.Hq;
     const int64_t hk = (hok[c] ? h0 + c : h0) / grp;
-    kh[c] = (const __bf16*)p.k + b * p.k_sb + hk * p.k_sh + 8 * g;
-    vh[c] = (const __bf16*)p.v + b * p.k_sb + hk * p.k_sh + 8 * (lane & 1);
+    kh[c] = (const E*)p.k + b * p.k_sb + hk * p.k_sh + 8 * g;
+    vh[c] = (const E*)p.v + b * p.k_sb + hk * p.k_sh + 8 * (lane & 1);
   }
   const int vkk = (lane >> 1) & 31;
-  auto load_tile = [&](int64_t k0, bf16x8 (&ka)[4], bf16x8 (&vv)[4]) {
+  auto load_tile = [&](int64_t k0, e8 (&ka)[4], e8 (&vv)[4]) {
     const int64_t key = k0 + n, kj = k0 + vkk;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      ka[c] = (bf16x8){};
-      if (hok[c] && key < kend) ka[c] = *(const bf16x8*)(kh[c] + key * p.k_st);
-      vv[c] = (bf16x8){};
-      if (hok[c] && kj < kend) vv[c] = *(const bf16x8*)(vh[c] + kj * p.k_st);
+      ka[c] = (e8){};
+      if (hok[c] && key < kend) ka[c] = *(const e8*)(kh[c] + key * p.k_st);
+      vv[c] = (e8){};
+      if (hok[c] && kj < kend) vv[c] = *(const e8*)(vh[c] + kj * p.k_st);
     }
   };
-  bf16x8 ka[4], vv[4];
+  e8 ka[4], vv[4];
   if (kbeg < kend) load_tile(kbeg, ka, vv);
   for (int64_t k0 = kbeg; k0 < kend; k0 += 32) {
     __syncthreads();                 // previous tile's V reads are done
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int e = lane + 64 * r;
-      *(bf16x8*)&vl[e >> 6][(e >> 1) & 31][8 * (e & 1)] = vv[r];
+      *(e8*)&vl[e >> 6][(e >> 1) & 31][8 * (e & 1)] = vv[r];
     }
     f32x16 s = (f32x16){};
 #pragma unroll
-    for (int c = 0; c < 4; ++c) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[c], qb[c], s, 0, 0, 0);
+    for (int c = 0; c < 4; ++c) s = mfma32(ka[c], qb[c], s);
     if (k0 + 32 < kend) load_tile(k0 + 32, ka, vv);
     // Scores -> log2 units with masks.
     float x[16];
@@ -143,14 +144,14 @@ __global__ __launch_bounds__(64) void d16_qpack_kernel(FwdParams p, int keys_per
       o[0][i] *= alpha;
       o[1][i] *= alpha;
     }
-    bf16x8 pb[2];
+    e8 pb[2];
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float pv = fexp2(x[8 * kc + e] - mref);
         l += pv;
-        pb[kc][e] = (__bf16)pv;
+        pb[kc][e] = (E)pv;
       }
     __syncthreads();                 // V tile visible to every lane
     // V'^T operands: rows (head 2*rb + (n/16), d = n % 16); element e <-> key
@@ -159,11 +160,11 @@ __global__ __launch_bounds__(64) void d16_qpack_kernel(FwdParams p, int keys_per
     for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
       for (int kc = 0; kc < 2; ++kc) {
-        bf16x8 va;
+        e8 va;
         const int hv = 2 * rb + (n >> 4), d = n & 15;
 #pragma unroll
         for (int e = 0; e < 8; ++e) va[e] = vl[hv][16 * kc + 8 * (e / 4) + 4 * g + (e % 4)][d];
-        o[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[kc], o[rb], 0, 0, 0);
+        o[rb] = mfma32(va, pb[kc], o[rb]);
       }
   }
   // Lane (hh, t) keeps the O^T rows of its own head: block hh / 2, rows
@@ -189,11 +190,11 @@ __global__ __launch_bounds__(64) void d16_qpack_kernel(FwdParams p, int keys_per
   const int64_t ob = b * p.q_sb + hcol * p.q_sh + qcol * p.q_st;
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    if (p.out_dtype == 1) {
-      bf16x4 v;
+    if (p.out_dtype != 0) {
+      e4 v;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = (__bf16)(ov[4 * j + e] * inv);
-      *(bf16x4*)((__bf16*)p.o + ob + 8 * j + 4 * g) = v;
+      for (int e = 0; e < 4; ++e) v[e] = (E)(ov[4 * j + e] * inv);
+      *(e4*)((E*)p.o + ob + 8 * j + 4 * g) = v;
     } else {
       *(f32x4*)((float*)p.o + ob + 8 * j + 4 * g) =
           (f32x4){ov[4 * j] * inv, ov[4 * j + 1] * inv, ov[4 * j + 2] * inv, ov[4 * j + 3] * inv};
@@ -218,7 +219,9 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+template <typename E>
 __global__ __launch_bounds__(256) void d16_combine_kernel(FwdParams p) {
+  typedef typename Vec16<E>::x8 e8;
   const int64_t rows = p.B * p.Hq * p.Tq;
   const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -253,15 +256,15 @@ __global__ __launch_bounds__(256) void d16_combine_kernel(FwdParams p) {
   const float inv = L > 0.0f ? 1.0f / L : 0.0f;
   const int64_t b = r / (p.Hq * p.Tq), h = (r / p.Tq) % p.Hq, i = r % p.Tq;
   const int64_t ob = b * p.q_sb + h * p.q_sh + i * p.q_st;
-  if (p.out_dtype == 1) {
-    bf16x8 v0, v1;
+  if (p.out_dtype != 0) {
+    e8 v0, v1;
 #pragma unroll
     for (int d = 0; d < 8; ++d) {
-      v0[d] = (__bf16)(acc[d] * inv);
-      v1[d] = (__bf16)(acc[d + 8] * inv);
+      v0[d] = (E)(acc[d] * inv);
+      v1[d] = (E)(acc[d + 8] * inv);
     }
-    *(bf16x8*)((__bf16*)p.o + ob) = v0;
-    *(bf16x8*)((__bf16*)p.o + ob + 8) = v1;
+    *(e8*)((E*)p.o + ob) = v0;
+    *(e8*)((E*)p.o + ob + 8) = v1;
   } else {
     f32x4* op = (f32x4*)((float*)p.o + ob);
 #pragma unroll
@@ -273,8 +276,10 @@ __global__ __launch_bounds__(256) void d16_combine_kernel(FwdParams p) {
 // -------------------------------------------------------------- key packing
 // grid: (ceil(Tq / 32), B * ceil(Hq / 4)); one wave per block.  Lane column
 // n = lane % 32 is query q0 + n for all 4 heads; score rows are (head, key slot).
-template <int MF>
+template <typename E, int MF>
 __global__ __launch_bounds__(64) void d16_kpack_kernel(FwdParams p) {
+  typedef typename Vec16<E>::x8 e8;
+  typedef typename Vec16<E>::x4 e4;
   const int lane = threadIdx.x, g = lane >> 5, n = lane & 31;
   const int64_t ngrp = (p.Hq + 3) / 4;
   const int64_t b = blockIdx.y / ngrp, h0 = (blockIdx.y % ngrp) * 4;
@@ -282,12 +287,12 @@ __global__ __launch_bounds__(64) void d16_kpack_kernel(FwdParams p) {
   const bool qok = q < p.Tq;
   const int64_t grp = p.Hq / p.Hkv;
   // Q'^T operands: chunk c = head h0 + c (dense over the 32 query columns).
-  bf16x8 qb[4];
+  e8 qb[4];
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
-    qb[c] = (bf16x8){};
+    qb[c] = (e8){};
     if (qok && h0 + c < p.Hq)
-      qb[c] = *(const bf16x8*)((const __bf16*)p.q + b * p.q_sb + (h0 + c) * p.q_sh + q * p.q_st + 8 * g);
+      qb[c] = *(const e8*)((const E*)p.q + b * p.q_sb + (h0 + c) * p.q_sh + q * p.q_st + 8 * g);
   }
   const float c2 = p.scale * kLog2e;
   f32x16 o[2] = {(f32x16){}, (f32x16){}};
@@ -305,43 +310,43 @@ __global__ __launch_bounds__(64) void d16_kpack_kernel(FwdParams p) {
   //   lane loads elements 4 * (n/16) + 0..3.
   const int hr = n >> 3, jr = n & 7, vhalf = n >> 4;
   const bool kok = h0 + hr < p.Hq;
-  const __bf16* kbase = (const __bf16*)p.k + b * p.k_sb + ((kok ? h0 + hr : h0) / grp) * p.k_sh + 8 * g;
-  const __bf16* vbase[2];
+  const E* kbase = (const E*)p.k + b * p.k_sb + ((kok ? h0 + hr : h0) / grp) * p.k_sh + 8 * g;
+  const E* vbase[2];
   bool vok[2];
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb) {
     const int64_t hc = h0 + 2 * rb + vhalf;
     vok[rb] = hc < p.Hq;
-    vbase[rb] = (const __bf16*)p.v + b * p.k_sb + ((vok[rb] ? hc : h0) / grp) * p.k_sh + (n & 15);
+    vbase[rb] = (const E*)p.v + b * p.k_sb + ((vok[rb] ? hc : h0) / grp) * p.k_sh + (n & 15);
   }
-  auto load_tile = [&](int64_t k0, bf16x8 (&ka)[4], bf16x8 (&va)[2]) {
+  auto load_tile = [&](int64_t k0, e8 (&ka)[4], e8 (&va)[2]) {
     const int64_t kr = k0 + jr;
-    bf16x8 kv = (bf16x8){};
-    if (kok && kr < p.Tkv) kv = *(const bf16x8*)(kbase + kr * p.k_st);
+    e8 kv = (e8){};
+    if (kok && kr < p.Tkv) kv = *(const e8*)(kbase + kr * p.k_st);
 #pragma unroll
-    for (int c = 0; c < 4; ++c) ka[c] = (c == hr) ? kv : (bf16x8){};
+    for (int c = 0; c < 4; ++c) ka[c] = (c == hr) ? kv : (e8){};
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
-      __bf16 t[4];
+      E t[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int64_t kj = k0 + 4 * g + e;
-        t[e] = (vok[rb] && kj < p.Tkv) ? vbase[rb][kj * p.k_st] : (__bf16)0.0f;
+        t[e] = (vok[rb] && kj < p.Tkv) ? vbase[rb][kj * p.k_st] : (E)0.0f;
       }
-      const __bf16 z = (__bf16)0.0f;
-      va[rb] = vhalf ? (bf16x8){z, z, z, z, t[0], t[1], t[2], t[3]} : (bf16x8){t[0], t[1], t[2], t[3], z, z, z, z};
+      const E z = (E)0.0f;
+      va[rb] = vhalf ? (e8){z, z, z, z, t[0], t[1], t[2], t[3]} : (e8){t[0], t[1], t[2], t[3], z, z, z, z};
     }
   };
-  bf16x8 ka[4], va[2];
+  e8 ka[4], va[2];
   load_tile(0, ka, va);
   for (int64_t k0 = 0; k0 < p.Tkv; k0 += 8) {
     f32x16 s = (f32x16){};
 #pragma unroll
-    for (int c = 0; c < 4; ++c) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[c], qb[c], s, 0, 0, 0);
-    const bf16x8 vc0 = va[0], vc1 = va[1];
+    for (int c = 0; c < 4; ++c) s = mfma32(ka[c], qb[c], s);
+    const e8 vc0 = va[0], vc1 = va[1];
     if (k0 + 8 < p.Tkv) load_tile(k0 + 8, ka, va);
     // Registers 4hh..4hh+3 hold head hh, key slots 4g + 0..3.
-    bf16x8 pb[2];
+    e8 pb[2];
 #pragma unroll
     for (int hh = 0; hh < 4; ++hh) {
       const int64_t hc = h0 + hh;
@@ -367,11 +372,11 @@ __global__ __launch_bounds__(64) void d16_kpack_kernel(FwdParams p) {
       for (int e = 0; e < 4; ++e) {
         const float pv = fexp2(x[e] - mref);
         l[hh] += pv;
-        pb[hh >> 1][4 * (hh & 1) + e] = (__bf16)pv;
+        pb[hh >> 1][4 * (hh & 1) + e] = (E)pv;
       }
     }
-    o[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vc0, pb[0], o[0], 0, 0, 0);
-    o[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vc1, pb[1], o[1], 0, 0, 0);
+    o[0] = mfma32(vc0, pb[0], o[0]);
+    o[1] = mfma32(vc1, pb[1], o[1]);
   }
   if (!qok) return;
   // Block rb, register i: head 2rb + i/8, d = 8*((i%8)/4) + 4g + i%4.
@@ -386,11 +391,11 @@ __global__ __launch_bounds__(64) void d16_kpack_kernel(FwdParams p) {
     for (int i4 = 0; i4 < 2; ++i4) {
       const int d0 = 8 * i4 + 4 * g;
       const int reg = 8 * (hh & 1) + 4 * i4;
-      if (p.out_dtype == 1) {
-        bf16x4 v;
+      if (p.out_dtype != 0) {
+        e4 v;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = (__bf16)(o[hh >> 1][reg + e] * inv);
-        *(bf16x4*)((__bf16*)p.o + ob + d0) = v;
+        for (int e = 0; e < 4; ++e) v[e] = (E)(o[hh >> 1][reg + e] * inv);
+        *(e4*)((E*)p.o + ob + d0) = v;
       } else {
         f32x4 v;
 #pragma unroll
@@ -405,30 +410,35 @@ __global__ __launch_bounds__(64) void d16_kpack_kernel(FwdParams p) {
 }  // namespace
 
 bool d16_supports(const FwdParams& p) {
-  return p.dtype == 1 && p.D == 16 && p.bias != BIAS_RELPOS && (p.Tq <= 8 || p.Tkv <= 64);
+  return (p.dtype == 1 || p.dtype == 2) && p.D == 16 && p.bias != BIAS_RELPOS && (p.Tq <= 8 || p.Tkv <= 64);
 }
 
-hipError_t launch_d16(const FwdParams& p, hipStream_t s) {
+template <typename E>
+static hipError_t launch_d16_e(const FwdParams& p, hipStream_t s) {
   const int64_t ngrp = (p.Hq + 3) / 4;
   const int mf = p.bias == BIAS_NONE ? MF_NONE : (p.bias == BIAS_CAUSAL || p.bias == BIAS_SLIDING) ? MF_INDEX : MF_TENSOR;
   if (p.Tq <= 8) {
     const int splits = p.num_splits > 1 ? p.num_splits : 1;
     const int64_t kps = ((p.Tkv + splits - 1) / splits + 31) / 32 * 32;
     dim3 grid((unsigned)splits, (unsigned)((p.Tq + 7) / 8), (unsigned)(p.B * ngrp));
-    if (mf == MF_NONE) hipLaunchKernelGGL(d16_qpack_kernel<MF_NONE>, grid, dim3(64), 0, s, p, (int)kps);
-    else if (mf == MF_INDEX) hipLaunchKernelGGL(d16_qpack_kernel<MF_INDEX>, grid, dim3(64), 0, s, p, (int)kps);
-    else hipLaunchKernelGGL(d16_qpack_kernel<MF_TENSOR>, grid, dim3(64), 0, s, p, (int)kps);
+    if (mf == MF_NONE) hipLaunchKernelGGL((d16_qpack_kernel<E, MF_NONE>), grid, dim3(64), 0, s, p, (int)kps);
+    else if (mf == MF_INDEX) hipLaunchKernelGGL((d16_qpack_kernel<E, MF_INDEX>), grid, dim3(64), 0, s, p, (int)kps);
+    else hipLaunchKernelGGL((d16_qpack_kernel<E, MF_TENSOR>), grid, dim3(64), 0, s, p, (int)kps);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || splits == 1) return e;
     const int64_t rows = p.B * p.Hq * p.Tq;
-    hipLaunchKernelGGL(d16_combine_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((d16_combine_kernel<E>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, p);
     return hipGetLastError();
   }
   dim3 grid((unsigned)((p.Tq + 31) / 32), (unsigned)(p.B * ngrp));
-  if (mf == MF_NONE) hipLaunchKernelGGL(d16_kpack_kernel<MF_NONE>, grid, dim3(64), 0, s, p);
-  else if (mf == MF_INDEX) hipLaunchKernelGGL(d16_kpack_kernel<MF_INDEX>, grid, dim3(64), 0, s, p);
-  else hipLaunchKernelGGL(d16_kpack_kernel<MF_TENSOR>, grid, dim3(64), 0, s, p);
+  if (mf == MF_NONE) hipLaunchKernelGGL((d16_kpack_kernel<E, MF_NONE>), grid, dim3(64), 0, s, p);
+  else if (mf == MF_INDEX) hipLaunchKernelGGL((d16_kpack_kernel<E, MF_INDEX>), grid, dim3(64), 0, s, p);
+  else hipLaunchKernelGGL((d16_kpack_kernel<E, MF_TENSOR>), grid, dim3(64), 0, s, p);
   return hipGetLastError();
+}
+
+hipError_t launch_d16(const FwdParams& p, hipStream_t s) {
+  return p.dtype == 2 ? launch_d16_e<_Float16>(p, s) : launch_d16_e<__bf16>(p, s);
 }
 
 }  // namespace sdpa

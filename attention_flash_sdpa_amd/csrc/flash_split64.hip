@@ -28,15 +28,13 @@
 // are either formed here from Q and the tables (MFMA, as in the general
 // kernel) or read from precomputed term arrays.
 #include "common.h"
+#include "elem16.h"
 
 #include <type_traits>
 
 namespace sdpa {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -50,7 +48,7 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kTau = 8.0f;          // lazy-rescale threshold (log2 units)
 constexpr float kTauSum = 256.0f;     // a tile row sum above 2^tau flags a probability that may exceed 2^tau
 constexpr int BN = 32;                // keys per tile
-constexpr int ROWB = 128;             // bytes per K / V row (64 bf16)
+constexpr int ROWB = 128;             // bytes per K / V row (64 16-bit elements)
 constexpr int TILEB = BN * ROWB;      // 4 KB
 constexpr int TH_FLOATS = 2 * 64 * 34;   // term_h^T [2 query blocks][64 y][32 q]; the half exchange uses [2][34][64]
 
@@ -72,7 +70,8 @@ __device__ __forceinline__ int kswz(int r) { return (r >> 1) & 7; }
 // Transposing reads take 4 rows x 64 contiguous bytes: flip 64-byte halves.
 __device__ __forceinline__ int vswz(int r) { return ((r >> 1) & 1) << 2; }
 
-__device__ __forceinline__ bf16x8 lds_b128(const lds_char* p) { return *(const __attribute__((address_space(3))) bf16x8*)p; }
+template <typename V>
+__device__ __forceinline__ V lds_b128(const lds_char* p) { return *(const __attribute__((address_space(3))) V*)p; }
 __device__ __forceinline__ s16x4 lds_tr(const lds_char* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p);
 }
@@ -87,8 +86,11 @@ __device__ __forceinline__ float pair_sum(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <int MODE, bool OUT_BF16>
+template <typename E, int MODE, bool OUT16>
 __global__ __launch_bounds__(256, 3) void flash_split64_kernel(FwdParams p) {
+  typedef typename Vec16<E>::x8 e8;
+  typedef typename Vec16<E>::x4 e4;
+  typedef typename Vec16<E>::x2 e2;
   lds_char* const ka = (lds_char*)s64_ka;
   lds_char* const kb = (lds_char*)s64_kb;
   lds_char* const va = (lds_char*)s64_va;
@@ -112,10 +114,10 @@ __global__ __launch_bounds__(256, 3) void flash_split64_kernel(FwdParams p) {
   const bool qvalid = qrow < p.Tq;
   const int64_t qsafe = qvalid ? qrow : 0;
 
-  const __bf16* qp = (const __bf16*)p.q + b * p.q_sb + h * p.q_sh;
-  bf16x8 qf[4];
+  const E* qp = (const E*)p.q + b * p.q_sb + h * p.q_sh;
+  e8 qf[4];
 #pragma unroll
-  for (int c = 0; c < 4; ++c) qf[c] = qvalid ? *(const bf16x8*)(qp + qrow * p.q_st + c * 16 + 8 * g) : (bf16x8){};
+  for (int c = 0; c < 4; ++c) qf[c] = qvalid ? *(const e8*)(qp + qrow * p.q_st + c * 16 + 8 * g) : (e8){};
 
   const float c2 = p.scale * kLog2e;
   // ---- rel-pos: accumulator initialisation (term_w / scale) and term_h access
@@ -152,7 +154,7 @@ __global__ __launch_bounds__(256, 3) void flash_split64_kernel(FwdParams p) {
       // ka, rel_pos_w rows 0..63 in kb and 64..127 in va), K-tile swizzle;
       // rows past each table read as zero (record count = table size).
       const __amdgpu_buffer_rsrc_t rhs = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)((const __bf16*)p.rel_h + r * 64), 0, (int)max((int64_t)0, (2 * gh - 1 - r) * 128), 0x00020000);
+          (void*)((const E*)p.rel_h + r * 64), 0, (int)max((int64_t)0, (2 * gh - 1 - r) * 128), 0x00020000);
       const __amdgpu_buffer_rsrc_t rws = __builtin_amdgcn_make_buffer_rsrc((void*)p.rel_w, 0, 127 * 128, 0x00020000);
 #pragma unroll
       for (int j = 0; j < 6; ++j) {                 // 6 x 256 lanes x 16 B = 24 KB
@@ -178,8 +180,8 @@ __global__ __launch_bounds__(256, 3) void flash_split64_kernel(FwdParams p) {
         const int lr = max(gh - 1 - y, 0);
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          const bf16x8 a = lds_b128(ka + lr * ROWB + (((2 * c + g) ^ kswz(lr)) << 4));
-          th[yb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(y < gh ? a : (bf16x8){}, qf[c], th[yb], 0, 0, 0);
+          const e8 a = lds_b128<e8>(ka + lr * ROWB + (((2 * c + g) ^ kswz(lr)) << 4));
+          th[yb] = mfma32(y < gh ? a : (e8){}, qf[c], th[yb]);
         }
       }
 #pragma unroll
@@ -189,8 +191,7 @@ __global__ __launch_bounds__(256, 3) void flash_split64_kernel(FwdParams p) {
         const lds_char* rowp = (m < 64 ? kb + m * ROWB : va + (m - 64) * ROWB);
 #pragma unroll
         for (int c = 0; c < 4; ++c)
-          aw[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(rowp + (((2 * c + g) ^ kswz(m & 63)) << 4)),
-                                                           qf[c], aw[mb], 0, 0, 0);
+          aw[mb] = mfma32(lds_b128<e8>(rowp + (((2 * c + g) ^ kswz(m & 63)) << 4)), qf[c], aw[mb]);
       }
     }
     __syncthreads();                                 // table rows no longer needed
@@ -235,7 +236,7 @@ __global__ __launch_bounds__(256, 3) void flash_split64_kernel(FwdParams p) {
   const int tbeg = hf ? nt0 : 0;
   const int tend = hf ? nt : nt0;
   const int niter = nt0;                        // half 0 has at least as many tiles
-  const char* kvbase = (const char*)((const __bf16*)(qb ? p.v : p.k) + b * p.k_sb + hk * p.k_sh);
+  const char* kvbase = (const char*)((const E*)(qb ? p.v : p.k) + b * p.k_sb + hk * p.k_sh);
   // Wave qb of half hf copies the K (qb = 0) or V (qb = 1) tile of its half.
   const int rstride = (int)(p.k_st * 2);
   const int64_t span = ((p.Tkv - 1) * p.k_st + 64) * 2;     // bytes from the row base to the end of the last key row
@@ -287,7 +288,7 @@ __global__ __launch_bounds__(256, 3) void flash_split64_kernel(FwdParams p) {
     const lds_char* vs = (PAR ? vb : va) + hf * TILEB;
     f32x16 s = (MODE == S_NONE) ? (f32x16){} : cinit[PAR];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(ks + kro[c]), qf[c], s, 0, 0, 0);
+    for (int c = 0; c < 4; ++c) s = mfma32(lds_b128<e8>(ks + kro[c]), qf[c], s);
     if ((t + 1) * BN > p.Tkv) {
       asm volatile("" ::: "memory");     // ragged last tile: a real branch, full tiles skip it
       const int kl0 = t * BN + 4 * g;
@@ -300,18 +301,18 @@ __global__ __launch_bounds__(256, 3) void flash_split64_kernel(FwdParams p) {
     // the tile's row sum, which also catches overflow and the first tile
     // (m = -inf) -- sends the wave through the exact path, which moves m to
     // the tile max, rescales O and l, and recomputes the probabilities.
-    bf16x8 pb[2];
+    e8 pb[2];
     auto probs = [&](float off) -> float {
       float acc0 = 0.0f, acc1 = 0.0f;
 #pragma unroll
       for (int tc = 0; tc < 2; ++tc) {
-        bf16x2 pk[4];
+        e2 pk[4];
 #pragma unroll
         for (int e = 0; e < 8; e += 2) {
           const f32x2 pp = {fexp2(fmaf(s[8 * tc + e], c2, off)), fexp2(fmaf(s[8 * tc + e + 1], c2, off))};
-          pk[e / 2] = __builtin_convertvector(pp, bf16x2);
-          if (e & 2) acc1 = __builtin_amdgcn_fdot2_f32_bf16(pk[e / 2], (bf16x2){(__bf16)1.0f, (__bf16)1.0f}, acc1, false);
-          else acc0 = __builtin_amdgcn_fdot2_f32_bf16(pk[e / 2], (bf16x2){(__bf16)1.0f, (__bf16)1.0f}, acc0, false);
+          pk[e / 2] = __builtin_convertvector(pp, e2);
+          if (e & 2) acc1 = dot2_ones(pk[e / 2], acc1);
+          else acc0 = dot2_ones(pk[e / 2], acc0);
         }
         pb[tc] = __builtin_shufflevector(__builtin_shufflevector(pk[0], pk[1], 0, 1, 2, 3),
                                          __builtin_shufflevector(pk[2], pk[3], 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
@@ -346,7 +347,7 @@ __global__ __launch_bounds__(256, 3) void flash_split64_kernel(FwdParams p) {
         const s16x4 lo4 = lds_tr(vs + vro[tc][d]);
         const s16x4 hi4 = lds_tr(vs + vro[tc][d] + 8 * ROWB);
         const s16x8 a8 = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
-        o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a8), pb[tc], o[d], 0, 0, 0);
+        o[d] = mfma32(__builtin_bit_cast(e8, a8), pb[tc], o[d]);
       }
   };
 
@@ -409,11 +410,11 @@ __global__ __launch_bounds__(256, 3) void flash_split64_kernel(FwdParams p) {
         const int i = 4 * i4 + e;
         v[e] = fmaf(o[d][i], w0, xch[128 + (d * 16 + i) * 64 + lane] * w1) * inv;
       }
-      if (OUT_BF16) {
-        bf16x4 vb;
+      if (OUT16) {
+        e4 vb;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) vb[e] = (__bf16)v[e];
-        *(bf16x4*)((__bf16*)p.o + ob + dd) = vb;
+        for (int e = 0; e < 4; ++e) vb[e] = (E)v[e];
+        *(e4*)((E*)p.o + ob + dd) = vb;
       } else {
         *(f32x4*)((float*)p.o + ob + dd) = (f32x4){v[0], v[1], v[2], v[3]};
       }
@@ -421,18 +422,18 @@ __global__ __launch_bounds__(256, 3) void flash_split64_kernel(FwdParams p) {
   if (p.lse && g == 0) p.lse[(b * p.Hq + h) * p.Tq + qrow] = lt > 0.0f ? (mm + __log2f(lt)) * kLn2 : -INFINITY;
 }
 
-template <int MODE>
+template <typename E, int MODE>
 hipError_t launch_mode(const FwdParams& p, hipStream_t s) {
   dim3 grid((unsigned)((p.Tq + 63) / 64), (unsigned)p.Hq, (unsigned)p.B);
-  if (p.out_dtype == 1) hipLaunchKernelGGL((flash_split64_kernel<MODE, true>), grid, dim3(256), 0, s, p);
-  else hipLaunchKernelGGL((flash_split64_kernel<MODE, false>), grid, dim3(256), 0, s, p);
+  if (p.out_dtype != 0) hipLaunchKernelGGL((flash_split64_kernel<E, MODE, true>), grid, dim3(256), 0, s, p);
+  else hipLaunchKernelGGL((flash_split64_kernel<E, MODE, false>), grid, dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
 }  // namespace
 
 bool split64_supports(const FwdParams& p) {
-  if (p.dtype != 1 || p.D != 64 || p.num_splits != 1) return false;
+  if ((p.dtype != 1 && p.dtype != 2) || p.D != 64 || p.num_splits != 1) return false;
   // key rows addressed with 32-bit byte offsets
   if ((p.Tkv + BN) * p.k_st * 2 > 0x7fffffffLL) return false;
   // worth it when the query blocks leave SIMDs idle: fewer than ~4 blocks of 32 rows per SIMD
@@ -446,9 +447,14 @@ bool split64_supports(const FwdParams& p) {
   return false;
 }
 
+template <typename E>
+static hipError_t launch_s64_e(const FwdParams& p, hipStream_t s) {
+  if (p.bias == BIAS_RELPOS) return p.term_h ? launch_mode<E, S_RELPOS_TERMS>(p, s) : launch_mode<E, S_RELPOS_FUSED>(p, s);
+  return launch_mode<E, S_NONE>(p, s);
+}
+
 hipError_t launch_split64(const FwdParams& p, hipStream_t s) {
-  if (p.bias == BIAS_RELPOS) return p.term_h ? launch_mode<S_RELPOS_TERMS>(p, s) : launch_mode<S_RELPOS_FUSED>(p, s);
-  return launch_mode<S_NONE>(p, s);
+  return p.dtype == 2 ? launch_s64_e<_Float16>(p, s) : launch_s64_e<__bf16>(p, s);
 }
 
 }  // namespace sdpa

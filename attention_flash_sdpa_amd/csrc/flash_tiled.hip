@@ -1,6 +1,7 @@
-// Flash attention forward for head_dim 64 / 128 with no mask or a causal /
-// sliding-window mask, grouped-query K/V sharing, bshd or bhsd layouts: the
-// decoder-style path (many query rows, long key ranges).
+// Flash attention forward for head_dim 64 / 128, bf16 or fp16 inputs, with no
+// mask, a causal / sliding-window mask or a tensor mask, grouped-query K/V
+// sharing, bshd or bhsd layouts: the decoder-style path (many query rows,
+// long key ranges).
 //
 //   O = softmax(Q . K^T * scale + M) . V     ([Axon PR 650]
 //   "Axon.Layers.scaled_dot_product_attention/4", description: masks
@@ -32,15 +33,13 @@
 // 2^8, an overflow, or no reference yet) takes the exact path that moves the
 // reference to the tile max and rescales O and the row sum.
 #include "common.h"
+#include "elem16.h"
 
 #include <type_traits>
 
 namespace sdpa {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -85,7 +84,8 @@ struct TCfg {
   static __device__ __forceinline__ int vswz(int r) { return ((r / RPB) % (4 / RPB)) << 2; }
 };
 
-__device__ __forceinline__ bf16x8 lds_b128(const lds_char* p) { return *(const __attribute__((address_space(3))) bf16x8*)p; }
+template <typename V>
+__device__ __forceinline__ V lds_b128(const lds_char* p) { return *(const __attribute__((address_space(3))) V*)p; }
 __device__ __forceinline__ s16x4 lds_tr(const lds_char* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p);
 }
@@ -100,8 +100,11 @@ __device__ __forceinline__ float pair_sum(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <int D, int MODE, bool OUT_BF16>
+template <typename E, int D, int MODE, bool OUT16>
 __global__ __launch_bounds__(256, 3) void flash_tiled_kernel(FwdParams p, int hpw, int64_t mask_bytes) {
+  typedef typename Vec16<E>::x8 e8;
+  typedef typename Vec16<E>::x4 e4;
+  typedef typename Vec16<E>::x2 e2;
   constexpr bool TENSOR = MODE >= T_ADD_F32;
   using M = MCfg<MODE>;
   using C = TCfg<D>;
@@ -139,10 +142,10 @@ __global__ __launch_bounds__(256, 3) void flash_tiled_kernel(FwdParams p, int hp
   const int64_t qrow = wq0 + ql;
   const bool qvalid = qrow < p.Tq;
 
-  const __bf16* qp = (const __bf16*)p.q + b * p.q_sb + h * p.q_sh;
-  bf16x8 qf[C::QC];
+  const E* qp = (const E*)p.q + b * p.q_sb + h * p.q_sh;
+  e8 qf[C::QC];
 #pragma unroll
-  for (int c = 0; c < C::QC; ++c) qf[c] = qvalid ? *(const bf16x8*)(qp + qrow * p.q_st + c * 16 + 8 * g) : (bf16x8){};
+  for (int c = 0; c < C::QC; ++c) qf[c] = qvalid ? *(const e8*)(qp + qrow * p.q_st + c * 16 + 8 * g) : (e8){};
   const float c2 = p.scale * kLog2e;
 
   // Key tiles of the workgroup.
@@ -161,8 +164,8 @@ __global__ __launch_bounds__(256, 3) void flash_tiled_kernel(FwdParams p, int hp
   }
 
   // LDS-direct copies: every wave issues C::NI of the 1 KB pieces of each tile.
-  const char* kbase = (const char*)((const __bf16*)p.k + b * p.k_sb + hk * p.k_sh);
-  const char* vbase = (const char*)((const __bf16*)p.v + b * p.k_sb + hk * p.k_sh);
+  const char* kbase = (const char*)((const E*)p.k + b * p.k_sb + hk * p.k_sh);
+  const char* vbase = (const char*)((const E*)p.v + b * p.k_sb + hk * p.k_sh);
   const int rstride = (int)(p.k_st * 2);
   const int64_t span = ((p.Tkv - 1) * p.k_st + D) * 2;
   int kvo[2], vvo[2];                   // C::NI <= 2 (a dependent bound here breaks the host-side lambda capture)
@@ -240,7 +243,7 @@ __global__ __launch_bounds__(256, 3) void flash_tiled_kernel(FwdParams p, int hp
     const lds_char* vs = PAR ? vb : va;
     f32x16 s = (f32x16){};
 #pragma unroll
-    for (int c = 0; c < C::QC; ++c) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(ks + kro[c]), qf[c], s, 0, 0, 0);
+    for (int c = 0; c < C::QC; ++c) s = mfma32(lds_b128<e8>(ks + kro[c]), qf[c], s);
     if (TENSOR) {
       // this lane's 16 mask values: keys 8 * i4 + 4g + e of the tile, row ql
       const lds_char* mrow = (const lds_char*)(PAR ? ft_mb : ft_ma) + M::WB * wave + ql * M::ROWB;
@@ -254,7 +257,7 @@ __global__ __launch_bounds__(256, 3) void flash_tiled_kernel(FwdParams p, int hp
 #pragma unroll
           for (int e = 0; e < 4; ++e) s[4 * i4 + e] = fmaf(v[e], inv_scale, s[4 * i4 + e]);
         } else if (MODE == T_ADD_BF16) {
-          const bf16x4 v = *(const __attribute__((address_space(3))) bf16x4*)a;
+          const Vec16<__bf16>::x4 v = *(const __attribute__((address_space(3))) Vec16<__bf16>::x4*)a;
 #pragma unroll
           for (int e = 0; e < 4; ++e) s[4 * i4 + e] = fmaf((float)v[e], inv_scale, s[4 * i4 + e]);
         } else {
@@ -278,18 +281,18 @@ __global__ __launch_bounds__(256, 3) void flash_tiled_kernel(FwdParams p, int hp
         s[i] = (key <= lim_hi && key > lim_lo) ? s[i] : -INFINITY;
       }
     }
-    bf16x8 pb[2];
+    e8 pb[2];
     auto probs = [&](float off) -> float {
       float acc0 = 0.0f, acc1 = 0.0f;
 #pragma unroll
       for (int tc = 0; tc < 2; ++tc) {
-        bf16x2 pk[4];
+        e2 pk[4];
 #pragma unroll
         for (int e = 0; e < 8; e += 2) {
           const f32x2 pp = {fexp2(fmaf(s[8 * tc + e], c2, off)), fexp2(fmaf(s[8 * tc + e + 1], c2, off))};
-          pk[e / 2] = __builtin_convertvector(pp, bf16x2);
-          if (e & 2) acc1 = __builtin_amdgcn_fdot2_f32_bf16(pk[e / 2], (bf16x2){(__bf16)1.0f, (__bf16)1.0f}, acc1, false);
-          else acc0 = __builtin_amdgcn_fdot2_f32_bf16(pk[e / 2], (bf16x2){(__bf16)1.0f, (__bf16)1.0f}, acc0, false);
+          pk[e / 2] = __builtin_convertvector(pp, e2);
+          if (e & 2) acc1 = dot2_ones(pk[e / 2], acc1);
+          else acc0 = dot2_ones(pk[e / 2], acc0);
         }
         pb[tc] = __builtin_shufflevector(__builtin_shufflevector(pk[0], pk[1], 0, 1, 2, 3),
                                          __builtin_shufflevector(pk[2], pk[3], 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
@@ -322,7 +325,7 @@ __global__ __launch_bounds__(256, 3) void flash_tiled_kernel(FwdParams p, int hp
         const s16x4 lo4 = lds_tr(vs + vro[tc][d]);
         const s16x4 hi4 = lds_tr(vs + vro[tc][d] + 8 * C::ROWB);
         const s16x8 a8 = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
-        o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a8), pb[tc], o[d], 0, 0, 0);
+        o[d] = mfma32(__builtin_bit_cast(e8, a8), pb[tc], o[d]);
       }
   };
 
@@ -353,11 +356,11 @@ __global__ __launch_bounds__(256, 3) void flash_tiled_kernel(FwdParams p, int hp
 #pragma unroll
     for (int i4 = 0; i4 < 4; ++i4) {
       const int dd = d * 32 + 8 * i4 + 4 * g;
-      if (OUT_BF16) {
-        bf16x4 vb4;
+      if (OUT16) {
+        e4 vb4;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) vb4[e] = (__bf16)(o[d][4 * i4 + e] * inv);
-        *(bf16x4*)((__bf16*)p.o + ob + dd) = vb4;
+        for (int e = 0; e < 4; ++e) vb4[e] = (E)(o[d][4 * i4 + e] * inv);
+        *(e4*)((E*)p.o + ob + dd) = vb4;
       } else {
         f32x4 v;
 #pragma unroll
@@ -370,7 +373,7 @@ __global__ __launch_bounds__(256, 3) void flash_tiled_kernel(FwdParams p, int hp
 
 int mask_es(const FwdParams& p) { return p.bias == BIAS_BOOL ? 1 : (p.mdtype == 0 ? 4 : 2); }
 
-template <int D, int MODE>
+template <typename E, int D, int MODE>
 hipError_t launch_t(const FwdParams& p, hipStream_t s) {
   const int64_t grp = p.Hq / p.Hkv;
   const int hpw = (grp % 4 == 0) ? 4 : (grp % 2 == 0) ? 2 : 1;
@@ -387,26 +390,26 @@ hipError_t launch_t(const FwdParams& p, hipStream_t s) {
     mask_bytes = ((p.B - 1) * p.ms[0] + (p.Hq - 1) * p.ms[1] + (p.Tq - 1) * p.ms[2] + (p.Tkv - 1) * p.ms[3] + 1) *
                  mask_es(p);
   mask_bytes = (mask_bytes + 15) & ~(int64_t)15;
-  if (p.out_dtype == 1) hipLaunchKernelGGL((flash_tiled_kernel<D, MODE, true>), grid, dim3(256), 0, s, p, hpw, mask_bytes);
-  else hipLaunchKernelGGL((flash_tiled_kernel<D, MODE, false>), grid, dim3(256), 0, s, p, hpw, mask_bytes);
+  if (p.out_dtype != 0) hipLaunchKernelGGL((flash_tiled_kernel<E, D, MODE, true>), grid, dim3(256), 0, s, p, hpw, mask_bytes);
+  else hipLaunchKernelGGL((flash_tiled_kernel<E, D, MODE, false>), grid, dim3(256), 0, s, p, hpw, mask_bytes);
   return hipGetLastError();
 }
 
-template <int D>
+template <typename E, int D>
 hipError_t launch_d(const FwdParams& p, hipStream_t s) {
   switch (p.bias) {
     case BIAS_CAUSAL:
-    case BIAS_SLIDING: return launch_t<D, T_INDEX>(p, s);
-    case BIAS_ADDITIVE: return p.mdtype == 0 ? launch_t<D, T_ADD_F32>(p, s) : launch_t<D, T_ADD_BF16>(p, s);
-    case BIAS_BOOL: return launch_t<D, T_BOOL>(p, s);
-    default: return launch_t<D, T_NONE>(p, s);
+    case BIAS_SLIDING: return launch_t<E, D, T_INDEX>(p, s);
+    case BIAS_ADDITIVE: return p.mdtype == 0 ? launch_t<E, D, T_ADD_F32>(p, s) : launch_t<E, D, T_ADD_BF16>(p, s);
+    case BIAS_BOOL: return launch_t<E, D, T_BOOL>(p, s);
+    default: return launch_t<E, D, T_NONE>(p, s);
   }
 }
 
 }  // namespace
 
 bool tiled_supports(const FwdParams& p) {
-  if (p.dtype != 1 || (p.D != 64 && p.D != 128) || p.num_splits != 1) return false;
+  if ((p.dtype != 1 && p.dtype != 2) || (p.D != 64 && p.D != 128) || p.num_splits != 1) return false;
   if (p.bias == BIAS_ADDITIVE || p.bias == BIAS_BOOL) {
     // mask blocks are copied by 16-byte chunks along contiguous keys; row
     // offsets of one block and every element offset stay within 32 / 64 bits
@@ -427,7 +430,8 @@ bool tiled_supports(const FwdParams& p) {
 }
 
 hipError_t launch_tiled(const FwdParams& p, hipStream_t s) {
-  return p.D == 64 ? launch_d<64>(p, s) : launch_d<128>(p, s);
+  if (p.dtype == 2) return p.D == 64 ? launch_d<_Float16, 64>(p, s) : launch_d<_Float16, 128>(p, s);
+  return p.D == 64 ? launch_d<__bf16, 64>(p, s) : launch_d<__bf16, 128>(p, s);
 }
 
 }  // namespace sdpa

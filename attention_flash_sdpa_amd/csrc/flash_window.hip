@@ -1,5 +1,5 @@
 // Windowed attention with the decomposed rel-pos bias, for SAM's 14 x 14
-// windows (196 tokens, head_dim 64, bf16): one workgroup per (window, head),
+// windows (196 tokens, head_dim 64, bf16 or fp16): one workgroup per (window, head),
 // the bias terms formed inside the kernel.
 //
 //   z_ij = scale * q_i . k_j + term_h[i, row(j)] + term_w[i, col(j)]
@@ -20,19 +20,17 @@
 //     accumulators, identical for every tile (slots 28..31 start at -inf);
 //   * term_h / scale depends on (query, tile, s / 14): it enters the matrix op
 //     as one extra 16-deep chunk, K' rows one-hot in s / 14 against the query's
-//     two term_h values of the tile, each split into a bf16 high and low part
-//     (so the bias keeps ~16 bits, not bf16's 8); the products Q . Rh^T stay
+//     two term_h values of the tile, each split into a 16-bit high and low
+//     part (so the bias keeps about twice the element's mantissa); the products Q . Rh^T stay
 //     in LDS and each tile reads its two values.
 // The terms come from two 32 x 32 x 64 products per wave, Q . Rh^T and
 // Q . Rw^T over all 27 table rows, followed by a skewed gather through LDS.
 #include "common.h"
+#include "elem16.h"
 
 namespace sdpa {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -53,7 +51,7 @@ constexpr int RPT = 32 / G;           // grid rows per key tile
 constexpr int TK = RPT * G;           // keys per tile
 constexpr int NT = G / RPT;           // key tiles
 constexpr int NW = (T + 31) / 32;     // waves (32 query rows each)
-constexpr int ROWB = 128;             // bytes per K / V row (64 bf16)
+constexpr int ROWB = 128;             // bytes per K / V row (64 16-bit elements)
 constexpr int ROWS = (NT - 1) * TK + 32;   // LDS rows: the last tile reads 32 rows
 constexpr int PIECES = ROWS * ROWB / 1024; // 1 KB copy pieces per tensor
 static_assert(G % RPT == 0 && RPT <= 4, "tile = whole grid rows, at most 4");
@@ -65,7 +63,8 @@ __shared__ __attribute__((aligned(16))) float fw_sc[NW * 32 * 32];    // per-wav
 
 __device__ __forceinline__ int kswz(int r) { return (r >> 1) & 7; }
 __device__ __forceinline__ int vswz(int r) { return ((r >> 1) & 1) << 2; }
-__device__ __forceinline__ bf16x8 lds_b128(const lds_char* p) { return *(const __attribute__((address_space(3))) bf16x8*)p; }
+template <typename V>
+__device__ __forceinline__ V lds_b128(const lds_char* p) { return *(const __attribute__((address_space(3))) V*)p; }
 __device__ __forceinline__ s16x4 lds_tr(const lds_char* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p);
 }
@@ -80,8 +79,11 @@ __device__ __forceinline__ float pair_sum(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <bool OUT_BF16>
+template <typename E, bool OUT16>
 __global__ __launch_bounds__(NW * 64, 4) void flash_window_kernel(FwdParams p) {
+  typedef typename Vec16<E>::x8 e8;
+  typedef typename Vec16<E>::x4 e4;
+  typedef typename Vec16<E>::x2 e2;
   lds_char* const ks = (lds_char*)fw_k;
   lds_char* const vs = (lds_char*)fw_v;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -93,8 +95,8 @@ __global__ __launch_bounds__(NW * 64, 4) void flash_window_kernel(FwdParams p) {
   {
     const int rstride = (int)(p.k_st * 2);
     const int nrec = (int)(((int64_t)(T - 1) * p.k_st + 64) * 2);
-    const char* kb = (const char*)((const __bf16*)p.k + b * p.k_sb + h * p.k_sh);
-    const char* vb = (const char*)((const __bf16*)p.v + b * p.k_sb + h * p.k_sh);
+    const char* kb = (const char*)((const E*)p.k + b * p.k_sb + h * p.k_sh);
+    const char* vb = (const char*)((const E*)p.v + b * p.k_sb + h * p.k_sh);
     const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)kb, 0, nrec, 0x00020000);
     const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)vb, 0, nrec, 0x00020000);
     for (int pc = wave; pc < PIECES; pc += NW) {
@@ -112,20 +114,20 @@ __global__ __launch_bounds__(NW * 64, 4) void flash_window_kernel(FwdParams p) {
   const bool qvalid = qrow < T;
   const int qs = qvalid ? qrow : T - 1;
   const int ih = qs / G, iw = qs % G;
-  const __bf16* qp = (const __bf16*)p.q + b * p.q_sb + h * p.q_sh + (int64_t)qs * p.q_st + 8 * g;
+  const E* qp = (const E*)p.q + b * p.q_sb + h * p.q_sh + (int64_t)qs * p.q_st + 8 * g;
   const int trow = ql < NTAB ? ql : NTAB - 1;
-  const __bf16* rhp = (const __bf16*)p.rel_h + trow * 64 + 8 * g;
-  const __bf16* rwp = (const __bf16*)p.rel_w + trow * 64 + 8 * g;
-  bf16x8 qf[4], rh[4], rw[4];
+  const E* rhp = (const E*)p.rel_h + trow * 64 + 8 * g;
+  const E* rwp = (const E*)p.rel_w + trow * 64 + 8 * g;
+  e8 qf[4], rh[4], rw[4];
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
-    qf[c] = *(const bf16x8*)(qp + c * 16);
-    rh[c] = *(const bf16x8*)(rhp + c * 16);
-    rw[c] = *(const bf16x8*)(rwp + c * 16);
+    qf[c] = *(const e8*)(qp + c * 16);
+    rh[c] = *(const e8*)(rhp + c * 16);
+    rw[c] = *(const e8*)(rwp + c * 16);
   }
   if (ql >= NTAB) {
 #pragma unroll
-    for (int c = 0; c < 4; ++c) rh[c] = rw[c] = (bf16x8){};
+    for (int c = 0; c < 4; ++c) rh[c] = rw[c] = (e8){};
   }
   const float c2 = p.scale * kLog2e;
   const float inv_scale = 1.0f / p.scale;
@@ -133,10 +135,10 @@ __global__ __launch_bounds__(NW * 64, 4) void flash_window_kernel(FwdParams p) {
   // ---- rel-pos terms: A^T[r, q] = table[r] . q on the matrix cores, then the
   // skewed gathers term[q, y] = A[q, coord(q) - y + G - 1] through LDS.
   lds_float* const sc = (lds_float*)fw_sc + wave * 1024;
-  auto table_product = [&](const bf16x8 (&tab)[4]) {
+  auto table_product = [&](const e8 (&tab)[4]) {
     f32x16 a = (f32x16){};
 #pragma unroll
-    for (int c = 0; c < 4; ++c) a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tab[c], qf[c], a, 0, 0, 0);
+    for (int c = 0; c < 4; ++c) a = mfma32(tab[c], qf[c], a);
 #pragma unroll
     for (int i = 0; i < 16; ++i) sc[(8 * (i / 4) + 4 * g + (i % 4)) * 32 + ql] = a[i];
   };
@@ -155,13 +157,13 @@ __global__ __launch_bounds__(NW * 64, 4) void flash_window_kernel(FwdParams p) {
   // A_h stays in LDS; each tile reads its two term_h values from it.
   table_product(rh);
   // K' chunk: key slot ql (lanes g = 0) is one-hot at s / 14 and 4 + s / 14.
-  bf16x8 kaug = (bf16x8){};
+  e8 kaug = (e8){};
   if (g == 0 && ql < TK) {
     const int ro = ql / G;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      kaug[e] = (__bf16)(e == ro ? 1.0f : 0.0f);
-      kaug[4 + e] = (__bf16)(e == ro ? 1.0f : 0.0f);
+      kaug[e] = (E)(e == ro ? 1.0f : 0.0f);
+      kaug[4 + e] = (E)(e == ro ? 1.0f : 0.0f);
     }
   }
   __builtin_amdgcn_s_waitcnt(0);        // this wave's copies have landed
@@ -173,38 +175,38 @@ __global__ __launch_bounds__(NW * 64, 4) void flash_window_kernel(FwdParams p) {
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     // Q' chunk of this tile: high parts of term_h rows RPT*t + e at e, low parts at 4 + e.
-    bf16x8 qaug = (bf16x8){};
+    e8 qaug = (e8){};
     if (g == 0) {
 #pragma unroll
       for (int e = 0; e < RPT; ++e) {
         const float th = sc[(ih - RPT * t - e + G - 1) * 32 + ql] * inv_scale;
-        const __bf16 hi = (__bf16)th;
+        const E hi = (E)th;
         qaug[e] = hi;
-        qaug[4 + e] = (__bf16)(th - (float)hi);
+        qaug[4 + e] = (E)(th - (float)hi);
       }
     }
-    f32x16 s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kaug, qaug, cinit, 0, 0, 0);
+    f32x16 s = mfma32(kaug, qaug, cinit);
     const int kr = TK * t + ql;
-    bf16x8 kf[4];
+    e8 kf[4];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) kf[c] = lds_b128(ks + kr * ROWB + (((2 * c + g) ^ kswz(kr)) << 4));
+    for (int c = 0; c < 4; ++c) kf[c] = lds_b128<e8>(ks + kr * ROWB + (((2 * c + g) ^ kswz(kr)) << 4));
 #pragma unroll
-    for (int c = 0; c < 4; ++c) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[c], qf[c], s, 0, 0, 0);
+    for (int c = 0; c < 4; ++c) s = mfma32(kf[c], qf[c], s);
     // Probabilities against the running reference m; only a tile whose row
     // sum passes 2^8 (or the first tile) takes the exact path that moves m
     // to the tile max and rescales O and l.
-    bf16x8 pb[2];
+    e8 pb[2];
     auto probs = [&](float off) -> float {
       float acc0 = 0.0f, acc1 = 0.0f;
 #pragma unroll
       for (int tc = 0; tc < 2; ++tc) {
-        bf16x2 pk[4];
+        e2 pk[4];
 #pragma unroll
         for (int e = 0; e < 8; e += 2) {
           const f32x2 pp = {fexp2(fmaf(s[8 * tc + e], c2, off)), fexp2(fmaf(s[8 * tc + e + 1], c2, off))};
-          pk[e / 2] = __builtin_convertvector(pp, bf16x2);
-          if (e & 2) acc1 = __builtin_amdgcn_fdot2_f32_bf16(pk[e / 2], (bf16x2){(__bf16)1.0f, (__bf16)1.0f}, acc1, false);
-          else acc0 = __builtin_amdgcn_fdot2_f32_bf16(pk[e / 2], (bf16x2){(__bf16)1.0f, (__bf16)1.0f}, acc0, false);
+          pk[e / 2] = __builtin_convertvector(pp, e2);
+          if (e & 2) acc1 = dot2_ones(pk[e / 2], acc1);
+          else acc0 = dot2_ones(pk[e / 2], acc0);
         }
         pb[tc] = __builtin_shufflevector(__builtin_shufflevector(pk[0], pk[1], 0, 1, 2, 3),
                                          __builtin_shufflevector(pk[2], pk[3], 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
@@ -238,7 +240,7 @@ __global__ __launch_bounds__(NW * 64, 4) void flash_window_kernel(FwdParams p) {
         const s16x4 lo4 = lds_tr(vs + vo);
         const s16x4 hi4 = lds_tr(vs + vo + 8 * ROWB);
         const s16x8 a8 = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
-        o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a8), pb[tc], o[d], 0, 0, 0);
+        o[d] = mfma32(__builtin_bit_cast(e8, a8), pb[tc], o[d]);
       }
   }
 
@@ -251,11 +253,11 @@ __global__ __launch_bounds__(NW * 64, 4) void flash_window_kernel(FwdParams p) {
 #pragma unroll
     for (int i4 = 0; i4 < 4; ++i4) {
       const int dd = d * 32 + 8 * i4 + 4 * g;
-      if (OUT_BF16) {
-        bf16x4 v4;
+      if (OUT16) {
+        e4 v4;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v4[e] = (__bf16)(o[d][4 * i4 + e] * inv);
-        *(bf16x4*)((__bf16*)p.o + ob + dd) = v4;
+        for (int e = 0; e < 4; ++e) v4[e] = (E)(o[d][4 * i4 + e] * inv);
+        *(e4*)((E*)p.o + ob + dd) = v4;
       } else {
         f32x4 v4;
 #pragma unroll
@@ -269,15 +271,20 @@ __global__ __launch_bounds__(NW * 64, 4) void flash_window_kernel(FwdParams p) {
 }  // namespace
 
 bool window_supports(const FwdParams& p) {
-  return p.dtype == 1 && p.D == 64 && p.bias == BIAS_RELPOS && !p.term_h && p.rel_h && p.rel_w &&
+  return (p.dtype == 1 || p.dtype == 2) && p.D == 64 && p.bias == BIAS_RELPOS && !p.term_h && p.rel_h && p.rel_w &&
          p.grid_h == G && p.grid_w == G && p.Tq == T && p.Tkv == T && p.Hq == p.Hkv && p.num_splits == 1 &&
          p.B * p.Hq <= 0x7fffffffLL && (int64_t)T * p.k_st * 2 <= 0x7fffffffLL;
 }
 
 hipError_t launch_window(const FwdParams& p, hipStream_t s) {
   const dim3 grid((unsigned)(p.B * p.Hq));
-  if (p.out_dtype == 1) hipLaunchKernelGGL(flash_window_kernel<true>, grid, dim3(NW * 64), 0, s, p);
-  else hipLaunchKernelGGL(flash_window_kernel<false>, grid, dim3(NW * 64), 0, s, p);
+  if (p.dtype == 2) {
+    if (p.out_dtype != 0) hipLaunchKernelGGL((flash_window_kernel<_Float16, true>), grid, dim3(NW * 64), 0, s, p);
+    else hipLaunchKernelGGL((flash_window_kernel<_Float16, false>), grid, dim3(NW * 64), 0, s, p);
+  } else {
+    if (p.out_dtype != 0) hipLaunchKernelGGL((flash_window_kernel<__bf16, true>), grid, dim3(NW * 64), 0, s, p);
+    else hipLaunchKernelGGL((flash_window_kernel<__bf16, false>), grid, dim3(NW * 64), 0, s, p);
+  }
   return hipGetLastError();
 }
 

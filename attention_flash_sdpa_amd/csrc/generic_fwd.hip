@@ -1,5 +1,5 @@
-// Generic fused attention on the vector ALUs: any head_dim up to 128, fp32 or
-// bf16 inputs, every bias kind.  It serves the fp32 path and shapes that the
+// Generic fused attention on the vector ALUs: any head_dim up to 128, fp32,
+// bf16 or fp16 inputs, every bias kind.  It serves the fp32 path and shapes that the
 // MFMA kernels do not cover.
 //
 // One wave per block, one query row per lane.  K/V tiles of 32 keys are staged
@@ -197,26 +197,26 @@ __global__ __launch_bounds__(64) void generic_fwd_kernel(FwdParams p) {
     float* op = (float*)p.o + ob;
 #pragma unroll
     for (int c = 0; c < DMAX; ++c) if (c < D) op[c] = acc[c] * inv;
-  } else {
-    __bf16* op = (__bf16*)p.o + ob;
+  } else {                            // 16-bit output in the input's type
+    TIN* op = (TIN*)p.o + ob;
 #pragma unroll
-    for (int c = 0; c < DMAX; ++c) if (c < D) op[c] = (__bf16)(acc[c] * inv);
+    for (int c = 0; c < DMAX; ++c) if (c < D) op[c] = (TIN)(acc[c] * inv);
   }
   if (p.lse) p.lse[(b * p.Hq + h) * p.Tq + i] = (l > 0.0f) ? m + logf(l) : -INFINITY;
 }
 
 // Bytes of dynamic LDS for rel-pos: per-lane term rows, plus the tables when
 // the terms are formed in the kernel.
-size_t relpos_lds(const FwdParams& p, bool fused) {
+static size_t relpos_lds(const FwdParams& p, bool fused) {
   size_t n = (size_t)(p.grid_h + p.grid_w) * 64;
   if (fused) n += (size_t)(2 * p.grid_h - 1 + 2 * p.grid_w - 1) * p.D;
   return n * sizeof(float);
 }
 
-int dmax_of(int64_t D) { return D <= 16 ? 16 : D <= 32 ? 32 : D <= 64 ? 64 : 128; }
+static int dmax_of(int64_t D) { return D <= 16 ? 16 : D <= 32 ? 32 : D <= 64 ? 64 : 128; }
 
 // Static LDS of one instance: K and V tiles plus the score column block.
-size_t static_lds(int64_t D) { return (size_t)2 * 32 * dmax_of(D) * 4 + 32 * 64 * 4; }
+static size_t static_lds(int64_t D) { return (size_t)2 * 32 * dmax_of(D) * 4 + 32 * 64 * 4; }
 
 template <typename TIN, int DMAX>
 static void launch_dim(const FwdParams& p, dim3 grid, hipStream_t s) {
@@ -250,7 +250,8 @@ bool generic_relpos_supported(const FwdParams& p, bool fused) {
 }
 
 hipError_t launch_generic_fwd(const FwdParams& p, hipStream_t s) {
-  return p.dtype == 0 ? launch_typed<float>(p, s) : launch_typed<__bf16>(p, s);
+  if (p.dtype == 0) return launch_typed<float>(p, s);
+  return p.dtype == 2 ? launch_typed<_Float16>(p, s) : launch_typed<__bf16>(p, s);
 }
 
 }  // namespace sdpa

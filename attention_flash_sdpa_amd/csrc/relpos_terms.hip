@@ -58,6 +58,7 @@ hipError_t launch_relpos_terms(const TermsParams& p, hipStream_t s) {
   const size_t lds = sizeof(float) * (size_t)(p.D + 1) * (size_t)p.grid_w;
   dim3 grid((unsigned)p.grid_h, (unsigned)p.H, (unsigned)p.B);
   if (p.dtype == 0) hipLaunchKernelGGL(relpos_terms_kernel<float>, grid, dim3(256), lds, s, p);
+  else if (p.dtype == 2) hipLaunchKernelGGL(relpos_terms_kernel<_Float16>, grid, dim3(256), lds, s, p);
   else hipLaunchKernelGGL(relpos_terms_kernel<__bf16>, grid, dim3(256), lds, s, p);
   return hipGetLastError();
 }

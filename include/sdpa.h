@@ -64,7 +64,11 @@ typedef enum sdpa_status {
   SDPA_ERR_HIP = -4           /* a kernel launch failed; see sdpa_last_error()           */
 } sdpa_status;
 
-typedef enum sdpa_dtype { SDPA_F32 = 0, SDPA_BF16 = 1 } sdpa_dtype;
+/* Element types.  SDPA_F16 inputs ([mlx-examples issue 1451], body: fp16
+ * together with the fused kernel, and the question of the additive rel-pos
+ * bias in fp16) run on the same kernels as SDPA_BF16; scores, the rel-pos
+ * bias and the softmax statistics stay in fp32 whatever the input type. */
+typedef enum sdpa_dtype { SDPA_F32 = 0, SDPA_BF16 = 1, SDPA_F16 = 2 } sdpa_dtype;
 
 /* [Axon PR 650], description: `:axes` is :bshd (default) or :bhsd. */
 typedef enum sdpa_layout { SDPA_BSHD = 0, SDPA_BHSD = 1 } sdpa_layout;
@@ -101,10 +105,10 @@ size_t sdpa_workspace_size(int64_t B, int64_t Hq, int64_t Hkv, int64_t Tq, int64
 /*
  * Fused attention with an optional mask.  [Axon PR 650], description.
  *   q [B, Hq, Tq, D] / [B, Tq, Hq, D], k and v [.., Hkv, Tkv, ..], o like q.
- *   dtype      element type of q, k, v (SDPA_F32 or SDPA_BF16).
+ *   dtype      element type of q, k, v (SDPA_F32, SDPA_BF16 or SDPA_F16).
  *   out_dtype  element type of o: dtype, or SDPA_F32 for unrounded output.
  *   Hq % Hkv == 0; query head h reads KV head h / (Hq / Hkv).
- *   D          head_dim: 16, 32, 64 or 128 (SDPA_BF16); 1..128 (SDPA_F32).
+ *   D          head_dim: 16, 32, 64 or 128 (16-bit types); 1..128 (SDPA_F32).
  *   scale      multiplies Q.K^T; NaN selects 1/sqrt(D).
  *   mask       NULL or &sdpa_mask{kind = NONE} for no mask.
  *   lse        optional [B, Hq, Tq] fp32 log-sum-exp of each score row

@@ -155,3 +155,21 @@ def test_last_kernel_starts_empty_per_thread():
     th.start()
     th.join()
     assert got == [b""]
+
+
+def test_no_symbol_defined_in_two_objects():
+    """Every externally visible function of the library comes from one object
+    file: two sources defining the same (e.g. template) helper would silently
+    resolve both call sites to one of them at link time."""
+    build = os.path.join(ROOT, "attention_flash_sdpa_amd", "_build")
+    objs = sorted(f for f in os.listdir(build) if f.endswith(".o")) if os.path.isdir(build) else []
+    if not objs:
+        pytest.skip("library objects not built here")
+    seen = {}
+    for f in objs:
+        out = subprocess.run(["nm", "--defined-only", "-g", os.path.join(build, f)], capture_output=True, text=True).stdout
+        for line in out.splitlines():
+            parts = line.split()
+            if len(parts) == 3 and parts[1] in "TWV" and "sdpa" in parts[2] and "__device_stub" not in parts[2]:
+                assert parts[2] not in seen, f"{parts[2]} in {seen.get(parts[2])} and {f}"
+                seen[parts[2]] = f

@@ -50,6 +50,45 @@ def test_full_size_sampled_rows(gpu, name):
     assert torch.isfinite(o).all()
 
 
+F16_NAMES = [n for n in NAMES if workloads.WORKLOADS[n].dtype == "bf16"]
+
+
+@pytest.mark.parametrize("layout", ["bhsd", "bshd"])
+@pytest.mark.parametrize("name", F16_NAMES)
+def test_replica_fp16(gpu, name, layout):
+    """fp16 inputs on every 16-bit route: the same kernel as bf16, within the
+    fp16 bound (probabilities rounded to fp16), lse, and fp16 output."""
+    wb = workloads.replica(name)
+    run_gpu(gpu, wb, gpu_inputs(workloads.generate(wb, seed=1, layout=layout)), layout)
+    torch.cuda.synchronize()
+    kernel_bf16 = gpu.last_kernel()
+    wl = workloads.replica(name, dtype="fp16")
+    print(f"[parity] fp16 replica {name} {layout}", flush=True)
+    x = workloads.generate(wl, seed=1, layout=layout)
+    o, lse = run_gpu(gpu, wl, gpu_inputs(x), layout, return_lse=True)
+    torch.cuda.synchronize()
+    assert gpu.last_kernel() == kernel_bf16
+    ref = run_oracle(wl, x, layout)
+    err = max_err(np64(o), ref["o"])
+    assert err <= TOL["fp16"], f"{name} {layout}: max-abs {err:.3e}"
+    assert max_err(np64(lse), ref["lse"]) <= TOL["fp16"]
+    ob = run_gpu(gpu, wl, gpu_inputs(x), layout, out_dtype=None)
+    assert ob.dtype == torch.float16
+    d = np.abs(np64(ob) - ref["o"]) - np.abs(ref["o"]) * 2.0 ** -11
+    assert d.max() <= TOL["fp16"], f"{name} {layout}: output-dtype excess {d.max():.3e}"
+
+
+def test_full_size_fp16_global_relpos(gpu):
+    wl = workloads.WORKLOADS["sam_global_relpos"].with_(dtype="fp16")
+    x = workloads.generate(wl, seed=0)
+    o, lse = run_gpu(gpu, wl, gpu_inputs(x), wl.layout, return_lse=True)
+    torch.cuda.synchronize()
+    picks = sample_picks(wl, n_random=24)
+    ro, rl = oracle.sdpa_rows(np64(x["q"]), np64(x["k"]), np64(x["v"]), picks, **oracle_kwargs(wl, x, wl.layout))
+    assert max_err(np64(rows_of(o, picks, wl.layout)), ro) <= TOL["fp16"]
+    assert max_err(np64(torch.stack([lse[b, h, i] for b, h, i in picks])), rl) <= TOL["fp16"]
+
+
 def test_relpos_terms_match_oracle(gpu):
     for name in ("tiny_relpos_fp32", "sam_window_relpos", "sam_global_relpos"):
         wl = workloads.replica(name)

@@ -87,7 +87,7 @@ WORKLOADS = {
         description="decoder-style GQA 4:1, causal + sliding window 1024"),
 }
 
-_TORCH_DTYPE = {"fp32": torch.float32, "bf16": torch.bfloat16}
+_TORCH_DTYPE = {"fp32": torch.float32, "bf16": torch.bfloat16, "fp16": torch.float16}
 
 
 def _round(x, dtype):
