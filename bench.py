@@ -230,6 +230,8 @@ def main():
     ap.add_argument("--workload", default="sam_global_relpos")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--dtype", choices=["bf16", "fp16"], default=None,
+                    help="override the workload's 16-bit input type (fp16 runs the same kernels)")
     ap.add_argument("--route", choices=["relpos", "additive"], default="relpos",
                     help="rel-pos workloads: 'additive' times the bias materialised as a [B, H, T, T] "
                          "additive mask in the input dtype (formed before timing) instead of the fused terms")
@@ -253,6 +255,11 @@ def main():
     if os.environ.get("SDPA_BENCH_UNFUSED", "0") == "1":
         fa.set_tuning("relpos_fused", 0)
     wl = workloads.WORKLOADS[args.workload]
+    if args.dtype:
+        if wl.dtype == "fp32":
+            print("bench.py: --dtype applies to 16-bit workloads", file=sys.stderr)
+            sys.exit(2)
+        wl = wl.with_(dtype=args.dtype)
     x = workloads.generate(wl, seed=0)
     g = {k: t.cuda() for k, t in x.items()}
     if wl.relpos:
@@ -277,7 +284,10 @@ def main():
     call_ms, terms_ms = kernel_events(fa, wl, g, args.steps)
     run_call(fa, wl, g, torch.empty_like(g["q"]))
     kernel = fa.last_kernel()
-    traffic, traffic_src = recorded_traffic(kernel, wl.name if args.route == "relpos" else wl.name + "_additive")
+    rec_name = wl.name + ("_additive" if args.route == "additive" else "")
+    if args.dtype and args.dtype != workloads.WORKLOADS[args.workload].dtype:
+        rec_name += "_" + args.dtype
+    traffic, traffic_src = recorded_traffic(kernel, rec_name)
     flash_ms = call_ms - terms_ms
     flash_flops = attn + (2 * allowed_pairs(wl) * wl.B * wl.Hq if wl.relpos else 0)
     if wl.relpos and terms_ms == 0.0:
@@ -296,7 +306,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if wl.dtype == "bf16" else "f32",
+        "dtype": {"bf16": "bf16", "fp16": "f16"}.get(wl.dtype, "f32"),
         "data": "synthetic",
         "config": {"workload": wl.name, "description": wl.description, "layout": wl.layout, "B": wl.B,
                    "Hq": wl.Hq, "Hkv": wl.Hkv, "Tq": wl.Tq, "Tkv": wl.Tkv, "head_dim": wl.D,
