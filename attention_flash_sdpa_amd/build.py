@@ -34,7 +34,7 @@ def hipcc():
 # Per-file extra flags.  The MFMA attention kernels take row maxima of scores
 # produced by the matrix cores; without NaN honouring the maxima need no
 # quieting moves (NaN scores still reach the output through exp and P.V).
-EXTRA = {f: ["-fno-honor-nans"] for f in ("flash_mfma.hip", "flash_split64.hip", "flash_tiled.hip", "flash_window.hip")}
+EXTRA = {f: ["-fno-honor-nans"] for f in ("flash_mfma.hip", "flash_split64.hip", "flash_split64w.hip", "flash_tiled.hip", "flash_window.hip")}
 # Matrix-op accumulators in ordinary VGPRs: the tiled kernel's mask modes
 # otherwise move them to AGPRs and lose a wave per SIMD.
 EXTRA["flash_tiled.hip"] = EXTRA["flash_tiled.hip"] + ["-mllvm", "-amdgpu-mfma-vgpr-form"]

@@ -21,6 +21,7 @@ thread_local const char* g_last_kernel = "";
 std::atomic<int64_t> g_num_splits{0};
 std::atomic<int64_t> g_relpos_fused{1};
 std::atomic<int64_t> g_split64{1};
+std::atomic<int64_t> g_split64w{1};
 std::atomic<int64_t> g_tiled{1};
 
 int fail(int status, const char* fmt, ...) {
@@ -106,7 +107,7 @@ sdpa::FwdParams base_params(const void* q, const void* k, const void* v, void* o
   return p;
 }
 
-enum Route { R_GENERIC, R_D16, R_WINDOW, R_SPLIT64, R_TILED, R_MFMA };
+enum Route { R_GENERIC, R_D16, R_WINDOW, R_SPLIT64W, R_SPLIT64, R_TILED, R_MFMA };
 
 // The kernel a call runs on: the first route whose conditions hold.
 Route route_of(const sdpa::FwdParams& p) {
@@ -115,6 +116,8 @@ Route route_of(const sdpa::FwdParams& p) {
   if (!(p.scale > 0.0f && std::isfinite(p.scale))) return R_GENERIC;
   if (sdpa::d16_supports(p)) return R_D16;
   if (sdpa::window_supports(p)) return R_WINDOW;
+  const int64_t wide = g_split64w.load();     // 0 off, 1 where the shape fills the CUs, 2 wherever supported
+  if (g_split64.load() && wide && sdpa::split64w_supports(p, wide == 1)) return R_SPLIT64W;
   if (g_split64.load() && sdpa::split64_supports(p)) return R_SPLIT64;
   if (g_tiled.load() && sdpa::tiled_supports(p)) return R_TILED;
   if (sdpa::flash_mfma_supports(p)) return R_MFMA;
@@ -130,6 +133,7 @@ int launch(const sdpa::FwdParams& p, hipStream_t s) {
       e = sdpa::launch_d16(p, s);
       break;
     case R_WINDOW: name = "flash_window_kernel"; e = sdpa::launch_window(p, s); break;
+    case R_SPLIT64W: name = "flash_split64w_kernel"; e = sdpa::launch_split64w(p, s); break;
     case R_SPLIT64: name = "flash_split64_kernel"; e = sdpa::launch_split64(p, s); break;
     case R_TILED: name = "flash_tiled_kernel"; e = sdpa::launch_tiled(p, s); break;
     case R_MFMA: name = "flash_mfma_kernel"; e = sdpa::launch_flash_mfma(p, s); break;
@@ -314,6 +318,11 @@ int sdpa_set_tuning(const char* key, int64_t value) {
   if (!std::strcmp(key, "split_halves")) {
     if (value != 0 && value != 1) return fail(SDPA_ERR_INVALID, "split_halves must be 0 or 1");
     g_split64.store(value);
+    return SDPA_OK;
+  }
+  if (!std::strcmp(key, "split_wide")) {
+    if (value < 0 || value > 2) return fail(SDPA_ERR_INVALID, "split_wide must be 0, 1 or 2");
+    g_split64w.store(value);
     return SDPA_OK;
   }
   if (!std::strcmp(key, "tiled")) {

@@ -233,34 +233,40 @@ __global__ __launch_bounds__(256, 3) void flash_split64_kernel(FwdParams p) {
   // tile parity (which half of a 64-wide grid row) is then the unrolled step.
   const int nt = (int)((p.Tkv + BN - 1) / BN);
   const int nt0 = min(nt, (((nt + 1) / 2) + 1) & ~1);
+  const int tfull = (int)(p.Tkv / BN);          // tiles with no key past the end
   const int tbeg = hf ? nt0 : 0;
   const int tend = hf ? nt : nt0;
   const int niter = nt0;                        // half 0 has at least as many tiles
   const char* kvbase = (const char*)((const E*)(qb ? p.v : p.k) + b * p.k_sb + hk * p.k_sh);
-  // Wave qb of half hf copies the K (qb = 0) or V (qb = 1) tile of its half.
+  // Key rows are addressed with 32-bit byte offsets (the launcher checks that
+  // the key range spans less than 2^31 bytes).
   const int rstride = (int)(p.k_st * 2);
-  const int64_t span = ((p.Tkv - 1) * p.k_st + 64) * 2;     // bytes from the row base to the end of the last key row
+  const int tile_bytes = BN * rstride;
+  const int span = (int)(((p.Tkv - 1) * p.k_st + 64) * 2);   // bytes from the row base to the end of the last key row
   // Wave qb of half hf copies the K (qb = 0) or V (qb = 1) tile of its half:
   // 4 instructions of 64 lanes x 16 bytes; lane data lands at LDS offset 16 * lane.
   // Per-lane byte offsets inside a tile are fixed; a per-tile descriptor moves
   // the base and shrinks the record count, so rows past the key range read 0.
+  // Instruction j carries the immediate offset j * 1 KB, which moves both the
+  // LDS destination and the memory address, so the memory offsets drop it.
   int voff[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int L = 64 * j + lane, row = L >> 3, pos = L & 7;
-    voff[j] = row * rstride + ((pos ^ (qb ? vswz(row) : kswz(row))) << 4);
+    voff[j] = row * rstride + ((pos ^ (qb ? vswz(row) : kswz(row))) << 4) - j * 1024;
   }
   auto stage = [&](int t, auto par) {          // tile t into the parity-PAR objects
     constexpr int PAR = decltype(par)::value;
-    const int64_t tb = (int64_t)t * BN * rstride;
-    const int nrec = (int)max((int64_t)0, min(span - tb, (int64_t)0x7fffffff));
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)(kvbase + tb), 0, nrec, 0x00020000);
+    const int tb = t * tile_bytes;
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(kvbase + (unsigned)tb), 0, max(span - tb, 0), 0x00020000);
     auto issue = [&](lds_char* obj) {
       lds_char* dst = obj + hf * TILEB;
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(dst + j * 1024), 16,
-                                                 voff[j], 0, 0, 0);
+      __attribute__((address_space(3))) void* d = (__attribute__((address_space(3))) void*)dst;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, d, 16, voff[0], 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, d, 16, voff[1], 0, 1024, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, d, 16, voff[2], 0, 2048, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, d, 16, voff[3], 0, 3072, 0);
     };
     if (qb == 0) issue(PAR ? kb : ka);          // one static destination object per call site
     else issue(PAR ? vb : va);
@@ -268,28 +274,40 @@ __global__ __launch_bounds__(256, 3) void flash_split64_kernel(FwdParams p) {
 
   f32x16 o[2] = {(f32x16){}, (f32x16){}};
   float m = -INFINITY, l = 0.0f;
+  float mz = 0.0f;                              // m, or 0 while m = -inf
   const int j16 = lane & 15, dh = (lane >> 4) & 1;
-  // Transposing-read offsets of the V tile (tile-invariant).
+  // Tile-invariant LDS byte offsets (this half's tile included) of the
+  // transposing V reads and of the K reads.
   int vro[2][2];
 #pragma unroll
   for (int tc = 0; tc < 2; ++tc)
 #pragma unroll
     for (int d = 0; d < 2; ++d) {
       const int row0 = 16 * tc + 4 * g + (j16 >> 2);
-      vro[tc][d] = row0 * ROWB + ((((4 * d + 2 * dh + ((j16 & 3) >> 1)) ^ vswz(row0)) << 4) + ((j16 & 1) << 3));
+      vro[tc][d] = hf * TILEB + row0 * ROWB + ((((4 * d + 2 * dh + ((j16 & 3) >> 1)) ^ vswz(row0)) << 4) + ((j16 & 1) << 3));
     }
   int kro[4];
 #pragma unroll
-  for (int c = 0; c < 4; ++c) kro[c] = ql * ROWB + (((2 * c + g) ^ kswz(ql)) << 4);
+  for (int c = 0; c < 4; ++c) kro[c] = hf * TILEB + ql * ROWB + (((2 * c + g) ^ kswz(ql)) << 4);
 
   auto step = [&](int t, auto par, float th_pair) {
     constexpr int PAR = decltype(par)::value;     // tile parity: buffer and grid-row half
-    const lds_char* ks = (PAR ? kb : ka) + hf * TILEB;
-    const lds_char* vs = (PAR ? vb : va) + hf * TILEB;
+    const lds_char* ks = PAR ? kb : ka;
+    const lds_char* vs = PAR ? vb : va;
     f32x16 s = (MODE == S_NONE) ? (f32x16){} : cinit[PAR];
 #pragma unroll
     for (int c = 0; c < 4; ++c) s = mfma32(lds_b128<e8>(ks + kro[c]), qf[c], s);
-    if ((t + 1) * BN > p.Tkv) {
+    // V fragments now, so their LDS latency passes under the softmax.
+    e8 vf[2][2];
+#pragma unroll
+    for (int tc = 0; tc < 2; ++tc)
+#pragma unroll
+      for (int d = 0; d < 2; ++d) {
+        const s16x4 lo4 = lds_tr(vs + vro[tc][d]);
+        const s16x4 hi4 = lds_tr(vs + vro[tc][d] + 8 * ROWB);
+        vf[tc][d] = __builtin_bit_cast(e8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+    if (t >= tfull) {
       asm volatile("" ::: "memory");     // ragged last tile: a real branch, full tiles skip it
       const int kl0 = t * BN + 4 * g;
 #pragma unroll
@@ -303,7 +321,7 @@ __global__ __launch_bounds__(256, 3) void flash_split64_kernel(FwdParams p) {
     // the tile max, rescales O and l, and recomputes the probabilities.
     e8 pb[2];
     auto probs = [&](float off) -> float {
-      float acc0 = 0.0f, acc1 = 0.0f;
+      float acc = 0.0f;
 #pragma unroll
       for (int tc = 0; tc < 2; ++tc) {
         e2 pk[4];
@@ -311,17 +329,16 @@ __global__ __launch_bounds__(256, 3) void flash_split64_kernel(FwdParams p) {
         for (int e = 0; e < 8; e += 2) {
           const f32x2 pp = {fexp2(fmaf(s[8 * tc + e], c2, off)), fexp2(fmaf(s[8 * tc + e + 1], c2, off))};
           pk[e / 2] = __builtin_convertvector(pp, e2);
-          if (e & 2) acc1 = dot2_ones(pk[e / 2], acc1);
-          else acc0 = dot2_ones(pk[e / 2], acc0);
+          acc = dot2_ones(pk[e / 2], acc);
         }
         pb[tc] = __builtin_shufflevector(__builtin_shufflevector(pk[0], pk[1], 0, 1, 2, 3),
                                          __builtin_shufflevector(pk[2], pk[3], 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
       }
-      return acc0 + acc1;
+      return acc;
     };
-    float lt = probs(rowb - ((m == -INFINITY) ? 0.0f : m));
+    float lt = probs(rowb - mz);
     // (m = -inf: no key seen yet; the reference must come from an actual max)
-    if (__builtin_expect(__any(!(lt <= kTauSum) || m == -INFINITY), 0)) {
+    if (__builtin_expect((__builtin_amdgcn_ballot_w64(!(lt <= kTauSum)) | __builtin_amdgcn_ballot_w64(m == -INFINITY)) != 0, 0)) {
       float smax = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
 #pragma unroll
       for (int i = 4; i < 16; i += 2) smax = fmaxf(smax, fmaxf(s[i], s[i + 1]));
@@ -331,24 +348,20 @@ __global__ __launch_bounds__(256, 3) void flash_split64_kernel(FwdParams p) {
       const float mn = need ? tmax : m;
       const float alpha = need ? ((m == -INFINITY) ? 0.0f : fexp2(m - mn)) : 1.0f;
       m = mn;
+      mz = (m == -INFINITY) ? 0.0f : m;
       l *= alpha;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         o[0][i] *= alpha;
         o[1][i] *= alpha;
       }
-      lt = probs(rowb - ((m == -INFINITY) ? 0.0f : m));
+      lt = probs(rowb - mz);
     }
     l += lt;
 #pragma unroll
     for (int tc = 0; tc < 2; ++tc)
 #pragma unroll
-      for (int d = 0; d < 2; ++d) {
-        const s16x4 lo4 = lds_tr(vs + vro[tc][d]);
-        const s16x4 hi4 = lds_tr(vs + vro[tc][d] + 8 * ROWB);
-        const s16x8 a8 = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
-        o[d] = mfma32(__builtin_bit_cast(e8, a8), pb[tc], o[d]);
-      }
+      for (int d = 0; d < 2; ++d) o[d] = mfma32(vf[tc][d], pb[tc], o[d]);
   };
 
   using P0 = std::integral_constant<int, 0>;
@@ -363,7 +376,23 @@ __global__ __launch_bounds__(256, 3) void flash_split64_kernel(FwdParams p) {
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   float th_next = (tbeg < tend) ? th_of(tbeg) : 0.0f;
-  for (int it = 0; it < niter; it += 2) {
+  // Steady state: every tile the body touches exists in both halves.
+  const int cmin = min(nt0, nt - nt0);
+  int it = 0;
+  for (; it + 2 < cmin; it += 2) {
+    const int t = tbeg + it;
+    const float th_cur = th_next;
+    th_next = th_of(t + 2);
+    stage(t + 1, P1{});
+    step(t, P0{}, th_cur);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    stage(t + 2, P0{});
+    step(t + 1, P1{}, th_cur);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+  for (; it < niter; it += 2) {
     const int t = tbeg + it;
     const float th_cur = th_next;
     if (t + 2 < tend) th_next = th_of(t + 2);

@@ -31,6 +31,7 @@ HBM_PEAK_GBS = 8000.0               # MI355X HBM3E, published
 # Source file of each attention kernel, for matching recorded counter data.
 KERNEL_SOURCE = {
     "flash_split64_kernel": "flash_split64.hip",
+    "flash_split64w_kernel": "flash_split64w.hip",
     "flash_tiled_kernel": "flash_tiled.hip",
     "flash_window_kernel": "flash_window.hip",
     "flash_mfma_kernel": "flash_mfma.hip",

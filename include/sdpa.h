@@ -185,6 +185,10 @@ const char* sdpa_last_kernel(void);
  *   "split_halves" 1 (default) = for head_dim 64 with few query rows, each
  *                  workgroup splits the key range between its waves and merges
  *                  the halves; 0 = always one key range per wave.
+ *   "split_wide"   1 (default) = of those, shapes whose query rows fill the
+ *                  CUs in workgroups of 192 rows run on 12-wave workgroups
+ *                  (six 32-row query blocks x two key halves); 2 = every such
+ *                  shape runs on them; 0 = always the 4-wave workgroups.
  *   "tiled"        1 (default) = bf16 head_dim 64 / 128 attention with no mask
  *                  or a causal / sliding mask runs on the double-buffered
  *                  kernel; 0 = on the general MFMA kernel.

@@ -123,6 +123,9 @@ def test_status_strings_and_tuning():
     assert lib.sdpa_set_tuning(b"num_splits", -1) == -1
     assert lib.sdpa_set_tuning(b"num_splits", 0) == 0
     assert lib.sdpa_set_tuning(b"relpos_fused", 2) == -1
+    assert lib.sdpa_set_tuning(b"split_wide", 3) == -1
+    assert lib.sdpa_set_tuning(b"split_wide", 2) == 0
+    assert lib.sdpa_set_tuning(b"split_wide", 1) == 0
     assert lib.sdpa_set_tuning(b"relpos_fused", 1) == 0
     assert lib.sdpa_relpos_fused(1, 64, 64, 64) == 1      # SAM ViT-B global grid: one kernel
     assert lib.sdpa_relpos_fused(1, 64, 14, 14) == 1      # SAM 14x14 window: one kernel

@@ -213,21 +213,37 @@ def test_d16_masks(gpu):
     check(gpu, 1, 4, 4, 100, 50, 16, mask={"kind": "sliding", "window": 5, "offset": -40}, seed=20)
 
 
+def _split_mode(gpu, mode):
+    """0: one key range per wave; 1: key halves in 4-wave workgroups; 2: key
+    halves in 12-wave workgroups (forced for any size)."""
+    gpu.set_tuning("split_halves", 1 if mode else 0)
+    gpu.set_tuning("split_wide", 2 if mode == 2 else 0)
+
+
+def _split_default(gpu):
+    gpu.set_tuning("split_halves", 1)
+    gpu.set_tuning("split_wide", 1)
+
+
 @pytest.mark.parametrize("name", ["sam_global_relpos"])
-@pytest.mark.parametrize("halves", [0, 1])
+@pytest.mark.parametrize("halves", [0, 1, 2])
 @pytest.mark.parametrize("fused", [0, 1])
-def test_relpos_kernel_variants(gpu, name, halves, fused):
+@pytest.mark.parametrize("gh", [5, 7])
+def test_relpos_kernel_variants(gpu, name, halves, fused, gh):
     """Every kernel route for the SAM global rel-pos shape agrees with the oracle:
-    key range split in-workgroup or not, terms formed in-kernel or precomputed."""
-    wl = workloads.replica(name, grid=(5, 64), Tq=5 * 64, Tkv=5 * 64)
+    key range split in-workgroup or not (4- or 12-wave workgroups; 5 and 7
+    grid rows leave the last 192-row workgroup partly empty), terms formed
+    in-kernel or precomputed."""
+    wl = workloads.replica(name, grid=(gh, 64), Tq=gh * 64, Tkv=gh * 64)
     x = {k_: t.cuda() for k_, t in workloads.generate(wl, seed=5).items()}
-    gpu.set_tuning("split_halves", halves)
+    _split_mode(gpu, halves)
     gpu.set_tuning("relpos_fused", fused)
     try:
         o, lse = gpu.sdpa_relpos(x["q"], x["k"], x["v"], x["rel_pos_h"], x["rel_pos_w"], wl.grid, scale=wl.scale,
                                  out_dtype=torch.float32, return_lse=True)
+        assert gpu.last_kernel() == ["flash_mfma_kernel", "flash_split64_kernel", "flash_split64w_kernel"][halves]
     finally:
-        gpu.set_tuning("split_halves", 1)
+        _split_default(gpu)
         gpu.set_tuning("relpos_fused", 1)
     ref = oracle.sdpa(np64(x["q"].cpu()), np64(x["k"].cpu()), np64(x["v"].cpu()), scale=wl.scale,
                       rel_pos={"rel_pos_h": np64(x["rel_pos_h"].cpu()), "rel_pos_w": np64(x["rel_pos_w"].cpu()),
@@ -236,15 +252,36 @@ def test_relpos_kernel_variants(gpu, name, halves, fused):
     assert max_err(np64(lse), ref["lse"]) <= TOL["bf16"]
 
 
-@pytest.mark.parametrize("halves", [0, 1])
+@pytest.mark.parametrize("fused", [0, 1])
+def test_wide_split_fp16(gpu, fused):
+    """The 12-wave workgroups on fp16 inputs with fp16 output."""
+    wl = workloads.replica("sam_global_relpos", grid=(7, 64), Tq=7 * 64, Tkv=7 * 64, dtype="fp16")
+    x = {k_: t.cuda() for k_, t in workloads.generate(wl, seed=6).items()}
+    _split_mode(gpu, 2)
+    gpu.set_tuning("relpos_fused", fused)
+    try:
+        o = gpu.sdpa_relpos(x["q"], x["k"], x["v"], x["rel_pos_h"], x["rel_pos_w"], wl.grid, scale=wl.scale)
+        assert gpu.last_kernel() == "flash_split64w_kernel"
+    finally:
+        _split_default(gpu)
+        gpu.set_tuning("relpos_fused", 1)
+    assert o.dtype == torch.float16
+    ref = oracle.sdpa(np64(x["q"].cpu()), np64(x["k"].cpu()), np64(x["v"].cpu()), scale=wl.scale,
+                      rel_pos={"rel_pos_h": np64(x["rel_pos_h"].cpu()), "rel_pos_w": np64(x["rel_pos_w"].cpu()),
+                               "grid": wl.grid})
+    assert max_err(np64(o), ref["o"]) <= TOL["fp16"]
+
+
+@pytest.mark.parametrize("halves", [0, 1, 2])
 @pytest.mark.parametrize("Tkv", [32, 33, 95, 200, 4096])
 def test_d64_no_mask_key_splits(gpu, halves, Tkv):
-    gpu.set_tuning("split_halves", halves)
+    _split_mode(gpu, halves)
     try:
         check(gpu, 1, 3, 3, 130, Tkv, 64, seed=21)
         check(gpu, 1, 4, 2, 64, Tkv, 64, layout="bshd", seed=22)
+        check(gpu, 2, 2, 1, 400, Tkv, 64, seed=23)
     finally:
-        gpu.set_tuning("split_halves", 1)
+        _split_default(gpu)
 
 
 @pytest.mark.parametrize("pattern", ["rising", "falling", "spike", "huge"])
@@ -270,13 +307,13 @@ def test_running_max_paths(gpu, pattern, D):
         k = k * 40.0
     q, k, v = (x.to(torch.bfloat16) for x in (q, k, v))
     ref = oracle.sdpa(np64(q), np64(k), np64(v), scale=1.0 / D ** 0.5)
-    for halves, tiled in ((0, 0), (0, 1), (1, 1)):
-        gpu.set_tuning("split_halves", halves)
+    for halves, tiled in ((0, 0), (0, 1), (1, 1), (2, 1)):
+        _split_mode(gpu, halves)
         gpu.set_tuning("tiled", tiled)
         try:
             o = gpu.sdpa(q.cuda(), k.cuda(), v.cuda(), scale=1.0 / D ** 0.5, out_dtype=torch.float32)
         finally:
-            gpu.set_tuning("split_halves", 1)
+            _split_default(gpu)
             gpu.set_tuning("tiled", 1)
         assert max_err(np64(o), ref["o"]) <= TOL["bf16"], (pattern, halves, tiled)
 
@@ -349,6 +386,11 @@ def test_dispatch_names_the_kernel(gpu):
     gpu.sdpa_relpos(x["q"], x["k"], x["v"], x["rel_pos_h"], x["rel_pos_w"], wl.grid)
     torch.cuda.synchronize()
     assert gpu.last_kernel() == "flash_split64_kernel"
+    wl = workloads.WORKLOADS["sam_global_relpos"]              # 256 workgroups of 192 rows: one per CU
+    x = {k_: t.cuda() for k_, t in workloads.generate(wl, seed=0, layout="bhsd").items()}
+    gpu.sdpa_relpos(x["q"], x["k"], x["v"], x["rel_pos_h"], x["rel_pos_w"], wl.grid)
+    torch.cuda.synchronize()
+    assert gpu.last_kernel() == "flash_split64w_kernel"
     wl = workloads.replica("sam_window_relpos")
     x = {k_: t.cuda() for k_, t in workloads.generate(wl, seed=0, layout="bhsd").items()}
     gpu.sdpa_relpos(x["q"], x["k"], x["v"], x["rel_pos_h"], x["rel_pos_w"], wl.grid)
