@@ -64,17 +64,17 @@ constexpr int TILEB = BN * ROWB;      // 4 KB
 constexpr int GSLOT = 32 * 97;        // floats of one query block's term_w gather slot
 constexpr int UBYTES = 3 * GSLOT * 4;     // shared region: tables / gather slots / merge exchange (3 blocks at a time)
 
-// LDS.  Four distinct objects for the K / V tiles of buffer parity 0 / 1
-// ([head slot][key half][tile] each): a step copies into the parity-(t+1)
-// objects while it reads the parity-t ones, and because they are distinct
+// LDS.  Two distinct objects for the K / V tiles of buffer parity 0 / 1, each
+// [head slot][K, V][key half][tile]: a step copies into the parity-(t+1)
+// object while it reads the parity-t one, and because they are distinct
 // objects the compiler knows the in-flight LDS-direct copies cannot alias the
 // reads.  term_h^T per query block [y][32 q] for the whole kernel; one region
 // that holds in turn the rel-pos tables, the term_w gather slots and the
 // merge exchange.
-__shared__ __attribute__((aligned(16))) char w64_ka[4 * TILEB];
-__shared__ __attribute__((aligned(16))) char w64_kb[4 * TILEB];
-__shared__ __attribute__((aligned(16))) char w64_va[4 * TILEB];
-__shared__ __attribute__((aligned(16))) char w64_vb[4 * TILEB];
+__shared__ __attribute__((aligned(16))) char w64_t0[8 * TILEB];
+__shared__ __attribute__((aligned(16))) char w64_t1[8 * TILEB];
+// byte offset of a tile in a parity object
+__host__ __device__ constexpr int tile_off(int hs, int kv, int half) { return ((2 * hs + kv) * 2 + half) * TILEB; }
 __shared__ __attribute__((aligned(16))) float w64_th[NQB * 64 * 32];
 __shared__ __attribute__((aligned(16))) char w64_u[UBYTES];
 
@@ -109,10 +109,8 @@ __global__ __launch_bounds__(64 * NW, 1) void flash_split64w_kernel(FwdParams p)
   typedef typename Vec16<E>::x8 e8;
   typedef typename Vec16<E>::x4 e4;
   typedef typename Vec16<E>::x2 e2;
-  lds_char* const ka = (lds_char*)w64_ka;
-  lds_char* const kb = (lds_char*)w64_kb;
-  lds_char* const va = (lds_char*)w64_va;
-  lds_char* const vb = (lds_char*)w64_vb;
+  lds_char* const tp0 = (lds_char*)w64_t0;
+  lds_char* const tp1 = (lds_char*)w64_t1;
   lds_float* const ths = (lds_float*)w64_th;
   lds_char* const ureg = (lds_char*)w64_u;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -181,33 +179,38 @@ __global__ __launch_bounds__(64 * NW, 1) void flash_split64w_kernel(FwdParams p)
     const int L = 128 * dp + 64 * j + lane, row = L >> 3, pos = L & 7;
     voff[j] = row * rstride + ((pos ^ (dk ? vswz(row) : kswz(row))) << 4) - j * 1024;
   }
-  // Tile it of the copier's half into the parity-PAR objects.
-  auto stage = [&](int it, auto par) {
+  const int dst = cslot1 ? tile_off(1, dk, dh) : tile_off(0, dk, dh) + dp * 2048;   // byte offset in a parity object
+  // Copy role, fixed per wave: 0 none, 1 a 2 KB part (head slot 0), 2 a whole
+  // tile (head slot 1).  The main loop is instantiated per role, so no step
+  // branches on it.
+  const int role = !copier ? 0 : (cslot1 ? 2 : 1);
+  // Tile it of the copier's half into the parity-PAR object (GUARD: skip tiles
+  // past the half's end).
+  auto stage = [&](int it, auto par, auto rl, auto guard) {
     constexpr int PAR = decltype(par)::value;
+    constexpr int ROLE = decltype(rl)::value;
+    if (ROLE == 0) return;
     const int t = dtbeg + it;
-    if (!copier || t >= dtend) return;
+    if (decltype(guard)::value && t >= dtend) return;
     const int tb = t * tile_bytes;
     const __amdgpu_buffer_rsrc_t rs =
         __builtin_amdgcn_make_buffer_rsrc((void*)(kvbase + (unsigned)tb), 0, max(span - tb, 0), 0x00020000);
-    auto issue = [&](lds_char* obj) {
-      if (!cslot1) {
-        lds_void* d = (lds_void*)(obj + dh * TILEB + dp * 2048);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, d, 16, voff[0], 0, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, d, 16, voff[1], 0, 1024, 0);
-      } else {
-        lds_void* d = (lds_void*)(obj + (2 + dh) * TILEB);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, d, 16, voff[0], 0, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, d, 16, voff[1], 0, 1024, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, d, 16, voff[2], 0, 2048, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, d, 16, voff[3], 0, 3072, 0);
-      }
-    };
-    if (dk == 0) issue(PAR ? kb : ka);          // one static destination object per call site
-    else issue(PAR ? vb : va);
+    lds_void* d = (lds_void*)((PAR ? tp1 : tp0) + dst);     // one static destination object per call site
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, d, 16, voff[0], 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, d, 16, voff[1], 0, 1024, 0);
+    if (ROLE == 2) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, d, 16, voff[2], 0, 2048, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, d, 16, voff[3], 0, 3072, 0);
+    }
   };
   using P0 = std::integral_constant<int, 0>;
   using P1 = std::integral_constant<int, 1>;
-  stage(0, P0{});                               // the first tiles travel during the set-up below
+  using R1 = std::integral_constant<int, 1>;
+  using R2 = std::integral_constant<int, 2>;
+  using G1 = std::true_type;
+  // the first tiles travel during the set-up below
+  if (role == 1) stage(0, P0{}, R1{}, G1{});
+  else if (role == 2) stage(0, P0{}, R2{}, G1{});
 
   const E* qp = (const E*)p.q + b * p.q_sb + h * p.q_sh;
   e8 qf[4];
@@ -340,16 +343,16 @@ __global__ __launch_bounds__(64 * NW, 1) void flash_split64w_kernel(FwdParams p)
 #pragma unroll
     for (int d = 0; d < 2; ++d) {
       const int row0 = 16 * tc + 4 * g + (j16 >> 2);
-      vro[tc][d] = (2 * hs + hf) * TILEB + row0 * ROWB + ((((4 * d + 2 * dhl + ((j16 & 3) >> 1)) ^ vswz(row0)) << 4) + ((j16 & 1) << 3));
+      vro[tc][d] = tile_off(hs, 0, hf) + row0 * ROWB + ((((4 * d + 2 * dhl + ((j16 & 3) >> 1)) ^ vswz(row0)) << 4) + ((j16 & 1) << 3));
     }
   int kro[4];
 #pragma unroll
-  for (int c = 0; c < 4; ++c) kro[c] = (2 * hs + hf) * TILEB + ql * ROWB + (((2 * c + g) ^ kswz(ql)) << 4);
+  for (int c = 0; c < 4; ++c) kro[c] = tile_off(hs, 0, hf) + ql * ROWB + (((2 * c + g) ^ kswz(ql)) << 4);
 
-  auto step = [&](int t, auto par, float th_pair) {
+  auto step = [&](int t, auto par, float th_pair, auto ragged) {
     constexpr int PAR = decltype(par)::value;     // tile parity: buffer and grid-row half
-    const lds_char* ks = PAR ? kb : ka;
-    const lds_char* vs = PAR ? vb : va;
+    const lds_char* ks = PAR ? tp1 : tp0;
+    const lds_char* vs = (PAR ? tp1 : tp0) + tile_off(0, 1, 0);
     f32x16 s = (MODE == S_NONE) ? (f32x16){} : cinit[PAR];
 #pragma unroll
     for (int c = 0; c < 4; ++c) s = mfma32(lds_b128<e8>(ks + kro[c]), qf[c], s);
@@ -363,7 +366,7 @@ __global__ __launch_bounds__(64 * NW, 1) void flash_split64w_kernel(FwdParams p)
         const s16x4 hi4 = lds_tr(vs + vro[tc][d] + 8 * ROWB);
         vf[tc][d] = __builtin_bit_cast(e8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
       }
-    if (t >= tfull) {
+    if (decltype(ragged)::value && t >= tfull) {
       asm volatile("" ::: "memory");     // ragged last tile: a real branch, full tiles skip it
       const int kl0 = t * BN + 4 * g;
 #pragma unroll
@@ -427,37 +430,44 @@ __global__ __launch_bounds__(64 * NW, 1) void flash_split64w_kernel(FwdParams p)
     return 0.0f;
   };
   float th_next = (tbeg < tend) ? th_of(tbeg) : 0.0f;
-  // Steady state: every tile the body touches exists in both halves.
-  const int cmin = min(nt0, nt - nt0);
-  int it = 0;
-  for (; it + 2 < cmin; it += 2) {
-    const int t = tbeg + it;
-    const float th_cur = th_next;
-    th_next = th_of(t + 2);
-    stage(it + 1, P1{});
-    step(t, P0{}, th_cur);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    stage(it + 2, P0{});
-    step(t + 1, P1{}, th_cur);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-  }
-  for (; it < niter; it += 2) {
-    const int t = tbeg + it;
-    const float th_cur = th_next;
-    if (t + 2 < tend) th_next = th_of(t + 2);
-    stage(it + 1, P1{});
-    if (t < tend) step(t, P0{}, th_cur);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (it + 1 < niter) {
-      stage(it + 2, P0{});
-      if (t + 1 < tend) step(t + 1, P1{}, th_cur);
+  using G0 = std::false_type;
+  auto main_loop = [&](auto rl) {
+    // Steady state: every tile the body touches exists in both halves and is
+    // full (only the last tile of the key range can be ragged).
+    const int cmin = min(nt0, nt - nt0);
+    int it = 0;
+    for (; it + 2 < cmin; it += 2) {
+      const int t = tbeg + it;
+      const float th_cur = th_next;
+      th_next = th_of(t + 2);
+      stage(it + 1, P1{}, rl, G0{});
+      step(t, P0{}, th_cur, G0{});
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      stage(it + 2, P0{}, rl, G0{});
+      step(t + 1, P1{}, th_cur, G0{});
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
     }
-  }
+    for (; it < niter; it += 2) {
+      const int t = tbeg + it;
+      const float th_cur = th_next;
+      if (t + 2 < tend) th_next = th_of(t + 2);
+      stage(it + 1, P1{}, rl, G1{});
+      if (t < tend) step(t, P0{}, th_cur, G1{});
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (it + 1 < niter) {
+        stage(it + 2, P0{}, rl, G1{});
+        if (t + 1 < tend) step(t + 1, P1{}, th_cur, G1{});
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+      }
+    }
+  };
+  if (role == 1) main_loop(R1{});
+  else if (role == 2) main_loop(R2{});
+  else main_loop(std::integral_constant<int, 0>{});
 
   // ---- merge the two key halves of each query block through LDS, three
   // query blocks per pass (the exchange reuses the shared region; with an
