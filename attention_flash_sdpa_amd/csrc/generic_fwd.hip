@@ -42,12 +42,15 @@ __global__ __launch_bounds__(64) void generic_fwd_kernel(FwdParams p) {
   const TIN* kp = (const TIN*)p.k + b * p.k_sb + hk * p.k_sh;
   const TIN* vp = (const TIN*)p.v + b * p.k_sb + hk * p.k_sh;
 
+  // (qp points at a valid row for every lane, so the loads need no lane test)
   float qr[DMAX], acc[DMAX];
 #pragma unroll
   for (int c = 0; c < DMAX; ++c) {
-    qr[c] = (c < D && live) ? to_f32(qp[c]) : 0.0f;
+    qr[c] = (D == DMAX || c < D) ? to_f32(qp[c]) : 0.0f;
     acc[c] = 0.0f;
   }
+#pragma unroll
+  for (int c = 0; c < DMAX; ++c) qr[c] = live ? qr[c] : 0.0f;
   float m = -INFINITY, l = 0.0f;
 
   // Key range any row of this block can see.
@@ -71,39 +74,63 @@ __global__ __launch_bounds__(64) void generic_fwd_kernel(FwdParams p) {
     thg = p.term_h + ((b * p.Hq + h) * p.Tq + is) * gh;
     twg = p.term_w + ((b * p.Hq + h) * p.Tq + is) * gw;
   }
+  // Copies into LDS that issue 8 loads per lane before the first store (one
+  // memory round trip per batch): a lane's own row of n values to
+  // dst[e * 64], and a cooperative copy of n elements to dst[e].
+  constexpr int NB = 8;
+  auto copy_row = [&](float* dst, const float* src, int n) {
+    for (int e0 = 0; e0 < n; e0 += NB) {
+      float v[NB];
+#pragma unroll
+      for (int u = 0; u < NB; ++u) v[u] = e0 + u < n ? src[e0 + u] : 0.0f;
+#pragma unroll
+      for (int u = 0; u < NB; ++u)
+        if (e0 + u < n) dst[(e0 + u) * 64] = v[u];
+    }
+  };
+  auto copy_all = [&](float* dst, const TIN* src, int n) {
+    for (int e0 = 0; e0 < n; e0 += NB * 64) {
+      float v[NB];
+#pragma unroll
+      for (int u = 0; u < NB; ++u) {
+        const int e = e0 + 64 * u + lane;
+        v[u] = e < n ? to_f32(src[e]) : 0.0f;
+      }
+#pragma unroll
+      for (int u = 0; u < NB; ++u) {
+        const int e = e0 + 64 * u + lane;
+        if (e < n) dst[e] = v[u];
+      }
+    }
+  };
   if (rows_in_lds) {
     const int64_t is = live ? i : 0;
-    if (p.term_h) {                   // terms from the workspace
+    if (p.term_h) {                   // terms from the workspace: this lane's rows, one value per LDS row
       const float* th = p.term_h + ((b * p.Hq + h) * p.Tq + is) * gh;
       const float* tw = p.term_w + ((b * p.Hq + h) * p.Tq + is) * gw;
-#pragma unroll 4
-      for (int y = 0; y < gh; ++y) dyn[y * 64 + lane] = th[y];
-#pragma unroll 4
-      for (int x = 0; x < gw; ++x) dyn[(gh + x) * 64 + lane] = tw[x];
+      copy_row(dyn + lane, th, gh);
+      copy_row(dyn + gh * 64 + lane, tw, gw);
     } else {                          // terms formed here: term[i, y] = q_i . table[coord(i) - y + G - 1]
       float* tab = dyn + (gh + gw) * 64;
       const int nh = 2 * gh - 1, nw = 2 * gw - 1;
-#pragma unroll 8
-      for (int e = lane; e < (nh + nw) * D; e += 64) {
-        const int r = e / D, c = e % D;
-        tab[e] = r < nh ? to_f32(((const TIN*)p.rel_h)[r * D + c]) : to_f32(((const TIN*)p.rel_w)[(r - nh) * D + c]);
-      }
+      // [nh + nw][D]: rel_pos_h rows then rel_pos_w rows, both stored row-major
+      copy_all(tab, (const TIN*)p.rel_h, nh * D);
+      copy_all(tab + nh * D, (const TIN*)p.rel_w, nw * D);
       __syncthreads();
       const int ih = (int)(is / gw), iw = (int)(is % gw);
-      for (int y = 0; y < gh; ++y) {
-        const float* row = tab + (ih - y + gh - 1) * D;
+      auto dotrow = [&](const float* row) -> float {
         float d = 0.0f;
+        if (D == DMAX) {
 #pragma unroll
-        for (int c = 0; c < DMAX; ++c) d = (c < D) ? fmaf(qr[c], row[c], d) : d;
-        dyn[y * 64 + lane] = d;
-      }
-      for (int x = 0; x < gw; ++x) {
-        const float* row = tab + (nh + iw - x + gw - 1) * D;
-        float d = 0.0f;
+          for (int c = 0; c < DMAX; ++c) d = fmaf(qr[c], row[c], d);
+        } else {
 #pragma unroll
-        for (int c = 0; c < DMAX; ++c) d = (c < D) ? fmaf(qr[c], row[c], d) : d;
-        dyn[(gh + x) * 64 + lane] = d;
-      }
+          for (int c = 0; c < DMAX; ++c) d = (c < D) ? fmaf(qr[c], row[c], d) : d;
+        }
+        return d;
+      };
+      for (int y = 0; y < gh; ++y) dyn[y * 64 + lane] = dotrow(tab + (ih - y + gh - 1) * D);
+      for (int x = 0; x < gw; ++x) dyn[(gh + x) * 64 + lane] = dotrow(tab + (nh + iw - x + gw - 1) * D);
     }
   }
 
