@@ -162,7 +162,7 @@ __global__ __launch_bounds__(64 * NW, 1) void flash_split64w_kernel(FwdParams p)
   const int dk = cslot1 ? wave & 1 : (wave >> 1) & 1;
   const int dp = cslot1 ? 0 : wave & 1;
   const int dtbeg = dh ? nt0 : 0, dtend = dh ? nt : nt0;
-  const int64_t cbh = cslot1 ? bh0 + 1 : bh0;      // (batch, head) whose tiles this wave copies
+  const int64_t cbh = (cslot1 && two) ? bh0 + 1 : bh0;   // (batch, head) whose tiles this wave copies
   const int64_t chk = (cbh % p.Hq) / (p.Hq / p.Hkv);
   const char* kvbase = (const char*)((const E*)(dk ? p.v : p.k) + (cbh / p.Hq) * p.k_sb + chk * p.k_sh);
   const int rstride = (int)(p.k_st * 2);
