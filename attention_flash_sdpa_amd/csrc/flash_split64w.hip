@@ -151,16 +151,16 @@ __global__ __launch_bounds__(64 * NW, 1) void flash_split64w_kernel(FwdParams p)
   const int tbeg = hf ? nt0 : 0;
   const int tend = hf ? nt : nt0;
   const int niter = nt0;                        // half 0 has at least as many tiles
-  // Copies per tile step.  Head slot 0: waves 0..7 each copy one 2 KB part
-  // (dp) of the K or V (dk) tile of one key half (dh).  Head slot 1, in a
-  // workgroup holding two heads: waves 8..11 each copy a whole 4 KB tile
-  // (key half dh, tensor dk).  Key rows are addressed with 32-bit byte offsets
-  // (the launcher checks that the key range spans less than 2^31 bytes).
-  const bool cslot1 = wave >= 8;
-  const bool copier = !cslot1 || two;
-  const int dh = cslot1 ? (wave >> 1) & 1 : (wave >> 2) & 1;
-  const int dk = cslot1 ? wave & 1 : (wave >> 1) & 1;
-  const int dp = cslot1 ? 0 : wave & 1;
+  // Copies per tile step, each a whole 4 KB K or V (dk) tile of one key half
+  // (dh).  They go to the oldest waves of each SIMD (waves w, w + 4, w + 8
+  // share one), which otherwise wait longest at the step's barrier: waves
+  // 0..3 copy head slot 0, waves 4..7 head slot 1 in a workgroup holding two
+  // heads, waves 8..11 nothing.  Key rows are addressed with 32-bit byte
+  // offsets (the launcher checks that the key range spans less than 2^31
+  // bytes).
+  const bool cslot1 = wave >= 4;
+  const bool copier = wave < 4 || (wave < 8 && two);
+  const int dh = (wave >> 1) & 1, dk = wave & 1;
   const int dtbeg = dh ? nt0 : 0, dtend = dh ? nt : nt0;
   const int64_t cbh = (cslot1 && two) ? bh0 + 1 : bh0;   // (batch, head) whose tiles this wave copies
   const int64_t chk = (cbh % p.Hq) / (p.Hq / p.Hkv);
@@ -176,14 +176,13 @@ __global__ __launch_bounds__(64 * NW, 1) void flash_split64w_kernel(FwdParams p)
   int voff[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int L = 128 * dp + 64 * j + lane, row = L >> 3, pos = L & 7;
+    const int L = 64 * j + lane, row = L >> 3, pos = L & 7;
     voff[j] = row * rstride + ((pos ^ (dk ? vswz(row) : kswz(row))) << 4) - j * 1024;
   }
-  const int dst = cslot1 ? tile_off(1, dk, dh) : tile_off(0, dk, dh) + dp * 2048;   // byte offset in a parity object
-  // Copy role, fixed per wave: 0 none, 1 a 2 KB part (head slot 0), 2 a whole
-  // tile (head slot 1).  The main loop is instantiated per role, so no step
-  // branches on it.
-  const int role = !copier ? 0 : (cslot1 ? 2 : 1);
+  const int dst = tile_off(cslot1 ? 1 : 0, dk, dh);   // byte offset in a parity object
+  // Copy role, fixed per wave: 0 none, 1 a whole tile.  The main loop is
+  // instantiated per role, so no step branches on it.
+  const int role = copier ? 1 : 0;
   // Tile it of the copier's half into the parity-PAR object (GUARD: skip tiles
   // past the half's end).
   auto stage = [&](int it, auto par, auto rl, auto guard) {
@@ -198,19 +197,15 @@ __global__ __launch_bounds__(64 * NW, 1) void flash_split64w_kernel(FwdParams p)
     lds_void* d = (lds_void*)((PAR ? tp1 : tp0) + dst);     // one static destination object per call site
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, d, 16, voff[0], 0, 0, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, d, 16, voff[1], 0, 1024, 0);
-    if (ROLE == 2) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, d, 16, voff[2], 0, 2048, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, d, 16, voff[3], 0, 3072, 0);
-    }
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, d, 16, voff[2], 0, 2048, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, d, 16, voff[3], 0, 3072, 0);
   };
   using P0 = std::integral_constant<int, 0>;
   using P1 = std::integral_constant<int, 1>;
   using R1 = std::integral_constant<int, 1>;
-  using R2 = std::integral_constant<int, 2>;
   using G1 = std::true_type;
   // the first tiles travel during the set-up below
   if (role == 1) stage(0, P0{}, R1{}, G1{});
-  else if (role == 2) stage(0, P0{}, R2{}, G1{});
 
   const E* qp = (const E*)p.q + b * p.q_sb + h * p.q_sh;
   e8 qf[4];
@@ -466,7 +461,6 @@ __global__ __launch_bounds__(64 * NW, 1) void flash_split64w_kernel(FwdParams p)
     }
   };
   if (role == 1) main_loop(R1{});
-  else if (role == 2) main_loop(R2{});
   else main_loop(std::integral_constant<int, 0>{});
 
   // ---- merge the two key halves of each query block through LDS, three
