@@ -8,3 +8,7 @@ from .sdpa_oracle import (  # noqa: F401
     to_bhsd, from_bhsd, kv_head_of, relpos_terms, relpos_bias, mask_bias,
     softmax_rows, sdpa, sdpa_rows,
 )
+from .sdpa_train_oracle import (  # noqa: F401
+    philox4x32_10, dropout_threshold, dropout_keep, pack_keep_words, unpack_keep_words,
+    sdpa_train_fwd, attention_weights, sdpa_bwd,
+)
