@@ -26,7 +26,8 @@ import threading
 import torch
 
 __all__ = ["load", "lib_path", "sdpa", "sdpa_relpos", "relpos_terms", "workspace_size", "relpos_fused",
-           "set_tuning", "SdpaError", "F32", "BF16", "F16", "BSHD", "BHSD"]
+           "set_tuning", "dropout_mask", "sdpa_backward", "attention_weights", "SdpaError", "F32", "BF16", "F16",
+           "BSHD", "BHSD"]
 
 F32, BF16, F16 = 0, 1, 2
 BSHD, BHSD = 0, 1
@@ -87,6 +88,19 @@ def load():
         lib.sdpa_set_tuning.argtypes = [ctypes.c_char_p, _I64]
         lib.sdpa_relpos_fused.restype = _I32
         lib.sdpa_relpos_fused.argtypes = [_I32, _I64, _I64, _I64]
+        lib.sdpa_dropout_mask.restype = _I32
+        lib.sdpa_dropout_mask.argtypes = [ctypes.c_uint64, ctypes.c_uint32, _F] + [_I64] * 4 + [_P, _P]
+        lib.sdpa_fwd_dropout.restype = _I32
+        lib.sdpa_fwd_dropout.argtypes = [_P, _P, _P, _P, _I32, _I32, _I32] + [_I64] * 6 + \
+            [_F, ctypes.POINTER(_Mask), _P, _F, _P, _P, ctypes.c_size_t, _P]
+        lib.sdpa_bwd_workspace_size.restype = ctypes.c_size_t
+        lib.sdpa_bwd_workspace_size.argtypes = [_I64] * 3
+        lib.sdpa_bwd.restype = _I32
+        lib.sdpa_bwd.argtypes = [_P] * 9 + [_I32] * 4 + [_I64] * 6 + \
+            [_F, ctypes.POINTER(_Mask), _P, _F, _P, ctypes.c_size_t, _P]
+        lib.sdpa_attention_weights.restype = _I32
+        lib.sdpa_attention_weights.argtypes = [_P, _P, _I32, _I32] + [_I64] * 6 + \
+            [_F, ctypes.POINTER(_Mask), _P, _P, _F, _P, _P]
         _LIB = lib
         return lib
 
@@ -180,14 +194,27 @@ def _mask_struct(mask, B, Hq, Tq, Tkv, keep):
     return m
 
 
+def _dropout_args(dropout, B, Hq, Tq, Tkv):
+    """(keep pointer, rate) from {"keep": int32 words [B, Hq, Tq, ceil(Tkv/32)], "rate": r} or None."""
+    if dropout is None:
+        return None, 0.0
+    keep = dropout["keep"]
+    if not keep.is_cuda or keep.dtype != torch.int32 or not keep.is_contiguous():
+        raise ValueError("dropout keep bits must be a contiguous int32 GPU tensor (from dropout_mask)")
+    if keep.numel() != B * Hq * Tq * ((Tkv + 31) // 32):
+        raise ValueError("dropout keep bits have the wrong size")
+    return _ptr(keep), float(dropout["rate"])
+
+
 def sdpa(q, k, v, *, layout="bhsd", scale=None, mask=None, out_dtype=None, return_lse=False,
-         stream=None, out=None):
+         stream=None, out=None, dropout=None):
     """Fused attention on the GPU.
 
     q: [B, Hq, Tq, D] (bhsd) or [B, Tq, Hq, D] (bshd); k, v with Hkv heads.
     mask: None | {"kind": "causal", "offset": d} | {"kind": "sliding", "window": w, "offset": d}
           | {"kind": "additive", "data": tensor} | {"kind": "bool", "data": bool tensor}
     out_dtype: None (= q.dtype) or torch.float32.
+    dropout: None | {"keep": keep bits from dropout_mask, "rate": r} (attention dropout).
     """
     lib = load()
     _need_gpu(q, k, v)
@@ -202,10 +229,70 @@ def sdpa(q, k, v, *, layout="bhsd", scale=None, mask=None, out_dtype=None, retur
     ws_n = lib.sdpa_workspace_size(B, Hq, Hkv, Tq, Tkv, D, 0, 0, 0)
     ws = torch.empty(ws_n, dtype=torch.uint8, device=q.device) if ws_n else None
     sc = float("nan") if scale is None else float(scale)
+    if dropout is not None:
+        kp, rate = _dropout_args(dropout, B, Hq, Tq, Tkv)
+        st = lib.sdpa_fwd_dropout(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _DTYPE[q.dtype], _DTYPE[odt],
+                                  _LAYOUT[layout], B, Hq, Hkv, Tq, Tkv, D, sc, ctypes.byref(ms), kp, rate,
+                                  _ptr(lse), None, 0, _stream(stream))
+        _check(st, "sdpa_fwd_dropout")
+        return (o, lse) if return_lse else o
     st = lib.sdpa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _DTYPE[q.dtype], _DTYPE[odt], _LAYOUT[layout],
                       B, Hq, Hkv, Tq, Tkv, D, sc, ctypes.byref(ms), _ptr(lse), _ptr(ws), ws_n, _stream(stream))
     _check(st, "sdpa_fwd")
     return (o, lse) if return_lse else o
+
+
+def dropout_mask(seed, step, rate, B, Hq, Tq, Tkv, *, device="cuda", stream=None):
+    """Dropout keep bits [B, Hq, Tq, ceil(Tkv / 32)] as int32 words (Philox4x32-10 of (seed, step))."""
+    lib = load()
+    keep = torch.empty((B, Hq, Tq, (Tkv + 31) // 32), dtype=torch.int32, device=device)
+    st = lib.sdpa_dropout_mask(int(seed) & (2**64 - 1), int(step) & 0xFFFFFFFF, float(rate), B, Hq, Tq, Tkv,
+                               _ptr(keep), _stream(stream))
+    _check(st, "sdpa_dropout_mask")
+    return keep
+
+
+def sdpa_backward(q, k, v, o, dout, lse, *, layout="bhsd", scale=None, mask=None, dropout=None,
+                  grad_dtype=None, stream=None):
+    """(dq, dk, dv) of attention for the upstream gradient dout (o and lse from the forward call)."""
+    lib = load()
+    _need_gpu(q, k, v, o, dout, lse)
+    if q.dtype not in _DTYPE or k.dtype != q.dtype or v.dtype != q.dtype or dout.dtype != q.dtype:
+        raise ValueError("q, k, v and dout must share one dtype")
+    if o.dtype not in (q.dtype, torch.float32) or lse.dtype != torch.float32:
+        raise ValueError("o must be in q's dtype or float32, lse float32")
+    B, Hq, Hkv, Tq, Tkv, D = _dims(q, k, layout)
+    gdt = q.dtype if grad_dtype is None else grad_dtype
+    dq = torch.empty(q.shape, dtype=gdt, device=q.device)
+    dk = torch.empty(k.shape, dtype=gdt, device=q.device)
+    dv = torch.empty(v.shape, dtype=gdt, device=q.device)
+    keep_refs = []
+    ms = _mask_struct(mask, B, Hq, Tq, Tkv, keep_refs)
+    kp, rate = _dropout_args(dropout, B, Hq, Tq, Tkv)
+    ws_n = lib.sdpa_bwd_workspace_size(B, Hq, Tq)
+    ws = torch.empty(ws_n, dtype=torch.uint8, device=q.device)
+    sc = float("nan") if scale is None else float(scale)
+    st = lib.sdpa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
+                      _DTYPE[q.dtype], _DTYPE[o.dtype], _DTYPE[gdt], _LAYOUT[layout], B, Hq, Hkv, Tq, Tkv, D, sc,
+                      ctypes.byref(ms), kp, rate, _ptr(ws), ws_n, _stream(stream))
+    _check(st, "sdpa_bwd")
+    return dq, dk, dv
+
+
+def attention_weights(q, k, lse, *, layout="bhsd", scale=None, mask=None, dropout=None, stream=None):
+    """[B, Hq, Tq, Tkv] fp32 weights that multiply V (lse from the forward call on the same inputs)."""
+    lib = load()
+    _need_gpu(q, k, lse)
+    B, Hq, Hkv, Tq, Tkv, D = _dims(q, k, layout)
+    w = torch.empty((B, Hq, Tq, Tkv), dtype=torch.float32, device=q.device)
+    keep_refs = []
+    ms = _mask_struct(mask, B, Hq, Tq, Tkv, keep_refs)
+    kp, rate = _dropout_args(dropout, B, Hq, Tq, Tkv)
+    sc = float("nan") if scale is None else float(scale)
+    st = lib.sdpa_attention_weights(_ptr(q), _ptr(k), _DTYPE[q.dtype], _LAYOUT[layout], B, Hq, Hkv, Tq, Tkv, D,
+                                    sc, ctypes.byref(ms), _ptr(lse), kp, rate, _ptr(w), _stream(stream))
+    _check(st, "sdpa_attention_weights")
+    return w
 
 
 def relpos_terms(q, rel_pos_h, rel_pos_w, grid, *, layout="bhsd", stream=None):

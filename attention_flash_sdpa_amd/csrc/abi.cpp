@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <cstdarg>
@@ -107,6 +108,52 @@ sdpa::FwdParams base_params(const void* q, const void* k, const void* v, void* o
   return p;
 }
 
+// Mask argument -> bias fields of the kernel parameters (FwdParams or BwdParams).
+template <class P>
+int apply_mask(const sdpa_mask* mask, P& p) {
+  if (!mask || mask->kind == SDPA_MASK_NONE) return SDPA_OK;
+  switch (mask->kind) {
+    case SDPA_MASK_CAUSAL:
+      p.bias = sdpa::BIAS_CAUSAL;
+      p.offset = mask->offset;
+      return SDPA_OK;
+    case SDPA_MASK_SLIDING:
+      if (mask->window < 1) return fail(SDPA_ERR_INVALID, "sliding window must be >= 1 (got %lld)", (long long)mask->window);
+      p.bias = sdpa::BIAS_SLIDING;
+      p.offset = mask->offset;
+      p.window = mask->window;
+      return SDPA_OK;
+    case SDPA_MASK_ADDITIVE:
+    case SDPA_MASK_BOOL:
+      if (!mask->data) return fail(SDPA_ERR_INVALID, "tensor mask needs a data pointer");
+      if (mask->kind == SDPA_MASK_ADDITIVE && mask->data_dtype != SDPA_F32 && mask->data_dtype != SDPA_BF16)
+        return fail(SDPA_ERR_INVALID, "additive mask dtype must be SDPA_F32 or SDPA_BF16");
+      for (int a = 0; a < 4; ++a)
+        if (mask->stride[a] < 0) return fail(SDPA_ERR_INVALID, "mask strides must be >= 0");
+      p.bias = mask->kind == SDPA_MASK_ADDITIVE ? sdpa::BIAS_ADDITIVE : sdpa::BIAS_BOOL;
+      p.mdata = mask->data;
+      p.mdtype = mask->data_dtype;
+      for (int a = 0; a < 4; ++a) p.ms[a] = mask->stride[a];
+      return SDPA_OK;
+    default:
+      return fail(SDPA_ERR_INVALID, "unknown mask kind %d", mask->kind);
+  }
+}
+
+// Dropout rate -> (16-bit keep threshold, factor of a kept weight): keep iff
+// the element's 16-bit uniform >= thresh, thresh = floor(rate * 65536 + 0.5)
+// clamped to 65535, so the kept fraction is (65536 - thresh) / 65536 and the
+// factor 65536 / (65536 - thresh) makes the dropped weights unbiased.
+int dropout_plan(float rate, uint32_t* thresh, float* kscale) {
+  if (!(rate >= 0.0f && rate < 1.0f)) return fail(SDPA_ERR_INVALID, "dropout rate must be in [0, 1) (got %g)", (double)rate);
+  const double t = std::floor((double)rate * 65536.0 + 0.5);
+  *thresh = (uint32_t)std::min(65535.0, t);
+  *kscale = (float)(65536.0 / (65536.0 - (double)*thresh));
+  return SDPA_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
 enum Route { R_GENERIC, R_D16, R_WINDOW, R_SPLIT64W, R_SPLIT64, R_TILED, R_MFMA };
 
 // The kernel a call runs on: the first route whose conditions hold.
@@ -114,6 +161,8 @@ Route route_of(const sdpa::FwdParams& p) {
   // The MFMA kernels take each row's running max on scores already multiplied
   // by scale, which needs scale > 0; other scales run on the generic kernel.
   if (!(p.scale > 0.0f && std::isfinite(p.scale))) return R_GENERIC;
+  // Dropout runs on the general MFMA kernel where it applies, else on the generic one.
+  if (p.keep) return sdpa::flash_mfma_supports(p) ? R_MFMA : R_GENERIC;
   if (sdpa::d16_supports(p)) return R_D16;
   if (sdpa::window_supports(p)) return R_WINDOW;
   const int64_t wide = g_split64w.load();     // 0 off, 1 where the shape fills the CUs, 2 wherever supported
@@ -179,34 +228,8 @@ int sdpa_fwd(const void* q, const void* k, const void* v, void* o, int dtype, in
   st = check_dtypes(dtype, out_dtype, layout, D);
   if (st) return st;
   sdpa::FwdParams p = base_params(q, k, v, o, dtype, out_dtype, layout, B, Hq, Hkv, Tq, Tkv, D, scale, lse);
-  if (mask && mask->kind != SDPA_MASK_NONE) {
-    switch (mask->kind) {
-      case SDPA_MASK_CAUSAL:
-        p.bias = sdpa::BIAS_CAUSAL;
-        p.offset = mask->offset;
-        break;
-      case SDPA_MASK_SLIDING:
-        if (mask->window < 1) return fail(SDPA_ERR_INVALID, "sliding window must be >= 1 (got %lld)", (long long)mask->window);
-        p.bias = sdpa::BIAS_SLIDING;
-        p.offset = mask->offset;
-        p.window = mask->window;
-        break;
-      case SDPA_MASK_ADDITIVE:
-      case SDPA_MASK_BOOL:
-        if (!mask->data) return fail(SDPA_ERR_INVALID, "tensor mask needs a data pointer");
-        if (mask->kind == SDPA_MASK_ADDITIVE && mask->data_dtype != SDPA_F32 && mask->data_dtype != SDPA_BF16)
-          return fail(SDPA_ERR_INVALID, "additive mask dtype must be SDPA_F32 or SDPA_BF16");
-        for (int a = 0; a < 4; ++a)
-          if (mask->stride[a] < 0) return fail(SDPA_ERR_INVALID, "mask strides must be >= 0");
-        p.bias = mask->kind == SDPA_MASK_ADDITIVE ? sdpa::BIAS_ADDITIVE : sdpa::BIAS_BOOL;
-        p.mdata = mask->data;
-        p.mdtype = mask->data_dtype;
-        for (int a = 0; a < 4; ++a) p.ms[a] = mask->stride[a];
-        break;
-      default:
-        return fail(SDPA_ERR_INVALID, "unknown mask kind %d", mask->kind);
-    }
-  }
+  st = apply_mask(mask, p);
+  if (st) return st;
   p.num_splits = plan_splits(B, Hq, Tq, Tkv, D, dtype);
   const size_t need = split_bytes(p.num_splits, B, Hq, Tq, D);
   if (need) {
@@ -290,6 +313,131 @@ int sdpa_relpos_fused(int dtype, int64_t D, int64_t grid_h, int64_t grid_w) {
   p.num_splits = 1;
   p.bias = sdpa::BIAS_RELPOS;
   return (g_relpos_fused.load() && grid_h > 0 && grid_w > 0 && relpos_fused_ok(p)) ? 1 : 0;
+}
+
+int sdpa_dropout_mask(uint64_t seed, uint32_t step, float rate, int64_t B, int64_t Hq, int64_t Tq, int64_t Tkv,
+                      uint32_t* keep, void* stream) {
+  g_last_error.clear();
+  if (!keep) return fail(SDPA_ERR_INVALID, "keep must be non-null");
+  if (B <= 0 || Hq <= 0 || Tq <= 0 || Tkv <= 0) return fail(SDPA_ERR_INVALID, "all sizes must be positive");
+  if (Tq > INT32_MAX || Tkv > INT32_MAX || B * Hq > INT32_MAX)
+    return fail(SDPA_ERR_UNSUPPORTED, "sizes beyond the generator's 32-bit counter words");
+  sdpa::DropoutParams d;
+  float kscale;
+  int st = dropout_plan(rate, &d.thresh, &kscale);
+  if (st) return st;
+  d.seed = seed;
+  d.step = step;
+  d.B = B; d.Hq = Hq; d.Tq = Tq; d.Tkv = Tkv;
+  d.keep_words = (Tkv + 31) / 32;
+  d.keep = keep;
+  hipError_t e = sdpa::launch_dropout_mask(d, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(SDPA_ERR_HIP, "dropout mask launch failed: %s", hipGetErrorString(e));
+  g_last_kernel = "dropout_mask_kernel";
+  return SDPA_OK;
+}
+
+int sdpa_fwd_dropout(const void* q, const void* k, const void* v, void* o, int dtype, int out_dtype, int layout,
+                     int64_t B, int64_t Hq, int64_t Hkv, int64_t Tq, int64_t Tkv, int64_t D, float scale,
+                     const sdpa_mask* mask, const uint32_t* keep, float rate, float* lse, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  if (!q || !k || !v || !o || !keep) return fail(SDPA_ERR_INVALID, "q, k, v, o and keep must be non-null");
+  int st = check_sizes(B, Hq, Hkv, Tq, Tkv, D);
+  if (st) return st;
+  st = check_dtypes(dtype, out_dtype, layout, D);
+  if (st) return st;
+  uint32_t thresh;
+  float kscale;
+  st = dropout_plan(rate, &thresh, &kscale);
+  if (st) return st;
+  sdpa::FwdParams p = base_params(q, k, v, o, dtype, out_dtype, layout, B, Hq, Hkv, Tq, Tkv, D, scale, lse);
+  st = apply_mask(mask, p);
+  if (st) return st;
+  p.keep = keep;
+  p.keep_words = (Tkv + 31) / 32;
+  p.keep_scale = kscale;
+  (void)workspace;
+  (void)workspace_bytes;
+  return launch(p, (hipStream_t)stream);
+}
+
+size_t sdpa_bwd_workspace_size(int64_t B, int64_t Hq, int64_t Tq) {
+  if (B <= 0 || Hq <= 0 || Tq <= 0) return (size_t)-1;
+  return align256((size_t)B * Hq * Tq * 4);
+}
+
+int sdpa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+             void* dq, void* dk, void* dv, int dtype, int o_dtype, int grad_dtype, int layout,
+             int64_t B, int64_t Hq, int64_t Hkv, int64_t Tq, int64_t Tkv, int64_t D, float scale,
+             const sdpa_mask* mask, const uint32_t* keep, float rate, void* workspace, size_t workspace_bytes,
+             void* stream) {
+  g_last_error.clear();
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv)
+    return fail(SDPA_ERR_INVALID, "q, k, v, o, dout, lse, dq, dk and dv must be non-null");
+  int st = check_sizes(B, Hq, Hkv, Tq, Tkv, D);
+  if (st) return st;
+  st = check_dtypes(dtype, o_dtype, layout, D);
+  if (st) return st;
+  if (grad_dtype != dtype && grad_dtype != SDPA_F32) return fail(SDPA_ERR_INVALID, "grad_dtype must equal dtype or be SDPA_F32");
+  sdpa::BwdParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.q = q; p.k = k; p.v = v; p.o = o; p.dout = dout; p.lse = lse; p.dq = dq; p.dk = dk; p.dv = dv;
+  p.dtype = dtype; p.o_dtype = o_dtype; p.grad_dtype = grad_dtype;
+  p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.Tq = Tq; p.Tkv = Tkv; p.D = D;
+  set_strides(layout, Hq, Tq, D, &p.q_sb, &p.q_sh, &p.q_st);
+  set_strides(layout, Hkv, Tkv, D, &p.k_sb, &p.k_sh, &p.k_st);
+  p.scale = std::isnan(scale) ? (float)(1.0 / std::sqrt((double)D)) : scale;
+  if (!std::isfinite(p.scale)) return fail(SDPA_ERR_INVALID, "scale must be finite");
+  st = apply_mask(mask, p);
+  if (st) return st;
+  if (keep) {
+    uint32_t thresh;
+    st = dropout_plan(rate, &thresh, &p.keep_scale);
+    if (st) return st;
+    p.keep = keep;
+    p.keep_words = (Tkv + 31) / 32;
+  }
+  if (!sdpa::bwd_supports(p))
+    return fail(SDPA_ERR_UNSUPPORTED, "the backward pass is built for bf16 / fp16 inputs with head_dim 32, 64 or 128");
+  const void* ptrs[] = {q, k, v, o, dout, dq, dk, dv};
+  for (const void* x : ptrs)
+    if (!aligned16(x)) return fail(SDPA_ERR_UNSUPPORTED, "the backward pass needs 16-byte aligned tensors");
+  const size_t need = align256((size_t)B * Hq * Tq * 4);
+  if (!workspace || workspace_bytes < need)
+    return fail(SDPA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : (size_t)0);
+  p.delta = (float*)workspace;
+  hipError_t e = sdpa::launch_bwd(p, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(SDPA_ERR_HIP, "backward launch failed: %s", hipGetErrorString(e));
+  g_last_kernel = "bwd_dkdv_kernel";
+  return SDPA_OK;
+}
+
+int sdpa_attention_weights(const void* q, const void* k, int dtype, int layout, int64_t B, int64_t Hq, int64_t Hkv,
+                           int64_t Tq, int64_t Tkv, int64_t D, float scale, const sdpa_mask* mask, const float* lse,
+                           const uint32_t* keep, float rate, float* weights, void* stream) {
+  g_last_error.clear();
+  if (!q || !k || !lse || !weights) return fail(SDPA_ERR_INVALID, "q, k, lse and weights must be non-null");
+  int st = check_sizes(B, Hq, Hkv, Tq, Tkv, D);
+  if (st) return st;
+  st = check_dtypes(dtype, dtype, layout, D);
+  if (st) return st;
+  if (B * Hq > 65535 || (Tq + 63) / 64 > 65535) return fail(SDPA_ERR_UNSUPPORTED, "sizes beyond the launch grid limits");
+  sdpa::FwdParams p = base_params(q, k, nullptr, nullptr, dtype, dtype, layout, B, Hq, Hkv, Tq, Tkv, D, scale,
+                                  const_cast<float*>(lse));
+  st = apply_mask(mask, p);
+  if (st) return st;
+  if (keep) {
+    uint32_t thresh;
+    st = dropout_plan(rate, &thresh, &p.keep_scale);
+    if (st) return st;
+    p.keep = keep;
+    p.keep_words = (Tkv + 31) / 32;
+  }
+  hipError_t e = sdpa::launch_attn_weights(p, weights, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(SDPA_ERR_HIP, "attention weights launch failed: %s", hipGetErrorString(e));
+  g_last_kernel = "attn_weights_kernel";
+  return SDPA_OK;
 }
 
 const char* sdpa_status_string(int status) {

@@ -1,0 +1,74 @@
+// Attention-dropout keep bits from a counter-based generator.
+//
+// [Axon PR 650] "Axon.Layers.scaled_dot_product_attention/4", description:
+// `:dropout_rate` drops attention probabilities in :train mode, and the graph
+// layer threads a PRNG key from step to step.  Here the key is a 64-bit seed
+// and the step is a 32-bit counter word, fed to Philox4x32-10 (Salmon,
+// Moraes, Dror and Shaw, "Parallel random numbers: as easy as 1, 2, 3",
+// SC 2011): score element (b, h, i, j) takes the 16-bit half j % 8 of the
+// block Philox(counter = (j / 8, i, b * Hq + h, step), key = seed), low half
+// of word (j % 8) / 2 first, and is kept iff that half >= thresh.
+//
+// Output: one 32-bit word per 32 keys of a score row, [B, Hq, Tq, ceil(Tkv / 32)],
+// bit j % 32 of word j / 32; bits past Tkv are zero.  Every thread writes one
+// word (four Philox blocks), so the stores are coalesced along the row.
+#include "common.h"
+
+namespace sdpa {
+namespace {
+
+// Philox4x32 round multipliers and Weyl key increments (Salmon et al., SC 2011).
+constexpr uint32_t kPhiloxM0 = 0xD2511F53u, kPhiloxM1 = 0xCD9E8D57u;
+constexpr uint32_t kPhiloxW0 = 0x9E3779B9u, kPhiloxW1 = 0xBB67AE85u;
+
+__device__ __forceinline__ void philox4x32_10(uint32_t c[4], uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r) {
+      k0 += kPhiloxW0;
+      k1 += kPhiloxW1;
+    }
+    const uint32_t lo0 = kPhiloxM0 * c[0], hi0 = __umulhi(kPhiloxM0, c[0]);
+    const uint32_t lo1 = kPhiloxM1 * c[2], hi1 = __umulhi(kPhiloxM1, c[2]);
+    const uint32_t n0 = hi1 ^ c[1] ^ k0, n2 = hi0 ^ c[3] ^ k1;
+    c[0] = n0;
+    c[1] = lo1;
+    c[2] = n2;
+    c[3] = lo0;
+  }
+}
+
+__global__ __launch_bounds__(256) void dropout_mask_kernel(DropoutParams p, int64_t total) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= total) return;
+  const int64_t row = idx / p.keep_words;
+  const int64_t w = idx % p.keep_words;
+  const uint32_t bh = (uint32_t)(row / p.Tq), i = (uint32_t)(row % p.Tq);
+  const uint32_t k0 = (uint32_t)p.seed, k1 = (uint32_t)(p.seed >> 32);
+  uint32_t word = 0;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int64_t j0 = 32 * w + 8 * c;          // first key of this Philox block
+    uint32_t x[4] = {(uint32_t)(j0 / 8), i, bh, p.step};
+    philox4x32_10(x, k0, k1);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t u = (e & 1) ? (x[e >> 1] >> 16) : (x[e >> 1] & 0xFFFFu);
+      const bool kept = (u >= p.thresh) && (j0 + e < p.Tkv);
+      word |= (uint32_t)kept << (8 * c + e);
+    }
+  }
+  p.keep[idx] = word;
+}
+
+}  // namespace
+
+hipError_t launch_dropout_mask(const DropoutParams& p, hipStream_t s) {
+  const int64_t total = p.B * p.Hq * p.Tq * p.keep_words;
+  const int64_t blocks = (total + 255) / 256;
+  if (blocks > INT32_MAX) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(dropout_mask_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p, total);
+  return hipGetLastError();
+}
+
+}  // namespace sdpa

@@ -1,0 +1,597 @@
+// Backward of fused attention on gfx950 matrix cores (MFMA 32x32x16, bf16 / fp16).
+//
+// For O = (W * Z) . V with W = softmax(scale * Q.K^T + B) and Z the dropout
+// factor ([Axon PR 650] "Axon.Layers.scaled_dot_product_attention/4",
+// description: attention-probability dropout in :train mode), the gradients
+// of a loss with upstream gradient dO are
+//   dV  = (W * Z)^T . dO
+//   dW  = (dO . V^T) * Z
+//   dS  = W * (dW - delta),   delta_i = sum_j W_ij dW_ij = dO_i . O_i
+//   dQ  = scale * dS . K,     dK = scale * dS^T . Q
+// The weights are rebuilt tile by tile from Q, K and the forward pass's row
+// log-sum-exp (W = exp(s - lse)), so no T_q x T_kv array is stored.
+//
+// Three launches, none with atomics (the result is bitwise deterministic):
+//   delta: rowsum(dO * O) per query row;
+//   dK/dV: one workgroup per 128 keys (4 waves x 32 keys, K and V of the wave
+//          held in registers), looping over the query heads that share the KV
+//          head and over 64-query tiles of Q and dO staged through LDS;
+//   dQ:    one workgroup per 128 query rows (4 waves x 32 rows, Q and dO in
+//          registers), looping over 64-key tiles of K and V staged through LDS.
+//
+// Matrix-core layouts (32x32x16: A lane l holds row l % 32, k = 8 (l / 32) .. +7;
+// B lane l holds column l % 32, same k; D lane l holds column l % 32, rows
+// 8 (r / 4) + 4 (l / 32) + r % 4 for r = 0..15):
+//   dK/dV: S[q, key] = Q . K^T and dW[q, key] = dO . V^T put one key per lane,
+//          16 queries in registers.  Those registers are directly the B operand
+//          of dV^T[d, key] += dO^T . (W*Z) and dK^T[d, key] += Q^T . dS over a
+//          16-query chunk, the k index running over queries in the order the
+//          D layout holds them; dO^T and Q^T come from the row-major LDS tiles
+//          through the transposing LDS read (ds_read_b64_tr_b16), which reads
+//          rows in exactly that order.
+//   dQ:    S^T[key, q] = K . Q^T and dW^T = V . dO^T put one query per lane;
+//          dQ^T[d, q] += K^T . dS^T with K^T from the K tile by transposing reads.
+// Q, dO (dK/dV) and K (dQ) tiles are read both by 16-byte rows and by
+// transposing reads, so their 16-byte chunks are XOR-swizzled with a pattern
+// that keeps both kinds of access spread over the LDS banks.
+#include "common.h"
+#include "elem16.h"
+
+namespace sdpa {
+namespace {
+
+typedef __attribute__((address_space(3))) char lds_char;
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+constexpr float kLog2e = 1.4426950408889634f;
+
+enum BMode { B_NONE = 0, B_INDEX = 1, B_TENSOR = 2 };
+
+template <int D>
+struct BCfg {
+  static constexpr int PITCH = D * 2;   // bytes per LDS row (unpadded)
+  static constexpr int CH = D / 8;      // 16-byte chunks per row
+  static constexpr int QC = D / 16;     // k-chunks of a contraction over head_dim
+  static constexpr int DB = D / 32;     // 32-wide blocks of head_dim
+  // Chunk c of row r sits at chunk position c ^ swz(r).  16 consecutive rows
+  // read at one chunk index hit 16 distinct 16-byte bank groups, and the 4
+  // consecutive rows of a transposing read (32 contiguous bytes each) land in
+  // 4 distinct 32-byte bank groups.
+  static __device__ __forceinline__ int swz(int r) {
+    if (D == 32) return (r >> 2) & 3;
+    if (D == 64) return (((r >> 1) & 3) << 1) | ((r >> 3) & 1);
+    return ((r & 7) << 1) | ((r >> 3) & 1);
+  }
+};
+
+template <typename E>
+using V8 = typename Vec16<E>::x8;
+
+template <typename E, int D>
+__device__ __forceinline__ V8<E> ld_row(const lds_char* t, int row, int c, int g) {
+  using C = BCfg<D>;
+  return *(const __attribute__((address_space(3))) V8<E>*)(t + row * C::PITCH + (((2 * c + g) ^ C::swz(row)) << 4));
+}
+
+// A-operand fragment of the transposed tile: lane l gets column colbase + l % 32
+// of rows rowbase + 4 (l / 32) + {0..3} and rowbase + 8 + 4 (l / 32) + {0..3}.
+template <typename E, int D>
+__device__ __forceinline__ V8<E> ld_tr(const lds_char* t, int rowbase, int colbase, int lane) {
+  using C = BCfg<D>;
+  const int j = lane & 15, dh = (lane >> 4) & 1, gg = lane >> 5;
+  const int col = colbase + 16 * dh + 4 * (j & 3);
+  const int r0 = rowbase + 4 * gg + (j >> 2), r1 = r0 + 8;
+  const int chunk = col >> 3, within = (col & 7) * 2;
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(t + r0 * C::PITCH + ((chunk ^ C::swz(r0)) << 4) + within));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(t + r1 * C::PITCH + ((chunk ^ C::swz(r1)) << 4) + within));
+  const s16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(V8<E>, a);
+}
+
+template <typename E>
+__device__ __forceinline__ V8<E> pack8(const float* x) {
+  const f32x8 v = {x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]};
+  return __builtin_convertvector(v, V8<E>);
+}
+
+template <typename T>
+__device__ __forceinline__ T lds_load(const lds_char* p) {
+  return *(const __attribute__((address_space(3))) T*)p;
+}
+template <typename T>
+__device__ __forceinline__ void lds_store(lds_char* p, T v) {
+  *(__attribute__((address_space(3))) T*)p = v;
+}
+
+// Workgroups are dealt to the 8 XCDs round-robin by linear id; renumber them so
+// each XCD takes a contiguous range of (batch, head, block) and keeps those
+// heads' tensors in its own L2.
+__device__ __forceinline__ void xcd_block(int64_t& bx, int64_t& by, int64_t& bz) {
+  const int64_t nblk = (int64_t)gridDim.x * gridDim.y * gridDim.z;
+  const int64_t lin = blockIdx.x + (int64_t)gridDim.x * (blockIdx.y + (int64_t)gridDim.y * blockIdx.z);
+  const int64_t per = nblk / 8, rem = nblk % 8, xcd = lin % 8;
+  const int64_t lid = xcd * per + min(xcd, rem) + lin / 8;
+  bx = lid % gridDim.x;
+  by = (lid / gridDim.x) % gridDim.y;
+  bz = lid / ((int64_t)gridDim.x * gridDim.y);
+}
+
+__device__ __forceinline__ float mask_value(const BwdParams& p, int64_t b, int64_t h, int64_t i, int64_t j) {
+  const int64_t off = b * p.ms[0] + h * p.ms[1] + i * p.ms[2] + j * p.ms[3];
+  if (p.bias == BIAS_BOOL) return ((const uint8_t*)p.mdata)[off] ? 0.0f : -INFINITY;
+  if (p.mdtype == 0) return ((const float*)p.mdata)[off];
+  return (float)((const __bf16*)p.mdata)[off];
+}
+
+// lse in the log2 domain; a row with no allowed key (lse = -inf) or past the
+// end gets +inf so that every weight of it is exp2(-inf) = 0.
+__device__ __forceinline__ float lse2_of(const BwdParams& p, int64_t row, bool valid) {
+  if (!valid) return INFINITY;
+  const float l = p.lse[row];
+  return l == -INFINITY ? INFINITY : l * kLog2e;
+}
+
+template <typename G>
+__device__ __forceinline__ void store4(G* dst, const float* v, float s) {
+  if constexpr (sizeof(G) == 4) {
+    *(f32x4*)dst = (f32x4){v[0] * s, v[1] * s, v[2] * s, v[3] * s};
+  } else {
+    typedef G g4 __attribute__((ext_vector_type(4)));
+    *(g4*)dst = (g4){(G)(v[0] * s), (G)(v[1] * s), (G)(v[2] * s), (G)(v[3] * s)};
+  }
+}
+
+// ------------------------------------------------------------------ delta --
+template <typename E, typename EO, int D>
+__global__ __launch_bounds__(256) void bwd_delta_kernel(BwdParams p, int64_t rows) {
+  constexpr int CH = D / 8;                // threads per row, 8 elements each
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t row = gid / CH;
+  const int c = (int)(gid % CH);
+  float acc = 0.0f;
+  if (row < rows) {
+    const int64_t bh = row / p.Tq, i = row % p.Tq, b = bh / p.Hq, h = bh % p.Hq;
+    const int64_t off = b * p.q_sb + h * p.q_sh + i * p.q_st + 8 * c;
+    const V8<E> dv = *(const V8<E>*)((const E*)p.dout + off);
+    float ov[8];
+    if constexpr (sizeof(EO) == 4) {
+      const f32x4 a = *(const f32x4*)((const float*)p.o + off);
+      const f32x4 bq = *(const f32x4*)((const float*)p.o + off + 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        ov[e] = a[e];
+        ov[4 + e] = bq[e];
+      }
+    } else {
+      const V8<E> o8 = *(const V8<E>*)((const E*)p.o + off);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ov[e] = (float)o8[e];
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc = fmaf((float)dv[e], ov[e], acc);
+  }
+#pragma unroll
+  for (int m = 1; m < CH; m <<= 1) acc += __shfl_xor(acc, m);
+  if (row < rows && c == 0) p.delta[row] = acc;
+}
+
+// ------------------------------------------------------------------ dK / dV --
+template <typename E, int D, int MODE, bool DROP, typename G>
+__global__ __launch_bounds__(256, (D == 128 ? 1 : 2)) void bwd_dkdv_kernel(BwdParams p) {
+  using C = BCfg<D>;
+  constexpr int BQ = 64;                           // queries per staged tile
+  constexpr int TQ = BQ * C::PITCH;                // bytes of one Q or dO tile
+  constexpr int NLD = BQ * C::CH / 256;            // 16-byte pieces per thread per tile
+  constexpr int SOFF = 4 * TQ;                     // [buf][lse2 | delta][BQ] fp32
+  constexpr int KOFF = SOFF + 2 * 2 * BQ * 4;      // [buf][wave][BQ] keep words
+  constexpr int SMEM = KOFF + (DROP ? 2 * 4 * BQ * 4 : 0);
+  __shared__ __attribute__((aligned(16))) char smem_raw[SMEM];
+  lds_char* smem = (lds_char*)smem_raw;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 5, nl = lane & 31;
+  int64_t bx, by, bz;
+  xcd_block(bx, by, bz);
+  const int64_t b = bz, hk = by;
+  const int64_t kb0 = bx * 128;                    // first key of the workgroup
+  const int64_t key = kb0 + 32 * wave + nl;        // this lane's key
+  const bool kvalid = key < p.Tkv;
+  const int grp = (int)(p.Hq / p.Hkv);
+  const float c2 = p.scale * kLog2e;
+
+  const E* kp = (const E*)p.k + b * p.k_sb + hk * p.k_sh;
+  const E* vp = (const E*)p.v + b * p.k_sb + hk * p.k_sh;
+  V8<E> kf[C::QC], vf[C::QC];
+#pragma unroll
+  for (int c = 0; c < C::QC; ++c) {
+    kf[c] = kvalid ? *(const V8<E>*)(kp + key * p.k_st + 16 * c + 8 * g) : (V8<E>){};
+    vf[c] = kvalid ? *(const V8<E>*)(vp + key * p.k_st + 16 * c + 8 * g) : (V8<E>){};
+  }
+
+  // Queries that can see any key of the workgroup.
+  int64_t qlo = 0, qhi = p.Tq;
+  if (MODE == B_INDEX) {
+    const int64_t klast = min(kb0 + 127, p.Tkv - 1);
+    qlo = max((int64_t)0, kb0 - p.offset);
+    if (p.bias == BIAS_SLIDING) qhi = min(p.Tq, klast - p.offset + p.window);
+  }
+  const int64_t qt0 = qlo / BQ;
+  const int nqt = qhi > qlo ? (int)((qhi + BQ - 1) / BQ - qt0) : 0;
+  const int niter = nqt * grp;
+
+  V8<E> qst[NLD], dst_[NLD];
+  float sval = 0.0f;
+  uint32_t kwv = 0;
+  auto gload = [&](int it) {
+    const int64_t hq = hk * grp + it / nqt;
+    const int64_t q0 = (qt0 + it % nqt) * BQ;
+    const E* qb = (const E*)p.q + b * p.q_sb + hq * p.q_sh;
+    const E* db = (const E*)p.dout + b * p.q_sb + hq * p.q_sh;
+#pragma unroll
+    for (int u = 0; u < NLD; ++u) {
+      const int idx = tid + 256 * u, row = idx / C::CH, ch = idx % C::CH;
+      const bool ok = q0 + row < p.Tq;
+      qst[u] = ok ? *(const V8<E>*)(qb + (q0 + row) * p.q_st + 8 * ch) : (V8<E>){};
+      dst_[u] = ok ? *(const V8<E>*)(db + (q0 + row) * p.q_st + 8 * ch) : (V8<E>){};
+    }
+    const int64_t rbase = (b * p.Hq + hq) * p.Tq;
+    if (tid < BQ) {
+      sval = lse2_of(p, rbase + q0 + tid, q0 + tid < p.Tq);
+    } else if (tid < 2 * BQ) {
+      const int64_t qi = q0 + tid - BQ;
+      sval = qi < p.Tq ? p.delta[rbase + qi] : 0.0f;
+    }
+    if (DROP) {
+      const int64_t qi = q0 + (tid & 63);
+      const int64_t w = kb0 / 32 + (tid >> 6);
+      kwv = (qi < p.Tq && w < p.keep_words) ? p.keep[(rbase + qi) * p.keep_words + w] : 0u;
+    }
+  };
+  auto lstore = [&](int buf) {
+    lds_char* qt = smem + buf * 2 * TQ;
+    lds_char* dt = qt + TQ;
+#pragma unroll
+    for (int u = 0; u < NLD; ++u) {
+      const int idx = tid + 256 * u, row = idx / C::CH, ch = idx % C::CH;
+      const int off = row * C::PITCH + ((ch ^ C::swz(row)) << 4);
+      lds_store(qt + off, qst[u]);
+      lds_store(dt + off, dst_[u]);
+    }
+    if (tid < 2 * BQ) lds_store(smem + SOFF + buf * 2 * BQ * 4 + tid * 4, sval);
+    if (DROP) lds_store(smem + KOFF + buf * 4 * BQ * 4 + tid * 4, kwv);
+  };
+
+  f32x16_e dvT[C::DB], dkT[C::DB];
+#pragma unroll
+  for (int nb = 0; nb < C::DB; ++nb) {
+    dvT[nb] = (f32x16_e){};
+    dkT[nb] = (f32x16_e){};
+  }
+  if (niter > 0) {
+    gload(0);
+    lstore(0);
+  }
+  __syncthreads();
+
+  for (int it = 0; it < niter; ++it) {
+    const int buf = it & 1;
+    const bool more = it + 1 < niter;
+    if (more) gload(it + 1);
+    const int64_t hq = hk * grp + it / nqt;
+    const int64_t q0 = (qt0 + it % nqt) * BQ;
+    const lds_char* qt = smem + buf * 2 * TQ;
+    const lds_char* dt = qt + TQ;
+    const lds_char* l2s = smem + SOFF + buf * 2 * BQ * 4;
+    const lds_char* dls = l2s + BQ * 4;
+    const lds_char* kws = smem + KOFF + buf * 4 * BQ * 4 + wave * BQ * 4;
+#pragma unroll 1
+    for (int s = 0; s < 2; ++s) {
+      const int64_t qa = q0 + 32 * s;
+      if (qa >= p.Tq) break;
+      if (MODE == B_INDEX) {       // no allowed (query, key) pair between this sub-tile and the wave's keys
+        const int64_t kw0 = kb0 + 32 * wave;
+        if (kw0 > qa + 31 + p.offset) continue;
+        if (p.bias == BIAS_SLIDING && kw0 + 31 <= qa + p.offset - p.window) continue;
+      }
+      f32x16_e sacc = (f32x16_e){}, dpacc = (f32x16_e){};
+#pragma unroll
+      for (int c = 0; c < C::QC; ++c) {
+        sacc = mfma32(ld_row<E, D>(qt, 32 * s + nl, c, g), kf[c], sacc);
+        dpacc = mfma32(ld_row<E, D>(dt, 32 * s + nl, c, g), vf[c], dpacc);
+      }
+      float l2[16], dl[16], pt[16], ds[16];
+      uint32_t kw[16];
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const int qo = 32 * s + 8 * a + 4 * g;
+        const f32x4 x = lds_load<f32x4>(l2s + qo * 4);
+        const f32x4 y = lds_load<f32x4>(dls + qo * 4);
+        u32x4 z = (u32x4){};
+        if (DROP) z = lds_load<u32x4>(kws + qo * 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          l2[4 * a + e] = x[e];
+          dl[4 * a + e] = y[e];
+          kw[4 * a + e] = z[e];
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t qq = qa + 8 * (r / 4) + 4 * g + (r % 4);
+        bool ok = kvalid;
+        float xb = -l2[r];
+        if (MODE == B_INDEX) {
+          ok = ok && key <= qq + p.offset;
+          if (p.bias == BIAS_SLIDING) ok = ok && key > qq + p.offset - p.window;
+        }
+        if (MODE == B_TENSOR) {
+          if (ok && qq < p.Tq) xb += mask_value(p, b, hq, qq, key) * kLog2e;
+        }
+        const float pr = ok ? __builtin_amdgcn_exp2f(fmaf(sacc[r], c2, xb)) : 0.0f;
+        float dw = dpacc[r];
+        if (DROP) {
+          const bool kept = (kw[r] >> nl) & 1u;
+          pt[r] = kept ? pr * p.keep_scale : 0.0f;
+          dw = kept ? dw * p.keep_scale : 0.0f;
+        } else {
+          pt[r] = pr;
+        }
+        ds[r] = pr * (dw - dl[r]);
+      }
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const V8<E> pb = pack8<E>(pt + 8 * c);
+        const V8<E> sb = pack8<E>(ds + 8 * c);
+#pragma unroll
+        for (int nb = 0; nb < C::DB; ++nb) {
+          dvT[nb] = mfma32(ld_tr<E, D>(dt, 32 * s + 16 * c, 32 * nb, lane), pb, dvT[nb]);
+          dkT[nb] = mfma32(ld_tr<E, D>(qt, 32 * s + 16 * c, 32 * nb, lane), sb, dkT[nb]);
+        }
+      }
+    }
+    if (more) lstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  // dV^T / dK^T: lane = key, registers = head dims 32 nb + 8 (r / 4) + 4 g + r % 4.
+  if (kvalid) {
+    G* dkp = (G*)p.dk + b * p.k_sb + hk * p.k_sh + key * p.k_st;
+    G* dvp = (G*)p.dv + b * p.k_sb + hk * p.k_sh + key * p.k_st;
+#pragma unroll
+    for (int nb = 0; nb < C::DB; ++nb)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int d = 32 * nb + 8 * i4 + 4 * g;
+        float a[4], c4[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          a[e] = dvT[nb][4 * i4 + e];
+          c4[e] = dkT[nb][4 * i4 + e];
+        }
+        store4(dvp + d, a, 1.0f);
+        store4(dkp + d, c4, p.scale);
+      }
+  }
+}
+
+// ---------------------------------------------------------------------- dQ --
+template <typename E, int D, int MODE, bool DROP, typename G>
+__global__ __launch_bounds__(256, (D == 128 ? 1 : 2)) void bwd_dq_kernel(BwdParams p) {
+  using C = BCfg<D>;
+  constexpr int BN = 64;                           // keys per staged tile
+  constexpr int TK = BN * C::PITCH;
+  constexpr int NLD = BN * C::CH / 256;
+  __shared__ __attribute__((aligned(16))) char smem_raw[4 * TK];   // [buf][K | V]
+  lds_char* smem = (lds_char*)smem_raw;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 5, nl = lane & 31;
+  int64_t bx, by, bz;
+  xcd_block(bx, by, bz);
+  const int64_t b = bz, h = by;
+  const int64_t hk = h / (p.Hq / p.Hkv);
+  const int64_t wg_q0 = bx * 128;
+  const int64_t wq0 = wg_q0 + 32 * wave;
+  const int64_t qrow = wq0 + nl;
+  const bool qvalid = qrow < p.Tq;
+  const float c2 = p.scale * kLog2e;
+
+  const int64_t qoff = b * p.q_sb + h * p.q_sh + (qvalid ? qrow : 0) * p.q_st;
+  V8<E> qf[C::QC], of[C::QC];
+#pragma unroll
+  for (int c = 0; c < C::QC; ++c) {
+    qf[c] = qvalid ? *(const V8<E>*)((const E*)p.q + qoff + 16 * c + 8 * g) : (V8<E>){};
+    of[c] = qvalid ? *(const V8<E>*)((const E*)p.dout + qoff + 16 * c + 8 * g) : (V8<E>){};
+  }
+  const int64_t srow = (b * p.Hq + h) * p.Tq + qrow;
+  const float l2 = lse2_of(p, srow, qvalid);
+  const float dl = qvalid ? p.delta[srow] : 0.0f;
+
+  int64_t lo = 0, hi = p.Tkv;
+  if (MODE == B_INDEX) {
+    const int64_t wg_q1 = min(wg_q0 + 127, p.Tq - 1);
+    hi = min(hi, wg_q1 + p.offset + 1);
+    if (p.bias == BIAS_SLIDING) lo = max((int64_t)0, wg_q0 + p.offset - p.window + 1);
+  }
+  const int64_t t0 = lo / BN;
+  const int ntiles = hi > lo ? (int)((hi - t0 * BN + BN - 1) / BN) : 0;
+
+  const E* kp = (const E*)p.k + b * p.k_sb + hk * p.k_sh;
+  const E* vp = (const E*)p.v + b * p.k_sb + hk * p.k_sh;
+  V8<E> kst[NLD], vst[NLD];
+  auto gload = [&](int it) {
+    const int64_t k0 = (t0 + it) * BN;
+#pragma unroll
+    for (int u = 0; u < NLD; ++u) {
+      const int idx = tid + 256 * u, row = idx / C::CH, ch = idx % C::CH;
+      const bool ok = k0 + row < p.Tkv;
+      kst[u] = ok ? *(const V8<E>*)(kp + (k0 + row) * p.k_st + 8 * ch) : (V8<E>){};
+      vst[u] = ok ? *(const V8<E>*)(vp + (k0 + row) * p.k_st + 8 * ch) : (V8<E>){};
+    }
+  };
+  auto lstore = [&](int buf) {
+    lds_char* ks = smem + buf * 2 * TK;
+#pragma unroll
+    for (int u = 0; u < NLD; ++u) {
+      const int idx = tid + 256 * u, row = idx / C::CH, ch = idx % C::CH;
+      const int off = row * C::PITCH + ((ch ^ C::swz(row)) << 4);
+      lds_store(ks + off, kst[u]);
+      lds_store(ks + TK + off, vst[u]);
+    }
+  };
+
+  f32x16_e dqT[C::DB];
+#pragma unroll
+  for (int nb = 0; nb < C::DB; ++nb) dqT[nb] = (f32x16_e){};
+  if (ntiles > 0) {
+    gload(0);
+    lstore(0);
+  }
+  __syncthreads();
+
+  for (int it = 0; it < ntiles; ++it) {
+    const int buf = it & 1;
+    const bool more = it + 1 < ntiles;
+    if (more) gload(it + 1);
+    const int64_t k0 = (t0 + it) * BN;
+    const lds_char* ks = smem + buf * 2 * TK;
+    const lds_char* vs = ks + TK;
+    bool skip = wq0 >= p.Tq;
+    if (MODE == B_INDEX) {
+      if (k0 > wq0 + 31 + p.offset) skip = true;
+      if (p.bias == BIAS_SLIDING && k0 + BN - 1 <= wq0 + p.offset - p.window) skip = true;
+    }
+    if (!skip) {
+      uint32_t kw[2] = {0u, 0u};
+      if (DROP && qvalid) {
+        const int64_t w0 = k0 / 32;
+        const uint32_t* kr = p.keep + srow * p.keep_words;
+        kw[0] = kr[w0];
+        kw[1] = w0 + 1 < p.keep_words ? kr[w0 + 1] : 0u;
+      }
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        f32x16_e sacc = (f32x16_e){}, dpacc = (f32x16_e){};
+#pragma unroll
+        for (int c = 0; c < C::QC; ++c) {
+          sacc = mfma32(ld_row<E, D>(ks, 32 * kb + nl, c, g), qf[c], sacc);
+          dpacc = mfma32(ld_row<E, D>(vs, 32 * kb + nl, c, g), of[c], dpacc);
+        }
+        float ds[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int kofs = 8 * (r / 4) + 4 * g + (r % 4);
+          const int64_t key = k0 + 32 * kb + kofs;
+          bool ok = key < p.Tkv;
+          float xb = -l2;
+          if (MODE == B_INDEX) {
+            ok = ok && key <= qrow + p.offset;
+            if (p.bias == BIAS_SLIDING) ok = ok && key > qrow + p.offset - p.window;
+          }
+          if (MODE == B_TENSOR) {
+            if (ok && qvalid) xb += mask_value(p, b, h, qrow, key) * kLog2e;
+          }
+          const float pr = ok ? __builtin_amdgcn_exp2f(fmaf(sacc[r], c2, xb)) : 0.0f;
+          float dw = dpacc[r];
+          if (DROP) dw = ((kw[kb] >> kofs) & 1u) ? dw * p.keep_scale : 0.0f;
+          ds[r] = pr * (dw - dl);
+        }
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const V8<E> sb = pack8<E>(ds + 8 * c);
+#pragma unroll
+          for (int nb = 0; nb < C::DB; ++nb)
+            dqT[nb] = mfma32(ld_tr<E, D>(ks, 32 * kb + 16 * c, 32 * nb, lane), sb, dqT[nb]);
+        }
+      }
+    }
+    if (more) lstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  // dQ^T: lane = query, registers = head dims 32 nb + 8 (r / 4) + 4 g + r % 4.
+  if (qvalid) {
+    G* dqp = (G*)p.dq + qoff;
+#pragma unroll
+    for (int nb = 0; nb < C::DB; ++nb)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        float a[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) a[e] = dqT[nb][4 * i4 + e];
+        store4(dqp + 32 * nb + 8 * i4 + 4 * g, a, p.scale);
+      }
+  }
+}
+
+// ---------------------------------------------------------------- launchers --
+int bmode_of(const BwdParams& p) {
+  switch (p.bias) {
+    case BIAS_NONE: return B_NONE;
+    case BIAS_CAUSAL:
+    case BIAS_SLIDING: return B_INDEX;
+    case BIAS_ADDITIVE:
+    case BIAS_BOOL: return B_TENSOR;
+    default: return -1;
+  }
+}
+
+template <typename E, int D, int MODE, bool DROP, typename G>
+void launch_main(const BwdParams& p, hipStream_t s) {
+  dim3 gkv((unsigned)((p.Tkv + 127) / 128), (unsigned)p.Hkv, (unsigned)p.B);
+  hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, MODE, DROP, G>), gkv, dim3(256), 0, s, p);
+  dim3 gq((unsigned)((p.Tq + 127) / 128), (unsigned)p.Hq, (unsigned)p.B);
+  hipLaunchKernelGGL((bwd_dq_kernel<E, D, MODE, DROP, G>), gq, dim3(256), 0, s, p);
+}
+
+template <typename E, int D, typename G>
+void launch_modes(const BwdParams& p, hipStream_t s) {
+  const bool drop = p.keep != nullptr;
+  switch (bmode_of(p)) {
+    case B_NONE: drop ? launch_main<E, D, B_NONE, true, G>(p, s) : launch_main<E, D, B_NONE, false, G>(p, s); break;
+    case B_INDEX: drop ? launch_main<E, D, B_INDEX, true, G>(p, s) : launch_main<E, D, B_INDEX, false, G>(p, s); break;
+    default: drop ? launch_main<E, D, B_TENSOR, true, G>(p, s) : launch_main<E, D, B_TENSOR, false, G>(p, s); break;
+  }
+}
+
+template <typename E, int D>
+void launch_typed(const BwdParams& p, hipStream_t s) {
+  const int64_t rows = p.B * p.Hq * p.Tq;
+  const int64_t blocks = (rows * (D / 8) + 255) / 256;
+  if (p.o_dtype == 0) hipLaunchKernelGGL((bwd_delta_kernel<E, float, D>), dim3((unsigned)blocks), dim3(256), 0, s, p, rows);
+  else hipLaunchKernelGGL((bwd_delta_kernel<E, E, D>), dim3((unsigned)blocks), dim3(256), 0, s, p, rows);
+  if (p.grad_dtype == 0) launch_modes<E, D, float>(p, s);
+  else launch_modes<E, D, E>(p, s);
+}
+
+template <typename E>
+void launch_e(const BwdParams& p, hipStream_t s) {
+  if (p.D == 32) launch_typed<E, 32>(p, s);
+  else if (p.D == 64) launch_typed<E, 64>(p, s);
+  else launch_typed<E, 128>(p, s);
+}
+
+}  // namespace
+
+bool bwd_supports(const BwdParams& p) {
+  if (p.dtype != 1 && p.dtype != 2) return false;
+  if (p.D != 32 && p.D != 64 && p.D != 128) return false;
+  if (bmode_of(p) < 0) return false;
+  if (p.B * p.Hq * p.Tq * (p.D / 8) / 256 + 1 > INT32_MAX) return false;
+  return true;
+}
+
+hipError_t launch_bwd(const BwdParams& p, hipStream_t s) {
+  if (p.dtype == 2) launch_e<_Float16>(p, s);
+  else launch_e<__bf16>(p, s);
+  return hipGetLastError();
+}
+
+}  // namespace sdpa

@@ -4,7 +4,10 @@
 //   "Axon.Layers.scaled_dot_product_attention/4", description)
 //
 // computed tile by tile with an online softmax, so no T_q x T_kv array is
-// written.  Bias kinds: none, causal / sliding-window (index masks, with
+// written.  Optional attention dropout (keep bits per score, [Axon PR 650],
+// description: dropout in :train mode): the row sum takes every weight and
+// P.V only the kept ones, and the output is multiplied by the kept-weight
+// factor at the end.  Bias kinds: none, causal / sliding-window (index masks, with
 // tile skipping), additive / boolean tensors (through broadcast strides), and
 // SAM's decomposed rel-pos bias rebuilt in registers from the per-query
 // term rows ([Candle PR 3280] "feat(metal): SDPA with Relative Positional
@@ -175,7 +178,7 @@ __device__ __forceinline__ void relpos_prologue(const FwdParams& p, lds_char* sm
     for (int i = 0; i < 16; ++i) ths[(yb * 32 + 8 * (i / 4) + 4 * g + (i % 4)) * 32 + ql] = th[yb][i];
 }
 
-template <int D, int MODE, bool OUT_BF16>
+template <int D, int MODE, bool OUT_BF16, bool DROP>
 __global__ __launch_bounds__(256, 2) void flash_mfma_kernel(FwdParams p, int hpw) {
   using C = Cfg<D>;
   // Software pipelining (next tile's scores in flight during this tile's
@@ -378,6 +381,14 @@ __global__ __launch_bounds__(256, 2) void flash_mfma_kernel(FwdParams p, int hpw
 
     if (!skip) {
       const lds_char* vs = vbuf(it);
+      // Dropout keep bits of this lane's row for the tile's 64 keys (tiles start at multiples of 64).
+      uint32_t kw[2] = {0u, 0u};
+      if (DROP && qvalid) {
+        const int64_t w0 = k0 / 32;
+        const uint32_t* kr = p.keep + ((b * p.Hq + h) * p.Tq + qrow) * p.keep_words + w0;
+        kw[0] = kr[0];
+        kw[1] = (w0 + 1 < p.keep_words) ? kr[1] : 0u;
+      }
       // Masks and tensor biases act on the raw scores (bias / scale), so every
       // mode shares one exponent: p = exp2(s * scale * log2e + (rowb - m)).
       if (MODE == M_TENSOR) {
@@ -445,6 +456,12 @@ __global__ __launch_bounds__(256, 2) void flash_mfma_kernel(FwdParams p, int hpw
                             fast_exp2(fmaf(s[t / 2][8 * (t % 2) + e + 1], c2, off))};
           pk[e / 2] = __builtin_convertvector(pp, bf16x2);
           l = __builtin_amdgcn_fdot2_f32_bf16(pk[e / 2], kOnes2, l, false);
+          if (DROP) {       // dropped weights leave P.V (the row sum above keeps them)
+            const int i0 = 8 * (t % 2) + e;                      // even: i0 and i0 + 1 are adjacent keys
+            const uint32_t two = (kw[t / 2] >> (8 * (i0 / 4) + 4 * g + (i0 % 4))) & 3u;
+            const uint32_t msk = ((two & 1u) ? 0xFFFFu : 0u) | ((two & 2u) ? 0xFFFF0000u : 0u);
+            pk[e / 2] = __builtin_bit_cast(bf16x2, __builtin_bit_cast(uint32_t, pk[e / 2]) & msk);
+          }
         }
         pb[t] = __builtin_shufflevector(__builtin_shufflevector(pk[0], pk[1], 0, 1, 2, 3),
                                         __builtin_shufflevector(pk[2], pk[3], 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
@@ -479,7 +496,7 @@ __global__ __launch_bounds__(256, 2) void flash_mfma_kernel(FwdParams p, int hpw
 
   // Epilogue: the two lane halves hold disjoint keys of the same query.
   const float lt = halves_sum(l);
-  const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+  const float inv = lt > 0.0f ? (DROP ? p.keep_scale : 1.0f) / lt : 0.0f;
   if (qvalid) {
     const int64_t ob = b * p.q_sb + h * p.q_sh + qrow * p.q_st;
 #pragma unroll
@@ -524,8 +541,15 @@ hipError_t launch_mode(const FwdParams& p, hipStream_t s) {
   const int hpw = (grp % 4 == 0) ? 4 : (grp % 2 == 0) ? 2 : 1;
   const int64_t rows = 32 * (4 / hpw);
   dim3 grid((unsigned)((p.Tq + rows - 1) / rows), (unsigned)(p.Hq / hpw), (unsigned)p.B);
-  if (p.out_dtype == 1) hipLaunchKernelGGL((flash_mfma_kernel<D, MODE, true>), grid, dim3(256), 0, s, p, hpw);
-  else hipLaunchKernelGGL((flash_mfma_kernel<D, MODE, false>), grid, dim3(256), 0, s, p, hpw);
+  constexpr bool CAN_DROP = MODE == M_NONE || MODE == M_INDEX || MODE == M_TENSOR;
+  if (CAN_DROP && p.keep) {
+    if (p.out_dtype == 1) hipLaunchKernelGGL((flash_mfma_kernel<D, MODE, true, CAN_DROP>), grid, dim3(256), 0, s, p, hpw);
+    else hipLaunchKernelGGL((flash_mfma_kernel<D, MODE, false, CAN_DROP>), grid, dim3(256), 0, s, p, hpw);
+  } else if (p.out_dtype == 1) {
+    hipLaunchKernelGGL((flash_mfma_kernel<D, MODE, true, false>), grid, dim3(256), 0, s, p, hpw);
+  } else {
+    hipLaunchKernelGGL((flash_mfma_kernel<D, MODE, false, false>), grid, dim3(256), 0, s, p, hpw);
+  }
   return hipGetLastError();
 }
 
@@ -555,6 +579,7 @@ bool flash_mfma_supports(const FwdParams& p) {
     if (p.D != 64 || p.grid_w != 64) return false;
     if (!p.term_h && !relpos_fused_supported(p)) return false;
   }
+  if (p.keep && p.bias == BIAS_RELPOS) return false;      // dropout runs with index / tensor masks only
   // Tensor masks index keys with 32-bit deltas inside a tile.
   if ((p.bias == BIAS_ADDITIVE || p.bias == BIAS_BOOL) && p.ms[3] * 4 * 64 > INT32_MAX) return false;
   return true;

@@ -1,5 +1,5 @@
 // Generic fused attention on the vector ALUs: any head_dim up to 128, fp32,
-// bf16 or fp16 inputs, every bias kind.  It serves the fp32 path and shapes that the
+// bf16 or fp16 inputs, every bias kind, optional attention dropout.  It serves the fp32 path and shapes that the
 // MFMA kernels do not cover.
 //
 // One wave per block, one query row per lane.  K/V tiles of 32 keys are staged
@@ -65,6 +65,8 @@ __global__ __launch_bounds__(64) void generic_fwd_kernel(FwdParams p) {
     }
   }
   const int gh = p.grid_h, gw = p.grid_w;
+  // Dropout keep bits of this lane's score row (nullptr: no dropout).
+  const uint32_t* krow = p.keep ? p.keep + ((b * p.Hq + h) * p.Tq + (live ? i : 0)) * p.keep_words : nullptr;
   // Grids too large for LDS rows read the workspace terms from memory.
   const bool rows_in_lds = (GF == GF_RELPOS) && (p.relpos_rows_lds != 0);
   const float* thg = nullptr;
@@ -212,13 +214,20 @@ __global__ __launch_bounds__(64) void generic_fwd_kernel(FwdParams p) {
         const float z = zs[jj][lane];
         const float pj = (z == -INFINITY) ? 0.0f : expf(z - m);
         l += pj;
+        // dropout: the row sum takes every weight, P.V only the kept ones
+        // (the common factor of kept weights is applied at the end)
+        float pv = pj;
+        if (krow) {
+          const int64_t j = j0 + jj;
+          pv = ((krow[j >> 5] >> (j & 31)) & 1u) ? pj : 0.0f;
+        }
 #pragma unroll
-        for (int c = 0; c < DMAX; ++c) acc[c] = fmaf(pj, vs[jj][c], acc[c]);
+        for (int c = 0; c < DMAX; ++c) acc[c] = fmaf(pv, vs[jj][c], acc[c]);
       }
     }
   }
   if (!live) return;
-  const float inv = (l > 0.0f) ? 1.0f / l : 0.0f;
+  const float inv = (l > 0.0f) ? (krow ? p.keep_scale : 1.0f) / l : 0.0f;
   const int64_t ob = b * p.q_sb + h * p.q_sh + i * p.q_st;
   if (p.out_dtype == 0) {
     float* op = (float*)p.o + ob;

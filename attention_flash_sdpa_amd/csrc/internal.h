@@ -42,6 +42,48 @@ struct FwdParams {
   int num_splits;             // split-KV chunks (1 = no split)
   float* part_o;              // split-KV partial outputs [splits, B, Hq, Tq, D] fp32
   float* part_ml;             // split-KV partial (max, sum) [splits, B, Hq, Tq, 2] fp32
+  const uint32_t* keep;       // dropout keep bits [B, Hq, Tq, keep_words] or nullptr (no dropout)
+  int64_t keep_words;         // 32-bit words per score row: ceil(Tkv / 32)
+  float keep_scale;           // factor of a kept weight: 65536 / (65536 - threshold)
+};
+
+// Everything the backward kernels need.  q, o, dout and dq share the q strides;
+// k, v, dk and dv share the k strides.
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;           // [B, Hq, Tq] natural-log row log-sum-exp of the forward pass
+  void* dq;
+  void* dk;
+  void* dv;
+  float* delta;               // workspace [B, Hq, Tq]: rowsum(dout * o)
+  int dtype;                  // SDPA_BF16 / SDPA_F16
+  int o_dtype;                // element type of o: dtype or SDPA_F32
+  int grad_dtype;             // element type of dq, dk, dv: dtype or SDPA_F32
+  int64_t B, Hq, Hkv, Tq, Tkv, D;
+  int64_t q_sb, q_sh, q_st;
+  int64_t k_sb, k_sh, k_st;
+  float scale;
+  int bias;                   // BiasKind (no rel-pos)
+  int64_t offset, window;
+  const void* mdata;
+  int mdtype;
+  int64_t ms[4];
+  const uint32_t* keep;
+  int64_t keep_words;
+  float keep_scale;
+};
+
+// Dropout keep bits (Philox4x32-10): word [b, h, i, j / 32], bit j % 32.
+struct DropoutParams {
+  uint64_t seed;
+  uint32_t step;
+  uint32_t thresh;            // keep iff the element's 16-bit uniform >= thresh
+  int64_t B, Hq, Tq, Tkv, keep_words;
+  uint32_t* keep;
 };
 
 struct TermsParams {
@@ -78,5 +120,12 @@ hipError_t launch_tiled(const FwdParams& p, hipStream_t s);          // bf16, D 
 bool tiled_supports(const FwdParams& p);
 // Rel-pos terms can be formed inside the MFMA kernel (no term arrays needed).
 bool relpos_fused_supported(const FwdParams& p);
+hipError_t launch_dropout_mask(const DropoutParams& p, hipStream_t s);
+// Backward (16-bit inputs, head_dim 32 / 64 / 128, every bias kind but rel-pos):
+// delta, then dK / dV (one workgroup per key block), then dQ (one per query block).
+bool bwd_supports(const BwdParams& p);
+hipError_t launch_bwd(const BwdParams& p, hipStream_t s);
+// Attention weights [B, Hq, Tq, Tkv] fp32 from the forward pass's lse (any dtype, head_dim <= 128).
+hipError_t launch_attn_weights(const FwdParams& p, float* weights, hipStream_t s);
 
 }  // namespace sdpa

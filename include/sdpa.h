@@ -200,6 +200,86 @@ const char* sdpa_last_kernel(void);
  */
 int sdpa_set_tuning(const char* key, int64_t value);
 
+/* ---------------------------------------------------------------------------
+ * Training path.  [Axon PR 650], description: `:dropout_rate` drops attention
+ * probabilities in :train mode, with a PRNG key that the graph layer threads
+ * across steps; `:return_attention_weights`; and the gradients a training
+ * step needs.
+ *
+ * Dropout works on keep bits: one bit per score element, packed as uint32
+ * words [B, Hq, Tq, ceil(Tkv / 32)] (bit j % 32 of word j / 32 keeps score
+ * (b, h, i, j); bits past Tkv are zero).  A dropped weight contributes nothing
+ * to O; a kept one is multiplied by 65536 / (65536 - thresh), where
+ * thresh = floor(rate * 65536 + 0.5) clamped to 65535, so the kept weights are
+ * unbiased.  The row normalisation and lse are those of the undropped scores.
+ * ------------------------------------------------------------------------- */
+
+/*
+ * Keep bits from the counter-based generator Philox4x32-10 (Salmon, Moraes,
+ * Dror and Shaw, "Parallel random numbers: as easy as 1, 2, 3", SC 2011):
+ * score (b, h, i, j) takes the 16-bit half j % 8 (low half of word
+ * (j % 8) / 2 first) of Philox(counter = (j / 8, i, b * Hq + h, step),
+ * key = (seed low 32 bits, seed high 32 bits)) and is kept iff that half
+ * >= thresh.  The same (seed, step) always gives the same bits; a training
+ * loop advances `step` (or the seed) every call.
+ *   keep   device output, B * Hq * Tq * ceil(Tkv / 32) uint32 words.
+ *   rate   in [0, 1).  B * Hq, Tq and Tkv must fit in 31 bits.
+ */
+int sdpa_dropout_mask(uint64_t seed, uint32_t step, float rate, int64_t B, int64_t Hq, int64_t Tq, int64_t Tkv,
+                      uint32_t* keep, void* stream);
+
+/*
+ * Fused attention with attention dropout: O = (W * Z) . V, with W the softmax
+ * weights of sdpa_fwd and Z = keep bit * 65536 / (65536 - thresh).  Arguments
+ * as in sdpa_fwd, plus the keep bits (required, device) and the rate that
+ * produced them.  lse (optional) is that of the undropped scores.
+ * Runs on the general matrix-core kernel (bf16, head_dim 64 / 128, positive
+ * scale), else on the generic kernel; the workspace is not used (may be NULL).
+ */
+int sdpa_fwd_dropout(const void* q, const void* k, const void* v, void* o, int dtype, int out_dtype, int layout,
+                     int64_t B, int64_t Hq, int64_t Hkv, int64_t Tq, int64_t Tkv, int64_t D, float scale,
+                     const sdpa_mask* mask, const uint32_t* keep, float rate, float* lse, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
+/* Bytes of device workspace sdpa_bwd needs ((size_t)-1 for invalid sizes). */
+size_t sdpa_bwd_workspace_size(int64_t B, int64_t Hq, int64_t Tq);
+
+/*
+ * Gradients of attention: for a loss with upstream gradient dout = dL/dO,
+ *   dv = (W * Z)^T . dout            (summed over the query heads sharing a KV head)
+ *   dW = (dout . v^T) * Z,   dS = W * (dW - rowsum(dout * o))
+ *   dq = scale * dS . k,     dk = scale * dS^T . q   (summed likewise)
+ * with W rebuilt from q, k, the mask and the forward pass's lse (no T x T
+ * array is stored).  Rows with no allowed key get zero gradients.
+ *   q, k, v, o, dout  as in sdpa_fwd (o and dout shaped like q); o in o_dtype
+ *                     (dtype or SDPA_F32), the forward pass's output.
+ *   lse               [B, Hq, Tq] fp32 from the forward pass (required).
+ *   dq, dk, dv        outputs shaped like q, k, v, in grad_dtype (dtype or SDPA_F32);
+ *                     fully overwritten.
+ *   mask              as in sdpa_fwd; keep / rate as in sdpa_fwd_dropout
+ *                     (keep NULL = no dropout).
+ *   workspace         at least sdpa_bwd_workspace_size(B, Hq, Tq) bytes.
+ * Built for bf16 / fp16 inputs with head_dim 32, 64 or 128 and 16-byte aligned
+ * tensors (SDPA_ERR_UNSUPPORTED otherwise).  Deterministic: no atomics.
+ */
+int sdpa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+             void* dq, void* dk, void* dv, int dtype, int o_dtype, int grad_dtype, int layout,
+             int64_t B, int64_t Hq, int64_t Hkv, int64_t Tq, int64_t Tkv, int64_t D, float scale,
+             const sdpa_mask* mask, const uint32_t* keep, float rate, void* workspace, size_t workspace_bytes,
+             void* stream);
+
+/*
+ * The attention weights (`:return_attention_weights`): weights[b, h, i, j] =
+ * exp(scale * q_i . k_j + bias_ij - lse_i) * Z_ij, i.e. the weights that
+ * multiply V in the forward pass that produced lse (Z = 1 without keep bits).
+ *   weights  device output [B, Hq, Tq, Tkv] fp32 (a T x T array: a debug output).
+ *   lse      [B, Hq, Tq] fp32 from sdpa_fwd / sdpa_fwd_dropout on the same inputs.
+ * Any dtype and head_dim up to 128; B * Hq and Tq / 64 must stay below 65536.
+ */
+int sdpa_attention_weights(const void* q, const void* k, int dtype, int layout, int64_t B, int64_t Hq, int64_t Hkv,
+                           int64_t Tq, int64_t Tkv, int64_t D, float scale, const sdpa_mask* mask, const float* lse,
+                           const uint32_t* keep, float rate, float* weights, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -24,7 +24,9 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("sdpa_fwd", "sdpa_relpos_fwd", "relpos_terms", "sdpa_workspace_size",
-              "sdpa_status_string", "sdpa_last_error", "sdpa_last_kernel", "sdpa_set_tuning"):
+              "sdpa_status_string", "sdpa_last_error", "sdpa_last_kernel", "sdpa_set_tuning",
+              "sdpa_dropout_mask", "sdpa_fwd_dropout", "sdpa_bwd", "sdpa_bwd_workspace_size",
+              "sdpa_attention_weights"):
         assert n in names
 
 
@@ -176,3 +178,44 @@ def test_no_symbol_defined_in_two_objects():
             if len(parts) == 3 and parts[1] in "TWV" and "sdpa" in parts[2] and "__device_stub" not in parts[2]:
                 assert parts[2] not in seen, f"{parts[2]} in {seen.get(parts[2])} and {f}"
                 seen[parts[2]] = f
+
+
+def test_training_entry_points_reject_bad_arguments():
+    lib = fa.load()
+    m = None
+    # dropout mask: null output, bad rate, bad sizes
+    assert lib.sdpa_dropout_mask(1, 0, 0.1, 1, 1, 8, 8, None, None) == -1
+    assert lib.sdpa_dropout_mask(1, 0, 1.0, 1, 1, 8, 8, FAKE, None) == -1
+    assert lib.sdpa_dropout_mask(1, 0, -0.1, 1, 1, 8, 8, FAKE, None) == -1
+    assert lib.sdpa_dropout_mask(1, 0, float("nan"), 1, 1, 8, 8, FAKE, None) == -1
+    assert lib.sdpa_dropout_mask(1, 0, 0.1, 1, 0, 8, 8, FAKE, None) == -1
+    # dropout forward: keep bits are required, rate checked
+    fwd = lambda keep, rate, **kw: lib.sdpa_fwd_dropout(FAKE, FAKE, FAKE, FAKE, kw.get("dtype", 1), kw.get("dtype", 1), 1,
+                                                       1, 2, 2, 8, 8, kw.get("D", 64), float("nan"), m, keep, rate,
+                                                       None, None, 0, None)
+    assert fwd(None, 0.1) == -1
+    assert fwd(FAKE, 1.5) == -1
+    assert fwd(FAKE, 0.1, D=48) == -2
+    # backward: required pointers, dtype support, workspace
+    def bwd(**kw):
+        a = dict(q=FAKE, lse=FAKE, dq=FAKE, dtype=1, odt=1, gdt=1, D=64, ws=FAKE, wsn=1 << 20, keep=None, rate=0.0)
+        a.update(kw)
+        return lib.sdpa_bwd(a["q"], FAKE, FAKE, FAKE, FAKE, a["lse"], a["dq"], FAKE, FAKE, a["dtype"], a["odt"],
+                            a["gdt"], 1, 1, 2, 2, 8, 8, a["D"], float("nan"), m, a["keep"], a["rate"], a["ws"],
+                            a["wsn"], None)
+    assert bwd(q=None) == -1
+    assert bwd(lse=None) == -1
+    assert bwd(dq=None) == -1
+    assert bwd(gdt=2) == -1                       # grads must be dtype or fp32
+    assert bwd(dtype=0, odt=0, gdt=0) == -2       # fp32 inputs: not built
+    assert bwd(D=16) == -2                        # head_dim 16: not built
+    assert bwd(ws=None, wsn=0) == -3
+    assert bwd(wsn=16) == -3
+    assert bwd(keep=FAKE, rate=2.0) == -1
+    assert lib.sdpa_bwd_workspace_size(2, 3, 100) == 2560
+    assert lib.sdpa_bwd_workspace_size(0, 3, 100) == ctypes.c_size_t(-1).value
+    # attention weights
+    assert lib.sdpa_attention_weights(FAKE, FAKE, 1, 1, 1, 2, 2, 8, 8, 64, float("nan"), m, None, None, 0.0,
+                                      FAKE, None) == -1
+    assert lib.sdpa_attention_weights(FAKE, FAKE, 1, 1, 1, 2, 2, 8, 8, 64, float("nan"), m, FAKE, FAKE, 1.0,
+                                      FAKE, None) == -1

@@ -1,0 +1,275 @@
+"""GPU parity of the training path (dropout keep bits, dropout forward,
+attention weights, backward) against the fp64 oracle, through the C ABI.
+
+Every oracle input comes from the seeded generators or from the oracle
+itself (the keep bits the kernels consume are the oracle's Philox bits, the
+forward output and lse handed to the backward kernels are the oracle's);
+the GPU generator is checked separately, bit for bit.
+
+Gradient tolerance (normalised error max|g_gpu - g| / max|g|): the kernels
+round the weights and dS to the input type before the matrix products
+(2^-9 relative for bf16, 2^-11 for fp16), take O in the input type for
+rowsum(dO * O), and store the gradients in the input type.  Emulating
+exactly those roundings in fp64 numpy on unit-normal inputs (T 333..1024,
+head_dim 64 / 128) gives 3-5e-3 (bf16) and 4-7e-4 (fp16); the bounds below
+are 3x that.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import sdpa_train_oracle as st
+from parity_util import TOL, max_err, np64
+
+pytestmark = pytest.mark.gpu
+
+GTOL = {torch.bfloat16: 1.5e-2, torch.float16: 2e-3}
+DT = {"bf16": torch.bfloat16, "fp16": torch.float16, "fp32": torch.float32}
+
+
+def draw(rng, shape, dt):
+    return torch.from_numpy(rng.standard_normal(shape, dtype=np.float32)).to(dt)
+
+
+def shp(layout, B, H, T, D):
+    return (B, H, T, D) if layout == "bhsd" else (B, T, H, D)
+
+
+def keep_words_tensor(keep_bool):
+    w = st.pack_keep_words(keep_bool)                      # uint32
+    return torch.from_numpy(w.view(np.int32)).cuda()
+
+
+def norm_err(a, b):
+    a, b = np.asarray(a, np.float64), np.asarray(b, np.float64)
+    assert np.all(np.isfinite(a))
+    return float(np.max(np.abs(a - b)) / max(np.max(np.abs(b)), 1e-30))
+
+
+# --------------------------------------------------------- dropout keep bits --
+@pytest.mark.parametrize("seed,step,rate,shape", [
+    (0, 0, 0.1, (1, 2, 5, 40)), (0x123456789ABCDEF0, 7, 0.3, (2, 3, 17, 97)),
+    (42, 123456, 0.5, (1, 1, 64, 256)), (7, 1, 0.0, (1, 2, 3, 33)), (9, 2, 0.95, (2, 1, 9, 8)),
+])
+def test_dropout_mask_bits_match_oracle(gpu, seed, step, rate, shape):
+    B, Hq, Tq, Tkv = shape
+    got = gpu.dropout_mask(seed, step, rate, B, Hq, Tq, Tkv)
+    torch.cuda.synchronize()
+    ref = st.pack_keep_words(st.dropout_keep(seed, step, rate, B, Hq, Tq, Tkv))
+    assert np.array_equal(got.cpu().numpy().view(np.uint32), ref)
+
+
+def test_dropout_mask_large_rows(gpu):
+    """A bench-sized score array (1 x 12 x 4096 x 4096), checked on sampled rows:
+    the oracle's generator draws just those rows (counters depend only on
+    (j // 8, i, b * Hq + h, step))."""
+    B, Hq, Tq, Tkv, seed, step, rate = 1, 12, 4096, 4096, 5, 3, 0.1
+    got = gpu.dropout_mask(seed, step, rate, B, Hq, Tq, Tkv).cpu().numpy().view(np.uint32)
+    thresh, _ = st.dropout_threshold(rate)
+    ng = Tkv // 8
+    for (b, h, i) in [(0, 0, 0), (0, 11, 4095), (0, 5, 2049), (0, 7, 31)]:
+        words = st.philox4x32_10((np.arange(ng), np.full(ng, i), np.full(ng, b * Hq + h), np.full(ng, step)),
+                                 (seed, 0))
+        halves = np.stack([x for w in words for x in (w & np.uint64(0xFFFF), w >> np.uint64(16))], axis=-1)
+        row = st.pack_keep_words(halves.reshape(-1) >= np.uint64(thresh))
+        assert np.array_equal(got[b, h, i], row)
+
+
+# ------------------------------------------------------------ dropout forward --
+FWD_CASES = [
+    ("bf16", "bhsd", 2, 4, 2, 200, 333, 64, None),                       # matrix-core kernel, GQA
+    ("bf16", "bshd", 1, 2, 2, 97, 130, 128, {"kind": "causal", "offset": 3}),
+    ("bf16", "bhsd", 1, 2, 1, 150, 150, 64, {"kind": "sliding", "window": 40, "offset": 0}),
+    ("bf16", "bhsd", 1, 2, 2, 70, 90, 64, "additive"),
+    ("fp16", "bhsd", 1, 2, 2, 100, 77, 64, None),                        # generic kernel
+    ("fp32", "bshd", 2, 2, 1, 65, 40, 48, {"kind": "causal", "offset": 0}),
+    ("bf16", "bhsd", 1, 1, 1, 33, 50, 32, "bool"),
+]
+
+
+@pytest.mark.parametrize("case", FWD_CASES, ids=[f"{c[0]}-{c[1]}-D{c[7]}-{c[8] if isinstance(c[8], str) else (c[8] or {}).get('kind', 'none')}" for c in FWD_CASES])
+def test_dropout_forward_matches_oracle(gpu, case):
+    dts, layout, B, Hq, Hkv, Tq, Tkv, D, mask = case
+    dt = DT[dts]
+    rng = np.random.default_rng(31)
+    q = draw(rng, shp(layout, B, Hq, Tq, D), dt)
+    k = draw(rng, shp(layout, B, Hkv, Tkv, D), dt)
+    v = draw(rng, shp(layout, B, Hkv, Tkv, D), dt)
+    omask = gmask = mask
+    if mask == "additive":
+        m = torch.from_numpy(rng.standard_normal((1, Hq, Tq, Tkv), dtype=np.float32))
+        omask, gmask = {"kind": "additive", "data": m.numpy()}, {"kind": "additive", "data": m.cuda()}
+    elif mask == "bool":
+        m = torch.from_numpy(rng.random((B, 1, Tq, Tkv)) < 0.8)
+        m[..., 0] = True
+        omask, gmask = {"kind": "bool", "data": m.numpy()}, {"kind": "bool", "data": m.cuda()}
+    rate = 0.2
+    keep = st.dropout_keep(11, 4, rate, B, Hq, Tq, Tkv)
+    scale = 1.0 / np.sqrt(D)
+    o, lse = gpu.sdpa(q.cuda(), k.cuda(), v.cuda(), layout=layout, scale=scale, mask=gmask,
+                      out_dtype=torch.float32, return_lse=True,
+                      dropout={"keep": keep_words_tensor(keep), "rate": rate})
+    torch.cuda.synchronize()
+    ref = st.sdpa_train_fwd(np64(q), np64(k), np64(v), layout=layout, scale=scale, mask=omask, keep=keep, rate=rate)
+    # the forward tolerances of the same kernels; kept weights are scaled by 1 / (1 - rate) on the output
+    assert max_err(np64(o), ref["o"]) < TOL[dts] * 1.5
+    # lse comes from the row sum of the weights as rounded for P.V, like the forward pass without dropout
+    assert max_err(np64(lse), ref["lse"]) <= TOL[dts]
+
+
+# --------------------------------------------------------- attention weights --
+@pytest.mark.parametrize("dts,mask,drop", [("bf16", None, False), ("bf16", {"kind": "causal", "offset": 1}, True),
+                                           ("fp32", {"kind": "sliding", "window": 9, "offset": 0}, False),
+                                           ("fp16", None, True)])
+def test_attention_weights_match_oracle(gpu, dts, mask, drop):
+    dt = DT[dts]
+    rng = np.random.default_rng(32)
+    B, Hq, Hkv, Tq, Tkv, D = 2, 2, 1, 70, 100, 64
+    q, k = draw(rng, (B, Hq, Tq, D), dt), draw(rng, (B, Hkv, Tkv, D), dt)
+    v = draw(rng, (B, Hkv, Tkv, D), dt)
+    scale = 0.125
+    keep, rate, dro = None, 0.0, None
+    if drop:
+        rate = 0.25
+        keep = st.dropout_keep(3, 9, rate, B, Hq, Tq, Tkv)
+        dro = {"keep": keep_words_tensor(keep), "rate": rate}
+    lse = oracle.sdpa(np64(q), np64(k), np64(v), scale=scale, mask=mask)["lse"]
+    w = gpu.attention_weights(q.cuda(), k.cuda(), torch.from_numpy(lse.astype(np.float32)).cuda(), scale=scale,
+                              mask=mask, dropout=dro)
+    torch.cuda.synchronize()
+    ref = st.attention_weights(np64(q), np64(k), scale=scale, mask=mask, keep=keep, rate=rate)
+    assert max_err(np64(w), ref) < 2e-5
+
+
+# ------------------------------------------------------------------ backward --
+BWD_CASES = [
+    # dtype, layout, B, Hq, Hkv, Tq, Tkv, D, mask, drop, grad fp32
+    ("bf16", "bhsd", 1, 2, 2, 200, 333, 64, None, False, False),
+    ("bf16", "bshd", 2, 4, 2, 97, 130, 128, None, False, False),
+    ("bf16", "bhsd", 1, 8, 2, 333, 333, 128, {"kind": "causal", "offset": 0}, False, False),
+    ("bf16", "bhsd", 1, 2, 2, 150, 150, 64, {"kind": "sliding", "window": 40, "offset": 0}, False, True),
+    ("bf16", "bhsd", 1, 2, 2, 130, 100, 64, {"kind": "causal", "offset": -40}, False, False),   # dead rows
+    ("bf16", "bhsd", 1, 2, 1, 96, 200, 32, "additive", False, False),
+    ("bf16", "bshd", 1, 2, 2, 64, 64, 64, "bool", True, False),
+    ("bf16", "bhsd", 2, 2, 2, 160, 224, 64, None, True, False),
+    ("bf16", "bhsd", 1, 4, 1, 129, 257, 128, {"kind": "causal", "offset": 5}, True, True),
+    ("fp16", "bhsd", 1, 2, 2, 200, 333, 64, None, False, False),
+    ("fp16", "bshd", 1, 4, 2, 100, 77, 128, {"kind": "sliding", "window": 30, "offset": 2}, True, False),
+    ("fp16", "bhsd", 1, 2, 2, 1, 5, 32, None, False, True),                                    # tiny
+]
+
+
+def _bwd_case_id(c):
+    m = c[8] if isinstance(c[8], str) else (c[8] or {}).get("kind", "none")
+    return f"{c[0]}-{c[1]}-{c[3]}x{c[4]}-{c[5]}x{c[6]}-D{c[7]}-{m}{'-drop' if c[9] else ''}{'-g32' if c[10] else ''}"
+
+
+@pytest.mark.parametrize("case", BWD_CASES, ids=[_bwd_case_id(c) for c in BWD_CASES])
+def test_backward_matches_oracle(gpu, case):
+    dts, layout, B, Hq, Hkv, Tq, Tkv, D, mask, drop, g32 = case
+    dt = DT[dts]
+    rng = np.random.default_rng(33)
+    q = draw(rng, shp(layout, B, Hq, Tq, D), dt)
+    k = draw(rng, shp(layout, B, Hkv, Tkv, D), dt)
+    v = draw(rng, shp(layout, B, Hkv, Tkv, D), dt)
+    do = draw(rng, shp(layout, B, Hq, Tq, D), dt)
+    omask = gmask = mask
+    if mask == "additive":
+        m = torch.from_numpy(rng.standard_normal((1, Hq, Tq, Tkv), dtype=np.float32)).to(torch.bfloat16)
+        omask, gmask = {"kind": "additive", "data": np64(m)}, {"kind": "additive", "data": m.cuda()}
+    elif mask == "bool":
+        m = torch.from_numpy(rng.random((B, Hq, Tq, Tkv)) < 0.7)
+        omask, gmask = {"kind": "bool", "data": m.numpy()}, {"kind": "bool", "data": m.cuda()}
+    rate, keep, dro = 0.0, None, None
+    if drop:
+        rate = 0.15
+        keep = st.dropout_keep(21, 2, rate, B, Hq, Tq, Tkv)
+        dro = {"keep": keep_words_tensor(keep), "rate": rate}
+    scale = 1.0 / np.sqrt(D)
+    kw = dict(layout=layout, scale=scale, mask=omask, keep=keep, rate=rate)
+    fwd = st.sdpa_train_fwd(np64(q), np64(k), np64(v), **kw)
+    o = torch.from_numpy(np.ascontiguousarray(fwd["o"], dtype=np.float32)).to(dt)
+    lse = torch.from_numpy(fwd["lse"].astype(np.float32))
+    dq, dk, dv = gpu.sdpa_backward(q.cuda(), k.cuda(), v.cuda(), o.cuda(), do.cuda(), lse.cuda(), layout=layout,
+                                   scale=scale, mask=gmask, dropout=dro,
+                                   grad_dtype=torch.float32 if g32 else None)
+    torch.cuda.synchronize()
+    ref = st.sdpa_bwd(np64(q), np64(k), np64(v), np64(do), **kw)
+    for name, got in (("dq", dq), ("dk", dk), ("dv", dv)):
+        e = norm_err(np64(got), ref[name])
+        assert e < GTOL[dt], (name, e)
+    if isinstance(mask, dict) and mask.get("offset", 0) < 0:       # rows that see no key: exact zeros
+        dead = -mask["offset"]
+        assert torch.all(dq[:, :, :dead] == 0) if layout == "bhsd" else torch.all(dq[:, :dead] == 0)
+
+
+def test_backward_is_deterministic(gpu):
+    rng = np.random.default_rng(34)
+    B, H, T, D = 1, 4, 300, 64
+    t = [draw(rng, (B, H, T, D), torch.bfloat16).cuda() for _ in range(4)]
+    o, lse = gpu.sdpa(t[0], t[1], t[2], return_lse=True)
+    a = gpu.sdpa_backward(t[0], t[1], t[2], o, t[3], lse)
+    b = gpu.sdpa_backward(t[0], t[1], t[2], o, t[3], lse)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+def test_backward_after_library_forward(gpu):
+    """End to end on the GPU: forward with dropout (library keep bits), then the
+    backward from the library's own O and lse, against the oracle on the same bits."""
+    rng = np.random.default_rng(35)
+    B, Hq, Hkv, T, D = 1, 4, 2, 257, 64
+    q, k, v, do = (draw(rng, (B, H, T, D), torch.bfloat16) for H in (Hq, Hkv, Hkv, Hq))
+    rate = 0.1
+    keep_g = gpu.dropout_mask(77, 5, rate, B, Hq, T, T)
+    dro = {"keep": keep_g, "rate": rate}
+    o, lse = gpu.sdpa(q.cuda(), k.cuda(), v.cuda(), return_lse=True, dropout=dro)
+    dq, dk, dv = gpu.sdpa_backward(q.cuda(), k.cuda(), v.cuda(), o, do.cuda(), lse, dropout=dro)
+    torch.cuda.synchronize()
+    keep = st.dropout_keep(77, 5, rate, B, Hq, T, T)
+    assert np.array_equal(keep_g.cpu().numpy().view(np.uint32), st.pack_keep_words(keep))
+    ref = st.sdpa_bwd(np64(q), np64(k), np64(v), np64(do), keep=keep, rate=rate)
+    for name, got in (("dq", dq), ("dk", dk), ("dv", dv)):
+        assert norm_err(np64(got), ref[name]) < GTOL[torch.bfloat16], name
+
+
+def test_backward_rejects_unsupported(gpu):
+    x = torch.zeros(1, 1, 8, 16, device="cuda", dtype=torch.bfloat16)
+    lse = torch.zeros(1, 1, 8, device="cuda")
+    with pytest.raises(gpu.SdpaError):
+        gpu.sdpa_backward(x, x, x, x, x, lse)                       # head_dim 16 is not built
+    y = torch.zeros(1, 1, 8, 64, device="cuda", dtype=torch.float32)
+    with pytest.raises(gpu.SdpaError):
+        gpu.sdpa_backward(y, y, y, y, y, lse)                       # fp32 inputs are not built
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name", ["gqa_causal", "sam_global_nobias"])
+def test_backward_full_size_sampled_heads(gpu, name):
+    """Bench-sized shapes in the launch configuration the benchmark times; the
+    oracle checks the full gradients of sampled (batch, KV head) groups."""
+    import workloads
+    if name == "sam_global_nobias":
+        wl = workloads.WORKLOADS["sam_global_relpos"].with_(grid=None)
+    else:
+        wl = workloads.WORKLOADS[name]
+    x = workloads.generate(wl, seed=0)
+    rng = np.random.default_rng(36)
+    do = draw(rng, tuple(x["q"].shape), torch.bfloat16)
+    g = {k: v.cuda() for k, v in x.items()}
+    o, lse = gpu.sdpa(g["q"], g["k"], g["v"], layout=wl.layout, scale=wl.scale, mask=wl.mask, return_lse=True)
+    dq, dk, dv = gpu.sdpa_backward(g["q"], g["k"], g["v"], o, do.cuda(), lse, layout=wl.layout, scale=wl.scale,
+                                   mask=wl.mask)
+    torch.cuda.synchronize()
+    grp = wl.Hq // wl.Hkv
+    to_b = (lambda t: t) if wl.layout == "bhsd" else (lambda t: t.permute(0, 2, 1, 3))
+    for (b, hk) in [(0, 0), (wl.B - 1, wl.Hkv - 1)]:
+        hs = slice(hk * grp, (hk + 1) * grp)
+        qs, dos = np64(to_b(x["q"])[b:b + 1, hs]), np64(to_b(do)[b:b + 1, hs])
+        ks, vs = np64(to_b(x["k"])[b:b + 1, hk:hk + 1]), np64(to_b(x["v"])[b:b + 1, hk:hk + 1])
+        ref = st.sdpa_bwd(qs, ks, vs, dos, scale=wl.scale, mask=wl.mask)
+        assert norm_err(np64(to_b(dq.cpu())[b:b + 1, hs]), ref["dq"]) < GTOL[torch.bfloat16]
+        assert norm_err(np64(to_b(dk.cpu())[b:b + 1, hk:hk + 1]), ref["dk"]) < GTOL[torch.bfloat16]
+        assert norm_err(np64(to_b(dv.cpu())[b:b + 1, hk:hk + 1]), ref["dv"]) < GTOL[torch.bfloat16]
