@@ -26,7 +26,7 @@ import threading
 import torch
 
 __all__ = ["load", "lib_path", "sdpa", "sdpa_relpos", "relpos_terms", "workspace_size", "relpos_fused",
-           "set_tuning", "dropout_mask", "sdpa_backward", "attention_weights", "SdpaError", "F32", "BF16", "F16",
+           "set_tuning", "dropout_mask", "sdpa_backward", "sdpa_relpos_backward", "attention_weights", "SdpaError", "F32", "BF16", "F16",
            "BSHD", "BHSD"]
 
 F32, BF16, F16 = 0, 1, 2
@@ -98,6 +98,10 @@ def load():
         lib.sdpa_bwd.restype = _I32
         lib.sdpa_bwd.argtypes = [_P] * 9 + [_I32] * 4 + [_I64] * 6 + \
             [_F, ctypes.POINTER(_Mask), _P, _F, _P, ctypes.c_size_t, _P]
+        lib.sdpa_relpos_bwd_workspace_size.restype = ctypes.c_size_t
+        lib.sdpa_relpos_bwd_workspace_size.argtypes = [_I64] * 5
+        lib.sdpa_relpos_bwd.restype = _I32
+        lib.sdpa_relpos_bwd.argtypes = [_P] * 11 + [_I32] * 4 + [_I64] * 5 + [_P, _P, _F, _P, ctypes.c_size_t, _P]
         lib.sdpa_attention_weights.restype = _I32
         lib.sdpa_attention_weights.argtypes = [_P, _P, _I32, _I32] + [_I64] * 6 + \
             [_F, ctypes.POINTER(_Mask), _P, _P, _F, _P, _P]
@@ -277,6 +281,39 @@ def sdpa_backward(q, k, v, o, dout, lse, *, layout="bhsd", scale=None, mask=None
                       ctypes.byref(ms), kp, rate, _ptr(ws), ws_n, _stream(stream))
     _check(st, "sdpa_bwd")
     return dq, dk, dv
+
+
+def sdpa_relpos_backward(q, k, v, o, dout, lse, rel_pos_h, rel_pos_w, grid, *, layout="bhsd", scale=None,
+                         grad_dtype=None, stream=None, workspace=None):
+    """(dq, dk, dv, d_rel_pos_h, d_rel_pos_w) of sdpa_relpos (tables' gradients in float32)."""
+    lib = load()
+    _need_gpu(q, k, v, o, dout, lse, rel_pos_h, rel_pos_w)
+    if q.dtype not in _DTYPE or k.dtype != q.dtype or v.dtype != q.dtype or dout.dtype != q.dtype:
+        raise ValueError("q, k, v and dout must share one dtype")
+    gh, gw = grid
+    if layout == "bhsd":
+        B, H, T, D = q.shape
+    else:
+        B, T, H, D = q.shape
+    gdt = q.dtype if grad_dtype is None else grad_dtype
+    dq = torch.empty(q.shape, dtype=gdt, device=q.device)
+    dk = torch.empty(k.shape, dtype=gdt, device=q.device)
+    dv = torch.empty(v.shape, dtype=gdt, device=q.device)
+    drh = torch.empty(tuple(rel_pos_h.shape), dtype=torch.float32, device=q.device)
+    drw = torch.empty(tuple(rel_pos_w.shape), dtype=torch.float32, device=q.device)
+    ws_n = lib.sdpa_relpos_bwd_workspace_size(B, H, gh, gw, D)
+    if ws_n == ctypes.c_size_t(-1).value:
+        raise ValueError("invalid sizes for sdpa_relpos_bwd")
+    ws = workspace
+    if ws is None or ws.numel() < ws_n:
+        ws = torch.empty(ws_n, dtype=torch.uint8, device=q.device)
+    sc = float("nan") if scale is None else float(scale)
+    st = lib.sdpa_relpos_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
+                             _ptr(drh), _ptr(drw), _DTYPE[q.dtype], _DTYPE[o.dtype], _DTYPE[gdt], _LAYOUT[layout],
+                             B, H, gh, gw, D, _ptr(rel_pos_h), _ptr(rel_pos_w), sc, _ptr(ws), ws.numel(),
+                             _stream(stream))
+    _check(st, "sdpa_relpos_bwd")
+    return dq, dk, dv, drh, drw
 
 
 def attention_weights(q, k, lse, *, layout="bhsd", scale=None, mask=None, dropout=None, stream=None):

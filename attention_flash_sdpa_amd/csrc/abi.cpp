@@ -413,6 +413,88 @@ int sdpa_bwd(const void* q, const void* k, const void* v, const void* o, const v
   return SDPA_OK;
 }
 
+// Workspace of sdpa_relpos_bwd: delta | term_h | term_w | dterm_h | dterm_w | dq_acc | group_h | group_w.
+size_t relpos_bwd_bytes(int64_t B, int64_t H, int64_t gh, int64_t gw, int64_t D, size_t* offs) {
+  const int64_t T = gh * gw;
+  const size_t sz[8] = {align256((size_t)B * H * T * 4),      align256((size_t)B * H * T * gh * 4),
+                        align256((size_t)B * H * T * gw * 4), align256((size_t)B * H * T * gh * 4),
+                        align256((size_t)B * H * T * gw * 4), align256((size_t)B * H * T * D * 4),
+                        align256((size_t)gh * gh * D * 4),    align256((size_t)gw * gw * D * 4)};
+  size_t tot = 0;
+  for (int a = 0; a < 8; ++a) {
+    if (offs) offs[a] = tot;
+    tot += sz[a];
+  }
+  return tot;
+}
+
+size_t sdpa_relpos_bwd_workspace_size(int64_t B, int64_t H, int64_t grid_h, int64_t grid_w, int64_t D) {
+  if (B <= 0 || H <= 0 || grid_h <= 0 || grid_w <= 0 || D <= 0) return (size_t)-1;
+  return relpos_bwd_bytes(B, H, grid_h, grid_w, D, nullptr);
+}
+
+int sdpa_relpos_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                    void* dq, void* dk, void* dv, float* d_rel_pos_h, float* d_rel_pos_w, int dtype, int o_dtype,
+                    int grad_dtype, int layout, int64_t B, int64_t H, int64_t grid_h, int64_t grid_w, int64_t D,
+                    const void* rel_pos_h, const void* rel_pos_w, float scale, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !d_rel_pos_h || !d_rel_pos_w || !rel_pos_h ||
+      !rel_pos_w)
+    return fail(SDPA_ERR_INVALID, "every tensor argument must be non-null");
+  if (grid_h <= 0 || grid_w <= 0) return fail(SDPA_ERR_INVALID, "grid sizes must be positive");
+  const int64_t T = grid_h * grid_w;
+  int st = check_sizes(B, H, H, T, T, D);
+  if (st) return st;
+  st = check_dtypes(dtype, o_dtype, layout, D);
+  if (st) return st;
+  if (grad_dtype != dtype && grad_dtype != SDPA_F32) return fail(SDPA_ERR_INVALID, "grad_dtype must equal dtype or be SDPA_F32");
+  sdpa::BwdParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.q = q; p.k = k; p.v = v; p.o = o; p.dout = dout; p.lse = lse; p.dq = dq; p.dk = dk; p.dv = dv;
+  p.dtype = dtype; p.o_dtype = o_dtype; p.grad_dtype = grad_dtype;
+  p.B = B; p.Hq = H; p.Hkv = H; p.Tq = T; p.Tkv = T; p.D = D;
+  set_strides(layout, H, T, D, &p.q_sb, &p.q_sh, &p.q_st);
+  set_strides(layout, H, T, D, &p.k_sb, &p.k_sh, &p.k_st);
+  p.scale = std::isnan(scale) ? (float)(1.0 / std::sqrt((double)D)) : scale;
+  if (!std::isfinite(p.scale)) return fail(SDPA_ERR_INVALID, "scale must be finite");
+  p.bias = sdpa::BIAS_RELPOS;
+  p.grid_h = (int)grid_h;
+  p.grid_w = (int)grid_w;
+  p.rel_h = rel_pos_h;
+  p.rel_w = rel_pos_w;
+  p.drel_h = d_rel_pos_h;
+  p.drel_w = d_rel_pos_w;
+  if (!sdpa::bwd_supports(p))
+    return fail(SDPA_ERR_UNSUPPORTED, "the rel-pos backward is built for bf16 / fp16 inputs, head_dim 32, 64 or 128, "
+                                      "grid_w >= 4 and grid_h + grid_w <= 128");
+  const void* ptrs[] = {q, k, v, o, dout, dq, dk, dv};
+  for (const void* x : ptrs)
+    if (!aligned16(x)) return fail(SDPA_ERR_UNSUPPORTED, "the backward pass needs 16-byte aligned tensors");
+  size_t off[8];
+  const size_t need = relpos_bwd_bytes(B, H, grid_h, grid_w, D, off);
+  if (!workspace || workspace_bytes < need)
+    return fail(SDPA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : (size_t)0);
+  char* ws = (char*)workspace;
+  p.delta = (float*)(ws + off[0]);
+  float* th = (float*)(ws + off[1]);
+  float* tw = (float*)(ws + off[2]);
+  p.term_h = th;
+  p.term_w = tw;
+  p.dterm_h = (float*)(ws + off[3]);
+  p.dterm_w = (float*)(ws + off[4]);
+  p.dq_acc = (float*)(ws + off[5]);
+  p.group_h = (float*)(ws + off[6]);
+  p.group_w = (float*)(ws + off[7]);
+  st = relpos_terms(q, dtype, layout, B, H, grid_h, grid_w, D, rel_pos_h, rel_pos_w, th, tw, stream);
+  if (st) return st;
+  hipError_t e = sdpa::launch_bwd(p, (hipStream_t)stream);
+  if (e == hipSuccess) e = sdpa::launch_relpos_bwd_tail(p, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(SDPA_ERR_HIP, "rel-pos backward launch failed: %s", hipGetErrorString(e));
+  g_last_kernel = "bwd_dkdv_kernel";
+  return SDPA_OK;
+}
+
 int sdpa_attention_weights(const void* q, const void* k, int dtype, int layout, int64_t B, int64_t Hq, int64_t Hkv,
                            int64_t Tq, int64_t Tkv, int64_t D, float scale, const sdpa_mask* mask, const float* lse,
                            const uint32_t* keep, float rate, float* weights, void* stream) {

@@ -48,7 +48,21 @@ typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 constexpr float kLog2e = 1.4426950408889634f;
 
-enum BMode { B_NONE = 0, B_INDEX = 1, B_TENSOR = 2 };
+enum BMode { B_NONE = 0, B_INDEX = 1, B_TENSOR = 2, B_RELPOS = 3 };
+
+// Rel-pos term rows held in LDS: grid_h + grid_w <= kMaxGT floats per query.
+constexpr int kMaxGT = 128;
+
+// Grid row and column of key `key` on a grid `gw` wide, from a known (row, col)
+// of an earlier key `base` (key - base < 4 gw is enough for the short loop).
+__device__ __forceinline__ void grid_step(int base_row, int base_col, int delta, int gw, int& row, int& col) {
+  row = base_row;
+  col = base_col + delta;
+  while (col >= gw) {
+    col -= gw;
+    ++row;
+  }
+}
 
 template <int D>
 struct BCfg {
@@ -189,7 +203,8 @@ __global__ __launch_bounds__(256, (D == 128 ? 1 : 2)) void bwd_dkdv_kernel(BwdPa
   constexpr int NLD = BQ * C::CH / 256;            // 16-byte pieces per thread per tile
   constexpr int SOFF = 4 * TQ;                     // [buf][lse2 | delta][BQ] fp32
   constexpr int KOFF = SOFF + 2 * 2 * BQ * 4;      // [buf][wave][BQ] keep words
-  constexpr int SMEM = KOFF + (DROP ? 2 * 4 * BQ * 4 : 0);
+  constexpr int TOFF = KOFF + (DROP ? 2 * 4 * BQ * 4 : 0);   // rel-pos: [buf][BQ][grid_h + grid_w] fp32
+  constexpr int SMEM = TOFF + (MODE == B_RELPOS ? 2 * BQ * kMaxGT * 4 : 0);
   __shared__ __attribute__((aligned(16))) char smem_raw[SMEM];
   lds_char* smem = (lds_char*)smem_raw;
 
@@ -204,6 +219,9 @@ __global__ __launch_bounds__(256, (D == 128 ? 1 : 2)) void bwd_dkdv_kernel(BwdPa
   const bool kvalid = key < p.Tkv;
   const int grp = (int)(p.Hq / p.Hkv);
   const float c2 = p.scale * kLog2e;
+  const int gh = p.grid_h, gw = p.grid_w, GT = gh + gw;
+  const int jrow = MODE == B_RELPOS ? (int)((kvalid ? key : 0) / gw) : 0;   // this lane's key on the grid
+  const int jcol = MODE == B_RELPOS ? (int)((kvalid ? key : 0) % gw) : 0;
 
   const E* kp = (const E*)p.k + b * p.k_sb + hk * p.k_sh;
   const E* vp = (const E*)p.v + b * p.k_sb + hk * p.k_sh;
@@ -253,7 +271,7 @@ __global__ __launch_bounds__(256, (D == 128 ? 1 : 2)) void bwd_dkdv_kernel(BwdPa
       kwv = (qi < p.Tq && w < p.keep_words) ? p.keep[(rbase + qi) * p.keep_words + w] : 0u;
     }
   };
-  auto lstore = [&](int buf) {
+  auto lstore = [&](int buf, int it) {
     lds_char* qt = smem + buf * 2 * TQ;
     lds_char* dt = qt + TQ;
 #pragma unroll
@@ -265,6 +283,18 @@ __global__ __launch_bounds__(256, (D == 128 ? 1 : 2)) void bwd_dkdv_kernel(BwdPa
     }
     if (tid < 2 * BQ) lds_store(smem + SOFF + buf * 2 * BQ * 4 + tid * 4, sval);
     if (DROP) lds_store(smem + KOFF + buf * 4 * BQ * 4 + tid * 4, kwv);
+    if (MODE == B_RELPOS) {          // term rows of the tile's queries: [q][term_h row | term_w row]
+      const int64_t hq = hk * grp + it / nqt;
+      const int64_t q0 = (qt0 + it % nqt) * BQ;
+      const int64_t rbase = (b * p.Hq + hq) * p.Tq;
+      lds_char* tl = smem + TOFF + buf * BQ * kMaxGT * 4;
+      for (int e = tid; e < BQ * GT; e += 256) {
+        const int q = e / GT, c = e % GT;
+        float v = 0.0f;
+        if (q0 + q < p.Tq) v = c < gh ? p.term_h[(rbase + q0 + q) * gh + c] : p.term_w[(rbase + q0 + q) * gw + c - gh];
+        lds_store(tl + (q * GT + c) * 4, v);
+      }
+    }
   };
 
   f32x16_e dvT[C::DB], dkT[C::DB];
@@ -275,7 +305,7 @@ __global__ __launch_bounds__(256, (D == 128 ? 1 : 2)) void bwd_dkdv_kernel(BwdPa
   }
   if (niter > 0) {
     gload(0);
-    lstore(0);
+    lstore(0, 0);
   }
   __syncthreads();
 
@@ -290,6 +320,7 @@ __global__ __launch_bounds__(256, (D == 128 ? 1 : 2)) void bwd_dkdv_kernel(BwdPa
     const lds_char* l2s = smem + SOFF + buf * 2 * BQ * 4;
     const lds_char* dls = l2s + BQ * 4;
     const lds_char* kws = smem + KOFF + buf * 4 * BQ * 4 + wave * BQ * 4;
+    const lds_char* tls = smem + TOFF + buf * BQ * kMaxGT * 4;
 #pragma unroll 1
     for (int s = 0; s < 2; ++s) {
       const int64_t qa = q0 + 32 * s;
@@ -333,6 +364,12 @@ __global__ __launch_bounds__(256, (D == 128 ? 1 : 2)) void bwd_dkdv_kernel(BwdPa
         if (MODE == B_TENSOR) {
           if (ok && qq < p.Tq) xb += mask_value(p, b, hq, qq, key) * kLog2e;
         }
+        if (MODE == B_RELPOS) {      // term_h[q, row(key)] + term_w[q, col(key)] from the staged rows
+          const int qo = 32 * s + 8 * (r / 4) + 4 * g + (r % 4);
+          const float th = lds_load<float>(tls + (qo * GT + jrow) * 4);
+          const float tw = lds_load<float>(tls + (qo * GT + gh + jcol) * 4);
+          xb += (th + tw) * kLog2e;
+        }
         const float pr = ok ? __builtin_amdgcn_exp2f(fmaf(sacc[r], c2, xb)) : 0.0f;
         float dw = dpacc[r];
         if (DROP) {
@@ -355,7 +392,7 @@ __global__ __launch_bounds__(256, (D == 128 ? 1 : 2)) void bwd_dkdv_kernel(BwdPa
         }
       }
     }
-    if (more) lstore(buf ^ 1);
+    if (more) lstore(buf ^ 1, it + 1);
     __syncthreads();
   }
 
@@ -387,7 +424,9 @@ __global__ __launch_bounds__(256, (D == 128 ? 1 : 2)) void bwd_dq_kernel(BwdPara
   constexpr int BN = 64;                           // keys per staged tile
   constexpr int TK = BN * C::PITCH;
   constexpr int NLD = BN * C::CH / 256;
-  __shared__ __attribute__((aligned(16))) char smem_raw[4 * TK];   // [buf][K | V]
+  // [buf][K | V] tiles; rel-pos: then the per-query sums of dS, [128 q][grid_h + grid_w] fp32
+  constexpr int DOFF = 4 * TK;
+  __shared__ __attribute__((aligned(16))) char smem_raw[DOFF + (MODE == B_RELPOS ? 128 * kMaxGT * 4 : 0)];
   lds_char* smem = (lds_char*)smem_raw;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -422,6 +461,18 @@ __global__ __launch_bounds__(256, (D == 128 ? 1 : 2)) void bwd_dq_kernel(BwdPara
   }
   const int64_t t0 = lo / BN;
   const int ntiles = hi > lo ? (int)((hi - t0 * BN + BN - 1) / BN) : 0;
+
+  const int gh = p.grid_h, gw = p.grid_w, GT = gh + gw;
+  const float* thr = nullptr;
+  const float* twr = nullptr;
+  __attribute__((address_space(3))) float* dts = nullptr;
+  if (MODE == B_RELPOS) {
+    thr = p.term_h + (qvalid ? srow : 0) * gh;
+    twr = p.term_w + (qvalid ? srow : 0) * gw;
+    dts = (__attribute__((address_space(3))) float*)(smem + DOFF);
+    for (int e = tid; e < 128 * GT; e += 256) dts[e] = 0.0f;
+    dts += (32 * wave + nl) * GT;     // this lane's query row
+  }
 
   const E* kp = (const E*)p.k + b * p.k_sb + hk * p.k_sh;
   const E* vp = (const E*)p.v + b * p.k_sb + hk * p.k_sh;
@@ -485,12 +536,29 @@ __global__ __launch_bounds__(256, (D == 128 ? 1 : 2)) void bwd_dq_kernel(BwdPara
           dpacc = mfma32(ld_row<E, D>(vs, 32 * kb + nl, c, g), of[c], dpacc);
         }
         float ds[16];
+        // rel-pos: grid (row, col) of the first key of each group of 4 this lane holds
+        int grow[4] = {0, 0, 0, 0}, gcol[4] = {0, 0, 0, 0};
+        if (MODE == B_RELPOS) {
+          const int64_t kbase = k0 + 32 * kb;
+          const int brow = (int)(kbase / gw), bcol = (int)(kbase % gw);
+#pragma unroll
+          for (int a = 0; a < 4; ++a) grid_step(brow, bcol, 8 * a + 4 * g, gw, grow[a], gcol[a]);
+        }
+        int krow[16], kcol[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          if (MODE == B_RELPOS) grid_step(grow[r / 4], gcol[r / 4], r % 4, gw, krow[r], kcol[r]);
+          else krow[r] = kcol[r] = 0;
+        }
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int kofs = 8 * (r / 4) + 4 * g + (r % 4);
           const int64_t key = k0 + 32 * kb + kofs;
           bool ok = key < p.Tkv;
           float xb = -l2;
+          if (MODE == B_RELPOS) {
+            if (ok && qvalid) xb += (thr[krow[r]] + twr[kcol[r]]) * kLog2e;
+          }
           if (MODE == B_INDEX) {
             ok = ok && key <= qrow + p.offset;
             if (p.bias == BIAS_SLIDING) ok = ok && key > qrow + p.offset - p.window;
@@ -502,6 +570,23 @@ __global__ __launch_bounds__(256, (D == 128 ? 1 : 2)) void bwd_dq_kernel(BwdPara
           float dw = dpacc[r];
           if (DROP) dw = ((kw[kb] >> kofs) & 1u) ? dw * p.keep_scale : 0.0f;
           ds[r] = pr * (dw - dl);
+        }
+        if (MODE == B_RELPOS && qvalid) {
+          // dterm_h[q, row] and dterm_w[q, col] collect dS.  The two lane halves hold the
+          // same query, so they add in turn: no two lanes of one instruction share an
+          // address, and the order of the additions is fixed.
+#pragma unroll
+          for (int half = 0; half < 2; ++half) {
+            if (g == half) {
+#pragma unroll
+              for (int r = 0; r < 16; ++r) {
+                if (k0 + 32 * kb + 8 * (r / 4) + 4 * g + (r % 4) < p.Tkv) {
+                  dts[krow[r]] += ds[r];
+                  dts[gh + kcol[r]] += ds[r];
+                }
+              }
+            }
+          }
         }
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
@@ -516,6 +601,29 @@ __global__ __launch_bounds__(256, (D == 128 ? 1 : 2)) void bwd_dq_kernel(BwdPara
     __syncthreads();
   }
 
+  if (MODE == B_RELPOS) {
+    // scale * dS . K in fp32 (the tables' part is added by the tail kernel) and the
+    // per-query dS sums (each lane half writes every other entry of its query row)
+    __syncthreads();
+    if (qvalid) {
+      float* acc = p.dq_acc + srow * p.D;
+#pragma unroll
+      for (int nb = 0; nb < C::DB; ++nb)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          float a[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) a[e] = dqT[nb][4 * i4 + e];
+          store4(acc + 32 * nb + 8 * i4 + 4 * g, a, p.scale);
+        }
+      for (int c = g; c < GT; c += 2) {
+        const float v = dts[c];
+        if (c < gh) p.dterm_h[srow * gh + c] = v;
+        else p.dterm_w[srow * gw + c - gh] = v;
+      }
+    }
+    return;
+  }
   // dQ^T: lane = query, registers = head dims 32 nb + 8 (r / 4) + 4 g + r % 4.
   if (qvalid) {
     G* dqp = (G*)p.dq + qoff;
@@ -539,6 +647,7 @@ int bmode_of(const BwdParams& p) {
     case BIAS_SLIDING: return B_INDEX;
     case BIAS_ADDITIVE:
     case BIAS_BOOL: return B_TENSOR;
+    case BIAS_RELPOS: return B_RELPOS;
     default: return -1;
   }
 }
@@ -557,6 +666,7 @@ void launch_modes(const BwdParams& p, hipStream_t s) {
   switch (bmode_of(p)) {
     case B_NONE: drop ? launch_main<E, D, B_NONE, true, G>(p, s) : launch_main<E, D, B_NONE, false, G>(p, s); break;
     case B_INDEX: drop ? launch_main<E, D, B_INDEX, true, G>(p, s) : launch_main<E, D, B_INDEX, false, G>(p, s); break;
+    case B_RELPOS: launch_main<E, D, B_RELPOS, false, G>(p, s); break;
     default: drop ? launch_main<E, D, B_TENSOR, true, G>(p, s) : launch_main<E, D, B_TENSOR, false, G>(p, s); break;
   }
 }
@@ -584,6 +694,9 @@ bool bwd_supports(const BwdParams& p) {
   if (p.dtype != 1 && p.dtype != 2) return false;
   if (p.D != 32 && p.D != 64 && p.D != 128) return false;
   if (bmode_of(p) < 0) return false;
+  if (p.bias == BIAS_RELPOS && (p.keep || p.grid_w < 4 || p.grid_h < 1 || p.grid_h + p.grid_w > kMaxGT ||
+                                p.B * p.Hq > 65535))
+    return false;
   if (p.B * p.Hq * p.Tq * (p.D / 8) / 256 + 1 > INT32_MAX) return false;
   return true;
 }

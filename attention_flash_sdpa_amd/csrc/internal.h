@@ -75,6 +75,21 @@ struct BwdParams {
   const uint32_t* keep;
   int64_t keep_words;
   float keep_scale;
+  // Decomposed rel-pos (bias = BIAS_RELPOS): the forward terms, the per-query
+  // sums of dS over each grid row / column they receive, an fp32 copy of
+  // scale * dS . K (the tables' part is added after), and the tables.
+  const float* term_h;        // [B, Hq, Tq, grid_h]
+  const float* term_w;        // [B, Hq, Tq, grid_w]
+  float* dterm_h;             // [B, Hq, Tq, grid_h]
+  float* dterm_w;             // [B, Hq, Tq, grid_w]
+  float* dq_acc;              // [B, Hq, Tq, D] fp32
+  const void* rel_h;          // [2 grid_h - 1, D] in dtype
+  const void* rel_w;          // [2 grid_w - 1, D]
+  float* drel_h;              // [2 grid_h - 1, D] fp32 output
+  float* drel_w;              // [2 grid_w - 1, D] fp32 output
+  float* group_h;             // [grid_h (row r), grid_h (y), D] fp32 scratch
+  float* group_w;             // [grid_w (column c), grid_w (x), D] fp32 scratch
+  int grid_h, grid_w;
 };
 
 // Dropout keep bits (Philox4x32-10): word [b, h, i, j / 32], bit j % 32.
@@ -125,6 +140,8 @@ hipError_t launch_dropout_mask(const DropoutParams& p, hipStream_t s);
 // delta, then dK / dV (one workgroup per key block), then dQ (one per query block).
 bool bwd_supports(const BwdParams& p);
 hipError_t launch_bwd(const BwdParams& p, hipStream_t s);
+// Rel-pos tail of the backward: dq = dq_acc + the tables' part, d rel_pos_h / w.
+hipError_t launch_relpos_bwd_tail(const BwdParams& p, hipStream_t s);
 // Attention weights [B, Hq, Tq, Tkv] fp32 from the forward pass's lse (any dtype, head_dim <= 128).
 hipError_t launch_attn_weights(const FwdParams& p, float* weights, hipStream_t s);
 

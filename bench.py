@@ -223,6 +223,67 @@ def cpu_baseline(wl, x, budget_s=20.0):
                       f"{t_total:.1f} s wall"}
 
 
+def bench_backward(fa, wl, x, g, args):
+    """One sdpa_backward call per step: delta, dK/dV and dQ kernels.  Algorithmic
+    FLOPs are those of the five products per allowed pair (S = Q.K^T, dW = dO.V^T,
+    dV, dK, dQ: 10 * D), the usual accounting of 2.5x the forward pass."""
+    import statistics
+    import numpy as np
+    import torch
+    if wl.relpos:
+        print("bench.py: --pass backward takes unmasked or index-masked workloads", file=sys.stderr)
+        sys.exit(2)
+    rng = np.random.default_rng(1)
+    do = torch.from_numpy(rng.standard_normal(tuple(x["q"].shape), dtype=np.float32)).to(g["q"].dtype).cuda()
+    o, lse = fa.sdpa(g["q"], g["k"], g["v"], layout=wl.layout, scale=wl.scale, mask=wl.mask, return_lse=True)
+    call = lambda: fa.sdpa_backward(g["q"], g["k"], g["v"], o, do, lse, layout=wl.layout, scale=wl.scale,
+                                    mask=wl.mask)
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        call()
+    torch.cuda.synchronize()
+    sec = (time.perf_counter() - t0) / args.steps
+    s = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ts = []
+    for _ in range(5):
+        torch.cuda.synchronize()
+        _hold_stream(2.0 + 1.5 * args.steps)
+        ev[0].record(s)
+        for _ in range(args.steps):
+            call()
+        ev[1].record(s)
+        ev[1].synchronize()
+        ts.append(ev[0].elapsed_time(ev[1]) / args.steps)
+    call_ms = statistics.median(ts)
+    pairs = allowed_pairs(wl) * wl.B * wl.Hq
+    flops = 10 * wl.D * pairs
+    achieved = flops / (call_ms * 1e-3) / 1e12
+    es = 2
+    nbytes = es * wl.D * (4 * wl.B * wl.Hq * wl.Tq + 4 * wl.B * wl.Hkv * wl.Tkv) + 8 * wl.B * wl.Hq * wl.Tq
+    line = {
+        "metric": "attention backward TFLOP/s (10 D per allowed pair)",
+        "value": round(flops / sec / 1e12, 3),
+        "unit": "TFLOP/s",
+        "pct_of_bf16_peak": round(100.0 * flops / sec / 1e12 / MFMA_BF16_PEAK_TFLOPS, 2),
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(sec * 1e3, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": {"bf16": "bf16", "fp16": "f16"}.get(wl.dtype, "f32"), "data": "synthetic",
+        "config": {"workload": wl.name + "_backward", "description": wl.description + ", backward pass",
+                   "layout": wl.layout, "B": wl.B, "Hq": wl.Hq, "Hkv": wl.Hkv, "Tq": wl.Tq, "Tkv": wl.Tkv,
+                   "head_dim": wl.D, "mask": wl.mask, "scale": wl.scale, "flop_per_step": flops},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel": "bwd_delta_kernel + bwd_dkdv_kernel + bwd_dq_kernel (one call)",
+                     "kernel_ms": round(call_ms, 5), "flop_per_launch": flops,
+                     "algorithmic_bytes_per_launch": nbytes},
+    }
+    print(json.dumps(line))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -236,6 +297,9 @@ def main():
     ap.add_argument("--route", choices=["relpos", "additive"], default="relpos",
                     help="rel-pos workloads: 'additive' times the bias materialised as a [B, H, T, T] "
                          "additive mask in the input dtype (formed before timing) instead of the fused terms")
+    ap.add_argument("--pass", dest="pass_", choices=["forward", "backward"], default="forward",
+                    help="'backward' times one sdpa_backward call per step (dQ, dK, dV from the forward "
+                         "pass's O and lse, formed before timing); index-mask and unmasked workloads only")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB per step (counter calibration)")
     args = ap.parse_args()
@@ -263,6 +327,9 @@ def main():
         wl = wl.with_(dtype=args.dtype)
     x = workloads.generate(wl, seed=0)
     g = {k: t.cuda() for k, t in x.items()}
+    if args.pass_ == "backward":
+        bench_backward(fa, wl, x, g, args)
+        return
     if wl.relpos:
         n = fa.workspace_size(wl.B, wl.Hq, wl.Hkv, wl.Tq, wl.Tkv, wl.D, True, wl.grid)
         g["ws"] = torch.empty(n, dtype=torch.uint8, device="cuda")

@@ -268,6 +268,33 @@ int sdpa_bwd(const void* q, const void* k, const void* v, const void* o, const v
              const sdpa_mask* mask, const uint32_t* keep, float rate, void* workspace, size_t workspace_bytes,
              void* stream);
 
+/* Bytes of device workspace sdpa_relpos_bwd needs ((size_t)-1 for invalid sizes). */
+size_t sdpa_relpos_bwd_workspace_size(int64_t B, int64_t H, int64_t grid_h, int64_t grid_w, int64_t D);
+
+/*
+ * Gradients of the rel-pos attention of sdpa_relpos_fwd ([mlx-examples issue
+ * 1451], body: SAM's add_decomposed_rel_pos; [Candle PR 3280], Key Changes:
+ * term_h / term_w): as sdpa_bwd for the bias B[i, j] = term_h[i, row(j)] +
+ * term_w[i, col(j)], which also depends on q and on the tables:
+ *   dq_i += sum_y dT_h[i, y] rel_pos_h[row(i) - y + grid_h - 1]
+ *         + sum_x dT_w[i, x] rel_pos_w[col(i) - x + grid_w - 1],
+ *   d_rel_pos_h[t] = sum over (b, h, i, y) with row(i) - y + grid_h - 1 = t of dT_h[i, y] q_i
+ *   (d_rel_pos_w alike), with dT_h[i, y] the sum of dS[i, j] over the keys j of
+ *   grid row y and dT_w[i, x] over grid column x.
+ *   q .. lse, dq, dk, dv   as in sdpa_bwd with Hq = Hkv = H and Tq = Tkv = grid_h * grid_w.
+ *   rel_pos_h, rel_pos_w   the tables of the forward call, in dtype.
+ *   d_rel_pos_h            [2 grid_h - 1, D] fp32 output; d_rel_pos_w [2 grid_w - 1, D].
+ *   workspace              at least sdpa_relpos_bwd_workspace_size(B, H, grid_h, grid_w, D) bytes.
+ * Built for bf16 / fp16, head_dim 32, 64 or 128, grid_w >= 4 and grid_h + grid_w
+ * <= 128 (SAM's 14 x 14 windows and 64 x 64 global grid), no dropout.
+ * Deterministic: no atomics.
+ */
+int sdpa_relpos_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                    void* dq, void* dk, void* dv, float* d_rel_pos_h, float* d_rel_pos_w, int dtype, int o_dtype,
+                    int grad_dtype, int layout, int64_t B, int64_t H, int64_t grid_h, int64_t grid_w, int64_t D,
+                    const void* rel_pos_h, const void* rel_pos_w, float scale, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
 /*
  * The attention weights (`:return_attention_weights`): weights[b, h, i, j] =
  * exp(scale * q_i . k_j + bias_ij - lse_i) * Z_ij, i.e. the weights that

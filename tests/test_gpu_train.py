@@ -273,3 +273,87 @@ def test_backward_full_size_sampled_heads(gpu, name):
         assert norm_err(np64(to_b(dq.cpu())[b:b + 1, hs]), ref["dq"]) < GTOL[torch.bfloat16]
         assert norm_err(np64(to_b(dk.cpu())[b:b + 1, hk:hk + 1]), ref["dk"]) < GTOL[torch.bfloat16]
         assert norm_err(np64(to_b(dv.cpu())[b:b + 1, hk:hk + 1]), ref["dv"]) < GTOL[torch.bfloat16]
+
+
+# ---------------------------------------------------------- rel-pos backward --
+RELPOS_BWD_CASES = [
+    # dtype, layout, B, H, grid, D, grad fp32
+    ("bf16", "bhsd", 1, 2, (16, 64), 64, False),      # SAM global rows (64 wide), 16 of them
+    ("bf16", "bshd", 2, 3, (14, 14), 64, False),      # SAM windows
+    ("fp16", "bhsd", 1, 2, (14, 14), 64, True),
+    ("bf16", "bhsd", 1, 2, (8, 8), 32, True),
+    ("bf16", "bhsd", 1, 1, (5, 27), 128, False),      # ragged: T = 135
+]
+
+
+@pytest.mark.parametrize("case", RELPOS_BWD_CASES,
+                         ids=[f"{c[0]}-{c[1]}-B{c[2]}H{c[3]}-{c[4][0]}x{c[4][1]}-D{c[5]}{'-g32' if c[6] else ''}"
+                              for c in RELPOS_BWD_CASES])
+def test_relpos_backward_matches_oracle(gpu, case):
+    dts, layout, B, H, grid, D, g32 = case
+    dt = DT[dts]
+    gh, gw = grid
+    T = gh * gw
+    rng = np.random.default_rng(37)
+    q, k, v, do = (draw(rng, shp(layout, B, H, T, D), dt) for _ in range(4))
+    rh = (0.3 * draw(rng, (2 * gh - 1, D), torch.float32)).to(dt)
+    rw = (0.3 * draw(rng, (2 * gw - 1, D), torch.float32)).to(dt)
+    scale = 1.0 / np.sqrt(D)
+    rp = {"rel_pos_h": np64(rh), "rel_pos_w": np64(rw), "grid": grid}
+    fwd = st.sdpa_train_fwd(np64(q), np64(k), np64(v), layout=layout, scale=scale, rel_pos=rp)
+    o = torch.from_numpy(np.ascontiguousarray(fwd["o"], dtype=np.float32)).to(dt)
+    lse = torch.from_numpy(fwd["lse"].astype(np.float32))
+    dq, dk, dv, drh, drw = gpu.sdpa_relpos_backward(q.cuda(), k.cuda(), v.cuda(), o.cuda(), do.cuda(), lse.cuda(),
+                                                    rh.cuda(), rw.cuda(), grid, layout=layout, scale=scale,
+                                                    grad_dtype=torch.float32 if g32 else None)
+    torch.cuda.synchronize()
+    ref = st.sdpa_bwd(np64(q), np64(k), np64(v), np64(do), layout=layout, scale=scale, rel_pos=rp)
+    for name, got in (("dq", dq), ("dk", dk), ("dv", dv), ("drel_pos_h", drh), ("drel_pos_w", drw)):
+        e = norm_err(np64(got), ref[name])
+        assert e < GTOL[dt], (name, e)
+
+
+def test_relpos_backward_after_library_forward(gpu):
+    """The library's own forward (fused terms) feeding its backward, SAM window shape."""
+    rng = np.random.default_rng(38)
+    B, H, grid, D = 2, 2, (14, 14), 64
+    T = grid[0] * grid[1]
+    q, k, v, do = (draw(rng, (B, H, T, D), torch.bfloat16) for _ in range(4))
+    rh = (0.3 * draw(rng, (27, D), torch.float32)).to(torch.bfloat16)
+    rw = (0.3 * draw(rng, (27, D), torch.float32)).to(torch.bfloat16)
+    g = [t.cuda() for t in (q, k, v, do, rh, rw)]
+    o, lse = gpu.sdpa_relpos(g[0], g[1], g[2], g[4], g[5], grid, return_lse=True)
+    out = gpu.sdpa_relpos_backward(g[0], g[1], g[2], o, g[3], lse, g[4], g[5], grid)
+    again = gpu.sdpa_relpos_backward(g[0], g[1], g[2], o, g[3], lse, g[4], g[5], grid)
+    torch.cuda.synchronize()
+    for x, y in zip(out, again):
+        assert torch.equal(x, y)                     # deterministic
+    rp = {"rel_pos_h": np64(rh), "rel_pos_w": np64(rw), "grid": grid}
+    ref = st.sdpa_bwd(np64(q), np64(k), np64(v), np64(do), rel_pos=rp)
+    for name, got in zip(("dq", "dk", "dv", "drel_pos_h", "drel_pos_w"), out):
+        assert norm_err(np64(got), ref[name]) < GTOL[torch.bfloat16], name
+
+
+@pytest.mark.slow
+def test_relpos_backward_full_size_sampled_heads(gpu):
+    """SAM ViT-B global attention at full size; dq, dk, dv of two heads against the oracle."""
+    import workloads
+    wl = workloads.WORKLOADS["sam_global_relpos"]
+    x = workloads.generate(wl, seed=0)
+    rng = np.random.default_rng(39)
+    do = draw(rng, tuple(x["q"].shape), torch.bfloat16)
+    g = {k: v.cuda() for k, v in x.items()}
+    o, lse = gpu.sdpa_relpos(g["q"], g["k"], g["v"], g["rel_pos_h"], g["rel_pos_w"], wl.grid, scale=wl.scale,
+                             return_lse=True)
+    dq, dk, dv, drh, drw = gpu.sdpa_relpos_backward(g["q"], g["k"], g["v"], o, do.cuda(), lse, g["rel_pos_h"],
+                                                    g["rel_pos_w"], wl.grid, scale=wl.scale)
+    torch.cuda.synchronize()
+    assert torch.all(torch.isfinite(drh)) and torch.all(torch.isfinite(drw))
+    rp = {"rel_pos_h": np64(x["rel_pos_h"]), "rel_pos_w": np64(x["rel_pos_w"]), "grid": wl.grid}
+    for h in (0, wl.Hq - 1):
+        sl = slice(h, h + 1)
+        ref = st.sdpa_bwd(np64(x["q"][:, sl]), np64(x["k"][:, sl]), np64(x["v"][:, sl]), np64(do[:, sl]),
+                          scale=wl.scale, rel_pos=rp)
+        assert norm_err(np64(dq[:, sl]), ref["dq"]) < GTOL[torch.bfloat16]
+        assert norm_err(np64(dk[:, sl]), ref["dk"]) < GTOL[torch.bfloat16]
+        assert norm_err(np64(dv[:, sl]), ref["dv"]) < GTOL[torch.bfloat16]
