@@ -419,7 +419,8 @@ size_t relpos_bwd_bytes(int64_t B, int64_t H, int64_t gh, int64_t gw, int64_t D,
   const size_t sz[8] = {align256((size_t)B * H * T * 4),      align256((size_t)B * H * T * gh * 4),
                         align256((size_t)B * H * T * gw * 4), align256((size_t)B * H * T * gh * 4),
                         align256((size_t)B * H * T * gw * 4), align256((size_t)B * H * T * D * 4),
-                        align256((size_t)gh * gh * D * 4),    align256((size_t)gw * gw * D * 4)};
+                        align256((size_t)sdpa::relpos_group_splits(B * H * gw, gh) * gh * gh * D * 4),
+                        align256((size_t)sdpa::relpos_group_splits(B * H * gh, gw) * gw * gw * D * 4)};
   size_t tot = 0;
   for (int a = 0; a < 8; ++a) {
     if (offs) offs[a] = tot;
@@ -486,6 +487,8 @@ int sdpa_relpos_bwd(const void* q, const void* k, const void* v, const void* o, 
   p.dq_acc = (float*)(ws + off[5]);
   p.group_h = (float*)(ws + off[6]);
   p.group_w = (float*)(ws + off[7]);
+  p.split_h = sdpa::relpos_group_splits(B * H * grid_w, grid_h);
+  p.split_w = sdpa::relpos_group_splits(B * H * grid_h, grid_w);
   st = relpos_terms(q, dtype, layout, B, H, grid_h, grid_w, D, rel_pos_h, rel_pos_w, th, tw, stream);
   if (st) return st;
   hipError_t e = sdpa::launch_bwd(p, (hipStream_t)stream);

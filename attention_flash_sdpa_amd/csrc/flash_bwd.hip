@@ -48,7 +48,8 @@ typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 constexpr float kLog2e = 1.4426950408889634f;
 
-enum BMode { B_NONE = 0, B_INDEX = 1, B_TENSOR = 2, B_RELPOS = 3 };
+// B_RELPOS64: rel-pos on a 64-wide grid, where a 64-key tile is one grid row.
+enum BMode { B_NONE = 0, B_INDEX = 1, B_TENSOR = 2, B_RELPOS = 3, B_RELPOS64 = 4 };
 
 // Rel-pos term rows held in LDS: grid_h + grid_w <= kMaxGT floats per query.
 constexpr int kMaxGT = 128;
@@ -150,6 +151,12 @@ __device__ __forceinline__ float lse2_of(const BwdParams& p, int64_t row, bool v
   return l == -INFINITY ? INFINITY : l * kLog2e;
 }
 
+// Sum of the value held by lane l and lane l ^ 32 (v_permlane32_swap).
+__device__ __forceinline__ float halves_sum(float v) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 template <typename G>
 __device__ __forceinline__ void store4(G* dst, const float* v, float s) {
   if constexpr (sizeof(G) == 4) {
@@ -203,8 +210,11 @@ __global__ __launch_bounds__(256, (D == 128 ? 1 : 2)) void bwd_dkdv_kernel(BwdPa
   constexpr int NLD = BQ * C::CH / 256;            // 16-byte pieces per thread per tile
   constexpr int SOFF = 4 * TQ;                     // [buf][lse2 | delta][BQ] fp32
   constexpr int KOFF = SOFF + 2 * 2 * BQ * 4;      // [buf][wave][BQ] keep words
-  constexpr int TOFF = KOFF + (DROP ? 2 * 4 * BQ * 4 : 0);   // rel-pos: [buf][BQ][grid_h + grid_w] fp32
-  constexpr int SMEM = TOFF + (MODE == B_RELPOS ? 2 * BQ * kMaxGT * 4 : 0);
+  // rel-pos: [buf][BQ][grid_h + grid_w] fp32 term rows; on a 64-wide grid only
+  // the 64 columns and the two grid rows of the workgroup's keys: [buf][BQ][64], [BQ][2]
+  constexpr int TOFF = KOFF + (DROP ? 2 * 4 * BQ * 4 : 0);
+  constexpr int TBUF = MODE == B_RELPOS ? BQ * kMaxGT * 4 : (MODE == B_RELPOS64 ? BQ * 66 * 4 : 0);
+  constexpr int SMEM = TOFF + 2 * TBUF;
   __shared__ __attribute__((aligned(16))) char smem_raw[SMEM];
   lds_char* smem = (lds_char*)smem_raw;
 
@@ -287,13 +297,46 @@ __global__ __launch_bounds__(256, (D == 128 ? 1 : 2)) void bwd_dkdv_kernel(BwdPa
       const int64_t hq = hk * grp + it / nqt;
       const int64_t q0 = (qt0 + it % nqt) * BQ;
       const int64_t rbase = (b * p.Hq + hq) * p.Tq;
-      lds_char* tl = smem + TOFF + buf * BQ * kMaxGT * 4;
-      for (int e = tid; e < BQ * GT; e += 256) {
-        const int q = e / GT, c = e % GT;
-        float v = 0.0f;
-        if (q0 + q < p.Tq) v = c < gh ? p.term_h[(rbase + q0 + q) * gh + c] : p.term_w[(rbase + q0 + q) * gw + c - gh];
-        lds_store(tl + (q * GT + c) * 4, v);
+      lds_char* tl = smem + TOFF + buf * TBUF;
+      for (int e0 = 0; e0 < BQ * GT; e0 += 6 * 256) {    // 6 loads in flight per lane, then the stores
+        float v[6];
+#pragma unroll
+        for (int u = 0; u < 6; ++u) {
+          const int e = e0 + tid + 256 * u, q = e / GT, c = e % GT;
+          v[u] = 0.0f;
+          if (e < BQ * GT && q0 + q < p.Tq)
+            v[u] = c < gh ? p.term_h[(rbase + q0 + q) * gh + c] : p.term_w[(rbase + q0 + q) * gw + c - gh];
+        }
+#pragma unroll
+        for (int u = 0; u < 6; ++u) {
+          const int e = e0 + tid + 256 * u;
+          if (e < BQ * GT) lds_store(tl + e * 4, v[u]);
+        }
       }
+    }
+    if (MODE == B_RELPOS64) {
+      // [q][64] term_w rows (one contiguous 16 KB range: four 16-byte loads per
+      // thread, all in flight), then [q][2] term_h at the 2 grid rows of the keys
+      const int64_t hq = hk * grp + it / nqt;
+      const int64_t q0 = (qt0 + it % nqt) * BQ;
+      const int64_t rbase = (b * p.Hq + hq) * p.Tq;
+      const int64_t row0 = kb0 / 64;
+      lds_char* tl = smem + TOFF + buf * TBUF;
+      const float* src = p.term_w + (rbase + q0) * 64;
+      f32x4 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int e = 4 * (tid + 256 * u);              // float index in the [64][64] block
+        v[u] = (q0 + e / 64 < p.Tq) ? *(const f32x4*)(src + e) : (f32x4){};
+      }
+      float hv = 0.0f;
+      if (tid < 2 * BQ) {
+        const int q = tid >> 1, c = tid & 1;
+        if (q0 + q < p.Tq && row0 + c < gh) hv = p.term_h[(rbase + q0 + q) * gh + row0 + c];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) lds_store(tl + 16 * (tid + 256 * u), v[u]);
+      if (tid < 2 * BQ) lds_store(tl + BQ * 64 * 4 + tid * 4, hv);
     }
   };
 
@@ -320,7 +363,7 @@ __global__ __launch_bounds__(256, (D == 128 ? 1 : 2)) void bwd_dkdv_kernel(BwdPa
     const lds_char* l2s = smem + SOFF + buf * 2 * BQ * 4;
     const lds_char* dls = l2s + BQ * 4;
     const lds_char* kws = smem + KOFF + buf * 4 * BQ * 4 + wave * BQ * 4;
-    const lds_char* tls = smem + TOFF + buf * BQ * kMaxGT * 4;
+    const lds_char* tls = smem + TOFF + buf * TBUF;
 #pragma unroll 1
     for (int s = 0; s < 2; ++s) {
       const int64_t qa = q0 + 32 * s;
@@ -368,6 +411,12 @@ __global__ __launch_bounds__(256, (D == 128 ? 1 : 2)) void bwd_dkdv_kernel(BwdPa
           const int qo = 32 * s + 8 * (r / 4) + 4 * g + (r % 4);
           const float th = lds_load<float>(tls + (qo * GT + jrow) * 4);
           const float tw = lds_load<float>(tls + (qo * GT + gh + jcol) * 4);
+          xb += (th + tw) * kLog2e;
+        }
+        if (MODE == B_RELPOS64) {    // the wave's keys lie in grid row kb0 / 64 + wave / 2
+          const int qo = 32 * s + 8 * (r / 4) + 4 * g + (r % 4);
+          const float th = lds_load<float>(tls + (BQ * 64 + qo * 2 + (wave >> 1)) * 4);
+          const float tw = lds_load<float>(tls + (qo * 64 + 32 * (wave & 1) + nl) * 4);
           xb += (th + tw) * kLog2e;
         }
         const float pr = ok ? __builtin_amdgcn_exp2f(fmaf(sacc[r], c2, xb)) : 0.0f;
@@ -466,6 +515,19 @@ __global__ __launch_bounds__(256, (D == 128 ? 1 : 2)) void bwd_dq_kernel(BwdPara
   const float* thr = nullptr;
   const float* twr = nullptr;
   __attribute__((address_space(3))) float* dts = nullptr;
+  // 64-wide grid: a 64-key tile is one grid row y, and the lane's 32 registers of
+  // a tile always hold the same 32 columns, so the running sums of dS per column
+  // stay in registers (term_w of those columns is re-read per tile, from cache).
+  constexpr bool RP64 = MODE == B_RELPOS64;
+  float dtw[RP64 ? 2 : 1][16];
+  const float* twq = RP64 ? p.term_w + (qvalid ? srow : 0) * 64 : nullptr;
+  if (RP64) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dtw[kb][r] = 0.0f;
+  }
+  if (RP64) thr = p.term_h + (qvalid ? srow : 0) * gh;
   if (MODE == B_RELPOS) {
     thr = p.term_h + (qvalid ? srow : 0) * gh;
     twr = p.term_w + (qvalid ? srow : 0) * gw;
@@ -527,6 +589,9 @@ __global__ __launch_bounds__(256, (D == 128 ? 1 : 2)) void bwd_dq_kernel(BwdPara
         kw[0] = kr[w0];
         kw[1] = w0 + 1 < p.keep_words ? kr[w0 + 1] : 0u;
       }
+      // 64-wide grid: term_h of this tile's grid row, and the row's running dS sum
+      const float th2 = (RP64 && qvalid) ? thr[k0 / 64] * kLog2e : 0.0f;
+      float tsum = 0.0f;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         f32x16_e sacc = (f32x16_e){}, dpacc = (f32x16_e){};
@@ -550,6 +615,15 @@ __global__ __launch_bounds__(256, (D == 128 ? 1 : 2)) void bwd_dq_kernel(BwdPara
           if (MODE == B_RELPOS) grid_step(grow[r / 4], gcol[r / 4], r % 4, gw, krow[r], kcol[r]);
           else krow[r] = kcol[r] = 0;
         }
+        float tw2[RP64 ? 16 : 1];
+        if (RP64) {
+#pragma unroll
+          for (int a = 0; a < 4; ++a) {
+            const f32x4 t = *(const f32x4*)(twq + 32 * kb + 8 * a + 4 * g);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) tw2[4 * a + e] = t[e] * kLog2e;
+          }
+        }
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int kofs = 8 * (r / 4) + 4 * g + (r % 4);
@@ -559,6 +633,7 @@ __global__ __launch_bounds__(256, (D == 128 ? 1 : 2)) void bwd_dq_kernel(BwdPara
           if (MODE == B_RELPOS) {
             if (ok && qvalid) xb += (thr[krow[r]] + twr[kcol[r]]) * kLog2e;
           }
+          if (RP64) xb += th2 + tw2[r];
           if (MODE == B_INDEX) {
             ok = ok && key <= qrow + p.offset;
             if (p.bias == BIAS_SLIDING) ok = ok && key > qrow + p.offset - p.window;
@@ -570,6 +645,13 @@ __global__ __launch_bounds__(256, (D == 128 ? 1 : 2)) void bwd_dq_kernel(BwdPara
           float dw = dpacc[r];
           if (DROP) dw = ((kw[kb] >> kofs) & 1u) ? dw * p.keep_scale : 0.0f;
           ds[r] = pr * (dw - dl);
+        }
+        if (RP64) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            dtw[kb][r] += ds[r];
+            tsum += ds[r];
+          }
         }
         if (MODE == B_RELPOS && qvalid) {
           // dterm_h[q, row] and dterm_w[q, col] collect dS.  The two lane halves hold the
@@ -596,12 +678,16 @@ __global__ __launch_bounds__(256, (D == 128 ? 1 : 2)) void bwd_dq_kernel(BwdPara
             dqT[nb] = mfma32(ld_tr<E, D>(ks, 32 * kb + 16 * c, 32 * nb, lane), sb, dqT[nb]);
         }
       }
+      if (RP64) {
+        const float tot = halves_sum(tsum);      // the two lane halves hold the row's other keys
+        if (g == 0 && qvalid) p.dterm_h[srow * gh + k0 / 64] = tot;
+      }
     }
     if (more) lstore(buf ^ 1);
     __syncthreads();
   }
 
-  if (MODE == B_RELPOS) {
+  if (MODE == B_RELPOS || RP64) {
     // scale * dS . K in fp32 (the tables' part is added by the tail kernel) and the
     // per-query dS sums (each lane half writes every other entry of its query row)
     __syncthreads();
@@ -616,10 +702,18 @@ __global__ __launch_bounds__(256, (D == 128 ? 1 : 2)) void bwd_dq_kernel(BwdPara
           for (int e = 0; e < 4; ++e) a[e] = dqT[nb][4 * i4 + e];
           store4(acc + 32 * nb + 8 * i4 + 4 * g, a, p.scale);
         }
-      for (int c = g; c < GT; c += 2) {
-        const float v = dts[c];
-        if (c < gh) p.dterm_h[srow * gh + c] = v;
-        else p.dterm_w[srow * gw + c - gh] = v;
+      if (RP64) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int a = 0; a < 4; ++a)
+            store4(p.dterm_w + srow * 64 + 32 * kb + 8 * a + 4 * g, &dtw[kb][4 * a], 1.0f);
+      } else {
+        for (int c = g; c < GT; c += 2) {
+          const float v = dts[c];
+          if (c < gh) p.dterm_h[srow * gh + c] = v;
+          else p.dterm_w[srow * gw + c - gh] = v;
+        }
       }
     }
     return;
@@ -647,7 +741,7 @@ int bmode_of(const BwdParams& p) {
     case BIAS_SLIDING: return B_INDEX;
     case BIAS_ADDITIVE:
     case BIAS_BOOL: return B_TENSOR;
-    case BIAS_RELPOS: return B_RELPOS;
+    case BIAS_RELPOS: return p.grid_w == 64 ? B_RELPOS64 : B_RELPOS;
     default: return -1;
   }
 }
@@ -667,6 +761,7 @@ void launch_modes(const BwdParams& p, hipStream_t s) {
     case B_NONE: drop ? launch_main<E, D, B_NONE, true, G>(p, s) : launch_main<E, D, B_NONE, false, G>(p, s); break;
     case B_INDEX: drop ? launch_main<E, D, B_INDEX, true, G>(p, s) : launch_main<E, D, B_INDEX, false, G>(p, s); break;
     case B_RELPOS: launch_main<E, D, B_RELPOS, false, G>(p, s); break;
+    case B_RELPOS64: launch_main<E, D, B_RELPOS64, false, G>(p, s); break;
     default: drop ? launch_main<E, D, B_TENSOR, true, G>(p, s) : launch_main<E, D, B_TENSOR, false, G>(p, s); break;
   }
 }

@@ -87,10 +87,20 @@ struct BwdParams {
   const void* rel_w;          // [2 grid_w - 1, D]
   float* drel_h;              // [2 grid_h - 1, D] fp32 output
   float* drel_w;              // [2 grid_w - 1, D] fp32 output
-  float* group_h;             // [grid_h (row r), grid_h (y), D] fp32 scratch
-  float* group_w;             // [grid_w (column c), grid_w (x), D] fp32 scratch
+  float* group_h;             // [split_h][grid_h (row r)][grid_h (y)][D] fp32 scratch
+  float* group_w;             // [split_w][grid_w (column c)][grid_w (x)][D] fp32 scratch
   int grid_h, grid_w;
+  int split_h, split_w;       // query slices of the grouped table products
 };
+
+// Query slices of a grouped table product: about 512 workgroups in all, each
+// with at least 64 queries.  Used by the launcher and the workspace planner.
+inline int relpos_group_splits(int64_t members, int64_t groups) {
+  int64_t s = (512 + groups - 1) / groups;
+  const int64_t cap = members / 64 > 1 ? members / 64 : 1;
+  if (s > cap) s = cap;
+  return (int)(s < 1 ? 1 : s);
+}
 
 // Dropout keep bits (Philox4x32-10): word [b, h, i, j / 32], bit j % 32.
 struct DropoutParams {

@@ -12,8 +12,10 @@
 //   dRh[t] = sum over (b, h, i, y) with row(i) - y + gh - 1 = t of dT_h[i, y] q_i    (dRw alike).
 // The table gradients are grouped by the query's grid row r (columns c for
 // Rw): G_h[r][y] = sum over (b, h) and the gw queries of row r of dT_h[i, y] q_i
-// (a [gh x D] product per row), then dRh[t] = sum_r G_h[r][r + gh - 1 - t], a
-// fixed-order sum (no atomics: the result is deterministic).
+// (a [gh x D] product per row, cut into slices of the queries so that several
+// hundred workgroups share the work), then dRh[t] = sum over slices and rows r
+// of G_h[r][r + gh - 1 - t], a fixed-order sum (no atomics: the result is
+// deterministic).
 #include "common.h"
 
 namespace sdpa {
@@ -80,20 +82,25 @@ __global__ __launch_bounds__(256) void relpos_group_kernel(BwdParams p) {
   const int aw = ROWS ? gh : gw;          // width of A (entries per query)
   const int nmem = ROWS ? gw : gh;        // members per (b, h)
   const float* A = ROWS ? p.dterm_h : p.dterm_w;
-  float* out = (ROWS ? p.group_h : p.group_w) + (int64_t)blockIdx.x * aw * D;
+  const int ngroups = ROWS ? gh : gw;
   const int gidx = blockIdx.x;
-  const int tid = threadIdx.x, ta = tid / 16, td = tid % 16;
+  // this workgroup's slice of the group's members (queries over every (b, h))
   const int64_t total = p.B * p.Hq * nmem;
+  const int nsplit = gridDim.y;
+  const int64_t per = ((total + nsplit - 1) / nsplit + CM - 1) / CM * CM;
+  const int64_t m_lo = (int64_t)blockIdx.y * per, m_hi = min(total, m_lo + per);
+  float* out = (ROWS ? p.group_h : p.group_w) + ((int64_t)blockIdx.y * ngroups + gidx) * aw * D;
+  const int tid = threadIdx.x, ta = tid / 16, td = tid % 16;
   for (int oa = 0; oa < aw; oa += 64)
     for (int od = 0; od < D; od += 64) {
       float acc[4][4] = {};
-      for (int64_t m0 = 0; m0 < total; m0 += CM) {
+      for (int64_t m0 = m_lo; m0 < m_hi; m0 += CM) {
         __syncthreads();
         for (int e = tid; e < CM * 64; e += 256) {
           const int m = e / 64, c = e % 64;
           const int64_t mm = m0 + m;
           float av = 0.0f, qv = 0.0f;
-          if (mm < total) {
+          if (mm < m_hi) {
             const int64_t bh = mm / nmem, k = mm % nmem;
             const int64_t i = ROWS ? (int64_t)gidx * gw + k : k * gw + gidx;
             if (oa + c < aw) av = A[(bh * p.Tq + i) * aw + oa + c];
@@ -130,18 +137,29 @@ __global__ __launch_bounds__(256) void relpos_group_kernel(BwdParams p) {
     }
 }
 
-// dR[t][d] = sum over groups r (in order) of G[r][r + n - 1 - t][d], for the
-// entries with 0 <= r + n - 1 - t < n.
-__global__ __launch_bounds__(256) void relpos_diag_kernel(const float* G, float* dR, int n, int D) {
-  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (e >= (int64_t)(2 * n - 1) * D) return;
-  const int t = (int)(e / D), d = (int)(e % D);
+// dR[t][d] = sum over slices s and groups r of G[s][r][r + n - 1 - t][d], for the
+// entries with 0 <= r + n - 1 - t < n.  One workgroup per (16 head dims, t): 16
+// partial sums per dim over the (s, r) pairs k = s * n + r with k % 16 = part,
+// then added in part order (a fixed order: deterministic).
+__global__ __launch_bounds__(256) void relpos_diag_kernel(const float* G, float* dR, int n, int D, int nsplit) {
+  __shared__ float red[16][16];
+  const int part = threadIdx.x / 16, dd = threadIdx.x % 16;
+  const int d = blockIdx.x * 16 + dd, t = blockIdx.y;
   float acc = 0.0f;
-  for (int r = 0; r < n; ++r) {
-    const int y = r + n - 1 - t;
-    if (y >= 0 && y < n) acc += G[((int64_t)r * n + y) * D + d];
+  if (d < D) {
+    for (int k = part; k < nsplit * n; k += 16) {
+      const int sl = k / n, r = k % n, y = r + n - 1 - t;
+      if (y >= 0 && y < n) acc += G[(((int64_t)sl * n + r) * n + y) * D + d];
+    }
   }
-  dR[e] = acc;
+  red[part][dd] = acc;
+  __syncthreads();
+  if (part == 0 && d < D) {
+    float tot = 0.0f;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) tot += red[u][dd];
+    dR[(int64_t)t * D + d] = tot;
+  }
 }
 
 template <typename E, int D, typename G>
@@ -149,11 +167,12 @@ void tail_typed(const BwdParams& p, hipStream_t s) {
   constexpr int QPB = 256 / (D / 16);
   dim3 gq((unsigned)((p.Tq + QPB - 1) / QPB), (unsigned)(p.B * p.Hq));
   hipLaunchKernelGGL((relpos_bwd_dq_kernel<E, D, G>), gq, dim3(256), 0, s, p);
-  hipLaunchKernelGGL((relpos_group_kernel<E, D, true>), dim3((unsigned)p.grid_h), dim3(256), 0, s, p);
-  hipLaunchKernelGGL((relpos_group_kernel<E, D, false>), dim3((unsigned)p.grid_w), dim3(256), 0, s, p);
-  const int nbh = (int)(((2 * p.grid_h - 1) * D + 255) / 256), nbw = (int)(((2 * p.grid_w - 1) * D + 255) / 256);
-  hipLaunchKernelGGL(relpos_diag_kernel, dim3(nbh), dim3(256), 0, s, (const float*)p.group_h, p.drel_h, p.grid_h, D);
-  hipLaunchKernelGGL(relpos_diag_kernel, dim3(nbw), dim3(256), 0, s, (const float*)p.group_w, p.drel_w, p.grid_w, D);
+  hipLaunchKernelGGL((relpos_group_kernel<E, D, true>), dim3((unsigned)p.grid_h, (unsigned)p.split_h), dim3(256), 0, s, p);
+  hipLaunchKernelGGL((relpos_group_kernel<E, D, false>), dim3((unsigned)p.grid_w, (unsigned)p.split_w), dim3(256), 0, s, p);
+  hipLaunchKernelGGL(relpos_diag_kernel, dim3((unsigned)((D + 15) / 16), (unsigned)(2 * p.grid_h - 1)), dim3(256), 0, s,
+                     (const float*)p.group_h, p.drel_h, p.grid_h, D, p.split_h);
+  hipLaunchKernelGGL(relpos_diag_kernel, dim3((unsigned)((D + 15) / 16), (unsigned)(2 * p.grid_w - 1)), dim3(256), 0, s,
+                     (const float*)p.group_w, p.drel_w, p.grid_w, D, p.split_w);
 }
 
 template <typename E, int D>
