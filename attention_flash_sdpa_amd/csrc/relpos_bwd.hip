@@ -30,12 +30,18 @@ template <typename E, int D, typename G>
 __global__ __launch_bounds__(256) void relpos_bwd_dq_kernel(BwdParams p) {
   constexpr int TPQ = D / 16;            // threads per query, 16 head dims each
   constexpr int QPB = 256 / TPQ;         // queries per workgroup
-  __shared__ float tab[kMaxTabRows * D]; // [Rh rows | Rw rows][D] fp32
+  // [Rh rows | Rw rows][D + 4] fp32: the 4-float pad shifts consecutive rows by
+  // 16 bytes of banks, so the 16 queries a wave reads (different rows) spread out
+  constexpr int TP = D + 4;
+  __shared__ __attribute__((aligned(16))) float tab[kMaxTabRows * TP];
   const int gh = p.grid_h, gw = p.grid_w, nh = 2 * gh - 1, nw = 2 * gw - 1;
   const int tid = threadIdx.x;
   const E* rh = (const E*)p.rel_h;
   const E* rw = (const E*)p.rel_w;
-  for (int e = tid; e < (nh + nw) * D; e += 256) tab[e] = (float)(e < nh * D ? rh[e] : rw[e - nh * D]);
+  for (int e = tid; e < (nh + nw) * D; e += 256) {
+    const int t = e / D, c = e % D;
+    tab[t * TP + c] = (float)(e < nh * D ? rh[e] : rw[e - nh * D]);
+  }
   __syncthreads();
   const int64_t bh = blockIdx.y;
   const int64_t i = (int64_t)blockIdx.x * QPB + tid / TPQ;
@@ -51,16 +57,18 @@ __global__ __launch_bounds__(256) void relpos_bwd_dq_kernel(BwdParams p) {
     acc[e] = v[0]; acc[e + 1] = v[1]; acc[e + 2] = v[2]; acc[e + 3] = v[3];
   }
   const float* th = p.dterm_h + srow * gh;
+#pragma unroll 4
   for (int y = 0; y < gh; ++y) {
     const float c = th[y];
-    const float* t = tab + (row - y + gh - 1) * D + d0;
+    const float* t = tab + (row - y + gh - 1) * TP + d0;
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[e] = fmaf(c, t[e], acc[e]);
   }
   const float* tw = p.dterm_w + srow * gw;
+#pragma unroll 4
   for (int x = 0; x < gw; ++x) {
     const float c = tw[x];
-    const float* t = tab + (nh + col - x + gw - 1) * D + d0;
+    const float* t = tab + (nh + col - x + gw - 1) * TP + d0;
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[e] = fmaf(c, t[e], acc[e]);
   }
