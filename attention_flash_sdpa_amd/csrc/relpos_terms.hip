@@ -54,8 +54,19 @@ __global__ __launch_bounds__(256) void relpos_terms_kernel(TermsParams p) {
   for (int t = threadIdx.x / tpq; t < gw; t += 256 / tpq) {
     float qr[DMAX];
     const TIN* qrow = qb + (row * gw + t) * p.q_st;
+    if (VEC && (p.q_st * sizeof(TIN)) % 16 == 0 && ((uintptr_t)qb & 15) == 0) {
+      constexpr int EPP = 16 / sizeof(TIN);
+      typedef TIN tin16 __attribute__((ext_vector_type(EPP)));
 #pragma unroll
-    for (int c = 0; c < DMAX; ++c) qr[c] = (c < D) ? to_f32(qrow[c]) : 0.0f;
+      for (int c = 0; c < DMAX; c += EPP) {
+        const tin16 v = (c < D) ? *(const tin16*)(qrow + c) : (tin16){};
+#pragma unroll
+        for (int e = 0; e < EPP; ++e) qr[c + e] = to_f32(v[e]);
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < DMAX; ++c) qr[c] = (c < D) ? to_f32(qrow[c]) : 0.0f;
+    }
     auto dot = [&](const TIN* r) -> float {
       float acc = 0.0f;
       if (VEC) {
@@ -79,6 +90,10 @@ __global__ __launch_bounds__(256) void relpos_terms_kernel(TermsParams p) {
     // each thread forms runs of 4 consecutive outputs and stores them together
     // (one 16-byte store when the row allows it)
     auto run = [&](float* out, int n, const TIN* tab, int tbase) {      // table row tbase - k for output k
+      if (n < 4 * tpq) {           // few outputs per thread (small grids): one at a time, all threads busy
+        for (int k = part; k < n; k += tpq) out[k] = dot(tab + (int64_t)(tbase - k) * pitch);
+        return;
+      }
       const bool v4 = (n & 3) == 0;
       for (int k0 = 4 * part; k0 < n; k0 += 4 * tpq) {
         float r4[4];

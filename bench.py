@@ -27,6 +27,7 @@ if ROOT not in sys.path:
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 HBM_PEAK_GBS = 8000.0               # MI355X HBM3E, published
+FP32_VECTOR_PEAK_TFLOPS = 157.3     # MI355X fp32 vector, published
 
 # Source file of each attention kernel, for matching recorded counter data.
 KERNEL_SOURCE = {
@@ -224,20 +225,27 @@ def cpu_baseline(wl, x, budget_s=20.0):
 
 
 def bench_backward(fa, wl, x, g, args):
-    """One sdpa_backward call per step: delta, dK/dV and dQ kernels.  Algorithmic
-    FLOPs are those of the five products per allowed pair (S = Q.K^T, dW = dO.V^T,
-    dV, dK, dQ: 10 * D), the usual accounting of 2.5x the forward pass."""
+    """One backward call per step (sdpa_backward, or sdpa_relpos_backward for rel-pos
+    workloads): delta, dK/dV and dQ kernels (plus the rel-pos terms and tail).
+    Algorithmic FLOPs are those of the five products per allowed pair
+    (S = Q.K^T, dW = dO.V^T, dV, dK, dQ: 10 * D), the usual accounting of 2.5x
+    the forward pass, plus the rel-pos products."""
     import statistics
     import numpy as np
     import torch
-    if wl.relpos:
-        print("bench.py: --pass backward takes unmasked or index-masked workloads", file=sys.stderr)
-        sys.exit(2)
     rng = np.random.default_rng(1)
     do = torch.from_numpy(rng.standard_normal(tuple(x["q"].shape), dtype=np.float32)).to(g["q"].dtype).cuda()
-    o, lse = fa.sdpa(g["q"], g["k"], g["v"], layout=wl.layout, scale=wl.scale, mask=wl.mask, return_lse=True)
-    call = lambda: fa.sdpa_backward(g["q"], g["k"], g["v"], o, do, lse, layout=wl.layout, scale=wl.scale,
-                                    mask=wl.mask)
+    if wl.relpos:
+        o, lse = fa.sdpa_relpos(g["q"], g["k"], g["v"], g["rel_pos_h"], g["rel_pos_w"], wl.grid, layout=wl.layout,
+                                scale=wl.scale, return_lse=True)
+        n = fa.load().sdpa_relpos_bwd_workspace_size(wl.B, wl.Hq, wl.grid[0], wl.grid[1], wl.D)
+        ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+        call = lambda: fa.sdpa_relpos_backward(g["q"], g["k"], g["v"], o, do, lse, g["rel_pos_h"], g["rel_pos_w"],
+                                               wl.grid, layout=wl.layout, scale=wl.scale, workspace=ws)
+    else:
+        o, lse = fa.sdpa(g["q"], g["k"], g["v"], layout=wl.layout, scale=wl.scale, mask=wl.mask, return_lse=True)
+        call = lambda: fa.sdpa_backward(g["q"], g["k"], g["v"], o, do, lse, layout=wl.layout, scale=wl.scale,
+                                        mask=wl.mask)
     for _ in range(args.warmup):
         call()
     torch.cuda.synchronize()
@@ -261,6 +269,8 @@ def bench_backward(fa, wl, x, g, args):
     call_ms = statistics.median(ts)
     pairs = allowed_pairs(wl) * wl.B * wl.Hq
     flops = 10 * wl.D * pairs
+    if wl.relpos:       # terms recomputed, the tables' part of dQ, the tables' gradients: 2 D (gh + gw) per query each
+        flops += 3 * 2 * wl.D * (wl.grid[0] + wl.grid[1]) * wl.B * wl.Hq * wl.Tq
     achieved = flops / (call_ms * 1e-3) / 1e12
     es = 2
     nbytes = es * wl.D * (4 * wl.B * wl.Hq * wl.Tq + 4 * wl.B * wl.Hkv * wl.Tkv) + 8 * wl.B * wl.Hq * wl.Tq
@@ -274,13 +284,117 @@ def bench_backward(fa, wl, x, g, args):
         "dtype": {"bf16": "bf16", "fp16": "f16"}.get(wl.dtype, "f32"), "data": "synthetic",
         "config": {"workload": wl.name + "_backward", "description": wl.description + ", backward pass",
                    "layout": wl.layout, "B": wl.B, "Hq": wl.Hq, "Hkv": wl.Hkv, "Tq": wl.Tq, "Tkv": wl.Tkv,
-                   "head_dim": wl.D, "mask": wl.mask, "scale": wl.scale, "flop_per_step": flops},
+                   "head_dim": wl.D, "mask": wl.mask, "grid": list(wl.grid) if wl.grid else None,
+                   "scale": wl.scale, "flop_per_step": flops},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
-                     "kernel": "bwd_delta_kernel + bwd_dkdv_kernel + bwd_dq_kernel (one call)",
+                     "kernel": "bwd_delta_kernel + bwd_dkdv_kernel + bwd_dq_kernel" +
+                               (" + rel-pos terms and tail (one call)" if wl.relpos else " (one call)"),
                      "kernel_ms": round(call_ms, 5), "flop_per_launch": flops,
                      "algorithmic_bytes_per_launch": nbytes},
     }
+    print(json.dumps(line))
+
+
+def _events_ms(call, steps, hold_ms):
+    """Median over 5 repetitions of the HIP-event time per call, launches queued behind a spin."""
+    import statistics
+    import torch
+    s = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ts = []
+    for _ in range(5):
+        torch.cuda.synchronize()
+        _hold_stream(hold_ms)
+        ev[0].record(s)
+        for _ in range(steps):
+            call()
+        ev[1].record(s)
+        ev[1].synchronize()
+        ts.append(ev[0].elapsed_time(ev[1]) / steps)
+    return statistics.median(ts)
+
+
+def bench_train_forward(fa, wl, g, args):
+    """'dropout': per step, draw the keep bits (Philox4x32-10, one bit per score) and run the
+    forward pass with attention dropout; the forward kernel's roofline is reported (attention
+    FLOPs as for the forward pass), and the keep-bit kernel's time beside it.
+    'weights': the [B, Hq, Tq, Tkv] fp32 attention weights rebuilt from lse (a debug output):
+    bound by writing 4 bytes per score."""
+    import torch
+    if wl.relpos:
+        print("bench.py: --pass dropout / weights take unmasked or index-masked workloads", file=sys.stderr)
+        sys.exit(2)
+    rate = 0.1
+    pairs = allowed_pairs(wl) * wl.B * wl.Hq
+    if args.pass_ == "dropout":
+        keep = fa.dropout_mask(1, 0, rate, wl.B, wl.Hq, wl.Tq, wl.Tkv)
+        out = torch.empty_like(g["q"])
+        fwd = lambda: fa.sdpa(g["q"], g["k"], g["v"], layout=wl.layout, scale=wl.scale, mask=wl.mask, out=out,
+                              dropout={"keep": keep, "rate": rate})
+        mask_call = lambda: fa.dropout_mask(1, 0, rate, wl.B, wl.Hq, wl.Tq, wl.Tkv)
+        step = lambda: (mask_call(), fwd())
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+        sec = (time.perf_counter() - t0) / args.steps
+        fwd_ms = _events_ms(fwd, args.steps, 2.0 + 1.0 * args.steps)
+        fwd()
+        kernel = fa.last_kernel()
+        mask_ms = _events_ms(mask_call, args.steps, 2.0 + 0.2 * args.steps)
+        flops = 4 * wl.D * pairs
+        achieved = flops / (fwd_ms * 1e-3) / 1e12
+        keep_bytes = wl.B * wl.Hq * wl.Tq * ((wl.Tkv + 31) // 32) * 4
+        line = {"metric": "attention TFLOP/s with attention dropout (keep bits drawn every step)",
+                "value": round(flops / sec / 1e12, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+                "warmup": args.warmup, "ms_per_step": round(sec * 1e3, 5), "higher_is_better": True,
+                "scaling": "weak", "vs_baseline": None, "dtype": {"bf16": "bf16", "fp16": "f16"}.get(wl.dtype, "f32"),
+                "data": "synthetic",
+                "config": {"workload": wl.name + "_dropout", "rate": rate, "B": wl.B, "Hq": wl.Hq, "Hkv": wl.Hkv,
+                           "Tq": wl.Tq, "Tkv": wl.Tkv, "head_dim": wl.D, "mask": wl.mask, "flop_per_step": flops},
+                "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": MFMA_BF16_PEAK_TFLOPS,
+                             "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                             "kernel": kernel, "kernel_ms": round(fwd_ms, 5)},
+                "keep_bits": {"kernel": "dropout_mask_kernel", "kernel_ms": round(mask_ms, 5), "bytes": keep_bytes,
+                              "GB_per_s": round(keep_bytes / (mask_ms * 1e-3) / 1e9, 1)}}
+    else:
+        o, lse = fa.sdpa(g["q"], g["k"], g["v"], layout=wl.layout, scale=wl.scale, mask=wl.mask, return_lse=True)
+        call = lambda: fa.attention_weights(g["q"], g["k"], lse, layout=wl.layout, scale=wl.scale, mask=wl.mask)
+        for _ in range(args.warmup):
+            call()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            call()
+        torch.cuda.synchronize()
+        sec = (time.perf_counter() - t0) / args.steps
+        ms = _events_ms(call, args.steps, 2.0 + 1.0 * args.steps)
+        nbytes = wl.B * wl.Hq * wl.Tq * wl.Tkv * 4
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        # the kernel forms each score as an fp32 dot product on the vector ALUs (2 D FLOPs per score):
+        # whichever of that and the 4-byte write per score takes longer at peak bounds it
+        vflops = 2 * wl.D * wl.B * wl.Hq * wl.Tq * wl.Tkv
+        alu_bound = vflops / (FP32_VECTOR_PEAK_TFLOPS * 1e12) > nbytes / (HBM_PEAK_GBS * 1e9)
+        line = {"metric": "attention-weights output GB/s (fp32 [B, Hq, Tq, Tkv])",
+                "value": round(nbytes / sec / 1e9, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+                "warmup": args.warmup, "ms_per_step": round(sec * 1e3, 5), "higher_is_better": True,
+                "scaling": "weak", "vs_baseline": None, "dtype": {"bf16": "bf16", "fp16": "f16"}.get(wl.dtype, "f32"),
+                "data": "synthetic",
+                "config": {"workload": wl.name + "_weights", "B": wl.B, "Hq": wl.Hq, "Tq": wl.Tq, "Tkv": wl.Tkv,
+                           "head_dim": wl.D, "mask": wl.mask},
+                "roofline": ({"bound": "alu", "achieved": round(vflops / (ms * 1e-3) / 1e12, 3),
+                              "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
+                              "frac": round(vflops / (ms * 1e-3) / 1e12 / FP32_VECTOR_PEAK_TFLOPS, 4)}
+                             if alu_bound else
+                             {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                              "frac": round(gbs / HBM_PEAK_GBS, 4)})}
+        line["roofline"].update({"traffic": None, "kernel": "attn_weights_kernel", "kernel_ms": round(ms, 5),
+                                 "algorithmic_bytes_per_launch": nbytes, "flop_per_launch": vflops,
+                                 "write_GB_per_s": round(gbs, 1)})
     print(json.dumps(line))
 
 
@@ -297,9 +411,11 @@ def main():
     ap.add_argument("--route", choices=["relpos", "additive"], default="relpos",
                     help="rel-pos workloads: 'additive' times the bias materialised as a [B, H, T, T] "
                          "additive mask in the input dtype (formed before timing) instead of the fused terms")
-    ap.add_argument("--pass", dest="pass_", choices=["forward", "backward"], default="forward",
-                    help="'backward' times one sdpa_backward call per step (dQ, dK, dV from the forward "
-                         "pass's O and lse, formed before timing); index-mask and unmasked workloads only")
+    ap.add_argument("--pass", dest="pass_", choices=["forward", "backward", "dropout", "weights"], default="forward",
+                    help="'backward' times one backward call per step (dQ, dK, dV from the forward pass's O and "
+                         "lse, formed before timing); 'dropout' times drawing the keep bits plus the forward "
+                         "pass with attention dropout (rate 0.1); 'weights' times the attention-weights output "
+                         "(unmasked or index-masked workloads)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB per step (counter calibration)")
     args = ap.parse_args()
@@ -329,6 +445,9 @@ def main():
     g = {k: t.cuda() for k, t in x.items()}
     if args.pass_ == "backward":
         bench_backward(fa, wl, x, g, args)
+        return
+    if args.pass_ in ("dropout", "weights"):
+        bench_train_forward(fa, wl, g, args)
         return
     if wl.relpos:
         n = fa.workspace_size(wl.B, wl.Hq, wl.Hkv, wl.Tq, wl.Tkv, wl.D, True, wl.grid)
