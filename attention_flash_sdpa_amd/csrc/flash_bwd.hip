@@ -108,6 +108,45 @@ __device__ __forceinline__ V8<E> ld_tr(const lds_char* t, int rowbase, int colba
   return __builtin_bit_cast(V8<E>, a);
 }
 
+// The swizzle of row r depends only on r % 16, so every read below is the
+// tile base + a compile-time row-group offset + a per-lane offset computed once.
+template <int D>
+struct LaneOff {
+  int row[BCfg<D>::QC];                  // 16-byte row reads: row lane % 32, chunk 2 c + lane / 32
+  int trlo[BCfg<D>::DB], trhi[BCfg<D>::DB];   // transposing reads of 16-row groups, column block nb
+  __device__ __forceinline__ void init(int lane) {
+    using C = BCfg<D>;
+    const int nl = lane & 31, g = lane >> 5;
+#pragma unroll
+    for (int c = 0; c < C::QC; ++c) row[c] = nl * C::PITCH + (((2 * c + g) ^ C::swz(nl)) << 4);
+    const int j = lane & 15, dh = (lane >> 4) & 1;
+    const int r0 = 4 * g + (j >> 2), r1 = r0 + 8;
+#pragma unroll
+    for (int nb = 0; nb < C::DB; ++nb) {
+      const int col = 32 * nb + 16 * dh + 4 * (j & 3);
+      const int chunk = col >> 3, within = (col & 7) * 2;
+      trlo[nb] = r0 * C::PITCH + ((chunk ^ C::swz(r0)) << 4) + within;
+      trhi[nb] = r1 * C::PITCH + ((chunk ^ C::swz(r1)) << 4) + within;
+    }
+  }
+};
+
+// Row read of row base32 + lane % 32 (base32 a multiple of 32), chunk 2 c + lane / 32.
+template <typename E, int D>
+__device__ __forceinline__ V8<E> ld_row_o(const lds_char* t, int base32, const LaneOff<D>& lo, int c) {
+  return *(const __attribute__((address_space(3))) V8<E>*)(t + base32 * BCfg<D>::PITCH + lo.row[c]);
+}
+
+// ld_tr for rowbase a multiple of 16 and colbase = 32 nb.
+template <typename E, int D>
+__device__ __forceinline__ V8<E> ld_tr_o(const lds_char* t, int rowbase, const LaneOff<D>& lo, int nb) {
+  const lds_char* b = t + rowbase * BCfg<D>::PITCH;
+  const s16x4 l4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(b + lo.trlo[nb]));
+  const s16x4 h4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(b + lo.trhi[nb]));
+  const s16x8 a = __builtin_shufflevector(l4, h4, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(V8<E>, a);
+}
+
 template <typename E>
 __device__ __forceinline__ V8<E> pack8(const float* x) {
   const f32x8 v = {x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]};
@@ -242,6 +281,9 @@ __global__ __launch_bounds__(256, (D == 128 ? 1 : 2)) void bwd_dkdv_kernel(BwdPa
     vf[c] = kvalid ? *(const V8<E>*)(vp + key * p.k_st + 16 * c + 8 * g) : (V8<E>){};
   }
 
+  LaneOff<D> lo;
+  lo.init(lane);
+
   // Queries that can see any key of the workgroup.
   int64_t qlo = 0, qhi = p.Tq;
   if (MODE == B_INDEX) {
@@ -368,16 +410,26 @@ __global__ __launch_bounds__(256, (D == 128 ? 1 : 2)) void bwd_dkdv_kernel(BwdPa
     for (int s = 0; s < 2; ++s) {
       const int64_t qa = q0 + 32 * s;
       if (qa >= p.Tq) break;
-      if (MODE == B_INDEX) {       // no allowed (query, key) pair between this sub-tile and the wave's keys
+      // Index masks: skip a sub-tile with no allowed (query, key) pair, test per score
+      // only where the band edge crosses it (allowed: key - offset <= q < key - offset + window).
+      bool edge = false;
+      int qa32 = 0, mlo = 0, mhi = 0;
+      if (MODE == B_INDEX) {
         const int64_t kw0 = kb0 + 32 * wave;
         if (kw0 > qa + 31 + p.offset) continue;
-        if (p.bias == BIAS_SLIDING && kw0 + 31 <= qa + p.offset - p.window) continue;
+        const bool sl = p.bias == BIAS_SLIDING;
+        if (sl && kw0 + 31 <= qa + p.offset - p.window) continue;
+        edge = !(kw0 + 31 <= qa + p.offset && (!sl || kw0 > qa + 31 + p.offset - p.window));
+        const int64_t l64 = key - p.offset, h64 = sl ? key - p.offset + p.window : p.Tq + 64;
+        qa32 = (int)qa;
+        mlo = (int)max(min(l64, (int64_t)INT32_MAX), (int64_t)INT32_MIN);
+        mhi = (int)max(min(h64, (int64_t)INT32_MAX), (int64_t)INT32_MIN);
       }
       f32x16_e sacc = (f32x16_e){}, dpacc = (f32x16_e){};
 #pragma unroll
       for (int c = 0; c < C::QC; ++c) {
-        sacc = mfma32(ld_row<E, D>(qt, 32 * s + nl, c, g), kf[c], sacc);
-        dpacc = mfma32(ld_row<E, D>(dt, 32 * s + nl, c, g), vf[c], dpacc);
+        sacc = mfma32(ld_row_o<E, D>(qt, 32 * s, lo, c), kf[c], sacc);
+        dpacc = mfma32(ld_row_o<E, D>(dt, 32 * s, lo, c), vf[c], dpacc);
       }
       float l2[16], dl[16], pt[16], ds[16];
       uint32_t kw[16];
@@ -400,9 +452,9 @@ __global__ __launch_bounds__(256, (D == 128 ? 1 : 2)) void bwd_dkdv_kernel(BwdPa
         const int64_t qq = qa + 8 * (r / 4) + 4 * g + (r % 4);
         bool ok = kvalid;
         float xb = -l2[r];
-        if (MODE == B_INDEX) {
-          ok = ok && key <= qq + p.offset;
-          if (p.bias == BIAS_SLIDING) ok = ok && key > qq + p.offset - p.window;
+        if (MODE == B_INDEX && edge) {
+          const int q32 = qa32 + 8 * (r / 4) + 4 * g + (r % 4);
+          ok = ok && q32 >= mlo && q32 < mhi;
         }
         if (MODE == B_TENSOR) {
           if (ok && qq < p.Tq) xb += mask_value(p, b, hq, qq, key) * kLog2e;
@@ -436,8 +488,8 @@ __global__ __launch_bounds__(256, (D == 128 ? 1 : 2)) void bwd_dkdv_kernel(BwdPa
         const V8<E> sb = pack8<E>(ds + 8 * c);
 #pragma unroll
         for (int nb = 0; nb < C::DB; ++nb) {
-          dvT[nb] = mfma32(ld_tr<E, D>(dt, 32 * s + 16 * c, 32 * nb, lane), pb, dvT[nb]);
-          dkT[nb] = mfma32(ld_tr<E, D>(qt, 32 * s + 16 * c, 32 * nb, lane), sb, dkT[nb]);
+          dvT[nb] = mfma32(ld_tr_o<E, D>(dt, 32 * s + 16 * c, lo, nb), pb, dvT[nb]);
+          dkT[nb] = mfma32(ld_tr_o<E, D>(qt, 32 * s + 16 * c, lo, nb), sb, dkT[nb]);
         }
       }
     }
