@@ -525,9 +525,12 @@ __global__ __launch_bounds__(256, (D == 128 ? 1 : 2)) void bwd_dq_kernel(BwdPara
   constexpr int BN = 64;                           // keys per staged tile
   constexpr int TK = BN * C::PITCH;
   constexpr int NLD = BN * C::CH / 256;
-  // [buf][K | V] tiles; rel-pos: then the per-query sums of dS, [128 q][grid_h + grid_w] fp32
+  // [buf][K | V] tiles; rel-pos: then the per-query sums of dS, [128 q][grid_h + grid_w] fp32;
+  // 64-wide grid: then term_w of the workgroup's 128 queries, [128 q][64 + 4 pad] fp32
   constexpr int DOFF = 4 * TK;
-  __shared__ __attribute__((aligned(16))) char smem_raw[DOFF + (MODE == B_RELPOS ? 128 * kMaxGT * 4 : 0)];
+  constexpr int TWP = 68;
+  __shared__ __attribute__((aligned(16))) char smem_raw[DOFF + (MODE == B_RELPOS ? 128 * kMaxGT * 4 : 0) +
+                                                       (MODE == B_RELPOS64 ? 128 * TWP * 4 : 0)];
   lds_char* smem = (lds_char*)smem_raw;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -572,7 +575,16 @@ __global__ __launch_bounds__(256, (D == 128 ? 1 : 2)) void bwd_dq_kernel(BwdPara
   // stay in registers (term_w of those columns is re-read per tile, from cache).
   constexpr bool RP64 = MODE == B_RELPOS64;
   float dtw[RP64 ? 2 : 1][16];
-  const float* twq = RP64 ? p.term_w + (qvalid ? srow : 0) * 64 : nullptr;
+  // term_w rows staged in LDS (read once per tile from there); rows padded by 16 bytes
+  const lds_char* twq = smem + DOFF + (32 * wave + nl) * TWP * 4;
+  if (RP64) {
+    const float* src = p.term_w + ((b * p.Hq + h) * p.Tq + wg_q0) * 64;
+    for (int e = tid; e < 128 * 16; e += 256) {      // 16-byte pieces of the [128][64] block
+      const int q = e >> 4, c4 = (e & 15) * 4;
+      const f32x4 v = wg_q0 + q < p.Tq ? *(const f32x4*)(src + q * 64 + c4) : (f32x4){};
+      lds_store(smem + DOFF + (q * TWP + c4) * 4, v);
+    }
+  }
   if (RP64) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -615,6 +627,7 @@ __global__ __launch_bounds__(256, (D == 128 ? 1 : 2)) void bwd_dq_kernel(BwdPara
   f32x16_e dqT[C::DB];
 #pragma unroll
   for (int nb = 0; nb < C::DB; ++nb) dqT[nb] = (f32x16_e){};
+  float th_next = (RP64 && qvalid && ntiles > 0) ? thr[t0] : 0.0f;   // 64-wide grid: term_h of the first tile's row
   if (ntiles > 0) {
     gload(0);
     lstore(0);
@@ -642,7 +655,8 @@ __global__ __launch_bounds__(256, (D == 128 ? 1 : 2)) void bwd_dq_kernel(BwdPara
         kw[1] = w0 + 1 < p.keep_words ? kr[w0 + 1] : 0u;
       }
       // 64-wide grid: term_h of this tile's grid row, and the row's running dS sum
-      const float th2 = (RP64 && qvalid) ? thr[k0 / 64] * kLog2e : 0.0f;
+      const float th2 = RP64 ? th_next * kLog2e : 0.0f;
+      if (RP64 && it + 1 < ntiles) th_next = qvalid ? thr[k0 / 64 + 1] : 0.0f;   // next tile's grid row
       float tsum = 0.0f;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
@@ -671,7 +685,7 @@ __global__ __launch_bounds__(256, (D == 128 ? 1 : 2)) void bwd_dq_kernel(BwdPara
         if (RP64) {
 #pragma unroll
           for (int a = 0; a < 4; ++a) {
-            const f32x4 t = *(const f32x4*)(twq + 32 * kb + 8 * a + 4 * g);
+            const f32x4 t = lds_load<f32x4>(twq + (32 * kb + 8 * a + 4 * g) * 4);
 #pragma unroll
             for (int e = 0; e < 4; ++e) tw2[4 * a + e] = t[e] * kLog2e;
           }
