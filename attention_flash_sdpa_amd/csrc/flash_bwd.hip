@@ -252,7 +252,10 @@ __global__ __launch_bounds__(256, (D == 128 ? 1 : 2)) void bwd_dkdv_kernel(BwdPa
   // rel-pos: [buf][BQ][grid_h + grid_w] fp32 term rows; on a 64-wide grid only
   // the 64 columns and the two grid rows of the workgroup's keys: [buf][BQ][64], [BQ][2]
   constexpr int TOFF = KOFF + (DROP ? 2 * 4 * BQ * 4 : 0);
-  constexpr int TBUF = MODE == B_RELPOS ? BQ * kMaxGT * 4 : (MODE == B_RELPOS64 ? BQ * 66 * 4 : 0);
+  // 64-wide grid: term_w transposed, [64 columns][BQ + 4 pad] (a lane's 4 consecutive queries
+  // are one 16-byte read), then term_h at the 2 grid rows of the keys, [2][BQ]
+  constexpr int TWQ = BQ + 4;
+  constexpr int TBUF = MODE == B_RELPOS ? BQ * kMaxGT * 4 : (MODE == B_RELPOS64 ? (64 * TWQ + 2 * BQ) * 4 : 0);
   constexpr int SMEM = TOFF + 2 * TBUF;
   __shared__ __attribute__((aligned(16))) char smem_raw[SMEM];
   lds_char* smem = (lds_char*)smem_raw;
@@ -377,8 +380,12 @@ __global__ __launch_bounds__(256, (D == 128 ? 1 : 2)) void bwd_dkdv_kernel(BwdPa
         if (q0 + q < p.Tq && row0 + c < gh) hv = p.term_h[(rbase + q0 + q) * gh + row0 + c];
       }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) lds_store(tl + 16 * (tid + 256 * u), v[u]);
-      if (tid < 2 * BQ) lds_store(tl + BQ * 64 * 4 + tid * 4, hv);
+      for (int u = 0; u < 4; ++u) {                     // transposed: [column][query]
+        const int e = 4 * (tid + 256 * u), q = e / 64, c = e % 64;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) lds_store(tl + ((c + x) * TWQ + q) * 4, v[u][x]);
+      }
+      if (tid < 2 * BQ) lds_store(tl + (64 * TWQ + (tid & 1) * BQ + (tid >> 1)) * 4, hv);
     }
   };
 
@@ -433,6 +440,7 @@ __global__ __launch_bounds__(256, (D == 128 ? 1 : 2)) void bwd_dkdv_kernel(BwdPa
       }
       float l2[16], dl[16], pt[16], ds[16];
       uint32_t kw[16];
+      f32x4 bias4 = (f32x4){};
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
         const int qo = 32 * s + 8 * a + 4 * g;
@@ -466,10 +474,13 @@ __global__ __launch_bounds__(256, (D == 128 ? 1 : 2)) void bwd_dkdv_kernel(BwdPa
           xb += (th + tw) * kLog2e;
         }
         if (MODE == B_RELPOS64) {    // the wave's keys lie in grid row kb0 / 64 + wave / 2
-          const int qo = 32 * s + 8 * (r / 4) + 4 * g + (r % 4);
-          const float th = lds_load<float>(tls + (BQ * 64 + qo * 2 + (wave >> 1)) * 4);
-          const float tw = lds_load<float>(tls + (qo * 64 + 32 * (wave & 1) + nl) * 4);
-          xb += (th + tw) * kLog2e;
+          if (r % 4 == 0) {           // term_h + term_w of the 4 queries 32 s + 8 (r / 4) + 4 g + 0..3
+            const int qo0 = 32 * s + 8 * (r / 4) + 4 * g;
+            const f32x4 tw4 = lds_load<f32x4>(tls + ((32 * (wave & 1) + nl) * TWQ + qo0) * 4);
+            const f32x4 th4 = lds_load<f32x4>(tls + (64 * TWQ + (wave >> 1) * BQ + qo0) * 4);
+            bias4 = (tw4 + th4) * kLog2e;
+          }
+          xb += bias4[r % 4];
         }
         const float pr = ok ? __builtin_amdgcn_exp2f(fmaf(sacc[r], c2, xb)) : 0.0f;
         float dw = dpacc[r];
