@@ -161,8 +161,12 @@ Route route_of(const sdpa::FwdParams& p) {
   // The MFMA kernels take each row's running max on scores already multiplied
   // by scale, which needs scale > 0; other scales run on the generic kernel.
   if (!(p.scale > 0.0f && std::isfinite(p.scale))) return R_GENERIC;
-  // Dropout runs on the general MFMA kernel where it applies, else on the generic one.
-  if (p.keep) return sdpa::flash_mfma_supports(p) ? R_MFMA : R_GENERIC;
+  // Dropout runs on the double-buffered kernel (no mask, causal, sliding), else on the
+  // general MFMA kernel where it applies, else on the generic one.
+  if (p.keep) {
+    if (g_tiled.load() && sdpa::tiled_supports(p)) return R_TILED;
+    return sdpa::flash_mfma_supports(p) ? R_MFMA : R_GENERIC;
+  }
   if (sdpa::d16_supports(p)) return R_D16;
   if (sdpa::window_supports(p)) return R_WINDOW;
   const int64_t wide = g_split64w.load();     // 0 off, 1 where the shape fills the CUs, 2 wherever supported

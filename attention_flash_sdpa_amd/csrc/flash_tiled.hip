@@ -28,6 +28,13 @@
 // wave copies its 32 x 32 block of the mask next to the K/V tile, XOR-swizzled
 // by 16-byte chunks, and reads its 16 values per tile with 4 vector LDS reads.
 //
+// Attention dropout (no mask or causal / sliding masks): the weights that
+// multiply V are scaled by keep / (1 - rate) while lse and the row sum stay
+// those of the undropped scores ([Axon PR 650] "Axon.Layers.scaled_dot_product_attention/4",
+// description: `:dropout_rate` in :train mode).  Each lane reads its row's
+// keep word for the 32-key tile and zeroes its packed 16-bit weights after
+// they enter the row sum; the 1 / (1 - rate) factor joins the final 1 / l.
+//
 // The running max is optimistic: probabilities are formed against the current
 // reference and only a tile whose row sum exceeds 2^8 (a probability above
 // 2^8, an overflow, or no reference yet) takes the exact path that moves the
@@ -100,7 +107,7 @@ __device__ __forceinline__ float pair_sum(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <typename E, int D, int MODE, bool OUT16>
+template <typename E, int D, int MODE, bool OUT16, bool DROP>
 __global__ __launch_bounds__(256, 3) void flash_tiled_kernel(FwdParams p, int hpw, int64_t mask_bytes) {
   typedef typename Vec16<E>::x8 e8;
   typedef typename Vec16<E>::x4 e4;
@@ -231,6 +238,13 @@ __global__ __launch_bounds__(256, 3) void flash_tiled_kernel(FwdParams p, int hp
 #pragma unroll
   for (int d = 0; d < C::DB; ++d) o[d] = (f32x16){};
   float m = -INFINITY, l = 0.0f;
+  // Attention dropout: keep bits, one 32-bit word per 32-key tile of a score
+  // row, read through a descriptor over this (batch, head)'s rows with the
+  // lane's row as a 32-bit offset and the tile as the scalar offset.
+  const __amdgpu_buffer_rsrc_t krs_keep = __builtin_amdgcn_make_buffer_rsrc(
+      DROP ? (void*)(p.keep + (b * p.Hq + h) * p.Tq * p.keep_words) : nullptr, 0,
+      DROP ? (int)(p.Tq * p.keep_words * 4) : 0, 0x00020000);
+  const int keep_vo = DROP ? (int)((qvalid ? qrow : 0) * p.keep_words * 4) : 0;
 
   auto step = [&](int t, auto par) {
     constexpr int PAR = decltype(par)::value;
@@ -241,6 +255,8 @@ __global__ __launch_bounds__(256, 3) void flash_tiled_kernel(FwdParams p, int hp
     }
     const lds_char* ks = PAR ? kb : ka;
     const lds_char* vs = PAR ? vb : va;
+    // this tile's keep bits (tiles start at multiples of 32 keys)
+    const uint32_t kw = DROP ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(krs_keep, keep_vo, 4 * t, 0) : 0u;
     f32x16 s = (f32x16){};
 #pragma unroll
     for (int c = 0; c < C::QC; ++c) s = mfma32(lds_b128<e8>(ks + kro[c]), qf[c], s);
@@ -293,6 +309,12 @@ __global__ __launch_bounds__(256, 3) void flash_tiled_kernel(FwdParams p, int hp
           pk[e / 2] = __builtin_convertvector(pp, e2);
           if (e & 2) acc1 = dot2_ones(pk[e / 2], acc1);
           else acc0 = dot2_ones(pk[e / 2], acc0);
+          if (DROP) {     // dropped weights leave P.V (the row sum above keeps them)
+            const int i0 = 8 * tc + e;                      // even: keys i0 and i0 + 1 are adjacent
+            const uint32_t two = (kw >> (8 * (i0 / 4) + 4 * g + (i0 % 4))) & 3u;
+            const uint32_t msk = ((two & 1u) ? 0xFFFFu : 0u) | ((two & 2u) ? 0xFFFF0000u : 0u);
+            pk[e / 2] = __builtin_bit_cast(e2, __builtin_bit_cast(uint32_t, pk[e / 2]) & msk);
+          }
         }
         pb[tc] = __builtin_shufflevector(__builtin_shufflevector(pk[0], pk[1], 0, 1, 2, 3),
                                          __builtin_shufflevector(pk[2], pk[3], 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
@@ -348,7 +370,7 @@ __global__ __launch_bounds__(256, 3) void flash_tiled_kernel(FwdParams p, int hp
   }
 
   const float lt = pair_sum(l);
-  const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+  const float inv = lt > 0.0f ? (DROP ? p.keep_scale : 1.0f) / lt : 0.0f;
   if (!qvalid) return;
   const int64_t ob = b * p.q_sb + h * p.q_sh + qrow * p.q_st;
 #pragma unroll
@@ -390,8 +412,15 @@ hipError_t launch_t(const FwdParams& p, hipStream_t s) {
     mask_bytes = ((p.B - 1) * p.ms[0] + (p.Hq - 1) * p.ms[1] + (p.Tq - 1) * p.ms[2] + (p.Tkv - 1) * p.ms[3] + 1) *
                  mask_es(p);
   mask_bytes = (mask_bytes + 15) & ~(int64_t)15;
-  if (p.out_dtype != 0) hipLaunchKernelGGL((flash_tiled_kernel<E, D, MODE, true>), grid, dim3(256), 0, s, p, hpw, mask_bytes);
-  else hipLaunchKernelGGL((flash_tiled_kernel<E, D, MODE, false>), grid, dim3(256), 0, s, p, hpw, mask_bytes);
+  constexpr bool CAN_DROP = MODE == T_NONE || MODE == T_INDEX;
+  if (CAN_DROP && p.keep) {
+    if (p.out_dtype != 0) hipLaunchKernelGGL((flash_tiled_kernel<E, D, MODE, true, CAN_DROP>), grid, dim3(256), 0, s, p, hpw, mask_bytes);
+    else hipLaunchKernelGGL((flash_tiled_kernel<E, D, MODE, false, CAN_DROP>), grid, dim3(256), 0, s, p, hpw, mask_bytes);
+  } else if (p.out_dtype != 0) {
+    hipLaunchKernelGGL((flash_tiled_kernel<E, D, MODE, true, false>), grid, dim3(256), 0, s, p, hpw, mask_bytes);
+  } else {
+    hipLaunchKernelGGL((flash_tiled_kernel<E, D, MODE, false, false>), grid, dim3(256), 0, s, p, hpw, mask_bytes);
+  }
   return hipGetLastError();
 }
 
@@ -410,6 +439,9 @@ hipError_t launch_d(const FwdParams& p, hipStream_t s) {
 
 bool tiled_supports(const FwdParams& p) {
   if ((p.dtype != 1 && p.dtype != 2) || (p.D != 64 && p.D != 128) || p.num_splits != 1) return false;
+  // attention dropout is built for no mask and causal / sliding masks
+  if (p.keep && p.bias != BIAS_NONE && p.bias != BIAS_CAUSAL && p.bias != BIAS_SLIDING) return false;
+  if (p.keep && p.Tq * p.keep_words * 4 > 0x7fffffffLL) return false;   // keep rows of a head: 32-bit offsets
   if (p.bias == BIAS_ADDITIVE || p.bias == BIAS_BOOL) {
     // mask blocks are copied by 16-byte chunks along contiguous keys; row
     // offsets of one block and every element offset stay within 32 / 64 bits

@@ -233,8 +233,10 @@ int sdpa_dropout_mask(uint64_t seed, uint32_t step, float rate, int64_t B, int64
  * weights of sdpa_fwd and Z = keep bit * 65536 / (65536 - thresh).  Arguments
  * as in sdpa_fwd, plus the keep bits (required, device) and the rate that
  * produced them.  lse (optional) is that of the undropped scores.
- * Runs on the general matrix-core kernel (bf16, head_dim 64 / 128, positive
- * scale), else on the generic kernel; the workspace is not used (may be NULL).
+ * Runs on the double-buffered matrix-core kernel (bf16 / fp16, head_dim
+ * 64 / 128, no mask or a causal / sliding mask, positive scale), else on the
+ * general matrix-core kernel (bf16, head_dim 64 / 128, positive scale), else
+ * on the generic kernel; the workspace is not used (may be NULL).
  */
 int sdpa_fwd_dropout(const void* q, const void* k, const void* v, void* o, int dtype, int out_dtype, int layout,
                      int64_t B, int64_t Hq, int64_t Hkv, int64_t Tq, int64_t Tkv, int64_t D, float scale,

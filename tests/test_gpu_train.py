@@ -88,8 +88,12 @@ FWD_CASES = [
 ]
 
 
+@pytest.mark.parametrize("tiled", [1, 0], ids=["tiled-on", "tiled-off"])
 @pytest.mark.parametrize("case", FWD_CASES, ids=[f"{c[0]}-{c[1]}-D{c[7]}-{c[8] if isinstance(c[8], str) else (c[8] or {}).get('kind', 'none')}" for c in FWD_CASES])
-def test_dropout_forward_matches_oracle(gpu, case):
+def test_dropout_forward_matches_oracle(gpu, case, tiled):
+    """Each case with the double-buffered kernel allowed (it takes 16-bit
+    inputs at head_dim 64 / 128 with no mask or a causal / sliding mask) and
+    with it switched off (the general MFMA kernel, else the generic one)."""
     dts, layout, B, Hq, Hkv, Tq, Tkv, D, mask = case
     dt = DT[dts]
     rng = np.random.default_rng(31)
@@ -107,10 +111,17 @@ def test_dropout_forward_matches_oracle(gpu, case):
     rate = 0.2
     keep = st.dropout_keep(11, 4, rate, B, Hq, Tq, Tkv)
     scale = 1.0 / np.sqrt(D)
-    o, lse = gpu.sdpa(q.cuda(), k.cuda(), v.cuda(), layout=layout, scale=scale, mask=gmask,
-                      out_dtype=torch.float32, return_lse=True,
-                      dropout={"keep": keep_words_tensor(keep), "rate": rate})
-    torch.cuda.synchronize()
+    gpu.set_tuning("tiled", tiled)
+    try:
+        o, lse = gpu.sdpa(q.cuda(), k.cuda(), v.cuda(), layout=layout, scale=scale, mask=gmask,
+                          out_dtype=torch.float32, return_lse=True,
+                          dropout={"keep": keep_words_tensor(keep), "rate": rate})
+        torch.cuda.synchronize()
+        kernel = gpu.last_kernel()
+    finally:
+        gpu.set_tuning("tiled", 1)
+    eligible = dts != "fp32" and D in (64, 128) and (mask is None or isinstance(mask, dict))
+    assert (kernel == "flash_tiled_kernel") == bool(tiled and eligible), kernel
     ref = st.sdpa_train_fwd(np64(q), np64(k), np64(v), layout=layout, scale=scale, mask=omask, keep=keep, rate=rate)
     # the forward tolerances of the same kernels; kept weights are scaled by 1 / (1 - rate) on the output
     assert max_err(np64(o), ref["o"]) < TOL[dts] * 1.5
