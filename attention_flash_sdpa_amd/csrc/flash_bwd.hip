@@ -462,7 +462,7 @@ __global__ __launch_bounds__(256, (D == 128 ? 1 : 2)) void bwd_dkdv_kernel(BwdPa
         float xb = -l2[r];
         if (MODE == B_INDEX && edge) {
           const int q32 = qa32 + 8 * (r / 4) + 4 * g + (r % 4);
-          ok = ok && q32 >= mlo && q32 < mhi;
+          ok = ok & (q32 >= mlo) & (q32 < mhi);
         }
         if (MODE == B_TENSOR) {
           if (ok && qq < p.Tq) xb += mask_value(p, b, hq, qq, key) * kLog2e;
@@ -482,7 +482,8 @@ __global__ __launch_bounds__(256, (D == 128 ? 1 : 2)) void bwd_dkdv_kernel(BwdPa
           }
           xb += bias4[r % 4];
         }
-        const float pr = ok ? __builtin_amdgcn_exp2f(fmaf(sacc[r], c2, xb)) : 0.0f;
+        // a select before the exponential, not after it (exp2(-inf) = 0): no branch per score
+        const float pr = __builtin_amdgcn_exp2f(ok ? fmaf(sacc[r], c2, xb) : -INFINITY);
         float dw = dpacc[r];
         if (DROP) {
           const bool kept = (kw[r] >> nl) & 1u;
@@ -581,6 +582,8 @@ __global__ __launch_bounds__(256, (D == 128 ? 1 : 2)) void bwd_dq_kernel(BwdPara
   const float* thr = nullptr;
   const float* twr = nullptr;
   __attribute__((address_space(3))) float* dts = nullptr;
+  constexpr bool FASTM = MODE == B_NONE || MODE == B_INDEX || MODE == B_RELPOS64;
+  const bool sl = MODE == B_INDEX && p.bias == BIAS_SLIDING;
   // 64-wide grid: a 64-key tile is one grid row y, and the lane's 32 registers of
   // a tile always hold the same 32 columns, so the running sums of dS per column
   // stay in registers (term_w of those columns is re-read per tile, from cache).
@@ -671,6 +674,32 @@ __global__ __launch_bounds__(256, (D == 128 ? 1 : 2)) void bwd_dq_kernel(BwdPara
       float tsum = 0.0f;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
+        // No mask, index masks, 64-wide rel-pos grids: masks are tested only on the
+        // 32-key sub-tiles that the band edge or the end of the keys crosses (a
+        // wave-uniform test), per score in 32-bit offsets from the sub-tile's first
+        // key (allowed: lim_lo < offset <= lim_hi); sub-tiles with no allowed pair
+        // for the wave's queries are skipped.
+        const int64_t kbase = k0 + 32 * kb;
+        bool edge = false;
+        int lim_hi = 31, lim_lo = -1;
+        if (FASTM) {
+          if (MODE == B_INDEX) {
+            if (kbase > wq0 + 31 + p.offset) continue;
+            if (sl && kbase + 31 <= wq0 + p.offset - p.window) continue;
+            if (kbase + 31 > wq0 + p.offset) edge = true;
+            if (sl && kbase <= wq0 + 31 + p.offset - p.window) edge = true;
+          }
+          if (kbase + 32 > p.Tkv) edge = true;
+          if (edge) {
+            int64_t h64 = p.Tkv - 1 - kbase, l64 = -1;
+            if (MODE == B_INDEX) {
+              h64 = min(h64, qrow + p.offset - kbase);
+              if (sl) l64 = qrow + p.offset - p.window - kbase;
+            }
+            lim_hi = (int)max(min(h64, (int64_t)31), (int64_t)-1);
+            lim_lo = (int)max(min(l64, (int64_t)32), (int64_t)-1);
+          }
+        }
         f32x16_e sacc = (f32x16_e){}, dpacc = (f32x16_e){};
 #pragma unroll
         for (int c = 0; c < C::QC; ++c) {
@@ -701,8 +730,32 @@ __global__ __launch_bounds__(256, (D == 128 ? 1 : 2)) void bwd_dq_kernel(BwdPara
             for (int e = 0; e < 4; ++e) tw2[4 * a + e] = t[e] * kLog2e;
           }
         }
+        if (FASTM) {
+          float xs[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
+          for (int r = 0; r < 16; ++r) {
+            float xb = -l2;
+            if (RP64) xb += th2 + tw2[r];
+            xs[r] = fmaf(sacc[r], c2, xb);
+          }
+          if (edge) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int kofs = 8 * (r / 4) + 4 * g + (r % 4);
+              xs[r] = ((kofs <= lim_hi) & (kofs > lim_lo)) ? xs[r] : -INFINITY;
+            }
+          }
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int kofs = 8 * (r / 4) + 4 * g + (r % 4);
+            const float pr = __builtin_amdgcn_exp2f(xs[r]);      // exp2(-inf) = 0: masked scores
+            float dw = dpacc[r];
+            if (DROP) dw = ((kw[kb] >> kofs) & 1u) ? dw * p.keep_scale : 0.0f;
+            ds[r] = pr * (dw - dl);
+          }
+        }
+#pragma unroll
+        for (int r = 0; r < 16 && !FASTM; ++r) {
           const int kofs = 8 * (r / 4) + 4 * g + (r % 4);
           const int64_t key = k0 + 32 * kb + kofs;
           bool ok = key < p.Tkv;
