@@ -455,17 +455,16 @@ __global__ __launch_bounds__(256, (D == 128 ? 1 : 2)) void bwd_dkdv_kernel(BwdPa
           kw[4 * a + e] = z[e];
         }
       }
+      // exponent arguments first, then the index mask under one wave-uniform branch, then
+      // the exponentials: masked scores become -inf before exp2 (exp2(-inf) = 0), so no
+      // score takes a branch of its own
+      float xs[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int64_t qq = qa + 8 * (r / 4) + 4 * g + (r % 4);
-        bool ok = kvalid;
         float xb = -l2[r];
-        if (MODE == B_INDEX && edge) {
-          const int q32 = qa32 + 8 * (r / 4) + 4 * g + (r % 4);
-          ok = ok & (q32 >= mlo) & (q32 < mhi);
-        }
         if (MODE == B_TENSOR) {
-          if (ok && qq < p.Tq) xb += mask_value(p, b, hq, qq, key) * kLog2e;
+          if (kvalid && qq < p.Tq) xb += mask_value(p, b, hq, qq, key) * kLog2e;
         }
         if (MODE == B_RELPOS) {      // term_h[q, row(key)] + term_w[q, col(key)] from the staged rows
           const int qo = 32 * s + 8 * (r / 4) + 4 * g + (r % 4);
@@ -482,8 +481,18 @@ __global__ __launch_bounds__(256, (D == 128 ? 1 : 2)) void bwd_dkdv_kernel(BwdPa
           }
           xb += bias4[r % 4];
         }
-        // a select before the exponential, not after it (exp2(-inf) = 0): no branch per score
-        const float pr = __builtin_amdgcn_exp2f(ok ? fmaf(sacc[r], c2, xb) : -INFINITY);
+        xs[r] = kvalid ? fmaf(sacc[r], c2, xb) : -INFINITY;
+      }
+      if (MODE == B_INDEX && edge) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int q32 = qa32 + 8 * (r / 4) + 4 * g + (r % 4);
+          xs[r] = ((q32 >= mlo) & (q32 < mhi)) ? xs[r] : -INFINITY;
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float pr = __builtin_amdgcn_exp2f(xs[r]);
         float dw = dpacc[r];
         if (DROP) {
           const bool kept = (kw[r] >> nl) & 1u;
