@@ -60,11 +60,19 @@ __global__ __launch_bounds__(256) void attn_weights_kernel(FwdParams p, float* o
     for (int v = 0; v < 4; ++v) {
       const int64_t j = j0 + 4 * tx + v;
       float z = acc[u][v] * p.scale;
-      bool ok = j < p.Tkv && lse != -INFINITY;
-      if (p.bias == BIAS_CAUSAL || p.bias == BIAS_SLIDING) ok = ok && index_allowed(p.bias, i, j, p.offset, p.window);
-      if (ok && (p.bias == BIAS_ADDITIVE || p.bias == BIAS_BOOL)) z += tensor_mask_bias(p, b, h, i, j);
-      float wv = ok ? __expf(z - lse) : 0.0f;
-      if (kr && ok) wv = ((kr[j >> 5] >> (j & 31)) & 1u) ? wv * p.keep_scale : 0.0f;
+      // conditions combined without short-circuit and applied before the exponential
+      // (exp(-inf) = 0), so no score takes a branch of its own
+      bool ok = (j < p.Tkv) & (lse != -INFINITY);
+      if (p.bias == BIAS_CAUSAL) ok = ok & (j <= i + p.offset);
+      if (p.bias == BIAS_SLIDING) ok = ok & (j <= i + p.offset) & (j > i + p.offset - p.window);
+      if (p.bias == BIAS_ADDITIVE || p.bias == BIAS_BOOL) {
+        if (ok) z += tensor_mask_bias(p, b, h, i, j);
+      }
+      float wv = __expf(ok ? z - lse : -INFINITY);
+      if (kr) {      // the word index is clamped to the row, so the load needs no guard
+        const uint32_t word = kr[min(j, p.Tkv - 1) >> 5];
+        wv = (ok & (((word >> (j & 31)) & 1u) != 0u)) ? wv * p.keep_scale : 0.0f;
+      }
       w[v] = wv;
     }
     float* orow = out + (bh * p.Tq + i) * p.Tkv + j0 + 4 * tx;
