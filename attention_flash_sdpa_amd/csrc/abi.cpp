@@ -525,7 +525,7 @@ int sdpa_attention_weights(const void* q, const void* k, int dtype, int layout, 
   }
   hipError_t e = sdpa::launch_attn_weights(p, weights, (hipStream_t)stream);
   if (e != hipSuccess) return fail(SDPA_ERR_HIP, "attention weights launch failed: %s", hipGetErrorString(e));
-  g_last_kernel = "attn_weights_kernel";
+  g_last_kernel = sdpa::attn_weights_mfma(p) ? "attn_weights_mfma_kernel" : "attn_weights_kernel";
   return SDPA_OK;
 }
 

@@ -7,10 +7,19 @@
 // given and 1 otherwise.  Written as fp32 [B, Hq, Tq, Tkv].  This is a debug
 // output: the T_q x T_kv write bounds it, and it runs on the vector ALUs.
 //
-// One workgroup per 64 x 64 block of one (batch, head); the Q and K blocks
-// are staged through LDS as fp32 and each thread forms a 4 x 4 patch, stored
-// as 16-byte rows (a wavefront covers four full 256-byte output rows).
+// 16-bit inputs at head_dim 32 / 64 / 128: the scores come from the matrix
+// cores (32x32x16 products, fp32 accumulation).  A workgroup is 4 waves of 32
+// queries over 256 keys; each wave keeps its queries' fragments in registers
+// and loads each 32-key block's K fragments straight from memory (the four
+// waves read the same lines).  A lane holds one key and 16 queries of the
+// block, so every store instruction writes two 128-byte row segments; the
+// stores bypass the caches' retention (the output is written once).
+//
+// Other inputs (fp32, other head dims): one workgroup per 64 x 64 block of
+// one (batch, head); the Q and K blocks are staged through LDS as fp32 and
+// each thread forms a 4 x 4 patch, stored as 16-byte rows.
 #include "common.h"
+#include "elem16.h"
 
 namespace sdpa {
 namespace {
@@ -86,6 +95,106 @@ __global__ __launch_bounds__(256) void attn_weights_kernel(FwdParams p, float* o
   }
 }
 
+enum WMode { W_NONE = 0, W_INDEX = 1, W_TENSOR = 2 };
+
+template <typename E, int D, int MODE>
+__global__ __launch_bounds__(256) void attn_weights_mfma_kernel(FwdParams p, float* out) {
+  typedef typename Vec16<E>::x8 e8;
+  constexpr int QC = D / 16;               // 16-deep chunks of head_dim
+  constexpr int KB = 8;                    // 32-key blocks per workgroup
+  const int lane = threadIdx.x & 63, g = lane >> 5, nl = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t bh = blockIdx.z, b = bh / p.Hq, h = bh % p.Hq;
+  const int64_t hk = h / (p.Hq / p.Hkv);
+  const int64_t q0 = (int64_t)blockIdx.y * 128 + 32 * wave;
+  if (q0 >= p.Tq) return;                  // no barrier in this kernel: idle waves leave
+  const E* qp = (const E*)p.q + b * p.q_sb + h * p.q_sh;
+  const E* kp = (const E*)p.k + b * p.k_sb + hk * p.k_sh;
+  // A operand of S = Q . K^T: query q0 + lane % 32, head dims 16 c + 8 (lane / 32) .. + 7
+  const int64_t qa = q0 + nl;
+  e8 qf[QC];
+#pragma unroll
+  for (int c = 0; c < QC; ++c) qf[c] = qa < p.Tq ? *(const e8*)(qp + qa * p.q_st + 16 * c + 8 * g) : (e8){};
+  // result rows of this lane: queries q0 + 8 (r / 4) + 4 (lane / 32) + r % 4
+  float lse[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int64_t i = q0 + 8 * (r / 4) + 4 * g + (r % 4);
+    lse[r] = i < p.Tq ? p.lse[bh * p.Tq + i] : -INFINITY;
+  }
+  const bool sl = p.bias == BIAS_SLIDING;
+  for (int kb = 0; kb < KB; ++kb) {
+    const int64_t k0 = (int64_t)blockIdx.x * (32 * KB) + 32 * kb;
+    if (k0 >= p.Tkv) break;
+    const int64_t j = k0 + nl;               // this lane's key
+    const bool jok = j < p.Tkv;
+    f32x16_e sacc = (f32x16_e){};
+#pragma unroll
+    for (int c = 0; c < QC; ++c) {
+      const e8 kf = jok ? *(const e8*)(kp + j * p.k_st + 16 * c + 8 * g) : (e8){};
+      sacc = mfma32(qf[c], kf, sacc);
+    }
+    // Row r of this lane is query i0 + ro(r), ro(r) = 8 (r / 4) + r % 4, i0 = q0 + 4 (lane / 32).
+    // In 32-bit offsets: i < Tq iff ro < nrow; causal j <= i + offset iff ro >= -dj;
+    // sliding also i + offset - j < window iff ro < window - dj (dj = i0 + offset - j, clamped).
+    const int64_t i0 = q0 + 4 * g;
+    const int nrow = (int)min(p.Tq - i0, (int64_t)32);
+    int dlo = 0, dhi = 32;
+    if (MODE == W_INDEX) {
+      const int64_t dj = i0 + p.offset - j;
+      dlo = (int)max(min(-dj, (int64_t)33), (int64_t)-1);
+      dhi = sl ? (int)max(min(p.window - dj, (int64_t)33), (int64_t)-1) : 32;
+    }
+    float* orow = out + (bh * p.Tq + i0) * p.Tkv + j;
+    const uint32_t* krow = p.keep ? p.keep + (bh * p.Tq + i0) * p.keep_words + (k0 >> 5) : nullptr;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int ro = 8 * (r / 4) + (r % 4);
+      if (!jok || ro >= nrow) continue;
+      float z = sacc[r] * p.scale;
+      bool ok = lse[r] != -INFINITY;
+      if (MODE == W_INDEX) ok = ok & (ro >= dlo) & (ro < dhi);
+      if (MODE == W_TENSOR) {
+        if (ok) z += tensor_mask_bias(p, b, h, i0 + ro, j);
+      }
+      float w = __expf(ok ? z - lse[r] : -INFINITY);
+      if (krow) {
+        const uint32_t word = krow[ro * p.keep_words];
+        w = ((word >> nl) & 1u) ? w * p.keep_scale : 0.0f;
+      }
+      __builtin_nontemporal_store(w, orow + ro * p.Tkv);
+    }
+  }
+}
+
+template <typename E, int D>
+void launch_mfma_d(const FwdParams& p, float* w, hipStream_t s) {
+  dim3 grid((unsigned)((p.Tkv + 255) / 256), (unsigned)((p.Tq + 127) / 128), (unsigned)(p.B * p.Hq));
+  if (p.bias == BIAS_CAUSAL || p.bias == BIAS_SLIDING)
+    hipLaunchKernelGGL((attn_weights_mfma_kernel<E, D, W_INDEX>), grid, dim3(256), 0, s, p, w);
+  else if (p.bias == BIAS_ADDITIVE || p.bias == BIAS_BOOL)
+    hipLaunchKernelGGL((attn_weights_mfma_kernel<E, D, W_TENSOR>), grid, dim3(256), 0, s, p, w);
+  else
+    hipLaunchKernelGGL((attn_weights_mfma_kernel<E, D, W_NONE>), grid, dim3(256), 0, s, p, w);
+}
+
+template <typename E>
+void launch_mfma(const FwdParams& p, float* w, hipStream_t s) {
+  if (p.D == 32) launch_mfma_d<E, 32>(p, w, s);
+  else if (p.D == 64) launch_mfma_d<E, 64>(p, w, s);
+  else launch_mfma_d<E, 128>(p, w, s);
+}
+
+// 16-byte fragment loads: 16-byte aligned bases, element strides in multiples of 8.
+bool mfma_ok(const FwdParams& p) {
+  if (p.dtype != 1 && p.dtype != 2) return false;
+  if (p.D != 32 && p.D != 64 && p.D != 128) return false;
+  if (((uintptr_t)p.q & 15) || ((uintptr_t)p.k & 15)) return false;
+  for (int64_t st : {p.q_sb, p.q_sh, p.q_st, p.k_sb, p.k_sh, p.k_st})
+    if (st % 8 != 0) return false;
+  return (p.Tq + 127) / 128 <= 65535;
+}
+
 template <typename TIN>
 hipError_t launch_t(const FwdParams& p, float* w, hipStream_t s) {
   dim3 grid((unsigned)((p.Tkv + 63) / 64), (unsigned)((p.Tq + 63) / 64), (unsigned)(p.B * p.Hq));
@@ -97,7 +206,14 @@ hipError_t launch_t(const FwdParams& p, float* w, hipStream_t s) {
 
 }  // namespace
 
+bool attn_weights_mfma(const FwdParams& p) { return mfma_ok(p); }
+
 hipError_t launch_attn_weights(const FwdParams& p, float* weights, hipStream_t s) {
+  if (mfma_ok(p)) {
+    if (p.dtype == 2) launch_mfma<_Float16>(p, weights, s);
+    else launch_mfma<__bf16>(p, weights, s);
+    return hipGetLastError();
+  }
   if (p.dtype == 0) return launch_t<float>(p, weights, s);
   return p.dtype == 2 ? launch_t<_Float16>(p, weights, s) : launch_t<__bf16>(p, weights, s);
 }

@@ -154,5 +154,7 @@ hipError_t launch_bwd(const BwdParams& p, hipStream_t s);
 hipError_t launch_relpos_bwd_tail(const BwdParams& p, hipStream_t s);
 // Attention weights [B, Hq, Tq, Tkv] fp32 from the forward pass's lse (any dtype, head_dim <= 128).
 hipError_t launch_attn_weights(const FwdParams& p, float* weights, hipStream_t s);
+// True if the call runs on the matrix-core weights kernel (16-bit inputs, head_dim 32 / 64 / 128).
+bool attn_weights_mfma(const FwdParams& p);
 
 }  // namespace sdpa

@@ -373,12 +373,18 @@ def bench_train_forward(fa, wl, g, args):
         torch.cuda.synchronize()
         sec = (time.perf_counter() - t0) / args.steps
         ms = _events_ms(call, args.steps, 2.0 + 1.0 * args.steps)
-        nbytes = wl.B * wl.Hq * wl.Tq * wl.Tkv * 4
+        call()
+        kernel = fa.last_kernel()
+        elem = 2 if wl.dtype in ("bf16", "fp16") else 4
+        wbytes = wl.B * wl.Hq * wl.Tq * wl.Tkv * 4
+        # algorithmic bytes: the fp32 weights written once, Q, K and lse read once
+        nbytes = wbytes + (wl.B * wl.Hq * wl.Tq + wl.B * wl.Hkv * wl.Tkv) * wl.D * elem + wl.B * wl.Hq * wl.Tq * 4
         gbs = nbytes / (ms * 1e-3) / 1e9
-        # the kernel forms each score as an fp32 dot product on the vector ALUs (2 D FLOPs per score):
-        # whichever of that and the 4-byte write per score takes longer at peak bounds it
+        # 2 D FLOPs per score: on the matrix cores (16-bit inputs) the write bounds the kernel; on the
+        # vector ALUs (fp32 inputs, other head dims) whichever of the two takes longer at peak does
         vflops = 2 * wl.D * wl.B * wl.Hq * wl.Tq * wl.Tkv
-        alu_bound = vflops / (FP32_VECTOR_PEAK_TFLOPS * 1e12) > nbytes / (HBM_PEAK_GBS * 1e9)
+        alu_bound = (kernel == "attn_weights_kernel"
+                     and vflops / (FP32_VECTOR_PEAK_TFLOPS * 1e12) > nbytes / (HBM_PEAK_GBS * 1e9))
         line = {"metric": "attention-weights output GB/s (fp32 [B, Hq, Tq, Tkv])",
                 "value": round(nbytes / sec / 1e9, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
                 "warmup": args.warmup, "ms_per_step": round(sec * 1e3, 5), "higher_is_better": True,
@@ -392,9 +398,9 @@ def bench_train_forward(fa, wl, g, args):
                              if alu_bound else
                              {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                               "frac": round(gbs / HBM_PEAK_GBS, 4)})}
-        line["roofline"].update({"traffic": None, "kernel": "attn_weights_kernel", "kernel_ms": round(ms, 5),
+        line["roofline"].update({"traffic": None, "kernel": kernel, "kernel_ms": round(ms, 5),
                                  "algorithmic_bytes_per_launch": nbytes, "flop_per_launch": vflops,
-                                 "write_GB_per_s": round(gbs, 1)})
+                                 "write_GB_per_s": round(wbytes / (ms * 1e-3) / 1e9, 1)})
     print(json.dumps(line))
 
 

@@ -130,26 +130,52 @@ def test_dropout_forward_matches_oracle(gpu, case, tiled):
 
 
 # --------------------------------------------------------- attention weights --
-@pytest.mark.parametrize("dts,mask,drop", [("bf16", None, False), ("bf16", {"kind": "causal", "offset": 1}, True),
-                                           ("fp32", {"kind": "sliding", "window": 9, "offset": 0}, False),
-                                           ("fp16", None, True)])
-def test_attention_weights_match_oracle(gpu, dts, mask, drop):
+WEIGHT_CASES = [
+    # dtype, layout, B, Hq, Hkv, Tq, Tkv, D, mask, drop, matrix-core kernel
+    ("bf16", "bhsd", 2, 2, 1, 70, 100, 64, None, False, True),
+    ("bf16", "bhsd", 2, 2, 1, 70, 100, 64, {"kind": "causal", "offset": 1}, True, True),
+    ("fp32", "bhsd", 2, 2, 1, 70, 100, 64, {"kind": "sliding", "window": 9, "offset": 0}, False, False),
+    ("fp16", "bhsd", 2, 2, 1, 70, 100, 64, None, True, True),
+    # 3 query blocks of 128 and 3 key ranges of 256, both ragged; GQA; bshd
+    ("bf16", "bshd", 1, 4, 2, 300, 520, 128, {"kind": "sliding", "window": 100, "offset": 3}, True, True),
+    ("bf16", "bhsd", 1, 2, 2, 130, 100, 32, {"kind": "causal", "offset": -40}, False, True),     # dead rows
+    ("fp16", "bhsd", 1, 2, 1, 50, 90, 64, "additive", False, True),
+    ("bf16", "bhsd", 1, 2, 2, 40, 70, 64, "bool", True, True),
+    ("bf16", "bhsd", 1, 2, 2, 40, 70, 16, None, False, False),                                 # vector ALUs
+]
+
+
+@pytest.mark.parametrize("case", WEIGHT_CASES, ids=[
+    f"{c[0]}-{c[1]}-{c[5]}x{c[6]}-D{c[7]}-{c[8] if isinstance(c[8], str) else (c[8] or {}).get('kind', 'none')}"
+    f"{'-drop' if c[9] else ''}" for c in WEIGHT_CASES])
+def test_attention_weights_match_oracle(gpu, case):
+    """Weights against the oracle's, on the matrix-core kernel (16-bit inputs at head_dim 32 / 64 / 128)
+    and on the vector-ALU kernel (fp32 inputs, other head dims), asserting which one ran."""
+    dts, layout, B, Hq, Hkv, Tq, Tkv, D, mask, drop, mfma = case
     dt = DT[dts]
     rng = np.random.default_rng(32)
-    B, Hq, Hkv, Tq, Tkv, D = 2, 2, 1, 70, 100, 64
-    q, k = draw(rng, (B, Hq, Tq, D), dt), draw(rng, (B, Hkv, Tkv, D), dt)
-    v = draw(rng, (B, Hkv, Tkv, D), dt)
+    q, k = draw(rng, shp(layout, B, Hq, Tq, D), dt), draw(rng, shp(layout, B, Hkv, Tkv, D), dt)
+    v = draw(rng, shp(layout, B, Hkv, Tkv, D), dt)
     scale = 0.125
+    omask = gmask = mask
+    if mask == "additive":
+        m = torch.from_numpy(rng.standard_normal((1, Hq, Tq, Tkv), dtype=np.float32))
+        omask, gmask = {"kind": "additive", "data": m.numpy()}, {"kind": "additive", "data": m.cuda()}
+    elif mask == "bool":
+        m = torch.from_numpy(rng.random((B, 1, Tq, Tkv)) < 0.7)
+        m[..., 0] = True
+        omask, gmask = {"kind": "bool", "data": m.numpy()}, {"kind": "bool", "data": m.cuda()}
     keep, rate, dro = None, 0.0, None
     if drop:
         rate = 0.25
         keep = st.dropout_keep(3, 9, rate, B, Hq, Tq, Tkv)
         dro = {"keep": keep_words_tensor(keep), "rate": rate}
-    lse = oracle.sdpa(np64(q), np64(k), np64(v), scale=scale, mask=mask)["lse"]
-    w = gpu.attention_weights(q.cuda(), k.cuda(), torch.from_numpy(lse.astype(np.float32)).cuda(), scale=scale,
-                              mask=mask, dropout=dro)
+    lse = oracle.sdpa(np64(q), np64(k), np64(v), layout=layout, scale=scale, mask=omask)["lse"]
+    w = gpu.attention_weights(q.cuda(), k.cuda(), torch.from_numpy(lse.astype(np.float32)).cuda(), layout=layout,
+                              scale=scale, mask=gmask, dropout=dro)
     torch.cuda.synchronize()
-    ref = st.attention_weights(np64(q), np64(k), scale=scale, mask=mask, keep=keep, rate=rate)
+    assert gpu.last_kernel() == ("attn_weights_mfma_kernel" if mfma else "attn_weights_kernel")
+    ref = st.attention_weights(np64(q), np64(k), layout=layout, scale=scale, mask=omask, keep=keep, rate=rate)
     assert max_err(np64(w), ref) < 2e-5
 
 
