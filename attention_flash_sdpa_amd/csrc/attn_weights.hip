@@ -107,7 +107,7 @@ __global__ __launch_bounds__(256) void attn_weights_mfma_kernel(FwdParams p, flo
   const int64_t bh = blockIdx.z, b = bh / p.Hq, h = bh % p.Hq;
   const int64_t hk = h / (p.Hq / p.Hkv);
   const int64_t q0 = (int64_t)blockIdx.y * 128 + 32 * wave;
-  if (q0 >= p.Tq) return;                  // no barrier in this kernel: idle waves leave
+  if (q0 >= p.Tq) return;                  // no workgroup barrier in this kernel: idle waves leave
   const E* qp = (const E*)p.q + b * p.q_sb + h * p.q_sh;
   const E* kp = (const E*)p.k + b * p.k_sb + hk * p.k_sh;
   // A operand of S = Q . K^T: query q0 + lane % 32, head dims 16 c + 8 (lane / 32) .. + 7
@@ -123,6 +123,13 @@ __global__ __launch_bounds__(256) void attn_weights_mfma_kernel(FwdParams p, flo
     lse[r] = i < p.Tq ? p.lse[bh * p.Tq + i] : -INFINITY;
   }
   const bool sl = p.bias == BIAS_SLIDING;
+  // per-wave 32 x 32 fp32 tile for the transposed write-back; rows padded to 36 floats so
+  // the two lane halves (rows 4 apart) write distinct banks and 16-byte reads stay aligned
+  constexpr int TP = 36;
+  __shared__ __attribute__((aligned(16))) float tiles[4][32 * TP];
+  float* tw = tiles[wave];
+  // 16-byte stores need 16-byte aligned rows
+  const bool vec_ok = (p.Tkv % 4 == 0) && (((uintptr_t)out & 15) == 0);
   for (int kb = 0; kb < KB; ++kb) {
     const int64_t k0 = (int64_t)blockIdx.x * (32 * KB) + 32 * kb;
     if (k0 >= p.Tkv) break;
@@ -145,25 +152,50 @@ __global__ __launch_bounds__(256) void attn_weights_mfma_kernel(FwdParams p, flo
       dlo = (int)max(min(-dj, (int64_t)33), (int64_t)-1);
       dhi = sl ? (int)max(min(p.window - dj, (int64_t)33), (int64_t)-1) : 32;
     }
-    float* orow = out + (bh * p.Tq + i0) * p.Tkv + j;
     const uint32_t* krow = p.keep ? p.keep + (bh * p.Tq + i0) * p.keep_words + (k0 >> 5) : nullptr;
+    // weights of this lane's 16 (query, key) pairs into the wave's tile, row 4 (lane / 32) + ro(r)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int ro = 8 * (r / 4) + (r % 4);
-      if (!jok || ro >= nrow) continue;
+      const bool inb = jok & (ro < nrow);
       float z = sacc[r] * p.scale;
-      bool ok = lse[r] != -INFINITY;
+      bool ok = inb & (lse[r] != -INFINITY);
       if (MODE == W_INDEX) ok = ok & (ro >= dlo) & (ro < dhi);
       if (MODE == W_TENSOR) {
         if (ok) z += tensor_mask_bias(p, b, h, i0 + ro, j);
       }
       float w = __expf(ok ? z - lse[r] : -INFINITY);
-      if (krow) {
+      if (krow && inb) {
         const uint32_t word = krow[ro * p.keep_words];
         w = ((word >> nl) & 1u) ? w * p.keep_scale : 0.0f;
       }
-      __builtin_nontemporal_store(w, orow + ro * p.Tkv);
+      tw[(ro + 4 * g) * TP + nl] = w;
     }
+    // lanes exchange values through the tile: order the writes before the reads
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // row-major read-back: lane l takes row 8 jj + l / 8, keys 4 (l % 8) .. + 3; each store
+    // instruction writes 8 rows of 128 contiguous bytes
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int row = 8 * jj + (lane >> 3), c4 = 4 * (lane & 7);
+      const f32x4 v = *(const f32x4*)(tw + row * TP + c4);
+      const int64_t i = q0 + row, j0 = k0 + c4;
+      if (i >= p.Tq) continue;
+      float* o = out + (bh * p.Tq + i) * p.Tkv + j0;
+      if (vec_ok && j0 + 3 < p.Tkv) {
+        __builtin_nontemporal_store(v, (f32x4*)o);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (j0 + e < p.Tkv) __builtin_nontemporal_store(v[e], o + e);
+      }
+    }
+    // the next block's writes come after these reads
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
 }
 
