@@ -304,6 +304,9 @@ int sdpa_relpos_bwd(const void* q, const void* k, const void* v, const void* o, 
  *   weights  device output [B, Hq, Tq, Tkv] fp32 (a T x T array: a debug output).
  *   lse      [B, Hq, Tq] fp32 from sdpa_fwd / sdpa_fwd_dropout on the same inputs.
  * Any dtype and head_dim up to 128; B * Hq and Tq / 64 must stay below 65536.
+ * 16-bit inputs at head_dim 32 / 64 / 128 with 16-byte aligned Q and K and
+ * strides in multiples of 8 elements run on the matrix cores; other calls on
+ * the vector ALUs (same results up to fp32 summation order).
  */
 int sdpa_attention_weights(const void* q, const void* k, int dtype, int layout, int64_t B, int64_t Hq, int64_t Hkv,
                            int64_t Tq, int64_t Tkv, int64_t D, float scale, const sdpa_mask* mask, const float* lse,
