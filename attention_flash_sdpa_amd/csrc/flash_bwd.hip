@@ -544,7 +544,10 @@ __global__ __launch_bounds__(256, (D == 128 ? 1 : 2)) void bwd_dkdv_kernel(BwdPa
 }
 
 // ---------------------------------------------------------------------- dQ --
-template <typename E, int D, int MODE, bool DROP, typename G>
+// RPS (rel-pos grids of at most 32 x 32): the per-query sums of dS over grid rows and
+// columns are matrix products, dT_h^T = E_h^T . dS^T with E_h[key][y] = 1 iff key lies in
+// grid row y (E_w alike), fed the same packed dS as the dQ product; no LDS sums.
+template <typename E, int D, int MODE, bool DROP, typename G, bool RPS = false>
 __global__ __launch_bounds__(256, (D == 128 ? 1 : 2)) void bwd_dq_kernel(BwdParams p) {
   using C = BCfg<D>;
   constexpr int BN = 64;                           // keys per staged tile
@@ -554,7 +557,7 @@ __global__ __launch_bounds__(256, (D == 128 ? 1 : 2)) void bwd_dq_kernel(BwdPara
   // 64-wide grid: then term_w of the workgroup's 128 queries, [128 q][64 + 4 pad] fp32
   constexpr int DOFF = 4 * TK;
   constexpr int TWP = 68;
-  __shared__ __attribute__((aligned(16))) char smem_raw[DOFF + (MODE == B_RELPOS ? 128 * kMaxGT * 4 : 0) +
+  __shared__ __attribute__((aligned(16))) char smem_raw[DOFF + (MODE == B_RELPOS && !RPS ? 128 * kMaxGT * 4 : 0) +
                                                        (MODE == B_RELPOS64 ? 128 * TWP * 4 : 0)];
   lds_char* smem = (lds_char*)smem_raw;
 
@@ -622,6 +625,9 @@ __global__ __launch_bounds__(256, (D == 128 ? 1 : 2)) void bwd_dq_kernel(BwdPara
   if (MODE == B_RELPOS) {
     thr = p.term_h + (qvalid ? srow : 0) * gh;
     twr = p.term_w + (qvalid ? srow : 0) * gw;
+  }
+  f32x16_e dthT = (f32x16_e){}, dtwT = (f32x16_e){};    // RPS: rows y / x of this lane's query
+  if (MODE == B_RELPOS && !RPS) {
     dts = (__attribute__((address_space(3))) float*)(smem + DOFF);
     for (int e = tid; e < 128 * GT; e += 256) dts[e] = 0.0f;
     dts += (32 * wave + nl) * GT;     // this lane's query row
@@ -796,7 +802,7 @@ __global__ __launch_bounds__(256, (D == 128 ? 1 : 2)) void bwd_dq_kernel(BwdPara
             tsum += ds[r];
           }
         }
-        if (MODE == B_RELPOS && qvalid) {
+        if (MODE == B_RELPOS && !RPS && qvalid) {
           // dterm_h[q, row] and dterm_w[q, col] collect dS.  The two lane halves hold the
           // same query, so they add in turn: no two lanes of one instruction share an
           // address, and the order of the additions is fixed.
@@ -819,6 +825,18 @@ __global__ __launch_bounds__(256, (D == 128 ? 1 : 2)) void bwd_dq_kernel(BwdPara
 #pragma unroll
           for (int nb = 0; nb < C::DB; ++nb)
             dqT[nb] = mfma32(ld_tr<E, D>(ks, 32 * kb + 16 * c, 32 * nb, lane), sb, dqT[nb]);
+          if (RPS) {
+            // element e of this lane's k-slice is key offset 8 (r / 4) + 4 g + r % 4, r = 8 c + e
+            // (the order dS is packed in); A row = lane % 32 is the grid row / column index
+            float eh[8], ew[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              eh[e] = krow[8 * c + e] == nl ? 1.0f : 0.0f;
+              ew[e] = kcol[8 * c + e] == nl ? 1.0f : 0.0f;
+            }
+            dthT = mfma32(pack8<E>(eh), sb, dthT);
+            dtwT = mfma32(pack8<E>(ew), sb, dtwT);
+          }
         }
       }
       if (RP64) {
@@ -851,6 +869,14 @@ __global__ __launch_bounds__(256, (D == 128 ? 1 : 2)) void bwd_dq_kernel(BwdPara
 #pragma unroll
           for (int a = 0; a < 4; ++a)
             store4(p.dterm_w + srow * 64 + 32 * kb + 8 * a + 4 * g, &dtw[kb][4 * a], 1.0f);
+      } else if (RPS) {
+        // lane = query; rows y = 8 (r / 4) + 4 g + r % 4 of the two products
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int y = 8 * (r / 4) + 4 * g + (r % 4);
+          if (y < gh) p.dterm_h[srow * gh + y] = dthT[r];
+          if (y < gw) p.dterm_w[srow * gw + y] = dtwT[r];
+        }
       } else {
         for (int c = g; c < GT; c += 2) {
           const float v = dts[c];
@@ -889,12 +915,12 @@ int bmode_of(const BwdParams& p) {
   }
 }
 
-template <typename E, int D, int MODE, bool DROP, typename G>
+template <typename E, int D, int MODE, bool DROP, typename G, bool RPS = false>
 void launch_main(const BwdParams& p, hipStream_t s) {
   dim3 gkv((unsigned)((p.Tkv + 127) / 128), (unsigned)p.Hkv, (unsigned)p.B);
   hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, MODE, DROP, G>), gkv, dim3(256), 0, s, p);
   dim3 gq((unsigned)((p.Tq + 127) / 128), (unsigned)p.Hq, (unsigned)p.B);
-  hipLaunchKernelGGL((bwd_dq_kernel<E, D, MODE, DROP, G>), gq, dim3(256), 0, s, p);
+  hipLaunchKernelGGL((bwd_dq_kernel<E, D, MODE, DROP, G, RPS>), gq, dim3(256), 0, s, p);
 }
 
 template <typename E, int D, typename G>
@@ -903,7 +929,10 @@ void launch_modes(const BwdParams& p, hipStream_t s) {
   switch (bmode_of(p)) {
     case B_NONE: drop ? launch_main<E, D, B_NONE, true, G>(p, s) : launch_main<E, D, B_NONE, false, G>(p, s); break;
     case B_INDEX: drop ? launch_main<E, D, B_INDEX, true, G>(p, s) : launch_main<E, D, B_INDEX, false, G>(p, s); break;
-    case B_RELPOS: launch_main<E, D, B_RELPOS, false, G>(p, s); break;
+    case B_RELPOS:
+      if (p.grid_h <= 32 && p.grid_w <= 32) launch_main<E, D, B_RELPOS, false, G, true>(p, s);
+      else launch_main<E, D, B_RELPOS, false, G>(p, s);
+      break;
     case B_RELPOS64: launch_main<E, D, B_RELPOS64, false, G>(p, s); break;
     default: drop ? launch_main<E, D, B_TENSOR, true, G>(p, s) : launch_main<E, D, B_TENSOR, false, G>(p, s); break;
   }

@@ -320,6 +320,7 @@ RELPOS_BWD_CASES = [
     ("fp16", "bhsd", 1, 2, (14, 14), 64, True),
     ("bf16", "bhsd", 1, 2, (8, 8), 32, True),
     ("bf16", "bhsd", 1, 1, (5, 27), 128, False),      # ragged: T = 135
+    ("bf16", "bhsd", 1, 2, (40, 24), 64, False),      # grid rows beyond 32: dS sums through LDS
 ]
 
 
