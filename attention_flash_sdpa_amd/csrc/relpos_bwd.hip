@@ -99,26 +99,50 @@ __global__ __launch_bounds__(256) void relpos_group_kernel(BwdParams p) {
   const int64_t m_lo = (int64_t)blockIdx.y * per, m_hi = min(total, m_lo + per);
   float* out = (ROWS ? p.group_h : p.group_w) + ((int64_t)blockIdx.y * ngroups + gidx) * aw * D;
   const int tid = threadIdx.x, ta = tid / 16, td = tid % 16;
+  // Staging: thread tid fills column c = tid % 64 of members m = tid / 64 + 4 u (u = 0..3)
+  // of each 16-member step; each slot's member index advances by 16 per step, so its
+  // (b, h, k) position is stepped forward instead of divided out per element.
+  const int c = tid % 64;
+  int64_t bh0[4];
+  int k0[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int64_t mm = m_lo + tid / 64 + 4 * u;
+    bh0[u] = mm / nmem;
+    k0[u] = (int)(mm % nmem);
+  }
   for (int oa = 0; oa < aw; oa += 64)
     for (int od = 0; od < D; od += 64) {
       float acc[4][4] = {};
+      int64_t bh[4];
+      int kk[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        bh[u] = bh0[u];
+        kk[u] = k0[u];
+      }
       for (int64_t m0 = m_lo; m0 < m_hi; m0 += CM) {
         __syncthreads();
-        for (int e = tid; e < CM * 64; e += 256) {
-          const int m = e / 64, c = e % 64;
-          const int64_t mm = m0 + m;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int m = tid / 64 + 4 * u;
           float av = 0.0f, qv = 0.0f;
-          if (mm < m_hi) {
-            const int64_t bh = mm / nmem, k = mm % nmem;
-            const int64_t i = ROWS ? (int64_t)gidx * gw + k : k * gw + gidx;
-            if (oa + c < aw) av = A[(bh * p.Tq + i) * aw + oa + c];
+          if (m0 + m < m_hi) {
+            const int64_t i = ROWS ? (int64_t)gidx * gw + kk[u] : (int64_t)kk[u] * gw + gidx;
+            if (oa + c < aw) av = A[(bh[u] * p.Tq + i) * aw + oa + c];
             if (od + c < D) {
-              const int64_t b = bh / p.Hq, h = bh % p.Hq;
+              const int bh32 = (int)bh[u], hq32 = (int)p.Hq;    // B * Hq < 2^16
+              const int64_t b = bh32 / hq32, h = bh32 - (bh32 / hq32) * hq32;
               qv = (float)((const E*)p.q)[b * p.q_sb + h * p.q_sh + i * p.q_st + od + c];
             }
           }
           as[m][c] = av;
           qs[m][c] = qv;
+          kk[u] += CM;                       // the slot's next member: 16 further on
+          while (kk[u] >= nmem) {
+            kk[u] -= nmem;
+            ++bh[u];
+          }
         }
         __syncthreads();
 #pragma unroll 4
