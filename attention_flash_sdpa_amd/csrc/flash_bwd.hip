@@ -481,10 +481,10 @@ __global__ __launch_bounds__(256, (D == 128 ? 1 : 2)) void bwd_dkdv_kernel(BwdPa
           }
           xb += bias4[r % 4];
         }
-        // A lane is a key: past the end of the keys (zero K, V rows, finite scores) its
-        // weights only reach this key's own dK / dV columns, which are not stored, so
-        // without a mask or with index masks no select is needed.
-        if (MODE == B_NONE || MODE == B_INDEX) xs[r] = fmaf(sacc[r], c2, xb);
+        // A lane is a key: past the end of the keys (zero K, V rows, finite scores; on
+        // 64-wide grids the staged term rows of such keys are zero) its weights only reach
+        // this key's own dK / dV columns, which are not stored, so no select is needed.
+        if (MODE == B_NONE || MODE == B_INDEX || MODE == B_RELPOS64) xs[r] = fmaf(sacc[r], c2, xb);
         else xs[r] = kvalid ? fmaf(sacc[r], c2, xb) : -INFINITY;
       }
       if (MODE == B_INDEX && edge) {

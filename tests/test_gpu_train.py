@@ -321,6 +321,7 @@ RELPOS_BWD_CASES = [
     ("bf16", "bhsd", 1, 2, (8, 8), 32, True),
     ("bf16", "bhsd", 1, 1, (5, 27), 128, False),      # ragged: T = 135
     ("bf16", "bhsd", 1, 2, (40, 24), 64, False),      # grid rows beyond 32: dS sums through LDS
+    ("bf16", "bhsd", 1, 2, (5, 64), 64, False),       # 64 wide, 320 keys: half the last 128-key block past the end
 ]
 
 
