@@ -54,12 +54,14 @@ __global__ __launch_bounds__(256) void dropout_mask_kernel(DropoutParams p, int6
     uint32_t x[4] = {(uint32_t)(j0 / 8), i, bh, p.step};
     philox4x32_10(x, k0, k1);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const uint32_t u = (e & 1) ? (x[e >> 1] >> 16) : (x[e >> 1] & 0xFFFFu);
-      const bool kept = (u >= p.thresh) && (j0 + e < p.Tkv);
-      word |= (uint32_t)kept << (8 * c + e);
+    for (int h = 0; h < 4; ++h) {               // keys 2 h (low half) and 2 h + 1 (high half)
+      word |= (uint32_t)((x[h] & 0xFFFFu) >= p.thresh) << (8 * c + 2 * h);
+      word |= (uint32_t)((x[h] >> 16) >= p.thresh) << (8 * c + 2 * h + 1);
     }
   }
+  // only a row's last word can reach past Tkv: clear those bits once
+  const int64_t valid = p.Tkv - 32 * w;
+  if (valid < 32) word &= valid <= 0 ? 0u : ((1u << valid) - 1u);
   p.keep[idx] = word;
 }
 
