@@ -69,7 +69,7 @@ def load():
             raise RuntimeError(f"{path} is missing: build it with attention_flash_sdpa_amd/build.py")
         lib = ctypes.CDLL(path)
         lib.sdpa_workspace_size.restype = ctypes.c_size_t
-        lib.sdpa_workspace_size.argtypes = [_I64] * 6 + [_I32, _I64, _I64]
+        lib.sdpa_workspace_size.argtypes = [_I32] + [_I64] * 6 + [_F, _I32, _I64, _I64]
         lib.sdpa_fwd.restype = _I32
         lib.sdpa_fwd.argtypes = [_P, _P, _P, _P, _I32, _I32, _I32] + [_I64] * 6 + \
             [_F, ctypes.POINTER(_Mask), _P, _P, ctypes.c_size_t, _P]
@@ -148,40 +148,98 @@ def relpos_fused(dtype, D, grid):
     return bool(load().sdpa_relpos_fused(_DTYPE[dtype], D, grid[0], grid[1]))
 
 
-def workspace_size(B, Hq, Hkv, Tq, Tkv, D, relpos=False, grid=(0, 0)):
-    n = load().sdpa_workspace_size(B, Hq, Hkv, Tq, Tkv, D, int(bool(relpos)), grid[0], grid[1])
+def workspace_size(B, Hq, Hkv, Tq, Tkv, D, relpos=False, grid=(0, 0), dtype=torch.bfloat16, scale=None):
+    """Device workspace bytes of sdpa (relpos=False) or sdpa_relpos for these sizes and dtype."""
+    sc = float("nan") if scale is None else float(scale)
+    n = load().sdpa_workspace_size(_DTYPE[dtype], B, Hq, Hkv, Tq, Tkv, D, sc, int(bool(relpos)), grid[0], grid[1])
     if n == ctypes.c_size_t(-1).value:
         raise ValueError("invalid sizes for sdpa_workspace_size")
     return n
 
 
+def _layout_of(layout):
+    if layout not in _LAYOUT:
+        raise ValueError(f"layout must be 'bhsd' or 'bshd' (got {layout!r})")
+    return _LAYOUT[layout]
+
+
 def _dims(q, k, layout):
+    """(B, Hq, Hkv, Tq, Tkv, D) of rank-4 q and k in the layout; q and k must agree on B and D."""
+    _layout_of(layout)
     if q.dim() != 4 or k.dim() != 4:
         raise ValueError("q, k, v must be rank-4")
     if layout == "bhsd":
         B, Hq, Tq, D = q.shape
-        _, Hkv, Tkv, _ = k.shape
+        Bk, Hkv, Tkv, Dk = k.shape
     else:
         B, Tq, Hq, D = q.shape
-        _, Tkv, Hkv, _ = k.shape
+        Bk, Tkv, Hkv, Dk = k.shape
+    if Bk != B or Dk != D:
+        raise ValueError(f"q {tuple(q.shape)} and k {tuple(k.shape)} disagree on batch or head_dim ({layout})")
     return B, Hq, Hkv, Tq, Tkv, D
 
 
-def _mask_struct(mask, B, Hq, Tq, Tkv, keep):
+def _expect(name, t, shape, dtype, device):
+    """t must be a contiguous tensor of exactly this shape and dtype on q's device."""
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _check_qkv(q, k, v, layout):
+    """Shapes, dtypes and devices of q, k, v (before any launch); returns the sizes."""
+    if q.dtype not in _DTYPE:
+        raise ValueError("q, k, v must be float32, bfloat16 or float16")
+    dims = _dims(q, k, layout)
+    _expect("k", k, tuple(k.shape), q.dtype, q.device)
+    _expect("v", v, tuple(k.shape), q.dtype, q.device)
+    if not q.is_contiguous():
+        raise ValueError("q must be contiguous")
+    return dims
+
+
+def _check_tables(rel_pos_h, rel_pos_w, grid, D, q):
+    gh, gw = grid
+    _expect("rel_pos_h", rel_pos_h, (2 * gh - 1, D), q.dtype, q.device)
+    _expect("rel_pos_w", rel_pos_w, (2 * gw - 1, D), q.dtype, q.device)
+
+
+def _relpos_dims(q, k, v, grid, layout):
+    B, H, Hkv, T, Tkv, D = _check_qkv(q, k, v, layout)
+    gh, gw = grid
+    if Hkv != H or Tkv != T:
+        raise ValueError("rel-pos attention is self-attention: k and v must be shaped like q")
+    if gh <= 0 or gw <= 0 or gh * gw != T:
+        raise ValueError(f"grid {grid} does not match the sequence length {T}")
+    return B, H, T, D
+
+
+def _mask_struct(mask, B, Hq, Tq, Tkv, keep, device):
     m = _Mask()
     m.kind = 0
     if mask is None:
         return m
     kind = mask["kind"]
+    if kind not in _MASK_KIND:
+        raise ValueError(f"unknown mask kind {kind!r}")
     m.kind = _MASK_KIND[kind]
     m.offset = int(mask.get("offset", 0))
     m.window = int(mask.get("window", 0))
     if kind in ("additive", "bool"):
         data = mask["data"]
-        if not data.is_cuda:
-            raise ValueError("mask tensors must live on the GPU (no CPU path exists)")
         if data.dim() != 4:
             raise ValueError("tensor masks are rank-4, broadcastable to [B, Hq, Tq, Tkv]")
+        try:
+            torch.broadcast_shapes(tuple(data.shape), (B, Hq, Tq, Tkv))
+        except RuntimeError:
+            raise ValueError(f"mask of shape {tuple(data.shape)} does not broadcast to {(B, Hq, Tq, Tkv)}") from None
+        if data.device != device:
+            raise ValueError(f"mask is on {data.device}, expected {device} (no CPU path exists)")
         if kind == "bool":
             if data.dtype != torch.bool:
                 raise ValueError("bool masks must be torch.bool")
@@ -203,11 +261,19 @@ def _dropout_args(dropout, B, Hq, Tq, Tkv):
     if dropout is None:
         return None, 0.0
     keep = dropout["keep"]
+    if tuple(keep.shape) != (B, Hq, Tq, (Tkv + 31) // 32):
+        raise ValueError(f"dropout keep bits have shape {tuple(keep.shape)}, expected {(B, Hq, Tq, (Tkv + 31) // 32)}")
     if not keep.is_cuda or keep.dtype != torch.int32 or not keep.is_contiguous():
         raise ValueError("dropout keep bits must be a contiguous int32 GPU tensor (from dropout_mask)")
-    if keep.numel() != B * Hq * Tq * ((Tkv + 31) // 32):
-        raise ValueError("dropout keep bits have the wrong size")
     return _ptr(keep), float(dropout["rate"])
+
+
+def _check_bwd_io(q, o, dout, lse, B, Hq, Tq):
+    if o.dtype not in (q.dtype, torch.float32):
+        raise ValueError("o must be in q's dtype or float32")
+    _expect("o", o, tuple(q.shape), o.dtype, q.device)
+    _expect("dout", dout, tuple(q.shape), q.dtype, q.device)
+    _expect("lse", lse, (B, Hq, Tq), torch.float32, q.device)
 
 
 def sdpa(q, k, v, *, layout="bhsd", scale=None, mask=None, out_dtype=None, return_lse=False,
@@ -221,26 +287,28 @@ def sdpa(q, k, v, *, layout="bhsd", scale=None, mask=None, out_dtype=None, retur
     dropout: None | {"keep": keep bits from dropout_mask, "rate": r} (attention dropout).
     """
     lib = load()
-    _need_gpu(q, k, v)
-    if q.dtype not in _DTYPE or k.dtype != q.dtype or v.dtype != q.dtype:
-        raise ValueError("q, k, v must share dtype float32, bfloat16 or float16")
-    B, Hq, Hkv, Tq, Tkv, D = _dims(q, k, layout)
+    B, Hq, Hkv, Tq, Tkv, D = _check_qkv(q, k, v, layout)
     odt = q.dtype if out_dtype is None else out_dtype
+    if odt not in (q.dtype, torch.float32):
+        raise ValueError("out_dtype must be q's dtype or torch.float32")
+    if out is not None:
+        _expect("out", out, tuple(q.shape), odt, q.device)
+    _need_gpu(q, k, v)
     o = out if out is not None else torch.empty(q.shape, dtype=odt, device=q.device)
     lse = torch.empty((B, Hq, Tq), dtype=torch.float32, device=q.device) if return_lse else None
     keep = []
-    ms = _mask_struct(mask, B, Hq, Tq, Tkv, keep)
-    ws_n = lib.sdpa_workspace_size(B, Hq, Hkv, Tq, Tkv, D, 0, 0, 0)
-    ws = torch.empty(ws_n, dtype=torch.uint8, device=q.device) if ws_n else None
+    ms = _mask_struct(mask, B, Hq, Tq, Tkv, keep, q.device)
     sc = float("nan") if scale is None else float(scale)
+    ws_n = lib.sdpa_workspace_size(_DTYPE[q.dtype], B, Hq, Hkv, Tq, Tkv, D, sc, 0, 0, 0)
+    ws = torch.empty(ws_n, dtype=torch.uint8, device=q.device) if ws_n else None
     if dropout is not None:
         kp, rate = _dropout_args(dropout, B, Hq, Tq, Tkv)
         st = lib.sdpa_fwd_dropout(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _DTYPE[q.dtype], _DTYPE[odt],
-                                  _LAYOUT[layout], B, Hq, Hkv, Tq, Tkv, D, sc, ctypes.byref(ms), kp, rate,
+                                  _layout_of(layout), B, Hq, Hkv, Tq, Tkv, D, sc, ctypes.byref(ms), kp, rate,
                                   _ptr(lse), None, 0, _stream(stream))
         _check(st, "sdpa_fwd_dropout")
         return (o, lse) if return_lse else o
-    st = lib.sdpa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _DTYPE[q.dtype], _DTYPE[odt], _LAYOUT[layout],
+    st = lib.sdpa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _DTYPE[q.dtype], _DTYPE[odt], _layout_of(layout),
                       B, Hq, Hkv, Tq, Tkv, D, sc, ctypes.byref(ms), _ptr(lse), _ptr(ws), ws_n, _stream(stream))
     _check(st, "sdpa_fwd")
     return (o, lse) if return_lse else o
@@ -260,24 +328,23 @@ def sdpa_backward(q, k, v, o, dout, lse, *, layout="bhsd", scale=None, mask=None
                   grad_dtype=None, stream=None):
     """(dq, dk, dv) of attention for the upstream gradient dout (o and lse from the forward call)."""
     lib = load()
+    B, Hq, Hkv, Tq, Tkv, D = _check_qkv(q, k, v, layout)
+    _check_bwd_io(q, o, dout, lse, B, Hq, Tq)
     _need_gpu(q, k, v, o, dout, lse)
-    if q.dtype not in _DTYPE or k.dtype != q.dtype or v.dtype != q.dtype or dout.dtype != q.dtype:
-        raise ValueError("q, k, v and dout must share one dtype")
-    if o.dtype not in (q.dtype, torch.float32) or lse.dtype != torch.float32:
-        raise ValueError("o must be in q's dtype or float32, lse float32")
-    B, Hq, Hkv, Tq, Tkv, D = _dims(q, k, layout)
     gdt = q.dtype if grad_dtype is None else grad_dtype
+    if gdt not in (q.dtype, torch.float32):
+        raise ValueError("grad_dtype must be q's dtype or torch.float32")
     dq = torch.empty(q.shape, dtype=gdt, device=q.device)
     dk = torch.empty(k.shape, dtype=gdt, device=q.device)
     dv = torch.empty(v.shape, dtype=gdt, device=q.device)
     keep_refs = []
-    ms = _mask_struct(mask, B, Hq, Tq, Tkv, keep_refs)
+    ms = _mask_struct(mask, B, Hq, Tq, Tkv, keep_refs, q.device)
     kp, rate = _dropout_args(dropout, B, Hq, Tq, Tkv)
     ws_n = lib.sdpa_bwd_workspace_size(B, Hq, Tq)
     ws = torch.empty(ws_n, dtype=torch.uint8, device=q.device)
     sc = float("nan") if scale is None else float(scale)
     st = lib.sdpa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
-                      _DTYPE[q.dtype], _DTYPE[o.dtype], _DTYPE[gdt], _LAYOUT[layout], B, Hq, Hkv, Tq, Tkv, D, sc,
+                      _DTYPE[q.dtype], _DTYPE[o.dtype], _DTYPE[gdt], _layout_of(layout), B, Hq, Hkv, Tq, Tkv, D, sc,
                       ctypes.byref(ms), kp, rate, _ptr(ws), ws_n, _stream(stream))
     _check(st, "sdpa_bwd")
     return dq, dk, dv
@@ -287,15 +354,14 @@ def sdpa_relpos_backward(q, k, v, o, dout, lse, rel_pos_h, rel_pos_w, grid, *, l
                          grad_dtype=None, stream=None, workspace=None):
     """(dq, dk, dv, d_rel_pos_h, d_rel_pos_w) of sdpa_relpos (tables' gradients in float32)."""
     lib = load()
-    _need_gpu(q, k, v, o, dout, lse, rel_pos_h, rel_pos_w)
-    if q.dtype not in _DTYPE or k.dtype != q.dtype or v.dtype != q.dtype or dout.dtype != q.dtype:
-        raise ValueError("q, k, v and dout must share one dtype")
+    B, H, T, D = _relpos_dims(q, k, v, grid, layout)
     gh, gw = grid
-    if layout == "bhsd":
-        B, H, T, D = q.shape
-    else:
-        B, T, H, D = q.shape
+    _check_tables(rel_pos_h, rel_pos_w, grid, D, q)
+    _check_bwd_io(q, o, dout, lse, B, H, T)
+    _need_gpu(q, k, v, o, dout, lse, rel_pos_h, rel_pos_w)
     gdt = q.dtype if grad_dtype is None else grad_dtype
+    if gdt not in (q.dtype, torch.float32):
+        raise ValueError("grad_dtype must be q's dtype or torch.float32")
     dq = torch.empty(q.shape, dtype=gdt, device=q.device)
     dk = torch.empty(k.shape, dtype=gdt, device=q.device)
     dv = torch.empty(v.shape, dtype=gdt, device=q.device)
@@ -307,9 +373,11 @@ def sdpa_relpos_backward(q, k, v, o, dout, lse, rel_pos_h, rel_pos_w, grid, *, l
     ws = workspace
     if ws is None or ws.numel() < ws_n:
         ws = torch.empty(ws_n, dtype=torch.uint8, device=q.device)
+    elif ws.dtype != torch.uint8 or ws.device != q.device or not ws.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 tensor on q's device")
     sc = float("nan") if scale is None else float(scale)
     st = lib.sdpa_relpos_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
-                             _ptr(drh), _ptr(drw), _DTYPE[q.dtype], _DTYPE[o.dtype], _DTYPE[gdt], _LAYOUT[layout],
+                             _ptr(drh), _ptr(drw), _DTYPE[q.dtype], _DTYPE[o.dtype], _DTYPE[gdt], _layout_of(layout),
                              B, H, gh, gw, D, _ptr(rel_pos_h), _ptr(rel_pos_w), sc, _ptr(ws), ws.numel(),
                              _stream(stream))
     _check(st, "sdpa_relpos_bwd")
@@ -319,14 +387,20 @@ def sdpa_relpos_backward(q, k, v, o, dout, lse, rel_pos_h, rel_pos_w, grid, *, l
 def attention_weights(q, k, lse, *, layout="bhsd", scale=None, mask=None, dropout=None, stream=None):
     """[B, Hq, Tq, Tkv] fp32 weights that multiply V (lse from the forward call on the same inputs)."""
     lib = load()
-    _need_gpu(q, k, lse)
+    if q.dtype not in _DTYPE:
+        raise ValueError("q, k must be float32, bfloat16 or float16")
     B, Hq, Hkv, Tq, Tkv, D = _dims(q, k, layout)
+    _expect("k", k, tuple(k.shape), q.dtype, q.device)
+    _expect("lse", lse, (B, Hq, Tq), torch.float32, q.device)
+    if not q.is_contiguous():
+        raise ValueError("q must be contiguous")
+    _need_gpu(q, k, lse)
     w = torch.empty((B, Hq, Tq, Tkv), dtype=torch.float32, device=q.device)
     keep_refs = []
-    ms = _mask_struct(mask, B, Hq, Tq, Tkv, keep_refs)
+    ms = _mask_struct(mask, B, Hq, Tq, Tkv, keep_refs, q.device)
     kp, rate = _dropout_args(dropout, B, Hq, Tq, Tkv)
     sc = float("nan") if scale is None else float(scale)
-    st = lib.sdpa_attention_weights(_ptr(q), _ptr(k), _DTYPE[q.dtype], _LAYOUT[layout], B, Hq, Hkv, Tq, Tkv, D,
+    st = lib.sdpa_attention_weights(_ptr(q), _ptr(k), _DTYPE[q.dtype], _layout_of(layout), B, Hq, Hkv, Tq, Tkv, D,
                                     sc, ctypes.byref(ms), _ptr(lse), kp, rate, _ptr(w), _stream(stream))
     _check(st, "sdpa_attention_weights")
     return w
@@ -335,15 +409,25 @@ def attention_weights(q, k, lse, *, layout="bhsd", scale=None, mask=None, dropou
 def relpos_terms(q, rel_pos_h, rel_pos_w, grid, *, layout="bhsd", stream=None):
     """term_h [B, H, T, grid_h], term_w [B, H, T, grid_w] (fp32) on the GPU."""
     lib = load()
-    _need_gpu(q, rel_pos_h, rel_pos_w)
+    if q.dtype not in _DTYPE:
+        raise ValueError("q must be float32, bfloat16 or float16")
+    _layout_of(layout)
+    if q.dim() != 4:
+        raise ValueError("q must be rank-4")
     gh, gw = grid
     if layout == "bhsd":
         B, H, T, D = q.shape
     else:
         B, T, H, D = q.shape
+    if gh <= 0 or gw <= 0 or gh * gw != T:
+        raise ValueError(f"grid {grid} does not match the sequence length {T}")
+    _check_tables(rel_pos_h, rel_pos_w, grid, D, q)
+    if not q.is_contiguous():
+        raise ValueError("q must be contiguous")
+    _need_gpu(q, rel_pos_h, rel_pos_w)
     th = torch.empty((B, H, T, gh), dtype=torch.float32, device=q.device)
     tw = torch.empty((B, H, T, gw), dtype=torch.float32, device=q.device)
-    st = lib.relpos_terms(_ptr(q), _DTYPE[q.dtype], _LAYOUT[layout], B, H, gh, gw, D,
+    st = lib.relpos_terms(_ptr(q), _DTYPE[q.dtype], _layout_of(layout), B, H, gh, gw, D,
                           _ptr(rel_pos_h), _ptr(rel_pos_w), _ptr(th), _ptr(tw), _stream(stream))
     _check(st, "relpos_terms")
     return th, tw
@@ -353,27 +437,31 @@ def sdpa_relpos(q, k, v, rel_pos_h, rel_pos_w, grid, *, layout="bhsd", scale=Non
                 return_lse=False, stream=None, out=None, workspace=None):
     """Fused attention with the decomposed rel-pos bias (self-attention on a grid)."""
     lib = load()
-    _need_gpu(q, k, v, rel_pos_h, rel_pos_w)
-    if q.dtype not in _DTYPE or k.dtype != q.dtype or v.dtype != q.dtype:
-        raise ValueError("q, k, v must share dtype float32, bfloat16 or float16")
+    B, H, T, D = _relpos_dims(q, k, v, grid, layout)
     gh, gw = grid
-    if layout == "bhsd":
-        B, H, T, D = q.shape
-    else:
-        B, T, H, D = q.shape
+    _check_tables(rel_pos_h, rel_pos_w, grid, D, q)
     odt = q.dtype if out_dtype is None else out_dtype
+    if odt not in (q.dtype, torch.float32):
+        raise ValueError("out_dtype must be q's dtype or torch.float32")
+    if out is not None:
+        _expect("out", out, tuple(q.shape), odt, q.device)
+    _need_gpu(q, k, v, rel_pos_h, rel_pos_w)
     o = out if out is not None else torch.empty(q.shape, dtype=odt, device=q.device)
     lse = torch.empty((B, H, T), dtype=torch.float32, device=q.device) if return_lse else None
-    ws_n = lib.sdpa_workspace_size(B, H, H, T, T, D, 1, gh, gw)
+    sc = float("nan") if scale is None else float(scale)
+    ws_n = lib.sdpa_workspace_size(_DTYPE[q.dtype], B, H, H, T, T, D, sc, 1, gh, gw)
     if ws_n == ctypes.c_size_t(-1).value:
         raise ValueError("grid does not match the sequence length")
     ws = workspace
-    if ws is None or ws.numel() < ws_n:
+    if ws_n == 0:
+        ws = None                     # the fused route needs no workspace
+    elif ws is None or ws.numel() < ws_n:
         ws = torch.empty(ws_n, dtype=torch.uint8, device=q.device)
-    sc = float("nan") if scale is None else float(scale)
+    elif ws.dtype != torch.uint8 or ws.device != q.device or not ws.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 tensor on q's device")
     st = lib.sdpa_relpos_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _DTYPE[q.dtype], _DTYPE[odt],
-                             _LAYOUT[layout], B, H, gh, gw, D, _ptr(rel_pos_h), _ptr(rel_pos_w), sc,
-                             _ptr(lse), _ptr(ws), ws.numel(), _stream(stream))
+                             _layout_of(layout), B, H, gh, gw, D, _ptr(rel_pos_h), _ptr(rel_pos_w), sc,
+                             _ptr(lse), _ptr(ws), ws.numel() if ws is not None else 0, _stream(stream))
     _check(st, "sdpa_relpos_fwd")
     return (o, lse) if return_lse else o
 

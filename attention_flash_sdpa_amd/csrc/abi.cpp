@@ -25,6 +25,16 @@ std::atomic<int64_t> g_split64{1};
 std::atomic<int64_t> g_split64w{1};
 std::atomic<int64_t> g_tiled{1};
 
+// The tuning knobs as one call sees them: read once at the call's start, so
+// the route, the split count and the workspace check of that call agree even
+// if another thread changes a knob meanwhile.
+struct Tuning {
+  int64_t num_splits, relpos_fused, split64, split64w, tiled;
+};
+Tuning tuning_now() {
+  return {g_num_splits.load(), g_relpos_fused.load(), g_split64.load(), g_split64w.load(), g_tiled.load()};
+}
+
 int fail(int status, const char* fmt, ...) {
   char buf[512];
   va_list ap;
@@ -48,10 +58,10 @@ void set_strides(int layout, int64_t H, int64_t T, int64_t D, int64_t* sb, int64
 // Split-KV chunk count: few query rows against a long key range leave most of
 // the GPU idle, so the key range is cut into chunks that run in parallel and
 // are merged by their log-sum-exp afterwards.
-int plan_splits(int64_t B, int64_t Hq, int64_t Tq, int64_t Tkv, int64_t D, int dtype) {
+int plan_splits(int64_t B, int64_t Hq, int64_t Tq, int64_t Tkv, int64_t D, int dtype, const Tuning& tu) {
   // split-KV exists for the head_dim-16 query-packed kernel (few queries)
   if (!sdpa::kSplitKvBuilt || !is16(dtype) || D != 16 || Tq > 8) return 1;
-  const int64_t forced = g_num_splits.load();
+  const int64_t forced = tu.num_splits;
   if (forced >= 1) return (int)std::min<int64_t>(forced, std::max<int64_t>(1, (Tkv + 63) / 64));
   // one wave per (4 heads, 8 queries, key chunk): aim at ~512 waves with
   // chunks of >= 64 keys (two tiles: the loads of the second overlap the first)
@@ -157,30 +167,30 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 enum Route { R_GENERIC, R_D16, R_WINDOW, R_SPLIT64W, R_SPLIT64, R_TILED, R_MFMA };
 
 // The kernel a call runs on: the first route whose conditions hold.
-Route route_of(const sdpa::FwdParams& p) {
+Route route_of(const sdpa::FwdParams& p, const Tuning& tu) {
   // The MFMA kernels take each row's running max on scores already multiplied
   // by scale, which needs scale > 0; other scales run on the generic kernel.
   if (!(p.scale > 0.0f && std::isfinite(p.scale))) return R_GENERIC;
   // Dropout runs on the double-buffered kernel (no mask, causal, sliding), else on the
   // general MFMA kernel where it applies, else on the generic one.
   if (p.keep) {
-    if (g_tiled.load() && sdpa::tiled_supports(p)) return R_TILED;
+    if (tu.tiled && sdpa::tiled_supports(p)) return R_TILED;
     return sdpa::flash_mfma_supports(p) ? R_MFMA : R_GENERIC;
   }
   if (sdpa::d16_supports(p)) return R_D16;
   if (sdpa::window_supports(p)) return R_WINDOW;
-  const int64_t wide = g_split64w.load();     // 0 off, 1 where the shape fills the CUs, 2 wherever supported
-  if (g_split64.load() && wide && sdpa::split64w_supports(p, wide == 1)) return R_SPLIT64W;
-  if (g_split64.load() && sdpa::split64_supports(p)) return R_SPLIT64;
-  if (g_tiled.load() && sdpa::tiled_supports(p)) return R_TILED;
+  const int64_t wide = tu.split64w;     // 0 off, 1 where the shape fills the CUs, 2 wherever supported
+  if (tu.split64 && wide && sdpa::split64w_supports(p, wide == 1)) return R_SPLIT64W;
+  if (tu.split64 && sdpa::split64_supports(p)) return R_SPLIT64;
+  if (tu.tiled && sdpa::tiled_supports(p)) return R_TILED;
   if (sdpa::flash_mfma_supports(p)) return R_MFMA;
   return R_GENERIC;
 }
 
-int launch(const sdpa::FwdParams& p, hipStream_t s) {
+int launch(const sdpa::FwdParams& p, const Tuning& tu, hipStream_t s) {
   hipError_t e;
   const char* name;
-  switch (route_of(p)) {
+  switch (route_of(p, tu)) {
     case R_D16:
       name = p.Tq <= 8 ? "d16_qpack_kernel" : "d16_kpack_kernel";
       e = sdpa::launch_d16(p, s);
@@ -201,25 +211,52 @@ int launch(const sdpa::FwdParams& p, hipStream_t s) {
 // forms the terms itself (no relpos_terms launch): every MFMA route that
 // accepts such a call does; the generic kernel does where the tables and the
 // per-lane term rows fit its LDS.
-bool relpos_fused_ok(const sdpa::FwdParams& p) {
+bool relpos_fused_ok(const sdpa::FwdParams& p, const Tuning& tu) {
+  if (!tu.relpos_fused) return false;
   sdpa::FwdParams q = p;
   q.term_h = nullptr;
   q.term_w = nullptr;
-  return route_of(q) != R_GENERIC || sdpa::generic_relpos_supported(q, true);
+  return route_of(q, tu) != R_GENERIC || sdpa::generic_relpos_supported(q, true);
+}
+
+// Rel-pos limits of every route (the generic kernel's term staging, the terms kernel).
+int check_relpos_grid(int64_t grid_h, int64_t grid_w, int64_t D) {
+  if (grid_h > 1024 || grid_w > 1024 || (D + 1) * grid_w * 4 > 65536)
+    return fail(SDPA_ERR_UNSUPPORTED, "grid %lldx%lld with head_dim %lld is not built", (long long)grid_h,
+                (long long)grid_w, (long long)D);
+  return SDPA_OK;
+}
+
+// Kernel parameters of a rel-pos call (no term arrays yet).
+sdpa::FwdParams relpos_params(const void* q, const void* k, const void* v, void* o, int dtype, int out_dtype,
+                              int layout, int64_t B, int64_t H, int64_t grid_h, int64_t grid_w, int64_t D,
+                              const void* rel_pos_h, const void* rel_pos_w, float scale, float* lse) {
+  const int64_t T = grid_h * grid_w;
+  sdpa::FwdParams p = base_params(q, k, v, o, dtype, out_dtype, layout, B, H, H, T, T, D, scale, lse);
+  p.bias = sdpa::BIAS_RELPOS;
+  p.grid_h = (int)grid_h;
+  p.grid_w = (int)grid_w;
+  p.rel_h = rel_pos_h;
+  p.rel_w = rel_pos_w;
+  return p;
 }
 
 }  // namespace
 
 extern "C" {
 
-size_t sdpa_workspace_size(int64_t B, int64_t Hq, int64_t Hkv, int64_t Tq, int64_t Tkv, int64_t D, int relpos,
-                           int64_t grid_h, int64_t grid_w) {
-  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Tq <= 0 || Tkv <= 0 || D <= 0) return (size_t)-1;
+size_t sdpa_workspace_size(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t Tq, int64_t Tkv, int64_t D,
+                           float scale, int relpos, int64_t grid_h, int64_t grid_w) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Tq <= 0 || Tkv <= 0 || D <= 0 || !dtype_ok(dtype)) return (size_t)-1;
+  const Tuning tu = tuning_now();
   if (relpos) {
-    if (grid_h <= 0 || grid_w <= 0 || grid_h * grid_w != Tq || Tq != Tkv) return (size_t)-1;
-    return terms_bytes(B, Hq, Tq, grid_h, grid_w);
+    if (grid_h <= 0 || grid_w <= 0 || grid_h * grid_w != Tq || Tq != Tkv || Hkv != Hq) return (size_t)-1;
+    static const char dummy = 0;
+    const sdpa::FwdParams p = relpos_params(&dummy, &dummy, &dummy, (void*)&dummy, dtype, dtype, SDPA_BHSD, B, Hq,
+                                            grid_h, grid_w, D, &dummy, &dummy, scale, nullptr);
+    return relpos_fused_ok(p, tu) ? 0 : terms_bytes(B, Hq, Tq, grid_h, grid_w);
   }
-  return split_bytes(plan_splits(B, Hq, Tq, Tkv, D, SDPA_BF16), B, Hq, Tq, D);
+  return split_bytes(plan_splits(B, Hq, Tq, Tkv, D, dtype, tu), B, Hq, Tq, D);
 }
 
 int sdpa_fwd(const void* q, const void* k, const void* v, void* o, int dtype, int out_dtype, int layout,
@@ -234,7 +271,8 @@ int sdpa_fwd(const void* q, const void* k, const void* v, void* o, int dtype, in
   sdpa::FwdParams p = base_params(q, k, v, o, dtype, out_dtype, layout, B, Hq, Hkv, Tq, Tkv, D, scale, lse);
   st = apply_mask(mask, p);
   if (st) return st;
-  p.num_splits = plan_splits(B, Hq, Tq, Tkv, D, dtype);
+  const Tuning tu = tuning_now();
+  p.num_splits = plan_splits(B, Hq, Tq, Tkv, D, dtype, tu);
   const size_t need = split_bytes(p.num_splits, B, Hq, Tq, D);
   if (need) {
     if (!workspace || workspace_bytes < need)
@@ -242,7 +280,7 @@ int sdpa_fwd(const void* q, const void* k, const void* v, void* o, int dtype, in
     p.part_o = (float*)workspace;
     p.part_ml = (float*)((char*)workspace + align256((size_t)p.num_splits * B * Hq * Tq * D * 4));
   }
-  return launch(p, (hipStream_t)stream);
+  return launch(p, tu, (hipStream_t)stream);
 }
 
 int relpos_terms(const void* q, int dtype, int layout, int64_t B, int64_t H, int64_t grid_h, int64_t grid_w,
@@ -282,41 +320,31 @@ int sdpa_relpos_fwd(const void* q, const void* k, const void* v, void* o, int dt
   if (st) return st;
   st = check_dtypes(dtype, out_dtype, layout, D);
   if (st) return st;
-  if (grid_h > 1024 || grid_w > 1024 || (D + 1) * grid_w * 4 > 65536)
-    return fail(SDPA_ERR_UNSUPPORTED, "grid %lldx%lld with head_dim %lld is not built", (long long)grid_h,
-                (long long)grid_w, (long long)D);
-  sdpa::FwdParams p = base_params(q, k, v, o, dtype, out_dtype, layout, B, H, H, T, T, D, scale, lse);
-  p.bias = sdpa::BIAS_RELPOS;
-  p.grid_h = (int)grid_h;
-  p.grid_w = (int)grid_w;
-  p.rel_h = rel_pos_h;
-  p.rel_w = rel_pos_w;
+  st = check_relpos_grid(grid_h, grid_w, D);
+  if (st) return st;
+  sdpa::FwdParams p = relpos_params(q, k, v, o, dtype, out_dtype, layout, B, H, grid_h, grid_w, D, rel_pos_h,
+                                    rel_pos_w, scale, lse);
+  const Tuning tu = tuning_now();
+  // The fused route forms the terms inside the attention kernel: no workspace.
+  if (relpos_fused_ok(p, tu)) return launch(p, tu, (hipStream_t)stream);
   const size_t need = terms_bytes(B, H, T, grid_h, grid_w);
   if (!workspace || workspace_bytes < need)
     return fail(SDPA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : (size_t)0);
-  if (g_relpos_fused.load() && relpos_fused_ok(p)) return launch(p, (hipStream_t)stream);
   float* th = (float*)workspace;
   float* tw = (float*)((char*)workspace + align256((size_t)B * H * T * grid_h * 4));
   st = relpos_terms(q, dtype, layout, B, H, grid_h, grid_w, D, rel_pos_h, rel_pos_w, th, tw, stream);
   if (st) return st;
   p.term_h = th;
   p.term_w = tw;
-  return launch(p, (hipStream_t)stream);
+  return launch(p, tu, (hipStream_t)stream);
 }
 
 int sdpa_relpos_fused(int dtype, int64_t D, int64_t grid_h, int64_t grid_w) {
-  sdpa::FwdParams p;
-  std::memset(&p, 0, sizeof(p));
+  if (grid_h <= 0 || grid_w <= 0 || D <= 0 || !dtype_ok(dtype)) return 0;
   static const char dummy = 0;
-  p.dtype = dtype; p.D = D; p.grid_h = (int)grid_h; p.grid_w = (int)grid_w;
-  p.Tq = p.Tkv = grid_h * grid_w;
-  p.rel_h = p.rel_w = &dummy;
-  p.scale = 1.0f;
-  p.B = p.Hq = p.Hkv = 1;
-  p.k_st = p.q_st = D;
-  p.num_splits = 1;
-  p.bias = sdpa::BIAS_RELPOS;
-  return (g_relpos_fused.load() && grid_h > 0 && grid_w > 0 && relpos_fused_ok(p)) ? 1 : 0;
+  const sdpa::FwdParams p = relpos_params(&dummy, &dummy, &dummy, (void*)&dummy, dtype, dtype, SDPA_BHSD, 1, 1,
+                                          grid_h, grid_w, D, &dummy, &dummy, 1.0f, nullptr);
+  return relpos_fused_ok(p, tuning_now()) ? 1 : 0;
 }
 
 int sdpa_dropout_mask(uint64_t seed, uint32_t step, float rate, int64_t B, int64_t Hq, int64_t Tq, int64_t Tkv,
@@ -363,7 +391,7 @@ int sdpa_fwd_dropout(const void* q, const void* k, const void* v, void* o, int d
   p.keep_scale = kscale;
   (void)workspace;
   (void)workspace_bytes;
-  return launch(p, (hipStream_t)stream);
+  return launch(p, tuning_now(), (hipStream_t)stream);
 }
 
 size_t sdpa_bwd_workspace_size(int64_t B, int64_t Hq, int64_t Tq) {

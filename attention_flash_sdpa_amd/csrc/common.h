@@ -26,4 +26,21 @@ __device__ __forceinline__ bool index_allowed(int bias, int64_t i, int64_t j, in
   return true;
 }
 
+// Wait states after matrix ops whose results the vector ALU reads next.  A
+// vector read of a matrix op's result needs wait states (the 8-pass 32x32x16
+// op: at least 11) that the hardware does not enforce; the compiler inserts
+// them, but counts them along the first control-flow path it finds back to
+// the op.  Where an exec-mask branch around lane-divergent code sits between
+// the op and the read, the branch-taken path can then reach the read a few
+// instructions after the op, and the read sees registers the op has not yet
+// written.  This fence takes the results as operands where they are (the
+// accumulation registers, so it needs no copy), so the ops that produce them
+// come before it and every read of them after it, with 14 wait states in
+// between on every path.  For kernels whose matrix ops accumulate in AGPRs.
+typedef float f32x16_fence __attribute__((ext_vector_type(16)));
+__device__ __forceinline__ void mfma_drain(f32x16_fence& a) { asm volatile("s_nop 7\n\ts_nop 5" : "+a"(a)); }
+__device__ __forceinline__ void mfma_drain(f32x16_fence& a, f32x16_fence& b) {
+  asm volatile("s_nop 7\n\ts_nop 5" : "+a"(a), "+a"(b));
+}
+
 }  // namespace sdpa

@@ -725,6 +725,8 @@ __global__ __launch_bounds__(256, (D == 128 ? 1 : 2)) void bwd_dq_kernel(BwdPara
           sacc = mfma32(ld_row<E, D>(ks, 32 * kb + nl, c, g), qf[c], sacc);
           dpacc = mfma32(ld_row<E, D>(vs, 32 * kb + nl, c, g), of[c], dpacc);
         }
+        // the mask / term reads below branch on lane conditions before sacc and dpacc are read
+        if (!FASTM) mfma_drain(sacc, dpacc);
         float ds[16];
         // rel-pos: grid (row, col) of the first key of each group of 4 this lane holds
         int grow[4] = {0, 0, 0, 0}, gcol[4] = {0, 0, 0, 0};
@@ -802,19 +804,32 @@ __global__ __launch_bounds__(256, (D == 128 ? 1 : 2)) void bwd_dq_kernel(BwdPara
             tsum += ds[r];
           }
         }
-        if (MODE == B_RELPOS && !RPS && qvalid) {
-          // dterm_h[q, row] and dterm_w[q, col] collect dS.  The two lane halves hold the
-          // same query, so they add in turn: no two lanes of one instruction share an
-          // address, and the order of the additions is fixed.
+        if (MODE == B_RELPOS && !RPS) {
+          // dterm_h[q, row] and dterm_w[q, col] collect dS.  Lanes l and l + 32 hold the
+          // same query (keys 8 (r / 4) + r % 4 and 4 further on), so they swap their dS:
+          // then both hold all 32 keys of the sub-tile, lane half 0 adds every key into
+          // the grid-row sums [0, gh) of the query's LDS row and lane half 1 into the
+          // grid-column sums [gh, gh + gw).  Each LDS word has one writer lane, and that
+          // lane adds in a fixed order.
+          const int64_t kb0 = k0 + 32 * kb;
+          const int brow = (int)(kb0 / gw), bcol = (int)(kb0 % gw);
 #pragma unroll
-          for (int half = 0; half < 2; ++half) {
-            if (g == half) {
+          for (int a = 0; a < 4; ++a) {
+            int r0, c0, r1, c1;
+            grid_step(brow, bcol, 8 * a, gw, r0, c0);         // keys of lane half 0
+            grid_step(brow, bcol, 8 * a + 4, gw, r1, c1);     // keys of lane half 1
 #pragma unroll
-              for (int r = 0; r < 16; ++r) {
-                if (k0 + 32 * kb + 8 * (r / 4) + 4 * g + (r % 4) < p.Tkv) {
-                  dts[krow[r]] += ds[r];
-                  dts[gh + kcol[r]] += ds[r];
-                }
+            for (int e = 0; e < 4; ++e) {
+              const int r = 4 * a + e;
+              auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(ds[r]), __float_as_uint(ds[r]), false, false);
+              const float v0 = __uint_as_float(sw[0]), v1 = __uint_as_float(sw[1]);   // half 0's, half 1's dS
+              int y0, x0, y1, x1;
+              grid_step(r0, c0, e, gw, y0, x0);
+              grid_step(r1, c1, e, gw, y1, x1);
+              const bool in0 = kb0 + 8 * a + e < p.Tkv, in1 = kb0 + 8 * a + 4 + e < p.Tkv;
+              if (qvalid) {
+                if (in0) dts[g ? gh + x0 : y0] += v0;
+                if (in1) dts[g ? gh + x1 : y1] += v1;
               }
             }
           }
@@ -845,6 +860,12 @@ __global__ __launch_bounds__(256, (D == 128 ? 1 : 2)) void bwd_dq_kernel(BwdPara
       }
     }
     if (more) lstore(buf ^ 1);
+    // the accumulators are read after the loop, behind branches
+    if (!more) {
+#pragma unroll
+      for (int nb = 0; nb < C::DB; ++nb) mfma_drain(dqT[nb]);
+      if (MODE == B_RELPOS && RPS) mfma_drain(dthT, dtwT);
+    }
     __syncthreads();
   }
 

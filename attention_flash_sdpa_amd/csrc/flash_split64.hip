@@ -461,12 +461,10 @@ hipError_t launch_mode(const FwdParams& p, hipStream_t s) {
 
 }  // namespace
 
-bool split64_supports(const FwdParams& p) {
+bool split64_shape_ok(const FwdParams& p) {
   if ((p.dtype != 1 && p.dtype != 2) || p.D != 64 || p.num_splits != 1) return false;
   // key rows addressed with 32-bit byte offsets
   if ((p.Tkv + BN) * p.k_st * 2 > 0x7fffffffLL) return false;
-  // worth it when the query blocks leave SIMDs idle: fewer than ~4 blocks of 32 rows per SIMD
-  if (p.B * p.Hq * ((p.Tq + 31) / 32) > 4096) return false;
   if (p.bias == BIAS_NONE) return true;
   if (p.bias == BIAS_RELPOS) {
     if (p.grid_w != 64 || p.Tkv != p.Tq) return false;
@@ -474,6 +472,11 @@ bool split64_supports(const FwdParams& p) {
     return p.grid_h >= 1 && p.grid_h <= 64 && p.rel_h && p.rel_w;
   }
   return false;
+}
+
+bool split64_supports(const FwdParams& p) {
+  // worth it when the query blocks leave SIMDs idle: fewer than ~4 blocks of 32 rows per SIMD
+  return split64_shape_ok(p) && p.B * p.Hq * ((p.Tq + 31) / 32) <= 4096;
 }
 
 template <typename E>

@@ -533,12 +533,13 @@ hipError_t launch_w_e(const FwdParams& p, hipStream_t s) {
 
 }  // namespace
 
-// Shapes split64_supports takes whose heads have at least 5 query blocks (so
-// a workgroup spans at most two heads) and whose workgroup count fits a 1-D
+// Shapes of the split64 kernels (any number of query blocks: the workgroups
+// are dealt out in rounds) whose heads have at least 5 query blocks (so a
+// workgroup spans at most two heads) and whose workgroup count fits a 1-D
 // grid; with need_fill, also only where the workgroups fill the CUs in nearly
 // whole rounds (at least one full round, the rounds on average 3/4 busy).
 bool split64w_supports(const FwdParams& p, bool need_fill) {
-  if (!split64_supports(p) || (p.Tq + 31) / 32 < 5) return false;
+  if (!split64_shape_ok(p) || (p.Tq + 31) / 32 < 5) return false;
   const int64_t nwg = (p.B * p.Hq * ((p.Tq + 31) / 32) + NQB - 1) / NQB;
   if (nwg > 0x7fffffff) return false;
   if (!need_fill) return true;

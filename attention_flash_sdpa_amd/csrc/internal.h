@@ -137,6 +137,7 @@ hipError_t launch_d16(const FwdParams& p, hipStream_t s);            // bf16, D 
 bool d16_supports(const FwdParams& p);
 hipError_t launch_split64(const FwdParams& p, hipStream_t s);        // bf16, D = 64, key range split in-workgroup
 bool split64_supports(const FwdParams& p);
+bool split64_shape_ok(const FwdParams& p);                           // split64_supports without the block-count limit
 hipError_t launch_split64w(const FwdParams& p, hipStream_t s);       // as split64, 12-wave workgroups of 192 query rows
 bool split64w_supports(const FwdParams& p, bool need_fill);          // need_fill: its workgroups fill the CUs
 hipError_t launch_window(const FwdParams& p, hipStream_t s);         // bf16, D = 64, 14 x 14 rel-pos windows, terms in-kernel

@@ -84,15 +84,57 @@ def run_call(fa, wl, g, out):
     return fa.sdpa(g["q"], g["k"], g["v"], layout=wl.layout, scale=wl.scale, mask=wl.mask, out=out)
 
 
-def time_gpu(fa, wl, g, steps, warmup):
+MALL_BYTES = 256 * 2**20            # MI355X Infinity Cache: working sets below this can stay cache-resident
+ROTATE_BYTES = 512 * 2**20          # span of distinct buffer sets that HBM-cold timing cycles through
+
+
+def buffer_sets(g, min_bytes=ROTATE_BYTES):
+    """Distinct copies of the call's inputs and output, laid out one after the
+    other in one device arena spanning at least `min_bytes`, so that cycling
+    through them reads every input from HBM rather than from the caches.
+    Working sets of MALL size or more need no copies: one set is returned.
+    Each set is a dict like `g` plus its own "out"."""
     import torch
-    out = torch.empty_like(g["q"])
-    for _ in range(warmup):
-        run_call(fa, wl, g, out)
+    names = [k for k in ("q", "k", "v", "rel_pos_h", "rel_pos_w", "bias", "ws") if k in g]
+    al = lambda n: (n + 255) // 256 * 256
+    offs, sb = {}, 0
+    for k in names + ["out"]:
+        t = g["q"] if k == "out" else g[k]
+        offs[k] = sb
+        sb += al(t.numel() * t.element_size())
+    if sb >= MALL_BYTES:
+        one = dict(g)
+        one["out"] = torch.empty_like(g["q"])
+        return [one]
+    nsets = (min_bytes + sb - 1) // sb
+    arena = torch.empty(nsets * sb, dtype=torch.uint8, device=g["q"].device)
+    tmpl = torch.zeros(sb, dtype=torch.uint8, device=g["q"].device)
+    for k in names:
+        n = g[k].numel() * g[k].element_size()
+        tmpl[offs[k]:offs[k] + n].copy_(g[k].contiguous().view(-1).view(torch.uint8))
+    arena.view(nsets, sb).copy_(tmpl.expand(nsets, sb))
+    sets = []
+    for i in range(nsets):
+        d = {}
+        for k in names + ["out"]:
+            t = g["q"] if k == "out" else g[k]
+            n = t.numel() * t.element_size()
+            d[k] = arena[i * sb + offs[k]:i * sb + offs[k] + n].view(t.dtype).view(t.shape)
+        sets.append(d)
+    return sets
+
+
+def time_gpu(fa, wl, sets, steps, warmup):
+    """Host-clocked seconds per call over `steps` calls (synchronised on both
+    sides), cycling through the buffer sets."""
+    import torch
+    for i in range(warmup):
+        run_call(fa, wl, sets[i % len(sets)], sets[i % len(sets)]["out"])
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(steps):
-        run_call(fa, wl, g, out)
+    for i in range(steps):
+        s = sets[i % len(sets)]
+        run_call(fa, wl, s, s["out"])
     torch.cuda.synchronize()
     return (time.perf_counter() - t0) / steps
 
@@ -117,15 +159,15 @@ def _hold_stream(ms):
 _SPIN_PER_MS = None
 
 
-def kernel_events(fa, wl, g, steps, reps=5):
-    """Average GPU duration of the whole call and of the separate rel-pos terms
+def kernel_events(fa, wl, sets, steps, reps=5):
+    """GPU duration per call of the whole call and of the separate rel-pos terms
     launch, from HIP events recorded on the stream the kernels run on (torch's
     current stream, which the binding passes to the library).  The launches of
-    each repetition queue up behind a spin kernel, so they run back to back;
-    the median over `reps` repetitions is returned."""
+    each repetition queue up behind a spin kernel, so they run back to back,
+    cycling through the buffer sets.  Returns the median and the min over
+    `reps` repetitions of (call ms, terms ms)."""
     import statistics
     import torch
-    out = torch.empty_like(g["q"])
     s = torch.cuda.current_stream()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
 
@@ -135,18 +177,20 @@ def kernel_events(fa, wl, g, steps, reps=5):
             torch.cuda.synchronize()
             _hold_stream(2.0 + 0.2 * steps)
             ev[0].record(s)
-            for _ in range(steps):
-                fn()
+            for i in range(steps):
+                fn(sets[i % len(sets)])
             ev[1].record(s)
             ev[1].synchronize()
             ts.append(ev[0].elapsed_time(ev[1]) / steps)
-        return statistics.median(ts)
+        return statistics.median(ts), min(ts)
 
-    call_ms = timed(lambda: run_call(fa, wl, g, out))
-    terms_ms = 0.0
+    call_med, call_min = timed(lambda b: run_call(fa, wl, b, b["out"]))
+    terms_med = terms_min = 0.0
+    g = sets[0]
     if wl.relpos and "bias" not in g and not fa.relpos_fused(g["q"].dtype, wl.D, wl.grid):
-        terms_ms = timed(lambda: fa.relpos_terms(g["q"], g["rel_pos_h"], g["rel_pos_w"], wl.grid, layout=wl.layout))
-    return call_ms, terms_ms
+        terms_med, terms_min = timed(lambda b: fa.relpos_terms(b["q"], b["rel_pos_h"], b["rel_pos_w"], wl.grid,
+                                                                layout=wl.layout))
+    return (call_med, call_min), (terms_med, terms_min)
 
 
 def source_sha256(kernel):
@@ -192,9 +236,22 @@ def copy_calibration(mib, steps):
     print(json.dumps({"copy_bytes_per_dispatch": n, "read_bytes": n, "write_bytes": n, "steps": steps}))
 
 
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(wl, x, budget_s=20.0):
-    """Time the fp64 oracle on whole (batch, head) slices of the same inputs until
-    about `budget_s` seconds of CPU work are done; report it at the metric's unit."""
+    """Time the fp64 oracle on whole heads (every batch entry) of the same inputs
+    until about `budget_s` seconds of CPU work are done; report it at the
+    metric's unit."""
     import numpy as np
     import oracle
     from threadpoolctl import threadpool_info
@@ -206,7 +263,7 @@ def cpu_baseline(wl, x, budget_s=20.0):
     hsel = lambda a, h, grp=1: (a[:, h // grp:h // grp + 1] if wl.layout == "bhsd" else a[:, :, h // grp:h // grp + 1])
     grp = wl.Hq // wl.Hkv
     done, t_total = 0, 0.0
-    for h in range(wl.B * 0 + wl.Hq):
+    for h in range(wl.Hq):
         t0 = time.perf_counter()
         oracle.sdpa(hsel(q, h), hsel(k, h, grp), hsel(v, h, grp), **kw)
         t_total += time.perf_counter() - t0
@@ -218,10 +275,10 @@ def cpu_baseline(wl, x, budget_s=20.0):
     frac = done / wl.Hq
     info = threadpool_info()
     threads = max([i.get("num_threads", 1) for i in info] or [1])
-    return {"value": round((attn + bias) * (wl.B if False else 1) / t_total / 1e12, 6), "unit": "TFLOP/s",
-            "cores": threads, "kind": "oracle",
-            "sample": f"{done} of {wl.Hq} heads (batch 0; {frac:.3f} of the workload), fp64 numpy, "
-                      f"{t_total:.1f} s wall"}
+    return {"value": round((attn + bias) / t_total / 1e12, 6), "unit": "TFLOP/s",
+            "cores": threads, "kind": "oracle", "cpu_model": cpu_model(),
+            "sample": f"{done} of {wl.Hq} heads (each over all {wl.B} batch entries; {frac:.3f} of the "
+                      f"workload), fp64 numpy, {t_total:.1f} s wall"}
 
 
 def bench_backward(fa, wl, x, g, args):
@@ -456,8 +513,10 @@ def main():
         bench_train_forward(fa, wl, g, args)
         return
     if wl.relpos:
-        n = fa.workspace_size(wl.B, wl.Hq, wl.Hkv, wl.Tq, wl.Tkv, wl.D, True, wl.grid)
-        g["ws"] = torch.empty(n, dtype=torch.uint8, device="cuda")
+        n = fa.workspace_size(wl.B, wl.Hq, wl.Hkv, wl.Tq, wl.Tkv, wl.D, True, wl.grid, dtype=g["q"].dtype,
+                              scale=wl.scale)
+        if n:
+            g["ws"] = torch.empty(n, dtype=torch.uint8, device="cuda")
     if args.route == "additive":
         if not wl.relpos:
             print("bench.py: --route additive needs a rel-pos workload", file=sys.stderr)
@@ -468,14 +527,19 @@ def main():
         del th, tw, j
     torch.cuda.synchronize()
 
-    sec = time_gpu(fa, wl, g, args.steps, args.warmup)
+    # HBM-cold timing: working sets below the MALL's size cycle through >= 512 MiB of
+    # buffer sets; the warm (one buffer set) times are reported beside them.
+    sets = buffer_sets(g)
+    warm = [sets[0]]
+    sec = time_gpu(fa, wl, sets, args.steps, args.warmup)
     attn, bias = flop_model(wl)
     if args.route == "additive":
         bias = 2 * allowed_pairs(wl) * wl.B * wl.Hq      # the terms were formed before timing
     total = attn + bias
     tflops = total / sec / 1e12
-    call_ms, terms_ms = kernel_events(fa, wl, g, args.steps)
-    run_call(fa, wl, g, torch.empty_like(g["q"]))
+    (call_ms, call_min), (terms_ms, terms_min) = kernel_events(fa, wl, sets, args.steps)
+    (wcall_ms, wcall_min), (wterms_ms, _) = kernel_events(fa, wl, warm, args.steps)
+    run_call(fa, wl, sets[0], sets[0]["out"])
     kernel = fa.last_kernel()
     rec_name = wl.name + ("_additive" if args.route == "additive" else "")
     if args.dtype and args.dtype != workloads.WORKLOADS[args.workload].dtype:
@@ -486,6 +550,7 @@ def main():
     if wl.relpos and terms_ms == 0.0:
         flash_flops = total             # terms formed inside the flash kernel: one launch per call
     achieved = flash_flops / (flash_ms * 1e-3) / 1e12
+    set_bytes = sum(t.numel() * t.element_size() for t in sets[0].values())
     nbytes = byte_model(wl) + (g["bias"].numel() * g["bias"].element_size() if "bias" in g else 0)
     line = {
         "metric": "attention TFLOP/s + % bf16 MFMA peak, SAM ViT-B 64x64 global rel-pos SDPA",
@@ -509,8 +574,15 @@ def main():
                      "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": traffic,
                      "traffic_source": traffic_src,
                      "kernel": kernel, "kernel_ms": round(flash_ms, 5),
+                     "kernel_ms_min": round(call_min - terms_min, 5),
                      "terms_kernel_ms": round(terms_ms, 5), "flop_per_launch": flash_flops,
                      "algorithmic_bytes_per_launch": nbytes},
+        "timing": {"cache": (f"HBM-cold: {len(sets)} buffer sets of {set_bytes} bytes cycled"
+                             if len(sets) > 1 else "working set >= 256 MiB: one buffer set"),
+                   "call_ms_median": round(call_ms, 5), "call_ms_min": round(call_min, 5),
+                   "warm_call_ms_median": round(wcall_ms, 5), "warm_call_ms_min": round(wcall_min, 5),
+                   "warm_tflops": round(total / (wcall_ms * 1e-3) / 1e12, 3),
+                   "event_reps": 5, "calls_per_rep": args.steps},
     }
     if args.route == "additive":
         # Reading the materialised bias bounds this route: report it against HBM.

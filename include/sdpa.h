@@ -44,7 +44,12 @@
  *     untouched and need no GPU.  sdpa_last_error() gives a thread-local
  *     message for the most recent failing call on the calling thread.
  *   - Calls are thread-safe and deterministic (no atomics in reductions; the
- *     same inputs give bitwise-identical outputs on the same device).
+ *     same inputs give bitwise-identical outputs on the same device).  The
+ *     process-wide tuning knobs (sdpa_set_tuning) are read once per call, so
+ *     one call's route, split count and workspace check always agree; a size
+ *     query and the call it sizes see the same knobs unless another thread
+ *     changes them in between, and then the call returns SDPA_ERR_WORKSPACE
+ *     rather than overrun a short workspace.
  */
 #ifndef SDPA_MI355X_H
 #define SDPA_MI355X_H
@@ -95,12 +100,17 @@ typedef struct sdpa_mask {
 
 /*
  * Bytes of device workspace that sdpa_fwd (relpos = 0) or sdpa_relpos_fwd
- * (relpos = 1; then Tq = Tkv = grid_h * grid_w and Hkv = Hq) needs for these
- * sizes.  Pure host arithmetic: no HIP call.  Returns 0 when no workspace is
- * needed and (size_t)-1 for invalid sizes.
+ * (relpos = 1; then Tq = Tkv = grid_h * grid_w and Hkv = Hq) needs for a call
+ * with this input dtype, these sizes and this scale (NaN = 1/sqrt(D)), under
+ * the current tuning knobs.  The answer follows the route the call takes:
+ * split-KV partials for few-query head_dim-16 calls, fp32 term arrays for a
+ * rel-pos call that cannot form its terms inside the attention kernel, and 0
+ * when the call needs none (e.g. every fused rel-pos route, SAM ViT-B's
+ * 64 x 64 global grid included).  Pure host arithmetic: no HIP call.
+ * Returns (size_t)-1 for invalid sizes or dtype.
  */
-size_t sdpa_workspace_size(int64_t B, int64_t Hq, int64_t Hkv, int64_t Tq, int64_t Tkv,
-                           int64_t D, int relpos, int64_t grid_h, int64_t grid_w);
+size_t sdpa_workspace_size(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t Tq, int64_t Tkv,
+                           int64_t D, float scale, int relpos, int64_t grid_h, int64_t grid_w);
 
 /*
  * Fused attention with an optional mask.  [Axon PR 650], description.
@@ -114,7 +124,7 @@ size_t sdpa_workspace_size(int64_t B, int64_t Hq, int64_t Hkv, int64_t Tq, int64
  *   lse        optional [B, Hq, Tq] fp32 log-sum-exp of each score row
  *              (natural log; -inf for a row with no allowed key); NULL skips it.
  *   Rows with no allowed key produce O = 0.
- *   workspace  device scratch of at least sdpa_workspace_size(..., 0, 0, 0)
+ *   workspace  device scratch of at least sdpa_workspace_size(dtype, ..., scale, 0, 0, 0)
  *              bytes (may be NULL when that size is 0).
  */
 int sdpa_fwd(const void* q, const void* k, const void* v, void* o,
@@ -146,7 +156,9 @@ int relpos_terms(const void* q, int dtype, int layout,
  *   Self-attention on a grid_h x grid_w token grid: Tq = Tkv = grid_h*grid_w,
  *   Hq = Hkv = H.  Scores are scale * q.k + term_h[i,row(j)] + term_w[i,col(j)]
  *   (the bias is not scaled).  Other arguments as in sdpa_fwd.
- *   workspace  at least sdpa_workspace_size(B, H, H, T, T, D, 1, grid_h, grid_w).
+ *   workspace  at least sdpa_workspace_size(dtype, B, H, H, T, T, D, scale, 1, grid_h,
+ *              grid_w) bytes.  A call that forms the terms inside the attention
+ *              kernel (sdpa_relpos_fused) does not touch it: NULL / 0 is accepted.
  */
 int sdpa_relpos_fwd(const void* q, const void* k, const void* v, void* o,
                     int dtype, int out_dtype, int layout,
@@ -196,7 +208,7 @@ const char* sdpa_last_kernel(void);
  *                  inside the attention kernel where the grid allows it;
  *                  0 = always run relpos_terms into the workspace first.
  * Returns SDPA_OK, or SDPA_ERR_INVALID for an unknown key or bad value.
- * The workspace size accounts for every setting.
+ * sdpa_workspace_size answers for the knobs in force when it is called.
  */
 int sdpa_set_tuning(const char* key, int64_t value);
 

@@ -94,7 +94,15 @@ def test_fwd_rejects_bad_masks():
 def test_relpos_rejects():
     lib = fa.load()
     args = [FAKE, FAKE, FAKE, FAKE, 1, 1, 1, 1, 2, 8, 8, 64, FAKE, FAKE, float("nan"), None, None, 0, None]
-    assert lib.sdpa_relpos_fwd(*args) == -3          # no workspace
+    # the unfused route (terms kernel first) needs the term workspace
+    assert lib.sdpa_set_tuning(b"relpos_fused", 0) == 0
+    try:
+        assert lib.sdpa_relpos_fwd(*args) == -3      # no workspace
+        short = list(args)
+        short[16], short[17] = FAKE, 1024
+        assert lib.sdpa_relpos_fwd(*short) == -3     # too small
+    finally:
+        assert lib.sdpa_set_tuning(b"relpos_fused", 1) == 0
     bad = list(args)
     bad[12] = None
     assert lib.sdpa_relpos_fwd(*bad) == -1           # missing table
@@ -111,10 +119,117 @@ def test_relpos_rejects():
 
 def test_workspace_sizes():
     lib = fa.load()
-    assert lib.sdpa_workspace_size(1, 12, 12, 4096, 4096, 64, 1, 64, 64) >= 1 * 12 * 4096 * 128 * 4
-    assert lib.sdpa_workspace_size(1, 12, 12, 4096, 4096, 64, 1, 63, 64) == ctypes.c_size_t(-1).value
-    assert lib.sdpa_workspace_size(0, 12, 12, 4096, 4096, 64, 0, 0, 0) == ctypes.c_size_t(-1).value
-    assert lib.sdpa_workspace_size(4, 32, 8, 4096, 4096, 128, 0, 0, 0) == 0
+    nan, BAD = float("nan"), ctypes.c_size_t(-1).value
+    # SAM ViT-B global rel-pos (bf16 / fp16, any batch): the terms are formed in the kernel, no workspace
+    for dt in (1, 2):
+        for B in (1, 4):
+            assert lib.sdpa_workspace_size(dt, B, 12, 12, 4096, 4096, 64, nan, 1, 64, 64) == 0
+    # the same grid with the fused terms switched off: both fp32 term arrays
+    assert lib.sdpa_set_tuning(b"relpos_fused", 0) == 0
+    try:
+        assert lib.sdpa_workspace_size(1, 1, 12, 12, 4096, 4096, 64, nan, 1, 64, 64) >= 1 * 12 * 4096 * 128 * 4
+    finally:
+        assert lib.sdpa_set_tuning(b"relpos_fused", 1) == 0
+    # route-aware: head_dim 128 on a 64-wide grid cannot stage the tables, so the terms kernel runs first
+    assert lib.sdpa_workspace_size(1, 1, 2, 2, 4096, 4096, 128, nan, 1, 64, 64) >= 2 * 4096 * 128 * 4
+    assert lib.sdpa_workspace_size(1, 1, 12, 12, 4096, 4096, 64, nan, 1, 63, 64) == BAD
+    assert lib.sdpa_workspace_size(1, 0, 12, 12, 4096, 4096, 64, nan, 0, 0, 0) == BAD
+    assert lib.sdpa_workspace_size(9, 1, 12, 12, 4096, 4096, 64, nan, 0, 0, 0) == BAD     # unknown dtype
+    assert lib.sdpa_workspace_size(1, 4, 32, 8, 4096, 4096, 128, nan, 0, 0, 0) == 0
+    # few-query head_dim 16 (split-KV partials): bf16 / fp16 only, and it follows num_splits
+    assert lib.sdpa_workspace_size(1, 1, 8, 8, 7, 4096, 16, 0.25, 0, 0, 0) > 0
+    assert lib.sdpa_workspace_size(0, 1, 8, 8, 7, 4096, 16, 0.25, 0, 0, 0) == 0
+    assert lib.sdpa_set_tuning(b"num_splits", 1) == 0
+    try:
+        assert lib.sdpa_workspace_size(1, 1, 8, 8, 7, 4096, 16, 0.25, 0, 0, 0) == 0
+    finally:
+        assert lib.sdpa_set_tuning(b"num_splits", 0) == 0
+
+
+# ---- the binding checks every shape, dtype and device before any launch (no GPU needed:
+# each case below raises ValueError before the first HIP call)
+def _t(*shape, dtype=None):
+    import torch
+    return torch.zeros(*shape, dtype=dtype or torch.bfloat16)
+
+
+@pytest.mark.parametrize("case", [
+    "k_batch", "k_headdim", "v_shape", "v_dtype", "out_shape", "out_dtype", "bad_out_dtype", "layout", "rank",
+    "mask_shape",
+])
+def test_binding_rejects_bad_shapes(case):
+    import torch
+    q, k, v = _t(2, 4, 64, 64), _t(2, 2, 80, 64), _t(2, 2, 80, 64)
+    kw = {}
+    if case == "k_batch":
+        k = _t(1, 2, 80, 64)
+    elif case == "k_headdim":
+        k = _t(2, 2, 80, 32)
+    elif case == "v_shape":
+        v = _t(2, 2, 79, 64)
+    elif case == "v_dtype":
+        v = _t(2, 2, 80, 64, dtype=torch.float16)
+    elif case == "out_shape":
+        kw["out"] = _t(2, 4, 63, 64)
+    elif case == "out_dtype":
+        kw["out"] = _t(2, 4, 64, 64, dtype=torch.float16)
+    elif case == "bad_out_dtype":
+        kw["out_dtype"] = torch.float16
+    elif case == "layout":
+        kw["layout"] = "sbhd"
+    elif case == "rank":
+        q = _t(2, 4, 64)
+    elif case == "mask_shape":
+        kw["mask"] = {"kind": "additive", "data": torch.zeros(2, 4, 64, 81)}
+    with pytest.raises(ValueError):
+        fa.sdpa(q, k, v, **kw)
+
+
+@pytest.mark.parametrize("case", ["fp32_tables", "short_table", "table_headdim", "grid", "kv_shape", "out"])
+def test_binding_rejects_bad_relpos_arguments(case):
+    import torch
+    q = k = v = _t(1, 2, 64, 64)
+    rh, rw, grid, kw = _t(15, 64), _t(15, 64), (8, 8), {}
+    if case == "fp32_tables":                 # SAM keeps fp32 tables: the caller casts them to q's dtype
+        rh = _t(15, 64, dtype=torch.float32)
+    elif case == "short_table":
+        rw = _t(13, 64)
+    elif case == "table_headdim":
+        rh = _t(15, 32)
+    elif case == "grid":
+        grid = (4, 8)
+    elif case == "kv_shape":
+        k = _t(1, 2, 60, 64)
+    elif case == "out":
+        kw["out"] = _t(1, 2, 64, 32)
+    with pytest.raises(ValueError):
+        fa.sdpa_relpos(q, k, v, rh, rw, grid, **kw)
+    if case in ("fp32_tables", "short_table", "table_headdim", "grid"):
+        with pytest.raises(ValueError):
+            fa.relpos_terms(q, rh, rw, grid)
+
+
+@pytest.mark.parametrize("case", ["o_shape", "dout_dtype", "lse_shape", "lse_dtype", "grad_dtype", "keep_shape"])
+def test_binding_rejects_bad_backward_arguments(case):
+    import torch
+    q, k, v = _t(1, 2, 40, 64), _t(1, 1, 50, 64), _t(1, 1, 50, 64)
+    o, do, lse, kw = _t(1, 2, 40, 64), _t(1, 2, 40, 64), torch.zeros(1, 2, 40), {}
+    if case == "o_shape":
+        o = _t(1, 2, 41, 64)
+    elif case == "dout_dtype":
+        do = _t(1, 2, 40, 64, dtype=torch.float16)
+    elif case == "lse_shape":
+        lse = torch.zeros(1, 2, 39)
+    elif case == "lse_dtype":
+        lse = torch.zeros(1, 2, 40, dtype=torch.float64)
+    elif case == "grad_dtype":
+        kw["grad_dtype"] = torch.float16
+    elif case == "keep_shape":
+        kw["dropout"] = {"keep": torch.zeros(1, 2, 40, 1, dtype=torch.int32), "rate": 0.1}
+    with pytest.raises(ValueError):
+        fa.sdpa_backward(q, k, v, o, do, lse, **kw)
+    with pytest.raises(ValueError):
+        fa.attention_weights(q, k, torch.zeros(1, 2, 39))
 
 
 def test_status_strings_and_tuning():

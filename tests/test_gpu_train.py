@@ -123,8 +123,10 @@ def test_dropout_forward_matches_oracle(gpu, case, tiled):
     eligible = dts != "fp32" and D in (64, 128) and (mask is None or isinstance(mask, dict))
     assert (kernel == "flash_tiled_kernel") == bool(tiled and eligible), kernel
     ref = st.sdpa_train_fwd(np64(q), np64(k), np64(v), layout=layout, scale=scale, mask=omask, keep=keep, rate=rate)
-    # the forward tolerances of the same kernels; kept weights are scaled by 1 / (1 - rate) on the output
-    assert max_err(np64(o), ref["o"]) < TOL[dts] * 1.5
+    # The forward tolerance of the same kernels, scaled by the kept weights' factor: the
+    # weights carry the same rounding as without dropout and are multiplied by
+    # 65536 / (65536 - thresh) = 1.25 at rate 0.2, so the error of O scales by that factor.
+    assert max_err(np64(o), ref["o"]) < TOL[dts] * (65536.0 / (65536.0 - round(rate * 65536)))
     # lse comes from the row sum of the weights as rounded for P.V, like the forward pass without dropout
     assert max_err(np64(lse), ref["lse"]) <= TOL[dts]
 
@@ -322,6 +324,16 @@ RELPOS_BWD_CASES = [
     ("bf16", "bhsd", 1, 1, (5, 27), 128, False),      # ragged: T = 135
     ("bf16", "bhsd", 1, 2, (40, 24), 64, False),      # grid rows beyond 32: dS sums through LDS
     ("bf16", "bhsd", 1, 2, (5, 64), 64, False),       # 64 wide, 320 keys: half the last 128-key block past the end
+    # more LDS-path grids (a side beyond 32, not 64 wide): head_dim 128 and 32, fp16, bshd, B * H > 2
+    ("bf16", "bshd", 2, 3, (40, 24), 128, False),
+    ("fp16", "bhsd", 2, 2, (33, 20), 32, True),
+    ("fp16", "bshd", 1, 3, (24, 40), 64, False),
+    ("bf16", "bhsd", 3, 1, (36, 9), 128, True),
+    # grouped table products cut into many query slices (split_h = 24, split_w = 6)
+    ("bf16", "bhsd", 2, 12, (16, 64), 64, False),
+    # the two shapes on which earlier dQ variants gave wrong gradients
+    ("bf16", "bshd", 2, 3, (14, 14), 64, False),
+    ("bf16", "bhsd", 1, 1, (5, 27), 128, False),
 ]
 
 
@@ -375,7 +387,10 @@ def test_relpos_backward_after_library_forward(gpu):
 
 @pytest.mark.slow
 def test_relpos_backward_full_size_sampled_heads(gpu):
-    """SAM ViT-B global attention at full size; dq, dk, dv of two heads against the oracle."""
+    """SAM ViT-B global attention at full size in the launch configuration the
+    benchmark times: dq, dk, dv of two heads, and both table gradients (which
+    sum over every head, so the oracle runs all twelve heads one at a time)
+    against the oracle."""
     import workloads
     wl = workloads.WORKLOADS["sam_global_relpos"]
     x = workloads.generate(wl, seed=0)
@@ -387,12 +402,17 @@ def test_relpos_backward_full_size_sampled_heads(gpu):
     dq, dk, dv, drh, drw = gpu.sdpa_relpos_backward(g["q"], g["k"], g["v"], o, do.cuda(), lse, g["rel_pos_h"],
                                                     g["rel_pos_w"], wl.grid, scale=wl.scale)
     torch.cuda.synchronize()
-    assert torch.all(torch.isfinite(drh)) and torch.all(torch.isfinite(drw))
     rp = {"rel_pos_h": np64(x["rel_pos_h"]), "rel_pos_w": np64(x["rel_pos_w"]), "grid": wl.grid}
-    for h in (0, wl.Hq - 1):
+    drh_ref, drw_ref = 0.0, 0.0
+    for h in range(wl.Hq):
         sl = slice(h, h + 1)
         ref = st.sdpa_bwd(np64(x["q"][:, sl]), np64(x["k"][:, sl]), np64(x["v"][:, sl]), np64(do[:, sl]),
                           scale=wl.scale, rel_pos=rp)
-        assert norm_err(np64(dq[:, sl]), ref["dq"]) < GTOL[torch.bfloat16]
-        assert norm_err(np64(dk[:, sl]), ref["dk"]) < GTOL[torch.bfloat16]
-        assert norm_err(np64(dv[:, sl]), ref["dv"]) < GTOL[torch.bfloat16]
+        drh_ref = drh_ref + ref["drel_pos_h"]
+        drw_ref = drw_ref + ref["drel_pos_w"]
+        if h in (0, wl.Hq - 1):
+            assert norm_err(np64(dq[:, sl]), ref["dq"]) < GTOL[torch.bfloat16]
+            assert norm_err(np64(dk[:, sl]), ref["dk"]) < GTOL[torch.bfloat16]
+            assert norm_err(np64(dv[:, sl]), ref["dv"]) < GTOL[torch.bfloat16]
+    assert norm_err(np64(drh), drh_ref) < GTOL[torch.bfloat16]
+    assert norm_err(np64(drw), drw_ref) < GTOL[torch.bfloat16]
