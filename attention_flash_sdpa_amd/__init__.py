@@ -25,7 +25,7 @@ import threading
 
 import torch
 
-__all__ = ["load", "lib_path", "sdpa", "sdpa_relpos", "relpos_terms", "workspace_size", "relpos_fused",
+__all__ = ["load", "lib_path", "sdpa", "sdpa_noalloc", "sdpa_relpos", "relpos_terms", "workspace_size", "relpos_fused",
            "set_tuning", "dropout_mask", "sdpa_backward", "sdpa_relpos_backward", "attention_weights", "SdpaError", "F32", "BF16", "F16",
            "BSHD", "BHSD"]
 
@@ -73,6 +73,9 @@ def load():
         lib.sdpa_fwd.restype = _I32
         lib.sdpa_fwd.argtypes = [_P, _P, _P, _P, _I32, _I32, _I32] + [_I64] * 6 + \
             [_F, ctypes.POINTER(_Mask), _P, _P, ctypes.c_size_t, _P]
+        lib.sdpa_fwd_noalloc.restype = _I32
+        lib.sdpa_fwd_noalloc.argtypes = [_P, _P, _P, _P, _I32, _I32, _I32] + [_I64] * 6 + \
+            [_F, ctypes.POINTER(_Mask), _P, _P]
         lib.relpos_terms.restype = _I32
         lib.relpos_terms.argtypes = [_P, _I32, _I32] + [_I64] * 5 + [_P, _P, _P, _P, _P]
         lib.sdpa_relpos_fwd.restype = _I32
@@ -312,6 +315,26 @@ def sdpa(q, k, v, *, layout="bhsd", scale=None, mask=None, out_dtype=None, retur
                       B, Hq, Hkv, Tq, Tkv, D, sc, ctypes.byref(ms), _ptr(lse), _ptr(ws), ws_n, _stream(stream))
     _check(st, "sdpa_fwd")
     return (o, lse) if return_lse else o
+
+
+def sdpa_noalloc(q, k, v, out, *, layout="bhsd", scale=None, mask=None, lse=None, stream=None):
+    """sdpa into the caller's `out` (and optional `lse` [B, Hq, Tq] fp32) through the
+    allocation-free entry point: neither the library nor this wrapper allocates."""
+    lib = load()
+    B, Hq, Hkv, Tq, Tkv, D = _check_qkv(q, k, v, layout)
+    if out.dtype not in (q.dtype, torch.float32):
+        raise ValueError("out must be in q's dtype or torch.float32")
+    _expect("out", out, tuple(q.shape), out.dtype, q.device)
+    if lse is not None:
+        _expect("lse", lse, (B, Hq, Tq), torch.float32, q.device)
+    _need_gpu(q, k, v)
+    ms = _mask_struct(mask, B, Hq, Tq, Tkv, [], q.device)
+    sc = float("nan") if scale is None else float(scale)
+    st = lib.sdpa_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _DTYPE[q.dtype], _DTYPE[out.dtype],
+                              _layout_of(layout), B, Hq, Hkv, Tq, Tkv, D, sc, ctypes.byref(ms), _ptr(lse),
+                              _stream(stream))
+    _check(st, "sdpa_fwd_noalloc")
+    return out
 
 
 def dropout_mask(seed, step, rate, B, Hq, Tq, Tkv, *, device="cuda", stream=None):

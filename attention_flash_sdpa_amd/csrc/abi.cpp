@@ -259,10 +259,15 @@ size_t sdpa_workspace_size(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_
   return split_bytes(plan_splits(B, Hq, Tq, Tkv, D, dtype, tu), B, Hq, Tq, D);
 }
 
-int sdpa_fwd(const void* q, const void* k, const void* v, void* o, int dtype, int out_dtype, int layout,
-             int64_t B, int64_t Hq, int64_t Hkv, int64_t Tq, int64_t Tkv, int64_t D, float scale,
-             const sdpa_mask* mask, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
-  g_last_error.clear();
+}  // extern "C"
+
+namespace {
+
+// Validation and kernel parameters shared by sdpa_fwd and sdpa_fwd_noalloc:
+// *need is the split-KV scratch the call's route takes (0 = none).
+int fwd_prepare(const void* q, const void* k, const void* v, void* o, int dtype, int out_dtype, int layout,
+                int64_t B, int64_t Hq, int64_t Hkv, int64_t Tq, int64_t Tkv, int64_t D, float scale,
+                const sdpa_mask* mask, float* lse, const Tuning& tu, sdpa::FwdParams* out, size_t* need) {
   if (!q || !k || !v || !o) return fail(SDPA_ERR_INVALID, "q, k, v and o must be non-null");
   int st = check_sizes(B, Hq, Hkv, Tq, Tkv, D);
   if (st) return st;
@@ -271,14 +276,55 @@ int sdpa_fwd(const void* q, const void* k, const void* v, void* o, int dtype, in
   sdpa::FwdParams p = base_params(q, k, v, o, dtype, out_dtype, layout, B, Hq, Hkv, Tq, Tkv, D, scale, lse);
   st = apply_mask(mask, p);
   if (st) return st;
-  const Tuning tu = tuning_now();
   p.num_splits = plan_splits(B, Hq, Tq, Tkv, D, dtype, tu);
-  const size_t need = split_bytes(p.num_splits, B, Hq, Tq, D);
+  *need = split_bytes(p.num_splits, B, Hq, Tq, D);
+  *out = p;
+  return SDPA_OK;
+}
+
+void set_split_buffers(sdpa::FwdParams& p, void* base) {
+  p.part_o = (float*)base;
+  p.part_ml = (float*)((char*)base + align256((size_t)p.num_splits * p.B * p.Hq * p.Tq * p.D * 4));
+}
+
+}  // namespace
+
+extern "C" {
+
+int sdpa_fwd(const void* q, const void* k, const void* v, void* o, int dtype, int out_dtype, int layout,
+             int64_t B, int64_t Hq, int64_t Hkv, int64_t Tq, int64_t Tkv, int64_t D, float scale,
+             const sdpa_mask* mask, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  const Tuning tu = tuning_now();
+  sdpa::FwdParams p;
+  size_t need = 0;
+  int st = fwd_prepare(q, k, v, o, dtype, out_dtype, layout, B, Hq, Hkv, Tq, Tkv, D, scale, mask, lse, tu, &p, &need);
+  if (st) return st;
   if (need) {
     if (!workspace || workspace_bytes < need)
       return fail(SDPA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : (size_t)0);
-    p.part_o = (float*)workspace;
-    p.part_ml = (float*)((char*)workspace + align256((size_t)p.num_splits * B * Hq * Tq * D * 4));
+    set_split_buffers(p, workspace);
+  }
+  return launch(p, tu, (hipStream_t)stream);
+}
+
+int sdpa_fwd_noalloc(const void* q, const void* k, const void* v, void* o, int dtype, int out_dtype, int layout,
+                     int64_t B, int64_t Hq, int64_t Hkv, int64_t Tq, int64_t Tkv, int64_t D, float scale,
+                     const sdpa_mask* mask, float* lse, void* stream) {
+  g_last_error.clear();
+  const Tuning tu = tuning_now();
+  sdpa::FwdParams p;
+  size_t need = 0;
+  int st = fwd_prepare(q, k, v, o, dtype, out_dtype, layout, B, Hq, Hkv, Tq, Tkv, D, scale, mask, lse, tu, &p, &need);
+  if (st) return st;
+  if (need) {
+    if (need > sdpa::kNoAllocScratchBytes)
+      return fail(SDPA_ERR_UNSUPPORTED, "split-KV partials of %zu bytes exceed the fixed %zu-byte scratch", need,
+                  sdpa::kNoAllocScratchBytes);
+    void* scratch = nullptr;
+    const hipError_t e = sdpa::noalloc_scratch(&scratch);
+    if (e != hipSuccess) return fail(SDPA_ERR_HIP, "scratch address lookup failed: %s", hipGetErrorString(e));
+    set_split_buffers(p, scratch);
   }
   return launch(p, tu, (hipStream_t)stream);
 }

@@ -126,6 +126,12 @@ struct TermsParams {
 // Split-KV (chunked key range + log-sum-exp merge) is available.
 constexpr bool kSplitKvBuilt = true;
 
+// Allocation-free forward: bytes of the fixed per-device scratch array that
+// holds the split-KV partials, and its device address on the current device
+// (looked up once per device).
+constexpr size_t kNoAllocScratchBytes = 8u << 20;
+hipError_t noalloc_scratch(void** ptr);
+
 // Launchers: return hipSuccess or the launch error.  Each only enqueues work.
 hipError_t launch_generic_fwd(const FwdParams& p, hipStream_t s);
 // Rel-pos on the generic kernel: the per-lane term rows (and, fused, the tables) fit its LDS.

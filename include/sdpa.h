@@ -134,6 +134,25 @@ int sdpa_fwd(const void* q, const void* k, const void* v, void* o,
              void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * sdpa_fwd for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments, results and kernels as sdpa_fwd, minus the workspace: the
+ * split-KV partials of the few-query head_dim-16 route live in a fixed
+ * 8 MiB device array inside the library (one copy per GPU, held until the
+ * process ends).  The call allocates and frees nothing; its first call on a
+ * device looks up that device's copy of the array (hipGetSymbolAddress).
+ * A call whose partials exceed 8 MiB returns SDPA_ERR_UNSUPPORTED (the
+ * automatic split count stays far below it; a large forced "num_splits" can
+ * reach it).  Every call on one GPU shares that GPU's array and leaves the
+ * last call's partials in it: calls that overlap on one GPU (concurrent
+ * streams or threads) race on it and must be serialised by the caller.
+ */
+int sdpa_fwd_noalloc(const void* q, const void* k, const void* v, void* o,
+                     int dtype, int out_dtype, int layout,
+                     int64_t B, int64_t Hq, int64_t Hkv, int64_t Tq, int64_t Tkv, int64_t D,
+                     float scale, const sdpa_mask* mask, float* lse, void* stream);
+
+/*
  * Decomposed rel-pos terms of SAM's attention ([mlx-examples issue 1451],
  * body: add_decomposed_rel_pos; [Candle PR 3280], Key Changes: term_h/term_w):
  *   term_h[b,h,i,y] = sum_c q[b,h,i,c] * rel_pos_h[row(i) - y + grid_h - 1, c]
