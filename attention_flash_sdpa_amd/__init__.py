@@ -303,6 +303,8 @@ def sdpa(q, k, v, *, layout="bhsd", scale=None, mask=None, out_dtype=None, retur
     ms = _mask_struct(mask, B, Hq, Tq, Tkv, keep, q.device)
     sc = float("nan") if scale is None else float(scale)
     ws_n = lib.sdpa_workspace_size(_DTYPE[q.dtype], B, Hq, Hkv, Tq, Tkv, D, sc, 0, 0, 0)
+    if ws_n == ctypes.c_size_t(-1).value:
+        ws_n = 0                      # sizes the library refuses: the call below reports why
     ws = torch.empty(ws_n, dtype=torch.uint8, device=q.device) if ws_n else None
     if dropout is not None:
         kp, rate = _dropout_args(dropout, B, Hq, Tq, Tkv)

@@ -11,6 +11,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <initializer_list>
 #include <string>
 
 #include "internal.h"
@@ -81,6 +82,22 @@ size_t terms_bytes(int64_t B, int64_t H, int64_t T, int64_t gh, int64_t gw) {
   return align256((size_t)B * H * T * gh * 4) + align256((size_t)B * H * T * gw * 4);
 }
 
+// Largest tensor, in elements, that a call may describe: 2^40 elements is
+// several times the memory of any one device, and keeps every element offset
+// the kernels and the workspace planning form far from 64-bit overflow.
+constexpr int64_t kMaxElements = int64_t(1) << 40;
+
+// True if the product of the positive factors is at most kMaxElements
+// (checked factor by factor, so the product itself never overflows).
+bool elements_ok(std::initializer_list<int64_t> factors) {
+  int64_t acc = 1;
+  for (int64_t f : factors) {
+    if (f <= 0 || acc > kMaxElements / f) return false;
+    acc *= f;
+  }
+  return true;
+}
+
 int check_sizes(int64_t B, int64_t Hq, int64_t Hkv, int64_t Tq, int64_t Tkv, int64_t D) {
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || Tq <= 0 || Tkv <= 0 || D <= 0)
     return fail(SDPA_ERR_INVALID, "all sizes must be positive (B=%lld Hq=%lld Hkv=%lld Tq=%lld Tkv=%lld D=%lld)",
@@ -88,6 +105,8 @@ int check_sizes(int64_t B, int64_t Hq, int64_t Hkv, int64_t Tq, int64_t Tkv, int
   if (Hq % Hkv) return fail(SDPA_ERR_INVALID, "Hq (%lld) must be a multiple of Hkv (%lld)", (long long)Hq, (long long)Hkv);
   if (Tq > INT32_MAX || Tkv > INT32_MAX || B > 65535 || Hq > 65535)
     return fail(SDPA_ERR_UNSUPPORTED, "sizes beyond the launch grid limits");
+  if (!elements_ok({B, Hq, Tq, D}) || !elements_ok({B, Hkv, Tkv, D}) || !elements_ok({B, Hq, Tq, Tkv}))
+    return fail(SDPA_ERR_UNSUPPORTED, "tensors of more than 2^40 elements are beyond device memory");
   return SDPA_OK;
 }
 
@@ -221,7 +240,8 @@ bool relpos_fused_ok(const sdpa::FwdParams& p, const Tuning& tu) {
 
 // Rel-pos limits of every route (the generic kernel's term staging, the terms kernel).
 int check_relpos_grid(int64_t grid_h, int64_t grid_w, int64_t D) {
-  if (grid_h > 1024 || grid_w > 1024 || (D + 1) * grid_w * 4 > 65536)
+  if (D <= 0) return fail(SDPA_ERR_INVALID, "head_dim must be positive (got %lld)", (long long)D);
+  if (grid_h > 1024 || grid_w > 1024 || D > 128 || (D + 1) * grid_w * 4 > 65536)
     return fail(SDPA_ERR_UNSUPPORTED, "grid %lldx%lld with head_dim %lld is not built", (long long)grid_h,
                 (long long)grid_w, (long long)D);
   return SDPA_OK;
@@ -247,10 +267,12 @@ extern "C" {
 
 size_t sdpa_workspace_size(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t Tq, int64_t Tkv, int64_t D,
                            float scale, int relpos, int64_t grid_h, int64_t grid_w) {
-  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Tq <= 0 || Tkv <= 0 || D <= 0 || !dtype_ok(dtype)) return (size_t)-1;
+  if (!dtype_ok(dtype) || check_sizes(B, Hq, Hkv, Tq, Tkv, D)) return (size_t)-1;
   const Tuning tu = tuning_now();
   if (relpos) {
-    if (grid_h <= 0 || grid_w <= 0 || grid_h * grid_w != Tq || Tq != Tkv || Hkv != Hq) return (size_t)-1;
+    if (grid_h <= 0 || grid_w <= 0 || grid_h > 1024 || grid_w > 1024 || grid_h * grid_w != Tq || Tq != Tkv ||
+        Hkv != Hq)
+      return (size_t)-1;
     static const char dummy = 0;
     const sdpa::FwdParams p = relpos_params(&dummy, &dummy, &dummy, (void*)&dummy, dtype, dtype, SDPA_BHSD, B, Hq,
                                             grid_h, grid_w, D, &dummy, &dummy, scale, nullptr);
@@ -342,6 +364,8 @@ int relpos_terms(const void* q, int dtype, int layout, int64_t B, int64_t H, int
     return fail(SDPA_ERR_UNSUPPORTED, "grid %lldx%lld with head_dim %lld is not built", (long long)grid_h,
                 (long long)grid_w, (long long)D);
   if (B > 65535 || H > 65535) return fail(SDPA_ERR_UNSUPPORTED, "sizes beyond the launch grid limits");
+  if (!elements_ok({B, H, grid_h * grid_w, grid_h + grid_w}))
+    return fail(SDPA_ERR_UNSUPPORTED, "term arrays of more than 2^40 elements are beyond device memory");
   sdpa::TermsParams t;
   t.q = q; t.dtype = dtype; t.B = B; t.H = H; t.T = grid_h * grid_w; t.D = D;
   set_strides(layout, H, t.T, D, &t.q_sb, &t.q_sh, &t.q_st);
@@ -361,12 +385,12 @@ int sdpa_relpos_fwd(const void* q, const void* k, const void* v, void* o, int dt
   if (!q || !k || !v || !o || !rel_pos_h || !rel_pos_w)
     return fail(SDPA_ERR_INVALID, "q, k, v, o and both tables must be non-null");
   if (grid_h <= 0 || grid_w <= 0) return fail(SDPA_ERR_INVALID, "grid sizes must be positive");
+  int st = check_relpos_grid(grid_h, grid_w, D);
+  if (st) return st;
   const int64_t T = grid_h * grid_w;
-  int st = check_sizes(B, H, H, T, T, D);
+  st = check_sizes(B, H, H, T, T, D);
   if (st) return st;
   st = check_dtypes(dtype, out_dtype, layout, D);
-  if (st) return st;
-  st = check_relpos_grid(grid_h, grid_w, D);
   if (st) return st;
   sdpa::FwdParams p = relpos_params(q, k, v, o, dtype, out_dtype, layout, B, H, grid_h, grid_w, D, rel_pos_h,
                                     rel_pos_w, scale, lse);
@@ -386,7 +410,7 @@ int sdpa_relpos_fwd(const void* q, const void* k, const void* v, void* o, int dt
 }
 
 int sdpa_relpos_fused(int dtype, int64_t D, int64_t grid_h, int64_t grid_w) {
-  if (grid_h <= 0 || grid_w <= 0 || D <= 0 || !dtype_ok(dtype)) return 0;
+  if (grid_h <= 0 || grid_w <= 0 || D <= 0 || !dtype_ok(dtype) || grid_h > 1024 || grid_w > 1024 || D > 128) return 0;
   static const char dummy = 0;
   const sdpa::FwdParams p = relpos_params(&dummy, &dummy, &dummy, (void*)&dummy, dtype, dtype, SDPA_BHSD, 1, 1,
                                           grid_h, grid_w, D, &dummy, &dummy, 1.0f, nullptr);
@@ -398,8 +422,10 @@ int sdpa_dropout_mask(uint64_t seed, uint32_t step, float rate, int64_t B, int64
   g_last_error.clear();
   if (!keep) return fail(SDPA_ERR_INVALID, "keep must be non-null");
   if (B <= 0 || Hq <= 0 || Tq <= 0 || Tkv <= 0) return fail(SDPA_ERR_INVALID, "all sizes must be positive");
-  if (Tq > INT32_MAX || Tkv > INT32_MAX || B * Hq > INT32_MAX)
+  if (Tq > INT32_MAX || Tkv > INT32_MAX || B > INT32_MAX || Hq > INT32_MAX || B * Hq > INT32_MAX)
     return fail(SDPA_ERR_UNSUPPORTED, "sizes beyond the generator's 32-bit counter words");
+  if (!elements_ok({B, Hq, Tq, (Tkv + 31) / 32}))
+    return fail(SDPA_ERR_UNSUPPORTED, "keep-bit array of more than 2^40 words is beyond device memory");
   sdpa::DropoutParams d;
   float kscale;
   int st = dropout_plan(rate, &d.thresh, &kscale);
@@ -441,7 +467,7 @@ int sdpa_fwd_dropout(const void* q, const void* k, const void* v, void* o, int d
 }
 
 size_t sdpa_bwd_workspace_size(int64_t B, int64_t Hq, int64_t Tq) {
-  if (B <= 0 || Hq <= 0 || Tq <= 0) return (size_t)-1;
+  if (!elements_ok({B, Hq, Tq})) return (size_t)-1;
   return align256((size_t)B * Hq * Tq * 4);
 }
 
@@ -508,7 +534,8 @@ size_t relpos_bwd_bytes(int64_t B, int64_t H, int64_t gh, int64_t gw, int64_t D,
 }
 
 size_t sdpa_relpos_bwd_workspace_size(int64_t B, int64_t H, int64_t grid_h, int64_t grid_w, int64_t D) {
-  if (B <= 0 || H <= 0 || grid_h <= 0 || grid_w <= 0 || D <= 0) return (size_t)-1;
+  if (grid_h <= 0 || grid_w <= 0 || grid_h > 1024 || grid_w > 1024 || D <= 0 || D > 128) return (size_t)-1;
+  if (B > 65535 || H > 65535 || !elements_ok({B, H, grid_h * grid_w, grid_h * grid_w})) return (size_t)-1;
   return relpos_bwd_bytes(B, H, grid_h, grid_w, D, nullptr);
 }
 
@@ -522,6 +549,8 @@ int sdpa_relpos_bwd(const void* q, const void* k, const void* v, const void* o, 
       !rel_pos_w)
     return fail(SDPA_ERR_INVALID, "every tensor argument must be non-null");
   if (grid_h <= 0 || grid_w <= 0) return fail(SDPA_ERR_INVALID, "grid sizes must be positive");
+  if (grid_h > 1024 || grid_w > 1024)
+    return fail(SDPA_ERR_UNSUPPORTED, "grid %lldx%lld is not built", (long long)grid_h, (long long)grid_w);
   const int64_t T = grid_h * grid_w;
   int st = check_sizes(B, H, H, T, T, D);
   if (st) return st;

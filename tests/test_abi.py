@@ -117,6 +117,51 @@ def test_relpos_rejects():
     assert lib.relpos_terms(FAKE, 3, 1, 1, 2, 8, 8, 64, FAKE, FAKE, FAKE, FAKE, None) == -1
 
 
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), -1), (dict(v=None), -1), (dict(Hkv=0), -1), (dict(Hq=3, Hkv=2), -1), (dict(layout=2), -1),
+    (dict(dtype=1, out_dtype=2), -1), (dict(D=24), -2), (dict(B=70000), -2),
+    (dict(B=65535, Hq=65535, Hkv=65535, Tq=2 ** 31 - 1, Tkv=2 ** 31 - 1, D=128), -2),
+])
+def test_noalloc_rejects(kw, status):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, dtype=1, out_dtype=1, layout=1, B=1, Hq=2, Hkv=2, Tq=8, Tkv=8, D=64)
+    a.update(kw)
+    lib = fa.load()
+    st = lib.sdpa_fwd_noalloc(a["q"], a["k"], a["v"], a["o"], a["dtype"], a["out_dtype"], a["layout"], a["B"],
+                              a["Hq"], a["Hkv"], a["Tq"], a["Tkv"], a["D"], float("nan"), None, None, None)
+    assert st == status
+    assert lib.sdpa_last_error().decode() != ""
+
+
+def test_noalloc_rejects_partials_beyond_its_scratch():
+    """Split-KV partials that would not fit the fixed 8 MiB scratch: refused with
+    SDPA_ERR_UNSUPPORTED before any HIP call (head_dim 16, 8 queries, 64 heads,
+    1024 key chunks = 64 MiB of partials)."""
+    lib = fa.load()
+    assert lib.sdpa_set_tuning(b"num_splits", 1024) == 0
+    try:
+        st = lib.sdpa_fwd_noalloc(FAKE, FAKE, FAKE, FAKE, 1, 1, 1, 1, 64, 64, 8, 1 << 20, 16, float("nan"), None,
+                                  None, None)
+        msg = lib.sdpa_last_error().decode()
+    finally:
+        assert lib.sdpa_set_tuning(b"num_splits", 0) == 0
+    assert st == -2 and "scratch" in msg
+
+
+def test_sizes_beyond_device_memory_are_refused():
+    """Each size within the launch-grid limits but the tensor as a whole beyond
+    2^40 elements: refused (no overflowing offsets reach a kernel), and the
+    size queries answer (size_t)-1."""
+    lib = fa.load()
+    BAD = ctypes.c_size_t(-1).value
+    assert call_fwd(B=65535, Hq=65535, Hkv=65535, Tq=2 ** 31 - 1, Tkv=2 ** 31 - 1, D=128) == -2
+    assert b"2^40" in lib.sdpa_last_error()
+    assert lib.sdpa_workspace_size(1, 65535, 65535, 65535, 2 ** 31 - 1, 16, 16, 0.25, 0, 0, 0) == BAD
+    assert lib.sdpa_workspace_size(1, 1, 2, 2, 2 ** 62, 2 ** 62, 64, 0.25, 1, 2 ** 31, 2 ** 31) == BAD
+    assert lib.sdpa_bwd_workspace_size(2 ** 40, 2 ** 40, 2 ** 40) == BAD
+    assert lib.sdpa_relpos_bwd_workspace_size(1, 1, 2 ** 40, 2 ** 40, 64) == BAD
+    assert lib.sdpa_relpos_fused(1, 2 ** 62, 64, 64) == 0
+
+
 def test_workspace_sizes():
     lib = fa.load()
     nan, BAD = float("nan"), ctypes.c_size_t(-1).value
