@@ -25,15 +25,17 @@ std::atomic<int64_t> g_relpos_fused{1};
 std::atomic<int64_t> g_split64{1};
 std::atomic<int64_t> g_split64w{1};
 std::atomic<int64_t> g_tiled{1};
+std::atomic<int64_t> g_generic_waves{0};
 
 // The tuning knobs as one call sees them: read once at the call's start, so
 // the route, the split count and the workspace check of that call agree even
 // if another thread changes a knob meanwhile.
 struct Tuning {
-  int64_t num_splits, relpos_fused, split64, split64w, tiled;
+  int64_t num_splits, relpos_fused, split64, split64w, tiled, generic_waves;
 };
 Tuning tuning_now() {
-  return {g_num_splits.load(), g_relpos_fused.load(), g_split64.load(), g_split64w.load(), g_tiled.load()};
+  return {g_num_splits.load(), g_relpos_fused.load(), g_split64.load(), g_split64w.load(), g_tiled.load(),
+          g_generic_waves.load()};
 }
 
 int fail(int status, const char* fmt, ...) {
@@ -206,9 +208,11 @@ Route route_of(const sdpa::FwdParams& p, const Tuning& tu) {
   return R_GENERIC;
 }
 
-int launch(const sdpa::FwdParams& p, const Tuning& tu, hipStream_t s) {
+int launch(const sdpa::FwdParams& p0, const Tuning& tu, hipStream_t s) {
   hipError_t e;
   const char* name;
+  sdpa::FwdParams p = p0;
+  p.generic_multiwave = tu.generic_waves != 1;
   switch (route_of(p, tu)) {
     case R_D16:
       name = p.Tq <= 8 ? "d16_qpack_kernel" : "d16_kpack_kernel";
@@ -663,6 +667,11 @@ int sdpa_set_tuning(const char* key, int64_t value) {
   if (!std::strcmp(key, "split_wide")) {
     if (value < 0 || value > 2) return fail(SDPA_ERR_INVALID, "split_wide must be 0, 1 or 2");
     g_split64w.store(value);
+    return SDPA_OK;
+  }
+  if (!std::strcmp(key, "generic_waves")) {
+    if (value != 0 && value != 1) return fail(SDPA_ERR_INVALID, "generic_waves must be 0 (automatic) or 1");
+    g_generic_waves.store(value);
     return SDPA_OK;
   }
   if (!std::strcmp(key, "tiled")) {

@@ -39,6 +39,7 @@ struct FwdParams {
   const void* rel_w;
   int grid_h, grid_w;
   int relpos_rows_lds;        // generic kernel: term rows staged in LDS (set by its launcher)
+  int generic_multiwave;      // generic kernel: key range split over 4 waves on small launches (1) or not (0)
   int num_splits;             // split-KV chunks (1 = no split)
   float* part_o;              // split-KV partial outputs [splits, B, Hq, Tq, D] fp32
   float* part_ml;             // split-KV partial (max, sum) [splits, B, Hq, Tq, 2] fp32

@@ -226,6 +226,10 @@ const char* sdpa_last_kernel(void);
  *   "relpos_fused" 1 (default) = sdpa_relpos_fwd forms the rel-pos terms
  *                  inside the attention kernel where the grid allows it;
  *                  0 = always run relpos_terms into the workspace first.
+ *   "generic_waves" 0 (default) = the vector-ALU kernel (fp32, and shapes no
+ *                  matrix-core kernel takes) splits each 64-row block's keys
+ *                  over 4 waves when the launch has fewer blocks than the GPU
+ *                  has compute units and head_dim <= 32; 1 = always one wave.
  * Returns SDPA_OK, or SDPA_ERR_INVALID for an unknown key or bad value.
  * sdpa_workspace_size answers for the knobs in force when it is called.
  */

@@ -445,3 +445,64 @@ def test_window_running_max(gpu, qmul):
     ref = oracle.sdpa(np64(x["q"]), np64(x["k"]), np64(x["v"]), scale=wl.scale,
                       rel_pos={"rel_pos_h": np64(x["rel_pos_h"]), "rel_pos_w": np64(x["rel_pos_w"]), "grid": wl.grid})
     assert max_err(np64(o), ref["o"]) <= TOL["bf16"]
+
+
+GENERIC_CASES = [
+    # B, Hq, Hkv, Tq, Tkv, D, dtype, mask
+    (1, 2, 2, 64, 64, 16, torch.float32, None),
+    (1, 2, 1, 50, 77, 16, torch.float32, None),                     # ragged, GQA
+    (2, 3, 3, 130, 17, 8, torch.float32, None),                     # D < 16: element-wise copies; 2 key tiles
+    (1, 2, 2, 70, 200, 32, torch.float32, {"kind": "causal", "offset": 5}),
+    (1, 2, 2, 70, 200, 24, torch.float32, {"kind": "sliding", "window": 19, "offset": 3}),
+    (1, 2, 2, 33, 1, 16, torch.float32, None),                       # one key (one wave)
+    (1, 4, 2, 70, 130, 32, torch.float32, "additive"),
+    (1, 2, 2, 70, 45, 16, torch.float32, "bool"),
+    (1, 2, 2, 70, 150, 40, torch.float32, None),                     # head_dim 40 stays on one wave
+]
+
+
+@pytest.mark.parametrize("waves", [0, 1])
+@pytest.mark.parametrize("case", range(len(GENERIC_CASES)))
+def test_generic_kernel_wave_split(gpu, waves, case):
+    """The vector-ALU kernel with its key range split over four waves (small
+    launches, head_dim <= 32) and with one wave: both against the oracle, on
+    ragged sizes, every mask family, a single key and head_dim below 16."""
+    B, Hq, Hkv, Tq, Tkv, D, dt, mask = GENERIC_CASES[case]
+    if mask in ("additive", "bool"):
+        g = torch.Generator().manual_seed(40 + case)
+        if mask == "additive":
+            data = torch.randn((B, 1, Tq, Tkv), generator=g)
+        else:
+            data = torch.rand((1, Hq, Tq, Tkv), generator=g) > 0.3
+            data[..., 0] = True
+        mask = {"kind": mask, "data": data}
+    gpu.set_tuning("generic_waves", waves)
+    try:
+        check(gpu, B, Hq, Hkv, Tq, Tkv, D, dtype=dt, mask=mask, seed=30 + case)
+        assert gpu.last_kernel() == "generic_fwd_kernel"
+    finally:
+        gpu.set_tuning("generic_waves", 0)
+
+
+@pytest.mark.parametrize("waves", [0, 1])
+@pytest.mark.parametrize("fused", [0, 1])
+def test_generic_relpos_wave_split(gpu, waves, fused):
+    """The tiny fp32 rel-pos config (8x8 grid, head_dim 16) on both wave modes,
+    with the terms formed in the kernel and read from the workspace."""
+    wl = workloads.WORKLOADS["tiny_relpos_fp32"]
+    x = workloads.generate(wl, seed=3)
+    g = {k_: t.cuda() for k_, t in x.items()}
+    gpu.set_tuning("generic_waves", waves)
+    gpu.set_tuning("relpos_fused", fused)
+    try:
+        o, lse = gpu.sdpa_relpos(g["q"], g["k"], g["v"], g["rel_pos_h"], g["rel_pos_w"], wl.grid, layout=wl.layout,
+                                 scale=wl.scale, return_lse=True)
+        torch.cuda.synchronize()
+        assert gpu.last_kernel() == "generic_fwd_kernel"
+    finally:
+        gpu.set_tuning("generic_waves", 0)
+        gpu.set_tuning("relpos_fused", 1)
+    rp = {"rel_pos_h": np64(x["rel_pos_h"]), "rel_pos_w": np64(x["rel_pos_w"]), "grid": wl.grid}
+    ref = oracle.sdpa(np64(x["q"]), np64(x["k"]), np64(x["v"]), layout=wl.layout, scale=wl.scale, rel_pos=rp)
+    assert max_err(np64(o), ref["o"]) <= TOL["fp32"]
+    assert max_err(np64(lse), ref["lse"]) <= TOL["fp32"]
