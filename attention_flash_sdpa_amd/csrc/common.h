@@ -26,6 +26,15 @@ __device__ __forceinline__ bool index_allowed(int bias, int64_t i, int64_t j, in
   return true;
 }
 
+// Orders this wave's LDS accesses before and after it: a wave's LDS
+// operations execute in issue order, and the fences keep the compiler from
+// moving them across.  Enough where only the wave's own lanes share the words.
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // Wait states after matrix ops whose results the vector ALU reads next.  A
 // vector read of a matrix op's result needs wait states (the 8-pass 32x32x16
 // op: at least 11) that the hardware does not enforce; the compiler inserts

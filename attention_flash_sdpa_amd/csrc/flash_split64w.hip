@@ -367,6 +367,10 @@ __global__ __launch_bounds__(64 * NW, 1) void flash_split64w_kernel(FwdParams p)
 #pragma unroll
       for (int i = 0; i < 16; ++i) s[i] = (kl0 + 8 * (i / 4) + (i % 4) < (int)p.Tkv) ? s[i] : -INFINITY;
     }
+    // The softmax runs at raised wave priority: it is the part of a step the
+    // other waves of the SIMD cannot hide (their matrix ops run under it), so
+    // its instructions go first when several waves are ready to issue.
+    __builtin_amdgcn_s_setprio(1);
     const float rowb = th_pair * kLog2e;
     // Probabilities against the running reference m (log2 units).  The tile
     // max is not computed up front: a probability above 2^tau -- detected from
@@ -412,6 +416,7 @@ __global__ __launch_bounds__(64 * NW, 1) void flash_split64w_kernel(FwdParams p)
       lt = probs(rowb - mz);
     }
     l += lt;
+    __builtin_amdgcn_s_setprio(0);
 #pragma unroll
     for (int tc = 0; tc < 2; ++tc)
 #pragma unroll

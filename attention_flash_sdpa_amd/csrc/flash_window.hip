@@ -142,10 +142,12 @@ __global__ __launch_bounds__(NW * 64, 4) void flash_window_kernel(FwdParams p) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) sc[(8 * (i / 4) + 4 * g + (i % 4)) * 32 + ql] = a[i];
   };
-  // term_w / scale per key slot of a tile: the score accumulators' start
+  // term_w / scale per key slot of a tile: the score accumulators' start.
+  // The slot is this wave's own, so its writes and reads need only the
+  // wave's own order (wave_sync), not a workgroup barrier.
   f32x16 cinit;
   table_product(rw);
-  __syncthreads();
+  wave_sync();
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const int s = 8 * (i / 4) + 4 * g + (i % 4);
@@ -153,7 +155,7 @@ __global__ __launch_bounds__(NW * 64, 4) void flash_window_kernel(FwdParams p) {
     const float t = sc[(iw - x + G - 1) * 32 + ql] * inv_scale;
     cinit[i] = s < TK ? t : -INFINITY;
   }
-  __syncthreads();
+  wave_sync();
   // A_h stays in LDS; each tile reads its two term_h values from it.
   table_product(rh);
   // K' chunk: key slot ql (lanes g = 0) is one-hot at s / 14 and 4 + s / 14.

@@ -25,15 +25,6 @@ namespace sdpa {
 // waves per CU, instruction fetch dominates large kernels).
 enum GenericFamily { GF_NONE = 0, GF_INDEX = 1, GF_TENSOR = 2, GF_RELPOS = 3 };
 
-// Orders this wave's LDS accesses before and after it (a wave's LDS
-// operations execute in issue order; the fences keep the compiler from moving
-// them across).  Enough where only the wave's own lanes share the words.
-__device__ __forceinline__ void wave_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
 // Key tile of one wave, and the words one wave needs: its K and V tiles and
 // its score block while it runs, then its (m, l, output) rows for the merge.
 template <int DMAX, int NW> struct GenericShape {

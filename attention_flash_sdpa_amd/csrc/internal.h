@@ -122,6 +122,7 @@ struct TermsParams {
   int grid_h, grid_w;
   float* term_h;
   float* term_w;
+  int use_mfma;               // 16-bit inputs: products on the matrix cores where the shape allows (1) or not (0)
 };
 
 // Split-KV (chunked key range + log-sum-exp merge) is available.

@@ -10,9 +10,127 @@
 // so term_h for the row is the small product Q_row [grid_w x D] . Rh_rows^T
 // [D x grid_h]; term_w for query (row, col) uses the rel_pos_w rows
 // col - x + grid_w - 1.  Every output is one fp32 dot product of length D.
+//
+// Two kernels.  16-bit inputs with head_dim 32, 64 or 128 on grids whose
+// products fit a 32 x 128 slot (SAM's 14 x 14 windows and 64 x 64 global
+// grid among them) run on the matrix cores: a wave takes 32 consecutive
+// tokens, forms the products P[i, r] = q_i . table[r] for every table row r
+// that any of its tokens needs (32 x 32 x 16 matrix ops, Q^T as the shared
+// operand), stores them in its own LDS slot and then reads each token's term
+// rows out of the slot along the skew r = coord(i) - y + G - 1.  The 32
+// tokens' term rows are one contiguous stretch of each output array, written
+// with 16-byte stores by consecutive lanes.  Other inputs use the vector-ALU
+// kernel below.
 #include "common.h"
+#include "elem16.h"
 
 namespace sdpa {
+
+namespace {
+constexpr int TRMAX = 128;            // table rows one 32-token block's products cover at most
+constexpr int TPITCH = TRMAX + 1;     // slot pitch (floats): rows of consecutive tokens start one bank apart
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// Rows of the product one block needs: term_h spans grid rows row0..row1 of
+// its tokens plus grid_h - 1; term_w spans columns col0..col1 plus grid_w - 1
+// when the block lies in one grid row, else the whole table.
+__host__ __device__ inline int terms_rows_h(int gh, int gw) { return gh + (gw + 30) / gw; }
+__host__ __device__ inline int terms_rows_w(int gw) { return gw % 32 == 0 ? 31 + gw : 2 * gw - 1; }
+}  // namespace
+
+template <typename E, int NC>
+__global__ __launch_bounds__(256) void relpos_terms_mfma_kernel(TermsParams p) {
+  typedef typename Vec16<E>::x8 e8;
+  __shared__ float slots[4][32 * TPITCH];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 5, ql = lane & 31;
+  const int64_t b = blockIdx.z, h = blockIdx.y;
+  const int64_t q0 = ((int64_t)blockIdx.x * 4 + wave) * 32;
+  if (q0 >= p.T) return;                      // whole wave; no workgroup barrier below
+  const int gh = p.grid_h, gw = p.grid_w, D = (int)p.D;
+  const int nq = (int)(p.T - q0 < 32 ? p.T - q0 : 32);
+  float* slot = slots[wave];
+  // Q^T operand: column ql = token q0 + ql (zero past the end), dims 16c + 8g ..
+  e8 qf[NC];
+  {
+    const E* qp = (const E*)p.q + b * p.q_sb + h * p.q_sh + (q0 + (ql < nq ? ql : 0)) * p.q_st + 8 * g;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) qf[c] = ql < nq ? *(const e8*)(qp + 16 * c) : (e8){};
+  }
+  const int64_t qlast = q0 + nq - 1;
+  const int row0 = (int)(q0 / gw), row1 = (int)(qlast / gw);
+  const int col0 = (int)(q0 % gw), col1 = (int)(qlast % gw);
+  // Table operands of up to four 32-row blocks, loaded together (one memory
+  // round trip; the rel_pos_w set goes out while the term_h rows are written).
+  e8 tf[TRMAX / 32][NC];
+  auto load_table = [&](const E* tab, int ntab, int r0, int nr) {
+#pragma unroll
+    for (int rb = 0; rb < TRMAX / 32; ++rb) {
+      const int rl = rb * 32 + ql, r = r0 + rl;
+      const bool ok = rl < nr && r < ntab;
+      const E* tp = tab + (int64_t)(ok ? r : 0) * D + 8 * g;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) tf[rb][c] = (rb * 32 < nr && ok) ? *(const e8*)(tp + 16 * c) : (e8){};
+    }
+  };
+  // Products over table rows r0 .. r0 + nr - 1 into the slot: slot[i][r - r0] = q_i . table[r].
+  auto products = [&](int nr) {
+#pragma unroll
+    for (int rb = 0; rb < TRMAX / 32; ++rb) {
+      if (rb * 32 >= nr) break;
+      f32x16_t acc = (f32x16_t){};
+#pragma unroll
+      for (int c = 0; c < NC; ++c) acc = mfma32(tf[rb][c], qf[c], acc);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) slot[ql * TPITCH + rb * 32 + 8 * (i / 4) + 4 * g + (i % 4)] = acc[i];
+    }
+  };
+  // Term rows of the block's tokens: out[i, y] = slot[i][base(i) - y],
+  // base(i) = coord(i) + G - 1 - r0; nq x nout contiguous floats.  Lane l
+  // writes elements e = W l, W l + 64 W, ... (W = 4 with 16-byte stores, else
+  // 1); its token index q = e / nout, offset y and grid coordinates advance by
+  // fixed steps, so only the first position takes a division.
+  auto read_out = [&](float* out, int nout, int G, int r0, bool by_row) {
+    const int total = nq * nout;
+    const int W = (nout & 3) == 0 ? 4 : 1;
+    const int stride = 64 * W;
+    int e = W * lane;
+    int q = e / nout, y = e - q * nout;
+    const int dq = stride / nout, dy = stride - dq * nout;
+    int row = (int)((q0 + q) / gw), col = (int)((q0 + q) % gw);
+    for (; e < total; e += stride) {
+      const float* sp = slot + q * TPITCH + (by_row ? row : col) + G - 1 - r0 - y;
+      if (W == 4) *(f32x4_t*)(out + e) = (f32x4_t){sp[0], sp[-1], sp[-2], sp[-3]};
+      else out[e] = sp[0];
+      int adv = dq;
+      y += dy;
+      if (y >= nout) {
+        y -= nout;
+        ++adv;
+      }
+      q += adv;
+      col += adv;
+      while (col >= gw) {
+        col -= gw;
+        ++row;
+      }
+    }
+  };
+  const int64_t row_first = (b * p.H + h) * p.T + q0;
+  const bool one_row = row0 == row1;
+  const int r0h = row0, nrh = row1 - row0 + gh;
+  const int r0w = one_row ? col0 : 0, nrw = one_row ? col1 - col0 + gw : 2 * gw - 1;
+  load_table((const E*)p.rel_h, 2 * gh - 1, r0h, nrh);
+  products(nrh);
+  load_table((const E*)p.rel_w, 2 * gw - 1, r0w, nrw);
+  wave_sync();
+  read_out(p.term_h + row_first * gh, gh, gh, r0h, true);
+  wave_sync();                                // slot reads done before the next products
+  products(nrw);
+  wave_sync();
+  read_out(p.term_w + row_first * gw, gw, gw, r0w, false);
+}
 
 // One workgroup per (b, h, grid row): its grid_w queries, each handled by
 // 256 / grid_w threads (or one thread per query and a loop when grid_w > 256).
@@ -134,7 +252,30 @@ static void launch_terms_typed(const TermsParams& p, dim3 grid, hipStream_t s) {
   else launch_terms_dim<TIN, 128>(p, grid, s);
 }
 
+// The matrix-core kernel's conditions: 16-bit inputs, head_dim a multiple of
+// 32 up to 128, 16-byte aligned rows, and products that fit the slot.
+static bool terms_mfma_ok(const TermsParams& p) {
+  if (!p.use_mfma || (p.dtype != 1 && p.dtype != 2) || (p.D != 32 && p.D != 64 && p.D != 128)) return false;
+  if (terms_rows_h(p.grid_h, p.grid_w) > TRMAX || terms_rows_w(p.grid_w) > TRMAX) return false;
+  if ((p.q_st % 8) != 0 || (((uintptr_t)p.q | (uintptr_t)p.rel_h | (uintptr_t)p.rel_w) & 15) != 0) return false;
+  if (((uintptr_t)p.term_h | (uintptr_t)p.term_w) & 15) return false;
+  return (p.T + 127) / 128 <= 0x7fffffff && p.H <= 65535 && p.B <= 65535;
+}
+
+template <typename E>
+static void launch_terms_mfma(const TermsParams& p, hipStream_t s) {
+  dim3 grid((unsigned)((p.T + 127) / 128), (unsigned)p.H, (unsigned)p.B);
+  if (p.D == 32) hipLaunchKernelGGL((relpos_terms_mfma_kernel<E, 2>), grid, dim3(256), 0, s, p);
+  else if (p.D == 64) hipLaunchKernelGGL((relpos_terms_mfma_kernel<E, 4>), grid, dim3(256), 0, s, p);
+  else hipLaunchKernelGGL((relpos_terms_mfma_kernel<E, 8>), grid, dim3(256), 0, s, p);
+}
+
 hipError_t launch_relpos_terms(const TermsParams& p, hipStream_t s) {
+  if (terms_mfma_ok(p)) {
+    if (p.dtype == 2) launch_terms_mfma<_Float16>(p, s);
+    else launch_terms_mfma<__bf16>(p, s);
+    return hipGetLastError();
+  }
   dim3 grid((unsigned)p.grid_h, (unsigned)p.H, (unsigned)p.B);
   if (p.dtype == 0) launch_terms_typed<float>(p, grid, s);
   else if (p.dtype == 2) launch_terms_typed<_Float16>(p, grid, s);

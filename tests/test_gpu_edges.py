@@ -506,3 +506,47 @@ def test_generic_relpos_wave_split(gpu, waves, fused):
     ref = oracle.sdpa(np64(x["q"]), np64(x["k"]), np64(x["v"]), layout=wl.layout, scale=wl.scale, rel_pos=rp)
     assert max_err(np64(o), ref["o"]) <= TOL["fp32"]
     assert max_err(np64(lse), ref["lse"]) <= TOL["fp32"]
+
+
+TERMS_GRIDS = [(14, 14), (64, 64), (40, 24), (5, 27), (16, 64), (9, 96), (3, 100)]
+
+
+@pytest.mark.parametrize("mfma", [1, 0])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("D", [32, 64, 128])
+@pytest.mark.parametrize("grid", TERMS_GRIDS, ids=[f"{a}x{b}" for a, b in TERMS_GRIDS])
+def test_relpos_terms_kernels(gpu, mfma, dtype, D, grid):
+    """relpos_terms on the matrix cores (32-token blocks, products over the
+    table rows each block needs, skewed read-out through LDS) and on the
+    vector ALUs, against the oracle: grids whose 32-token blocks stay in one
+    grid row (64 and 96 wide) or span several (14, 24, 27 wide), a ragged last
+    block (5 x 27 = 135 tokens), head_dim 32 / 64 / 128, both layouts, and a
+    100-wide grid that only the vector kernel takes."""
+    gh, gw = grid
+    T, B, H = gh * gw, 2, 3
+    layout = "bshd" if (gh + D) % 2 else "bhsd"
+    q = rnd(layout_shape(B, H, T, D, layout), dtype, 60 + gh)
+    g = torch.Generator().manual_seed(61 + gw)
+    rh = (0.02 * torch.randn((2 * gh - 1, D), generator=g)).to(dtype)
+    rw = (0.02 * torch.randn((2 * gw - 1, D), generator=g)).to(dtype)
+    gpu.set_tuning("terms_mfma", mfma)
+    try:
+        th, tw = gpu.relpos_terms(q.cuda(), rh.cuda(), rw.cuda(), grid, layout=layout)
+        torch.cuda.synchronize()
+    finally:
+        gpu.set_tuning("terms_mfma", 1)
+    rth, rtw = oracle.relpos_terms(oracle.to_bhsd(np64(q), layout), np64(rh), np64(rw), gh, gw)
+    assert max_err(np64(th), rth) <= 1e-4 and max_err(np64(tw), rtw) <= 1e-4
+
+
+def test_relpos_terms_full_size(gpu):
+    """SAM ViT-B global grid at full size (12 heads, 64 x 64, head_dim 64):
+    both term arrays against the oracle, every element."""
+    wl = workloads.WORKLOADS["sam_global_relpos"]
+    x = workloads.generate(wl, seed=4)
+    g = {k_: t.cuda() for k_, t in x.items()}
+    th, tw = gpu.relpos_terms(g["q"], g["rel_pos_h"], g["rel_pos_w"], wl.grid, layout=wl.layout)
+    torch.cuda.synchronize()
+    rth, rtw = oracle.relpos_terms(oracle.to_bhsd(np64(x["q"]), wl.layout), np64(x["rel_pos_h"]),
+                                   np64(x["rel_pos_w"]), *wl.grid)
+    assert max_err(np64(th), rth) <= 1e-4 and max_err(np64(tw), rtw) <= 1e-4
