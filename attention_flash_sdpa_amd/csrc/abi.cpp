@@ -26,7 +26,7 @@ std::atomic<int64_t> g_split64{1};
 std::atomic<int64_t> g_split64w{1};
 std::atomic<int64_t> g_tiled{1};
 std::atomic<int64_t> g_generic_waves{0};
-std::atomic<int64_t> g_terms_mfma{1};
+std::atomic<int64_t> g_relpos_mfma{1};
 
 // The tuning knobs as one call sees them: read once at the call's start, so
 // the route, the split count and the workspace check of that call agree even
@@ -377,7 +377,7 @@ int relpos_terms(const void* q, int dtype, int layout, int64_t B, int64_t H, int
   t.rel_h = rel_pos_h; t.rel_w = rel_pos_w;
   t.grid_h = (int)grid_h; t.grid_w = (int)grid_w;
   t.term_h = term_h; t.term_w = term_w;
-  t.use_mfma = g_terms_mfma.load() != 0;
+  t.use_mfma = g_relpos_mfma.load() != 0;
   hipError_t e = sdpa::launch_relpos_terms(t, (hipStream_t)stream);
   if (e != hipSuccess) return fail(SDPA_ERR_HIP, "relpos_terms launch failed: %s", hipGetErrorString(e));
   return SDPA_OK;
@@ -671,9 +671,9 @@ int sdpa_set_tuning(const char* key, int64_t value) {
     g_split64w.store(value);
     return SDPA_OK;
   }
-  if (!std::strcmp(key, "terms_mfma")) {
-    if (value != 0 && value != 1) return fail(SDPA_ERR_INVALID, "terms_mfma must be 0 or 1");
-    g_terms_mfma.store(value);
+  if (!std::strcmp(key, "relpos_mfma")) {
+    if (value != 0 && value != 1) return fail(SDPA_ERR_INVALID, "relpos_mfma must be 0 or 1");
+    g_relpos_mfma.store(value);
     return SDPA_OK;
   }
   if (!std::strcmp(key, "generic_waves")) {

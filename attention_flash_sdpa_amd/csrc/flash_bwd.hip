@@ -599,6 +599,9 @@ __global__ __launch_bounds__(256, (D == 128 ? 1 : 2)) void bwd_dq_kernel(BwdPara
   const float* twr = nullptr;
   __attribute__((address_space(3))) float* dts = nullptr;
   constexpr bool FASTM = MODE == B_NONE || MODE == B_INDEX || MODE == B_RELPOS64;
+  // the accumulators are read after the loop behind lane-divergent branches on
+  // the rel-pos paths (not needed on the matrix-product path at head_dim 32 / 64)
+  constexpr bool FENCE_END = !(RPS && D != 128);
   const bool sl = MODE == B_INDEX && p.bias == BIAS_SLIDING;
   // 64-wide grid: a 64-key tile is one grid row y, and the lane's 32 registers of
   // a tile always hold the same 32 columns, so the running sums of dS per column
@@ -725,8 +728,13 @@ __global__ __launch_bounds__(256, (D == 128 ? 1 : 2)) void bwd_dq_kernel(BwdPara
           sacc = mfma32(ld_row<E, D>(ks, 32 * kb + nl, c, g), qf[c], sacc);
           dpacc = mfma32(ld_row<E, D>(vs, 32 * kb + nl, c, g), of[c], dpacc);
         }
-        // the mask / term reads below branch on lane conditions before sacc and dpacc are read
-        if (!FASTM) mfma_drain(sacc, dpacc);
+        // The mask / term reads below branch on lane conditions before sacc and
+        // dpacc are read: fence them.  Not on the matrix-product dS-sum path at
+        // head_dim 32 / 64, where the compiler's own wait states hold on every
+        // path (tests/test_isa_hazards.py checks each instance) and the fence's
+        // AGPR operands would force copies and spills.
+        constexpr bool FENCE = !FASTM && !(MODE == B_RELPOS && RPS && D != 128);
+        if (FENCE) mfma_drain(sacc, dpacc);
         float ds[16];
         // rel-pos: grid (row, col) of the first key of each group of 4 this lane holds
         int grow[4] = {0, 0, 0, 0}, gcol[4] = {0, 0, 0, 0};
@@ -860,11 +868,14 @@ __global__ __launch_bounds__(256, (D == 128 ? 1 : 2)) void bwd_dq_kernel(BwdPara
       }
     }
     if (more) lstore(buf ^ 1);
-    // the accumulators are read after the loop, behind branches
-    if (!more) {
+    // The rel-pos paths read the accumulators after the loop behind
+    // lane-divergent branches: fence them there.  (Elsewhere the compiler's own
+    // wait states hold on every path, and an AGPR fence on the VGPR-resident
+    // accumulators would only add copies and spills.)
+    if (MODE == B_RELPOS && FENCE_END && !more) {
 #pragma unroll
       for (int nb = 0; nb < C::DB; ++nb) mfma_drain(dqT[nb]);
-      if (MODE == B_RELPOS && RPS) mfma_drain(dthT, dtwT);
+      if (RPS) mfma_drain(dthT, dtwT);
     }
     __syncthreads();
   }

@@ -479,6 +479,9 @@ def main():
                          "lse, formed before timing); 'dropout' times drawing the keep bits plus the forward "
                          "pass with attention dropout (rate 0.1); 'weights' times the attention-weights output "
                          "(unmasked or index-masked workloads)")
+    ap.add_argument("--batch", type=int, default=0, metavar="B",
+                    help="override the workload's batch size (windowed workloads then draw plain random windows "
+                         "instead of cutting them from one padded image); for scaling studies, not the headline")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB per step (counter calibration)")
     args = ap.parse_args()
@@ -504,6 +507,11 @@ def main():
             print("bench.py: --dtype applies to 16-bit workloads", file=sys.stderr)
             sys.exit(2)
         wl = wl.with_(dtype=args.dtype)
+    if args.batch:
+        if args.batch < 1:
+            print("bench.py: --batch must be positive", file=sys.stderr)
+            sys.exit(2)
+        wl = wl.with_(B=args.batch, window_image=None)
     x = workloads.generate(wl, seed=0)
     g = {k: t.cuda() for k, t in x.items()}
     if args.pass_ == "backward":
@@ -544,6 +552,8 @@ def main():
     rec_name = wl.name + ("_additive" if args.route == "additive" else "")
     if args.dtype and args.dtype != workloads.WORKLOADS[args.workload].dtype:
         rec_name += "_" + args.dtype
+    if args.batch:
+        rec_name += f"_b{args.batch}"
     traffic, traffic_src = recorded_traffic(kernel, rec_name)
     flash_ms = call_ms - terms_ms
     flash_flops = attn + (2 * allowed_pairs(wl) * wl.B * wl.Hq if wl.relpos else 0)

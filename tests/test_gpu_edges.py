@@ -529,12 +529,12 @@ def test_relpos_terms_kernels(gpu, mfma, dtype, D, grid):
     g = torch.Generator().manual_seed(61 + gw)
     rh = (0.02 * torch.randn((2 * gh - 1, D), generator=g)).to(dtype)
     rw = (0.02 * torch.randn((2 * gw - 1, D), generator=g)).to(dtype)
-    gpu.set_tuning("terms_mfma", mfma)
+    gpu.set_tuning("relpos_mfma", mfma)
     try:
         th, tw = gpu.relpos_terms(q.cuda(), rh.cuda(), rw.cuda(), grid, layout=layout)
         torch.cuda.synchronize()
     finally:
-        gpu.set_tuning("terms_mfma", 1)
+        gpu.set_tuning("relpos_mfma", 1)
     rth, rtw = oracle.relpos_terms(oracle.to_bhsd(np64(q), layout), np64(rh), np64(rw), gh, gw)
     assert max_err(np64(th), rth) <= 1e-4 and max_err(np64(tw), rtw) <= 1e-4
 

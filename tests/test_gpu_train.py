@@ -364,6 +364,56 @@ def test_relpos_backward_matches_oracle(gpu, case):
         assert e < GTOL[dt], (name, e)
 
 
+TERMS_KERNEL_CASES = [
+    # dtype, layout, B, H, grid, D
+    ("bf16", "bhsd", 1, 2, (16, 64), 64),     # blocks within one 64-wide grid row
+    ("bf16", "bshd", 2, 3, (14, 14), 64),     # blocks across rows (windows)
+    ("fp16", "bhsd", 1, 2, (5, 27), 128),     # ragged last block
+    ("bf16", "bhsd", 2, 2, (40, 24), 32),
+    ("fp16", "bshd", 1, 3, (24, 40), 64),
+]
+
+
+@pytest.mark.parametrize("case", TERMS_KERNEL_CASES,
+                         ids=[f"{c[0]}-{c[1]}-B{c[2]}H{c[3]}-{c[4][0]}x{c[4][1]}-D{c[5]}" for c in TERMS_KERNEL_CASES])
+def test_relpos_backward_with_either_terms_kernel(gpu, case):
+    """The rel-pos backward recomputes the terms with relpos_terms: with the
+    matrix-core terms kernel and with the vector one, both match the oracle,
+    and the fp32 dq of the two agree to u, the 16-bit type's unit roundoff
+    (2^-8 bf16, 2^-11 fp16), of its largest value: the two kernels' fp32
+    sums differ only in order, which can move a probability across a 16-bit
+    rounding boundary before the products."""
+    dts, layout, B, H, grid, D = case
+    dt = DT[dts]
+    gh, gw = grid
+    T = gh * gw
+    rng = np.random.default_rng(41)
+    q, k, v, do = (draw(rng, shp(layout, B, H, T, D), dt) for _ in range(4))
+    rh = (0.3 * draw(rng, (2 * gh - 1, D), torch.float32)).to(dt)
+    rw = (0.3 * draw(rng, (2 * gw - 1, D), torch.float32)).to(dt)
+    scale = 1.0 / np.sqrt(D)
+    rp = {"rel_pos_h": np64(rh), "rel_pos_w": np64(rw), "grid": grid}
+    fwd = st.sdpa_train_fwd(np64(q), np64(k), np64(v), layout=layout, scale=scale, rel_pos=rp)
+    o = torch.from_numpy(np.ascontiguousarray(fwd["o"], dtype=np.float32)).to(dt).cuda()
+    lse = torch.from_numpy(fwd["lse"].astype(np.float32)).cuda()
+    g = [t.cuda() for t in (q, k, v, do, rh, rw)]
+    outs = {}
+    try:
+        for mf in (1, 0):
+            gpu.set_tuning("relpos_mfma", mf)
+            outs[mf] = gpu.sdpa_relpos_backward(g[0], g[1], g[2], o, g[3], lse, g[4], g[5], grid, layout=layout,
+                                                scale=scale, grad_dtype=torch.float32)
+            torch.cuda.synchronize()
+    finally:
+        gpu.set_tuning("relpos_mfma", 1)
+    u = 2.0 ** -8 if dt == torch.bfloat16 else 2.0 ** -11
+    assert norm_err(np64(outs[1][0]), np64(outs[0][0])) < u
+    ref = st.sdpa_bwd(np64(q), np64(k), np64(v), np64(do), layout=layout, scale=scale, rel_pos=rp)
+    for mf in (1, 0):
+        for j, name in enumerate(("dq", "dk", "dv", "drel_pos_h", "drel_pos_w")):
+            assert norm_err(np64(outs[mf][j]), ref[name]) < GTOL[dt], (mf, name)
+
+
 def test_relpos_backward_after_library_forward(gpu):
     """The library's own forward (fused terms) feeding its backward, SAM window shape."""
     rng = np.random.default_rng(38)
