@@ -72,13 +72,16 @@ struct BCfg {
   static constexpr int QC = D / 16;     // k-chunks of a contraction over head_dim
   static constexpr int DB = D / 32;     // 32-wide blocks of head_dim
   // Chunk c of row r sits at chunk position c ^ swz(r).  16 consecutive rows
-  // read at one chunk index hit 16 distinct 16-byte bank groups, and the 4
-  // consecutive rows of a transposing read (32 contiguous bytes each) land in
-  // 4 distinct 32-byte bank groups.
+  // read at one chunk index hit 16 distinct 16-byte bank groups.  A
+  // transposing read takes 4 consecutive rows x 32 contiguous bytes for each
+  // of two 16-column halves; the swizzle moves the 4 rows' pieces apart in
+  // the bits above the lowest of the 32-byte group index, so the two halves
+  // (whose group indices differ in the lowest bit) never share a group: 8
+  // pieces in 8 distinct groups.  Depends on r % 16 only.
   static __device__ __forceinline__ int swz(int r) {
     if (D == 32) return (r >> 2) & 3;
-    if (D == 64) return (((r >> 1) & 3) << 1) | ((r >> 3) & 1);
-    return ((r & 7) << 1) | ((r >> 3) & 1);
+    if (D == 64) return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+    return ((r & 3) << 2) | (((r >> 2) & 1) << 1) | ((r >> 3) & 1);
   }
 };
 
