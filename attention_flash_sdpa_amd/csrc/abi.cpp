@@ -61,19 +61,36 @@ void set_strides(int layout, int64_t H, int64_t T, int64_t D, int64_t* sb, int64
 
 // Split-KV chunk count: few query rows against a long key range leave most of
 // the GPU idle, so the key range is cut into chunks that run in parallel and
-// are merged by their log-sum-exp afterwards.
-int plan_splits(int64_t B, int64_t Hq, int64_t Tq, int64_t Tkv, int64_t D, int dtype, const Tuning& tu) {
-  // split-KV exists for the head_dim-16 query-packed kernel (few queries)
-  if (!sdpa::kSplitKvBuilt || !is16(dtype) || D != 16 || Tq > 8) return 1;
+// are merged by their log-sum-exp afterwards.  The count depends on sizes and
+// knobs only (not on the mask), so sdpa_workspace_size can answer before the
+// call; a call whose route cannot split runs unsplit (fwd_prepare).
+int plan_splits(int64_t B, int64_t Hq, int64_t Hkv, int64_t Tq, int64_t Tkv, int64_t D, int dtype, const Tuning& tu) {
+  if (!sdpa::kSplitKvBuilt || !is16(dtype)) return 1;
   const int64_t forced = tu.num_splits;
-  if (forced >= 1) return (int)std::min<int64_t>(forced, std::max<int64_t>(1, (Tkv + 63) / 64));
-  // one wave per (4 heads, 8 queries, key chunk): aim at ~512 waves with
-  // chunks of >= 64 keys (two tiles: the loads of the second overlap the first)
-  const int64_t waves = B * ((Hq + 3) / 4) * ((Tq + 7) / 8);
-  if (waves >= 512 || Tkv <= 64) return 1;
-  int64_t s = (512 + waves - 1) / waves;
-  s = std::min<int64_t>(s, (Tkv + 63) / 64);
-  return (int)std::max<int64_t>(1, std::min<int64_t>(s, 1024));
+  if (D == 16) {
+    // the head_dim-16 query-packed kernel (few queries)
+    if (Tq > 8) return 1;
+    if (forced >= 1) return (int)std::min<int64_t>(forced, std::max<int64_t>(1, (Tkv + 63) / 64));
+    // one wave per (4 heads, 8 queries, key chunk): aim at ~512 waves with
+    // chunks of >= 64 keys (two tiles: the loads of the second overlap the first)
+    const int64_t waves = B * ((Hq + 3) / 4) * ((Tq + 7) / 8);
+    if (waves >= 512 || Tkv <= 64) return 1;
+    int64_t s = (512 + waves - 1) / waves;
+    s = std::min<int64_t>(s, (Tkv + 63) / 64);
+    return (int)std::max<int64_t>(1, std::min<int64_t>(s, 1024));
+  }
+  if ((D != 64 && D != 128) || !tu.tiled) return 1;
+  // the double-buffered head_dim 64 / 128 kernel: up to 64 chunks of >= 32 keys
+  if (forced >= 1) return (int)std::min<int64_t>({forced, 64, std::max<int64_t>(1, (Tkv + 31) / 32)});
+  // workgroups of 4 waves x 32 query rows (heads sharing a KV head packed
+  // together): under 128 of them leave the 256 CUs mostly idle; aim at ~512
+  // with chunks of >= 256 keys (8 tiles: the pipeline's fill is paid once per chunk)
+  const int64_t grp = Hq / std::max<int64_t>(Hkv, 1);
+  const int64_t hpw = grp % 4 == 0 ? 4 : grp % 2 == 0 ? 2 : 1;
+  const int64_t wgs = B * (Hq / hpw) * ((Tq + 32 * (4 / hpw) - 1) / (32 * (4 / hpw)));
+  if (wgs >= 128 || Tkv < 512) return 1;
+  const int64_t s = std::min<int64_t>({(512 + wgs - 1) / wgs, Tkv / 256, 64});
+  return (int)std::max<int64_t>(1, s);
 }
 
 size_t split_bytes(int splits, int64_t B, int64_t Hq, int64_t Tq, int64_t D) {
@@ -283,7 +300,7 @@ size_t sdpa_workspace_size(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_
                                             grid_h, grid_w, D, &dummy, &dummy, scale, nullptr);
     return relpos_fused_ok(p, tu) ? 0 : terms_bytes(B, Hq, Tq, grid_h, grid_w);
   }
-  return split_bytes(plan_splits(B, Hq, Tq, Tkv, D, dtype, tu), B, Hq, Tq, D);
+  return split_bytes(plan_splits(B, Hq, Hkv, Tq, Tkv, D, dtype, tu), B, Hq, Tq, D);
 }
 
 }  // extern "C"
@@ -303,7 +320,13 @@ int fwd_prepare(const void* q, const void* k, const void* v, void* o, int dtype,
   sdpa::FwdParams p = base_params(q, k, v, o, dtype, out_dtype, layout, B, Hq, Hkv, Tq, Tkv, D, scale, lse);
   st = apply_mask(mask, p);
   if (st) return st;
-  p.num_splits = plan_splits(B, Hq, Tq, Tkv, D, dtype, tu);
+  p.num_splits = plan_splits(B, Hq, Hkv, Tq, Tkv, D, dtype, tu);
+  // only the head_dim-16 and double-buffered kernels split; a call that lands
+  // elsewhere (e.g. a tensor mask at head_dim 64 / 128) runs unsplit
+  if (p.num_splits > 1) {
+    const Route r = route_of(p, tu);
+    if (r != R_D16 && r != R_TILED) p.num_splits = 1;
+  }
   *need = split_bytes(p.num_splits, B, Hq, Tq, D);
   *out = p;
   return SDPA_OK;
@@ -344,6 +367,11 @@ int sdpa_fwd_noalloc(const void* q, const void* k, const void* v, void* o, int d
   size_t need = 0;
   int st = fwd_prepare(q, k, v, o, dtype, out_dtype, layout, B, Hq, Hkv, Tq, Tkv, D, scale, mask, lse, tu, &p, &need);
   if (st) return st;
+  if (need > sdpa::kNoAllocScratchBytes && tu.num_splits == 0) {
+    // an automatic split count is lowered to what the fixed scratch holds
+    while (p.num_splits > 1 && split_bytes(p.num_splits, B, Hq, Tq, D) > sdpa::kNoAllocScratchBytes) --p.num_splits;
+    need = split_bytes(p.num_splits, B, Hq, Tq, D);
+  }
   if (need) {
     if (need > sdpa::kNoAllocScratchBytes)
       return fail(SDPA_ERR_UNSUPPORTED, "split-KV partials of %zu bytes exceed the fixed %zu-byte scratch", need,

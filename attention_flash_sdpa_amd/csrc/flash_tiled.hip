@@ -108,7 +108,7 @@ __device__ __forceinline__ float pair_sum(float v) {
 }
 
 template <typename E, int D, int MODE, bool OUT16, bool DROP>
-__global__ __launch_bounds__(256, 3) void flash_tiled_kernel(FwdParams p, int hpw, int64_t mask_bytes) {
+__global__ __launch_bounds__(256, 3) void flash_tiled_kernel(FwdParams p, int hpw, int64_t mask_bytes, int kps) {
   typedef typename Vec16<E>::x8 e8;
   typedef typename Vec16<E>::x4 e4;
   typedef typename Vec16<E>::x2 e2;
@@ -138,7 +138,11 @@ __global__ __launch_bounds__(256, 3) void flash_tiled_kernel(FwdParams p, int hp
   const int64_t lin = blockIdx.x + (int64_t)gridDim.x * (blockIdx.y + (int64_t)gridDim.y * blockIdx.z);
   const int64_t per = nblk / 8, rem = nblk % 8, xcd = lin % 8;
   const int64_t lid = xcd * per + min(xcd, rem) + lin / 8;
-  const int64_t bx = lid % gridDim.x, hgrp = (lid / gridDim.x) % gridDim.y, b = lid / ((int64_t)gridDim.x * gridDim.y);
+  const int64_t bx = lid % gridDim.x, hgrp = (lid / gridDim.x) % gridDim.y, bz = lid / ((int64_t)gridDim.x * gridDim.y);
+  // split-KV: the z index runs over (batch, key chunk); chunk `split` holds
+  // keys [split * kps, (split + 1) * kps), kps a multiple of the tile
+  const int nsplit = p.num_splits > 1 ? p.num_splits : 1;
+  const int64_t b = bz / nsplit, split = bz % nsplit;
   const int64_t qtile = (MODE == T_INDEX) ? (int64_t)gridDim.x - 1 - bx : bx;
   const int64_t h = hgrp * hpw + (wave % hpw);
   const int64_t hk = h / (p.Hq / p.Hkv);
@@ -160,6 +164,10 @@ __global__ __launch_bounds__(256, 3) void flash_tiled_kernel(FwdParams p, int hp
   if (MODE == T_INDEX) {
     hi = min(hi, wg_q1 + p.offset + 1);
     if (p.bias == BIAS_SLIDING) lo = max((int64_t)0, wg_q0 + p.offset - p.window + 1);
+  }
+  if (nsplit > 1) {
+    lo = max(lo, split * kps);
+    hi = min(hi, (split + 1) * kps);
   }
   const int tlo = (int)(lo / BN);
   const int thi = hi > lo ? (int)((hi + BN - 1) / BN) : tlo;
@@ -370,8 +378,21 @@ __global__ __launch_bounds__(256, 3) void flash_tiled_kernel(FwdParams p, int hp
   }
 
   const float lt = pair_sum(l);
-  const float inv = lt > 0.0f ? (DROP ? p.keep_scale : 1.0f) / lt : 0.0f;
   if (!qvalid) return;
+  if (nsplit > 1) {
+    // this chunk's unnormalised O and (running max in log2 units, row sum)
+    const int64_t prow = ((split * p.B + b) * p.Hq + h) * p.Tq + qrow;
+    float* po = p.part_o + prow * D;
+#pragma unroll
+    for (int d = 0; d < C::DB; ++d)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4)
+        *(f32x4*)(po + d * 32 + 8 * i4 + 4 * g) =
+            (f32x4){o[d][4 * i4], o[d][4 * i4 + 1], o[d][4 * i4 + 2], o[d][4 * i4 + 3]};
+    if (g == 0) *(f32x2*)(p.part_ml + prow * 2) = (f32x2){m, lt};
+    return;
+  }
+  const float inv = lt > 0.0f ? (DROP ? p.keep_scale : 1.0f) / lt : 0.0f;
   const int64_t ob = b * p.q_sb + h * p.q_sh + qrow * p.q_st;
 #pragma unroll
   for (int d = 0; d < C::DB; ++d)
@@ -393,6 +414,58 @@ __global__ __launch_bounds__(256, 3) void flash_tiled_kernel(FwdParams p, int hp
   if (p.lse && g == 0) p.lse[(b * p.Hq + h) * p.Tq + qrow] = lt > 0.0f ? (m + __log2f(lt)) * kLn2 : -INFINITY;
 }
 
+// Merge of the key chunks: O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s,
+// M = max_s m_s.  One workgroup per output row: thread t takes head dim t % D
+// and the chunks s = t / D, t / D + 256 / D, ... in order (loads eight chunks
+// at a time), and the 256 / D partial sums of a dim then add in a fixed order,
+// so the result does not depend on timing.
+template <typename E, int D, bool OUT16>
+__global__ __launch_bounds__(256) void tiled_combine_kernel(FwdParams p) {
+  constexpr int G = 256 / D;                   // chunk groups
+  constexpr int NB = 8;
+  __shared__ float msh[64], lsh[64];
+  __shared__ float part[G][D];
+  const int tid = threadIdx.x, d = tid % D, sg = tid / D;
+  const int S = p.num_splits;
+  const int64_t rows = p.B * p.Hq * p.Tq;
+  const int64_t r = blockIdx.x;
+  float M = -INFINITY, L = 0.0f;
+  // (m, l) of every chunk: S <= 64, one thread each
+  if (tid < S) {
+    const f32x2 ml = *(const f32x2*)(p.part_ml + ((int64_t)tid * rows + r) * 2);
+    msh[tid] = ml[0];
+    lsh[tid] = ml[1];
+  }
+  __syncthreads();
+  for (int s = 0; s < S; ++s) M = fmaxf(M, msh[s]);
+  for (int s = 0; s < S; ++s)
+    if (msh[s] != -INFINITY) L = fmaf(fexp2(msh[s] - M), lsh[s], L);
+  float acc = 0.0f;
+  for (int s0 = sg; s0 < S; s0 += G * NB) {
+    float v[NB], w[NB];
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+      const int s = s0 + G * u;
+      v[u] = s < S ? p.part_o[((int64_t)s * rows + r) * D + d] : 0.0f;
+      w[u] = (s < S && msh[s < S ? s : 0] != -INFINITY) ? fexp2(msh[s] - M) : 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < NB; ++u) acc = fmaf(w[u], v[u], acc);
+  }
+  part[sg][d] = acc;
+  __syncthreads();
+  if (sg != 0) return;
+  float tot = 0.0f;
+#pragma unroll
+  for (int u = 0; u < G; ++u) tot += part[u][d];
+  const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+  const int64_t b = r / (p.Hq * p.Tq), h = (r / p.Tq) % p.Hq, i = r % p.Tq;
+  const int64_t ob = b * p.q_sb + h * p.q_sh + i * p.q_st + d;
+  if (OUT16) ((E*)p.o)[ob] = (E)(tot * inv);
+  else ((float*)p.o)[ob] = tot * inv;
+  if (p.lse && d == 0) p.lse[r] = L > 0.0f ? (M + __log2f(L)) * kLn2 : -INFINITY;
+}
+
 int mask_es(const FwdParams& p) { return p.bias == BIAS_BOOL ? 1 : (p.mdtype == 0 ? 4 : 2); }
 
 template <typename E, int D, int MODE>
@@ -400,7 +473,9 @@ hipError_t launch_t(const FwdParams& p, hipStream_t s) {
   const int64_t grp = p.Hq / p.Hkv;
   const int hpw = (grp % 4 == 0) ? 4 : (grp % 2 == 0) ? 2 : 1;
   const int64_t rows = 32 * (4 / hpw);
-  dim3 grid((unsigned)((p.Tq + rows - 1) / rows), (unsigned)(p.Hq / hpw), (unsigned)p.B);
+  const int nsplit = p.num_splits > 1 ? p.num_splits : 1;
+  const int kps = (int)(((p.Tkv + nsplit - 1) / nsplit + BN - 1) / BN * BN);
+  dim3 grid((unsigned)((p.Tq + rows - 1) / rows), (unsigned)(p.Hq / hpw), (unsigned)(p.B * nsplit));
   // Record count of the mask descriptors: through the end of the 16-byte chunk
   // that holds the last element.  The copies move whole chunks and the
   // descriptor zeroes every dword past the record count, so a count that
@@ -414,13 +489,18 @@ hipError_t launch_t(const FwdParams& p, hipStream_t s) {
   mask_bytes = (mask_bytes + 15) & ~(int64_t)15;
   constexpr bool CAN_DROP = MODE == T_NONE || MODE == T_INDEX;
   if (CAN_DROP && p.keep) {
-    if (p.out_dtype != 0) hipLaunchKernelGGL((flash_tiled_kernel<E, D, MODE, true, CAN_DROP>), grid, dim3(256), 0, s, p, hpw, mask_bytes);
-    else hipLaunchKernelGGL((flash_tiled_kernel<E, D, MODE, false, CAN_DROP>), grid, dim3(256), 0, s, p, hpw, mask_bytes);
+    if (p.out_dtype != 0) hipLaunchKernelGGL((flash_tiled_kernel<E, D, MODE, true, CAN_DROP>), grid, dim3(256), 0, s, p, hpw, mask_bytes, kps);
+    else hipLaunchKernelGGL((flash_tiled_kernel<E, D, MODE, false, CAN_DROP>), grid, dim3(256), 0, s, p, hpw, mask_bytes, kps);
   } else if (p.out_dtype != 0) {
-    hipLaunchKernelGGL((flash_tiled_kernel<E, D, MODE, true, false>), grid, dim3(256), 0, s, p, hpw, mask_bytes);
+    hipLaunchKernelGGL((flash_tiled_kernel<E, D, MODE, true, false>), grid, dim3(256), 0, s, p, hpw, mask_bytes, kps);
   } else {
-    hipLaunchKernelGGL((flash_tiled_kernel<E, D, MODE, false, false>), grid, dim3(256), 0, s, p, hpw, mask_bytes);
+    hipLaunchKernelGGL((flash_tiled_kernel<E, D, MODE, false, false>), grid, dim3(256), 0, s, p, hpw, mask_bytes, kps);
   }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || nsplit == 1) return e;
+  const dim3 cgrid((unsigned)(p.B * p.Hq * p.Tq));
+  if (p.out_dtype != 0) hipLaunchKernelGGL((tiled_combine_kernel<E, D, true>), cgrid, dim3(256), 0, s, p);
+  else hipLaunchKernelGGL((tiled_combine_kernel<E, D, false>), cgrid, dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
@@ -438,7 +518,12 @@ hipError_t launch_d(const FwdParams& p, hipStream_t s) {
 }  // namespace
 
 bool tiled_supports(const FwdParams& p) {
-  if ((p.dtype != 1 && p.dtype != 2) || (p.D != 64 && p.D != 128) || p.num_splits != 1) return false;
+  if ((p.dtype != 1 && p.dtype != 2) || (p.D != 64 && p.D != 128)) return false;
+  // split-KV: no mask or causal / sliding masks, no dropout, at most 64 chunks, one merge workgroup per row
+  if (p.num_splits > 1 &&
+      (p.keep || p.num_splits > 64 || !(p.bias == BIAS_NONE || p.bias == BIAS_CAUSAL || p.bias == BIAS_SLIDING) ||
+       p.B * p.Hq * p.Tq > 0x7fffffffLL || p.B * p.num_splits > 65535))
+    return false;
   // attention dropout is built for no mask and causal / sliding masks
   if (p.keep && p.bias != BIAS_NONE && p.bias != BIAS_CAUSAL && p.bias != BIAS_SLIDING) return false;
   if (p.keep && p.Tq * p.keep_words * 4 > 0x7fffffffLL) return false;   // keep rows of a head: 32-bit offsets

@@ -595,9 +595,11 @@ def main():
                    "event_reps": 5, "calls_per_rep": args.steps},
     }
     if args.route == "additive":
-        # Reading the materialised bias bounds this route: report it against HBM.
-        gbs = nbytes / (flash_ms * 1e-3) / 1e9
         line["config"]["route"] = "additive mask (bias materialised before timing)"
+    if args.route == "additive" or flash_flops / nbytes < MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9):
+        # Below the ridge (FLOPs per algorithmic byte under peak FLOP/s / peak bytes/s: decode
+        # shapes, the windows, a materialised bias) HBM bounds the call: report it against HBM.
+        gbs = nbytes / (flash_ms * 1e-3) / 1e9
         line["roofline"].update({"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                  "frac": round(gbs / HBM_PEAK_GBS, 4), "attention_tflops": round(achieved, 3)})
     if not args.no_cpu:

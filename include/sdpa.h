@@ -103,10 +103,15 @@ typedef struct sdpa_mask {
  * (relpos = 1; then Tq = Tkv = grid_h * grid_w and Hkv = Hq) needs for a call
  * with this input dtype, these sizes and this scale (NaN = 1/sqrt(D)), under
  * the current tuning knobs.  The answer follows the route the call takes:
- * split-KV partials for few-query head_dim-16 calls, fp32 term arrays for a
- * rel-pos call that cannot form its terms inside the attention kernel, and 0
- * when the call needs none (e.g. every fused rel-pos route, SAM ViT-B's
- * 64 x 64 global grid included).  Pure host arithmetic: no HIP call.
+ * split-KV partials for few-query head_dim-16 calls and for 16-bit
+ * head_dim-64 / 128 calls whose query blocks leave most of the GPU idle
+ * against a long key range (decode shapes), fp32 term arrays for a rel-pos
+ * call that cannot form its terms inside the attention kernel, and 0 when the
+ * call needs none (e.g. every fused rel-pos route, SAM ViT-B's 64 x 64 global
+ * grid included).  The mask is not an argument: the answer is the unmasked
+ * call's, which is also enough for any mask (a head_dim-64 / 128 call with a
+ * tensor mask runs unsplit and leaves the workspace unused).  Pure host
+ * arithmetic: no HIP call.
  * Returns (size_t)-1 for invalid sizes or dtype.
  */
 size_t sdpa_workspace_size(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t Tq, int64_t Tkv,
@@ -137,13 +142,14 @@ int sdpa_fwd(const void* q, const void* k, const void* v, void* o,
  * sdpa_fwd for callers that cannot allocate device memory: code under HIP
  * graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same
  * arguments, results and kernels as sdpa_fwd, minus the workspace: the
- * split-KV partials of the few-query head_dim-16 route live in a fixed
- * 8 MiB device array inside the library (one copy per GPU, held until the
- * process ends).  The call allocates and frees nothing; its first call on a
- * device looks up that device's copy of the array (hipGetSymbolAddress).
- * A call whose partials exceed 8 MiB returns SDPA_ERR_UNSUPPORTED (the
- * automatic split count stays far below it; a large forced "num_splits" can
- * reach it).  Every call on one GPU shares that GPU's array and leaves the
+ * split-KV partials of the few-query routes live in a fixed 8 MiB device
+ * array inside the library (one copy per GPU, held until the process ends).
+ * The call allocates and frees nothing; its first call on a device looks up
+ * that device's copy of the array (hipGetSymbolAddress).  Where the automatic
+ * split count's partials would exceed 8 MiB the call runs with the largest
+ * count that fits (results then equal sdpa_fwd's up to rounding, not
+ * bitwise); a forced "num_splits" whose partials exceed 8 MiB returns
+ * SDPA_ERR_UNSUPPORTED.  Every call on one GPU shares that GPU's array and leaves the
  * last call's partials in it: calls that overlap on one GPU (concurrent
  * streams or threads) race on it and must be serialised by the caller.
  */
@@ -212,7 +218,10 @@ const char* sdpa_last_kernel(void);
 /*
  * Process-wide tuning knobs (tests and benchmarks), each an int64:
  *   "num_splits"   split-KV chunk count for sdpa_fwd; 0 = automatic (default),
- *                  1 = never split, n > 1 = n chunks when the kernel supports it.
+ *                  1 = never split, n > 1 = n chunks when the kernel supports it
+ *                  (head_dim 16 with <= 8 queries: chunks of >= 64 keys, at most
+ *                  1024; 16-bit head_dim 64 / 128 with no mask or a causal /
+ *                  sliding mask: chunks of >= 32 keys, at most 64).
  *   "split_halves" 1 (default) = for head_dim 64 with few query rows, each
  *                  workgroup splits the key range between its waves and merges
  *                  the halves; 0 = always one key range per wave.

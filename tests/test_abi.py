@@ -189,6 +189,31 @@ def test_workspace_sizes():
         assert lib.sdpa_workspace_size(1, 1, 8, 8, 7, 4096, 16, 0.25, 0, 0, 0) == 0
     finally:
         assert lib.sdpa_set_tuning(b"num_splits", 0) == 0
+    # head_dim 64 / 128 decode shapes (a few workgroups against a long key range): split-KV partials,
+    # fp32 [chunks, B, Hq, Tq, D] plus the (max, sum) pairs; none once the query blocks fill the GPU,
+    # none for short key ranges, none for fp32 inputs
+    for D in (64, 128):
+        n = lib.sdpa_workspace_size(1, 1, 32, 8, 1, 8192, D, nan, 0, 0, 0)
+        assert n >= 2 * 32 * D * 4 and n % 256 == 0
+        assert lib.sdpa_workspace_size(2, 1, 32, 8, 1, 8192, D, nan, 0, 0, 0) == n
+        assert lib.sdpa_workspace_size(0, 1, 32, 8, 1, 8192, D, nan, 0, 0, 0) == 0
+        assert lib.sdpa_workspace_size(1, 1, 32, 8, 1, 300, D, nan, 0, 0, 0) == 0
+        assert lib.sdpa_workspace_size(1, 64, 32, 8, 64, 8192, D, nan, 0, 0, 0) == 0
+    # a forced count is capped at 64 chunks of >= 32 keys
+    assert lib.sdpa_set_tuning(b"num_splits", 1000) == 0
+    try:
+        a256 = lambda n: (n + 255) // 256 * 256
+        need = lambda s: a256(s * 4 * 128 * 4) + a256(s * 4 * 2 * 4)     # 4 rows (B = 1, Hq = 4, Tq = 1)
+        assert lib.sdpa_workspace_size(1, 1, 4, 4, 1, 100000, 128, nan, 0, 0, 0) == need(64)
+        assert lib.sdpa_workspace_size(1, 1, 4, 4, 1, 100, 128, nan, 0, 0, 0) == need(4)
+    finally:
+        assert lib.sdpa_set_tuning(b"num_splits", 0) == 0
+    # with the double-buffered kernel switched off no head_dim 64 / 128 call splits
+    assert lib.sdpa_set_tuning(b"tiled", 0) == 0
+    try:
+        assert lib.sdpa_workspace_size(1, 1, 32, 8, 1, 8192, 128, nan, 0, 0, 0) == 0
+    finally:
+        assert lib.sdpa_set_tuning(b"tiled", 1) == 0
 
 
 # ---- the binding checks every shape, dtype and device before any launch (no GPU needed:

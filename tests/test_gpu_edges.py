@@ -198,6 +198,64 @@ def test_d16_split_kv_invariance(gpu, splits):
         gpu.set_tuning("num_splits", 0)
 
 
+TILED_SPLIT_CASES = [
+    # (B, Hq, Hkv, Tq, Tkv, layout, mask): decode-like shapes on the double-buffered kernel
+    (1, 8, 2, 1, 4096, "bhsd", None),                                            # 4 heads per workgroup
+    (2, 4, 4, 5, 1000, "bshd", {"kind": "causal", "offset": 995}),               # one head per workgroup
+    (1, 6, 3, 33, 3001, "bhsd", {"kind": "sliding", "window": 700, "offset": 2968}),   # chunks outside the window
+    (1, 4, 2, 3, 700, "bhsd", {"kind": "causal", "offset": -1}),                 # row 0 has no allowed key
+]
+
+
+@pytest.mark.parametrize("splits", [1, 2, 7, 64, 0])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+def test_tiled_split_kv_invariance(gpu, splits, D, dtype):
+    """Head_dim 64 / 128 split-KV: the key range cut into 1 .. 64 chunks (0 =
+    the automatic count), each chunk's (max, sum, unnormalised O) merged by
+    log-sum-exp, gives the attention and the log-sum-exp of the oracle; rows
+    with no allowed key stay O = 0, lse = -inf."""
+    gpu.set_tuning("num_splits", splits)
+    try:
+        for i, (B, Hq, Hkv, Tq, Tkv, layout, mask) in enumerate(TILED_SPLIT_CASES):
+            check(gpu, B, Hq, Hkv, Tq, Tkv, D, dtype=dtype, layout=layout, mask=mask, seed=40 + i)
+            if splits != 1:
+                assert gpu.last_kernel() == "flash_tiled_kernel"
+    finally:
+        gpu.set_tuning("num_splits", 0)
+
+
+def test_tiled_split_kv_automatic_and_deterministic(gpu):
+    """A decode shape takes the split route by itself (the workspace query
+    says so), and two calls give bit-identical output and log-sum-exp (the
+    chunks merge in a fixed order)."""
+    lib = gpu.load()
+    B, Hq, Hkv, Tq, Tkv, D = 1, 32, 8, 1, 8192, 128
+    assert lib.sdpa_workspace_size(1, B, Hq, Hkv, Tq, Tkv, D, float("nan"), 0, 0, 0) > 0
+    q, k, v = (rnd(s, torch.bfloat16, 50 + j).cuda()
+               for j, s in enumerate([(B, Hq, Tq, D), (B, Hkv, Tkv, D), (B, Hkv, Tkv, D)]))
+    o1, l1 = gpu.sdpa(q, k, v, out_dtype=torch.float32, return_lse=True)
+    assert gpu.last_kernel() == "flash_tiled_kernel"
+    o2, l2 = gpu.sdpa(q, k, v, out_dtype=torch.float32, return_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    ref = oracle.sdpa(np64(q), np64(k), np64(v))
+    assert max_err(np64(o1), ref["o"]) <= TOL["bf16"]
+    assert max_err(np64(l1), ref["lse"]) <= TOL["bf16"]
+
+
+def test_tiled_split_kv_tensor_mask_runs_unsplit(gpu):
+    """A forced chunk count with a tensor mask at head_dim 64: the split route
+    does not take tensor masks, so the call runs unsplit and stays exact."""
+    g = torch.Generator().manual_seed(51)
+    m = torch.rand((1, 4, 3, 2000), generator=g) < 0.7
+    gpu.set_tuning("num_splits", 8)
+    try:
+        check(gpu, 1, 4, 4, 3, 2000, 64, mask={"kind": "bool", "data": m}, seed=52)
+    finally:
+        gpu.set_tuning("num_splits", 0)
+
+
 @pytest.mark.parametrize("Tkv", [1, 7, 8, 9, 33, 64])
 def test_d16_key_packing(gpu, Tkv):
     check(gpu, 1, 8, 8, 300, Tkv, 16, scale=0.25, seed=14)

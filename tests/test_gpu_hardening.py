@@ -66,6 +66,7 @@ CANARY_CASES = [
     ("d16_qpack_splitkv", "sam_decoder_q7", "bhsd", True, {"num_splits": 5}),
     ("d16_kpack", "sam_decoder_kv7", "bshd", False, {}),
     ("tiled_causal", "gqa_causal", "bshd", False, {}),
+    ("tiled_splitkv", "gqa_decode", "bhsd", True, {}),
     ("generic_fp32_relpos", "tiny_relpos_fp32", "bhsd", True, {}),
     ("generic_relpos_terms", "tiny_relpos_fp32", "bshd", True, {"relpos_fused": 0}),
 ]
@@ -89,7 +90,7 @@ def test_guard_bands_untouched(gpu, case):
             ws_n = lib.sdpa_workspace_size(dt, wl.B, wl.Hq, wl.Hkv, wl.Tq, wl.Tkv, wl.D, wl.scale, 1, *wl.grid)
         else:
             ws_n = lib.sdpa_workspace_size(dt, wl.B, wl.Hq, wl.Hkv, wl.Tq, wl.Tkv, wl.D, wl.scale, 0, 0, 0)
-        if tuning.get("relpos_fused") == 0 or tuning.get("num_splits", 1) > 1:
+        if tuning.get("relpos_fused") == 0 or tuning.get("num_splits", 1) > 1 or wname == "gqa_decode":
             assert ws_n > 0            # the guarded workspace is really used
         n_o = g["q"].numel() * es_o
         n_l = wl.B * wl.Hq * wl.Tq * 4
@@ -120,10 +121,11 @@ def test_guard_bands_untouched(gpu, case):
     assert max_err(np64(lse), ref["lse"]) <= TOL[wl.dtype]
 
 
-@pytest.mark.parametrize("name", ["sam_global_relpos", "sam_decoder_q7"])
+@pytest.mark.parametrize("name", ["sam_global_relpos", "sam_decoder_q7", "gqa_decode"])
 def test_bitwise_determinism_full_size(gpu, name):
     """The headline kernel (12-wave workgroups, terms formed in the kernel) and
-    the split-KV route (partials merged in a fixed order) at full size: two
+    both split-KV routes (head_dim 16 and 128; partials merged in a fixed
+    order) at full size: two
     calls on the same inputs give the same bits, output and lse."""
     wl = workloads.WORKLOADS[name]
     x = workloads.generate(wl, seed=0)
@@ -132,7 +134,8 @@ def test_bitwise_determinism_full_size(gpu, name):
     k1 = gpu.last_kernel()
     b = run_gpu(gpu, wl, g, wl.layout, out_dtype=None, return_lse=True)
     torch.cuda.synchronize()
-    assert k1 == {"sam_global_relpos": "flash_split64w_kernel", "sam_decoder_q7": "d16_qpack_kernel"}[name]
+    assert k1 == {"sam_global_relpos": "flash_split64w_kernel", "sam_decoder_q7": "d16_qpack_kernel",
+                  "gqa_decode": "flash_tiled_kernel"}[name]
     assert torch.equal(a[0].view(torch.int16), b[0].view(torch.int16))
     assert torch.equal(a[1].view(torch.int32), b[1].view(torch.int32))
 

@@ -36,6 +36,8 @@ def _abi_noalloc(fa, q, k, v, o, lse, scale, mask=None):
     [(1, 8, 8, 7, 4096, 16), (1, 4, 2, 3, 1000, 16)],
     # no scratch needed (head_dim 64): the entry point runs the same kernels with no partials
     [(2, 4, 2, 100, 300, 64), (1, 2, 1, 40, 50, 64)],
+    # head_dim 128 / 64 decode shapes: split-KV on the double-buffered kernel, partials in the scratch
+    [(1, 32, 8, 1, 8192, 128), (1, 8, 8, 4, 2048, 64)],
 ])
 def test_noalloc_matches_sdpa_fwd(gpu, shapes):
     lib = gpu.load()
@@ -44,7 +46,7 @@ def test_noalloc_matches_sdpa_fwd(gpu, shapes):
         q, k, v = _inputs(B, Hq, Hkv, Tq, Tkv, D, seed=10 + i)
         scale = 1.0 / np.sqrt(D)
         ws_n = lib.sdpa_workspace_size(1, B, Hq, Hkv, Tq, Tkv, D, scale, 0, 0, 0)
-        if D == 16 and Tq <= 8:
+        if (D == 16 and Tq <= 8) or (Tq <= 4 and Tkv >= 2048):
             assert ws_n > 0                       # this call really uses the split-KV scratch
         ref, ref_lse = gpu.sdpa(q, k, v, scale=scale, out_dtype=torch.float32, return_lse=True)
         o = torch.full((B, Hq, Tq, D), float("nan"), device="cuda")
@@ -76,3 +78,32 @@ def test_noalloc_rejects_oversized_scratch(gpu):
     finally:
         gpu.set_tuning("num_splits", 0)
     assert st == -2 and b"scratch" in msg
+
+
+def test_noalloc_lowers_an_automatic_split_count(gpu):
+    """A head_dim-128 shape whose automatic split-KV partials (16 chunks, 33 MB)
+    exceed the fixed 8 MiB scratch: the entry point runs with fewer chunks
+    instead of failing, and the result stays within the parity bound of
+    sdpa_fwd's 16-chunk result and of the oracle (sampled rows)."""
+    lib = gpu.load()
+    B, Hq, Hkv, Tq, Tkv, D = 1, 16, 16, 256, 8192, 128
+    print(f"[noalloc] capped split: B{B} Hq{Hq} Tq{Tq} Tkv{Tkv} D{D}", flush=True)
+    assert lib.sdpa_workspace_size(1, B, Hq, Hkv, Tq, Tkv, D, float("nan"), 0, 0, 0) > (8 << 20)
+    q, k, v = _inputs(B, Hq, Hkv, Tq, Tkv, D, seed=30)
+    scale = 1.0 / np.sqrt(D)
+    ref, ref_lse = gpu.sdpa(q, k, v, scale=scale, out_dtype=torch.float32, return_lse=True)
+    for _ in range(2):
+        o = torch.full((B, Hq, Tq, D), float("nan"), device="cuda")
+        lse = torch.full((B, Hq, Tq), float("nan"), device="cuda")
+        _abi_noalloc(gpu, q, k, v, o, lse, scale)
+        torch.cuda.synchronize()
+        assert gpu.last_kernel() == "flash_tiled_kernel"
+        assert max_err(np64(o), np64(ref)) <= TOL["bf16"]
+        assert max_err(np64(lse), np64(ref_lse)) <= TOL["bf16"]
+    rows = [(h, i) for h in (0, 7, 15) for i in (0, 1, 100, 255)]
+    qs = torch.stack([q[0, h, i] for h, i in rows]).view(1, len(rows), 1, D)
+    ks = torch.stack([k[0, h] for h, _ in rows]).unsqueeze(0)
+    vs = torch.stack([v[0, h] for h, _ in rows]).unsqueeze(0)
+    want = oracle.sdpa(np64(qs), np64(ks), np64(vs), scale=scale)
+    got = torch.stack([o[0, h, i] for h, i in rows]).view(1, len(rows), 1, D)
+    assert max_err(np64(got), want["o"]) <= TOL["bf16"]

@@ -14,6 +14,8 @@ decoder, and the masked / grouped-query options of the Axon kernel):
   sam_global_relpos     bf16 bhsd B1 H12 T4096 (64x64 grid) D64, tables [127,64], scale 1/8
   gqa_causal            bf16 bshd B4 Hq32 Hkv8 S4096 D128, causal, scale 1/sqrt(128)
   gqa_sliding           same inputs, causal + sliding window 1024
+  gqa_decode            the same model's decode step: bshd B4 Hq32 Hkv8, one new query per
+                        sequence against a 4096-token K/V cache (causal, offset 4095), D128
 
 Generator: numpy PCG64 `default_rng(seed)`, `standard_normal(shape, float32)`
 drawn in the order Q, K, V, rel_pos_h, rel_pos_w in the logical [B, H, T, D]
@@ -85,6 +87,10 @@ WORKLOADS = {
         "gqa_sliding", "bf16", "bshd", 4, 32, 8, 4096, 4096, 128, 1.0 / math.sqrt(128),
         mask={"kind": "sliding", "window": 1024, "offset": 0},
         description="decoder-style GQA 4:1, causal + sliding window 1024"),
+    "gqa_decode": Workload(
+        "gqa_decode", "bf16", "bshd", 4, 32, 8, 1, 4096, 128, 1.0 / math.sqrt(128),
+        mask={"kind": "causal", "offset": 4095},
+        description="decode step of the decoder-style GQA 4:1 model: one query against a 4096-token cache"),
 }
 
 _TORCH_DTYPE = {"fp32": torch.float32, "bf16": torch.bfloat16, "fp16": torch.float16}
@@ -157,6 +163,7 @@ def replica(name, **overrides):
         "gqa_causal": dict(B=1, Hq=8, Hkv=2, Tq=333, Tkv=333),
         "gqa_sliding": dict(B=1, Hq=8, Hkv=2, Tq=333, Tkv=333,
                             mask={"kind": "sliding", "window": 100, "offset": 0}),
+        "gqa_decode": dict(B=2, Hq=8, Hkv=2, Tq=3, Tkv=1000, mask={"kind": "causal", "offset": 997}),
     }[name]
     small.update(overrides)
     return wl.with_(**small)
