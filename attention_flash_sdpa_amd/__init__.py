@@ -105,6 +105,14 @@ def load():
         lib.sdpa_relpos_bwd_workspace_size.argtypes = [_I64] * 5
         lib.sdpa_relpos_bwd.restype = _I32
         lib.sdpa_relpos_bwd.argtypes = [_P] * 11 + [_I32] * 4 + [_I64] * 5 + [_P, _P, _F, _P, ctypes.c_size_t, _P]
+        lib.sdpa_relpos_bwd_dropout.restype = _I32
+        lib.sdpa_relpos_bwd_dropout.argtypes = [_P] * 11 + [_I32] * 4 + [_I64] * 5 + \
+            [_P, _P, _F, _P, _F, _P, ctypes.c_size_t, _P]
+        lib.sdpa_relpos_fwd_dropout_workspace_size.restype = ctypes.c_size_t
+        lib.sdpa_relpos_fwd_dropout_workspace_size.argtypes = [_I64] * 4
+        lib.sdpa_relpos_fwd_dropout.restype = _I32
+        lib.sdpa_relpos_fwd_dropout.argtypes = [_P, _P, _P, _P, _I32, _I32, _I32] + [_I64] * 5 + \
+            [_P, _P, _F, _P, _F, _P, _P, ctypes.c_size_t, _P]
         lib.sdpa_attention_weights.restype = _I32
         lib.sdpa_attention_weights.argtypes = [_P, _P, _I32, _I32] + [_I64] * 6 + \
             [_F, ctypes.POINTER(_Mask), _P, _P, _F, _P, _P]
@@ -376,8 +384,9 @@ def sdpa_backward(q, k, v, o, dout, lse, *, layout="bhsd", scale=None, mask=None
 
 
 def sdpa_relpos_backward(q, k, v, o, dout, lse, rel_pos_h, rel_pos_w, grid, *, layout="bhsd", scale=None,
-                         grad_dtype=None, stream=None, workspace=None):
-    """(dq, dk, dv, d_rel_pos_h, d_rel_pos_w) of sdpa_relpos (tables' gradients in float32)."""
+                         grad_dtype=None, stream=None, workspace=None, dropout=None):
+    """(dq, dk, dv, d_rel_pos_h, d_rel_pos_w) of sdpa_relpos (tables' gradients in float32).
+    dropout: None or the {"keep", "rate"} given to the forward call."""
     lib = load()
     B, H, T, D = _relpos_dims(q, k, v, grid, layout)
     gh, gw = grid
@@ -401,6 +410,14 @@ def sdpa_relpos_backward(q, k, v, o, dout, lse, rel_pos_h, rel_pos_w, grid, *, l
     elif ws.dtype != torch.uint8 or ws.device != q.device or not ws.is_contiguous():
         raise ValueError("workspace must be a contiguous uint8 tensor on q's device")
     sc = float("nan") if scale is None else float(scale)
+    if dropout is not None:
+        kp, rate = _dropout_args(dropout, B, H, T, T)
+        st = lib.sdpa_relpos_bwd_dropout(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq),
+                                         _ptr(dk), _ptr(dv), _ptr(drh), _ptr(drw), _DTYPE[q.dtype], _DTYPE[o.dtype],
+                                         _DTYPE[gdt], _layout_of(layout), B, H, gh, gw, D, _ptr(rel_pos_h),
+                                         _ptr(rel_pos_w), sc, kp, rate, _ptr(ws), ws.numel(), _stream(stream))
+        _check(st, "sdpa_relpos_bwd_dropout")
+        return dq, dk, dv, drh, drw
     st = lib.sdpa_relpos_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
                              _ptr(drh), _ptr(drw), _DTYPE[q.dtype], _DTYPE[o.dtype], _DTYPE[gdt], _layout_of(layout),
                              B, H, gh, gw, D, _ptr(rel_pos_h), _ptr(rel_pos_w), sc, _ptr(ws), ws.numel(),
@@ -459,8 +476,9 @@ def relpos_terms(q, rel_pos_h, rel_pos_w, grid, *, layout="bhsd", stream=None):
 
 
 def sdpa_relpos(q, k, v, rel_pos_h, rel_pos_w, grid, *, layout="bhsd", scale=None, out_dtype=None,
-                return_lse=False, stream=None, out=None, workspace=None):
-    """Fused attention with the decomposed rel-pos bias (self-attention on a grid)."""
+                return_lse=False, stream=None, out=None, workspace=None, dropout=None):
+    """Fused attention with the decomposed rel-pos bias (self-attention on a grid).
+    dropout: None | {"keep": keep bits from dropout_mask(.., B, H, T, T), "rate": r}."""
     lib = load()
     B, H, T, D = _relpos_dims(q, k, v, grid, layout)
     gh, gw = grid
@@ -474,7 +492,10 @@ def sdpa_relpos(q, k, v, rel_pos_h, rel_pos_w, grid, *, layout="bhsd", scale=Non
     o = out if out is not None else torch.empty(q.shape, dtype=odt, device=q.device)
     lse = torch.empty((B, H, T), dtype=torch.float32, device=q.device) if return_lse else None
     sc = float("nan") if scale is None else float(scale)
-    ws_n = lib.sdpa_workspace_size(_DTYPE[q.dtype], B, H, H, T, T, D, sc, 1, gh, gw)
+    if dropout is not None:
+        ws_n = lib.sdpa_relpos_fwd_dropout_workspace_size(B, H, gh, gw)
+    else:
+        ws_n = lib.sdpa_workspace_size(_DTYPE[q.dtype], B, H, H, T, T, D, sc, 1, gh, gw)
     if ws_n == ctypes.c_size_t(-1).value:
         raise ValueError("grid does not match the sequence length")
     ws = workspace
@@ -484,6 +505,13 @@ def sdpa_relpos(q, k, v, rel_pos_h, rel_pos_w, grid, *, layout="bhsd", scale=Non
         ws = torch.empty(ws_n, dtype=torch.uint8, device=q.device)
     elif ws.dtype != torch.uint8 or ws.device != q.device or not ws.is_contiguous():
         raise ValueError("workspace must be a contiguous uint8 tensor on q's device")
+    if dropout is not None:
+        kp, rate = _dropout_args(dropout, B, H, T, T)
+        st = lib.sdpa_relpos_fwd_dropout(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _DTYPE[q.dtype], _DTYPE[odt],
+                                         _layout_of(layout), B, H, gh, gw, D, _ptr(rel_pos_h), _ptr(rel_pos_w), sc,
+                                         kp, rate, _ptr(lse), _ptr(ws), ws.numel(), _stream(stream))
+        _check(st, "sdpa_relpos_fwd_dropout")
+        return (o, lse) if return_lse else o
     st = lib.sdpa_relpos_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _DTYPE[q.dtype], _DTYPE[odt],
                              _layout_of(layout), B, H, gh, gw, D, _ptr(rel_pos_h), _ptr(rel_pos_w), sc,
                              _ptr(lse), _ptr(ws), ws.numel() if ws is not None else 0, _stream(stream))

@@ -257,7 +257,16 @@ bool relpos_fused_ok(const sdpa::FwdParams& p, const Tuning& tu) {
   sdpa::FwdParams q = p;
   q.term_h = nullptr;
   q.term_w = nullptr;
-  return route_of(q, tu) != R_GENERIC || sdpa::generic_relpos_supported(q, true);
+  if (route_of(q, tu) != R_GENERIC) return true;            // a matrix-core kernel forms the terms
+  // Only the vector-ALU kernel could form them: where a matrix-core kernel
+  // takes the call with precomputed terms (head_dim 128, grids other than the
+  // fused kernels'), the terms kernel runs first instead.
+  alignas(16) static float probe[4] = {};
+  sdpa::FwdParams t = q;
+  t.term_h = probe;
+  t.term_w = probe;
+  if (route_of(t, tu) != R_GENERIC) return false;
+  return sdpa::generic_relpos_supported(q, true);
 }
 
 // Rel-pos limits of every route (the generic kernel's term staging, the terms kernel).
@@ -443,6 +452,50 @@ int sdpa_relpos_fwd(const void* q, const void* k, const void* v, void* o, int dt
   return launch(p, tu, (hipStream_t)stream);
 }
 
+size_t sdpa_relpos_fwd_dropout_workspace_size(int64_t B, int64_t H, int64_t grid_h, int64_t grid_w) {
+  if (grid_h <= 0 || grid_w <= 0 || grid_h > 1024 || grid_w > 1024) return (size_t)-1;
+  if (!elements_ok({B, H, grid_h * grid_w, grid_h + grid_w})) return (size_t)-1;
+  return terms_bytes(B, H, grid_h * grid_w, grid_h, grid_w);
+}
+
+int sdpa_relpos_fwd_dropout(const void* q, const void* k, const void* v, void* o, int dtype, int out_dtype, int layout,
+                            int64_t B, int64_t H, int64_t grid_h, int64_t grid_w, int64_t D, const void* rel_pos_h,
+                            const void* rel_pos_w, float scale, const uint32_t* keep, float rate, float* lse,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  if (!q || !k || !v || !o || !rel_pos_h || !rel_pos_w || !keep)
+    return fail(SDPA_ERR_INVALID, "q, k, v, o, both tables and keep must be non-null");
+  if (grid_h <= 0 || grid_w <= 0) return fail(SDPA_ERR_INVALID, "grid sizes must be positive");
+  int st = check_relpos_grid(grid_h, grid_w, D);
+  if (st) return st;
+  const int64_t T = grid_h * grid_w;
+  st = check_sizes(B, H, H, T, T, D);
+  if (st) return st;
+  st = check_dtypes(dtype, out_dtype, layout, D);
+  if (st) return st;
+  uint32_t thresh;
+  float kscale;
+  st = dropout_plan(rate, &thresh, &kscale);
+  if (st) return st;
+  sdpa::FwdParams p = relpos_params(q, k, v, o, dtype, out_dtype, layout, B, H, grid_h, grid_w, D, rel_pos_h,
+                                    rel_pos_w, scale, lse);
+  // The terms always go through the workspace: the kernels that take dropout
+  // with the rel-pos bias read them from there.
+  const size_t need = terms_bytes(B, H, T, grid_h, grid_w);
+  if (!workspace || workspace_bytes < need)
+    return fail(SDPA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : (size_t)0);
+  float* th = (float*)workspace;
+  float* tw = (float*)((char*)workspace + align256((size_t)B * H * T * grid_h * 4));
+  st = relpos_terms(q, dtype, layout, B, H, grid_h, grid_w, D, rel_pos_h, rel_pos_w, th, tw, stream);
+  if (st) return st;
+  p.term_h = th;
+  p.term_w = tw;
+  p.keep = keep;
+  p.keep_words = (T + 31) / 32;
+  p.keep_scale = kscale;
+  return launch(p, tuning_now(), (hipStream_t)stream);
+}
+
 int sdpa_relpos_fused(int dtype, int64_t D, int64_t grid_h, int64_t grid_w) {
   if (grid_h <= 0 || grid_w <= 0 || D <= 0 || !dtype_ok(dtype) || grid_h > 1024 || grid_w > 1024 || D > 128) return 0;
   static const char dummy = 0;
@@ -573,11 +626,16 @@ size_t sdpa_relpos_bwd_workspace_size(int64_t B, int64_t H, int64_t grid_h, int6
   return relpos_bwd_bytes(B, H, grid_h, grid_w, D, nullptr);
 }
 
-int sdpa_relpos_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+}  // extern "C"
+
+namespace {
+
+// The rel-pos backward with optional dropout keep bits (keep NULL: none).
+int relpos_bwd_impl(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
                     void* dq, void* dk, void* dv, float* d_rel_pos_h, float* d_rel_pos_w, int dtype, int o_dtype,
                     int grad_dtype, int layout, int64_t B, int64_t H, int64_t grid_h, int64_t grid_w, int64_t D,
-                    const void* rel_pos_h, const void* rel_pos_w, float scale, void* workspace,
-                    size_t workspace_bytes, void* stream) {
+                    const void* rel_pos_h, const void* rel_pos_w, float scale, const uint32_t* keep, float rate,
+                    void* workspace, size_t workspace_bytes, void* stream) {
   g_last_error.clear();
   if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !d_rel_pos_h || !d_rel_pos_w || !rel_pos_h ||
       !rel_pos_w)
@@ -607,6 +665,13 @@ int sdpa_relpos_bwd(const void* q, const void* k, const void* v, const void* o, 
   p.rel_w = rel_pos_w;
   p.drel_h = d_rel_pos_h;
   p.drel_w = d_rel_pos_w;
+  if (keep) {
+    uint32_t thresh;
+    st = dropout_plan(rate, &thresh, &p.keep_scale);
+    if (st) return st;
+    p.keep = keep;
+    p.keep_words = (T + 31) / 32;
+  }
   if (!sdpa::bwd_supports(p))
     return fail(SDPA_ERR_UNSUPPORTED, "the rel-pos backward is built for bf16 / fp16 inputs, head_dim 32, 64 or 128, "
                                       "grid_w >= 4 and grid_h + grid_w <= 128");
@@ -637,6 +702,35 @@ int sdpa_relpos_bwd(const void* q, const void* k, const void* v, const void* o, 
   if (e != hipSuccess) return fail(SDPA_ERR_HIP, "rel-pos backward launch failed: %s", hipGetErrorString(e));
   g_last_kernel = "bwd_dkdv_kernel";
   return SDPA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sdpa_relpos_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                    void* dq, void* dk, void* dv, float* d_rel_pos_h, float* d_rel_pos_w, int dtype, int o_dtype,
+                    int grad_dtype, int layout, int64_t B, int64_t H, int64_t grid_h, int64_t grid_w, int64_t D,
+                    const void* rel_pos_h, const void* rel_pos_w, float scale, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  return relpos_bwd_impl(q, k, v, o, dout, lse, dq, dk, dv, d_rel_pos_h, d_rel_pos_w, dtype, o_dtype, grad_dtype,
+                         layout, B, H, grid_h, grid_w, D, rel_pos_h, rel_pos_w, scale, nullptr, 0.0f, workspace,
+                         workspace_bytes, stream);
+}
+
+int sdpa_relpos_bwd_dropout(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                            const float* lse, void* dq, void* dk, void* dv, float* d_rel_pos_h, float* d_rel_pos_w,
+                            int dtype, int o_dtype, int grad_dtype, int layout, int64_t B, int64_t H, int64_t grid_h,
+                            int64_t grid_w, int64_t D, const void* rel_pos_h, const void* rel_pos_w, float scale,
+                            const uint32_t* keep, float rate, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  if (!keep) {
+    g_last_error.clear();
+    return fail(SDPA_ERR_INVALID, "keep must be non-null");
+  }
+  return relpos_bwd_impl(q, k, v, o, dout, lse, dq, dk, dv, d_rel_pos_h, d_rel_pos_w, dtype, o_dtype, grad_dtype,
+                         layout, B, H, grid_h, grid_w, D, rel_pos_h, rel_pos_w, scale, keep, rate, workspace,
+                         workspace_bytes, stream);
 }
 
 int sdpa_attention_weights(const void* q, const void* k, int dtype, int layout, int64_t B, int64_t Hq, int64_t Hkv,

@@ -965,10 +965,15 @@ void launch_modes(const BwdParams& p, hipStream_t s) {
     case B_NONE: drop ? launch_main<E, D, B_NONE, true, G>(p, s) : launch_main<E, D, B_NONE, false, G>(p, s); break;
     case B_INDEX: drop ? launch_main<E, D, B_INDEX, true, G>(p, s) : launch_main<E, D, B_INDEX, false, G>(p, s); break;
     case B_RELPOS:
-      if (p.grid_h <= 32 && p.grid_w <= 32) launch_main<E, D, B_RELPOS, false, G, true>(p, s);
-      else launch_main<E, D, B_RELPOS, false, G>(p, s);
+      if (p.grid_h <= 32 && p.grid_w <= 32) {
+        drop ? launch_main<E, D, B_RELPOS, true, G, true>(p, s) : launch_main<E, D, B_RELPOS, false, G, true>(p, s);
+      } else {
+        drop ? launch_main<E, D, B_RELPOS, true, G>(p, s) : launch_main<E, D, B_RELPOS, false, G>(p, s);
+      }
       break;
-    case B_RELPOS64: launch_main<E, D, B_RELPOS64, false, G>(p, s); break;
+    case B_RELPOS64:
+      drop ? launch_main<E, D, B_RELPOS64, true, G>(p, s) : launch_main<E, D, B_RELPOS64, false, G>(p, s);
+      break;
     default: drop ? launch_main<E, D, B_TENSOR, true, G>(p, s) : launch_main<E, D, B_TENSOR, false, G>(p, s); break;
   }
 }
@@ -996,7 +1001,7 @@ bool bwd_supports(const BwdParams& p) {
   if (p.dtype != 1 && p.dtype != 2) return false;
   if (p.D != 32 && p.D != 64 && p.D != 128) return false;
   if (bmode_of(p) < 0) return false;
-  if (p.bias == BIAS_RELPOS && (p.keep || p.grid_w < 4 || p.grid_h < 1 || p.grid_h + p.grid_w > kMaxGT ||
+  if (p.bias == BIAS_RELPOS && (p.grid_w < 4 || p.grid_h < 1 || p.grid_h + p.grid_w > kMaxGT ||
                                 p.B * p.Hq > 65535))
     return false;
   if (p.B * p.Hq * p.Tq * (p.D / 8) / 256 + 1 > INT32_MAX) return false;

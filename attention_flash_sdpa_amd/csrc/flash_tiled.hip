@@ -28,7 +28,17 @@
 // wave copies its 32 x 32 block of the mask next to the K/V tile, XOR-swizzled
 // by 16-byte chunks, and reads its 16 values per tile with 4 vector LDS reads.
 //
-// Attention dropout (no mask or causal / sliding masks): the weights that
+// Decomposed rel-pos bias ([mlx-examples issue 1451] "segment_anything: fuse
+// attention with mx.fast.scaled_dot_product_attention", body:
+// add_decomposed_rel_pos): B[i, j] = term_h[i, j / grid_w] + term_w[i, j % grid_w]
+// from the fp32 term arrays that relpos_terms wrote.  Per tile each lane reads
+// its query's term_w values for its 16 keys (4 groups of 4 consecutive keys:
+// with grid_w a multiple of 4 a group never crosses a grid row, so one 16-byte
+// load each) and one term_h value per group, issued before the tile's Q.K^T
+// products so their latency overlaps them.  Any grid_w that is a multiple of 4
+// (SAM's 64 x 64 global grid at head_dim 128, other image sizes' grids).
+//
+// Attention dropout (no mask, causal / sliding masks or rel-pos): the weights that
 // multiply V are scaled by keep / (1 - rate) while lse and the row sum stay
 // those of the undropped scores ([Axon PR 650] "Axon.Layers.scaled_dot_product_attention/4",
 // description: `:dropout_rate` in :train mode).  Each lane reads its row's
@@ -59,9 +69,15 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kTau = 8.0f;
 constexpr float kTauSum = 256.0f;
 constexpr int BN = 32;
+#ifndef TILED_RELPOS128_OCC2
+#define TILED_RELPOS128_OCC2 1
+#endif
 
 
-enum Mode { T_NONE = 0, T_INDEX = 1, T_ADD_F32 = 2, T_ADD_BF16 = 3, T_BOOL = 4 };
+enum Mode { T_NONE = 0, T_INDEX = 1, T_ADD_F32 = 2, T_ADD_BF16 = 3, T_BOOL = 4, T_RELPOS = 5 };
+
+// Modes whose mask is a caller's tensor, staged in LDS beside the K/V tiles.
+constexpr bool is_tensor_mode(int mode) { return mode == T_ADD_F32 || mode == T_ADD_BF16 || mode == T_BOOL; }
 
 // Mask block geometry per mode: element size, bytes per 32-key row, 16-byte
 // chunks per row, copy instructions per wave, rows per 256-byte bank sweep.
@@ -107,12 +123,17 @@ __device__ __forceinline__ float pair_sum(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Three workgroups per CU; the head_dim-128 rel-pos instances keep the next
+// tile's terms in registers as well and run two (256 registers per lane).
+template <int D, int MODE>
+constexpr int tiled_min_blocks() { return (MODE == T_RELPOS && D == 128 && TILED_RELPOS128_OCC2) ? 2 : 3; }
+
 template <typename E, int D, int MODE, bool OUT16, bool DROP>
-__global__ __launch_bounds__(256, 3) void flash_tiled_kernel(FwdParams p, int hpw, int64_t mask_bytes, int kps) {
+__global__ __launch_bounds__(256, (tiled_min_blocks<D, MODE>())) void flash_tiled_kernel(FwdParams p, int hpw, int64_t mask_bytes, int kps) {
   typedef typename Vec16<E>::x8 e8;
   typedef typename Vec16<E>::x4 e4;
   typedef typename Vec16<E>::x2 e2;
-  constexpr bool TENSOR = MODE >= T_ADD_F32;
+  constexpr bool TENSOR = is_tensor_mode(MODE);
   using M = MCfg<MODE>;
   using C = TCfg<D>;
   // Double-buffered tiles, each buffer a distinct LDS object (no false
@@ -158,6 +179,24 @@ __global__ __launch_bounds__(256, 3) void flash_tiled_kernel(FwdParams p, int hp
 #pragma unroll
   for (int c = 0; c < C::QC; ++c) qf[c] = qvalid ? *(const e8*)(qp + qrow * p.q_st + c * 16 + 8 * g) : (e8){};
   const float c2 = p.scale * kLog2e;
+
+  // Rel-pos: descriptors over this (batch, head)'s term rows (reads past the
+  // last row return 0; keys past the grid are masked anyway), the lane's row
+  // offsets, and 1 / grid_w for the row / column split of a key.
+  constexpr bool RELPOS = MODE == T_RELPOS;
+  const int64_t tbh = (b * p.Hq + h) * p.Tq;
+  const __amdgpu_buffer_rsrc_t ths = __builtin_amdgcn_make_buffer_rsrc(
+      RELPOS ? (void*)(p.term_h + tbh * p.grid_h) : nullptr, 0, RELPOS ? (int)(p.Tq * p.grid_h * 4) : 0, 0x00020000);
+  const __amdgpu_buffer_rsrc_t tws = __builtin_amdgcn_make_buffer_rsrc(
+      RELPOS ? (void*)(p.term_w + tbh * p.grid_w) : nullptr, 0, RELPOS ? (int)(p.Tq * p.grid_w * 4) : 0, 0x00020000);
+  int thv = 0, twv = 0;
+  float rcp_gw = 0.0f;
+  if (RELPOS) {
+    const int qs = qvalid ? (int)qrow : 0;
+    thv = qs * p.grid_h * 4;
+    twv = qs * p.grid_w * 4;
+    rcp_gw = 1.0f / (float)p.grid_w;
+  }
 
   // Key tiles of the workgroup.
   int64_t lo = 0, hi = p.Tkv;
@@ -254,6 +293,25 @@ __global__ __launch_bounds__(256, 3) void flash_tiled_kernel(FwdParams p, int hp
       DROP ? (int)(p.Tq * p.keep_words * 4) : 0, 0x00020000);
   const int keep_vo = DROP ? (int)((qvalid ? qrow : 0) * p.keep_words * 4) : 0;
 
+  // Rel-pos terms of a tile's keys for this lane: keys t * 32 + 8 i4 + 4g + e
+  // lie in grid row r, columns c .. c + 3 (one 16-byte load of term_w and one
+  // term_h value per group), kept in registers until the tile is computed.
+  f32x4 twn[4];
+  float thn[4];
+  auto load_terms = [&](int t) {
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      const int key = t * BN + 8 * i4 + 4 * g;
+      // key / grid_w: key <= 2^20 and grid_w <= 1024, so the float quotient's
+      // error stays far below the 0.5 / grid_w margin the half key adds
+      const int r = (int)(((float)key + 0.5f) * rcp_gw);
+      const int c = key - r * p.grid_w;
+      twn[i4] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(tws, twv + 4 * c, 0, 0));
+      thn[i4] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ths, thv + 4 * r, 0, 0));
+    }
+  };
+  if (RELPOS && tlo < thi) load_terms(tlo);
+
   auto step = [&](int t, auto par) {
     constexpr int PAR = decltype(par)::value;
     const int64_t k0 = (int64_t)t * BN;
@@ -265,7 +323,20 @@ __global__ __launch_bounds__(256, 3) void flash_tiled_kernel(FwdParams p, int hp
     const lds_char* vs = PAR ? vb : va;
     // this tile's keep bits (tiles start at multiples of 32 keys)
     const uint32_t kw = DROP ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(krs_keep, keep_vo, 4 * t, 0) : 0u;
-    f32x16 s = (f32x16){};
+    // Rel-pos: the bias of this lane's keys (loaded during the previous tile),
+    // divided by scale, initialises the accumulator that the Q.K^T products
+    // add to; then the next tile's terms are requested.
+    f32x16 s;
+    if (RELPOS) {
+      const float inv_scale = 1.0f / p.scale;
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s[4 * i4 + e] = (thn[i4] + twn[i4][e]) * inv_scale;
+      if (t + 1 < thi) load_terms(t + 1);
+    } else {
+      s = (f32x16){};
+    }
 #pragma unroll
     for (int c = 0; c < C::QC; ++c) s = mfma32(lds_b128<e8>(ks + kro[c]), qf[c], s);
     if (TENSOR) {
@@ -416,41 +487,43 @@ __global__ __launch_bounds__(256, 3) void flash_tiled_kernel(FwdParams p, int hp
 
 // Merge of the key chunks: O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s,
 // M = max_s m_s.  One workgroup per output row: thread t takes head dim t % D
-// and the chunks s = t / D, t / D + 256 / D, ... in order (loads eight chunks
-// at a time), and the 256 / D partial sums of a dim then add in a fixed order,
-// so the result does not depend on timing.
+// and the chunks s = t / D, t / D + 256 / D, ... (at most 64 chunks: every
+// load of the thread, its partials and one chunk's (m, l), is issued before
+// the first wait, so the merge costs one memory round trip); the 256 / D
+// partial sums of a dim then add in a fixed order, so the result does not
+// depend on timing.
 template <typename E, int D, bool OUT16>
 __global__ __launch_bounds__(256) void tiled_combine_kernel(FwdParams p) {
   constexpr int G = 256 / D;                   // chunk groups
-  constexpr int NB = 8;
+  constexpr int NB = 64 / G;                   // chunks per thread
   __shared__ float msh[64], lsh[64];
   __shared__ float part[G][D];
   const int tid = threadIdx.x, d = tid % D, sg = tid / D;
   const int S = p.num_splits;
   const int64_t rows = p.B * p.Hq * p.Tq;
   const int64_t r = blockIdx.x;
-  float M = -INFINITY, L = 0.0f;
-  // (m, l) of every chunk: S <= 64, one thread each
-  if (tid < S) {
-    const f32x2 ml = *(const f32x2*)(p.part_ml + ((int64_t)tid * rows + r) * 2);
+  f32x2 ml = {-INFINITY, 0.0f};
+  if (tid < S) ml = *(const f32x2*)(p.part_ml + ((int64_t)tid * rows + r) * 2);
+  float v[NB];
+#pragma unroll
+  for (int u = 0; u < NB; ++u) {
+    const int s = sg + G * u;
+    v[u] = s < S ? p.part_o[((int64_t)s * rows + r) * D + d] : 0.0f;
+  }
+  if (tid < 64) {
     msh[tid] = ml[0];
     lsh[tid] = ml[1];
   }
   __syncthreads();
+  float M = -INFINITY, L = 0.0f;
   for (int s = 0; s < S; ++s) M = fmaxf(M, msh[s]);
   for (int s = 0; s < S; ++s)
     if (msh[s] != -INFINITY) L = fmaf(fexp2(msh[s] - M), lsh[s], L);
   float acc = 0.0f;
-  for (int s0 = sg; s0 < S; s0 += G * NB) {
-    float v[NB], w[NB];
 #pragma unroll
-    for (int u = 0; u < NB; ++u) {
-      const int s = s0 + G * u;
-      v[u] = s < S ? p.part_o[((int64_t)s * rows + r) * D + d] : 0.0f;
-      w[u] = (s < S && msh[s < S ? s : 0] != -INFINITY) ? fexp2(msh[s] - M) : 0.0f;
-    }
-#pragma unroll
-    for (int u = 0; u < NB; ++u) acc = fmaf(w[u], v[u], acc);
+  for (int u = 0; u < NB; ++u) {
+    const int s = sg + G * u;
+    if (s < S && msh[s] != -INFINITY) acc = fmaf(fexp2(msh[s] - M), v[u], acc);
   }
   part[sg][d] = acc;
   __syncthreads();
@@ -483,11 +556,11 @@ hipError_t launch_t(const FwdParams& p, hipStream_t s) {
   // chunk itself (16-byte aligned, like the base) lies within the allocation's
   // last page.  Bytes past the last element land on keys >= Tkv, masked anyway.
   int64_t mask_bytes = 0;
-  if (MODE >= T_ADD_F32)
+  if (is_tensor_mode(MODE))
     mask_bytes = ((p.B - 1) * p.ms[0] + (p.Hq - 1) * p.ms[1] + (p.Tq - 1) * p.ms[2] + (p.Tkv - 1) * p.ms[3] + 1) *
                  mask_es(p);
   mask_bytes = (mask_bytes + 15) & ~(int64_t)15;
-  constexpr bool CAN_DROP = MODE == T_NONE || MODE == T_INDEX;
+  constexpr bool CAN_DROP = MODE == T_NONE || MODE == T_INDEX || MODE == T_RELPOS;
   if (CAN_DROP && p.keep) {
     if (p.out_dtype != 0) hipLaunchKernelGGL((flash_tiled_kernel<E, D, MODE, true, CAN_DROP>), grid, dim3(256), 0, s, p, hpw, mask_bytes, kps);
     else hipLaunchKernelGGL((flash_tiled_kernel<E, D, MODE, false, CAN_DROP>), grid, dim3(256), 0, s, p, hpw, mask_bytes, kps);
@@ -511,6 +584,7 @@ hipError_t launch_d(const FwdParams& p, hipStream_t s) {
     case BIAS_SLIDING: return launch_t<E, D, T_INDEX>(p, s);
     case BIAS_ADDITIVE: return p.mdtype == 0 ? launch_t<E, D, T_ADD_F32>(p, s) : launch_t<E, D, T_ADD_BF16>(p, s);
     case BIAS_BOOL: return launch_t<E, D, T_BOOL>(p, s);
+    case BIAS_RELPOS: return launch_t<E, D, T_RELPOS>(p, s);
     default: return launch_t<E, D, T_NONE>(p, s);
   }
 }
@@ -524,10 +598,20 @@ bool tiled_supports(const FwdParams& p) {
       (p.keep || p.num_splits > 64 || !(p.bias == BIAS_NONE || p.bias == BIAS_CAUSAL || p.bias == BIAS_SLIDING) ||
        p.B * p.Hq * p.Tq > 0x7fffffffLL || p.B * p.num_splits > 65535))
     return false;
-  // attention dropout is built for no mask and causal / sliding masks
-  if (p.keep && p.bias != BIAS_NONE && p.bias != BIAS_CAUSAL && p.bias != BIAS_SLIDING) return false;
+  // attention dropout is built for no mask, causal / sliding masks and rel-pos
+  if (p.keep && p.bias != BIAS_NONE && p.bias != BIAS_CAUSAL && p.bias != BIAS_SLIDING && p.bias != BIAS_RELPOS)
+    return false;
   if (p.keep && p.Tq * p.keep_words * 4 > 0x7fffffffLL) return false;   // keep rows of a head: 32-bit offsets
-  if (p.bias == BIAS_ADDITIVE || p.bias == BIAS_BOOL) {
+  if (p.bias == BIAS_RELPOS) {
+    // precomputed fp32 term arrays of one grid over one (batch, head); 16-byte
+    // groups of term_w need grid_w % 4 == 0 and an aligned array; each
+    // (batch, head)'s rows are addressed with 32-bit byte offsets
+    if (!p.term_h || !p.term_w || p.grid_h < 1 || p.grid_w < 4 || p.grid_w % 4 != 0) return false;
+    if (p.grid_h > 1024 || p.grid_w > 1024) return false;          // the row split below stays exact
+    if (p.Hq != p.Hkv || p.Tq != p.Tkv || p.Tq != (int64_t)p.grid_h * p.grid_w) return false;
+    if (((uintptr_t)p.term_w & 15) != 0 || ((uintptr_t)p.term_h & 3) != 0) return false;
+    if (p.Tq * (int64_t)(p.grid_h > p.grid_w ? p.grid_h : p.grid_w) * 4 > 0x7fffffffLL) return false;
+  } else if (p.bias == BIAS_ADDITIVE || p.bias == BIAS_BOOL) {
     // mask blocks are copied by 16-byte chunks along contiguous keys; row
     // offsets of one block and every element offset stay within 32 / 64 bits
     if (p.ms[3] != 1 || !p.mdata) return false;

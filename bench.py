@@ -479,6 +479,10 @@ def main():
                          "lse, formed before timing); 'dropout' times drawing the keep bits plus the forward "
                          "pass with attention dropout (rate 0.1); 'weights' times the attention-weights output "
                          "(unmasked or index-masked workloads)")
+    ap.add_argument("--head-dim", type=int, default=0, metavar="D",
+                    help="override the workload's head_dim (16-bit MFMA routes take 16 / 32 / 64 / 128)")
+    ap.add_argument("--grid", default=None, metavar="GHxGW",
+                    help="rel-pos workloads: another token grid (T = GH * GW), e.g. 32x32")
     ap.add_argument("--batch", type=int, default=0, metavar="B",
                     help="override the workload's batch size (windowed workloads then draw plain random windows "
                          "instead of cutting them from one padded image); for scaling studies, not the headline")
@@ -512,6 +516,14 @@ def main():
             print("bench.py: --batch must be positive", file=sys.stderr)
             sys.exit(2)
         wl = wl.with_(B=args.batch, window_image=None)
+    if args.head_dim:
+        wl = wl.with_(D=args.head_dim)
+    if args.grid:
+        if not wl.relpos:
+            print("bench.py: --grid needs a rel-pos workload", file=sys.stderr)
+            sys.exit(2)
+        gh, gw = (int(t) for t in args.grid.lower().split("x"))
+        wl = wl.with_(grid=(gh, gw), Tq=gh * gw, Tkv=gh * gw, window_image=None)
     x = workloads.generate(wl, seed=0)
     g = {k: t.cuda() for k, t in x.items()}
     if args.pass_ == "backward":
@@ -554,6 +566,10 @@ def main():
         rec_name += "_" + args.dtype
     if args.batch:
         rec_name += f"_b{args.batch}"
+    if args.head_dim:
+        rec_name += f"_d{args.head_dim}"
+    if args.grid:
+        rec_name += f"_g{args.grid.lower()}"
     traffic, traffic_src = recorded_traffic(kernel, rec_name)
     flash_ms = call_ms - terms_ms
     flash_flops = attn + (2 * allowed_pairs(wl) * wl.B * wl.Hq if wl.relpos else 0)

@@ -290,6 +290,30 @@ int sdpa_fwd_dropout(const void* q, const void* k, const void* v, void* o, int d
                      const sdpa_mask* mask, const uint32_t* keep, float rate, float* lse, void* workspace,
                      size_t workspace_bytes, void* stream);
 
+/*
+ * Bytes of device workspace sdpa_relpos_fwd_dropout needs: both fp32 term
+ * arrays, [B, H, T, grid_h] and [B, H, T, grid_w], each 256-byte aligned
+ * ((size_t)-1 for invalid sizes).  Pure host arithmetic.
+ */
+size_t sdpa_relpos_fwd_dropout_workspace_size(int64_t B, int64_t H, int64_t grid_h, int64_t grid_w);
+
+/*
+ * sdpa_relpos_fwd with attention dropout ([Axon PR 650], description:
+ * `:dropout_rate` in :train mode, applied to the weights; [mlx-examples issue
+ * 1451], body: SAM's rel-pos bias): O = (W * Z) . V with W the softmax of
+ * scale * q.k + term_h[i,row(j)] + term_w[i,col(j)] and Z as in
+ * sdpa_fwd_dropout.  keep holds B * H * T * ceil(T / 32) words from
+ * sdpa_dropout_mask(seed, step, rate, B, H, T, T, ...); lse is that of the
+ * undropped scores.  relpos_terms always runs first into the workspace
+ * (sdpa_relpos_fwd_dropout_workspace_size bytes); the attention then runs on
+ * the double-buffered matrix-core kernel (bf16 / fp16, head_dim 64 / 128,
+ * grid_w a multiple of 4, positive scale), else on the generic kernel.
+ */
+int sdpa_relpos_fwd_dropout(const void* q, const void* k, const void* v, void* o, int dtype, int out_dtype,
+                            int layout, int64_t B, int64_t H, int64_t grid_h, int64_t grid_w, int64_t D,
+                            const void* rel_pos_h, const void* rel_pos_w, float scale, const uint32_t* keep,
+                            float rate, float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Bytes of device workspace sdpa_bwd needs ((size_t)-1 for invalid sizes). */
 size_t sdpa_bwd_workspace_size(int64_t B, int64_t Hq, int64_t Tq);
 
@@ -335,14 +359,28 @@ size_t sdpa_relpos_bwd_workspace_size(int64_t B, int64_t H, int64_t grid_h, int6
  *   d_rel_pos_h            [2 grid_h - 1, D] fp32 output; d_rel_pos_w [2 grid_w - 1, D].
  *   workspace              at least sdpa_relpos_bwd_workspace_size(B, H, grid_h, grid_w, D) bytes.
  * Built for bf16 / fp16, head_dim 32, 64 or 128, grid_w >= 4 and grid_h + grid_w
- * <= 128 (SAM's 14 x 14 windows and 64 x 64 global grid), no dropout.
- * Deterministic: no atomics.
+ * <= 128 (SAM's 14 x 14 windows and 64 x 64 global grid).  With dropout see
+ * sdpa_relpos_bwd_dropout.  Deterministic: no atomics.
  */
 int sdpa_relpos_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
                     void* dq, void* dk, void* dv, float* d_rel_pos_h, float* d_rel_pos_w, int dtype, int o_dtype,
                     int grad_dtype, int layout, int64_t B, int64_t H, int64_t grid_h, int64_t grid_w, int64_t D,
                     const void* rel_pos_h, const void* rel_pos_w, float scale, void* workspace,
                     size_t workspace_bytes, void* stream);
+
+/*
+ * sdpa_relpos_bwd for the forward pass of sdpa_relpos_fwd_dropout: the same
+ * gradients with the weights that multiply V scaled by Z (dW = (dout . v^T)
+ * * Z as in sdpa_bwd), so dS, the term gradients and the tables' gradients
+ * carry the dropout.  keep (required) and rate as given to the forward call;
+ * other arguments, limits and workspace as in sdpa_relpos_bwd.
+ */
+int sdpa_relpos_bwd_dropout(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                            const float* lse, void* dq, void* dk, void* dv, float* d_rel_pos_h, float* d_rel_pos_w,
+                            int dtype, int o_dtype, int grad_dtype, int layout, int64_t B, int64_t H, int64_t grid_h,
+                            int64_t grid_w, int64_t D, const void* rel_pos_h, const void* rel_pos_w, float scale,
+                            const uint32_t* keep, float rate, void* workspace, size_t workspace_bytes,
+                            void* stream);
 
 /*
  * The attention weights (`:return_attention_weights`): weights[b, h, i, j] =

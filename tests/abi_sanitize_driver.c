@@ -196,6 +196,24 @@ static void train_cases(void) {
       fprintf(stderr, "FAIL relpos bwd grid %lld: accepted without a workspace\n", (long long)x);
     }
   }
+  /* rel-pos with dropout: forward and backward */
+  expect(sdpa_relpos_fwd_dropout(FAKE, FAKE, FAKE, FAKE, 1, 1, 1, 1, 2, 8, 8, 64, FAKE, FAKE, NAN, NULL, 0.2f, NULL,
+                                 NULL, 0, NULL), SDPA_ERR_INVALID, "relpos dropout fwd keep null");
+  expect(sdpa_relpos_fwd_dropout(FAKE, FAKE, FAKE, FAKE, 1, 1, 1, 1, 2, 8, 8, 64, FAKE, FAKE, NAN, FAKEU, 1.0f, NULL,
+                                 NULL, 0, NULL), SDPA_ERR_INVALID, "relpos dropout fwd rate");
+  expect(sdpa_relpos_fwd_dropout(FAKE, FAKE, FAKE, FAKE, 1, 1, 1, 1, 2, 8, 8, 64, FAKE, FAKE, NAN, FAKEU, 0.2f, NULL,
+                                 NULL, 0, NULL), SDPA_ERR_WORKSPACE, "relpos dropout fwd without workspace");
+  expect(sdpa_relpos_fwd_dropout(FAKE, FAKE, FAKE, FAKE, 1, 1, 1, INT64_MAX, 2, 8, 8, 64, FAKE, FAKE, NAN, FAKEU,
+                                 0.2f, NULL, NULL, 0, NULL), SDPA_ERR_UNSUPPORTED, "relpos dropout fwd B max");
+  expect(sdpa_relpos_bwd_dropout(FAKE, FAKE, FAKE, FAKE, FAKE, FAKEF, FAKE, FAKE, FAKE, FAKEF, FAKEF, 1, 1, 1, 1, 1, 2,
+                                 8, 8, 64, FAKE, FAKE, NAN, NULL, 0.2f, NULL, 0, NULL), SDPA_ERR_INVALID,
+         "relpos dropout bwd keep null");
+  expect(sdpa_relpos_bwd_dropout(FAKE, FAKE, FAKE, FAKE, FAKE, FAKEF, FAKE, FAKE, FAKE, FAKEF, FAKEF, 1, 1, 1, 1, 1, 2,
+                                 8, 8, 64, FAKE, FAKE, NAN, FAKEU, -0.5f, NULL, 0, NULL), SDPA_ERR_INVALID,
+         "relpos dropout bwd rate");
+  expect(sdpa_relpos_bwd_dropout(FAKE, FAKE, FAKE, FAKE, FAKE, FAKEF, FAKE, FAKE, FAKE, FAKEF, FAKEF, 1, 1, 1, 1, 1, 2,
+                                 8, 8, 64, FAKE, FAKE, NAN, FAKEU, 0.2f, NULL, 0, NULL), SDPA_ERR_WORKSPACE,
+         "relpos dropout bwd without workspace");
   /* attention weights */
   expect(sdpa_attention_weights(FAKE, FAKE, 1, 1, 1, 2, 2, 8, 8, 64, NAN, NULL, NULL, NULL, 0.f, FAKEF, NULL),
          SDPA_ERR_INVALID, "weights null lse");
@@ -224,7 +242,9 @@ static void size_sweeps(void) {
         sink ^= sdpa_relpos_bwd_workspace_size(x, 12, 64, 64, 64);
         sink ^= sdpa_relpos_bwd_workspace_size(1, 1, x, y, 64);
         sink ^= sdpa_relpos_bwd_workspace_size(1, 1, 14, 14, x);
-        calls += 10;
+        sink ^= sdpa_relpos_fwd_dropout_workspace_size(x, y, 64, 64);
+        sink ^= sdpa_relpos_fwd_dropout_workspace_size(1, 2, x, y);
+        calls += 12;
       }
   /* the documented refusal and a few exact values */
   expect(sdpa_workspace_size(1, 0, 2, 2, 8, 8, 64, NAN, 0, 0, 0) == (size_t)-1, 1, "ws B=0 refused");

@@ -299,7 +299,11 @@ def test_relpos_kernel_variants(gpu, name, halves, fused, gh):
     try:
         o, lse = gpu.sdpa_relpos(x["q"], x["k"], x["v"], x["rel_pos_h"], x["rel_pos_w"], wl.grid, scale=wl.scale,
                                  out_dtype=torch.float32, return_lse=True)
-        assert gpu.last_kernel() == ["flash_mfma_kernel", "flash_split64_kernel", "flash_split64w_kernel"][halves]
+        # with the in-workgroup split off, precomputed terms go to the double-buffered
+        # kernel, terms formed in the kernel to the general MFMA kernel
+        want = ["flash_mfma_kernel" if fused else "flash_tiled_kernel", "flash_split64_kernel",
+                "flash_split64w_kernel"][halves]
+        assert gpu.last_kernel() == want
     finally:
         _split_default(gpu)
         gpu.set_tuning("relpos_fused", 1)
@@ -417,6 +421,64 @@ def test_relpos_non_positive_scale(gpu):
                       rel_pos={"rel_pos_h": np64(x["rel_pos_h"]), "rel_pos_w": np64(x["rel_pos_w"]), "grid": wl.grid})
     assert max_err(np64(o), ref["o"]) <= TOL["bf16"]
 
+
+
+TILED_RELPOS_CASES = [
+    # (B, H, grid, D, layout): rel-pos with precomputed terms on the double-buffered kernel
+    (1, 2, (64, 64), 128, "bhsd"),      # SAM's global grid at head_dim 128
+    (2, 3, (32, 32), 64, "bshd"),       # the grid of a 512-pixel image
+    (1, 2, (20, 12), 128, "bhsd"),      # grid_w not dividing the 32-key tile: tiles span grid rows
+    (2, 2, (7, 4), 64, "bhsd"),         # grid_w 4: eight grid rows per key tile, T = 28 (one partial tile)
+    (1, 3, (9, 36), 128, "bshd"),       # T = 324: ragged last tile
+]
+
+
+@pytest.mark.parametrize("case", TILED_RELPOS_CASES, ids=lambda c: f"B{c[0]}H{c[1]}g{c[2][0]}x{c[2][1]}D{c[3]}{c[4]}")
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+def test_tiled_relpos_grids(gpu, case, dtype):
+    """Rel-pos at head_dim 128 and on grids other than the fused kernels' (any
+    grid_w that is a multiple of 4): relpos_terms into the workspace, then the
+    double-buffered matrix-core kernel reads each key tile's terms.  Tables of
+    standard deviation 0.1 make the bias move the softmax (|bias| ~ 1)."""
+    B, H, (gh, gw), D, layout = case
+    T = gh * gw
+    assert not gpu.relpos_fused(dtype, D, (gh, gw))
+    q = rnd(layout_shape(B, H, T, D, layout), dtype, 60)
+    k = rnd(layout_shape(B, H, T, D, layout), dtype, 61)
+    v = rnd(layout_shape(B, H, T, D, layout), dtype, 62)
+    rh = (rnd((2 * gh - 1, D), torch.float32, 63) * 0.1).to(dtype)
+    rw = (rnd((2 * gw - 1, D), torch.float32, 64) * 0.1).to(dtype)
+    o, lse = gpu.sdpa_relpos(q.cuda(), k.cuda(), v.cuda(), rh.cuda(), rw.cuda(), (gh, gw), layout=layout,
+                             out_dtype=torch.float32, return_lse=True)
+    torch.cuda.synchronize()
+    assert gpu.last_kernel() == "flash_tiled_kernel"
+    ref = oracle.sdpa(np64(q), np64(k), np64(v), layout=layout,
+                      rel_pos={"rel_pos_h": np64(rh), "rel_pos_w": np64(rw), "grid": (gh, gw)})
+    tol = TOL["bf16" if dtype == torch.bfloat16 else "fp16"]
+    assert max_err(np64(o), ref["o"]) <= tol
+    assert max_err(np64(lse), ref["lse"]) <= tol
+
+
+def test_relpos_precomputed_terms_on_general_mfma_kernel(gpu):
+    """With the double-buffered kernel and the in-workgroup split switched off,
+    precomputed terms on a 64-wide grid run on the general MFMA kernel."""
+    wl = workloads.replica("sam_global_relpos", grid=(5, 64), Tq=320, Tkv=320)
+    x = {k_: t.cuda() for k_, t in workloads.generate(wl, seed=6).items()}
+    _split_mode(gpu, 0)
+    gpu.set_tuning("relpos_fused", 0)
+    gpu.set_tuning("tiled", 0)
+    try:
+        o = gpu.sdpa_relpos(x["q"], x["k"], x["v"], x["rel_pos_h"], x["rel_pos_w"], wl.grid, scale=wl.scale,
+                            out_dtype=torch.float32)
+        assert gpu.last_kernel() == "flash_mfma_kernel"
+    finally:
+        _split_default(gpu)
+        gpu.set_tuning("relpos_fused", 1)
+        gpu.set_tuning("tiled", 1)
+    ref = oracle.sdpa(np64(x["q"].cpu()), np64(x["k"].cpu()), np64(x["v"].cpu()), scale=wl.scale,
+                      rel_pos={"rel_pos_h": np64(x["rel_pos_h"].cpu()), "rel_pos_w": np64(x["rel_pos_w"].cpu()),
+                               "grid": wl.grid})
+    assert max_err(np64(o), ref["o"]) <= TOL["bf16"]
 
 def test_dispatch_names_the_kernel(gpu):
     """Which kernel each workload family reaches (the benchmark and profiles

@@ -364,6 +364,75 @@ def test_relpos_backward_matches_oracle(gpu, case):
         assert e < GTOL[dt], (name, e)
 
 
+RELPOS_DROP_CASES = [
+    # dtype, layout, B, H, grid, D: forward route (double-buffered kernel for 16-bit head_dim
+    # 64 / 128 with grid_w % 4 == 0, else the generic kernel) and backward mode
+    ("bf16", "bhsd", 1, 2, (16, 64), 64),      # 64-wide rows: tiled forward, 64-wide backward mode
+    ("bf16", "bshd", 2, 3, (14, 14), 64),      # SAM windows: generic forward, grid <= 32 backward
+    ("fp16", "bhsd", 1, 2, (20, 12), 128),     # tiled forward at head_dim 128
+    ("bf16", "bhsd", 1, 2, (40, 24), 64),      # a side beyond 32: dS sums through LDS in the backward
+    ("bf16", "bhsd", 1, 1, (5, 27), 128),      # grid_w 27: generic forward; ragged T = 135
+    ("bf16", "bhsd", 1, 2, (8, 8), 32),        # head_dim 32: generic forward
+]
+
+
+def _relpos_drop_inputs(case, seed):
+    dts, layout, B, H, grid, D = case
+    dt = DT[dts]
+    gh, gw = grid
+    T = gh * gw
+    rng = np.random.default_rng(seed)
+    q, k, v, do = (draw(rng, shp(layout, B, H, T, D), dt) for _ in range(4))
+    rh = (0.3 * draw(rng, (2 * gh - 1, D), torch.float32)).to(dt)
+    rw = (0.3 * draw(rng, (2 * gw - 1, D), torch.float32)).to(dt)
+    rate = 0.15
+    keep = st.dropout_keep(23, 5, rate, B, H, T, T)
+    rp = {"rel_pos_h": np64(rh), "rel_pos_w": np64(rw), "grid": grid}
+    return dt, layout, grid, D, q, k, v, do, rh, rw, rate, keep, rp
+
+
+@pytest.mark.parametrize("case", RELPOS_DROP_CASES,
+                         ids=[f"{c[0]}-{c[1]}-B{c[2]}H{c[3]}-{c[4][0]}x{c[4][1]}-D{c[5]}" for c in RELPOS_DROP_CASES])
+def test_relpos_dropout_forward_matches_oracle(gpu, case):
+    """Attention dropout with the rel-pos bias ([Axon PR 650], description:
+    `:dropout_rate` in :train mode; SAM's bias): O = (W * Z) . V against the
+    oracle on the same keep bits; lse is that of the undropped scores."""
+    dt, layout, grid, D, q, k, v, do, rh, rw, rate, keep, rp = _relpos_drop_inputs(case, 41)
+    scale = 1.0 / np.sqrt(D)
+    o, lse = gpu.sdpa_relpos(q.cuda(), k.cuda(), v.cuda(), rh.cuda(), rw.cuda(), grid, layout=layout, scale=scale,
+                             out_dtype=torch.float32, return_lse=True,
+                             dropout={"keep": keep_words_tensor(keep), "rate": rate})
+    torch.cuda.synchronize()
+    tiled = case[0] != "fp32" and D in (64, 128) and grid[1] % 4 == 0
+    assert gpu.last_kernel() == ("flash_tiled_kernel" if tiled else "generic_fwd_kernel")
+    ref = st.sdpa_train_fwd(np64(q), np64(k), np64(v), layout=layout, scale=scale, rel_pos=rp, keep=keep, rate=rate)
+    dts = case[0]
+    # as for dropout without the bias: the kept weights' factor 65536 / (65536 - thresh) scales the error
+    assert max_err(np64(o), ref["o"]) < TOL[dts] * (65536.0 / (65536.0 - round(rate * 65536)))
+    assert max_err(np64(lse), ref["lse"]) <= TOL[dts]
+
+
+@pytest.mark.parametrize("case", RELPOS_DROP_CASES,
+                         ids=[f"{c[0]}-{c[1]}-B{c[2]}H{c[3]}-{c[4][0]}x{c[4][1]}-D{c[5]}" for c in RELPOS_DROP_CASES])
+def test_relpos_dropout_backward_matches_oracle(gpu, case):
+    """Gradients of dropout with the rel-pos bias: dq, dk, dv and both tables'
+    gradients against the oracle, the forward pass's O and lse from the oracle."""
+    dt, layout, grid, D, q, k, v, do, rh, rw, rate, keep, rp = _relpos_drop_inputs(case, 43)
+    scale = 1.0 / np.sqrt(D)
+    kw = dict(layout=layout, scale=scale, rel_pos=rp, keep=keep, rate=rate)
+    fwd = st.sdpa_train_fwd(np64(q), np64(k), np64(v), **kw)
+    o = torch.from_numpy(np.ascontiguousarray(fwd["o"], dtype=np.float32)).to(dt)
+    lse = torch.from_numpy(fwd["lse"].astype(np.float32))
+    dq, dk, dv, drh, drw = gpu.sdpa_relpos_backward(q.cuda(), k.cuda(), v.cuda(), o.cuda(), do.cuda(), lse.cuda(),
+                                                    rh.cuda(), rw.cuda(), grid, layout=layout, scale=scale,
+                                                    dropout={"keep": keep_words_tensor(keep), "rate": rate})
+    torch.cuda.synchronize()
+    ref = st.sdpa_bwd(np64(q), np64(k), np64(v), np64(do), **kw)
+    for name, got in (("dq", dq), ("dk", dk), ("dv", dv), ("drel_pos_h", drh), ("drel_pos_w", drw)):
+        e = norm_err(np64(got), ref[name])
+        assert e < GTOL[dt], (name, e)
+
+
 TERMS_KERNEL_CASES = [
     # dtype, layout, B, H, grid, D
     ("bf16", "bhsd", 1, 2, (16, 64), 64),     # blocks within one 64-wide grid row

@@ -216,6 +216,52 @@ def test_backward_relpos_finite_differences():
                "rw": grads["drel_pos_w"]}, G, rng, npoints=8)
 
 
+
+def test_backward_relpos_dropout_finite_differences():
+    """Dropout together with the rel-pos bias: the gradients of q, k, v and of
+    both tables against central differences of the dropped forward pass."""
+    rng = np.random.default_rng(15)
+    B, H, gh, gw, D = 1, 2, 3, 2, 4
+    T = gh * gw
+    q, k, v = rnd(rng, B, H, T, D), rnd(rng, B, H, T, D), rnd(rng, B, H, T, D)
+    rh, rw = rnd(rng, 2 * gh - 1, D), rnd(rng, 2 * gw - 1, D)
+    G = rnd(rng, B, H, T, D)
+    rate = 0.3
+    keep = st.dropout_keep(17, 2, rate, B, H, T, T)
+    assert 0 < keep.mean() < 1
+    rp = lambda rh, rw: {"rel_pos_h": rh, "rel_pos_w": rw, "grid": (gh, gw)}
+    grads = st.sdpa_bwd(q, k, v, G, rel_pos=rp(rh, rw), keep=keep, rate=rate)
+    fn = lambda q, k, v, rh, rw: st.sdpa_train_fwd(q, k, v, rel_pos=rp(rh, rw), keep=keep, rate=rate)["o"]
+    _fd_check(fn, {"q": q, "k": k, "v": v, "rh": rh, "rw": rw},
+              {"q": grads["dq"], "k": grads["dk"], "v": grads["dv"], "rh": grads["drel_pos_h"],
+               "rw": grads["drel_pos_w"]}, G, rng, npoints=8)
+
+
+def test_relpos_dropout_forward_keeps_one_key():
+    """With one kept key j* per row, O_i = W[i, j*] * keep_scale * V[j*], where
+    W[i, j*] = exp(scale q_i.k_j* + bias_ij* - lse_i) from the plain rel-pos
+    oracle's lse: dropout and the bias compose as the pages state."""
+    rng = np.random.default_rng(16)
+    B, H, gh, gw, D = 1, 2, 2, 3, 4
+    T = gh * gw
+    q, k, v = rnd(rng, B, H, T, D), rnd(rng, B, H, T, D), rnd(rng, B, H, T, D)
+    rh, rw = rnd(rng, 2 * gh - 1, D), rnd(rng, 2 * gw - 1, D)
+    rp = {"rel_pos_h": rh, "rel_pos_w": rw, "grid": (gh, gw)}
+    jstar = 4
+    keep = np.zeros((B, H, T, T), dtype=bool)
+    keep[..., jstar] = True
+    rate = 0.25
+    _, ks = st.dropout_threshold(rate)
+    out = st.sdpa_train_fwd(q, k, v, scale=0.5, rel_pos=rp, keep=keep, rate=rate)
+    base = so.sdpa(q, k, v, scale=0.5, rel_pos=rp)
+    assert np.allclose(out["lse"], base["lse"], atol=1e-13)
+    for h in range(H):
+        for i in range(T):
+            th = q[0, h, i] @ rh[i // gw - jstar // gw + gh - 1]      # term_h[i, row(j*)]
+            tw = q[0, h, i] @ rw[i % gw - jstar % gw + gw - 1]        # term_w[i, col(j*)]
+            w = np.exp(0.5 * q[0, h, i] @ k[0, h, jstar] + th + tw - base["lse"][0, h, i])
+            assert np.allclose(out["o"][0, h, i], w * ks * v[0, h, jstar], atol=1e-12)
+
 def test_backward_matches_torch_autograd():
     """torch's CPU autograd (float64) on the plain composition softmax -> dropout factor -> @ V."""
     rng = np.random.default_rng(14)
