@@ -27,6 +27,7 @@ std::atomic<int64_t> g_split64w{1};
 std::atomic<int64_t> g_tiled{1};
 std::atomic<int64_t> g_generic_waves{0};
 std::atomic<int64_t> g_relpos_mfma{1};
+std::atomic<int64_t> g_tgrad_mfma{1};
 
 // The tuning knobs as one call sees them: read once at the call's start, so
 // the route, the split count and the workspace check of that call agree even
@@ -610,8 +611,10 @@ size_t relpos_bwd_bytes(int64_t B, int64_t H, int64_t gh, int64_t gw, int64_t D,
   const size_t sz[8] = {align256((size_t)B * H * T * 4),      align256((size_t)B * H * T * gh * 4),
                         align256((size_t)B * H * T * gw * 4), align256((size_t)B * H * T * gh * 4),
                         align256((size_t)B * H * T * gw * 4), align256((size_t)B * H * T * D * 4),
-                        align256((size_t)sdpa::relpos_group_splits(B * H * gw, gh) * gh * gh * D * 4),
-                        align256((size_t)sdpa::relpos_group_splits(B * H * gh, gw) * gw * gw * D * 4)};
+                        align256(std::max((size_t)sdpa::relpos_group_splits(B * H * gw, gh) * gh * gh * D * 4,
+                                          (size_t)sdpa::relpos_tgrad_wgs(B, H, gh, gw) * 128 * D * 4)),
+                        align256(std::max((size_t)sdpa::relpos_group_splits(B * H * gh, gw) * gw * gw * D * 4,
+                                          (size_t)sdpa::relpos_tgrad_wgs(B, H, gh, gw) * 128 * D * 4))};
   size_t tot = 0;
   for (int a = 0; a < 8; ++a) {
     if (offs) offs[a] = tot;
@@ -695,6 +698,7 @@ int relpos_bwd_impl(const void* q, const void* k, const void* v, const void* o, 
   p.group_w = (float*)(ws + off[7]);
   p.split_h = sdpa::relpos_group_splits(B * H * grid_w, grid_h);
   p.split_w = sdpa::relpos_group_splits(B * H * grid_h, grid_w);
+  p.tgrad_mfma = g_tgrad_mfma.load() != 0;
   st = relpos_terms(q, dtype, layout, B, H, grid_h, grid_w, D, rel_pos_h, rel_pos_w, th, tw, stream);
   if (st) return st;
   hipError_t e = sdpa::launch_bwd(p, (hipStream_t)stream);
@@ -796,6 +800,11 @@ int sdpa_set_tuning(const char* key, int64_t value) {
   if (!std::strcmp(key, "relpos_mfma")) {
     if (value != 0 && value != 1) return fail(SDPA_ERR_INVALID, "relpos_mfma must be 0 or 1");
     g_relpos_mfma.store(value);
+    return SDPA_OK;
+  }
+  if (!std::strcmp(key, "relpos_bwd_mfma")) {
+    if (value != 0 && value != 1) return fail(SDPA_ERR_INVALID, "relpos_bwd_mfma must be 0 or 1");
+    g_tgrad_mfma.store(value);
     return SDPA_OK;
   }
   if (!std::strcmp(key, "generic_waves")) {

@@ -92,10 +92,26 @@ struct BwdParams {
   float* group_w;             // [split_w][grid_w (column c)][grid_w (x)][D] fp32 scratch
   int grid_h, grid_w;
   int split_h, split_w;       // query slices of the grouped table products
+  int tgrad_mfma;             // table gradients on the matrix cores where the shape allows (1) or not (0)
 };
 
 // Query slices of a grouped table product: about 512 workgroups in all, each
 // with at least 64 queries.  Used by the launcher and the workspace planner.
+// Table gradients on the matrix cores: workgroups per table (each keeps a
+// [128 x D] fp32 partial sum in the group_h / group_w scratch), and whether a
+// shape fits the kernel (tables up to 64 entries wide, a line's dT and q rows
+// staged in 64 KB of LDS).
+inline int relpos_tgrad_wgs(int64_t B, int64_t H, int64_t gh, int64_t gw) {
+  const int64_t items = B * H * (gh > gw ? gh : gw);
+  return (int)(items < 256 ? items : 256);
+}
+inline bool relpos_tgrad_mfma_ok(int64_t B, int64_t H, int64_t gh, int64_t gw, int64_t D) {
+  if (gh > 64 || gw > 64 || (D != 32 && D != 64 && D != 128) || B * H > 65535) return false;
+  // dT and q are read through descriptors with 32-bit byte offsets
+  if (B * H * gh * gw * (gh > gw ? gh : gw) * 4 > 0x7fffffffLL || B * H * gh * gw * D * 2 > 0x7fffffffLL) return false;
+  return true;                                  // two staging buffers of at most 64 x (96 x 4 + 128 x 2) bytes
+}
+
 inline int relpos_group_splits(int64_t members, int64_t groups) {
   int64_t s = (512 + groups - 1) / groups;
   const int64_t cap = members / 64 > 1 ? members / 64 : 1;

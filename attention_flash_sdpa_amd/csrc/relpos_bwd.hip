@@ -22,6 +22,7 @@ namespace sdpa {
 namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kMaxTabRows = 2 * 128 - 2;     // (2 gh - 1) + (2 gw - 1) with gh + gw <= 128
 
@@ -194,11 +195,293 @@ __global__ __launch_bounds__(256) void relpos_diag_kernel(const float* G, float*
   }
 }
 
+// ------------------------------------------- table gradients on MFMA ------
+// Both tables' gradients as products on the matrix cores (fp32 operands, the
+// 32x32x2 fp32 matrix op, so dT enters unrounded).  The queries are taken by
+// lines: grid rows r for rel_pos_h (the line's grid_w queries share row(i) =
+// r), grid columns c for rel_pos_w (grid_h queries, col(i) = c).  For a table
+// of width G (G = grid_h for rows, grid_w for columns) and a line l, entry t
+// of the gradient collects dT[i][a] q_i over the line's queries with
+// a = l + G - 1 - t:
+//   dR[t][d] += sum_i A_l[t][i] q_i[d],   A_l[t][i] = dT[i][l + G - 1 - t]  (0 outside [0, G)).
+// A workgroup takes a run of (batch, head, line) items of one table
+// (blockIdx.y: 0 rows, 1 columns) and keeps the [2G - 1 <= 127 rows x D] sums
+// in MFMA accumulators, wave w owning rows 32w .. 32w + 31 (a wave whose rows
+// the line does not reach skips it); each workgroup's sums go to scratch and
+// a second kernel adds them in a fixed order (deterministic, no atomics).
+constexpr int kTgPad = 32;                     // row padding (floats): the two query rows of an MFMA k pair hit other banks
+constexpr int kTgGP = 64 + kTgPad;             // dT row stride in LDS (a 64-lane copy fills the first 64 floats)
+constexpr int kDqGP = 65;                      // the dq kernel's dT row stride: odd, >= 64
+
+// LDS bytes of one staging buffer: dT rows [L][kTgGP] fp32 and q rows [L rounded
+// up to 4][D] in the input type (a q copy moves up to 4 rows at once).
+__host__ __device__ inline int tg_buf_bytes(int L, int D) { return L * kTgGP * 4 + (L + 3) / 4 * 4 * D * 2; }
+
+template <typename E, int D>
+__global__ __launch_bounds__(256) void relpos_tgrad_kernel(BwdParams p, int ipw_h, int ipw_w) {
+  constexpr int DB = D / 32;
+  constexpr int QRB = D * 2;                    // bytes of one q row
+  constexpr int QRPI = 256 / QRB;               // q rows one 64-lane 4-byte copy moves (D 32: 4, 64: 2, 128: 1)
+  extern __shared__ __attribute__((aligned(16))) char tg_lds[];   // two staging buffers
+  const bool rows = blockIdx.y == 0;
+  const int gh = p.grid_h, gw = p.grid_w;
+  const int G = rows ? gh : gw, L = rows ? gw : gh;
+  const int BUF = tg_buf_bytes(L, D);
+  const float* dT = rows ? p.dterm_h : p.dterm_w;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int trow = 32 * wave + (lane & 31), kh = lane >> 5;
+  const int64_t T = p.Tq;
+  // Descriptors over all of dT and q: a lane past its row's end reads the next
+  // row (it lands in LDS padding) or, past the array, 0.
+  const __amdgpu_buffer_rsrc_t drs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)dT, 0, (int)(p.B * p.Hq * T * G * 4), 0x00020000);
+  const __amdgpu_buffer_rsrc_t qrs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)p.q, 0, (int)(((p.B - 1) * p.q_sb + (p.Hq - 1) * p.q_sh + (T - 1) * p.q_st + D) * 2), 0x00020000);
+  f32x16 acc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) acc[db] = (f32x16){};
+  const int64_t items = p.B * p.Hq * G;
+  const int ipw = rows ? ipw_h : ipw_w;
+  const int64_t it0 = (int64_t)blockIdx.x * ipw, it1 = min(items, it0 + ipw);
+  const int64_t istep = rows ? 1 : gw;          // query index step along the line
+  // Copies of a line's rows straight into LDS buffer `buf` (no registers):
+  // dT row qi -> 64 floats at row qi of the dT region; q rows in groups of QRPI.
+  auto issue = [&](int64_t it, int buf) {
+    const int64_t bh = it / G;
+    const int line = (int)(it - bh * G);
+    const int bh32 = (int)bh, hq32 = (int)p.Hq;        // B * Hq < 2^16
+    const int64_t b = bh32 / hq32, h = bh32 - (bh32 / hq32) * hq32;
+    const int64_t ibase = rows ? (int64_t)line * gw : (int64_t)line;
+    char* base = tg_lds + buf * BUF;
+    for (int qi = wave; qi < L; qi += 4) {
+      const int64_t i = ibase + qi * istep;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(drs, (__attribute__((address_space(3))) void*)(base + qi * kTgGP * 4), 4,
+                                               (int)(((bh * T + i) * G + lane) * 4), 0, 0, 0);
+    }
+    char* qbase = base + L * kTgGP * 4;
+    for (int q0 = wave * QRPI; q0 < L; q0 += 4 * QRPI) {
+      const int qi = q0 + lane / (64 / QRPI);
+      const int64_t i = ibase + (qi < L ? qi : q0) * istep;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          qrs, (__attribute__((address_space(3))) void*)(qbase + q0 * QRB), 4,
+          (int)((b * p.q_sb + h * p.q_sh + i * p.q_st) * 2 + (lane % (64 / QRPI)) * 4), 0, 0, 0);
+    }
+  };
+  if (it0 < it1) issue(it0, 0);
+  for (int64_t it = it0; it < it1; ++it) {
+    const int buf = (int)((it - it0) & 1);
+    const int line = (int)(it - (it / G) * G);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();                                   // this line's rows landed; the other buffer is free
+    if (it + 1 < it1) issue(it + 1, buf ^ 1);
+    if (32 * wave > line + G - 1 || 32 * wave + 31 < line) continue;   // rows this line does not reach
+    const float* dts = (const float*)(tg_lds + buf * BUF);
+    const E* qs = (const E*)(tg_lds + buf * BUF + L * kTgGP * 4);
+    const int a = line + G - 1 - trow;
+    const bool aok = a >= 0 && a < G;
+    const float* ar = dts + (aok ? a : 0) + kh * kTgGP;
+    const E* br = qs + (lane & 31) + kh * D;
+    int k0 = 0;
+    // 8 k pairs (16 queries) at a time: every LDS read of the batch is issued
+    // before its matrix ops
+    for (; k0 + 16 <= L; k0 += 16) {
+      float av[8], bv[8][DB];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        av[j] = aok ? ar[(k0 + 2 * j) * kTgGP] : 0.0f;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) bv[j][db] = (float)br[(k0 + 2 * j) * D + 32 * db];
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[j], bv[j][db], acc[db], 0, 0, 0);
+    }
+    for (; k0 < L; k0 += 2) {
+      const bool qok = k0 + kh < L;
+      const float av = (aok && qok) ? ar[k0 * kTgGP] : 0.0f;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const float bv = qok ? (float)br[k0 * D + 32 * db] : 0.0f;
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(av, bv, acc[db], 0, 0, 0);
+      }
+    }
+  }
+  // this workgroup's sums: [128 rows t][D], rows 8 (r / 4) + 4 kh + r % 4 of the wave's block
+  float* out = (rows ? p.group_h : p.group_w) + (int64_t)blockIdx.x * 128 * D;
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      out[(32 * wave + 8 * (r / 4) + 4 * kh + (r % 4)) * D + 32 * db + (lane & 31)] = acc[db][r];
+}
+
+// dR[t][d] = sum over the nwg workgroups' partial sums: thread (g, d) of a
+// workgroup adds the partials w = g, g + 4, ... of entry (t, d) for 64 head
+// dims (a wave reads 256 contiguous bytes of one partial row), then the four
+// sums add in order: a fixed order.  Grid: (max(2 grid_h - 1, 2 grid_w - 1),
+// ceil(D / 64), 2 tables).
+__global__ __launch_bounds__(256) void relpos_tgrad_reduce_kernel(BwdParams p, int nwg, int D) {
+  __shared__ float red[4][64];
+  const bool rows = blockIdx.z == 0;
+  const int Tn = 2 * (rows ? p.grid_h : p.grid_w) - 1;
+  const int t = blockIdx.x;
+  if (t >= Tn) return;                                // the whole workgroup
+  const float* part = rows ? p.group_h : p.group_w;
+  const int g = threadIdx.x >> 6, dd = threadIdx.x & 63, d = blockIdx.y * 64 + dd;
+  float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  if (d < D) {
+    int w = g;
+    for (; w + 12 < nwg; w += 16)                      // four loads in flight, each its own sum
+#pragma unroll
+      for (int u = 0; u < 4; ++u) acc[u] += part[((int64_t)(w + 4 * u) * 128 + t) * D + d];
+    for (; w < nwg; w += 4) acc[0] += part[((int64_t)w * 128 + t) * D + d];
+  }
+  red[g][dd] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+  __syncthreads();
+  if (g == 0 && d < D)
+    (rows ? p.drel_h : p.drel_w)[(int64_t)t * D + d] = ((red[0][dd] + red[1][dd]) + red[2][dd]) + red[3][dd];
+}
+
+// ---------------------------------------------- tables' part of dq, MFMA --
+// dq_i = dQ_acc_i + sum_y dT_h[i, y] Rh[row(i) - y + gh - 1] + sum_x dT_w[i, x] Rw[col(i) - x + gw - 1]
+// as line products on the matrix cores (fp32 operands): for a grid row r the
+// term_h part of its queries c is [c][y] x [y][d] with the reversed table
+// rows Rh[r + gh - 1 - y]; for a grid column c the term_w part of its
+// queries likewise with Rw[c + gw - 1 - x].  Pass ROWS adds the term_h part
+// into the fp32 dQ_acc; pass !ROWS adds the term_w part and writes dq.  One
+// workgroup per (batch, head, line); wave w owns output blocks w and w + 4 of
+// the [L (<= 64) queries x D] result (32 x 32 blocks, query blocks outer).
+template <typename E, int D, typename GT, bool ROWS>
+__global__ __launch_bounds__(256) void relpos_dq_mfma_kernel(BwdParams p) {
+  constexpr int DB = D / 32;
+  constexpr int QRB = D * 2;                    // bytes of one table row
+  constexpr int QRPI = 256 / QRB;               // table rows one 64-lane 4-byte copy moves
+  extern __shared__ __attribute__((aligned(16))) char dq_lds[];
+  const int gh = p.grid_h, gw = p.grid_w;
+  const int G = ROWS ? gh : gw, L = ROWS ? gw : gh;
+  const int MB = (L + 31) / 32;
+  // dT rows of the line's queries [L][kDqGP] fp32 (odd stride: the 32 query
+  // rows of an A read hit 32 banks), then the reversed table rows
+  // tab[a] = R[line + G - 1 - a], [G rounded up to 4][D] in the input type.
+  const float* dts = (const float*)dq_lds;
+  const E* tab = (const E*)(dq_lds + L * kDqGP * 4);
+  const float* dT = ROWS ? p.dterm_h : p.dterm_w;
+  const E* R = (const E*)(ROWS ? p.rel_h : p.rel_w);
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kh = lane >> 5, l32 = lane & 31;
+  const int64_t bh = blockIdx.x / G;
+  const int line = (int)(blockIdx.x - bh * G);
+  const int bh32 = (int)bh, hq32 = (int)p.Hq;           // B * Hq < 2^16
+  const int64_t b = bh32 / hq32, h = bh32 - (bh32 / hq32) * hq32;
+  const int64_t T = p.Tq;
+  auto query = [&](int qi) -> int64_t { return ROWS ? (int64_t)line * gw + qi : (int64_t)qi * gw + line; };
+  // Copies straight into LDS (no registers, one memory round trip): a lane
+  // past its row's end reads the next row (LDS padding) or, past the array, 0.
+  const __amdgpu_buffer_rsrc_t drs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)dT, 0, (int)(p.B * p.Hq * T * G * 4), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rrs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)R, 0, (int)((2 * G - 1) * D * 2), 0x00020000);
+  for (int qi = wave; qi < L; qi += 4)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(drs, (__attribute__((address_space(3))) void*)(dq_lds + qi * kDqGP * 4), 4,
+                                             (int)(((bh * T + query(qi)) * G + lane) * 4), 0, 0, 0);
+  char* tbase = dq_lds + L * kDqGP * 4;
+  for (int a0 = wave * QRPI; a0 < G; a0 += 4 * QRPI) {
+    const int a = a0 + lane / (64 / QRPI);
+    const int ra = line + G - 1 - (a < G ? a : a0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rrs, (__attribute__((address_space(3))) void*)(tbase + a0 * QRB), 4,
+                                             (int)(ra * QRB + (lane % (64 / QRPI)) * 4), 0, 0, 0);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  // this lane's dQ_acc entries of its (at most two) output blocks, requested
+  // now so that their round trip passes under the products
+  float pre[2][16];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int blk = wave + 4 * u;
+    const int mb = blk / DB, db = blk - mb * DB;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int qi = 32 * mb + 8 * (r / 4) + 4 * kh + (r % 4);
+      pre[u][r] = (blk < MB * DB && qi < L) ? p.dq_acc[(bh * T + query(qi)) * D + 32 * db + l32] : 0.0f;
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int blk = wave + 4 * u;
+    if (blk >= MB * DB) break;
+    const int mb = blk / DB, db = blk - mb * DB;
+    const int qrow = 32 * mb + l32;
+    const bool qok = qrow < L;
+    const float* ar = dts + (qok ? qrow : 0) * kDqGP + kh;
+    const E* br = tab + kh * D + 32 * db + l32;
+    f32x16 acc = (f32x16){};
+    int k0 = 0;
+    for (; k0 + 16 <= G; k0 += 16) {
+      float av[8], bv[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        av[j] = qok ? ar[k0 + 2 * j] : 0.0f;
+        bv[j] = (float)br[(k0 + 2 * j) * D];
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av[j], bv[j], acc, 0, 0, 0);
+    }
+    for (; k0 < G; k0 += 2) {
+      const bool kok = k0 + kh < G;
+      const float av = (qok && kok) ? ar[k0] : 0.0f;
+      const float bv = kok ? (float)br[k0 * D] : 0.0f;
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av, bv, acc, 0, 0, 0);
+    }
+    // rows 8 (r / 4) + 4 kh + r % 4 of the block are queries, the lane's column a head dim
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int qi = 32 * mb + 8 * (r / 4) + 4 * kh + (r % 4);
+      if (qi >= L) continue;
+      const int64_t i = query(qi);
+      const int d = 32 * db + l32;
+      if (ROWS) p.dq_acc[(bh * T + i) * D + d] = pre[u][r] + acc[r];
+      else ((GT*)p.dq)[b * p.q_sb + h * p.q_sh + i * p.q_st + d] = (GT)(pre[u][r] + acc[r]);
+    }
+  }
+}
+
+__host__ __device__ inline int dq_lds_bytes(int L, int G, int D) { return L * kDqGP * 4 + (G + 3) / 4 * 4 * D * 2; }
+
+template <int D>
+bool relpos_dq_mfma_ok(const BwdParams& p) {
+  const int64_t gh = p.grid_h, gw = p.grid_w;
+  // dT through a descriptor with 32-bit byte offsets; LDS: dT rows plus table rows
+  return gh <= 64 && gw <= 64 && p.B * p.Hq * gh * gw * (gh > gw ? gh : gw) * 4 <= 0x7fffffffLL;
+}
+
 template <typename E, int D, typename G>
 void tail_typed(const BwdParams& p, hipStream_t s) {
-  constexpr int QPB = 256 / (D / 16);
-  dim3 gq((unsigned)((p.Tq + QPB - 1) / QPB), (unsigned)(p.B * p.Hq));
-  hipLaunchKernelGGL((relpos_bwd_dq_kernel<E, D, G>), gq, dim3(256), 0, s, p);
+  if (p.tgrad_mfma && relpos_dq_mfma_ok<D>(p)) {
+    const size_t lh = dq_lds_bytes(p.grid_w, p.grid_h, D);
+    const size_t lw = dq_lds_bytes(p.grid_h, p.grid_w, D);
+    hipLaunchKernelGGL((relpos_dq_mfma_kernel<E, D, G, true>), dim3((unsigned)(p.B * p.Hq * p.grid_h)), dim3(256), lh,
+                       s, p);
+    hipLaunchKernelGGL((relpos_dq_mfma_kernel<E, D, G, false>), dim3((unsigned)(p.B * p.Hq * p.grid_w)), dim3(256), lw,
+                       s, p);
+  } else {
+    constexpr int QPB = 256 / (D / 16);
+    dim3 gq((unsigned)((p.Tq + QPB - 1) / QPB), (unsigned)(p.B * p.Hq));
+    hipLaunchKernelGGL((relpos_bwd_dq_kernel<E, D, G>), gq, dim3(256), 0, s, p);
+  }
+  if (relpos_tgrad_mfma_ok(p.B, p.Hq, p.grid_h, p.grid_w, D) && p.tgrad_mfma) {
+    const int nwg = relpos_tgrad_wgs(p.B, p.Hq, p.grid_h, p.grid_w);
+    const int64_t ih = p.B * p.Hq * p.grid_h, iw = p.B * p.Hq * p.grid_w;
+    const size_t lds = 2 * (size_t)std::max(tg_buf_bytes(p.grid_w, D), tg_buf_bytes(p.grid_h, D));
+    hipLaunchKernelGGL((relpos_tgrad_kernel<E, D>), dim3((unsigned)nwg, 2u), dim3(256), lds, s, p,
+                       (int)((ih + nwg - 1) / nwg), (int)((iw + nwg - 1) / nwg));
+    const int tmax = 2 * (p.grid_h > p.grid_w ? p.grid_h : p.grid_w) - 1;
+    hipLaunchKernelGGL(relpos_tgrad_reduce_kernel, dim3((unsigned)tmax, (unsigned)((D + 63) / 64), 2u), dim3(256), 0,
+                       s, p, nwg, D);
+    return;
+  }
   hipLaunchKernelGGL((relpos_group_kernel<E, D, true>), dim3((unsigned)p.grid_h, (unsigned)p.split_h), dim3(256), 0, s, p);
   hipLaunchKernelGGL((relpos_group_kernel<E, D, false>), dim3((unsigned)p.grid_w, (unsigned)p.split_w), dim3(256), 0, s, p);
   hipLaunchKernelGGL(relpos_diag_kernel, dim3((unsigned)((D + 15) / 16), (unsigned)(2 * p.grid_h - 1)), dim3(256), 0, s,

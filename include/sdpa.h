@@ -238,6 +238,10 @@ const char* sdpa_last_kernel(void);
  *   "relpos_mfma"  1 (default) = relpos_terms (also inside sdpa_relpos_bwd)
  *                  forms 16-bit inputs' terms on the matrix cores where
  *                  head_dim and the grid allow it; 0 = on the vector ALUs.
+ *   "relpos_bwd_mfma" 1 (default) = sdpa_relpos_bwd forms the tables'
+ *                  gradients and the tables' part of dq on the matrix cores
+ *                  where the grid allows it (both sides <= 64); 0 = on the
+ *                  vector ALUs.
  *   "generic_waves" 0 (default) = the vector-ALU kernel (fp32, and shapes no
  *                  matrix-core kernel takes) splits each 64-row block's keys
  *                  over 4 waves when the launch has fewer blocks than the GPU

@@ -433,6 +433,48 @@ def test_relpos_dropout_backward_matches_oracle(gpu, case):
         assert e < GTOL[dt], (name, e)
 
 
+TABLE_KERNEL_CASES = [
+    ("bf16", "bhsd", 1, 2, (16, 64), 64),
+    ("fp16", "bshd", 2, 3, (14, 14), 64),
+    ("bf16", "bhsd", 1, 2, (40, 24), 128),
+    ("bf16", "bhsd", 2, 2, (8, 8), 32),
+]
+
+
+@pytest.mark.parametrize("mfma", [1, 0], ids=["tables-mfma", "tables-valu"])
+@pytest.mark.parametrize("case", TABLE_KERNEL_CASES,
+                         ids=[f"{c[0]}-{c[1]}-B{c[2]}H{c[3]}-{c[4][0]}x{c[4][1]}-D{c[5]}" for c in TABLE_KERNEL_CASES])
+def test_relpos_backward_table_kernels(gpu, case, mfma):
+    """The tables' gradients from the matrix-core kernel (lines of the grid,
+    fp32 products, partial sums added in a fixed order) and from the
+    vector-ALU grouped products ("relpos_bwd_mfma" = 0), against the oracle."""
+    dts, layout, B, H, grid, D = case
+    dt = DT[dts]
+    gh, gw = grid
+    T = gh * gw
+    rng = np.random.default_rng(47)
+    q, k, v, do = (draw(rng, shp(layout, B, H, T, D), dt) for _ in range(4))
+    rh = (0.3 * draw(rng, (2 * gh - 1, D), torch.float32)).to(dt)
+    rw = (0.3 * draw(rng, (2 * gw - 1, D), torch.float32)).to(dt)
+    scale = 1.0 / np.sqrt(D)
+    rp = {"rel_pos_h": np64(rh), "rel_pos_w": np64(rw), "grid": grid}
+    fwd = st.sdpa_train_fwd(np64(q), np64(k), np64(v), layout=layout, scale=scale, rel_pos=rp)
+    o = torch.from_numpy(np.ascontiguousarray(fwd["o"], dtype=np.float32)).to(dt)
+    lse = torch.from_numpy(fwd["lse"].astype(np.float32))
+    gpu.set_tuning("relpos_bwd_mfma", mfma)
+    try:
+        dq, dk, dv, drh, drw = gpu.sdpa_relpos_backward(q.cuda(), k.cuda(), v.cuda(), o.cuda(), do.cuda(),
+                                                        lse.cuda(), rh.cuda(), rw.cuda(), grid, layout=layout,
+                                                        scale=scale)
+        torch.cuda.synchronize()
+    finally:
+        gpu.set_tuning("relpos_bwd_mfma", 1)
+    ref = st.sdpa_bwd(np64(q), np64(k), np64(v), np64(do), layout=layout, scale=scale, rel_pos=rp)
+    for name, got in (("dq", dq), ("drel_pos_h", drh), ("drel_pos_w", drw)):
+        e = norm_err(np64(got), ref[name])
+        assert e < GTOL[dt], (name, e)
+
+
 TERMS_KERNEL_CASES = [
     # dtype, layout, B, H, grid, D
     ("bf16", "bhsd", 1, 2, (16, 64), 64),     # blocks within one 64-wide grid row
