@@ -28,7 +28,7 @@ namespace sdpa {
 
 namespace {
 constexpr int TRMAX = 128;            // table rows one 32-token block's products cover at most
-constexpr int TPITCH = TRMAX + 1;     // slot pitch (floats): rows of consecutive tokens start one bank apart
+constexpr int TPITCH = TRMAX + 4;     // slot pitch (floats): 16-byte aligned rows, consecutive tokens four banks apart
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
@@ -42,7 +42,7 @@ __host__ __device__ inline int terms_rows_w(int gw) { return gw % 32 == 0 ? 31 +
 template <typename E, int NC>
 __global__ __launch_bounds__(256) void relpos_terms_mfma_kernel(TermsParams p) {
   typedef typename Vec16<E>::x8 e8;
-  __shared__ float slots[4][32 * TPITCH];
+  __shared__ __attribute__((aligned(16))) float slots[4][32 * TPITCH];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 5, ql = lane & 31;
   const int64_t b = blockIdx.z, h = blockIdx.y;
@@ -83,7 +83,9 @@ __global__ __launch_bounds__(256) void relpos_terms_mfma_kernel(TermsParams p) {
 #pragma unroll
       for (int c = 0; c < NC; ++c) acc = mfma32(tf[rb][c], qf[c], acc);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) slot[ql * TPITCH + rb * 32 + 8 * (i / 4) + 4 * g + (i % 4)] = acc[i];
+      for (int i4 = 0; i4 < 4; ++i4)
+        *(f32x4_t*)(slot + ql * TPITCH + rb * 32 + 8 * i4 + 4 * g) =
+            (f32x4_t){acc[4 * i4], acc[4 * i4 + 1], acc[4 * i4 + 2], acc[4 * i4 + 3]};
     }
   };
   // Term rows of the block's tokens: out[i, y] = slot[i][base(i) - y],
@@ -91,8 +93,38 @@ __global__ __launch_bounds__(256) void relpos_terms_mfma_kernel(TermsParams p) {
   // writes elements e = W l, W l + 64 W, ... (W = 4 with 16-byte stores, else
   // 1); its token index q = e / nout, offset y and grid coordinates advance by
   // fixed steps, so only the first position takes a division.
+  const float rcp_gw = 1.0f / (float)gw;
   auto read_out = [&](float* out, int nout, int G, int r0, bool by_row) {
     const int total = nq * nout;
+    if ((256 % nout) == 0 && (nout & 3) == 0) {
+      // nout divides the 256 floats one 16-byte store per lane covers: the
+      // lane's offset y stays fixed and its token advances by 256 / nout per
+      // step.  Four steps' slot reads go out before their stores.
+      const int dqs = 256 / nout, y = (4 * lane) % nout, qb = (4 * lane) / nout;
+      const int steps = (32 * nout + 255) / 256;         // 32 tokens x nout floats, 256 per step
+#pragma unroll
+      for (int k0 = 0; k0 < 32; k0 += 4) {
+        if (k0 >= steps) break;
+        f32x4_t v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int q = qb + (k0 + u) * dqs;
+          const int tq = (int)(q0 % gw) + q;             // token offset from the start of q0's grid row
+          // tq / gw, exact: tq < 2^20 and gw <= 1024 keep the float quotient
+          // far from the next integer (the 0.5 margin)
+          const int drow = (int)(((float)tq + 0.5f) * rcp_gw);
+          const int coord = by_row ? row0 + drow : tq - drow * gw;
+          const float* sp = slot + (q < nq ? q : 0) * TPITCH + coord + G - 1 - r0 - y;
+          v[u] = (f32x4_t){sp[0], sp[-1], sp[-2], sp[-3]};
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int q = qb + (k0 + u) * dqs;
+          if (k0 + u < steps && q < nq) *(f32x4_t*)(out + q * nout + y) = v[u];
+        }
+      }
+      return;
+    }
     const int W = (nout & 3) == 0 ? 4 : 1;
     const int stride = 64 * W;
     int e = W * lane;

@@ -628,7 +628,7 @@ def test_generic_relpos_wave_split(gpu, waves, fused):
     assert max_err(np64(lse), ref["lse"]) <= TOL["fp32"]
 
 
-TERMS_GRIDS = [(14, 14), (64, 64), (40, 24), (5, 27), (16, 64), (9, 96), (3, 100)]
+TERMS_GRIDS = [(14, 14), (64, 64), (40, 24), (5, 27), (16, 64), (9, 96), (3, 100), (8, 32), (4, 32)]
 
 
 @pytest.mark.parametrize("mfma", [1, 0])
@@ -640,8 +640,10 @@ def test_relpos_terms_kernels(gpu, mfma, dtype, D, grid):
     table rows each block needs, skewed read-out through LDS) and on the
     vector ALUs, against the oracle: grids whose 32-token blocks stay in one
     grid row (64 and 96 wide) or span several (14, 24, 27 wide), a ragged last
-    block (5 x 27 = 135 tokens), head_dim 32 / 64 / 128, both layouts, and a
-    100-wide grid that only the vector kernel takes."""
+    block (5 x 27 = 135 tokens), head_dim 32 / 64 / 128, both layouts, a
+    100-wide grid that only the vector kernel takes, and term rows of 4, 8,
+    16, 32 and 64 floats (widths that divide a 256-float store step take the
+    unrolled read-out)."""
     gh, gw = grid
     T, B, H = gh * gw, 2, 3
     layout = "bshd" if (gh + D) % 2 else "bhsd"
