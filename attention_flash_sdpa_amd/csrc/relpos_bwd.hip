@@ -317,6 +317,106 @@ __global__ __launch_bounds__(256) void relpos_tgrad_kernel(BwdParams p, int ipw_
       out[(32 * wave + 8 * (r / 4) + 4 * kh + (r % 4)) * D + 32 * db + (lane & 31)] = acc[db][r];
 }
 
+// Small grids (both sides <= 16: SAM's 14 x 14 windows): the 2G - 1 <= 31
+// gradient rows fit one 32-row block, so each wave takes its own run of lines
+// with its own staging buffers and keeps all of them in its accumulators;
+// the four waves' sums are added in LDS, and the workgroup writes rows
+// 0 .. 31 of its partial.  A line's <= 16 dT rows of
+// <= 16 floats go to LDS four rows per 64-lane copy, its q rows one to four
+// per copy.
+constexpr int kTsRows = 16;                    // line length and table width the small mode takes
+__host__ __device__ inline int ts_buf_bytes(int D) { return kTsRows * 16 * 4 + kTsRows * D * 2; }
+
+template <typename E, int D>
+__global__ __launch_bounds__(256) void relpos_tgrad_small_kernel(BwdParams p, int ipw_h, int ipw_w) {
+  constexpr int DB = D / 32;
+  constexpr int QRB = D * 2;
+  constexpr int QRPI = 256 / QRB;
+  extern __shared__ __attribute__((aligned(16))) char ts_lds[];   // [wave][2 buffers]
+  const bool rows = blockIdx.y == 0;
+  const int gh = p.grid_h, gw = p.grid_w;
+  const int G = rows ? gh : gw, L = rows ? gw : gh;
+  const float* dT = rows ? p.dterm_h : p.dterm_w;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int trow = lane & 31, kh = lane >> 5;
+  const int64_t T = p.Tq;
+  const __amdgpu_buffer_rsrc_t drs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)dT, 0, (int)(p.B * p.Hq * T * G * 4), 0x00020000);
+  const __amdgpu_buffer_rsrc_t qrs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)p.q, 0, (int)(((p.B - 1) * p.q_sb + (p.Hq - 1) * p.q_sh + (T - 1) * p.q_st + D) * 2), 0x00020000);
+  char* mine = ts_lds + wave * 2 * ts_buf_bytes(D);
+  f32x16 acc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) acc[db] = (f32x16){};
+  const int64_t items = p.B * p.Hq * G;
+  const int ipw = rows ? ipw_h : ipw_w;
+  const int64_t wid = (int64_t)blockIdx.x * 4 + wave;
+  const int64_t it0 = wid * ipw, it1 = min(items, it0 + ipw);
+  const int64_t istep = rows ? 1 : gw;
+  auto issue = [&](int64_t it, int buf) {
+    const int64_t bh = it / G;
+    const int line = (int)(it - bh * G);
+    const int bh32 = (int)bh, hq32 = (int)p.Hq;        // B * Hq < 2^16
+    const int64_t b = bh32 / hq32, h = bh32 - (bh32 / hq32) * hq32;
+    const int64_t ibase = rows ? (int64_t)line * gw : (int64_t)line;
+    char* base = mine + buf * ts_buf_bytes(D);
+    // dT rows: lane l -> row 4 c + l / 16, column l % 16 (rows and columns past L, G land in padding)
+#pragma unroll
+    for (int c = 0; c < kTsRows / 4; ++c) {
+      const int qi = 4 * c + lane / 16;
+      const int64_t i = ibase + (qi < L ? qi : 0) * istep;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(drs, (__attribute__((address_space(3))) void*)(base + c * 256), 4,
+                                               (int)(((bh * T + i) * G + (lane % 16)) * 4), 0, 0, 0);
+    }
+    char* qbase = base + kTsRows * 16 * 4;
+#pragma unroll
+    for (int q0 = 0; q0 < kTsRows; q0 += QRPI) {
+      const int qi = q0 + lane / (64 / QRPI);
+      const int64_t i = ibase + (qi < L ? qi : 0) * istep;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          qrs, (__attribute__((address_space(3))) void*)(qbase + q0 * QRB), 4,
+          (int)((b * p.q_sb + h * p.q_sh + i * p.q_st) * 2 + (lane % (64 / QRPI)) * 4), 0, 0, 0);
+    }
+  };
+  if (it0 < it1) issue(it0, 0);
+  for (int64_t it = it0; it < it1; ++it) {
+    const int buf = (int)((it - it0) & 1);
+    const int line = (int)(it - (it / G) * G);
+    __builtin_amdgcn_s_waitcnt(0);                    // this line's rows are in LDS (copies of this wave only)
+    wave_sync();                                      // and the wave's reads of the other buffer are done
+    if (it + 1 < it1) issue(it + 1, buf ^ 1);
+    const float* dts = (const float*)(mine + buf * ts_buf_bytes(D));
+    const E* qs = (const E*)(mine + buf * ts_buf_bytes(D) + kTsRows * 16 * 4);
+    const int a = line + G - 1 - trow;
+    const bool aok = a >= 0 && a < G;
+    const float* ar = dts + (aok ? a : 0) + kh * 16;
+    const E* br = qs + (lane & 31) + kh * D;
+    for (int k0 = 0; k0 < L; k0 += 2) {
+      const bool qok = k0 + kh < L;
+      const float av = (aok && qok) ? ar[k0 * 16] : 0.0f;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const float bv = qok ? (float)br[k0 * D + 32 * db] : 0.0f;
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(av, bv, acc[db], 0, 0, 0);
+      }
+    }
+    wave_sync();                                      // reads of this buffer done before the next issue
+  }
+  // the four waves' sums meet in LDS ([wave][32 rows][D]) and add in wave
+  // order (fixed); the workgroup's partial is rows 0 .. 31 of its 128-row slot
+  __syncthreads();                                    // every wave is done with its staging buffers
+  float* red = (float*)ts_lds;
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      red[(wave * 32 + 8 * (r / 4) + 4 * kh + (r % 4)) * D + 32 * db + (lane & 31)] = acc[db][r];
+  __syncthreads();
+  float* out = (rows ? p.group_h : p.group_w) + (int64_t)blockIdx.x * 128 * D;
+  for (int e = tid; e < 32 * D; e += 256)
+    out[e] = ((red[e] + red[32 * D + e]) + red[2 * 32 * D + e]) + red[3 * 32 * D + e];
+}
+
 // dR[t][d] = sum over the nwg workgroups' partial sums: thread (g, d) of a
 // workgroup adds the partials w = g, g + 4, ... of entry (t, d) for 64 head
 // dims (a wave reads 256 contiguous bytes of one partial row), then the four
@@ -333,9 +433,13 @@ __global__ __launch_bounds__(256) void relpos_tgrad_reduce_kernel(BwdParams p, i
   float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
   if (d < D) {
     int w = g;
-    for (; w + 12 < nwg; w += 16)                      // four loads in flight, each its own sum
+    for (; w + 28 < nwg; w += 32) {                    // eight loads in flight, into four sums
+      float v[8];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) acc[u] += part[((int64_t)(w + 4 * u) * 128 + t) * D + d];
+      for (int u = 0; u < 8; ++u) v[u] = part[((int64_t)(w + 4 * u) * 128 + t) * D + d];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) acc[u & 3] += v[u];
+    }
     for (; w < nwg; w += 4) acc[0] += part[((int64_t)w * 128 + t) * D + d];
   }
   red[g][dd] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
@@ -353,6 +457,9 @@ __global__ __launch_bounds__(256) void relpos_tgrad_reduce_kernel(BwdParams p, i
 // into the fp32 dQ_acc; pass !ROWS adds the term_w part and writes dq.  One
 // workgroup per (batch, head, line); wave w owns output blocks w and w + 4 of
 // the [L (<= 64) queries x D] result (32 x 32 blocks, query blocks outer).
+// LDS bytes of one line: dT rows [L][kDqGP] fp32 and table rows [G rounded up to 4][D].
+__host__ __device__ inline int dq_lds_bytes(int L, int G, int D) { return L * kDqGP * 4 + (G + 3) / 4 * 4 * D * 2; }
+
 template <typename E, int D, typename GT, bool ROWS>
 __global__ __launch_bounds__(256) void relpos_dq_mfma_kernel(BwdParams p) {
   constexpr int DB = D / 32;
@@ -362,17 +469,24 @@ __global__ __launch_bounds__(256) void relpos_dq_mfma_kernel(BwdParams p) {
   const int gh = p.grid_h, gw = p.grid_w;
   const int G = ROWS ? gh : gw, L = ROWS ? gw : gh;
   const int MB = (L + 31) / 32;
-  // dT rows of the line's queries [L][kDqGP] fp32 (odd stride: the 32 query
+  // Lines with fewer than four 32 x 32 output blocks share a workgroup: ipg
+  // lines, wpi = 4 / ipg waves each (wave sub-index wv).
+  const int nblk = MB * DB, ipg = nblk >= 4 ? 1 : 4 / nblk, wpi = 4 / ipg;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int sub = wave / wpi, wv = wave - sub * wpi;
+  const int64_t item = (int64_t)blockIdx.x * ipg + sub;
+  const bool have = item < p.B * p.Hq * G;
+  // Per line: dT rows of its queries [L][kDqGP] fp32 (odd stride: the 32 query
   // rows of an A read hit 32 banks), then the reversed table rows
   // tab[a] = R[line + G - 1 - a], [G rounded up to 4][D] in the input type.
-  const float* dts = (const float*)dq_lds;
-  const E* tab = (const E*)(dq_lds + L * kDqGP * 4);
+  char* region = dq_lds + sub * dq_lds_bytes(L, G, D);
+  const float* dts = (const float*)region;
+  const E* tab = (const E*)(region + L * kDqGP * 4);
   const float* dT = ROWS ? p.dterm_h : p.dterm_w;
   const E* R = (const E*)(ROWS ? p.rel_h : p.rel_w);
-  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int kh = lane >> 5, l32 = lane & 31;
-  const int64_t bh = blockIdx.x / G;
-  const int line = (int)(blockIdx.x - bh * G);
+  const int64_t bh = have ? item / G : 0;
+  const int line = (int)(have ? item - bh * G : 0);
   const int bh32 = (int)bh, hq32 = (int)p.Hq;           // B * Hq < 2^16
   const int64_t b = bh32 / hq32, h = bh32 - (bh32 / hq32) * hq32;
   const int64_t T = p.Tq;
@@ -383,11 +497,11 @@ __global__ __launch_bounds__(256) void relpos_dq_mfma_kernel(BwdParams p) {
       __builtin_amdgcn_make_buffer_rsrc((void*)dT, 0, (int)(p.B * p.Hq * T * G * 4), 0x00020000);
   const __amdgpu_buffer_rsrc_t rrs =
       __builtin_amdgcn_make_buffer_rsrc((void*)R, 0, (int)((2 * G - 1) * D * 2), 0x00020000);
-  for (int qi = wave; qi < L; qi += 4)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(drs, (__attribute__((address_space(3))) void*)(dq_lds + qi * kDqGP * 4), 4,
+  for (int qi = have ? wv : L; qi < L; qi += wpi)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(drs, (__attribute__((address_space(3))) void*)(region + qi * kDqGP * 4), 4,
                                              (int)(((bh * T + query(qi)) * G + lane) * 4), 0, 0, 0);
-  char* tbase = dq_lds + L * kDqGP * 4;
-  for (int a0 = wave * QRPI; a0 < G; a0 += 4 * QRPI) {
+  char* tbase = region + L * kDqGP * 4;
+  for (int a0 = have ? wv * QRPI : G; a0 < G; a0 += wpi * QRPI) {
     const int a = a0 + lane / (64 / QRPI);
     const int ra = line + G - 1 - (a < G ? a : a0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rrs, (__attribute__((address_space(3))) void*)(tbase + a0 * QRB), 4,
@@ -400,18 +514,18 @@ __global__ __launch_bounds__(256) void relpos_dq_mfma_kernel(BwdParams p) {
   float pre[2][16];
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
-    const int blk = wave + 4 * u;
+    const int blk = wv + wpi * u;
     const int mb = blk / DB, db = blk - mb * DB;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int qi = 32 * mb + 8 * (r / 4) + 4 * kh + (r % 4);
-      pre[u][r] = (blk < MB * DB && qi < L) ? p.dq_acc[(bh * T + query(qi)) * D + 32 * db + l32] : 0.0f;
+      pre[u][r] = (have && blk < nblk && qi < L) ? p.dq_acc[(bh * T + query(qi)) * D + 32 * db + l32] : 0.0f;
     }
   }
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
-    const int blk = wave + 4 * u;
-    if (blk >= MB * DB) break;
+    const int blk = wv + wpi * u;
+    if (!have || blk >= nblk) break;
     const int mb = blk / DB, db = blk - mb * DB;
     const int qrow = 32 * mb + l32;
     const bool qok = qrow < L;
@@ -448,8 +562,6 @@ __global__ __launch_bounds__(256) void relpos_dq_mfma_kernel(BwdParams p) {
   }
 }
 
-__host__ __device__ inline int dq_lds_bytes(int L, int G, int D) { return L * kDqGP * 4 + (G + 3) / 4 * 4 * D * 2; }
-
 template <int D>
 bool relpos_dq_mfma_ok(const BwdParams& p) {
   const int64_t gh = p.grid_h, gw = p.grid_w;
@@ -460,12 +572,14 @@ bool relpos_dq_mfma_ok(const BwdParams& p) {
 template <typename E, int D, typename G>
 void tail_typed(const BwdParams& p, hipStream_t s) {
   if (p.tgrad_mfma && relpos_dq_mfma_ok<D>(p)) {
-    const size_t lh = dq_lds_bytes(p.grid_w, p.grid_h, D);
-    const size_t lw = dq_lds_bytes(p.grid_h, p.grid_w, D);
-    hipLaunchKernelGGL((relpos_dq_mfma_kernel<E, D, G, true>), dim3((unsigned)(p.B * p.Hq * p.grid_h)), dim3(256), lh,
-                       s, p);
-    hipLaunchKernelGGL((relpos_dq_mfma_kernel<E, D, G, false>), dim3((unsigned)(p.B * p.Hq * p.grid_w)), dim3(256), lw,
-                       s, p);
+    // lines per workgroup as the kernel derives them: 4 / (32 x 32 output blocks per line), at least 1
+    auto ipg = [](int L) { const int nb = (L + 31) / 32 * (D / 32); return nb >= 4 ? 1 : 4 / nb; };
+    const int ih = ipg(p.grid_w), iw = ipg(p.grid_h);
+    const int64_t nh = p.B * p.Hq * p.grid_h, nw = p.B * p.Hq * p.grid_w;
+    hipLaunchKernelGGL((relpos_dq_mfma_kernel<E, D, G, true>), dim3((unsigned)((nh + ih - 1) / ih)), dim3(256),
+                       (size_t)ih * dq_lds_bytes(p.grid_w, p.grid_h, D), s, p);
+    hipLaunchKernelGGL((relpos_dq_mfma_kernel<E, D, G, false>), dim3((unsigned)((nw + iw - 1) / iw)), dim3(256),
+                       (size_t)iw * dq_lds_bytes(p.grid_h, p.grid_w, D), s, p);
   } else {
     constexpr int QPB = 256 / (D / 16);
     dim3 gq((unsigned)((p.Tq + QPB - 1) / QPB), (unsigned)(p.B * p.Hq));
@@ -474,10 +588,19 @@ void tail_typed(const BwdParams& p, hipStream_t s) {
   if (relpos_tgrad_mfma_ok(p.B, p.Hq, p.grid_h, p.grid_w, D) && p.tgrad_mfma) {
     const int nwg = relpos_tgrad_wgs(p.B, p.Hq, p.grid_h, p.grid_w);
     const int64_t ih = p.B * p.Hq * p.grid_h, iw = p.B * p.Hq * p.grid_w;
+    const int tmax = 2 * (p.grid_h > p.grid_w ? p.grid_h : p.grid_w) - 1;
+    if (p.grid_h <= kTsRows && p.grid_w <= kTsRows) {
+      const int nw = 4 * nwg;                         // waves, each with its own run of lines
+      const size_t lds = std::max((size_t)(4 * 2 * ts_buf_bytes(D)), (size_t)(4 * 32 * D * 4));
+      hipLaunchKernelGGL((relpos_tgrad_small_kernel<E, D>), dim3((unsigned)nwg, 2u), dim3(256), lds, s, p,
+                         (int)((ih + nw - 1) / nw), (int)((iw + nw - 1) / nw));
+      hipLaunchKernelGGL(relpos_tgrad_reduce_kernel, dim3((unsigned)tmax, (unsigned)((D + 63) / 64), 2u), dim3(256),
+                         0, s, p, nwg, D);
+      return;
+    }
     const size_t lds = 2 * (size_t)std::max(tg_buf_bytes(p.grid_w, D), tg_buf_bytes(p.grid_h, D));
     hipLaunchKernelGGL((relpos_tgrad_kernel<E, D>), dim3((unsigned)nwg, 2u), dim3(256), lds, s, p,
                        (int)((ih + nwg - 1) / nwg), (int)((iw + nwg - 1) / nwg));
-    const int tmax = 2 * (p.grid_h > p.grid_w ? p.grid_h : p.grid_w) - 1;
     hipLaunchKernelGGL(relpos_tgrad_reduce_kernel, dim3((unsigned)tmax, (unsigned)((D + 63) / 64), 2u), dim3(256), 0,
                        s, p, nwg, D);
     return;
