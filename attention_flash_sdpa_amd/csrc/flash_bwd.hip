@@ -550,8 +550,13 @@ __global__ __launch_bounds__(256, (D == 128 ? 1 : 2)) void bwd_dkdv_kernel(BwdPa
 // RPS (rel-pos grids of at most 32 x 32): the per-query sums of dS over grid rows and
 // columns are matrix products, dT_h^T = E_h^T . dS^T with E_h[key][y] = 1 iff key lies in
 // grid row y (E_w alike), fed the same packed dS as the dQ product; no LDS sums.
+// Two waves per SIMD, also at head_dim 128 with no mask or an index mask and
+// no dropout (the dQ accumulator, Q and dO fragments fit 256 registers with a
+// few spills; the second wave hides the per-tile latencies: gqa_causal
+// backward 3.06 -> 2.82 ms); the other head_dim-128 instances need more.
 template <typename E, int D, int MODE, bool DROP, typename G, bool RPS = false>
-__global__ __launch_bounds__(256, (D == 128 ? 1 : 2)) void bwd_dq_kernel(BwdParams p) {
+__global__ __launch_bounds__(256, (D == 128 && (DROP || !(MODE == B_NONE || MODE == B_INDEX)) ? 1 : 2))
+void bwd_dq_kernel(BwdParams p) {
   using C = BCfg<D>;
   constexpr int BN = 64;                           // keys per staged tile
   constexpr int TK = BN * C::PITCH;
