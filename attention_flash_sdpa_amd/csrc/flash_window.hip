@@ -25,6 +25,14 @@
 //     in LDS and each tile reads its two values.
 // The terms come from two 32 x 32 x 64 products per wave, Q . Rh^T and
 // Q . Rw^T over all 27 table rows, followed by a skewed gather through LDS.
+//
+// Placement.  Up to 256 (window, head) items, or more than 320, run one
+// workgroup of seven waves per item.  In between (SAM's 25 windows x 12
+// heads = 300), one workgroup per CU takes a whole item plus at most two query
+// blocks of one of the items past the first 256, with both items' K and V in
+// LDS.  Otherwise 44 CUs would run two whole items each and set the time.
+// Every wave computes exactly as in the one-item launch, so the results are
+// bitwise the same.
 #include "common.h"
 #include "elem16.h"
 
@@ -57,9 +65,12 @@ constexpr int PIECES = ROWS * ROWB / 1024; // 1 KB copy pieces per tensor
 static_assert(G % RPT == 0 && RPT <= 4, "tile = whole grid rows, at most 4");
 static_assert(ROWS * ROWB % 1024 == 0, "copy pieces of 64 lanes x 16 B");
 
-__shared__ __attribute__((aligned(16))) char fw_k[ROWS * ROWB];
-__shared__ __attribute__((aligned(16))) char fw_v[ROWS * ROWB];
-__shared__ __attribute__((aligned(16))) float fw_sc[NW * 32 * 32];    // per-wave [table row][query]
+// Balanced launches: one workgroup per CU, each holding one whole (window,
+// head) and up to two query blocks of one of the rest (see launch_window).
+constexpr int CUS = 256;              // compute units of the GPU
+constexpr int XNW = NW + 2;           // waves of a balanced workgroup
+constexpr int XCHUNKS = 4;            // query-block chunks of an extra (window, head): 2, 2, 2, 1 blocks
+static_assert(2 * (XCHUNKS - 1) + 1 == NW, "chunks cover the query blocks");
 
 __device__ __forceinline__ int kswz(int r) { return (r >> 1) & 7; }
 __device__ __forceinline__ int vswz(int r) { return ((r >> 1) & 1) << 2; }
@@ -79,39 +90,65 @@ __device__ __forceinline__ float pair_sum(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <typename E, bool OUT16>
-__global__ __launch_bounds__(NW * 64, 4) void flash_window_kernel(FwdParams p) {
+// XTRA = false: one workgroup of NW waves per (window, head), wave w taking
+// query block w.  XTRA = true (balanced): CUS workgroups of XNW waves;
+// workgroup j holds (window, head) j whole in waves 0..NW-1 and, for
+// j < XCHUNKS * (B * H - CUS), chunk j % XCHUNKS of (window, head)
+// CUS + j / XCHUNKS in waves NW, NW + 1 (blocks 2c, 2c + 1; the last chunk is
+// block NW - 1 alone), each (window, head) in its own K / V slot.
+template <typename E, bool OUT16, bool XTRA>
+__global__ __launch_bounds__((XTRA ? XNW : NW) * 64, (XTRA ? 1 : 4)) void flash_window_kernel(FwdParams p) {
   typedef typename Vec16<E>::x8 e8;
   typedef typename Vec16<E>::x4 e4;
   typedef typename Vec16<E>::x2 e2;
-  lds_char* const ks = (lds_char*)fw_k;
-  lds_char* const vs = (lds_char*)fw_v;
+  constexpr int WAVES = XTRA ? XNW : NW;
+  constexpr int SLOTS = XTRA ? 2 : 1;
+  __shared__ __attribute__((aligned(16))) char fw_k[SLOTS * ROWS * ROWB];
+  __shared__ __attribute__((aligned(16))) char fw_v[SLOTS * ROWS * ROWB];
+  __shared__ __attribute__((aligned(16))) float fw_sc[WAVES * 32 * 32];    // per-wave [table row][query]
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, ql = lane & 31;
-  const int64_t b = blockIdx.x / p.Hq, h = blockIdx.x % p.Hq;
+  // (window, head) items of the workgroup's K / V slots, and this wave's slot and query block
+  const int64_t nitem = p.B * p.Hq;
+  const int64_t item0 = blockIdx.x;
+  const int64_t item1 = XTRA ? CUS + blockIdx.x / XCHUNKS : -1;
+  const bool has1 = XTRA && item1 < nitem;
+  const int chunk = XTRA ? (int)(blockIdx.x % XCHUNKS) : 0;
+  const int slot = (XTRA && wave >= NW) ? 1 : 0;
+  const int qb = slot ? 2 * chunk + (wave - NW) : wave;
+  const bool active = slot == 0 || (has1 && qb < NW);
+  const int64_t item = (slot && has1) ? item1 : item0;   // an unused wave reads its workgroup's first item
+  const int64_t b = item / p.Hq, h = item % p.Hq;
+  lds_char* const ks = (lds_char*)fw_k + slot * (ROWS * ROWB);
+  lds_char* const vs = (lds_char*)fw_v + slot * (ROWS * ROWB);
 
-  // ---- K and V of the window into LDS (rows past the window read as zero)
+  // ---- K and V of the window(s) into LDS (rows past the window read as zero)
   {
     const int rstride = (int)(p.k_st * 2);
     const int nrec = (int)(((int64_t)(T - 1) * p.k_st + 64) * 2);
-    const char* kb = (const char*)((const E*)p.k + b * p.k_sb + h * p.k_sh);
-    const char* vb = (const char*)((const E*)p.v + b * p.k_sb + h * p.k_sh);
-    const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)kb, 0, nrec, 0x00020000);
-    const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)vb, 0, nrec, 0x00020000);
-    for (int pc = wave; pc < PIECES; pc += NW) {
-      const int L = 64 * pc + lane, row = L >> 3, pos = L & 7;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (__attribute__((address_space(3))) void*)(ks + 1024 * pc), 16,
+    // element offsets of the slots' (batch, head) rows
+    const int64_t off0 = (item0 / p.Hq) * p.k_sb + (item0 % p.Hq) * p.k_sh;
+    const int64_t off1 = has1 ? (item1 / p.Hq) * p.k_sb + (item1 % p.Hq) * p.k_sh : off0;
+    for (int pc = wave; pc < PIECES * (has1 ? 2 : 1); pc += WAVES) {
+      const int sl = pc >= PIECES ? 1 : 0, pp = pc - sl * PIECES;
+      const int64_t off = sl ? off1 : off0;
+      const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)((const E*)p.k + off), 0, nrec, 0x00020000);
+      const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)((const E*)p.v + off), 0, nrec, 0x00020000);
+      const int L = 64 * pp + lane, row = L >> 3, pos = L & 7;
+      lds_char* const kd = (lds_char*)fw_k + sl * (ROWS * ROWB) + 1024 * pp;
+      lds_char* const vd = (lds_char*)fw_v + sl * (ROWS * ROWB) + 1024 * pp;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (__attribute__((address_space(3))) void*)kd, 16,
                                                row * rstride + ((pos ^ kswz(row)) << 4), 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (__attribute__((address_space(3))) void*)(vs + 1024 * pc), 16,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (__attribute__((address_space(3))) void*)vd, 16,
                                                row * rstride + ((pos ^ vswz(row)) << 4), 0, 0, 0);
     }
   }
 
   // ---- queries of this wave, and the rel-pos table rows as matrix operands
   // (all issued together: one memory round trip; table rows past 2G-1 are zeroed)
-  const int qrow = 32 * wave + ql;
-  const bool qvalid = qrow < T;
+  const int qrow = 32 * qb + ql;
+  const bool qvalid = active && qrow < T;
   const int qs = qvalid ? qrow : T - 1;
   const int ih = qs / G, iw = qs % G;
   const E* qp = (const E*)p.q + b * p.q_sb + h * p.q_sh + (int64_t)qs * p.q_st + 8 * g;
@@ -170,6 +207,7 @@ __global__ __launch_bounds__(NW * 64, 4) void flash_window_kernel(FwdParams p) {
   }
   __builtin_amdgcn_s_waitcnt(0);        // this wave's copies have landed
   __syncthreads();                      // ... and every other wave's
+  if (!active) return;                  // a balanced workgroup's unused wave (no barrier follows)
 
   const int j16 = lane & 15, dh = (lane >> 4) & 1;
   f32x16 o[2] = {(f32x16){}, (f32x16){}};
@@ -278,14 +316,26 @@ bool window_supports(const FwdParams& p) {
          p.B * p.Hq <= 0x7fffffffLL && (int64_t)T * p.k_st * 2 <= 0x7fffffffLL;
 }
 
+// More (window, head) items than CUs but at most CUS + CUS / XCHUNKS: the
+// balanced launch (one workgroup per CU; the items past the first CUS are
+// spread over the workgroups in chunks of at most two query blocks), so no CU
+// runs two whole items.  Otherwise one workgroup per item.
+template <typename E, bool OUT16>
+void launch_window_e(const FwdParams& p, hipStream_t s) {
+  const int64_t nitem = p.B * p.Hq;
+  if (nitem > CUS && nitem <= CUS + CUS / XCHUNKS)
+    hipLaunchKernelGGL((flash_window_kernel<E, OUT16, true>), dim3(CUS), dim3(XNW * 64), 0, s, p);
+  else
+    hipLaunchKernelGGL((flash_window_kernel<E, OUT16, false>), dim3((unsigned)nitem), dim3(NW * 64), 0, s, p);
+}
+
 hipError_t launch_window(const FwdParams& p, hipStream_t s) {
-  const dim3 grid((unsigned)(p.B * p.Hq));
   if (p.dtype == 2) {
-    if (p.out_dtype != 0) hipLaunchKernelGGL((flash_window_kernel<_Float16, true>), grid, dim3(NW * 64), 0, s, p);
-    else hipLaunchKernelGGL((flash_window_kernel<_Float16, false>), grid, dim3(NW * 64), 0, s, p);
+    if (p.out_dtype != 0) launch_window_e<_Float16, true>(p, s);
+    else launch_window_e<_Float16, false>(p, s);
   } else {
-    if (p.out_dtype != 0) hipLaunchKernelGGL((flash_window_kernel<__bf16, true>), grid, dim3(NW * 64), 0, s, p);
-    else hipLaunchKernelGGL((flash_window_kernel<__bf16, false>), grid, dim3(NW * 64), 0, s, p);
+    if (p.out_dtype != 0) launch_window_e<__bf16, true>(p, s);
+    else launch_window_e<__bf16, false>(p, s);
   }
   return hipGetLastError();
 }
