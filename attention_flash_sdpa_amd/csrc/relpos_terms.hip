@@ -29,6 +29,11 @@ namespace sdpa {
 namespace {
 constexpr int TRMAX = 128;            // table rows one 32-token block's products cover at most
 constexpr int TPITCH = TRMAX + 4;     // slot pitch (floats): 16-byte aligned rows, consecutive tokens four banks apart
+// Waves per workgroup of the matrix-core kernel.  The waves share nothing, so
+// one-wave workgroups (17 KB of LDS each) let the dispatcher spread the waves
+// evenly over the CUs: 1536 waves of SAM ViT-B global attention land 6 per CU
+// instead of 4 or 8 in 384 workgroups of four.
+constexpr int TWPB = 1;
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
@@ -40,13 +45,13 @@ __host__ __device__ inline int terms_rows_w(int gw) { return gw % 32 == 0 ? 31 +
 }  // namespace
 
 template <typename E, int NC>
-__global__ __launch_bounds__(256) void relpos_terms_mfma_kernel(TermsParams p) {
+__global__ __launch_bounds__(64 * TWPB) void relpos_terms_mfma_kernel(TermsParams p) {
   typedef typename Vec16<E>::x8 e8;
-  __shared__ __attribute__((aligned(16))) float slots[4][32 * TPITCH];
+  __shared__ __attribute__((aligned(16))) float slots[TWPB][32 * TPITCH];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 5, ql = lane & 31;
   const int64_t b = blockIdx.z, h = blockIdx.y;
-  const int64_t q0 = ((int64_t)blockIdx.x * 4 + wave) * 32;
+  const int64_t q0 = ((int64_t)blockIdx.x * TWPB + wave) * 32;
   if (q0 >= p.T) return;                      // whole wave; no workgroup barrier below
   const int gh = p.grid_h, gw = p.grid_w, D = (int)p.D;
   const int nq = (int)(p.T - q0 < 32 ? p.T - q0 : 32);
@@ -291,15 +296,15 @@ static bool terms_mfma_ok(const TermsParams& p) {
   if (terms_rows_h(p.grid_h, p.grid_w) > TRMAX || terms_rows_w(p.grid_w) > TRMAX) return false;
   if ((p.q_st % 8) != 0 || (((uintptr_t)p.q | (uintptr_t)p.rel_h | (uintptr_t)p.rel_w) & 15) != 0) return false;
   if (((uintptr_t)p.term_h | (uintptr_t)p.term_w) & 15) return false;
-  return (p.T + 127) / 128 <= 0x7fffffff && p.H <= 65535 && p.B <= 65535;
+  return (p.T + 32 * TWPB - 1) / (32 * TWPB) <= 0x7fffffff && p.H <= 65535 && p.B <= 65535;
 }
 
 template <typename E>
 static void launch_terms_mfma(const TermsParams& p, hipStream_t s) {
-  dim3 grid((unsigned)((p.T + 127) / 128), (unsigned)p.H, (unsigned)p.B);
-  if (p.D == 32) hipLaunchKernelGGL((relpos_terms_mfma_kernel<E, 2>), grid, dim3(256), 0, s, p);
-  else if (p.D == 64) hipLaunchKernelGGL((relpos_terms_mfma_kernel<E, 4>), grid, dim3(256), 0, s, p);
-  else hipLaunchKernelGGL((relpos_terms_mfma_kernel<E, 8>), grid, dim3(256), 0, s, p);
+  dim3 grid((unsigned)((p.T + 32 * TWPB - 1) / (32 * TWPB)), (unsigned)p.H, (unsigned)p.B);
+  if (p.D == 32) hipLaunchKernelGGL((relpos_terms_mfma_kernel<E, 2>), grid, dim3(64 * TWPB), 0, s, p);
+  else if (p.D == 64) hipLaunchKernelGGL((relpos_terms_mfma_kernel<E, 4>), grid, dim3(64 * TWPB), 0, s, p);
+  else hipLaunchKernelGGL((relpos_terms_mfma_kernel<E, 8>), grid, dim3(64 * TWPB), 0, s, p);
 }
 
 hipError_t launch_relpos_terms(const TermsParams& p, hipStream_t s) {
