@@ -152,33 +152,36 @@ def test_windowed_equals_independent_windows(gpu):
     assert max_err(np64(o[24, :, 195]), np64(last)) <= 1e-3
 
 
-@pytest.mark.parametrize("B", [22, 26, 27])
-def test_window_balanced_launch(gpu, B):
+@pytest.mark.parametrize("B,dtype,layout", [(22, "bf16", "bhsd"), (26, "bf16", "bhsd"), (27, "bf16", "bhsd"),
+                                            (26, "fp16", "bshd")])
+def test_window_balanced_launch(gpu, B, dtype, layout):
     """More (window, head) items than CUs: 264 and 312 items take the balanced
     launch (one workgroup per CU, the items past the first 256 spread over the
     workgroups two query blocks at a time), 324 the one-workgroup-per-item
     launch.  Every window's output equals that window computed alone (one
     workgroup per item, the same per-wave arithmetic), and sampled rows match
-    the oracle."""
+    the oracle; also in fp16 and the bshd layout."""
     from parity_util import rows_of, sample_picks
-    wl = workloads.WORKLOADS["sam_window_relpos"].with_(B=B, window_image=None)
+    wl = workloads.WORKLOADS["sam_window_relpos"].with_(B=B, window_image=None, dtype=dtype, layout=layout)
     x = workloads.generate(wl, seed=B)
     g = {k_: t.cuda() for k_, t in x.items()}
-    o, lse = gpu.sdpa_relpos(g["q"], g["k"], g["v"], g["rel_pos_h"], g["rel_pos_w"], wl.grid, scale=wl.scale,
-                             out_dtype=torch.float32, return_lse=True)
+    o, lse = gpu.sdpa_relpos(g["q"], g["k"], g["v"], g["rel_pos_h"], g["rel_pos_w"], wl.grid, layout=layout,
+                             scale=wl.scale, out_dtype=torch.float32, return_lse=True)
     torch.cuda.synchronize()
     assert gpu.last_kernel() == "flash_window_kernel"
     for wdx in sorted({0, 1, B // 2, B - 2, B - 1}):
         s = slice(wdx, wdx + 1)
         o1 = gpu.sdpa_relpos(g["q"][s].contiguous(), g["k"][s].contiguous(), g["v"][s].contiguous(),
-                             g["rel_pos_h"], g["rel_pos_w"], wl.grid, scale=wl.scale, out_dtype=torch.float32)
+                             g["rel_pos_h"], g["rel_pos_w"], wl.grid, layout=layout, scale=wl.scale,
+                             out_dtype=torch.float32)
         assert torch.equal(o1, o[s]), wdx
     picks = sample_picks(wl, n_random=24, seed=B)
     picks += [(b, h, i) for b in (B - 1, B - 2) for h in (0, 11) for i in (0, 100, 191, 192, 195)]
     rp = {"rel_pos_h": np64(x["rel_pos_h"]), "rel_pos_w": np64(x["rel_pos_w"]), "grid": wl.grid}
-    ro, rl = oracle.sdpa_rows(np64(x["q"]), np64(x["k"]), np64(x["v"]), picks, scale=wl.scale, rel_pos=rp)
-    assert max_err(np64(rows_of(o, picks, "bhsd")), ro) <= TOL["bf16"]
-    assert max_err(np64(torch.stack([lse[b, h, i] for b, h, i in picks])), rl) <= TOL["bf16"]
+    ro, rl = oracle.sdpa_rows(np64(x["q"]), np64(x["k"]), np64(x["v"]), picks, layout=layout, scale=wl.scale,
+                              rel_pos=rp)
+    assert max_err(np64(rows_of(o, picks, layout)), ro) <= TOL[dtype]
+    assert max_err(np64(torch.stack([lse[b, h, i] for b, h, i in picks])), rl) <= TOL[dtype]
 
 
 def test_first_causal_row_is_v0(gpu):
