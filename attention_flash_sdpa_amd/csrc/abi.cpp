@@ -28,6 +28,7 @@ std::atomic<int64_t> g_tiled{1};
 std::atomic<int64_t> g_generic_waves{0};
 std::atomic<int64_t> g_relpos_mfma{1};
 std::atomic<int64_t> g_tgrad_mfma{1};
+std::atomic<int64_t> g_bwd_concurrent{1};
 
 // The tuning knobs as one call sees them: read once at the call's start, so
 // the route, the split count and the workspace check of that call agree even
@@ -599,6 +600,7 @@ int sdpa_bwd(const void* q, const void* k, const void* v, const void* o, const v
   if (!workspace || workspace_bytes < need)
     return fail(SDPA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : (size_t)0);
   p.delta = (float*)workspace;
+  p.concurrent = g_bwd_concurrent.load() != 0;
   hipError_t e = sdpa::launch_bwd(p, (hipStream_t)stream);
   if (e != hipSuccess) return fail(SDPA_ERR_HIP, "backward launch failed: %s", hipGetErrorString(e));
   g_last_kernel = "bwd_dkdv_kernel";
@@ -699,6 +701,7 @@ int relpos_bwd_impl(const void* q, const void* k, const void* v, const void* o, 
   p.split_h = sdpa::relpos_group_splits(B * H * grid_w, grid_h);
   p.split_w = sdpa::relpos_group_splits(B * H * grid_h, grid_w);
   p.tgrad_mfma = g_tgrad_mfma.load() != 0;
+  p.concurrent = g_bwd_concurrent.load() != 0;
   st = relpos_terms(q, dtype, layout, B, H, grid_h, grid_w, D, rel_pos_h, rel_pos_w, th, tw, stream);
   if (st) return st;
   hipError_t e = sdpa::launch_bwd(p, (hipStream_t)stream);
@@ -805,6 +808,11 @@ int sdpa_set_tuning(const char* key, int64_t value) {
   if (!std::strcmp(key, "relpos_bwd_mfma")) {
     if (value != 0 && value != 1) return fail(SDPA_ERR_INVALID, "relpos_bwd_mfma must be 0 or 1");
     g_tgrad_mfma.store(value);
+    return SDPA_OK;
+  }
+  if (!std::strcmp(key, "bwd_concurrent")) {
+    if (value != 0 && value != 1) return fail(SDPA_ERR_INVALID, "bwd_concurrent must be 0 or 1");
+    g_bwd_concurrent.store(value);
     return SDPA_OK;
   }
   if (!std::strcmp(key, "generic_waves")) {

@@ -37,6 +37,9 @@
 #include "common.h"
 #include "elem16.h"
 
+#include <algorithm>
+#include <mutex>
+
 namespace sdpa {
 namespace {
 
@@ -955,49 +958,126 @@ int bmode_of(const BwdParams& p) {
   }
 }
 
+// The second stream of the current device for the dQ kernel (created on first
+// use, default priority, not synchronising with the null stream) and the
+// device's compute-unit count; a null stream when none is available.  A
+// stream is not created while the caller's stream is being captured into a
+// graph.
+struct SideStream {
+  hipStream_t stream;
+  int cus;
+};
+
+SideStream side_stream(hipStream_t caller) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static SideStream per_dev[kMaxDevices] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return {nullptr, 0};
+  std::lock_guard<std::mutex> lock(mu);
+  SideStream& d = per_dev[dev];
+  if (!d.stream) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(caller, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return {nullptr, 0};
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      return {nullptr, 0};
+    hipStream_t st = nullptr;
+    if (hipStreamCreateWithFlags(&st, hipStreamNonBlocking) != hipSuccess) return {nullptr, 0};
+    d = {st, cus};
+  }
+  return d;
+}
+
+// dK/dV and dQ.  The two kernels read the same inputs and delta and write
+// disjoint outputs, so with p.concurrent the dQ kernel can run on the
+// device's second stream beside the dK/dV kernel: the workgroups of each
+// then fill CUs the other leaves idle.  That pays when both grids are short,
+// at most two rounds of the workgroups the chip holds at once (SAM ViT-B
+// global attention at batch 1 runs 384 + 384 workgroups where 512 fit; its
+// 14x14 windows 600 + 600).  Longer grids leave little tail to fill and run
+// one after the other, which keeps each kernel's workgroups together in the
+// caches.  An event forks the second stream from the caller's after delta,
+// another joins it back, so work queued later on the caller's stream sees
+// dq.  Returns the first HIP error.
 template <typename E, int D, int MODE, bool DROP, typename G, bool RPS = false>
-void launch_main(const BwdParams& p, hipStream_t s) {
+hipError_t launch_main(const BwdParams& p, hipStream_t s) {
   dim3 gkv((unsigned)((p.Tkv + 127) / 128), (unsigned)p.Hkv, (unsigned)p.B);
-  hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, MODE, DROP, G>), gkv, dim3(256), 0, s, p);
   dim3 gq((unsigned)((p.Tq + 127) / 128), (unsigned)p.Hq, (unsigned)p.B);
-  hipLaunchKernelGGL((bwd_dq_kernel<E, D, MODE, DROP, G, RPS>), gq, dim3(256), 0, s, p);
+  hipStream_t side = nullptr;
+  if (p.concurrent) {
+    const SideStream ss = side_stream(s);
+    const int64_t resident = (int64_t)ss.cus * (D == 128 ? 1 : 2);       // workgroups per CU at these launch bounds
+    const int64_t longest = std::max<int64_t>((int64_t)gkv.x * gkv.y * gkv.z, (int64_t)gq.x * gq.y * gq.z);
+    if (ss.stream && longest <= 2 * resident) side = ss.stream;
+  }
+  hipEvent_t fork = nullptr, join = nullptr;
+  if (side && hipEventCreateWithFlags(&fork, hipEventDisableTiming) != hipSuccess) side = nullptr;
+  if (side && hipEventCreateWithFlags(&join, hipEventDisableTiming) != hipSuccess) {
+    (void)hipEventDestroy(fork);
+    side = nullptr;
+  }
+  if (side) {
+    hipError_t e = hipEventRecord(fork, s);
+    if (e == hipSuccess) e = hipStreamWaitEvent(side, fork, 0);
+    if (e != hipSuccess) {                 // nothing launched yet: run both on the caller's stream
+      (void)hipEventDestroy(fork);
+      (void)hipEventDestroy(join);
+      side = nullptr;
+    }
+  }
+  if (!side) {
+    hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, MODE, DROP, G>), gkv, dim3(256), 0, s, p);
+    hipLaunchKernelGGL((bwd_dq_kernel<E, D, MODE, DROP, G, RPS>), gq, dim3(256), 0, s, p);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL((bwd_dq_kernel<E, D, MODE, DROP, G, RPS>), gq, dim3(256), 0, side, p);
+  hipError_t e = hipGetLastError();
+  hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, MODE, DROP, G>), gkv, dim3(256), 0, s, p);
+  const hipError_t e2 = hipGetLastError();
+  if (e == hipSuccess) e = e2;
+  const hipError_t e3 = hipEventRecord(join, side);
+  const hipError_t e4 = e3 == hipSuccess ? hipStreamWaitEvent(s, join, 0) : e3;
+  if (e == hipSuccess) e = e4;
+  (void)hipEventDestroy(fork);
+  (void)hipEventDestroy(join);
+  return e;
 }
 
 template <typename E, int D, typename G>
-void launch_modes(const BwdParams& p, hipStream_t s) {
+hipError_t launch_modes(const BwdParams& p, hipStream_t s) {
   const bool drop = p.keep != nullptr;
   switch (bmode_of(p)) {
-    case B_NONE: drop ? launch_main<E, D, B_NONE, true, G>(p, s) : launch_main<E, D, B_NONE, false, G>(p, s); break;
-    case B_INDEX: drop ? launch_main<E, D, B_INDEX, true, G>(p, s) : launch_main<E, D, B_INDEX, false, G>(p, s); break;
+    case B_NONE: return drop ? launch_main<E, D, B_NONE, true, G>(p, s) : launch_main<E, D, B_NONE, false, G>(p, s);
+    case B_INDEX: return drop ? launch_main<E, D, B_INDEX, true, G>(p, s) : launch_main<E, D, B_INDEX, false, G>(p, s);
     case B_RELPOS:
       if (p.grid_h <= 32 && p.grid_w <= 32) {
-        drop ? launch_main<E, D, B_RELPOS, true, G, true>(p, s) : launch_main<E, D, B_RELPOS, false, G, true>(p, s);
+        return drop ? launch_main<E, D, B_RELPOS, true, G, true>(p, s) : launch_main<E, D, B_RELPOS, false, G, true>(p, s);
       } else {
-        drop ? launch_main<E, D, B_RELPOS, true, G>(p, s) : launch_main<E, D, B_RELPOS, false, G>(p, s);
+        return drop ? launch_main<E, D, B_RELPOS, true, G>(p, s) : launch_main<E, D, B_RELPOS, false, G>(p, s);
       }
-      break;
     case B_RELPOS64:
-      drop ? launch_main<E, D, B_RELPOS64, true, G>(p, s) : launch_main<E, D, B_RELPOS64, false, G>(p, s);
-      break;
-    default: drop ? launch_main<E, D, B_TENSOR, true, G>(p, s) : launch_main<E, D, B_TENSOR, false, G>(p, s); break;
+      return drop ? launch_main<E, D, B_RELPOS64, true, G>(p, s) : launch_main<E, D, B_RELPOS64, false, G>(p, s);
+    default: return drop ? launch_main<E, D, B_TENSOR, true, G>(p, s) : launch_main<E, D, B_TENSOR, false, G>(p, s);
   }
 }
 
 template <typename E, int D>
-void launch_typed(const BwdParams& p, hipStream_t s) {
+hipError_t launch_typed(const BwdParams& p, hipStream_t s) {
   const int64_t rows = p.B * p.Hq * p.Tq;
   const int64_t blocks = (rows * (D / 8) + 255) / 256;
   if (p.o_dtype == 0) hipLaunchKernelGGL((bwd_delta_kernel<E, float, D>), dim3((unsigned)blocks), dim3(256), 0, s, p, rows);
   else hipLaunchKernelGGL((bwd_delta_kernel<E, E, D>), dim3((unsigned)blocks), dim3(256), 0, s, p, rows);
-  if (p.grad_dtype == 0) launch_modes<E, D, float>(p, s);
-  else launch_modes<E, D, E>(p, s);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return p.grad_dtype == 0 ? launch_modes<E, D, float>(p, s) : launch_modes<E, D, E>(p, s);
 }
 
 template <typename E>
-void launch_e(const BwdParams& p, hipStream_t s) {
-  if (p.D == 32) launch_typed<E, 32>(p, s);
-  else if (p.D == 64) launch_typed<E, 64>(p, s);
-  else launch_typed<E, 128>(p, s);
+hipError_t launch_e(const BwdParams& p, hipStream_t s) {
+  if (p.D == 32) return launch_typed<E, 32>(p, s);
+  if (p.D == 64) return launch_typed<E, 64>(p, s);
+  return launch_typed<E, 128>(p, s);
 }
 
 }  // namespace
@@ -1014,9 +1094,7 @@ bool bwd_supports(const BwdParams& p) {
 }
 
 hipError_t launch_bwd(const BwdParams& p, hipStream_t s) {
-  if (p.dtype == 2) launch_e<_Float16>(p, s);
-  else launch_e<__bf16>(p, s);
-  return hipGetLastError();
+  return p.dtype == 2 ? launch_e<_Float16>(p, s) : launch_e<__bf16>(p, s);
 }
 
 }  // namespace sdpa

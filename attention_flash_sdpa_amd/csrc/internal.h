@@ -93,6 +93,7 @@ struct BwdParams {
   int grid_h, grid_w;
   int split_h, split_w;       // query slices of the grouped table products
   int tgrad_mfma;             // table gradients on the matrix cores where the shape allows (1) or not (0)
+  int concurrent;             // dK/dV and dQ kernels on two streams, side by side (1) or in sequence (0)
 };
 
 // Query slices of a grouped table product: about 512 workgroups in all, each

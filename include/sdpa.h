@@ -39,6 +39,9 @@
  *     use Hkv heads.  No input is transposed or copied.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Every call only
  *     enqueues kernels on that stream and returns; it never synchronises.
+ *     The backward calls may also run one kernel on a second stream of the
+ *     device, forked from and joined back into `stream` with events (tuning
+ *     key "bwd_concurrent"), so ordering against `stream` is unchanged.
  *   - Status codes: SDPA_OK (0) or a negative sdpa_status.  Argument errors
  *     are detected before any HIP call is made, so they leave every output
  *     untouched and need no GPU.  sdpa_last_error() gives a thread-local
@@ -242,6 +245,18 @@ const char* sdpa_last_kernel(void);
  *                  gradients and the tables' part of dq on the matrix cores
  *                  where the grid allows it (both sides <= 64); 0 = on the
  *                  vector ALUs.
+ *   "bwd_concurrent" 1 (default) = where both grids of the dK/dV and dQ
+ *                  kernels are short (at most twice the workgroups the
+ *                  device holds at once), the backward calls run them side by
+ *                  side: dQ on a second stream of the device (created once
+ *                  per device, default priority, never while the caller's
+ *                  stream is being captured), forked from and joined back
+ *                  into the caller's stream with events, so later work on
+ *                  the caller's stream still sees every gradient.  The
+ *                  results are the same bit for bit.  Calls on several
+ *                  streams of one device share its second stream, so their
+ *                  dQ kernels run in the order the calls were made.
+ *                  0 = both on the caller's stream, one after the other.
  *   "generic_waves" 0 (default) = the vector-ALU kernel (fp32, and shapes no
  *                  matrix-core kernel takes) splits each 64-row block's keys
  *                  over 4 waves when the launch has fewer blocks than the GPU

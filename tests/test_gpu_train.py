@@ -255,6 +255,52 @@ def test_backward_is_deterministic(gpu):
         assert torch.equal(x, y)
 
 
+BWD_STREAM_CASES = [
+    ("plain", 1, 4, 4, 300, 64, None),
+    ("gqa", 2, 8, 2, 257, 128, None),
+    ("relpos", 2, 3, 3, 256, 64, (16, 16)),
+]
+
+
+@pytest.mark.parametrize("case", BWD_STREAM_CASES, ids=[c[0] for c in BWD_STREAM_CASES])
+def test_backward_concurrent_matches_sequential(gpu, case):
+    """dK/dV and dQ side by side on two streams give the same bits as one after
+    the other, also when the caller works on a stream of its own and uses the
+    gradients there at once (the join must order them before that work)."""
+    name, B, Hq, Hkv, T, D, grid = case
+    rng = np.random.default_rng(44)
+    q, do = (draw(rng, (B, Hq, T, D), torch.bfloat16).cuda() for _ in range(2))
+    k, v = (draw(rng, (B, Hkv, T, D), torch.bfloat16).cuda() for _ in range(2))
+    if grid:
+        rh = (0.3 * draw(rng, (2 * grid[0] - 1, D), torch.float32)).to(torch.bfloat16).cuda()
+        rw = (0.3 * draw(rng, (2 * grid[1] - 1, D), torch.float32)).to(torch.bfloat16).cuda()
+        o, lse = gpu.sdpa_relpos(q, k, v, rh, rw, grid, return_lse=True)
+        call = lambda: gpu.sdpa_relpos_backward(q, k, v, o, do, lse, rh, rw, grid)
+    else:
+        causal = {"kind": "causal", "offset": 0}
+        o, lse = gpu.sdpa(q, k, v, return_lse=True, mask=causal)
+        call = lambda: gpu.sdpa_backward(q, k, v, o, do, lse, mask=causal)
+    torch.cuda.synchronize()
+    outs = {}
+    try:
+        for conc in (0, 1):
+            gpu.set_tuning("bwd_concurrent", conc)
+            outs[conc] = call()
+            torch.cuda.synchronize()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            torch.cuda._sleep(2_000_000)              # the backward queues behind work on this stream
+            got = call()
+            snap = [t.clone() for t in got]          # read on the caller's stream right after the call
+        torch.cuda.synchronize()
+    finally:
+        gpu.set_tuning("bwd_concurrent", 1)
+    for x, y, z in zip(outs[0], outs[1], snap):
+        assert torch.equal(x, y)
+        assert torch.equal(x, z)
+
+
 def test_backward_after_library_forward(gpu):
     """End to end on the GPU: forward with dropout (library keep bits), then the
     backward from the library's own O and lse, against the oracle on the same bits."""
