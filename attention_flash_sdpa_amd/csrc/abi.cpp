@@ -704,8 +704,8 @@ int relpos_bwd_impl(const void* q, const void* k, const void* v, const void* o, 
   p.concurrent = g_bwd_concurrent.load() != 0;
   st = relpos_terms(q, dtype, layout, B, H, grid_h, grid_w, D, rel_pos_h, rel_pos_w, th, tw, stream);
   if (st) return st;
-  hipError_t e = sdpa::launch_bwd(p, (hipStream_t)stream);
-  if (e == hipSuccess) e = sdpa::launch_relpos_bwd_tail(p, (hipStream_t)stream);
+  const hipError_t e =
+      sdpa::launch_bwd(p, (hipStream_t)stream, sdpa::launch_relpos_bwd_dq, sdpa::launch_relpos_bwd_tables);
   if (e != hipSuccess) return fail(SDPA_ERR_HIP, "rel-pos backward launch failed: %s", hipGetErrorString(e));
   g_last_kernel = "bwd_dkdv_kernel";
   return SDPA_OK;

@@ -989,19 +989,23 @@ SideStream side_stream(hipStream_t caller) {
   return d;
 }
 
-// dK/dV and dQ.  The two kernels read the same inputs and delta and write
-// disjoint outputs, so with p.concurrent the dQ kernel can run on the
-// device's second stream beside the dK/dV kernel: the workgroups of each
-// then fill CUs the other leaves idle.  That pays when both grids are short,
-// at most two rounds of the workgroups the chip holds at once (SAM ViT-B
-// global attention at batch 1 runs 384 + 384 workgroups where 512 fit; its
-// 14x14 windows 600 + 600).  Longer grids leave little tail to fill and run
-// one after the other, which keeps each kernel's workgroups together in the
-// caches.  An event forks the second stream from the caller's after delta,
-// another joins it back, so work queued later on the caller's stream sees
-// dq.  Returns the first HIP error.
+// dK/dV and dQ, then two tails that need dq: `tail` on the caller's stream
+// and `side_tail`, independent of `tail`'s outputs (either may be null).
+// The two kernels read the same inputs and delta and write disjoint
+// outputs, so with p.concurrent the dQ kernel can run on the device's
+// second stream beside the dK/dV kernel: the workgroups of each then fill
+// CUs the other leaves idle.  That pays when both grids are short, at most
+// two rounds of the workgroups the chip holds at once (SAM ViT-B global
+// attention at batch 1 runs 384 + 384 workgroups where 512 fit; its 14x14
+// windows 600 + 600).  Longer grids leave little tail to fill and run one
+// after the other, which keeps each kernel's workgroups together in the
+// caches.  Side by side, an event forks the second stream from the caller's
+// after delta; `side_tail` follows dQ there, while `tail` runs on the
+// caller's stream once dQ (a second event) and dK/dV are done, and a third
+// event joins the second stream back, so work queued later on the caller's
+// stream sees every output.  Returns the first HIP error.
 template <typename E, int D, int MODE, bool DROP, typename G, bool RPS = false>
-hipError_t launch_main(const BwdParams& p, hipStream_t s) {
+hipError_t launch_main(const BwdParams& p, hipStream_t s, BwdTail tail, BwdTail side_tail) {
   dim3 gkv((unsigned)((p.Tkv + 127) / 128), (unsigned)p.Hkv, (unsigned)p.B);
   dim3 gq((unsigned)((p.Tq + 127) / 128), (unsigned)p.Hq, (unsigned)p.B);
   hipStream_t side = nullptr;
@@ -1011,73 +1015,79 @@ hipError_t launch_main(const BwdParams& p, hipStream_t s) {
     const int64_t longest = std::max<int64_t>((int64_t)gkv.x * gkv.y * gkv.z, (int64_t)gq.x * gq.y * gq.z);
     if (ss.stream && longest <= 2 * resident) side = ss.stream;
   }
-  hipEvent_t fork = nullptr, join = nullptr;
-  if (side && hipEventCreateWithFlags(&fork, hipEventDisableTiming) != hipSuccess) side = nullptr;
-  if (side && hipEventCreateWithFlags(&join, hipEventDisableTiming) != hipSuccess) {
-    (void)hipEventDestroy(fork);
-    side = nullptr;
+  hipEvent_t ev[3] = {nullptr, nullptr, nullptr};        // fork, dq done, join
+  for (int i = 0; side && i < 3; ++i) {
+    if (hipEventCreateWithFlags(&ev[i], hipEventDisableTiming) != hipSuccess) {
+      for (int j = 0; j < i; ++j) (void)hipEventDestroy(ev[j]);
+      side = nullptr;
+    }
   }
   if (side) {
-    hipError_t e = hipEventRecord(fork, s);
-    if (e == hipSuccess) e = hipStreamWaitEvent(side, fork, 0);
-    if (e != hipSuccess) {                 // nothing launched yet: run both on the caller's stream
-      (void)hipEventDestroy(fork);
-      (void)hipEventDestroy(join);
+    hipError_t e = hipEventRecord(ev[0], s);
+    if (e == hipSuccess) e = hipStreamWaitEvent(side, ev[0], 0);
+    if (e != hipSuccess) {                 // nothing launched yet: run everything on the caller's stream
+      for (hipEvent_t x : ev) (void)hipEventDestroy(x);
       side = nullptr;
     }
   }
   if (!side) {
     hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, MODE, DROP, G>), gkv, dim3(256), 0, s, p);
     hipLaunchKernelGGL((bwd_dq_kernel<E, D, MODE, DROP, G, RPS>), gq, dim3(256), 0, s, p);
-    return hipGetLastError();
+    hipError_t e = hipGetLastError();
+    if (e == hipSuccess && tail) e = tail(p, s);
+    if (e == hipSuccess && side_tail) e = side_tail(p, s);
+    return e;
   }
   hipLaunchKernelGGL((bwd_dq_kernel<E, D, MODE, DROP, G, RPS>), gq, dim3(256), 0, side, p);
   hipError_t e = hipGetLastError();
+  auto keep = [&e](hipError_t x) { if (e == hipSuccess) e = x; };
+  keep(hipEventRecord(ev[1], side));
+  if (e == hipSuccess && side_tail) e = side_tail(p, side);
   hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, MODE, DROP, G>), gkv, dim3(256), 0, s, p);
-  const hipError_t e2 = hipGetLastError();
-  if (e == hipSuccess) e = e2;
-  const hipError_t e3 = hipEventRecord(join, side);
-  const hipError_t e4 = e3 == hipSuccess ? hipStreamWaitEvent(s, join, 0) : e3;
-  if (e == hipSuccess) e = e4;
-  (void)hipEventDestroy(fork);
-  (void)hipEventDestroy(join);
+  keep(hipGetLastError());
+  keep(hipStreamWaitEvent(s, ev[1], 0));
+  if (e == hipSuccess && tail) e = tail(p, s);
+  const hipError_t ej = hipEventRecord(ev[2], side);
+  keep(ej);
+  keep(ej == hipSuccess ? hipStreamWaitEvent(s, ev[2], 0) : ej);
+  for (hipEvent_t x : ev) (void)hipEventDestroy(x);
   return e;
 }
 
 template <typename E, int D, typename G>
-hipError_t launch_modes(const BwdParams& p, hipStream_t s) {
+hipError_t launch_modes(const BwdParams& p, hipStream_t s, BwdTail tail, BwdTail side_tail) {
   const bool drop = p.keep != nullptr;
   switch (bmode_of(p)) {
-    case B_NONE: return drop ? launch_main<E, D, B_NONE, true, G>(p, s) : launch_main<E, D, B_NONE, false, G>(p, s);
-    case B_INDEX: return drop ? launch_main<E, D, B_INDEX, true, G>(p, s) : launch_main<E, D, B_INDEX, false, G>(p, s);
+    case B_NONE: return drop ? launch_main<E, D, B_NONE, true, G>(p, s, tail, side_tail) : launch_main<E, D, B_NONE, false, G>(p, s, tail, side_tail);
+    case B_INDEX: return drop ? launch_main<E, D, B_INDEX, true, G>(p, s, tail, side_tail) : launch_main<E, D, B_INDEX, false, G>(p, s, tail, side_tail);
     case B_RELPOS:
       if (p.grid_h <= 32 && p.grid_w <= 32) {
-        return drop ? launch_main<E, D, B_RELPOS, true, G, true>(p, s) : launch_main<E, D, B_RELPOS, false, G, true>(p, s);
+        return drop ? launch_main<E, D, B_RELPOS, true, G, true>(p, s, tail, side_tail) : launch_main<E, D, B_RELPOS, false, G, true>(p, s, tail, side_tail);
       } else {
-        return drop ? launch_main<E, D, B_RELPOS, true, G>(p, s) : launch_main<E, D, B_RELPOS, false, G>(p, s);
+        return drop ? launch_main<E, D, B_RELPOS, true, G>(p, s, tail, side_tail) : launch_main<E, D, B_RELPOS, false, G>(p, s, tail, side_tail);
       }
     case B_RELPOS64:
-      return drop ? launch_main<E, D, B_RELPOS64, true, G>(p, s) : launch_main<E, D, B_RELPOS64, false, G>(p, s);
-    default: return drop ? launch_main<E, D, B_TENSOR, true, G>(p, s) : launch_main<E, D, B_TENSOR, false, G>(p, s);
+      return drop ? launch_main<E, D, B_RELPOS64, true, G>(p, s, tail, side_tail) : launch_main<E, D, B_RELPOS64, false, G>(p, s, tail, side_tail);
+    default: return drop ? launch_main<E, D, B_TENSOR, true, G>(p, s, tail, side_tail) : launch_main<E, D, B_TENSOR, false, G>(p, s, tail, side_tail);
   }
 }
 
 template <typename E, int D>
-hipError_t launch_typed(const BwdParams& p, hipStream_t s) {
+hipError_t launch_typed(const BwdParams& p, hipStream_t s, BwdTail tail, BwdTail side_tail) {
   const int64_t rows = p.B * p.Hq * p.Tq;
   const int64_t blocks = (rows * (D / 8) + 255) / 256;
   if (p.o_dtype == 0) hipLaunchKernelGGL((bwd_delta_kernel<E, float, D>), dim3((unsigned)blocks), dim3(256), 0, s, p, rows);
   else hipLaunchKernelGGL((bwd_delta_kernel<E, E, D>), dim3((unsigned)blocks), dim3(256), 0, s, p, rows);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return p.grad_dtype == 0 ? launch_modes<E, D, float>(p, s) : launch_modes<E, D, E>(p, s);
+  return p.grad_dtype == 0 ? launch_modes<E, D, float>(p, s, tail, side_tail) : launch_modes<E, D, E>(p, s, tail, side_tail);
 }
 
 template <typename E>
-hipError_t launch_e(const BwdParams& p, hipStream_t s) {
-  if (p.D == 32) return launch_typed<E, 32>(p, s);
-  if (p.D == 64) return launch_typed<E, 64>(p, s);
-  return launch_typed<E, 128>(p, s);
+hipError_t launch_e(const BwdParams& p, hipStream_t s, BwdTail tail, BwdTail side_tail) {
+  if (p.D == 32) return launch_typed<E, 32>(p, s, tail, side_tail);
+  if (p.D == 64) return launch_typed<E, 64>(p, s, tail, side_tail);
+  return launch_typed<E, 128>(p, s, tail, side_tail);
 }
 
 }  // namespace
@@ -1093,8 +1103,8 @@ bool bwd_supports(const BwdParams& p) {
   return true;
 }
 
-hipError_t launch_bwd(const BwdParams& p, hipStream_t s) {
-  return p.dtype == 2 ? launch_e<_Float16>(p, s) : launch_e<__bf16>(p, s);
+hipError_t launch_bwd(const BwdParams& p, hipStream_t s, BwdTail tail, BwdTail side_tail) {
+  return p.dtype == 2 ? launch_e<_Float16>(p, s, tail, side_tail) : launch_e<__bf16>(p, s, tail, side_tail);
 }
 
 }  // namespace sdpa

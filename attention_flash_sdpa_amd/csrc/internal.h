@@ -175,9 +175,16 @@ hipError_t launch_dropout_mask(const DropoutParams& p, hipStream_t s);
 // Backward (16-bit inputs, head_dim 32 / 64 / 128, every bias kind but rel-pos):
 // delta, then dK / dV (one workgroup per key block), then dQ (one per query block).
 bool bwd_supports(const BwdParams& p);
-hipError_t launch_bwd(const BwdParams& p, hipStream_t s);
-// Rel-pos tail of the backward: dq = dq_acc + the tables' part, d rel_pos_h / w.
-hipError_t launch_relpos_bwd_tail(const BwdParams& p, hipStream_t s);
+// Work that needs dq: `tail` runs on s after every kernel of the pass;
+// `side_tail` (independent of `tail`'s outputs, and not reading dk / dv) may
+// run on a second stream right after the dQ kernel.
+using BwdTail = hipError_t (*)(const BwdParams& p, hipStream_t s);
+hipError_t launch_bwd(const BwdParams& p, hipStream_t s, BwdTail tail = nullptr, BwdTail side_tail = nullptr);
+// Rel-pos tail of the backward, in two independent parts:
+// dq = dq_acc + the tables' part ...
+hipError_t launch_relpos_bwd_dq(const BwdParams& p, hipStream_t s);
+// ... and d rel_pos_h / d rel_pos_w.
+hipError_t launch_relpos_bwd_tables(const BwdParams& p, hipStream_t s);
 // Attention weights [B, Hq, Tq, Tkv] fp32 from the forward pass's lse (any dtype, head_dim <= 128).
 hipError_t launch_attn_weights(const FwdParams& p, float* weights, hipStream_t s);
 // True if the call runs on the matrix-core weights kernel (16-bit inputs, head_dim 32 / 64 / 128).

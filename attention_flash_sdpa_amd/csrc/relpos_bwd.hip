@@ -569,22 +569,9 @@ bool relpos_dq_mfma_ok(const BwdParams& p) {
   return gh <= 64 && gw <= 64 && p.B * p.Hq * gh * gw * (gh > gw ? gh : gw) * 4 <= 0x7fffffffLL;
 }
 
-template <typename E, int D, typename G>
-void tail_typed(const BwdParams& p, hipStream_t s) {
-  if (p.tgrad_mfma && relpos_dq_mfma_ok<D>(p)) {
-    // lines per workgroup as the kernel derives them: 4 / (32 x 32 output blocks per line), at least 1
-    auto ipg = [](int L) { const int nb = (L + 31) / 32 * (D / 32); return nb >= 4 ? 1 : 4 / nb; };
-    const int ih = ipg(p.grid_w), iw = ipg(p.grid_h);
-    const int64_t nh = p.B * p.Hq * p.grid_h, nw = p.B * p.Hq * p.grid_w;
-    hipLaunchKernelGGL((relpos_dq_mfma_kernel<E, D, G, true>), dim3((unsigned)((nh + ih - 1) / ih)), dim3(256),
-                       (size_t)ih * dq_lds_bytes(p.grid_w, p.grid_h, D), s, p);
-    hipLaunchKernelGGL((relpos_dq_mfma_kernel<E, D, G, false>), dim3((unsigned)((nw + iw - 1) / iw)), dim3(256),
-                       (size_t)iw * dq_lds_bytes(p.grid_h, p.grid_w, D), s, p);
-  } else {
-    constexpr int QPB = 256 / (D / 16);
-    dim3 gq((unsigned)((p.Tq + QPB - 1) / QPB), (unsigned)(p.B * p.Hq));
-    hipLaunchKernelGGL((relpos_bwd_dq_kernel<E, D, G>), gq, dim3(256), 0, s, p);
-  }
+// The tables' gradients d rel_pos_h / d rel_pos_w from dterm_h / dterm_w and q.
+template <typename E, int D>
+void tables_typed(const BwdParams& p, hipStream_t s) {
   if (relpos_tgrad_mfma_ok(p.B, p.Hq, p.grid_h, p.grid_w, D) && p.tgrad_mfma) {
     const int nwg = relpos_tgrad_wgs(p.B, p.Hq, p.grid_h, p.grid_w);
     const int64_t ih = p.B * p.Hq * p.grid_h, iw = p.B * p.Hq * p.grid_w;
@@ -613,24 +600,52 @@ void tail_typed(const BwdParams& p, hipStream_t s) {
                      (const float*)p.group_w, p.drel_w, p.grid_w, D, p.split_w);
 }
 
+template <typename E, int D, typename G>
+void tail_typed(const BwdParams& p, hipStream_t s, bool dq_part) {
+  if (!dq_part) {
+    tables_typed<E, D>(p, s);
+    return;
+  }
+  if (p.tgrad_mfma && relpos_dq_mfma_ok<D>(p)) {
+    // lines per workgroup as the kernel derives them: 4 / (32 x 32 output blocks per line), at least 1
+    auto ipg = [](int L) { const int nb = (L + 31) / 32 * (D / 32); return nb >= 4 ? 1 : 4 / nb; };
+    const int ih = ipg(p.grid_w), iw = ipg(p.grid_h);
+    const int64_t nh = p.B * p.Hq * p.grid_h, nw = p.B * p.Hq * p.grid_w;
+    hipLaunchKernelGGL((relpos_dq_mfma_kernel<E, D, G, true>), dim3((unsigned)((nh + ih - 1) / ih)), dim3(256),
+                       (size_t)ih * dq_lds_bytes(p.grid_w, p.grid_h, D), s, p);
+    hipLaunchKernelGGL((relpos_dq_mfma_kernel<E, D, G, false>), dim3((unsigned)((nw + iw - 1) / iw)), dim3(256),
+                       (size_t)iw * dq_lds_bytes(p.grid_h, p.grid_w, D), s, p);
+  } else {
+    constexpr int QPB = 256 / (D / 16);
+    dim3 gq((unsigned)((p.Tq + QPB - 1) / QPB), (unsigned)(p.B * p.Hq));
+    hipLaunchKernelGGL((relpos_bwd_dq_kernel<E, D, G>), gq, dim3(256), 0, s, p);
+  }
+}
+
 template <typename E, int D>
-void tail_g(const BwdParams& p, hipStream_t s) {
-  if (p.grad_dtype == 0) tail_typed<E, D, float>(p, s);
-  else tail_typed<E, D, E>(p, s);
+void tail_g(const BwdParams& p, hipStream_t s, bool dq_part) {
+  if (p.grad_dtype == 0) tail_typed<E, D, float>(p, s, dq_part);
+  else tail_typed<E, D, E>(p, s, dq_part);
 }
 
 template <typename E>
-void tail_e(const BwdParams& p, hipStream_t s) {
-  if (p.D == 32) tail_g<E, 32>(p, s);
-  else if (p.D == 64) tail_g<E, 64>(p, s);
-  else tail_g<E, 128>(p, s);
+void tail_e(const BwdParams& p, hipStream_t s, bool dq_part) {
+  if (p.D == 32) tail_g<E, 32>(p, s, dq_part);
+  else if (p.D == 64) tail_g<E, 64>(p, s, dq_part);
+  else tail_g<E, 128>(p, s, dq_part);
 }
 
 }  // namespace
 
-hipError_t launch_relpos_bwd_tail(const BwdParams& p, hipStream_t s) {
-  if (p.dtype == 2) tail_e<_Float16>(p, s);
-  else tail_e<__bf16>(p, s);
+hipError_t launch_relpos_bwd_dq(const BwdParams& p, hipStream_t s) {
+  if (p.dtype == 2) tail_e<_Float16>(p, s, true);
+  else tail_e<__bf16>(p, s, true);
+  return hipGetLastError();
+}
+
+hipError_t launch_relpos_bwd_tables(const BwdParams& p, hipStream_t s) {
+  if (p.dtype == 2) tail_e<_Float16>(p, s, false);
+  else tail_e<__bf16>(p, s, false);
   return hipGetLastError();
 }
 

@@ -250,9 +250,10 @@ const char* sdpa_last_kernel(void);
  *                  device holds at once), the backward calls run them side by
  *                  side: dQ on a second stream of the device (created once
  *                  per device, default priority, never while the caller's
- *                  stream is being captured), forked from and joined back
- *                  into the caller's stream with events, so later work on
- *                  the caller's stream still sees every gradient.  The
+ *                  stream is being captured), followed there by the rel-pos
+ *                  tables' gradients, forked from and joined back into the
+ *                  caller's stream with events, so later work on the
+ *                  caller's stream still sees every gradient.  The
  *                  results are the same bit for bit.  Calls on several
  *                  streams of one device share its second stream, so their
  *                  dQ kernels run in the order the calls were made.
