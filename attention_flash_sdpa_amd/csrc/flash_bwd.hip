@@ -960,9 +960,9 @@ int bmode_of(const BwdParams& p) {
 
 // The second stream of the current device for the dQ kernel (created on first
 // use, default priority, not synchronising with the null stream) and the
-// device's compute-unit count; a null stream when none is available.  A
-// stream is not created while the caller's stream is being captured into a
-// graph.
+// device's compute-unit count; a null stream when none is available or the
+// caller's stream is being captured into a graph (a captured call keeps
+// every kernel on the caller's stream).
 struct SideStream {
   hipStream_t stream;
   int cus;
@@ -974,11 +974,11 @@ SideStream side_stream(hipStream_t caller) {
   static SideStream per_dev[kMaxDevices] = {};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return {nullptr, 0};
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(caller, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return {nullptr, 0};
   std::lock_guard<std::mutex> lock(mu);
   SideStream& d = per_dev[dev];
   if (!d.stream) {
-    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-    if (hipStreamIsCapturing(caller, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return {nullptr, 0};
     int cus = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
       return {nullptr, 0};

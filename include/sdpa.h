@@ -249,8 +249,9 @@ const char* sdpa_last_kernel(void);
  *                  kernels are short (at most twice the workgroups the
  *                  device holds at once), the backward calls run them side by
  *                  side: dQ on a second stream of the device (created once
- *                  per device, default priority, never while the caller's
- *                  stream is being captured), followed there by the rel-pos
+ *                  per device, default priority; a call on a stream that is
+ *                  being captured into a graph keeps both kernels on it),
+ *                  followed there by the rel-pos
  *                  tables' gradients, forked from and joined back into the
  *                  caller's stream with events, so later work on the
  *                  caller's stream still sees every gradient.  The

@@ -301,6 +301,47 @@ def test_backward_concurrent_matches_sequential(gpu, case):
         assert torch.equal(x, z)
 
 
+@pytest.mark.parametrize("case", [BWD_STREAM_CASES[0], BWD_STREAM_CASES[2]], ids=["plain", "relpos"])
+def test_backward_in_graph_matches_eager(gpu, case):
+    """A backward call captured into a graph keeps its kernels on the
+    capturing stream; every replay, with eager calls (which do use the second
+    stream) in between, gives the eager call's bits."""
+    name, B, Hq, Hkv, T, D, grid = case
+    rng = np.random.default_rng(45)
+    q, do = (draw(rng, (B, Hq, T, D), torch.bfloat16).cuda() for _ in range(2))
+    k, v = (draw(rng, (B, Hkv, T, D), torch.bfloat16).cuda() for _ in range(2))
+    if grid:
+        rh = (0.3 * draw(rng, (2 * grid[0] - 1, D), torch.float32)).to(torch.bfloat16).cuda()
+        rw = (0.3 * draw(rng, (2 * grid[1] - 1, D), torch.float32)).to(torch.bfloat16).cuda()
+        o, lse = gpu.sdpa_relpos(q, k, v, rh, rw, grid, return_lse=True)
+        call = lambda: gpu.sdpa_relpos_backward(q, k, v, o, do, lse, rh, rw, grid)
+    else:
+        o, lse = gpu.sdpa(q, k, v, return_lse=True)
+        call = lambda: gpu.sdpa_backward(q, k, v, o, do, lse)
+    eager = call()
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()                                       # warm-up off the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        captured = call()
+    for _ in range(3):
+        for t in captured:
+            t.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        for x, y in zip(eager, captured):
+            assert torch.equal(x, y)
+        again = call()                               # eager work between replays
+        torch.cuda.synchronize()
+        for x, y in zip(eager, again):
+            assert torch.equal(x, y)
+
+
 def test_backward_after_library_forward(gpu):
     """End to end on the GPU: forward with dropout (library keep bits), then the
     backward from the library's own O and lse, against the oracle on the same bits."""
