@@ -960,9 +960,10 @@ int bmode_of(const BwdParams& p) {
 
 // The second stream of the current device for the dQ kernel (created on first
 // use, default priority, not synchronising with the null stream) and the
-// device's compute-unit count; a null stream when none is available or the
-// caller's stream is being captured into a graph (a captured call keeps
-// every kernel on the caller's stream).
+// device's compute-unit count; a null stream when none is available, when
+// the caller's stream belongs to another device than the current one, or
+// when it is being captured into a graph (such calls keep every kernel on
+// the caller's stream).
 struct SideStream {
   hipStream_t stream;
   int cus;
@@ -972,8 +973,9 @@ SideStream side_stream(hipStream_t caller) {
   constexpr int kMaxDevices = 64;
   static std::mutex mu;
   static SideStream per_dev[kMaxDevices] = {};
-  int dev = 0;
+  int dev = 0, sdev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return {nullptr, 0};
+  if (hipStreamGetDevice(caller, &sdev) != hipSuccess || sdev != dev) return {nullptr, 0};
   hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
   if (hipStreamIsCapturing(caller, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return {nullptr, 0};
   std::lock_guard<std::mutex> lock(mu);

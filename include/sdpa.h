@@ -250,7 +250,9 @@ const char* sdpa_last_kernel(void);
  *                  device holds at once), the backward calls run them side by
  *                  side: dQ on a second stream of the device (created once
  *                  per device, default priority; a call on a stream that is
- *                  being captured into a graph keeps both kernels on it),
+ *                  being captured into a graph, or that belongs to another
+ *                  device than the calling thread's current one, keeps both
+ *                  kernels on it),
  *                  followed there by the rel-pos
  *                  tables' gradients, forked from and joined back into the
  *                  caller's stream with events, so later work on the
