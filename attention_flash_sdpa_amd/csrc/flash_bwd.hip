@@ -996,12 +996,13 @@ SideStream side_stream(hipStream_t caller) {
 // The two kernels read the same inputs and delta and write disjoint
 // outputs, so with p.concurrent the dQ kernel can run on the device's
 // second stream beside the dK/dV kernel: the workgroups of each then fill
-// CUs the other leaves idle.  That pays when both grids are short, at most
-// two rounds of the workgroups the chip holds at once (SAM ViT-B global
-// attention at batch 1 runs 384 + 384 workgroups where 512 fit; its 14x14
-// windows 600 + 600).  Longer grids leave little tail to fill and run one
-// after the other, which keeps each kernel's workgroups together in the
-// caches.  Side by side, an event forks the second stream from the caller's
+// CUs the other leaves idle.  That pays when a kernel's grid leaves at least
+// a tenth of the workgroup slots of its last round empty (rounds of the
+// workgroups the chip holds at once: SAM ViT-B global attention runs 384
+// workgroups per kernel and batch item where 512 fit, its 14x14 windows 600
+// per 25 windows).  Grids that fill their rounds (gqa_causal: 1024 and 4096
+// workgroups, 256 at a time) run one after the other, which keeps each
+// kernel's workgroups together in the caches.  Side by side, an event forks the second stream from the caller's
 // after delta; `side_tail` follows dQ there, while `tail` runs on the
 // caller's stream once dQ (a second event) and dK/dV are done, and a third
 // event joins the second stream back, so work queued later on the caller's
@@ -1014,8 +1015,13 @@ hipError_t launch_main(const BwdParams& p, hipStream_t s, BwdTail tail, BwdTail 
   if (p.concurrent) {
     const SideStream ss = side_stream(s);
     const int64_t resident = (int64_t)ss.cus * (D == 128 ? 1 : 2);       // workgroups per CU at these launch bounds
-    const int64_t longest = std::max<int64_t>((int64_t)gkv.x * gkv.y * gkv.z, (int64_t)gq.x * gq.y * gq.z);
-    if (ss.stream && longest <= 2 * resident) side = ss.stream;
+    // fraction of the last round of resident workgroups a kernel leaves empty
+    auto idle = [&](int64_t n) {
+      const int64_t r = (n + resident - 1) / resident;
+      return (double)(r * resident - n) / (double)(r * resident);
+    };
+    const int64_t nkv = (int64_t)gkv.x * gkv.y * gkv.z, nq = (int64_t)gq.x * gq.y * gq.z;
+    if (ss.stream && resident > 0 && std::max(idle(nkv), idle(nq)) >= 0.1) side = ss.stream;
   }
   hipEvent_t ev[3] = {nullptr, nullptr, nullptr};        // fork, dq done, join
   for (int i = 0; side && i < 3; ++i) {

@@ -245,10 +245,10 @@ const char* sdpa_last_kernel(void);
  *                  gradients and the tables' part of dq on the matrix cores
  *                  where the grid allows it (both sides <= 64); 0 = on the
  *                  vector ALUs.
- *   "bwd_concurrent" 1 (default) = where both grids of the dK/dV and dQ
- *                  kernels are short (at most twice the workgroups the
- *                  device holds at once), the backward calls run them side by
- *                  side: dQ on a second stream of the device (created once
+ *   "bwd_concurrent" 1 (default) = where the grid of the dK/dV or the dQ
+ *                  kernel leaves at least a tenth of its last round of
+ *                  resident workgroups empty, the backward calls run the two
+ *                  side by side: dQ on a second stream of the device (created once
  *                  per device, default priority; a call on a stream that is
  *                  being captured into a graph, or that belongs to another
  *                  device than the calling thread's current one, keeps both
